@@ -1,0 +1,75 @@
+"""Plant plausible mistakes in the oracle (on the CPU, in a temporary copy of
+its source) and check that the pins catch every one of them.  This is what
+makes the pins a real check of the oracle rather than a restatement of it.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "mdn_oracle.c")
+
+# (name, text in the oracle, replacement).  Each text must occur exactly once.
+MUTANTS = [
+    ("residual drops alpha",
+     "vt[c] = vv[c] - a * vt[c];", "vt[c] = vv[c] - vt[c];"),
+    ("residual sign",
+     "vt[c] = vv[c] - a * vt[c];", "vt[c] = vv[c] + a * vt[c];"),
+    ("momentum write sign",
+     "M[x] = m * M[x] - e * kt[i] * vt[c];", "M[x] = m * M[x] + e * kt[i] * vt[c];"),
+    ("momentum retention dropped",
+     "M[x] = m * M[x] - e * kt[i] * vt[c];", "M[x] = - e * kt[i] * vt[c];"),
+    ("eta dropped",
+     "M[x] = m * M[x] - e * kt[i] * vt[c];", "M[x] = m * M[x] - kt[i] * vt[c];"),
+    ("memory step sign",
+     "S[x] = a * S[x] - s * M[x];", "S[x] = a * S[x] + s * M[x];"),
+    ("memory decay dropped",
+     "S[x] = a * S[x] - s * M[x];", "S[x] = S[x] - s * M[x];"),
+    ("memory reads old momentum",
+     "                M[x] = m * M[x] - e * kt[i] * vt[c];\n"
+     "                S[x] = a * S[x] - s * M[x];",
+     "                S[x] = a * S[x] - s * M[x];\n"
+     "                M[x] = m * M[x] - e * kt[i] * vt[c];"),
+    ("read-out uses key",
+     "o[c] += S[(size_t)i * nc + c] * qt[i];", "o[c] += S[(size_t)i * nc + c] * kt[i];"),
+    ("residual uses query",
+     "vt[c] += S[(size_t)i * nc + c] * kt[i];", "vt[c] += S[(size_t)i * nc + c] * qt[i];"),
+    ("gates swapped",
+     "const double a = alpha[g];\n        const double m = mu[g];",
+     "const double a = mu[g];\n        const double m = alpha[g];"),
+    ("beta ignored",
+     "const double s = beta ? beta[g] : 1.0;", "const double s = 1.0;"),
+    ("initial momentum ignored",
+     "M[(size_t)i * nc + c] = M0 ? M0[IDX_STATE(b, h, i, c0 + c, H, Dk, Dv)] : 0.0;",
+     "M[(size_t)i * nc + c] = 0.0;"),
+    ("final states swapped",
+     "if (ST) ST[IDX_STATE(b, h, i, c0 + c, H, Dk, Dv)] = S[(size_t)i * nc + c];",
+     "if (ST) ST[IDX_STATE(b, h, i, c0 + c, H, Dk, Dv)] = M[(size_t)i * nc + c];"),
+    ("value column offset dropped",
+     "const double* vv = v + IDX_TOK(b, t, h, c0, T, H, Dv);",
+     "const double* vv = v + IDX_TOK(b, t, h, 0, T, H, Dv);"),
+    ("brute force: Gamma row shift off by one",
+     "if (j < i) x = G[(size_t)(i - 1) * n + j];", "if (j < i) x = G[(size_t)i * n + j];"),
+    ("brute force: carry uses old momentum sign",
+     "Mn[x] = mbar[n] * M[x] - wm;", "Mn[x] = mbar[n] * M[x] + wm;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, old, new, tmp_path):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for '{name}' not found exactly once"
+    mutated = tmp_path / "mutant.c"
+    mutated.write_text(src.replace(old, new))
+    so = oracle.build(str(mutated), str(tmp_path / "libmutant.so"))
+    lib = oracle.load(so)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, RuntimeError, FloatingPointError, ValueError,
+                __import__("numpy").linalg.LinAlgError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake '{name}'"
