@@ -1,0 +1,214 @@
+"""Benchmark of the MDN hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--decode-steps D] [--no-cpu-baseline]
+
+A step is one chunkwise forward (mdn_chunk_fwd: coefficients, T, A, residual
+solve, outputs and carried state) over the 1.3B-like layer B=8, H=16,
+T=4096, d_k=d_v=128, chunk 64, bf16 q/k/v with fp32 gates and state, inputs
+resident in HBM.  `value` is tokens/s = B*T per step / time per step.
+
+The same JSON line carries:
+  roofline      the dominant kernel's algorithmic FLOP rate against the bf16
+                MFMA peak, timed with HIP events on the launch stream;
+  kernels       every kernel's mean time over the timed steps;
+  decode        the recurrent decode step at 256 sequences x 16 heads, d 128
+                (GB/s of algorithmic state + token traffic);
+  cpu_baseline  the fp64 oracle timed on this host's cores.
+Rank 0 prints one JSON line; only one GPU is supported.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MDN chunkwise fwd tokens/s at H=16,d=128,T=4096; % MFMA peak; decode GB/s"
+PEAK_BF16_FLOPS = 2.5e15        # MI355X dense bf16 MFMA
+PEAK_HBM_BPS = 8.0e12           # MI355X HBM3E
+
+# algorithmic work (dense count, d = d_k = d_v, C = 64), per token and head
+D, C = 128, 64
+FLOP_SCAN = 12 * D * D + 4 * C * D       # K[S|M], Q[S|M], K^T[Vt], T R, A Vt
+FLOP_PREP = 4 * C * D                    # K K^T, Q K^T
+FLOP_FWD = FLOP_SCAN + FLOP_PREP         # 12 d^2 + 8 C d
+BYTES_FWD = 3 * D * 2 + D * 2 + 3 * 4    # q, k, v, O (bf16) + three gates (fp32)
+DEC_BYTES_HEAD = 4 * D * D * 4 + 3 * D * 2 + D * 2 + 3 * 4   # S, M in+out; q k v o; gates
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--decode-steps", type=int, default=64)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-decode", action="store_true")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def up(x, dtype):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(dtype)
+
+
+def bench_forward(args, torch, si, mdn):
+    cfg = si.CONFIGS[2]
+    t0 = time.time()
+    inp = si.make_forward(cfg)
+    log(f"inputs {cfg.name} drawn in {time.time() - t0:.1f}s")
+    bf = torch.bfloat16
+    f32 = torch.float32
+    plan = mdn.ChunkPlan(up(inp["q"], bf), up(inp["k"], bf), up(inp["v"], bf),
+                         up(inp["alpha"], f32), up(inp["mu"], f32), up(inp["eta"], f32))
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        plan.prepare()
+        plan.scan()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record()
+        plan.prepare()
+        ev[s][1].record()
+        plan.scan()
+        ev[s][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    prep_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    scan_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    span_ms = ev[0][0].elapsed_time(ev[-1][2])
+    step_ms = span_ms / args.steps
+    tokens = cfg.B * cfg.T
+    toh = cfg.B * cfg.T * cfg.H
+    log(f"forward: {step_ms * 1e3:.1f} us/step (prepare {prep_ms * 1e3:.1f} us, "
+        f"scan {scan_ms * 1e3:.1f} us), wall {wall / args.steps * 1e3:.1f} us/step")
+    kernels = {
+        "chunk_prep_kernel": {"us": prep_ms * 1e3, "flop": FLOP_PREP * toh,
+                              "tflops": FLOP_PREP * toh / (prep_ms * 1e-3) / 1e12},
+        "chunk_scan_kernel": {"us": scan_ms * 1e3, "flop": FLOP_SCAN * toh,
+                              "tflops": FLOP_SCAN * toh / (scan_ms * 1e-3) / 1e12},
+    }
+    dom = max(kernels, key=lambda n: kernels[n]["us"])
+    k = kernels[dom]
+    achieved = k["flop"] / (k["us"] * 1e-6)
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": achieved / 1e12,
+                "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_FLOPS, "traffic": None,
+                "flop_per_launch": k["flop"], "flop_per_tok_head": FLOP_SCAN
+                if dom == "chunk_scan_kernel" else FLOP_PREP}
+    fwd = {"us_per_step": step_ms * 1e3, "tokens_per_s": tokens / (step_ms * 1e-3),
+           "mfma_frac": FLOP_FWD * toh / (step_ms * 1e-3) / PEAK_BF16_FLOPS,
+           "hbm_frac_algorithmic": BYTES_FWD * toh / (step_ms * 1e-3) / PEAK_HBM_BPS}
+    return cfg, inp, step_ms, kernels, roofline, fwd
+
+
+def bench_decode(args, torch, si, mdn):
+    cfg = si.CONFIGS[4]
+    import dataclasses
+    dcfg = dataclasses.replace(cfg, steps=args.decode_steps)
+    t0 = time.time()
+    stream = si.decode_stream(dcfg)
+    S0, M0 = next(stream)
+    S = up(S0, torch.float32)
+    M = up(M0, torch.float32)
+    del S0, M0
+    bf, f32 = torch.bfloat16, torch.float32
+    toks = []
+    for _ in range(dcfg.steps):
+        t = next(stream)
+        toks.append((up(t["q"], bf), up(t["k"], bf), up(t["v"], bf), up(t["alpha"], f32),
+                     up(t["mu"], f32), up(t["eta"], f32)))
+    o = torch.empty((cfg.N, cfg.H, cfg.Dv), dtype=bf, device="cuda")
+    log(f"decode inputs ({dcfg.steps} steps) drawn in {time.time() - t0:.1f}s")
+    for i in range(min(3, dcfg.steps)):
+        mdn.decode_step(*toks[i], S, M, o)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in toks:
+        mdn.decode_step(*t, S, M, o)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / dcfg.steps * 1e3
+    heads = cfg.N * cfg.H
+    gbs = DEC_BYTES_HEAD * heads / (us * 1e-6) / 1e9
+    log(f"decode: {us:.1f} us/step, {gbs:.0f} GB/s algorithmic")
+    return {"workload": f"decode N{cfg.N} H{cfg.H} d{cfg.Dk} fp32 state, bf16 tokens",
+            "us_per_step": us, "GB_per_s": gbs, "hbm_frac": gbs * 1e9 / PEAK_HBM_BPS,
+            "bytes_per_step": DEC_BYTES_HEAD * heads, "steps_timed": dcfg.steps,
+            "kernel": "decode_step_kernel"}
+
+
+def cpu_baseline(inp, cfg):
+    import oracle
+    lib = oracle.load()
+    cores = oracle.max_threads(lib)
+    t0 = time.perf_counter()
+    oracle.recurrence(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["mu"], inp["eta"], lib=lib)
+    sec = time.perf_counter() - t0
+    log(f"oracle: {sec:.1f}s on {cores} threads")
+    return {"value": cfg.B * cfg.T / sec, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"the whole {cfg.name} workload (B{cfg.B} H{cfg.H} T{cfg.T} d{cfg.Dk}), "
+                      f"fp64 token recurrence, one pass, {sec:.1f}s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the MDN core shards "
+              "over batch x heads with no communication, so the per-GPU figure is the "
+              "--gpus 1 figure.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synthetic_inputs as si
+    from chunkwise_delta_rule_amd import mdn
+    if not os.path.exists(mdn.LIB_PATH):
+        from chunkwise_delta_rule_amd import build as libbuild
+        libbuild.build()
+    mdn.load_library()
+    cfg, inp, step_ms, kernels, roofline, fwd = bench_forward(args, torch, si, mdn)
+    decode = None if args.no_decode else bench_decode(args, torch, si, mdn)
+    base = None if args.no_cpu_baseline else cpu_baseline(inp, cfg)
+    tokens = cfg.B * cfg.T
+    line = {
+        "metric": METRIC,
+        "value": tokens / (step_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mdn_chunk_fwd 1.3B-like layer", "B": cfg.B, "T": cfg.T,
+                   "H": cfg.H, "d_k": cfg.Dk, "d_v": cfg.Dv, "chunk": cfg.chunk,
+                   "io": "bf16 q/k/v/O, fp32 gates and state", "tokens_per_step": tokens},
+        "roofline": roofline,
+        "forward": fwd,
+        "kernels": kernels,
+        "decode": decode,
+        "cpu_baseline": base,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

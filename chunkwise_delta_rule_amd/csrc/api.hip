@@ -1,0 +1,260 @@
+// api.hip -- the libmdn C ABI: host-side validation and dispatch.
+//
+// Every check happens here, before anything is launched; an error status
+// means nothing was enqueued.  Device data is never inspected.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/libmdn.h"
+
+namespace mdn {
+size_t chunk_workspace_bytes(int B, int T, int H, bool bf16);
+hipError_t launch_chunk_prepare(const void* q, const void* k, const float* alpha, const float* mu,
+                                const float* eta, int B, int T, int H, int Dk, bool bf16,
+                                void* workspace, hipStream_t stream);
+hipError_t launch_chunk_scan(const void* q, const void* k, const void* v, const float* S0,
+                             const float* M0, void* O, float* ST, float* MT, int B, int T, int H,
+                             int Dk, int Dv, bool bf16, const void* workspace, hipStream_t stream);
+hipError_t launch_decode(const void* q, const void* k, const void* v, const float* alpha,
+                         const float* mu, const float* eta, float* S, float* M, void* o,
+                         int heads, int Dk, int Dv, bool bf16, hipStream_t stream);
+}  // namespace mdn
+
+namespace {
+
+struct Span {
+    uintptr_t lo = 0, hi = 0;   // [lo, hi); empty when lo == hi
+};
+
+Span span(const void* p, size_t bytes)
+{
+    Span s;
+    if (p && bytes) {
+        s.lo = reinterpret_cast<uintptr_t>(p);
+        s.hi = s.lo + bytes;
+    }
+    return s;
+}
+
+bool overlap(const Span& a, const Span& b)
+{
+    return a.lo != a.hi && b.lo != b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
+// a * b * c * d without overflow past 2^62 (plenty for any device buffer)
+bool mul_ok(size_t a, size_t b, size_t c, size_t d, size_t* out)
+{
+    const size_t lim = (size_t)1 << 62;
+    size_t x = a;
+    for (size_t f : {b, c, d}) {
+        if (f != 0 && x > lim / f) return false;
+        x *= f;
+    }
+    *out = x;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mdn_status_string(mdn_status s)
+{
+    switch (s) {
+    case MDN_OK: return "MDN_OK";
+    case MDN_ERR_NULL: return "MDN_ERR_NULL: a required pointer is NULL";
+    case MDN_ERR_SHAPE: return "MDN_ERR_SHAPE: a size is negative or too large";
+    case MDN_ERR_UNSUPPORTED: return "MDN_ERR_UNSUPPORTED: head size, chunk or dtype not supported";
+    case MDN_ERR_ALIGN: return "MDN_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case MDN_ERR_ALIAS: return "MDN_ERR_ALIAS: an output overlaps another argument";
+    case MDN_ERR_WORKSPACE: return "MDN_ERR_WORKSPACE: workspace missing or too small";
+    case MDN_ERR_HIP: return "MDN_ERR_HIP: a HIP launch failed";
+    }
+    return "unknown mdn_status";
+}
+
+size_t mdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
+                                     mdn_dtype dt)
+{
+    if (B <= 0 || T <= 0 || H <= 0) return 0;
+    if (!head_dim_ok(Dk) || !head_dim_ok(Dv) || chunk != 64) return 0;
+    if (dt != MDN_F32 && dt != MDN_BF16) return 0;
+    size_t tmp;
+    if (!mul_ok((size_t)B, (size_t)T, (size_t)H, 1, &tmp)) return 0;
+    return mdn::chunk_workspace_bytes(B, T, H, dt == MDN_BF16);
+}
+
+}  // extern "C"
+
+namespace {
+
+enum Phase { PREPARE = 1, SCAN = 2, BOTH = 3 };
+
+struct FwdArgs {
+    const void *q, *k, *v;
+    const float *alpha, *mu, *eta, *S0, *M0;
+    void* O;
+    float *S_T, *M_T;
+    int B, T, H, Dk, Dv, chunk;
+    mdn_dtype dt;
+    const void* ws;
+    size_t ws_bytes;
+};
+
+// Every host-side check of the forward entry points.  `phase` says which
+// arguments the call uses: the prepare phase reads q, k and the gates and
+// writes the workspace; the scan reads q, k, v, the states and the workspace
+// and writes O and the final states.
+mdn_status validate_fwd(const FwdArgs& a, int phase, bool* no_work)
+{
+    *no_work = false;
+    if (a.B < 0 || a.T < 0 || a.H < 0) return MDN_ERR_SHAPE;
+    if (!head_dim_ok(a.Dk) || !head_dim_ok(a.Dv) || a.chunk != 64) return MDN_ERR_UNSUPPORTED;
+    if (a.dt != MDN_F32 && a.dt != MDN_BF16) return MDN_ERR_UNSUPPORTED;
+    if (a.B == 0 || a.H == 0 || (a.T == 0 && !(phase & SCAN))) {
+        *no_work = true;
+        return MDN_OK;
+    }
+    const size_t esz = a.dt == MDN_BF16 ? 2 : 4;
+    size_t nqk, nv, ngate, nstate;
+    if (!mul_ok((size_t)a.B, (size_t)a.T, (size_t)a.H, (size_t)a.Dk, &nqk) ||
+        !mul_ok((size_t)a.B, (size_t)a.T, (size_t)a.H, (size_t)a.Dv, &nv) ||
+        !mul_ok((size_t)a.B, (size_t)a.T, (size_t)a.H, 1, &ngate) ||
+        !mul_ok((size_t)a.B, (size_t)a.H, (size_t)a.Dk, (size_t)a.Dv, &nstate))
+        return MDN_ERR_SHAPE;
+    // one workgroup per chunk (prepare) or per head tile (scan), 1-D grids
+    if ((size_t)a.B * a.H * (((size_t)a.T + 63) / 64) > 0xffffffffu) return MDN_ERR_SHAPE;
+    const bool tok = a.T > 0;
+    if (tok && (!a.q || !a.k)) return MDN_ERR_NULL;
+    if (tok && (phase & PREPARE) && (!a.alpha || !a.mu || !a.eta)) return MDN_ERR_NULL;
+    if (tok && (phase & SCAN) && (!a.v || !a.O)) return MDN_ERR_NULL;
+
+    const void* ptrs[] = {a.q, a.k, a.v, a.alpha, a.mu, a.eta, a.S0, a.M0, a.O, a.S_T, a.M_T, a.ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MDN_ERR_ALIGN;
+
+    const size_t need = tok ? mdn::chunk_workspace_bytes(a.B, a.T, a.H, a.dt == MDN_BF16) : 0;
+    if (need > 0 && (!a.ws || a.ws_bytes < need)) return MDN_ERR_WORKSPACE;
+
+    const size_t nt = tok ? 1 : 0;   // token arrays are empty when T == 0
+    const bool prep = phase & PREPARE, scan = phase & SCAN;
+    const Span sq = span(a.q, nt * nqk * esz), sk = span(a.k, nt * nqk * esz),
+               sv = span(scan ? a.v : nullptr, nt * nv * esz),
+               sa = span(prep ? a.alpha : nullptr, nt * ngate * 4),
+               sm = span(prep ? a.mu : nullptr, nt * ngate * 4),
+               se = span(prep ? a.eta : nullptr, nt * ngate * 4),
+               sS0 = span(scan ? a.S0 : nullptr, nstate * 4),
+               sM0 = span(scan ? a.M0 : nullptr, nstate * 4),
+               sO = span(scan ? a.O : nullptr, nt * nv * esz),
+               sST = span(scan ? a.S_T : nullptr, nstate * 4),
+               sMT = span(scan ? a.M_T : nullptr, nstate * 4), sW = span(a.ws, need);
+    const Span inputs[] = {sq, sk, sv, sa, sm, se, sS0, sM0};
+    // O and the workspace overlap nothing
+    for (const Span& x : inputs)
+        if (overlap(sO, x) || overlap(sW, x)) return MDN_ERR_ALIAS;
+    if (overlap(sO, sW) || overlap(sO, sST) || overlap(sO, sMT) || overlap(sW, sST) ||
+        overlap(sW, sMT) || overlap(sST, sMT))
+        return MDN_ERR_ALIAS;
+    // final states overlap no input, except exactly in place over their own
+    // initial state
+    for (int i = 0; i < 8; ++i) {
+        if (overlap(sST, inputs[i]) && !(i == 6 && a.S_T == a.S0)) return MDN_ERR_ALIAS;
+        if (overlap(sMT, inputs[i]) && !(i == 7 && a.M_T == a.M0)) return MDN_ERR_ALIAS;
+    }
+    return MDN_OK;
+}
+
+mdn_status run_fwd(const FwdArgs& a, int phase, hipStream_t stream)
+{
+    bool no_work = false;
+    const mdn_status st = validate_fwd(a, phase, &no_work);
+    if (st != MDN_OK || no_work) return st;
+    const bool bf16 = a.dt == MDN_BF16;
+    if (phase & PREPARE) {
+        const hipError_t err =
+            mdn::launch_chunk_prepare(a.q, a.k, a.alpha, a.mu, a.eta, a.B, a.T, a.H, a.Dk, bf16,
+                                      const_cast<void*>(a.ws), stream);
+        if (err != hipSuccess) return MDN_ERR_HIP;
+    }
+    if (phase & SCAN) {
+        const hipError_t err =
+            mdn::launch_chunk_scan(a.q, a.k, a.v, a.S0, a.M0, a.O, a.S_T, a.M_T, a.B, a.T, a.H,
+                                   a.Dk, a.Dv, bf16, a.ws, stream);
+        if (err != hipSuccess) return MDN_ERR_HIP;
+    }
+    return MDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mdn_status mdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                         const float* mu, const float* eta, const float* S0, const float* M0,
+                         void* O, float* S_T, float* M_T, int B, int T, int H, int Dk, int Dv,
+                         int chunk, mdn_dtype dt, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream)
+{
+    const FwdArgs a{q, k, v, alpha, mu, eta, S0, M0, O, S_T, M_T, B, T, H, Dk, Dv, chunk, dt,
+                    workspace, workspace_bytes};
+    return run_fwd(a, BOTH, stream);
+}
+
+mdn_status mdn_chunk_fwd_prepare(const void* q, const void* k, const float* alpha,
+                                 const float* mu, const float* eta, int B, int T, int H, int Dk,
+                                 int chunk, mdn_dtype dt, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream)
+{
+    // the scan's Dv does not change the prepared data; any supported value
+    // validates the same
+    const FwdArgs a{q, k, nullptr, alpha, mu, eta, nullptr, nullptr, nullptr, nullptr, nullptr,
+                    B, T, H, Dk, 64, chunk, dt, workspace, workspace_bytes};
+    return run_fwd(a, PREPARE, stream);
+}
+
+mdn_status mdn_chunk_fwd_scan(const void* q, const void* k, const void* v, const float* S0,
+                              const float* M0, void* O, float* S_T, float* M_T, int B, int T,
+                              int H, int Dk, int Dv, int chunk, mdn_dtype dt,
+                              const void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const FwdArgs a{q, k, v, nullptr, nullptr, nullptr, S0, M0, O, S_T, M_T, B, T, H, Dk, Dv,
+                    chunk, dt, workspace, workspace_bytes};
+    return run_fwd(a, SCAN, stream);
+}
+
+mdn_status mdn_decode_step(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* mu, const float* eta, float* S, float* M, void* o,
+                           int N, int H, int Dk, int Dv, mdn_dtype dt, hipStream_t stream)
+{
+    if (N < 0 || H < 0) return MDN_ERR_SHAPE;
+    if (!head_dim_ok(Dk) || !head_dim_ok(Dv)) return MDN_ERR_UNSUPPORTED;
+    if (dt != MDN_F32 && dt != MDN_BF16) return MDN_ERR_UNSUPPORTED;
+    if (N == 0 || H == 0) return MDN_OK;
+    size_t heads, nstate;
+    if (!mul_ok((size_t)N, (size_t)H, 1, 1, &heads) ||
+        !mul_ok((size_t)N, (size_t)H, (size_t)Dk, (size_t)Dv, &nstate))
+        return MDN_ERR_SHAPE;
+    if (heads > 0x7fffffffu) return MDN_ERR_SHAPE;
+    if (!q || !k || !v || !alpha || !mu || !eta || !S || !M || !o) return MDN_ERR_NULL;
+    const void* ptrs[] = {q, k, v, alpha, mu, eta, S, M, o};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return MDN_ERR_ALIGN;
+    const size_t esz = dt == MDN_BF16 ? 2 : 4;
+    const Span sq = span(q, heads * Dk * esz), sk = span(k, heads * Dk * esz),
+               sv = span(v, heads * Dv * esz), sa = span(alpha, heads * 4),
+               sm = span(mu, heads * 4), se = span(eta, heads * 4), sS = span(S, nstate * 4),
+               sM = span(M, nstate * 4), so = span(o, heads * Dv * esz);
+    const Span inputs[] = {sq, sk, sv, sa, sm, se};
+    for (const Span& x : inputs)
+        if (overlap(so, x) || overlap(sS, x) || overlap(sM, x)) return MDN_ERR_ALIAS;
+    if (overlap(so, sS) || overlap(so, sM) || overlap(sS, sM)) return MDN_ERR_ALIAS;
+    const hipError_t err = mdn::launch_decode(q, k, v, alpha, mu, eta, S, M, o, (int)heads, Dk,
+                                              Dv, dt == MDN_BF16, stream);
+    return err == hipSuccess ? MDN_OK : MDN_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+// decode.hip -- the recurrent MDN decode step on gfx950.
+//
+// One token per (sequence n, head h), applied to the fixed-size state pair in
+// place ("MDN: Parallelizing Stepwise Momentum for Delta Linear Attention"
+// (slides), Sec. 3.1 Eqs. (3)-(5); decoding keeps S and M, "Chunk outputs
+// combine incoming states and local writes"):
+//     vt = v - alpha S^T k
+//     M  = mu M - eta k vt^T
+//     S  = alpha S - M
+//     o  = S^T q
+//
+// The step is bound by HBM traffic: each head reads and writes its two fp32
+// Dk x Dv matrices once (256 KiB per head at d = 128) and does 8 Dk Dv flops
+// on them.  One 256-thread workgroup owns one head.  Each thread keeps a
+// 4-column strip of RPT rows of S and M in registers, so the whole head is
+// loaded once with 16-byte coalesced loads (a wavefront covers two full rows
+// per load), reduced twice through LDS (S^T k before the update, S^T q after
+// it) and stored once.  The columns of S and M are independent, which is why
+// the only cross-thread traffic is the two column reductions over Dk.
+#include <hip/hip_runtime.h>
+
+#include "mfma.hpp"
+
+namespace mdn {
+
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(256) void decode_step_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ mu, const float* __restrict__ eta,
+    float* __restrict__ S, float* __restrict__ M, E* __restrict__ o)
+{
+    constexpr int CPR = DV / 4;       // threads across one row (4 columns each)
+    constexpr int RPP = 256 / CPR;    // rows covered by one pass of the block
+    constexpr int RPT = DK / RPP;     // rows per thread
+    static_assert(DV % 4 == 0 && 256 % CPR == 0 && DK % RPP == 0, "tile shape");
+
+    __shared__ float ks[DK];
+    __shared__ float qs[DK];
+    __shared__ f32x4 red[RPP][CPR];
+
+    const int tid = threadIdx.x;
+    const int tx = tid % CPR;
+    const int ty = tid / CPR;
+    const size_t head = blockIdx.x;                    // n * H + h
+    const size_t sbase = head * DK * DV;
+    float* Sh = S + sbase;
+    float* Mh = M + sbase;
+
+    // the whole strip of S and M is requested before anything waits on it
+    f32x4 s_reg[RPT], m_reg[RPT];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        const int row = ty + RPP * j;
+        s_reg[j] = *reinterpret_cast<const f32x4*>(Sh + (size_t)row * DV + 4 * tx);
+        m_reg[j] = *reinterpret_cast<const f32x4*>(Mh + (size_t)row * DV + 4 * tx);
+    }
+    for (int i = tid; i < DK; i += 256) {
+        ks[i] = to_f32(k[head * DK + i]);
+        qs[i] = to_f32(q[head * DK + i]);
+    }
+    const float a = alpha[head];
+    const float m = mu[head];
+    const float e = eta[head];
+    f32x4 vv;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vv[c] = to_f32(v[head * DV + 4 * tx + c]);
+    __syncthreads();
+
+    // S^T k over this thread's rows, then across the RPP row groups
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) acc += s_reg[j] * ks[ty + RPP * j];
+    red[ty][tx] = acc;
+    __syncthreads();
+    f32x4 skt = zero4();
+#pragma unroll
+    for (int g = 0; g < RPP; ++g) skt += red[g][tx];
+    const f32x4 vt = vv - a * skt;
+
+    // momentum then memory, in place; accumulate S^T q on the new memory
+    f32x4 acc_o = zero4();
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        const int row = ty + RPP * j;
+        const float kr = ks[row];
+        const f32x4 mn = m * m_reg[j] - (e * kr) * vt;
+        const f32x4 sn = a * s_reg[j] - mn;
+        *reinterpret_cast<f32x4*>(Mh + (size_t)row * DV + 4 * tx) = mn;
+        *reinterpret_cast<f32x4*>(Sh + (size_t)row * DV + 4 * tx) = sn;
+        acc_o += sn * qs[row];
+    }
+    __syncthreads();   // every thread has read red[] for S^T k
+    red[ty][tx] = acc_o;
+    __syncthreads();
+    if (ty == 0) {
+        f32x4 ot = zero4();
+#pragma unroll
+        for (int g = 0; g < RPP; ++g) ot += red[g][tx];
+        store4<E>(o + head * DV + 4 * tx, ot[0], ot[1], ot[2], ot[3]);
+    }
+}
+
+template <typename E, int DK, int DV>
+static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* alpha,
+                                  const float* mu, const float* eta, float* S, float* M, void* o,
+                                  int heads, hipStream_t stream)
+{
+    hipLaunchKernelGGL((decode_step_kernel<E, DK, DV>), dim3(heads), dim3(256), 0, stream,
+                       static_cast<const E*>(q), static_cast<const E*>(k),
+                       static_cast<const E*>(v), alpha, mu, eta, S, M, static_cast<E*>(o));
+    return hipGetLastError();
+}
+
+// Host entry used by the C ABI layer; shapes are validated there.
+hipError_t launch_decode(const void* q, const void* k, const void* v, const float* alpha,
+                         const float* mu, const float* eta, float* S, float* M, void* o,
+                         int heads, int Dk, int Dv, bool bf16, hipStream_t stream)
+{
+#define MDN_DEC(E, DK, DV)                                                                       \
+    if (Dk == DK && Dv == DV)                                                                    \
+        return launch_decode_t<E, DK, DV>(q, k, v, alpha, mu, eta, S, M, o, heads, stream);
+    if (bf16) {
+        MDN_DEC(__bf16, 64, 64) MDN_DEC(__bf16, 64, 128) MDN_DEC(__bf16, 128, 64)
+        MDN_DEC(__bf16, 128, 128)
+    } else {
+        MDN_DEC(float, 64, 64) MDN_DEC(float, 64, 128) MDN_DEC(float, 128, 64)
+        MDN_DEC(float, 128, 128)
+    }
+#undef MDN_DEC
+    return hipErrorInvalidValue;
+}
+
+}  // namespace mdn

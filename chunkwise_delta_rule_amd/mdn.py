@@ -1,0 +1,241 @@
+"""Python binding of libmdn: argument marshalling only.
+
+Every step of the computation runs in libmdn's HIP kernels.  This module
+checks devices, dtypes, shapes and contiguity, allocates outputs and the
+workspace with torch, and passes raw device pointers plus torch's current
+HIP stream through the C ABI declared in ``include/libmdn.h``.  There is no
+fallback: if ``libmdn.so`` has not been built, importing the library fails
+loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmdn.so")
+
+MDN_F32 = 0
+MDN_BF16 = 1
+CHUNK = 64
+HEAD_DIMS = (64, 128)
+
+STATUS_NAMES = {
+    0: "MDN_OK",
+    1: "MDN_ERR_NULL",
+    2: "MDN_ERR_SHAPE",
+    3: "MDN_ERR_UNSUPPORTED",
+    4: "MDN_ERR_ALIGN",
+    5: "MDN_ERR_ALIAS",
+    6: "MDN_ERR_WORKSPACE",
+    7: "MDN_ERR_HIP",
+}
+
+# every symbol include/libmdn.h declares
+EXPORTED = ("mdn_chunk_fwd_workspace_bytes", "mdn_chunk_fwd", "mdn_chunk_fwd_prepare",
+            "mdn_chunk_fwd_scan", "mdn_decode_step", "mdn_status_string")
+
+
+class MdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}")
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmdn.so (built in-tree by ``chunkwise_delta_rule_amd.build``)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libmdn.so not found at {path}; build it first with "
+                          "`python -m chunkwise_delta_rule_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.mdn_chunk_fwd_workspace_bytes.restype = S
+    lib.mdn_chunk_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.mdn_chunk_fwd.restype = I
+    lib.mdn_chunk_fwd.argtypes = [P] * 11 + [I] * 7 + [P, S, P]
+    lib.mdn_chunk_fwd_prepare.restype = I
+    lib.mdn_chunk_fwd_prepare.argtypes = [P] * 5 + [I] * 6 + [P, S, P]
+    lib.mdn_chunk_fwd_scan.restype = I
+    lib.mdn_chunk_fwd_scan.argtypes = [P] * 8 + [I] * 7 + [P, S, P]
+    lib.mdn_decode_step.restype = I
+    lib.mdn_decode_step.argtypes = [P] * 9 + [I] * 5 + [P]
+    lib.mdn_status_string.restype = ctypes.c_char_p
+    lib.mdn_status_string.argtypes = [I]
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return MDN_BF16
+    if t == torch.float32:
+        return MDN_F32
+    raise TypeError(f"q, k, v must be bfloat16 or float32, got {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None or t.numel() == 0:
+        return None
+    return t.data_ptr()
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype, device):
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def workspace_bytes(B: int, T: int, H: int, Dk: int, Dv: int, dtype: torch.dtype,
+                    chunk: int = CHUNK) -> int:
+    return int(load_library().mdn_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk,
+                                                             _dtype_code(dtype)))
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+              mu: torch.Tensor, eta: torch.Tensor, S0: Optional[torch.Tensor] = None,
+              M0: Optional[torch.Tensor] = None, *, chunk: int = CHUNK,
+              O: Optional[torch.Tensor] = None, S_T: Optional[torch.Tensor] = None,
+              M_T: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+              final_state: bool = True
+              ) -> Tuple[torch.Tensor, Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """Chunkwise MDN forward.  q, k [B, T, H, Dk], v [B, T, H, Dv] (bf16 or
+    fp32), gates [B, T, H] fp32, S0/M0 [B, H, Dk, Dv] fp32 or None.
+    Returns (O, S_T, M_T); S_T/M_T are None when ``final_state`` is False and
+    none were passed in."""
+    lib = load_library()
+    dev = q.device
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    code = _dtype_code(dt)
+    _check(q, "q", (B, T, H, Dk), dt, dev)
+    _check(k, "k", (B, T, H, Dk), dt, dev)
+    _check(v, "v", (B, T, H, Dv), dt, dev)
+    for name, g in (("alpha", alpha), ("mu", mu), ("eta", eta)):
+        _check(g, name, (B, T, H), torch.float32, dev)
+    for name, s in (("S0", S0), ("M0", M0)):
+        if s is not None:
+            _check(s, name, (B, H, Dk, Dv), torch.float32, dev)
+    if O is None:
+        O = torch.empty((B, T, H, Dv), dtype=dt, device=dev)
+    _check(O, "O", (B, T, H, Dv), dt, dev)
+    if final_state and S_T is None:
+        S_T = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+    if final_state and M_T is None:
+        M_T = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+    for name, s in (("S_T", S_T), ("M_T", M_T)):
+        if s is not None:
+            _check(s, name, (B, H, Dk, Dv), torch.float32, dev)
+    need = int(lib.mdn_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, code))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.mdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(mu), _ptr(eta), _ptr(S0),
+                           _ptr(M0), _ptr(O), _ptr(S_T), _ptr(M_T), B, T, H, Dk, Dv, chunk, code,
+                           _ptr(workspace), wbytes, _stream(dev))
+    if st != 0:
+        raise MdnError(st, "mdn_chunk_fwd")
+    return O, S_T, M_T
+
+
+class ChunkPlan:
+    """Pre-validated arguments for repeated forward calls on fixed buffers:
+    the phases can then be launched (and timed) one by one.  Holds the
+    outputs and the workspace; launching performs no allocation."""
+
+    def __init__(self, q, k, v, alpha, mu, eta, S0=None, M0=None, *, chunk: int = CHUNK,
+                 final_state: bool = True):
+        self.lib = load_library()
+        self.args = (q, k, v, alpha, mu, eta, S0, M0)
+        B, T, H, Dk = q.shape
+        Dv = v.shape[-1]
+        self.shape = (B, T, H, Dk, Dv)
+        self.chunk = chunk
+        self.code = _dtype_code(q.dtype)
+        dev = q.device
+        self.O = torch.empty((B, T, H, Dv), dtype=q.dtype, device=dev)
+        self.S_T = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev) if final_state else None
+        self.M_T = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev) if final_state else None
+        need = int(self.lib.mdn_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, self.code))
+        self.workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        self.ws_bytes = need
+        # one full call validates every argument (and fills the outputs)
+        chunk_fwd(*self.args, chunk=chunk, O=self.O, S_T=self.S_T, M_T=self.M_T,
+                  workspace=self.workspace)
+        self.stream = _stream(dev)
+
+    def prepare(self):
+        q, k, _, a, m, e, _, _ = self.args
+        B, T, H, Dk, _ = self.shape
+        st = self.lib.mdn_chunk_fwd_prepare(_ptr(q), _ptr(k), _ptr(a), _ptr(m), _ptr(e), B, T, H,
+                                            Dk, self.chunk, self.code, _ptr(self.workspace),
+                                            self.ws_bytes, self.stream)
+        if st != 0:
+            raise MdnError(st, "mdn_chunk_fwd_prepare")
+
+    def scan(self):
+        q, k, v, _, _, _, S0, M0 = self.args
+        B, T, H, Dk, Dv = self.shape
+        st = self.lib.mdn_chunk_fwd_scan(_ptr(q), _ptr(k), _ptr(v), _ptr(S0), _ptr(M0),
+                                         _ptr(self.O), _ptr(self.S_T), _ptr(self.M_T), B, T, H,
+                                         Dk, Dv, self.chunk, self.code, _ptr(self.workspace),
+                                         self.ws_bytes, self.stream)
+        if st != 0:
+            raise MdnError(st, "mdn_chunk_fwd_scan")
+
+    def forward(self):
+        q, k, v, a, m, e, S0, M0 = self.args
+        B, T, H, Dk, Dv = self.shape
+        st = self.lib.mdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(m), _ptr(e),
+                                    _ptr(S0), _ptr(M0), _ptr(self.O), _ptr(self.S_T),
+                                    _ptr(self.M_T), B, T, H, Dk, Dv, self.chunk, self.code,
+                                    _ptr(self.workspace), self.ws_bytes, self.stream)
+        if st != 0:
+            raise MdnError(st, "mdn_chunk_fwd")
+
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                mu: torch.Tensor, eta: torch.Tensor, S: torch.Tensor, M: torch.Tensor,
+                o: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step: q, k [N, H, Dk], v [N, H, Dv], gates [N, H]; S, M
+    [N, H, Dk, Dv] fp32 updated in place.  Returns o [N, H, Dv]."""
+    lib = load_library()
+    dev = q.device
+    N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    code = _dtype_code(dt)
+    _check(q, "q", (N, H, Dk), dt, dev)
+    _check(k, "k", (N, H, Dk), dt, dev)
+    _check(v, "v", (N, H, Dv), dt, dev)
+    for name, g in (("alpha", alpha), ("mu", mu), ("eta", eta)):
+        _check(g, name, (N, H), torch.float32, dev)
+    _check(S, "S", (N, H, Dk, Dv), torch.float32, dev)
+    _check(M, "M", (N, H, Dk, Dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((N, H, Dv), dtype=dt, device=dev)
+    _check(o, "o", (N, H, Dv), dt, dev)
+    st = lib.mdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(mu), _ptr(eta),
+                             _ptr(S), _ptr(M), _ptr(o), N, H, Dk, Dv, code, _stream(dev))
+    if st != 0:
+        raise MdnError(st, "mdn_decode_step")
+    return o

@@ -1,0 +1,158 @@
+/*
+ * libmdn.h -- C ABI of libmdn, a gfx950 (MI355X) implementation of the
+ * Momentum DeltaNet (MDN) memory core: its chunkwise-parallel forward pass
+ * and its recurrent decode step.
+ *
+ * The operation (per batch entry b and head h, tokens t = 1..T):
+ *     vt_t = v_t - alpha_t S_{t-1}^T k_t
+ *     M_t  = mu_t M_{t-1} - eta_t k_t vt_t^T
+ *     S_t  = alpha_t S_{t-1} - M_t                 (update step beta = 1)
+ *     o_t  = S_t^T q_t
+ * with S, M in R^{Dk x Dv}.  This is the two-state recurrence of "MDN:
+ * Parallelizing Stepwise Momentum for Delta Linear Attention" (slides),
+ * Sec. 3.1 Eqs. (3)-(5), with the update step beta fixed to 1.  The forward
+ * pass evaluates it chunk by chunk as in the same slides' Eqs. (7)-(9),
+ * (15)-(18) and (40)-(42) (Appendix C forms, residual mask shifted one row
+ * as in the backup frame "a one-row shift is essential for causality"),
+ * which is exact in real arithmetic; the decode step applies one token.
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates nothing and keeps no per-call state; it is reentrant.
+ *  - Calls only enqueue work on `stream` and never synchronise; results are
+ *    valid once the stream has been synchronised.
+ *  - Arguments are validated on the host before any launch; on an error
+ *    nothing is launched and the status says why.  MDN_ERR_HIP reports a
+ *    failed launch.  Device data is never inspected: gate values are not
+ *    range-checked and non-finite values propagate.
+ *  - Pointers must be 16-byte aligned (MDN_ERR_ALIGN otherwise).
+ *  - No query scaling is applied: fold any d_k^{-1/2} into q.
+ *  - Supported head sizes: Dk, Dv in {64, 128}; chunk length 64.
+ *
+ * Layouts (row-major, C order):
+ *    q, k    [B, T, H, Dk]     dtype `dt`
+ *    v, O    [B, T, H, Dv]     dtype `dt`
+ *    alpha, mu, eta  [B, T, H] float32
+ *    S0, M0, S_T, M_T [B, H, Dk, Dv] float32
+ *  Decode: q, k [N, H, Dk]; v, o [N, H, Dv]; gates [N, H]; S, M [N, H, Dk, Dv].
+ */
+#ifndef LIBMDN_H
+#define LIBMDN_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MDN_OK = 0,
+    MDN_ERR_NULL = 1,        /* a required pointer is NULL                       */
+    MDN_ERR_SHAPE = 2,       /* a size is negative or a product overflows        */
+    MDN_ERR_UNSUPPORTED = 3, /* head size, chunk length or dtype not supported    */
+    MDN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                  */
+    MDN_ERR_ALIAS = 5,       /* an output overlaps an input (other than in place) */
+    MDN_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required           */
+    MDN_ERR_HIP = 7          /* a HIP launch failed                               */
+} mdn_status;
+
+typedef enum {
+    MDN_F32 = 0,  /* q, k, v and the output in float32  */
+    MDN_BF16 = 1  /* q, k, v and the output in bfloat16 */
+} mdn_dtype;
+
+/*
+ * Bytes of device workspace mdn_chunk_fwd needs for this problem (per-chunk
+ * coefficient vectors and the chunk-local matrices T and A of the slides'
+ * Eqs. (15)-(18) and (40)-(42)).  Returns 0 for unsupported or invalid sizes
+ * and when no work is needed (B, T or H is 0).
+ */
+size_t mdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
+                                     mdn_dtype dt);
+
+/*
+ * Chunkwise MDN forward over T tokens.
+ *   q, k, v          inputs, layouts above, dtype dt.
+ *   alpha, mu, eta   per-token, per-head gates (float32).  Any finite values
+ *                    are accepted; mu = 0 is the gated delta rule and
+ *                    additionally alpha = 1 is DeltaNet.
+ *   S0, M0           initial memory and momentum (float32); NULL = zero.
+ *   O                output o_t for every token (dtype dt); must not overlap
+ *                    any input.
+ *   S_T, M_T         final memory and momentum (float32); NULL = not written.
+ *                    S_T may be exactly S0 and M_T exactly M0 (in place); any
+ *                    other overlap is MDN_ERR_ALIAS.
+ *   chunk            must be 64.  T need not be a multiple of it: the last
+ *                    chunk is then partial.
+ *   workspace        device buffer of at least
+ *                    mdn_chunk_fwd_workspace_bytes(...) bytes, owned by the
+ *                    caller; its contents on entry do not matter.
+ * B, H >= 0 and T >= 0.  With T = 0, S_T/M_T receive S0/M0 (zeros if NULL)
+ * and O is untouched; with B = 0 or H = 0 nothing is launched.
+ */
+mdn_status mdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                         const float* mu, const float* eta, const float* S0, const float* M0,
+                         void* O, float* S_T, float* M_T, int B, int T, int H, int Dk, int Dv,
+                         int chunk, mdn_dtype dt, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
+ * The two phases mdn_chunk_fwd runs, exported so that a caller can time them
+ * separately or run the chunk-local phase ahead of the scan (for instance on
+ * another stream).  The reading notes on the MDN paper (Sec. 2.4) point out
+ * that T = [I + (P Khat^T) o Gamma^-]^{-1} and the scalar coefficients depend
+ * only on chunk-local inputs, while the carried state enters afterwards; the
+ * split follows that.  mdn_chunk_fwd(...) is exactly
+ *   mdn_chunk_fwd_prepare(...) followed by mdn_chunk_fwd_scan(...)
+ * on one stream with one workspace.
+ *
+ * mdn_chunk_fwd_prepare: per chunk, the coefficients (abar, mubar, b, Gamma;
+ *   slides Eqs. (7)-(9)), T = L^{-1} (Eqs. (15)-(18)) and
+ *   A = (Q Khat^T) o Gamma (Eqs. (40)-(42)), written to `workspace`.
+ *   Reads q, k and the gates only (layouts as for mdn_chunk_fwd; Dk is the
+ *   head size of q and k).  The workspace must hold at least
+ *   mdn_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, dt) bytes for the Dv
+ *   the scan will use (the size does not depend on Dk or Dv) and must not
+ *   overlap any input.  T = 0, B = 0 or H = 0: nothing is launched.
+ *
+ * mdn_chunk_fwd_scan: the sequential part (residuals, outputs and the
+ *   carried state pair), reading q, k, v, S0/M0 and the workspace a previous
+ *   mdn_chunk_fwd_prepare with the same B, T, H, Dk, chunk and dt filled on
+ *   the same stream (or after it, in stream order).  Output rules as for
+ *   mdn_chunk_fwd.
+ * Both return the same status codes as mdn_chunk_fwd for the same errors.
+ */
+mdn_status mdn_chunk_fwd_prepare(const void* q, const void* k, const float* alpha,
+                                 const float* mu, const float* eta, int B, int T, int H, int Dk,
+                                 int chunk, mdn_dtype dt, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+mdn_status mdn_chunk_fwd_scan(const void* q, const void* k, const void* v, const float* S0,
+                              const float* M0, void* O, float* S_T, float* M_T, int B, int T,
+                              int H, int Dk, int Dv, int chunk, mdn_dtype dt,
+                              const void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One recurrent decode step for N independent sequences (the recurrence
+ * above with T = 1; the slides' Sec. 3.1 notes that decoding keeps the
+ * fixed-size pair S, M).
+ *   q, k [N, H, Dk], v [N, H, Dv]    this step's token (dtype dt).
+ *   alpha, mu, eta [N, H]            this step's gates (float32).
+ *   S, M [N, H, Dk, Dv]              state, read and updated IN PLACE (float32).
+ *   o [N, H, Dv]                     output (dtype dt); must not overlap any
+ *                                    other argument.
+ * N, H >= 0; N = 0 or H = 0 launches nothing.
+ */
+mdn_status mdn_decode_step(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* mu, const float* eta, float* S, float* M, void* o,
+                           int N, int H, int Dk, int Dv, mdn_dtype dt, hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char* mdn_status_string(mdn_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMDN_H */

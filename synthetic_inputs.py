@@ -105,8 +105,30 @@ def round_io(x: np.ndarray, io_dtype: str) -> np.ndarray:
     raise ValueError(io_dtype)
 
 
-def _l2_normalise(x: np.ndarray) -> np.ndarray:
-    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+_BLOCK = 1 << 20   # elements per generation block (bounds temporaries)
+
+
+def _normal_rows(rng: np.random.Generator, shape, io_dtype: str, normalise: bool,
+                 scale: float = 1.0) -> np.ndarray:
+    """Draw N(0, 1) for a whole array in C order (block by block; the stream
+    is the same as one call), optionally L2-normalise each last-axis row in
+    float64, scale, and round once to the I/O dtype.  Returns float32."""
+    D = shape[-1]
+    rows = int(np.prod(shape[:-1]))
+    out = np.empty(shape, np.float32)
+    flat = out.reshape(rows, D)
+    blk = max(1, _BLOCK // D)
+    buf = np.empty((min(blk, rows), D))
+    for r0 in range(0, rows, blk):
+        r1 = min(rows, r0 + blk)
+        x = buf[: r1 - r0]
+        rng.standard_normal(out=x)
+        if normalise:
+            x /= np.linalg.norm(x, axis=1, keepdims=True)
+        if scale != 1.0:
+            x *= scale
+        flat[r0:r1] = round_io(x, io_dtype)
+    return out
 
 
 def _softplus(z: np.ndarray) -> np.ndarray:
@@ -142,24 +164,21 @@ def make_forward(cfg: ForwardConfig, **overrides) -> Dict[str, Optional[np.ndarr
         cfg = replace(cfg, **overrides)
     rng = np.random.Generator(np.random.PCG64(cfg.seed))
     B, T, H, Dk, Dv = cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv
-    q = rng.standard_normal((B, T, H, Dk))
-    k = rng.standard_normal((B, T, H, Dk))
-    v = rng.standard_normal((B, T, H, Dv))
+    q = _normal_rows(rng, (B, T, H, Dk), cfg.io_dtype, normalise=True)
+    k = _normal_rows(rng, (B, T, H, Dk), cfg.io_dtype, normalise=True)
+    v = _normal_rows(rng, (B, T, H, Dv), cfg.io_dtype, normalise=False)
     alpha, mu, eta = _gates(rng, (B, T, H), cfg.gates)
     S0 = M0 = None
     if cfg.init_state_std > 0:
-        S0 = (cfg.init_state_std * rng.standard_normal((B, H, Dk, Dv))).astype(np.float32)
-        M0 = (cfg.init_state_std * rng.standard_normal((B, H, Dk, Dv))).astype(np.float32)
-    q = round_io(_l2_normalise(q), cfg.io_dtype)
-    k = round_io(_l2_normalise(k), cfg.io_dtype)
-    v = round_io(v, cfg.io_dtype)
+        S0 = _normal_rows(rng, (B, H, Dk, Dv), "f32", False, cfg.init_state_std)
+        M0 = _normal_rows(rng, (B, H, Dk, Dv), "f32", False, cfg.init_state_std)
     return dict(q=q, k=k, v=v, alpha=alpha, mu=mu, eta=eta, S0=S0, M0=M0, cfg=cfg)
 
 
 def decode_initial_state(cfg: DecodeConfig, rng: np.random.Generator):
     shape = (cfg.N, cfg.H, cfg.Dk, cfg.Dv)
-    S = (cfg.state_std * rng.standard_normal(shape)).astype(np.float32)
-    M = (cfg.state_std * rng.standard_normal(shape)).astype(np.float32)
+    S = _normal_rows(rng, shape, "f32", False, cfg.state_std)
+    M = _normal_rows(rng, shape, "f32", False, cfg.state_std)
     return S, M
 
 
@@ -167,13 +186,11 @@ def decode_token(cfg: DecodeConfig, rng: np.random.Generator) -> Dict[str, np.nd
     """One decode step's inputs, drawn fresh: q, k L2-normalised, v ~ N(0,1),
     gates from normal logits as in the 1.3B-like layer."""
     N, H = cfg.N, cfg.H
-    q = rng.standard_normal((N, H, cfg.Dk))
-    k = rng.standard_normal((N, H, cfg.Dk))
-    v = rng.standard_normal((N, H, cfg.Dv))
+    q = _normal_rows(rng, (N, H, cfg.Dk), cfg.io_dtype, normalise=True)
+    k = _normal_rows(rng, (N, H, cfg.Dk), cfg.io_dtype, normalise=True)
+    v = _normal_rows(rng, (N, H, cfg.Dv), cfg.io_dtype, normalise=False)
     alpha, mu, eta = _gates(rng, (N, H), "logit")
-    return dict(q=round_io(_l2_normalise(q), cfg.io_dtype),
-                k=round_io(_l2_normalise(k), cfg.io_dtype),
-                v=round_io(v, cfg.io_dtype), alpha=alpha, mu=mu, eta=eta)
+    return dict(q=q, k=k, v=v, alpha=alpha, mu=mu, eta=eta)
 
 
 def decode_stream(cfg: DecodeConfig, **overrides) -> Iterator:

@@ -1,0 +1,191 @@
+"""Host-side checks of the libmdn C ABI that need no GPU: the library loads,
+exports every function include/libmdn.h declares, and rejects bad arguments
+with the documented status before anything is launched.  Pointers here are
+fake integers: every call below fails (or returns early) in host-side
+validation, so no HIP call is ever made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from chunkwise_delta_rule_amd import mdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libmdn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mdn.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mdn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(mdn.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    for code, name in mdn.STATUS_NAMES.items():
+        assert lib.mdn_status_string(code).decode().startswith(name)
+    assert lib.mdn_status_string(99) == b"unknown mdn_status"
+
+
+def test_workspace_bytes(lib):
+    ws = lib.mdn_chunk_fwd_workspace_bytes
+    # per chunk: T and A (C x C in the I/O dtype) and 8 coefficient vectors
+    per_bf16 = 2 * 64 * 64 * 2 + 8 * 64 * 4
+    per_f32 = 2 * 64 * 64 * 4 + 8 * 64 * 4
+    assert ws(8, 4096, 16, 128, 128, 64, mdn.MDN_BF16) == 8 * 16 * 64 * per_bf16
+    assert ws(1, 65, 2, 64, 64, 64, mdn.MDN_F32) == 2 * 2 * per_f32      # ragged: 2 chunks
+    assert ws(1, 1, 1, 64, 128, 64, mdn.MDN_BF16) == per_bf16
+    for bad in [(0, 64, 1, 64, 64, 64, 1), (1, 0, 1, 64, 64, 64, 1), (1, 64, 1, 96, 64, 64, 1),
+                (1, 64, 1, 64, 64, 32, 1), (1, 64, 1, 64, 64, 64, 7), (-1, 64, 1, 64, 64, 64, 1)]:
+        assert ws(*bad) == 0
+
+
+# fake, 16-byte aligned, non-overlapping "device" addresses
+BASE = 1 << 40
+STEP = 1 << 32
+
+
+def fake(i, off=0):
+    return BASE + i * STEP + off
+
+
+def fwd_args(**over):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), mu=fake(4), eta=fake(5), S0=fake(6),
+             M0=fake(7), O=fake(8), S_T=fake(9), M_T=fake(10), B=2, T=100, H=3, Dk=64, Dv=128,
+             chunk=64, dt=mdn.MDN_BF16, ws=fake(11), wsb=1 << 31, stream=None)
+    a.update(over)
+    return a
+
+
+def call_fwd(lib, a):
+    return lib.mdn_chunk_fwd(a["q"], a["k"], a["v"], a["alpha"], a["mu"], a["eta"], a["S0"],
+                             a["M0"], a["O"], a["S_T"], a["M_T"], a["B"], a["T"], a["H"], a["Dk"],
+                             a["Dv"], a["chunk"], a["dt"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(Dk=96), "MDN_ERR_UNSUPPORTED"),
+    (dict(Dv=256), "MDN_ERR_UNSUPPORTED"),
+    (dict(chunk=32), "MDN_ERR_UNSUPPORTED"),
+    (dict(dt=5), "MDN_ERR_UNSUPPORTED"),
+    (dict(B=-1), "MDN_ERR_SHAPE"),
+    (dict(T=-5), "MDN_ERR_SHAPE"),
+    (dict(q=None), "MDN_ERR_NULL"),
+    (dict(eta=None), "MDN_ERR_NULL"),
+    (dict(O=None), "MDN_ERR_NULL"),
+    (dict(k=fake(1, 8)), "MDN_ERR_ALIGN"),
+    (dict(S_T=fake(9, 4)), "MDN_ERR_ALIGN"),
+    (dict(ws=None), "MDN_ERR_WORKSPACE"),
+    (dict(wsb=1000), "MDN_ERR_WORKSPACE"),
+    (dict(O=fake(0)), "MDN_ERR_ALIAS"),                 # output over q
+    (dict(O=fake(2, 4096)), "MDN_ERR_ALIAS"),           # output inside v
+    (dict(ws=fake(8)), "MDN_ERR_ALIAS"),                # workspace over output
+    (dict(S_T=fake(7)), "MDN_ERR_ALIAS"),               # final memory over initial momentum
+    (dict(S_T=fake(6, 16)), "MDN_ERR_ALIAS"),           # shifted, not exactly in place
+    (dict(M_T=fake(9)), "MDN_ERR_ALIAS"),               # both final states at one address
+])
+def test_chunk_fwd_rejects(lib, over, status):
+    assert mdn.STATUS_NAMES[call_fwd(lib, fwd_args(**over))] == status
+
+
+def test_chunk_fwd_no_work_returns_ok_without_launch(lib):
+    # B = 0 or H = 0: nothing to do; pointers are never touched
+    assert call_fwd(lib, fwd_args(B=0, q=None, O=None, ws=None)) == 0
+    assert call_fwd(lib, fwd_args(H=0, q=None, O=None, ws=None)) == 0
+
+
+def dec_args(**over):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), mu=fake(4), eta=fake(5), S=fake(6),
+             M=fake(7), o=fake(8), N=4, H=2, Dk=128, Dv=128, dt=mdn.MDN_BF16, stream=None)
+    a.update(over)
+    return a
+
+
+def call_dec(lib, a):
+    return lib.mdn_decode_step(a["q"], a["k"], a["v"], a["alpha"], a["mu"], a["eta"], a["S"],
+                               a["M"], a["o"], a["N"], a["H"], a["Dk"], a["Dv"], a["dt"],
+                               a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(Dk=32), "MDN_ERR_UNSUPPORTED"),
+    (dict(dt=2), "MDN_ERR_UNSUPPORTED"),
+    (dict(N=-1), "MDN_ERR_SHAPE"),
+    (dict(S=None), "MDN_ERR_NULL"),
+    (dict(o=None), "MDN_ERR_NULL"),
+    (dict(v=fake(2, 2)), "MDN_ERR_ALIGN"),
+    (dict(o=fake(0)), "MDN_ERR_ALIAS"),
+    (dict(M=fake(6, 1024)), "MDN_ERR_ALIAS"),
+    (dict(S=fake(1)), "MDN_ERR_ALIAS"),
+])
+def test_decode_rejects(lib, over, status):
+    assert mdn.STATUS_NAMES[call_dec(lib, dec_args(**over))] == status
+
+
+def test_decode_no_work_returns_ok(lib):
+    assert call_dec(lib, dec_args(N=0, q=None)) == 0
+    assert call_dec(lib, dec_args(H=0, S=None)) == 0
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ImportError):
+        mdn.load_library(str(tmp_path / "libmdn.so"))
+
+
+def call_prepare(lib, a):
+    return lib.mdn_chunk_fwd_prepare(a["q"], a["k"], a["alpha"], a["mu"], a["eta"], a["B"],
+                                     a["T"], a["H"], a["Dk"], a["chunk"], a["dt"], a["ws"],
+                                     a["wsb"], a["stream"])
+
+
+def call_scan(lib, a):
+    return lib.mdn_chunk_fwd_scan(a["q"], a["k"], a["v"], a["S0"], a["M0"], a["O"], a["S_T"],
+                                  a["M_T"], a["B"], a["T"], a["H"], a["Dk"], a["Dv"], a["chunk"],
+                                  a["dt"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(Dk=32), "MDN_ERR_UNSUPPORTED"),
+    (dict(T=-1), "MDN_ERR_SHAPE"),
+    (dict(k=None), "MDN_ERR_NULL"),
+    (dict(mu=None), "MDN_ERR_NULL"),
+    (dict(alpha=fake(3, 4)), "MDN_ERR_ALIGN"),
+    (dict(ws=None), "MDN_ERR_WORKSPACE"),
+    (dict(ws=fake(1)), "MDN_ERR_ALIAS"),            # workspace over k
+])
+def test_prepare_rejects(lib, over, status):
+    assert mdn.STATUS_NAMES[call_prepare(lib, fwd_args(**over))] == status
+
+
+def test_prepare_no_work(lib):
+    assert call_prepare(lib, fwd_args(T=0, q=None, ws=None)) == 0
+    assert call_prepare(lib, fwd_args(B=0, q=None, ws=None)) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(Dv=32), "MDN_ERR_UNSUPPORTED"),
+    (dict(v=None), "MDN_ERR_NULL"),
+    (dict(O=None), "MDN_ERR_NULL"),
+    (dict(wsb=64), "MDN_ERR_WORKSPACE"),
+    (dict(O=fake(11)), "MDN_ERR_ALIAS"),           # output over the workspace
+    (dict(S_T=fake(11, 4096)), "MDN_ERR_ALIAS"),   # final state inside the workspace
+    (dict(M_T=fake(6)), "MDN_ERR_ALIAS"),          # final momentum over initial memory
+])
+def test_scan_rejects(lib, over, status):
+    assert mdn.STATUS_NAMES[call_scan(lib, fwd_args(**over))] == status

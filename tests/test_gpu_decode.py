@@ -1,0 +1,124 @@
+"""GPU parity of mdn_decode_step against the fp64 oracle, through the C ABI.
+
+The decode loop of 256 sequences x 16 heads (d = 128) runs all 512 steps on
+the GPU with fresh seeded tokens each step; the oracle follows 32 sampled
+(sequence, head) pairs through every step, and o is compared at every step
+for them, then the final S and M.  Small shapes cover every head-size pair
+and both I/O dtypes.  Tolerances are in parity.py.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic_inputs as si
+from chunkwise_delta_rule_amd import mdn
+from parity import TORCH_DT, assert_close, errors, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode(cfg, pairs=None, steps=None):
+    """Run `steps` decode steps on the GPU and the oracle (on `pairs` or all
+    heads).  Returns the worst per-step o error and the final states."""
+    steps = cfg.steps if steps is None else steps
+    dt = TORCH_DT[cfg.io_dtype]
+    stream = si.decode_stream(cfg)
+    S0, M0 = next(stream)
+    S = to_dev(S0)
+    M = to_dev(M0)
+    if pairs is None:
+        pairs = [(n, h) for n in range(cfg.N) for h in range(cfg.H)]
+    ni = np.array([p[0] for p in pairs])
+    hi = np.array([p[1] for p in pairs])
+    Sr = S0[ni, hi][:, None].astype(np.float64)          # [P, 1, Dk, Dv]
+    Mr = M0[ni, hi][:, None].astype(np.float64)
+    worst = (0.0, 0.0, 0.0)
+    for step in range(steps):
+        tok = next(stream)
+        o = mdn.decode_step(to_dev(tok["q"], dt), to_dev(tok["k"], dt), to_dev(tok["v"], dt),
+                            to_dev(tok["alpha"]), to_dev(tok["mu"]), to_dev(tok["eta"]), S, M)
+        sel = lambda x: x[ni, hi][:, None]
+        o_ref, Sr, Mr = oracle.decode_step(sel(tok["q"]), sel(tok["k"]), sel(tok["v"]),
+                                           sel(tok["alpha"]), sel(tok["mu"]), sel(tok["eta"]),
+                                           Sr, Mr)
+        o_got = to_np(o)[ni, hi][:, None]
+        err = errors(o_got, o_ref)
+        if err[0] > worst[0]:
+            worst = err
+        if cfg.io_dtype == "f32":
+            assert_close(o_got, o_ref, "f32", f"o step {step}")
+        elif err[0] > 2e-2 * max(1.0, err[2]):
+            assert_close(o_got, o_ref, "bf16", f"o step {step}")
+    torch.cuda.synchronize()
+    Sg = to_np(S)[ni, hi][:, None]
+    Mg = to_np(M)[ni, hi][:, None]
+    return worst, (Sg, Mg), (Sr, Mr)
+
+
+SMALL = [(io, dk, dv) for io in ("f32", "bf16") for (dk, dv) in
+         ((64, 64), (64, 128), (128, 64), (128, 128))]
+
+
+@pytest.mark.parametrize("io,dk,dv", SMALL, ids=[f"{a}-dk{b}-dv{c}" for a, b, c in SMALL])
+def test_decode_small(io, dk, dv):
+    cfg = dataclasses.replace(si.CONFIGS[4], N=3, H=5, Dk=dk, Dv=dv, steps=20, state_std=0.3,
+                              io_dtype=io, seed=4000 + dk + dv)
+    worst, got, ref = run_decode(cfg)
+    print(f"[decode {io} dk{dk} dv{dv}] worst o err {worst[0]:.3e} (max|o| {worst[1]:.3e})")
+    assert_close(got[0], ref[0], io, "S")
+    assert_close(got[1], ref[1], io, "M")
+
+
+def test_decode_full_config_sampled_heads():
+    """256 x 16 heads, d = 128, 512 steps (the benchmarked launch); 32 sampled
+    heads followed by the oracle through every step."""
+    cfg = si.CONFIGS[4]
+    rng = np.random.default_rng(99)
+    flat = rng.choice(cfg.N * cfg.H, size=32, replace=False)
+    pairs = [(int(f) // cfg.H, int(f) % cfg.H) for f in flat]
+    worst, got, ref = run_decode(cfg, pairs)
+    print(f"[decode N256 H16 d128 x512] worst o err {worst[0]:.3e} "
+          f"bound {2e-2 * max(1.0, worst[2]):.3e}")
+    assert_close(got[0], ref[0], "bf16", "S")
+    assert_close(got[1], ref[1], "bf16", "M")
+
+
+def test_decode_matches_forward():
+    """Decode steps chained over T tokens equal one chunkwise forward over the
+    same tokens (outputs and final states), both against the oracle."""
+    inp = si.make_forward(si.CONFIGS[1], B=2, T=150, H=3, init_state_std=0.2, seed=9)
+    dt = torch.bfloat16
+    S = to_dev(inp["S0"])
+    M = to_dev(inp["M0"])
+    outs = []
+    for t in range(150):
+        outs.append(mdn.decode_step(to_dev(inp["q"][:, t], dt), to_dev(inp["k"][:, t], dt),
+                                    to_dev(inp["v"][:, t], dt), to_dev(inp["alpha"][:, t]),
+                                    to_dev(inp["mu"][:, t]), to_dev(inp["eta"][:, t]), S, M))
+    O_dec = to_np(torch.stack(outs, dim=1))
+    O_fwd, S_fwd, M_fwd = mdn.chunk_fwd(to_dev(inp["q"], dt), to_dev(inp["k"], dt),
+                                        to_dev(inp["v"], dt), to_dev(inp["alpha"]),
+                                        to_dev(inp["mu"]), to_dev(inp["eta"]),
+                                        to_dev(inp["S0"]), to_dev(inp["M0"]))
+    torch.cuda.synchronize()
+    ref = oracle.recurrence(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["mu"], inp["eta"],
+                            None, inp["S0"], inp["M0"])
+    print("[decode chain vs forward]")
+    assert_close(O_dec, ref[0], "bf16", "O (decode)")
+    assert_close(to_np(S), ref[1], "bf16", "S (decode)")
+    assert_close(to_np(M), ref[2], "bf16", "M (decode)")
+    assert_close(O_dec, to_np(O_fwd), "bf16", "O decode vs forward")
+    assert_close(to_np(S), to_np(S_fwd), "bf16", "S decode vs forward")
+
+
+def test_decode_bad_arguments_raise():
+    dt = torch.bfloat16
+    x = torch.zeros(2, 2, 64, dtype=dt, device="cuda")
+    g = torch.zeros(2, 2, device="cuda")
+    S = torch.zeros(2, 2, 64, 64, device="cuda")
+    with pytest.raises(mdn.MdnError) as ex:
+        mdn.decode_step(x, x, x, g, g, g, S, S)        # S and M are the same buffer
+    assert ex.value.status == 5
