@@ -29,6 +29,10 @@ HIPCC_FLAGS = [
     "-fPIC",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs where they fit: the kernels apply
+    # VALU arithmetic to their accumulators every chunk, and AGPR-resident
+    # accumulators would need a copy each way
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 

@@ -25,15 +25,16 @@
 //
 // Two kernels:
 //   chunk_prep_kernel  one workgroup per chunk, fully parallel.  Coefficients
-//                      (VALU, one lane per row / per column), K K^T and Q K^T
-//                      on MFMA, L, T = L^{-1} by a 16x16-blocked forward
-//                      substitution, A = (Q Khat^T) o Gamma.  Writes T, A and
-//                      the coefficient vectors to the workspace.
-//   chunk_scan_kernel  one workgroup per (batch, head, Dv tile), sequential
-//                      over chunks.  The fp32 S and M tiles stay in MFMA
-//                      accumulators for the whole sequence; per chunk it
-//                      forms K[S0|M0] and Q[S0|M0], R, Vt = T R, O, and the
-//                      carried state, all as 16x16 MFMA tiles through LDS.
+//                      (one pass over the rows, gates broadcast across lanes),
+//                      K K^T and Q K^T on MFMA, L, T = L^{-1} (16x16 diagonal
+//                      blocks by forward substitution, off-diagonal blocks on
+//                      fp32 MFMA), A = (Q Khat^T) o Gamma.  Writes T, A and the
+//                      coefficient vectors to the workspace.
+//   chunk_scan_kernel  one workgroup per (batch, head, 64 value columns),
+//                      sequential over chunks.  Each wavefront keeps 16
+//                      columns of S and M in fp32 MFMA accumulators for the
+//                      whole sequence and feeds them, and its R and Vt, back
+//                      into the next products directly from the accumulators.
 #include <hip/hip_runtime.h>
 
 #include "mfma.hpp"
@@ -78,27 +79,91 @@ __host__ __device__ inline Workspace<E> ws_carve(void* base, size_t nchunks)
     return w;
 }
 
-// Stage rows [t0, t0 + n) of one head of a [B, T, H, D] tensor into LDS rows
-// of stride LD (elements); rows >= n are zero.  16-byte vectors, coalesced
-// along each row.
-template <typename E, int D, int LD>
-__device__ __forceinline__ void stage_rows(E* dst, const E* __restrict__ src, size_t row0_off,
-                                           size_t row_stride, int n, int tid)
-{
-    constexpr int EPV = 16 / sizeof(E);
-    constexpr int VPR = D / EPV;
-    for (int idx = tid; idx < CH * VPR; idx += NT) {
-        const int row = idx / VPR;
-        const int col = (idx % VPR) * EPV;
-        uint4 x = {0u, 0u, 0u, 0u};
-        if (row < n) x = *reinterpret_cast<const uint4*>(src + row0_off + row * row_stride + col);
-        *reinterpret_cast<uint4*>(dst + row * LD + col) = x;
+// Column swizzle of the transposed K copy K^T[d][c]: groups of 4 chunk rows c
+// are XOR-permuted by the row d, so that the transposing writes (8 values of
+// one chunk row per thread) spread over the LDS banks instead of landing 16
+// deep on one bank, while every aligned group of 4 stays contiguous for the
+// 8-byte fragment reads.
+__device__ __forceinline__ int kt_swz(int d, int c) { return c ^ (4 * ((d >> 3) & 7)); }
+
+// Prefetch of CH rows x D columns of a row-major [*, row_stride] array into
+// registers (16-byte vectors; rows >= n read as zero), stored later into an
+// LDS array with row stride LD.
+template <typename E, int D>
+struct RowTile {
+    static constexpr int EPV = 16 / sizeof(E);   // elements per vector
+    static constexpr int VPR = D / EPV;          // vectors per row
+    static constexpr int NV = CH * VPR / NT;     // vectors per thread
+    static_assert(CH * VPR % NT == 0, "tile must split evenly over the workgroup");
+    uint4 r[NV];
+    int n = CH;
+
+    // base: row 0 of the tile (wave-uniform).  Rows >= n read row n - 1 (so
+    // every load is in bounds and none is predicated) and are zeroed when
+    // stored, so the loads can stay in flight until then.
+    __device__ __forceinline__ void load(const E* __restrict__ base, unsigned row_stride, int rows,
+                                         int tid)
+    {
+        n = rows;
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int idx = tid + NT * u;
+            const int row = idx / VPR;
+            const unsigned col = (unsigned)(idx % VPR) * EPV;
+            const unsigned off = (unsigned)min(row, n - 1) * row_stride + col;
+            r[u] = *reinterpret_cast<const uint4*>(base + off);
+        }
     }
+    __device__ __forceinline__ uint4 get(int u, int tid) const
+    {
+        // bitwise mask rather than a select, so no branch is generated
+        const unsigned m = (tid + NT * u) / VPR < n ? ~0u : 0u;
+        return uint4{r[u].x & m, r[u].y & m, r[u].z & m, r[u].w & m};
+    }
+    template <int LD>
+    __device__ __forceinline__ void store(E* dst, int tid) const
+    {
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int idx = tid + NT * u;
+            *reinterpret_cast<uint4*>(dst + (idx / VPR) * LD + (idx % VPR) * EPV) = get(u, tid);
+        }
+    }
+    // transposed store: element (row, col) goes to dst[col * LD + kt_swz(col, row)]
+    template <int LD>
+    __device__ __forceinline__ void store_transposed(E* dst, int tid) const
+    {
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int idx = tid + NT * u;
+            const int row = idx / VPR;
+            const int col = (idx % VPR) * EPV;
+            const uint4 x = get(u, tid);
+            const E* e = reinterpret_cast<const E*>(&x);
+#pragma unroll
+            for (int j = 0; j < EPV; ++j) dst[(col + j) * LD + kt_swz(col + j, row)] = e[j];
+        }
+    }
+};
+
+__device__ __forceinline__ float lane_bcast(float x, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
 
 // ---------------------------------------------------------------------------
 // Per-chunk preparation
 // ---------------------------------------------------------------------------
+template <typename E, int DK>
+struct PrepSmem {
+    static constexpr int LDK = DK + Mma<E>::PAD;
+    static constexpr int LDG = CH + 4;   // fp32 C x C matrices; 4 rows apart = 16 banks apart
+    static constexpr size_t kq_bytes = 2 * CH * LDK * sizeof(E);
+    static constexpr size_t lt_bytes = 2 * CH * LDG * sizeof(float);
+    static constexpr size_t region0 = kq_bytes > lt_bytes ? kq_bytes : lt_bytes;
+    static constexpr size_t region1 = CH * LDG * sizeof(float);
+};
+
 template <typename E, int DK>
 __global__ __launch_bounds__(NT) void chunk_prep_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const float* __restrict__ alpha,
@@ -106,20 +171,25 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
     E* __restrict__ Aw, float* __restrict__ Vw, int T, int H, int NC)
 {
     using MM = Mma<E>;
-    constexpr int LDK = DK + MM::PAD;
-    constexpr int LDG = CH + 1;          // fp32 C x C matrices
+    using MF = Mma<float>;
+    using SM = PrepSmem<E, DK>;
+    constexpr int LDK = SM::LDK;
+    constexpr int LDG = SM::LDG;
 
-    __shared__ __align__(16) E Ks[CH * LDK];
-    __shared__ __align__(16) E Qs[CH * LDK];
-    __shared__ float al[CH], mus[CH], et[CH];
-    __shared__ float Gam[CH * LDG];
-    __shared__ float Ls[CH * LDG];
-    __shared__ float Ts[CH * LDG];
-    __shared__ float Xs[16 * LDG];
-    __shared__ float vecs[NVEC * CH];
+    // region0: K and Q rows, later L and T (fp32); region1: Gamma
+    __shared__ __align__(16) char smem0[SM::region0];
+    __shared__ __align__(16) char smem1[SM::region1];
+    __shared__ __align__(16) float al[CH];
+    __shared__ __align__(16) float mus[CH];
+    __shared__ __align__(16) float et[CH];
+    E* Ks = reinterpret_cast<E*>(smem0);
+    E* Qs = Ks + CH * LDK;
+    float* Ls = reinterpret_cast<float*>(smem0);
+    float* Ts = Ls + CH * LDG;
+    float* Gam = reinterpret_cast<float*>(smem1);
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int lane = tid & 63;
     const int l16 = lane & 15;
     const int lg = lane >> 4;
@@ -130,66 +200,90 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
     const int b = (int)(ch / ((size_t)NC * H));
     const int t0 = c * CH;
     const int n = min(CH, T - t0);
-
     const size_t tok0 = ((size_t)b * T + t0) * H + h;   // (b, t0, h)
-    stage_rows<E, DK, LDK>(Ks, k, tok0 * DK, (size_t)H * DK, n, tid);
-    stage_rows<E, DK, LDK>(Qs, q, tok0 * DK, (size_t)H * DK, n, tid);
-    if (tid < CH) {
-        float a = 1.f, m = 0.f, e = 0.f;
-        if (tid < n) {
-            const size_t g = tok0 + (size_t)tid * H;
-            a = alpha[g];
-            m = mu[g];
-            e = eta[g];
-        }
-        al[tid] = a;
-        mus[tid] = m;
-        et[tid] = e;
+
+    {
+        RowTile<E, DK> kt, qt;
+        kt.load(k + tok0 * DK, (unsigned)(H * DK), n, tid);
+        qt.load(q + tok0 * DK, (unsigned)(H * DK), n, tid);
+        kt.template store<LDK>(Ks, tid);
+        qt.template store<LDK>(Qs, tid);
     }
-    for (int i = tid; i < CH * LDG; i += NT) Ts[i] = 0.f;
-    for (int i = tid; i < NVEC * CH; i += NT) vecs[i] = 0.f;
+    // gates of this chunk, one row per lane (rows >= n: alpha 1, mu 0, eta 0)
+    float a_l = 1.f, m_l = 0.f, e_l = 0.f;
+    if (lane < n) {
+        const size_t g = tok0 + (size_t)lane * H;
+        a_l = alpha[g];
+        m_l = mu[g];
+        e_l = eta[g];
+    }
+    if (wave == 0) {
+        al[lane] = a_l;
+        mus[lane] = m_l;
+        et[lane] = e_l;
+    }
     __syncthreads();
 
-    // ---- coefficients: wave 0, lane i for the row vectors, lane j for the
-    //      Gamma column j --------------------------------------------------
+    // ---- coefficients (wave 0): one pass over the chunk rows r.  Lane j
+    //      carries the Gamma column j (rows r >= j) and lane i the prefix
+    //      product abar_i.  The gates of row r are broadcast reads from LDS
+    //      and the pass is straight-line (rows >= n are masked, not branched
+    //      over), so the reads run ahead of the arithmetic.  Since
+    //      mubar_r = mu_0 prod_{u=1..r} mu_u, column 0 gives b_i = mu_0 gamma_{i,0}
+    //      and mubar_{n-1} = mu_0 m_{n-1,0}.
+    float* Vch = Vw + ch * NVEC * CH;
     if (wave == 0) {
-        const int i = lane;
-        if (i < n) {
-            float ab = 1.f, mb = 1.f, bb = 0.f, bprev = 0.f;
-            for (int r = 0; r <= i; ++r) {
-                bprev = bb;
-                const float a = al[r];
-                ab *= a;
-                mb *= mus[r];
-                bb = a * bb + mb;
+        float g = 0.f, mj = 1.f, ab = 1.f;
+        // blocks of 16 rows: the block's gates arrive in four 16-byte reads
+        // and its rows are unrolled; rows >= n are masked inside a block
+        for (int r0 = 0; r0 < n; r0 += 16) {
+            float ga[16], gm[16];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float4 a4 = *reinterpret_cast<const float4*>(al + r0 + 4 * u);
+                const float4 m4 = *reinterpret_cast<const float4*>(mus + r0 + 4 * u);
+                ga[4 * u + 0] = a4.x; ga[4 * u + 1] = a4.y; ga[4 * u + 2] = a4.z; ga[4 * u + 3] = a4.w;
+                gm[4 * u + 0] = m4.x; gm[4 * u + 1] = m4.y; gm[4 * u + 2] = m4.z; gm[4 * u + 3] = m4.w;
             }
-            vecs[V_ABAR * CH + i] = ab;
-            vecs[V_AB1 * CH + i] = al[i] * bprev;
-            vecs[V_B * CH + i] = bb;
-            if (i == n - 1) {
-                vecs[V_SCAL * CH + 0] = ab;
-                vecs[V_SCAL * CH + 1] = bb;
-                vecs[V_SCAL * CH + 2] = mb;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int r = r0 + u;
+                const bool act = r < n;
+                const bool below = r > lane;
+                const float mj_n = below ? mj * gm[u] : 1.f;
+                const float g_n = below ? ga[u] * g + mj_n : (r == lane ? 1.f : 0.f);
+                mj = act ? mj_n : mj;
+                g = act ? g_n : g;
+                ab = (act && r <= lane) ? ab * ga[u] : ab;
+                Gam[r * LDG + lane] = act ? g_n : 0.f;
             }
         }
-        const int j = lane;
-        for (int r = 0; r < CH; ++r)
-            if (r < j || r >= n) Gam[r * LDG + j] = 0.f;
-        if (j < n) {
-            float g = 1.f, mj = 1.f;
-            Gam[j * LDG + j] = 1.f;
-            for (int r = j + 1; r < n; ++r) {
-                mj *= mus[r];
-                g = al[r] * g + mj;
-                Gam[r * LDG + j] = g;
-            }
-            vecs[V_WS * CH + j] = et[j] * g;
-            vecs[V_WM * CH + j] = et[j] * mj;
-        }
+        for (int r = (n + 15) & ~15; r < CH; ++r) Gam[r * LDG + lane] = 0.f;
+        // lane i reads b_i = mu_0 gamma_{i,0} and b_{i-1} written by lane 0
+        // of this wavefront (LDS operations of one wavefront complete in order)
+        __builtin_amdgcn_wave_barrier();
+        const float mu0 = mus[0];
+        const bool live = lane < n;
+        const float bi = live ? mu0 * Gam[lane * LDG] : 0.f;
+        const float bprev = live && lane >= 1 ? mu0 * Gam[(lane - 1) * LDG] : 0.f;
+        Vch[V_ABAR * CH + lane] = live ? ab : 0.f;
+        Vch[V_AB1 * CH + lane] = live ? a_l * bprev : 0.f;
+        Vch[V_B * CH + lane] = bi;
+        Vch[V_WS * CH + lane] = live ? e_l * g : 0.f;
+        Vch[V_WM * CH + lane] = live ? e_l * mj : 0.f;
+        // [abar_{n-1}, b_{n-1}, mubar_{n-1}] from lanes n-1 and 0
+        const float ab_last = lane_bcast(ab, n - 1);
+        const float mj0 = lane_bcast(mj, 0);
+        const float b_last = lane_bcast(bi, n - 1);
+        float scal = 0.f;
+        if (lane == 0) scal = ab_last;
+        if (lane == 1) scal = b_last;
+        if (lane == 2) scal = mu0 * mj0;
+        Vch[V_SCAL * CH + lane] = scal;
     }
 
-    // ---- G = K K^T and P = Q K^T, lower block triangle only: wave w owns
-    //      row tile w ---------------------------------------------------------
+    // ---- G = K K^T and P = Q K^T on the lower block triangle: wave w owns
+    //      row tile w
     f32x4 accG[4], accP[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) accG[ct] = accP[ct] = zero4();
@@ -207,9 +301,10 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
             }
         }
     }
-    __syncthreads();   // Gamma and the coefficient vectors are ready
+    __syncthreads();   // Gamma ready; K and Q no longer read
 
-    // ---- L = I + (P Khat^T) o Gamma^-, A = (Q Khat^T) o Gamma --------------
+    // ---- L = I + (P Khat^T) o Gamma^- into LDS (over K/Q, no longer read)
+    //      and A = (Q Khat^T) o Gamma straight to the workspace
     E* Ach = Aw + ch * CH * CH;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
@@ -217,11 +312,13 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
         for (int r = 0; r < 4; ++r) {
             const int i = 16 * wave + 4 * lg + r;
             const int j = 16 * ct + l16;
-            float lv = (i == j) ? 1.f : 0.f;
-            float av = 0.f;
-            if (ct <= wave) {
-                if (j < i) lv = al[i] * accG[ct][r] * et[j] * Gam[(i - 1) * LDG + j];
-                if (j <= i) av = accP[ct][r] * et[j] * Gam[i * LDG + j];
+            float lv = 0.f, av = 0.f;
+            if (ct <= wave) {   // wave-uniform; the per-lane masks are selects
+                const float gm1 = Gam[max(i - 1, 0) * LDG + j];
+                const float g0 = Gam[i * LDG + j];
+                const float ej = et[j];
+                lv = j < i ? al[i] * accG[ct][r] * ej * gm1 : (i == j ? 1.f : 0.f);
+                av = j <= i ? accP[ct][r] * ej * g0 : 0.f;
             }
             Ls[i * LDG + j] = lv;
             Ach[i * CH + j] = to_elem<E>(av);
@@ -229,147 +326,197 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
     }
     __syncthreads();
 
-    // ---- T = L^{-1}: diagonal 16x16 blocks by forward substitution (one lane
-    //      per column), then block rows I = 1..3:
-    //      T_IJ = -T_II sum_{K<I} L_IK T_KJ --------------------------------
-    if (l16 == lane) {
+    // ---- T = L^{-1}.  Diagonal 16x16 blocks by column-oriented forward
+    //      substitution (wave w, lanes 0..15 = columns of block w): once t_j
+    //      is final, every later row subtracts its multiple, so the updates
+    //      of one step are independent ...
+    if (lane < 16) {
         const int base = 16 * wave;
         float t[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float acc = (i == lane) ? 1.f : 0.f;
+        for (int i = 0; i < 16; ++i) t[i] = (i == lane) ? 1.f : 0.f;
 #pragma unroll
-            for (int j = 0; j < i; ++j) acc -= Ls[(base + i) * LDG + base + j] * t[j];
-            t[i] = acc;
+        for (int j = 0; j < 15; ++j) {
+#pragma unroll
+            for (int i = j + 1; i < 16; ++i) t[i] -= Ls[(base + i) * LDG + base + j] * t[j];
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) Ts[(base + i) * LDG + base + lane] = t[i];
     }
     __syncthreads();
+    // ... then block rows I = 1..3: T_IJ = -T_II X_IJ, X_IJ = sum_{K<I} L_IK T_KJ,
+    //      on fp32 MFMA, block column J = wave.  X stays in accumulators and is
+    //      the B operand of the second product in k-permuted order.  Only
+    //      blocks on or below the diagonal are ever read.
     for (int I = 1; I < 4; ++I) {
-        const int w = 16 * I;
-        for (int e = tid; e < 16 * w; e += NT) {
-            const int r = e / w;
-            const int cc = e % w;
-            float acc = 0.f;
-            for (int j = cc; j < w; ++j) acc += Ls[(w + r) * LDG + j] * Ts[j * LDG + cc];
-            Xs[r * LDG + cc] = acc;
-        }
-        __syncthreads();
-        for (int e = tid; e < 16 * w; e += NT) {
-            const int r = e / w;
-            const int cc = e % w;
-            float acc = 0.f;
-            for (int s = 0; s <= r; ++s) acc += Ts[(w + r) * LDG + w + s] * Xs[s * LDG + cc];
-            Ts[(w + r) * LDG + cc] = -acc;
+        const int J = wave;
+        if (J < I) {
+            f32x4 x0 = zero4(), x1 = zero4();
+            for (int kk = 16 * J; kk < 16 * I; kk += 2 * MF::KSTEP) {
+                x0 = MF::mma(Ls[(16 * I + l16) * LDG + kk + lg], Ts[(kk + lg) * LDG + 16 * J + l16], x0);
+                x1 = MF::mma(Ls[(16 * I + l16) * LDG + kk + 4 + lg],
+                             Ts[(kk + 4 + lg) * LDG + 16 * J + l16], x1);
+            }
+            const f32x4 x = x0 + x1;
+            f32x4 t = zero4();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                // k = 4 lg + s: this lane's accumulator element s
+                const float a = Ts[(16 * I + l16) * LDG + 16 * I + 4 * lg + s];
+                t = MF::mma(a, -x[s], t);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Ts[(16 * I + 4 * lg + r) * LDG + 16 * J + l16] = t[r];
         }
         __syncthreads();
     }
 
+    // ---- write T (zero above the block diagonal) in the I/O type
     E* Tch = Tw + ch * CH * CH;
-    for (int e = tid; e < CH * CH; e += NT) Tch[e] = to_elem<E>(Ts[(e / CH) * LDG + (e % CH)]);
-    float* Vch = Vw + ch * NVEC * CH;
-    for (int e = tid; e < NVEC * CH; e += NT) Vch[e] = vecs[e];
+    constexpr int EPV = 16 / sizeof(E);
+    for (int idx = tid; idx < CH * CH / EPV; idx += NT) {
+        const int row = (idx * EPV) / CH;
+        const int col = (idx * EPV) % CH;
+        const bool upper = (col >> 4) > (row >> 4);
+        alignas(16) E tv[EPV];
+#pragma unroll
+        for (int j = 0; j < EPV; ++j) {
+            const float x = Ts[row * LDG + col + j];   // stale above the diagonal: masked
+            tv[j] = to_elem<E>(upper ? 0.f : x);
+        }
+        *reinterpret_cast<uint4*>(Tch + row * CH + col) = *reinterpret_cast<const uint4*>(tv);
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Sequential scan over chunks, one (batch, head, Dv tile) per workgroup
+// Sequential scan over chunks.  One workgroup per (batch, head, 64 value
+// columns); wavefront w owns 16 of those columns of S and M for the whole
+// sequence.  Everything a wavefront computes for its columns (K S, Q S, R,
+// Vt, O, the new S and M) depends only on its own columns and on the
+// chunk's shared operands (K, Q, V, T, A, coefficients) in LDS, so the four
+// wavefronts never wait for each other inside a chunk: they synchronise only
+// around the staging of the next chunk, whose global loads are issued before
+// the current chunk's arithmetic (bf16) so their latency is hidden.
 // ---------------------------------------------------------------------------
-template <typename E, int DK, int DV, int TV>
+template <typename E, int DK, int DV>
+struct ScanSmem {
+    static constexpr int TV = 64;
+    static constexpr int LDK = DK + Mma<E>::PAD;
+    static constexpr int LDV = TV + Mma<E>::PAD;
+    static constexpr int LDC = CH + Mma<E>::PAD;
+    static constexpr bool KT_COPY = sizeof(E) == 2;
+};
+
+template <typename E, int DK, int DV>
 __global__ __launch_bounds__(NT) void chunk_scan_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ Tw, const E* __restrict__ Aw, const float* __restrict__ Vw,
     const float* S0, const float* M0, E* __restrict__ O, float* ST, float* MT, int T, int H,
-    int NC)
+    int NC, int xcd_groups)
 {
     using MM = Mma<E>;
-    constexpr int LDK = DK + MM::PAD;   // rows of K, Q, S^T, M^T (k = d contiguous)
-    constexpr int LDV = TV + MM::PAD;   // rows of the V tile
-    constexpr int LDC = CH + MM::PAD;   // rows of T, A, R^T, Vt^T (k = chunk row contiguous)
-    constexpr int CT = TV / 16;         // column tiles of the Dv tile
-    constexpr int NSTATE = (DK / 16) * CT;
-    static_assert(NSTATE % 4 == 0, "state tiles must split over 4 wavefronts");
-    constexpr int NSW = NSTATE / 4;     // state tiles per wavefront
+    using SM = ScanSmem<E, DK, DV>;
+    constexpr int TV = SM::TV;
     constexpr int NTILE = DV / TV;
+    constexpr int LDK = SM::LDK;
+    constexpr int LDV = SM::LDV;
+    constexpr int LDC = SM::LDC;
+    constexpr bool KT_COPY = SM::KT_COPY;
+    constexpr bool PREFETCH = sizeof(E) == 2;
+    constexpr int RT = DK / 16;            // row tiles of the state
+    constexpr int SK = DK / MM::PERM_K;    // k-steps over d
+    constexpr int SC = CH / MM::PERM_K;    // k-steps over the chunk rows
+    static_assert(DV % TV == 0, "value tile");
 
     __shared__ __align__(16) E Ks[CH * LDK];
     __shared__ __align__(16) E Qs[CH * LDK];
+    __shared__ __align__(16) E KTs[KT_COPY ? DK * LDC : 8];
     __shared__ __align__(16) E Vs[CH * LDV];
     __shared__ __align__(16) E Ts[CH * LDC];
     __shared__ __align__(16) E As[CH * LDC];
-    __shared__ __align__(16) E SbT[TV * LDK];
-    __shared__ __align__(16) E MbT[TV * LDK];
-    __shared__ __align__(16) E RT[TV * LDC];
-    __shared__ __align__(16) E VtT[TV * LDC];
     __shared__ __align__(16) float vecs[6 * CH];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int lane = tid & 63;
     const int l16 = lane & 15;
     const int lg = lane >> 4;
 
-    const int tile = (int)(blockIdx.x % NTILE);
-    const int bh = (int)(blockIdx.x / NTILE);     // b * H + h
+    // Workgroups are dispatched round-robin over the 8 XCDs.  When the grid
+    // is a multiple of 8, renumber so that consecutive logical ids (the value
+    // tiles of one head, which read the same K, Q, T and A) run on one XCD
+    // and share its L2.
+    unsigned bid = blockIdx.x;
+    if (xcd_groups > 0) bid = (bid % 8u) * (unsigned)xcd_groups + bid / 8u;
+    const int tile = (int)(bid % NTILE);
+    const int bh = (int)(bid / NTILE);     // b * H + h
     const int h = bh % H;
     const int b = bh / H;
-    const int col0 = tile * TV;
+    const int wcol = tile * TV + 16 * wave;   // first value column of this wavefront
 
-    // the state tile, fp32, in accumulator layout: state tile sg = wave + 4 s
-    // covers rows 16 (sg / CT) .. and columns col0 + 16 (sg % CT) ..
-    f32x4 Sa[NSW], Ma[NSW];
+    // the state columns of this wavefront: rows 16 rt + 4 lg + r, column wcol + l16
+    f32x4 Sa[RT], Ma[RT];
     const size_t sbase = (size_t)bh * DK * DV;
+    auto load_state = [&](f32x4* X, const float* src) {
 #pragma unroll
-    for (int s = 0; s < NSW; ++s) {
-        const int sg = wave + 4 * s;
-        const int ri = sg / CT;
-        const int ci = sg % CT;
+        for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const size_t off = sbase + (size_t)(16 * ri + 4 * lg + r) * DV + col0 + 16 * ci + l16;
-            Sa[s][r] = S0 ? S0[off] : 0.f;
-            Ma[s][r] = M0 ? M0[off] : 0.f;
+            for (int r = 0; r < 4; ++r)
+                X[rt][r] = src ? src[sbase + (size_t)(16 * rt + 4 * lg + r) * DV + wcol + l16] : 0.f;
         }
-    }
+    };
+    if (S0) load_state(Sa, S0); else load_state(Sa, nullptr);
+    if (M0) load_state(Ma, M0); else load_state(Ma, nullptr);
+
+    RowTile<E, DK> pk, pq;
+    RowTile<E, TV> pv;
+    RowTile<E, CH> pt, pa;
+    float4 pvec = {0.f, 0.f, 0.f, 0.f};
+    auto fetch = [&](int c) {
+        const int t0 = c * CH;
+        const int n = min(CH, T - t0);
+        const size_t tok0 = ((size_t)b * T + t0) * H + h;
+        const size_t chn = (size_t)bh * NC + c;
+        pk.load(k + tok0 * DK, (unsigned)(H * DK), n, tid);
+        pq.load(q + tok0 * DK, (unsigned)(H * DK), n, tid);
+        pv.load(v + tok0 * DV + tile * TV, (unsigned)(H * DV), n, tid);
+        pt.load(Tw + chn * CH * CH, CH, CH, tid);
+        pa.load(Aw + chn * CH * CH, CH, CH, tid);
+        if (tid < 6 * CH / 4) pvec = reinterpret_cast<const float4*>(Vw + chn * NVEC * CH)[tid];
+    };
+    if (PREFETCH) fetch(0);
 
     for (int c = 0; c < NC; ++c) {
         const int t0 = c * CH;
         const int n = min(CH, T - t0);
-        const size_t ch = (size_t)bh * NC + c;
         const size_t tok0 = ((size_t)b * T + t0) * H + h;
 
-        // (1) operand copy of the entry state, transposed: SbT[t][d]
-#pragma unroll
-        for (int s = 0; s < NSW; ++s) {
-            const int sg = wave + 4 * s;
-            const int ri = sg / CT;
-            const int ci = sg % CT;
-            const int off = (16 * ci + l16) * LDK + 16 * ri + 4 * lg;
-            store4<E>(SbT + off, Sa[s][0], Sa[s][1], Sa[s][2], Sa[s][3]);
-            store4<E>(MbT + off, Ma[s][0], Ma[s][1], Ma[s][2], Ma[s][3]);
-        }
-        // (2) this chunk's K, Q, V tile, T, A and coefficients
-        stage_rows<E, DK, LDK>(Ks, k, tok0 * DK, (size_t)H * DK, n, tid);
-        stage_rows<E, DK, LDK>(Qs, q, tok0 * DK, (size_t)H * DK, n, tid);
-        stage_rows<E, TV, LDV>(Vs, v, tok0 * DV + col0, (size_t)H * DV, n, tid);
-        stage_rows<E, CH, LDC>(Ts, Tw + ch * CH * CH, 0, CH, CH, tid);
-        stage_rows<E, CH, LDC>(As, Aw + ch * CH * CH, 0, CH, CH, tid);
-        for (int e = tid; e < 6 * CH; e += NT) vecs[e] = Vw[ch * NVEC * CH + e];
+        if (!PREFETCH) fetch(c);
+        __syncthreads();   // the previous chunk's LDS operands are no longer read
+        pk.template store<LDK>(Ks, tid);
+        if (KT_COPY) pk.template store_transposed<LDC>(KTs, tid);
+        pq.template store<LDK>(Qs, tid);
+        pv.template store<LDV>(Vs, tid);
+        pt.template store<LDC>(Ts, tid);
+        pa.template store<LDC>(As, tid);
+        if (tid < 6 * CH / 4) reinterpret_cast<float4*>(vecs)[tid] = pvec;
         __syncthreads();
+        if (PREFETCH && c + 1 < NC) fetch(c + 1);
 
-        // (3) X = K [S0 | M0] and Y = Q [S0 | M0] for chunk rows 16 wave ..
-        f32x4 xs[CT], xm[CT], ys[CT], ym[CT];
+        // (1) X = K [S | M], Y = Q [S | M] for all chunk rows, this
+        //     wavefront's 16 columns; the state is the B operand straight
+        //     from its accumulators
+        f32x4 xs[4], xm[4], ys[4], ym[4];
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) xs[ct] = xm[ct] = ys[ct] = ym[ct] = zero4();
+        for (int ct = 0; ct < 4; ++ct) xs[ct] = xm[ct] = ys[ct] = ym[ct] = zero4();
 #pragma unroll
-        for (int ks = 0; ks < DK; ks += MM::KSTEP) {
-            const int kk = ks + MM::KW * lg;
-            const auto aK = MM::load(Ks + (16 * wave + l16) * LDK + kk);
-            const auto aQ = MM::load(Qs + (16 * wave + l16) * LDK + kk);
+        for (int s = 0; s < SK; ++s) {
+            const auto bS = MM::from_acc(Sa, s);
+            const auto bM = MM::from_acc(Ma, s);
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                const auto bS = MM::load(SbT + (16 * ct + l16) * LDK + kk);
-                const auto bM = MM::load(MbT + (16 * ct + l16) * LDK + kk);
+            for (int ct = 0; ct < 4; ++ct) {
+                const auto aK = MM::load_perm(Ks + (16 * ct + l16) * LDK, s, lg);
+                const auto aQ = MM::load_perm(Qs + (16 * ct + l16) * LDK, s, lg);
                 xs[ct] = MM::mma(aK, bS, xs[ct]);
                 xm[ct] = MM::mma(aK, bM, xm[ct]);
                 ys[ct] = MM::mma(aQ, bS, ys[ct]);
@@ -377,106 +524,454 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(
             }
         }
 
-        // (4) R = V - Diag(abar) K S0 + Diag(alpha b^-) K M0 -> R^T in LDS;
-        //     the entry-state part of O stays in registers
-        f32x4 oacc[CT];
+        // (2) R = V - Diag(abar) K S0 + Diag(alpha b^-) K M0 and the entry-state
+        //     part of O, element (row 16 ct + 4 lg + r, column l16)
+        f32x4 R[4], Oa[4];
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            float rv[4];
+        for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int i = 16 * wave + 4 * lg + r;
+                const int i = 16 * ct + 4 * lg + r;
                 const float ab = vecs[V_ABAR * CH + i];
-                rv[r] = to_f32(Vs[i * LDV + 16 * ct + l16]) - ab * xs[ct][r] +
-                        vecs[V_AB1 * CH + i] * xm[ct][r];
-                oacc[ct][r] = ab * ys[ct][r] - vecs[V_B * CH + i] * ym[ct][r];
-            }
-            store4<E>(RT + (16 * ct + l16) * LDC + 16 * wave + 4 * lg, rv[0], rv[1], rv[2], rv[3]);
-        }
-        __syncthreads();
-
-        // (5) Vt = T R
-        f32x4 vt[CT];
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) vt[ct] = zero4();
-#pragma unroll
-        for (int ks = 0; ks < CH; ks += MM::KSTEP) {
-            const int kk = ks + MM::KW * lg;
-            const auto aT = MM::load(Ts + (16 * wave + l16) * LDC + kk);
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                const auto bR = MM::load(RT + (16 * ct + l16) * LDC + kk);
-                vt[ct] = MM::mma(aT, bR, vt[ct]);
-            }
-        }
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-            store4<E>(VtT + (16 * ct + l16) * LDC + 16 * wave + 4 * lg, vt[ct][0], vt[ct][1],
-                      vt[ct][2], vt[ct][3]);
-        __syncthreads();
-
-        // (6) O += A Vt, rows < n to HBM
-#pragma unroll
-        for (int ks = 0; ks < CH; ks += MM::KSTEP) {
-            const int kk = ks + MM::KW * lg;
-            const auto aA = MM::load(As + (16 * wave + l16) * LDC + kk);
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                const auto bV = MM::load(VtT + (16 * ct + l16) * LDC + kk);
-                oacc[ct] = MM::mma(aA, bV, oacc[ct]);
-            }
-        }
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * wave + 4 * lg + r;
-                if (i < n)
-                    O[(tok0 + (size_t)i * H) * DV + col0 + 16 * ct + l16] = to_elem<E>(oacc[ct][r]);
+                R[ct][r] = to_f32(Vs[i * LDV + 16 * wave + l16]) - ab * xs[ct][r] +
+                           vecs[V_AB1 * CH + i] * xm[ct][r];
+                Oa[ct][r] = ab * ys[ct][r] - vecs[V_B * CH + i] * ym[ct][r];
             }
         }
 
-        // (7) carried state: S' = abar_n S0 - b_n M0 + Khat_gamma^T Vt,
-        //     M' = mubar_n M0 - Khat_m^T Vt (both from the old S0, M0)
+        // (3) Vt = T R
+        f32x4 Vt[4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) Vt[it] = zero4();
+#pragma unroll
+        for (int s = 0; s < SC; ++s) {
+            const auto bR = MM::from_acc(R, s);
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                Vt[it] = MM::mma(MM::load_perm(Ts + (16 * it + l16) * LDC, s, lg), bR, Vt[it]);
+        }
+
+        // (4) O = entry-state part + A Vt; rows < n to HBM
+#pragma unroll
+        for (int s = 0; s < SC; ++s) {
+            const auto bV = MM::from_acc(Vt, s);
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                Oa[it] = MM::mma(MM::load_perm(As + (16 * it + l16) * LDC, s, lg), bV, Oa[it]);
+        }
+        {
+            E* Ob = O + tok0 * DV + wcol + l16;
+            const unsigned ostride = (unsigned)(H * DV);
+            if (n == CH) {
+#pragma unroll
+                for (int it = 0; it < 4; ++it)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        Ob[(unsigned)(16 * it + 4 * lg + r) * ostride] = to_elem<E>(Oa[it][r]);
+            } else {
+#pragma unroll
+                for (int it = 0; it < 4; ++it)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 16 * it + 4 * lg + r;
+                        if (i < n) Ob[(unsigned)i * ostride] = to_elem<E>(Oa[it][r]);
+                    }
+            }
+        }
+
+        // (5) carried state from the old S0, M0:
+        //     S' = abar_n S0 - b_n M0 + K^T Diag(eta gamma_n) Vt
+        //     M' = mubar_n M0 - K^T Diag(eta mubar_n / mubar) Vt
         const float abn = vecs[V_SCAL * CH + 0];
         const float bn = vecs[V_SCAL * CH + 1];
         const float mbn = vecs[V_SCAL * CH + 2];
 #pragma unroll
-        for (int s = 0; s < NSW; ++s) {
-            Sa[s] = abn * Sa[s] - bn * Ma[s];
-            Ma[s] = mbn * Ma[s];
+        for (int rt = 0; rt < RT; ++rt) {
+            Sa[rt] = abn * Sa[rt] - bn * Ma[rt];
+            Ma[rt] = mbn * Ma[rt];
         }
 #pragma unroll
-        for (int ks = 0; ks < CH; ks += MM::KSTEP) {
-            const int kk = ks + MM::KW * lg;
+        for (int s = 0; s < SC; ++s) {
+            const auto bS = MM::from_acc_scaled(Vt, s, lg, vecs + V_WS * CH, 1.f);
+            const auto bM = MM::from_acc_scaled(Vt, s, lg, vecs + V_WM * CH, -1.f);
 #pragma unroll
-            for (int s = 0; s < NSW; ++s) {
-                const int sg = wave + 4 * s;
-                const int ri = sg / CT;
-                const int ci = sg % CT;
-                const E* kcol = Ks + kk * LDK + 16 * ri + l16;
-                const auto aS = MM::load_strided_scaled(kcol, LDK, vecs + V_WS * CH + kk, 1.f);
-                const auto aM = MM::load_strided_scaled(kcol, LDK, vecs + V_WM * CH + kk, -1.f);
-                const auto bV = MM::load(VtT + (16 * ci + l16) * LDC + kk);
-                Sa[s] = MM::mma(aS, bV, Sa[s]);
-                Ma[s] = MM::mma(aM, bV, Ma[s]);
+            for (int rt = 0; rt < RT; ++rt) {
+                typename MM::frag aK;
+                if constexpr (KT_COPY) {
+                    // row d = 16 rt + l16; its chunk-row groups are XOR-swizzled
+                    const int d = 16 * rt + l16;
+                    aK = MM::load_perm_xor(KTs + d * LDC, s, lg, 4 * ((d >> 3) & 7));
+                } else {
+                    aK = Ks[MM::perm_row(s, lg, 0) * LDK + 16 * rt + l16];
+                }
+                Sa[rt] = MM::mma(aK, bS, Sa[rt]);
+                Ma[rt] = MM::mma(aK, bM, Ma[rt]);
             }
         }
-        __syncthreads();   // LDS is rewritten by the next chunk
     }
 
+    auto store_state = [&](float* dst, const f32x4* X) {
 #pragma unroll
-    for (int s = 0; s < NSW; ++s) {
-        const int sg = wave + 4 * s;
-        const int ri = sg / CT;
-        const int ci = sg % CT;
+        for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const size_t off = sbase + (size_t)(16 * ri + 4 * lg + r) * DV + col0 + 16 * ci + l16;
-            if (ST) ST[off] = Sa[s][r];
-            if (MT) MT[off] = Ma[s][r];
+            for (int r = 0; r < 4; ++r)
+                dst[sbase + (size_t)(16 * rt + 4 * lg + r) * DV + wcol + l16] = X[rt][r];
+        }
+    };
+    if (ST) store_state(ST, Sa);
+    if (MT) store_state(MT, Ma);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 scan.  Same mathematics and wavefront/column ownership as
+// chunk_scan_kernel, arranged so that a wavefront issues as few instructions
+// as possible per chunk (one wavefront per SIMD is all the head-tile
+// parallelism the problem has, so issue slots are the limit):
+//
+//  * Row order.  The accumulator slot (tile t, lane group g, element j)
+//    of the state (rows d) and of the chunk-row results (rows c) represents
+//    the physical row phys_row(16 t + 4 g + j): inside each block of 32
+//    rows, slots 4g + j and 16 + 4g + j hold rows 8g + j and 8g + 4 + j.
+//    A k-step fed from accumulator tiles 2s and 2s + 1 then covers physical
+//    rows 32s + 8g + (0..7), so every A fragment is 8 contiguous elements
+//    of one row: a single 16-byte LDS read.
+//  * Operands reach LDS by direct global-to-LDS loads (no VGPR staging, no
+//    LDS write instructions), double-buffered: chunk c + 1 is in flight
+//    while chunk c is computed.  LDS rows are unpadded; their 16-byte chunks
+//    are XOR-swizzled by lds_swz(row), applied on the global side since a
+//    direct load writes 64 lanes x 16 bytes contiguously.
+//  * K^T, needed as the A operand of the state update, is built in LDS from
+//    the staged K (the only LDS-to-LDS copy).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int phys_row(int slot)
+{
+    const int q = slot & 31;
+    return (slot & ~31) + 8 * ((q & 15) >> 2) + 4 * (q >> 4) + (q & 3);
+}
+
+// One direct global-to-LDS load of 16 bytes per lane: lane l's bytes land at
+// lds_base + 16 l (lds_base is wave-uniform).
+__device__ __forceinline__ void direct_load16(const void* gsrc, void* lds_base)
+{
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
+                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// LDS layout of a 64-row bf16 tile with ROWB bytes per row (128 or 256).
+// Rows are unpadded; every 1 KB group of rows (one direct load of 64 lanes x
+// 16 bytes) is followed by PAD bytes, and inside a row the 16-byte chunks are
+// XOR-permuted by (row & 3).  A fragment read by 16 lanes of rows
+// phys_row(16 x + l16) -- rows r0 + {0..3, 8..11} or r0 + {4..7, 12..15} --
+// then touches 8 distinct 16-byte bank groups per 8 lanes, and the address of
+// step s is a per-row base plus 64 s bytes (an instruction immediate).
+template <int ROWB>
+struct TileLayout {
+    static constexpr int G = 1024 / ROWB;               // rows per 1 KB group
+    static constexpr int PAD = ROWB == 256 ? 32 : 64;   // bytes after each group
+    static constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
+    static constexpr int BYTES = CH * ROWB + (CH / G) * PAD;
+    __device__ __forceinline__ static int row_base(int row)
+    {
+        return row * ROWB + (row / G) * PAD;
+    }
+    // byte offset of 16-byte logical chunk qc of row
+    __device__ __forceinline__ static int chunk(int row, int qc)
+    {
+        return row_base(row) + 16 * (qc ^ (row & 3));
+    }
+    // Direct loads of rows [0, 64) of a row-major global tile (row stride in
+    // elements) for wavefront `wave` of 4: instruction u fills group
+    // 4 u' + wave.  full: all rows valid; otherwise rows >= n repeat n - 1.
+    __device__ __forceinline__ static void load(char* lds, const __bf16* __restrict__ g,
+                                                unsigned row_stride, int n, int wave, int lane)
+    {
+        constexpr int GROUPS = CH / G;
+        static_assert(GROUPS % 4 == 0, "groups must split over 4 wavefronts");
+#pragma unroll
+        for (int u = 0; u < GROUPS / 4; ++u) {
+            const int grp = 4 * u + wave;
+            const int row = grp * G + lane / CPR;
+            const int pc = lane % CPR;
+            const unsigned srow = (unsigned)min(row, n - 1);
+            direct_load16(g + srow * row_stride + 8 * (pc ^ (row & 3)), lds + grp * (1024 + PAD));
         }
     }
+};
+
+// ---------------------------------------------------------------------------
+// bf16 scan.  Same mathematics and wavefront/column ownership as
+// chunk_scan_kernel, arranged so that a wavefront issues as few instructions
+// per chunk as possible (one wavefront per SIMD is all the head-tile
+// parallelism a layer has, so issue slots bound the scan):
+//
+//  * Row order.  The accumulator slot (tile t, lane group g, element j) of
+//    the state (rows d) and of the chunk-row results (rows c) stands for
+//    physical row phys_row(16 t + 4 g + j): inside each block of 32 rows,
+//    slots 4g + j and 16 + 4g + j hold rows 8g + j and 8g + 4 + j.  A k-step
+//    fed from accumulator tiles 2s and 2s + 1 then covers physical rows
+//    32s + 8g + (0..7), so every A fragment is 8 contiguous elements of one
+//    row: one 16-byte LDS read.
+//  * Operands reach LDS by direct global-to-LDS loads (no VGPR staging, no
+//    LDS write instructions), double-buffered: chunk c + 1 is in flight
+//    while chunk c is computed.
+//  * K^T, the A operand of the state update, is built in LDS from the
+//    staged K; each wavefront writes whole K^T rows.
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ __launch_bounds__(NT) void chunk_scan_bf16_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ Tw, const __bf16* __restrict__ Aw, const float* __restrict__ Vw,
+    const float* S0, const float* M0, __bf16* __restrict__ O, float* ST, float* MT, int T,
+    int H, int NC, int xcd_groups)
+{
+    using E = __bf16;
+    using MM = Mma<E>;
+    using LK = TileLayout<DK * 2>;          // K, Q rows
+    using LC = TileLayout<CH * 2>;          // T, A, V-tile rows and K^T rows
+    constexpr int TV = 64;                  // value columns per workgroup
+    constexpr int NTILE = DV / TV;
+    constexpr int RT = DK / 16;             // state row tiles
+    constexpr int SK = DK / 32;             // k-steps over d
+    constexpr int SC = CH / 32;             // k-steps over the chunk rows
+    constexpr int KT_BYTES = DK * CH * 2 + (DK / LC::G) * LC::PAD;
+    constexpr int OFF_Q = LK::BYTES;
+    constexpr int OFF_V = 2 * LK::BYTES;
+    constexpr int OFF_T = OFF_V + LC::BYTES;
+    constexpr int OFF_A = OFF_T + LC::BYTES;
+    constexpr int BUF_BYTES = OFF_A + LC::BYTES;
+    static_assert(DV % TV == 0, "value tile");
+    static_assert(TV * 2 == CH * 2, "V tile rows use the chunk-row layout");
+
+    __shared__ __align__(16) char buf[2][BUF_BYTES];  // K, Q, V tile, T, A
+    __shared__ __align__(16) float vbuf[2][6 * CH];   // coefficient vectors
+    __shared__ __align__(16) char KTs[KT_BYTES];      // K^T of the current chunk
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l16 = lane & 15;
+    const int lg = lane >> 4;
+
+    unsigned bid = blockIdx.x;
+    if (xcd_groups > 0) bid = (bid % 8u) * (unsigned)xcd_groups + bid / 8u;
+    const int tile = (int)(bid % NTILE);
+    const int bh = (int)(bid / NTILE);
+    const int h = bh % H;
+    const int b = bh / H;
+    const int wl = 16 * wave + l16;            // this lane's column inside the tile
+    const int col = tile * TV + wl;            // ... inside the head
+
+    // state slots: S[phys_row(16 rt + 4 lg + r)][col]
+    f32x4 Sa[RT], Ma[RT];
+    const size_t sbase = (size_t)bh * DK * DV;
+    auto load_state = [&](f32x4* X, const float* src) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                X[rt][r] = src ? src[sbase + (size_t)phys_row(16 * rt + 4 * lg + r) * DV + col] : 0.f;
+    };
+    if (S0) load_state(Sa, S0); else load_state(Sa, nullptr);
+    if (M0) load_state(Ma, M0); else load_state(Ma, nullptr);
+
+    auto issue = [&](int c, int bi) {
+        const int t0 = c * CH;
+        const int n = min(CH, T - t0);
+        const size_t tok0 = ((size_t)b * T + t0) * H + h;
+        const size_t chn = (size_t)bh * NC + c;
+        char* B = buf[bi];
+        LK::load(B, k + tok0 * DK, (unsigned)(H * DK), n, wave, lane);
+        LK::load(B + OFF_Q, q + tok0 * DK, (unsigned)(H * DK), n, wave, lane);
+        LC::load(B + OFF_V, v + tok0 * DV + tile * TV, (unsigned)(H * DV), n, wave, lane);
+        LC::load(B + OFF_T, Tw + chn * CH * CH, CH, CH, wave, lane);
+        LC::load(B + OFF_A, Aw + chn * CH * CH, CH, CH, wave, lane);
+        // coefficient vectors: 6 x 64 floats = 96 chunks, plain layout
+        if (wave < 2 && (wave == 0 || lane < 32))
+            direct_load16(Vw + chn * NVEC * CH + 4 * (64 * wave + lane), vbuf[bi] + 256 * wave);
+    };
+    issue(0, 0);
+
+    // per-lane fragment row bases (bytes), the same every chunk
+    int kq_base[4], c_base[4], kt_base[RT];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        const int r = phys_row(16 * x + l16);
+        kq_base[x] = LK::chunk(r, lg);
+        c_base[x] = LC::chunk(r, lg);
+    }
+#pragma unroll
+    for (int x = 0; x < RT; ++x) kt_base[x] = LC::chunk(phys_row(16 * x + l16), lg);
+
+    for (int c = 0; c < NC; ++c) {
+        const int cur = c & 1;
+        const int t0 = c * CH;
+        const int n = min(CH, T - t0);
+        const size_t tok0 = ((size_t)b * T + t0) * H + h;
+        const char* Kb = buf[cur];
+        const char* Qb = Kb + OFF_Q;
+        const char* Vb = Kb + OFF_V;
+        const char* Tb = Kb + OFF_T;
+        const char* Ab = Kb + OFF_A;
+        const float* vec = vbuf[cur];
+
+        // this wavefront's direct loads for chunk c have landed; after the
+        // barrier everyone's have, and nobody still reads the other buffer
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (c + 1 < NC) issue(c + 1, cur ^ 1);
+
+        // K^T[d][c] from K[c][d]: lane = chunk row c, wavefront w takes the
+        // 16-byte chunks qd = w, w + 4, ...; each write instruction fills one
+        // K^T row (64 lanes x 2 bytes)
+#pragma unroll
+        for (int u = 0; u < DK / 32; ++u) {
+            const int qd = 4 * u + wave;
+            const bf16x8 x = *reinterpret_cast<const bf16x8*>(Kb + LK::chunk(lane, qd));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int d = 8 * qd + j;
+                *reinterpret_cast<E*>(KTs + LC::chunk(d, lane >> 3) + 2 * (lane & 7)) = x[j];
+            }
+        }
+        __syncthreads();
+
+        // (1) X = K [S | M]: the critical path first (the state update below
+        //     needs Vt, which needs R, which needs X)
+        f32x4 R[4];
+        {
+            f32x4 xs[4], xm[4];
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) xs[ct] = xm[ct] = zero4();
+#pragma unroll
+            for (int s = 0; s < SK; ++s) {
+                const auto bS = MM::from_acc(Sa, s);
+                const auto bM = MM::from_acc(Ma, s);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    const auto aK = *reinterpret_cast<const bf16x8*>(Kb + kq_base[ct] + 64 * s);
+                    xs[ct] = MM::mma(aK, bS, xs[ct]);
+                    xm[ct] = MM::mma(aK, bM, xm[ct]);
+                }
+            }
+            // (2) R = V - Diag(abar) K S0 + Diag(alpha b^-) K M0; slot (ct, lg, r)
+            //     is chunk row phys_row(16 ct + 4 lg + r), four consecutive rows
+            //     per (ct, lg)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                const int p0 = phys_row(16 * ct + 4 * lg);
+                const f32x4 ab = *reinterpret_cast<const f32x4*>(vec + V_ABAR * CH + p0);
+                const f32x4 ab1 = *reinterpret_cast<const f32x4*>(vec + V_AB1 * CH + p0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int p = p0 + r;
+                    const float vv = static_cast<float>(*reinterpret_cast<const E*>(
+                        Vb + LC::chunk(p, wl >> 3) + 2 * (wl & 7)));
+                    R[ct][r] = vv - ab[r] * xs[ct][r] + ab1[r] * xm[ct][r];
+                }
+            }
+        }
+
+        // (3) Vt = T R
+        f32x4 Vt[4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) Vt[it] = zero4();
+#pragma unroll
+        for (int s = 0; s < SC; ++s) {
+            const auto bR = MM::from_acc(R, s);
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                Vt[it] = MM::mma(*reinterpret_cast<const bf16x8*>(Tb + c_base[it] + 64 * s), bR,
+                                 Vt[it]);
+        }
+
+        // (4) O = Diag(abar) Q S0 - Diag(b) Q M0 + A Vt (off the critical path,
+        //     still from the entry state); rows < n to HBM
+        f32x4 Oa[4];
+        {
+            f32x4 ys[4], ym[4];
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) ys[ct] = ym[ct] = zero4();
+#pragma unroll
+            for (int s = 0; s < SK; ++s) {
+                const auto bS = MM::from_acc(Sa, s);
+                const auto bM = MM::from_acc(Ma, s);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    const auto aQ = *reinterpret_cast<const bf16x8*>(Qb + kq_base[ct] + 64 * s);
+                    ys[ct] = MM::mma(aQ, bS, ys[ct]);
+                    ym[ct] = MM::mma(aQ, bM, ym[ct]);
+                }
+            }
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                const int p0 = phys_row(16 * ct + 4 * lg);
+                const f32x4 ab = *reinterpret_cast<const f32x4*>(vec + V_ABAR * CH + p0);
+                const f32x4 bb = *reinterpret_cast<const f32x4*>(vec + V_B * CH + p0);
+                Oa[ct] = ab * ys[ct] - bb * ym[ct];
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < SC; ++s) {
+            const auto bV = MM::from_acc(Vt, s);
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                Oa[it] = MM::mma(*reinterpret_cast<const bf16x8*>(Ab + c_base[it] + 64 * s), bV,
+                                 Oa[it]);
+        }
+        {
+            E* Ob = O + tok0 * DV + col;
+            const unsigned ostride = (unsigned)(H * DV);
+            if (n == CH) {
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int p0 = phys_row(16 * it + 4 * lg);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        Ob[(unsigned)(p0 + r) * ostride] = static_cast<E>(Oa[it][r]);
+                }
+            } else {
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int p0 = phys_row(16 * it + 4 * lg);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (p0 + r < n) Ob[(unsigned)(p0 + r) * ostride] = static_cast<E>(Oa[it][r]);
+                }
+            }
+        }
+
+        // (5) S' = abar_n S0 - b_n M0 + K^T Diag(eta gamma_n) Vt,
+        //     M' = mubar_n M0 - K^T Diag(eta mubar_n / mubar) Vt
+        const float abn = vec[V_SCAL * CH + 0];
+        const float bn = vec[V_SCAL * CH + 1];
+        const float mbn = vec[V_SCAL * CH + 2];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            Sa[rt] = abn * Sa[rt] - bn * Ma[rt];
+            Ma[rt] = mbn * Ma[rt];
+        }
+#pragma unroll
+        for (int s = 0; s < SC; ++s) {
+            const auto bS = MM::from_acc_scaled8(Vt, s, vec + V_WS * CH + 32 * s + 8 * lg, 1.f);
+            const auto bM = MM::from_acc_scaled8(Vt, s, vec + V_WM * CH + 32 * s + 8 * lg, -1.f);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const auto aK = *reinterpret_cast<const bf16x8*>(KTs + kt_base[rt] + 64 * s);
+                Sa[rt] = MM::mma(aK, bS, Sa[rt]);
+                Ma[rt] = MM::mma(aK, bM, Ma[rt]);
+            }
+        }
+    }
+
+    auto store_state = [&](float* dst, const f32x4* X) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dst[sbase + (size_t)phys_row(16 * rt + 4 * lg + r) * DV + col] = X[rt][r];
+    };
+    if (ST) store_state(ST, Sa);
+    if (MT) store_state(MT, Ma);
 }
 
 // T = 0: the final state is the initial state (zero when absent)
@@ -504,7 +999,7 @@ static hipError_t launch_prepare_t(const void* q, const void* k, const float* al
     return hipGetLastError();
 }
 
-template <typename E, int DK, int DV, int TV>
+template <typename E, int DK, int DV>
 static hipError_t launch_scan_t(const void* q, const void* k, const void* v, const float* S0,
                                 const float* M0, void* O, float* ST, float* MT, int B, int T,
                                 int H, const void* workspace, hipStream_t stream)
@@ -512,11 +1007,19 @@ static hipError_t launch_scan_t(const void* q, const void* k, const void* v, con
     const int NC = (T + CH - 1) / CH;
     const size_t nchunks = (size_t)B * H * NC;
     Workspace<E> ws = ws_carve<E>(const_cast<void*>(workspace), nchunks);
-    const size_t nblk = (size_t)B * H * (DV / TV);
-    hipLaunchKernelGGL((chunk_scan_kernel<E, DK, DV, TV>), dim3((unsigned)nblk), dim3(NT), 0,
-                       stream, static_cast<const E*>(q), static_cast<const E*>(k),
-                       static_cast<const E*>(v), ws.T, ws.A, ws.vec, S0, M0, static_cast<E*>(O),
-                       ST, MT, T, H, NC);
+    const size_t nblk = (size_t)B * H * (DV / ScanSmem<E, DK, DV>::TV);
+    const int xcd_groups = nblk % 8 == 0 ? (int)(nblk / 8) : 0;
+    if constexpr (sizeof(E) == 2) {
+        hipLaunchKernelGGL((chunk_scan_bf16_kernel<DK, DV>), dim3((unsigned)nblk), dim3(NT), 0,
+                           stream, static_cast<const E*>(q), static_cast<const E*>(k),
+                           static_cast<const E*>(v), ws.T, ws.A, ws.vec, S0, M0,
+                           static_cast<E*>(O), ST, MT, T, H, NC, xcd_groups);
+    } else {
+        hipLaunchKernelGGL((chunk_scan_kernel<E, DK, DV>), dim3((unsigned)nblk), dim3(NT), 0,
+                           stream, static_cast<const E*>(q), static_cast<const E*>(k),
+                           static_cast<const E*>(v), ws.T, ws.A, ws.vec, S0, M0,
+                           static_cast<E*>(O), ST, MT, T, H, NC, xcd_groups);
+    }
     return hipGetLastError();
 }
 
@@ -563,16 +1066,15 @@ hipError_t launch_chunk_scan(const void* q, const void* k, const void* v, const 
         }
         return hipSuccess;
     }
-#define MDN_SCAN(E, DK, DV, TV)                                                                  \
+#define MDN_SCAN(E, DK, DV)                                                                      \
     if (Dk == DK && Dv == DV)                                                                    \
-        return launch_scan_t<E, DK, DV, TV>(q, k, v, S0, M0, O, ST, MT, B, T, H, workspace,     \
-                                            stream);
+        return launch_scan_t<E, DK, DV>(q, k, v, S0, M0, O, ST, MT, B, T, H, workspace, stream);
     if (bf16) {
-        MDN_SCAN(__bf16, 64, 64, 64) MDN_SCAN(__bf16, 64, 128, 64)
-        MDN_SCAN(__bf16, 128, 64, 64) MDN_SCAN(__bf16, 128, 128, 64)
+        MDN_SCAN(__bf16, 64, 64) MDN_SCAN(__bf16, 64, 128)
+        MDN_SCAN(__bf16, 128, 64) MDN_SCAN(__bf16, 128, 128)
     } else {
-        MDN_SCAN(float, 64, 64, 32) MDN_SCAN(float, 64, 128, 32)
-        MDN_SCAN(float, 128, 64, 16) MDN_SCAN(float, 128, 128, 16)
+        MDN_SCAN(float, 64, 64) MDN_SCAN(float, 64, 128)
+        MDN_SCAN(float, 128, 64) MDN_SCAN(float, 128, 128)
     }
 #undef MDN_SCAN
     return hipErrorInvalidValue;

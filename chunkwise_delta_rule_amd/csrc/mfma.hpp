@@ -14,6 +14,17 @@
 // use the same (lane, j) -> k assignment, so the product does not depend on
 // how the hardware orders k inside one instruction.
 // The accumulator holds D[i0 + 4*(l/16) + r][n0 + l%16] in element r (0..3).
+//
+// Accumulator-fed B operands ("k-permuted steps").  When the B operand of a
+// product is itself the result of earlier 16x16 products still held in
+// accumulators (B[k][n] in tiles of 16 k-rows), the k index of each step is
+// taken in the order the accumulators already hold it:
+//   bf16 step s: lane group g = l/16 supplies k = 32s + 4g + j (j < 4) and
+//                k = 32s + 16 + 4g + (j - 4) (j >= 4): accumulator tiles 2s
+//                and 2s + 1, elements 0..3 of each;
+//   fp32 step s: k = 16 (s / 4) + 4g + (s % 4): tile s / 4, element s % 4.
+// The B fragment is then a register move (plus a bf16 rounding), and the A
+// fragment is read with the same k order (two 8-byte reads for bf16).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -53,6 +64,62 @@ struct Mma<__bf16> {
             f[j] = static_cast<__bf16>(sign * s[j] * static_cast<float>(p[j * stride]));
         return f;
     }
+    // --- k-permuted steps -------------------------------------------------
+    static constexpr int PERM_K = 32;          // k per step
+    // first k row of element j of lane group g in step s
+    __device__ __forceinline__ static int perm_row(int s, int g, int j)
+    {
+        return 32 * s + (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
+    }
+    // A fragment of step s from a k-contiguous row p
+    __device__ __forceinline__ static frag load_perm(const __bf16* p, int s, int g)
+    {
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p + 32 * s + 4 * g);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 32 * s + 16 + 4 * g);
+        return frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    // same, with the 4-element groups of the row XOR-permuted by x (a
+    // multiple of 4)
+    __device__ __forceinline__ static frag load_perm_xor(const __bf16* p, int s, int g, int x)
+    {
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p + ((32 * s + 4 * g) ^ x));
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + ((32 * s + 16 + 4 * g) ^ x));
+        return frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    // B fragment of step s from accumulator tiles acc[2s], acc[2s + 1]
+    __device__ __forceinline__ static frag from_acc(const f32x4* acc, int s)
+    {
+        const f32x4 a = acc[2 * s], b = acc[2 * s + 1];
+        return frag{static_cast<__bf16>(a[0]), static_cast<__bf16>(a[1]),
+                    static_cast<__bf16>(a[2]), static_cast<__bf16>(a[3]),
+                    static_cast<__bf16>(b[0]), static_cast<__bf16>(b[1]),
+                    static_cast<__bf16>(b[2]), static_cast<__bf16>(b[3])};
+    }
+    // same, element j scaled by w8[j] (the 8 scale factors of this lane's
+    // k rows, contiguous)
+    __device__ __forceinline__ static frag from_acc_scaled8(const f32x4* acc, int s,
+                                                            const float* w8, float sign)
+    {
+        const f32x4 a = acc[2 * s], b = acc[2 * s + 1];
+        const f32x4 wa = *reinterpret_cast<const f32x4*>(w8);
+        const f32x4 wb = *reinterpret_cast<const f32x4*>(w8 + 4);
+        return frag{static_cast<__bf16>(sign * wa[0] * a[0]), static_cast<__bf16>(sign * wa[1] * a[1]),
+                    static_cast<__bf16>(sign * wa[2] * a[2]), static_cast<__bf16>(sign * wa[3] * a[3]),
+                    static_cast<__bf16>(sign * wb[0] * b[0]), static_cast<__bf16>(sign * wb[1] * b[1]),
+                    static_cast<__bf16>(sign * wb[2] * b[2]), static_cast<__bf16>(sign * wb[3] * b[3])};
+    }
+    // same, each k row scaled by w[k] (w indexed by absolute k row)
+    __device__ __forceinline__ static frag from_acc_scaled(const f32x4* acc, int s, int g,
+                                                           const float* w, float sign)
+    {
+        const f32x4 a = acc[2 * s], b = acc[2 * s + 1];
+        const f32x4 wa = *reinterpret_cast<const f32x4*>(w + 32 * s + 4 * g);
+        const f32x4 wb = *reinterpret_cast<const f32x4*>(w + 32 * s + 16 + 4 * g);
+        return frag{static_cast<__bf16>(sign * wa[0] * a[0]), static_cast<__bf16>(sign * wa[1] * a[1]),
+                    static_cast<__bf16>(sign * wa[2] * a[2]), static_cast<__bf16>(sign * wa[3] * a[3]),
+                    static_cast<__bf16>(sign * wb[0] * b[0]), static_cast<__bf16>(sign * wb[1] * b[1]),
+                    static_cast<__bf16>(sign * wb[2] * b[2]), static_cast<__bf16>(sign * wb[3] * b[3])};
+    }
 };
 
 template <>
@@ -70,6 +137,25 @@ struct Mma<float> {
                                                                float sign)
     {
         return sign * s[0] * p[0];
+    }
+    // --- k-permuted steps -------------------------------------------------
+    static constexpr int PERM_K = 4;
+    __device__ __forceinline__ static int perm_row(int s, int g, int)
+    {
+        return 16 * (s >> 2) + 4 * g + (s & 3);
+    }
+    __device__ __forceinline__ static frag load_perm(const float* p, int s, int g)
+    {
+        return p[perm_row(s, g, 0)];
+    }
+    __device__ __forceinline__ static frag from_acc(const f32x4* acc, int s)
+    {
+        return acc[s >> 2][s & 3];
+    }
+    __device__ __forceinline__ static frag from_acc_scaled(const f32x4* acc, int s, int g,
+                                                           const float* w, float sign)
+    {
+        return sign * w[perm_row(s, g, 0)] * acc[s >> 2][s & 3];
     }
 };
 
