@@ -622,27 +622,6 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(
     if (MT) store_state(MT, Ma);
 }
 
-// ---------------------------------------------------------------------------
-// bf16 scan.  Same mathematics and wavefront/column ownership as
-// chunk_scan_kernel, arranged so that a wavefront issues as few instructions
-// as possible per chunk (one wavefront per SIMD is all the head-tile
-// parallelism the problem has, so issue slots are the limit):
-//
-//  * Row order.  The accumulator slot (tile t, lane group g, element j)
-//    of the state (rows d) and of the chunk-row results (rows c) represents
-//    the physical row phys_row(16 t + 4 g + j): inside each block of 32
-//    rows, slots 4g + j and 16 + 4g + j hold rows 8g + j and 8g + 4 + j.
-//    A k-step fed from accumulator tiles 2s and 2s + 1 then covers physical
-//    rows 32s + 8g + (0..7), so every A fragment is 8 contiguous elements
-//    of one row: a single 16-byte LDS read.
-//  * Operands reach LDS by direct global-to-LDS loads (no VGPR staging, no
-//    LDS write instructions), double-buffered: chunk c + 1 is in flight
-//    while chunk c is computed.  LDS rows are unpadded; their 16-byte chunks
-//    are XOR-swizzled by lds_swz(row), applied on the global side since a
-//    direct load writes 64 lanes x 16 bytes contiguously.
-//  * K^T, needed as the A operand of the state update, is built in LDS from
-//    the staged K (the only LDS-to-LDS copy).
-// ---------------------------------------------------------------------------
 __device__ __forceinline__ int phys_row(int slot)
 {
     const int q = slot & 31;
@@ -681,19 +660,37 @@ struct TileLayout {
     }
     // Direct loads of rows [0, 64) of a row-major global tile (row stride in
     // elements) for wavefront `wave` of 4: instruction u fills group
-    // 4 u' + wave.  full: all rows valid; otherwise rows >= n repeat n - 1.
+    // 4 u + wave.  Since a group holds a multiple of 4 rows, the swizzle of a
+    // lane's row depends on the lane only, so each lane's source offset is
+    // one constant plus a wave-uniform group offset.  Rows >= n (a partial
+    // last chunk) read row n - 1 instead.
+    __device__ __forceinline__ static unsigned lane_offset(unsigned row_stride, int lane)
+    {
+        const int r = lane / CPR;
+        return (unsigned)r * row_stride + 8u * (unsigned)((lane % CPR) ^ (r & 3));
+    }
     __device__ __forceinline__ static void load(char* lds, const __bf16* __restrict__ g,
-                                                unsigned row_stride, int n, int wave, int lane)
+                                                unsigned row_stride, unsigned lane_off, int n,
+                                                int wave, int lane)
     {
         constexpr int GROUPS = CH / G;
-        static_assert(GROUPS % 4 == 0, "groups must split over 4 wavefronts");
+        static_assert(GROUPS % 4 == 0 && G % 4 == 0, "groups must split over 4 wavefronts");
+        if (n == CH) {
 #pragma unroll
-        for (int u = 0; u < GROUPS / 4; ++u) {
-            const int grp = 4 * u + wave;
-            const int row = grp * G + lane / CPR;
-            const int pc = lane % CPR;
-            const unsigned srow = (unsigned)min(row, n - 1);
-            direct_load16(g + srow * row_stride + 8 * (pc ^ (row & 3)), lds + grp * (1024 + PAD));
+            for (int u = 0; u < GROUPS / 4; ++u) {
+                const int grp = 4 * u + wave;
+                direct_load16(g + (unsigned)(grp * G) * row_stride + lane_off,
+                              lds + grp * (1024 + PAD));
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < GROUPS / 4; ++u) {
+                const int grp = 4 * u + wave;
+                const int row = grp * G + lane / CPR;
+                const unsigned srow = (unsigned)min(row, n - 1);
+                direct_load16(g + srow * row_stride + 8 * ((lane % CPR) ^ (row & 3)),
+                              lds + grp * (1024 + PAD));
+            }
         }
     }
 };
@@ -774,22 +771,32 @@ __global__ __launch_bounds__(NT) void chunk_scan_bf16_kernel(
     if (S0) load_state(Sa, S0); else load_state(Sa, nullptr);
     if (M0) load_state(Ma, M0); else load_state(Ma, nullptr);
 
-    auto issue = [&](int c, int bi) {
-        const int t0 = c * CH;
-        const int n = min(CH, T - t0);
-        const size_t tok0 = ((size_t)b * T + t0) * H + h;
+    const unsigned kq_stride = (unsigned)(H * DK), v_stride = (unsigned)(H * DV);
+    const unsigned kq_lane = LK::lane_offset(kq_stride, lane);
+    const unsigned v_lane = LC::lane_offset(v_stride, lane);
+    const unsigned c_lane = LC::lane_offset(CH, lane);
+    // The direct loads of chunk c + 1 are issued at the top of chunk c, as
+    // soon as the other buffer is free; they land while chunk c is computed.
+    auto issue_kq = [&](int c, int bi) {
+        const int n = min(CH, T - c * CH);
+        const size_t tok0 = ((size_t)b * T + c * CH) * H + h;
+        LK::load(buf[bi], k + tok0 * DK, kq_stride, kq_lane, n, wave, lane);
+        LK::load(buf[bi] + OFF_Q, q + tok0 * DK, kq_stride, kq_lane, n, wave, lane);
+    };
+    auto issue_rest = [&](int c, int bi) {
+        const int n = min(CH, T - c * CH);
+        const size_t tok0 = ((size_t)b * T + c * CH) * H + h;
         const size_t chn = (size_t)bh * NC + c;
         char* B = buf[bi];
-        LK::load(B, k + tok0 * DK, (unsigned)(H * DK), n, wave, lane);
-        LK::load(B + OFF_Q, q + tok0 * DK, (unsigned)(H * DK), n, wave, lane);
-        LC::load(B + OFF_V, v + tok0 * DV + tile * TV, (unsigned)(H * DV), n, wave, lane);
-        LC::load(B + OFF_T, Tw + chn * CH * CH, CH, CH, wave, lane);
-        LC::load(B + OFF_A, Aw + chn * CH * CH, CH, CH, wave, lane);
+        LC::load(B + OFF_V, v + tok0 * DV + tile * TV, v_stride, v_lane, n, wave, lane);
+        LC::load(B + OFF_T, Tw + chn * CH * CH, CH, c_lane, CH, wave, lane);
+        LC::load(B + OFF_A, Aw + chn * CH * CH, CH, c_lane, CH, wave, lane);
         // coefficient vectors: 6 x 64 floats = 96 chunks, plain layout
         if (wave < 2 && (wave == 0 || lane < 32))
             direct_load16(Vw + chn * NVEC * CH + 4 * (64 * wave + lane), vbuf[bi] + 256 * wave);
     };
-    issue(0, 0);
+    issue_kq(0, 0);
+    issue_rest(0, 0);
 
     // per-lane fragment row bases (bytes), the same every chunk
     int kq_base[4], c_base[4], kt_base[RT];
@@ -818,19 +825,28 @@ __global__ __launch_bounds__(NT) void chunk_scan_bf16_kernel(
         // barrier everyone's have, and nobody still reads the other buffer
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (c + 1 < NC) issue(c + 1, cur ^ 1);
+        if (c + 1 < NC) {
+            issue_kq(c + 1, cur ^ 1);
+            issue_rest(c + 1, cur ^ 1);
+        }
 
-        // K^T[d][c] from K[c][d]: lane = chunk row c, wavefront w takes the
-        // 16-byte chunks qd = w, w + 4, ...; each write instruction fills one
-        // K^T row (64 lanes x 2 bytes)
+        // K^T[d][c] from K[c][d]: thread t takes chunk rows 4 (t % 16) .. + 3
+        // and d = 8 (t / 16) .. + 7: four 16-byte reads, then eight 8-byte
+        // writes (4 consecutive c of one K^T row each)
+        {
+            const int i4 = 4 * (tid & 15);
+            const int qd = tid >> 4;
+            if (qd < DK / 8) {
+                bf16x8 x[4];
 #pragma unroll
-        for (int u = 0; u < DK / 32; ++u) {
-            const int qd = 4 * u + wave;
-            const bf16x8 x = *reinterpret_cast<const bf16x8*>(Kb + LK::chunk(lane, qd));
+                for (int r = 0; r < 4; ++r)
+                    x[r] = *reinterpret_cast<const bf16x8*>(Kb + LK::chunk(i4 + r, qd));
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int d = 8 * qd + j;
-                *reinterpret_cast<E*>(KTs + LC::chunk(d, lane >> 3) + 2 * (lane & 7)) = x[j];
+                for (int j = 0; j < 8; ++j) {
+                    const int d = 8 * qd + j;
+                    const bf16x4 w4 = {x[0][j], x[1][j], x[2][j], x[3][j]};
+                    *reinterpret_cast<bf16x4*>(KTs + LC::chunk(d, i4 >> 3) + 2 * (i4 & 7)) = w4;
+                }
             }
         }
         __syncthreads();
@@ -842,15 +858,20 @@ __global__ __launch_bounds__(NT) void chunk_scan_bf16_kernel(
             f32x4 xs[4], xm[4];
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) xs[ct] = xm[ct] = zero4();
+            bf16x8 aK[SK][4];
+#pragma unroll
+            for (int s = 0; s < SK; ++s)
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct)
+                    aK[s][ct] = *reinterpret_cast<const bf16x8*>(Kb + kq_base[ct] + 64 * s);
 #pragma unroll
             for (int s = 0; s < SK; ++s) {
                 const auto bS = MM::from_acc(Sa, s);
                 const auto bM = MM::from_acc(Ma, s);
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
-                    const auto aK = *reinterpret_cast<const bf16x8*>(Kb + kq_base[ct] + 64 * s);
-                    xs[ct] = MM::mma(aK, bS, xs[ct]);
-                    xm[ct] = MM::mma(aK, bM, xm[ct]);
+                    xs[ct] = MM::mma(aK[s][ct], bS, xs[ct]);
+                    xm[ct] = MM::mma(aK[s][ct], bM, xm[ct]);
                 }
             }
             // (2) R = V - Diag(abar) K S0 + Diag(alpha b^-) K M0; slot (ct, lg, r)
@@ -891,15 +912,20 @@ __global__ __launch_bounds__(NT) void chunk_scan_bf16_kernel(
             f32x4 ys[4], ym[4];
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) ys[ct] = ym[ct] = zero4();
+            bf16x8 aQ[SK][4];
+#pragma unroll
+            for (int s = 0; s < SK; ++s)
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct)
+                    aQ[s][ct] = *reinterpret_cast<const bf16x8*>(Qb + kq_base[ct] + 64 * s);
 #pragma unroll
             for (int s = 0; s < SK; ++s) {
                 const auto bS = MM::from_acc(Sa, s);
                 const auto bM = MM::from_acc(Ma, s);
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
-                    const auto aQ = *reinterpret_cast<const bf16x8*>(Qb + kq_base[ct] + 64 * s);
-                    ys[ct] = MM::mma(aQ, bS, ys[ct]);
-                    ym[ct] = MM::mma(aQ, bM, ym[ct]);
+                    ys[ct] = MM::mma(aQ[s][ct], bS, ys[ct]);
+                    ym[ct] = MM::mma(aQ[s][ct], bM, ym[ct]);
                 }
             }
 #pragma unroll
