@@ -8,9 +8,13 @@ T=4096, d_k=d_v=128, chunk 64, bf16 q/k/v with fp32 gates and state, inputs
 resident in HBM.  `value` is tokens/s = B*T per step / time per step.
 
 The same JSON line carries:
-  roofline      the dominant kernel's algorithmic FLOP rate against the bf16
-                MFMA peak, timed with HIP events on the launch stream;
-  kernels       every kernel's mean time over the timed steps;
+  roofline      the dominant kernel (the longest of the two phases) against the roof
+                its algorithmic work reaches last: bytes it must move vs the HBM peak,
+                or FLOP vs the bf16 MFMA peak; timed with HIP events on the launch
+                stream; `traffic` is its counter-measured HBM bytes per launch (null
+                once its sources differ from the profiled ones);
+  kernels       the same record for every kernel of the step;
+  forward       the whole step against both roofs;
   decode        the recurrent decode step at 256 sequences x 16 heads, d 128
                 (GB/s of algorithmic state + token traffic);
   cpu_baseline  the fp64 oracle timed on this host's cores.
@@ -38,7 +42,68 @@ FLOP_SCAN = 12 * D * D + 4 * C * D       # K[S|M], Q[S|M], K^T[Vt], T R, A Vt
 FLOP_PREP = 4 * C * D                    # K K^T, Q K^T
 FLOP_FWD = FLOP_SCAN + FLOP_PREP         # 12 d^2 + 8 C d
 BYTES_FWD = 3 * D * 2 + D * 2 + 3 * 4    # q, k, v, O (bf16) + three gates (fp32)
+# per kernel, per token and head: what each phase must read and write once
+BYTES_TA = 2 * C * C * 2 // C            # T and A, two C x C bf16 matrices per C tokens
+BYTES_VEC = 6 * 4                        # six coefficient rows (fp32) the scan reads
+BYTES_SCAN = 3 * D * 2 + D * 2 + BYTES_TA + BYTES_VEC     # + final S, M per (b, h)
+BYTES_PREP = 2 * D * 2 + 3 * 4 + BYTES_TA + BYTES_VEC
+STATE_BYTES_HEAD = 2 * D * D * 4         # S_T and M_T written once per (b, h)
 DEC_BYTES_HEAD = 4 * D * D * 4 + 3 * D * 2 + D * 2 + 3 * 4   # S, M in+out; q k v o; gates
+
+# HBM traffic per launch from rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, KiB per dispatch,
+# means over the profiled dispatches), recorded with the kernel sources whose sha256 is given;
+# the factors scale each counter to bytes as measured on torch's fp32 -> bf16 copy of
+# 67,108,864 elements (reads 262,144 KiB, FETCH_SIZE 131,093.8; writes 131,072 KiB, WRITE_SIZE
+# 131,072.0).  Figures and commands: profiles/chunk_fwd_B8H16T4096d128.md and
+# profiles/decode_step_N256H16d128.md.  A kernel whose sources changed reports traffic null.
+FETCH_FACTOR = 262144.0 / 131093.8
+WRITE_FACTOR = 131072.0 / 131072.0
+CSRC = os.path.join(ROOT, "chunkwise_delta_rule_amd", "csrc")
+TRAFFIC = {
+    "chunk_scan_bf16_kernel": dict(sources=("chunk_fwd.hip", "mfma.hpp"), fetch_kib=268400.8,
+                                   write_kib=147456.0, sha256="ce4cdb1b7d771bebf9d9d234d79fb6a4"
+                                   "a5aceba658923136ff2908f83b55f9fb"),
+    "chunk_prep_kernel": dict(sources=("chunk_fwd.hip", "mfma.hpp"), fetch_kib=134508.8,
+                              write_kib=144424.5, sha256="ce4cdb1b7d771bebf9d9d234d79fb6a4"
+                              "a5aceba658923136ff2908f83b55f9fb"),
+    "decode_step_kernel": dict(sources=("decode.hip", "mfma.hpp"), fetch_kib=264253.5,
+                               write_kib=525312.1, sha256="7efdc80c4829e435c48be8feda28c8ca"
+                               "e49104e837fccc5b6cabe05d471b6e7f"),
+}
+
+
+def sources_sha256(names):
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_bytes(kernel):
+    """Counter-derived HBM bytes per launch, or None when the kernel changed since."""
+    t = TRAFFIC.get(kernel)
+    if t is None or sources_sha256(t["sources"]) != t["sha256"]:
+        return None
+    return round(t["fetch_kib"] * 1024 * FETCH_FACTOR + t["write_kib"] * 1024 * WRITE_FACTOR)
+
+
+def roofline_of(kernel, us, flop, nbytes):
+    """The roof that bounds a kernel is the one its algorithmic work reaches last."""
+    t_mfma = flop / PEAK_BF16_FLOPS
+    t_hbm = nbytes / PEAK_HBM_BPS
+    sec = us * 1e-6
+    if t_hbm >= t_mfma:
+        r = {"bound": "hbm", "achieved": nbytes / sec / 1e9, "peak": PEAK_HBM_BPS / 1e9,
+             "unit": "GB/s", "frac": nbytes / sec / PEAK_HBM_BPS}
+    else:
+        r = {"bound": "mfma", "achieved": flop / sec / 1e12, "peak": PEAK_BF16_FLOPS / 1e12,
+             "unit": "TFLOP/s", "frac": flop / sec / PEAK_BF16_FLOPS}
+    r["traffic"] = traffic_bytes(kernel)
+    r.update({"kernel": kernel, "us": us, "algorithmic_bytes": nbytes, "algorithmic_flop": flop,
+              "mfma_frac": flop / sec / PEAK_BF16_FLOPS, "hbm_frac": nbytes / sec / PEAK_HBM_BPS})
+    return r
 
 
 def parse():
@@ -95,20 +160,16 @@ def bench_forward(args, torch, si, mdn):
     toh = cfg.B * cfg.T * cfg.H
     log(f"forward: {step_ms * 1e3:.1f} us/step (prepare {prep_ms * 1e3:.1f} us, "
         f"scan {scan_ms * 1e3:.1f} us), wall {wall / args.steps * 1e3:.1f} us/step")
+    heads = cfg.B * cfg.H
     kernels = {
-        "chunk_prep_kernel": {"us": prep_ms * 1e3, "flop": FLOP_PREP * toh,
-                              "tflops": FLOP_PREP * toh / (prep_ms * 1e-3) / 1e12},
-        "chunk_scan_kernel": {"us": scan_ms * 1e3, "flop": FLOP_SCAN * toh,
-                              "tflops": FLOP_SCAN * toh / (scan_ms * 1e-3) / 1e12},
+        "chunk_prep_kernel": roofline_of("chunk_prep_kernel", prep_ms * 1e3, FLOP_PREP * toh,
+                                         BYTES_PREP * toh),
+        "chunk_scan_bf16_kernel": roofline_of("chunk_scan_bf16_kernel", scan_ms * 1e3,
+                                              FLOP_SCAN * toh,
+                                              BYTES_SCAN * toh + STATE_BYTES_HEAD * heads),
     }
     dom = max(kernels, key=lambda n: kernels[n]["us"])
-    k = kernels[dom]
-    achieved = k["flop"] / (k["us"] * 1e-6)
-    roofline = {"kernel": dom, "bound": "mfma", "achieved": achieved / 1e12,
-                "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_FLOPS, "traffic": None,
-                "flop_per_launch": k["flop"], "flop_per_tok_head": FLOP_SCAN
-                if dom == "chunk_scan_kernel" else FLOP_PREP}
+    roofline = dict(kernels[dom])
     fwd = {"us_per_step": step_ms * 1e3, "tokens_per_s": tokens / (step_ms * 1e-3),
            "mfma_frac": FLOP_FWD * toh / (step_ms * 1e-3) / PEAK_BF16_FLOPS,
            "hbm_frac_algorithmic": BYTES_FWD * toh / (step_ms * 1e-3) / PEAK_HBM_BPS}
@@ -150,7 +211,7 @@ def bench_decode(args, torch, si, mdn):
     return {"workload": f"decode N{cfg.N} H{cfg.H} d{cfg.Dk} fp32 state, bf16 tokens",
             "us_per_step": us, "GB_per_s": gbs, "hbm_frac": gbs * 1e9 / PEAK_HBM_BPS,
             "bytes_per_step": DEC_BYTES_HEAD * heads, "steps_timed": dcfg.steps,
-            "kernel": "decode_step_kernel"}
+            "kernel": "decode_step_kernel", "traffic": traffic_bytes("decode_step_kernel")}
 
 
 def cpu_baseline(inp, cfg):
