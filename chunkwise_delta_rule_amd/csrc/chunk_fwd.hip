@@ -696,11 +696,16 @@ struct TileLayout {
 };
 
 // ---------------------------------------------------------------------------
-// bf16 scan.  Same mathematics and wavefront/column ownership as
-// chunk_scan_kernel, arranged so that a wavefront issues as few instructions
-// per chunk as possible (one wavefront per SIMD is all the head-tile
-// parallelism a layer has, so issue slots bound the scan):
+// bf16 scan.  Same mathematics and column ownership as chunk_scan_kernel;
+// one wavefront per SIMD is all the head-tile parallelism a layer has, so
+// the compute wavefronts are kept free of everything but their own chain.
 //
+//  * Roles.  Eight wavefronts: 0..3 compute (wavefront w owns 16 of the 64
+//    value columns of S and M for the whole sequence), 4..7 stage.  While
+//    the compute wavefronts work on chunk c, the staging wavefronts bring
+//    chunk c + 1 into the other LDS buffer (direct global-to-LDS loads of K,
+//    Q, T, A and the coefficient vectors) and build its K^T and V^T there.
+//    One barrier per chunk hands the buffers over.
 //  * Row order.  The accumulator slot (tile t, lane group g, element j) of
 //    the state (rows d) and of the chunk-row results (rows c) stands for
 //    physical row phys_row(16 t + 4 g + j): inside each block of 32 rows,
@@ -708,14 +713,27 @@ struct TileLayout {
 //    fed from accumulator tiles 2s and 2s + 1 then covers physical rows
 //    32s + 8g + (0..7), so every A fragment is 8 contiguous elements of one
 //    row: one 16-byte LDS read.
-//  * Operands reach LDS by direct global-to-LDS loads (no VGPR staging, no
-//    LDS write instructions), double-buffered: chunk c + 1 is in flight
-//    while chunk c is computed.
-//  * K^T, the A operand of the state update, is built in LDS from the
-//    staged K; each wavefront writes whole K^T rows.
+//  * Outputs are produced transposed, O^T = S^T Q^T + Vt^T A^T, so that a
+//    lane ends with 4 adjacent columns of one output row: one 8-byte store.
 // ---------------------------------------------------------------------------
 template <int DK, int DV>
-__global__ __launch_bounds__(NT) void chunk_scan_bf16_kernel(
+struct ScanBf16Layout {
+    using LK = TileLayout<DK * 2>;          // K, Q rows
+    using LC = TileLayout<CH * 2>;          // T, A rows and K^T rows
+    static constexpr int TV = 64;           // value columns per workgroup
+    static constexpr int VT_LD = 2 * CH + 8;                     // bytes per V^T row
+    static constexpr int KT_BYTES = DK * CH * 2 + (DK / LC::G) * LC::PAD;
+    static constexpr int OFF_Q = LK::BYTES;
+    static constexpr int OFF_T = 2 * LK::BYTES;
+    static constexpr int OFF_A = OFF_T + LC::BYTES;
+    static constexpr int OFF_KT = OFF_A + LC::BYTES;
+    static constexpr int OFF_VT = OFF_KT + KT_BYTES;
+    static constexpr int OFF_VEC = OFF_VT + TV * VT_LD;
+    static constexpr int BUF_BYTES = OFF_VEC + 6 * CH * 4;
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(2 * NT) void chunk_scan_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ Tw, const __bf16* __restrict__ Aw, const float* __restrict__ Vw,
     const float* S0, const float* M0, __bf16* __restrict__ O, float* ST, float* MT, int T,
@@ -723,25 +741,17 @@ __global__ __launch_bounds__(NT) void chunk_scan_bf16_kernel(
 {
     using E = __bf16;
     using MM = Mma<E>;
-    using LK = TileLayout<DK * 2>;          // K, Q rows
-    using LC = TileLayout<CH * 2>;          // T, A, V-tile rows and K^T rows
-    constexpr int TV = 64;                  // value columns per workgroup
+    using L = ScanBf16Layout<DK, DV>;
+    using LK = typename L::LK;
+    using LC = typename L::LC;
+    constexpr int TV = L::TV;
     constexpr int NTILE = DV / TV;
     constexpr int RT = DK / 16;             // state row tiles
     constexpr int SK = DK / 32;             // k-steps over d
     constexpr int SC = CH / 32;             // k-steps over the chunk rows
-    constexpr int KT_BYTES = DK * CH * 2 + (DK / LC::G) * LC::PAD;
-    constexpr int OFF_Q = LK::BYTES;
-    constexpr int OFF_V = 2 * LK::BYTES;
-    constexpr int OFF_T = OFF_V + LC::BYTES;
-    constexpr int OFF_A = OFF_T + LC::BYTES;
-    constexpr int BUF_BYTES = OFF_A + LC::BYTES;
     static_assert(DV % TV == 0, "value tile");
-    static_assert(TV * 2 == CH * 2, "V tile rows use the chunk-row layout");
 
-    __shared__ __align__(16) char buf[2][BUF_BYTES];  // K, Q, V tile, T, A
-    __shared__ __align__(16) float vbuf[2][6 * CH];   // coefficient vectors
-    __shared__ __align__(16) char KTs[KT_BYTES];      // K^T of the current chunk
+    __shared__ __align__(16) char buf[2][L::BUF_BYTES];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -755,6 +765,73 @@ __global__ __launch_bounds__(NT) void chunk_scan_bf16_kernel(
     const int bh = (int)(bid / NTILE);
     const int h = bh % H;
     const int b = bh / H;
+
+    if (wave >= 4) {
+        // ---------------- staging wavefronts ----------------
+        const int hw = wave - 4;
+        const unsigned kq_stride = (unsigned)(H * DK);
+        const unsigned kq_lane = LK::lane_offset(kq_stride, lane);
+        const unsigned c_lane = LC::lane_offset(CH, lane);
+        // K^T: this wavefront transposes the 16 K rows its own direct loads
+        // brought in (groups 4u + hw), in blocks of 4 rows x 8 columns
+        constexpr int QD = DK / 8;                  // 8-column blocks per row
+        const int blk = lane / QD;                  // 4-row block (< 4 when active)
+        const int qd = lane % QD;
+        const bool kt_lane = lane < 4 * QD;
+        const int i4 = LK::G * (4 * (blk / (LK::G / 4)) + hw) + 4 * (blk % (LK::G / 4));
+        // V^T: rows 16 hw + 4 (lane / 16) .. + 3, columns 4 (lane % 16) .. + 3
+        const int vr0 = 16 * hw + 4 * lg;
+        const int vc0 = 4 * l16;
+        auto stage = [&](int c, int bi) {
+            const int n = min(CH, T - c * CH);
+            const size_t tok0 = ((size_t)b * T + c * CH) * H + h;
+            const size_t chn = (size_t)bh * NC + c;
+            char* B = buf[bi];
+            bf16x4 vx[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const unsigned row = (unsigned)min(vr0 + r, n - 1);
+                vx[r] = *reinterpret_cast<const bf16x4*>(v + (tok0 + (size_t)row * H) * DV +
+                                                         tile * TV + vc0);
+            }
+            LK::load(B, k + tok0 * DK, kq_stride, kq_lane, n, hw, lane);
+            LK::load(B + L::OFF_Q, q + tok0 * DK, kq_stride, kq_lane, n, hw, lane);
+            LC::load(B + L::OFF_T, Tw + chn * CH * CH, CH, c_lane, CH, hw, lane);
+            LC::load(B + L::OFF_A, Aw + chn * CH * CH, CH, c_lane, CH, hw, lane);
+            // coefficient vectors: 6 x 64 floats = 96 pieces of 16 bytes
+            if (hw == 0 || (hw == 1 && lane < 32))
+                direct_load16(Vw + chn * NVEC * CH + 4 * (64 * hw + lane),
+                              B + L::OFF_VEC + 1024 * hw);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x4 w4 = {vx[0][j], vx[1][j], vx[2][j], vx[3][j]};
+                *reinterpret_cast<bf16x4*>(B + L::OFF_VT + (vc0 + j) * L::VT_LD + 2 * vr0) = w4;
+            }
+            if (kt_lane) {
+                bf16x8 x[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    x[r] = *reinterpret_cast<const bf16x8*>(B + LK::chunk(i4 + r, qd));
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int d = 8 * qd + j;
+                    const bf16x4 w4 = {x[0][j], x[1][j], x[2][j], x[3][j]};
+                    *reinterpret_cast<bf16x4*>(B + L::OFF_KT + LC::chunk(d, i4 >> 3) +
+                                               2 * (i4 & 7)) = w4;
+                }
+            }
+        };
+        stage(0, 0);
+        __syncthreads();
+        for (int c = 0; c < NC; ++c) {
+            if (c + 1 < NC) stage(c + 1, (c + 1) & 1);
+            __syncthreads();
+        }
+        return;
+    }
+
+    // ---------------- compute wavefronts ----------------
     const int wl = 16 * wave + l16;            // this lane's column inside the tile
     const int col = tile * TV + wl;            // ... inside the head
 
@@ -771,85 +848,31 @@ __global__ __launch_bounds__(NT) void chunk_scan_bf16_kernel(
     if (S0) load_state(Sa, S0); else load_state(Sa, nullptr);
     if (M0) load_state(Ma, M0); else load_state(Ma, nullptr);
 
-    const unsigned kq_stride = (unsigned)(H * DK), v_stride = (unsigned)(H * DV);
-    const unsigned kq_lane = LK::lane_offset(kq_stride, lane);
-    const unsigned v_lane = LC::lane_offset(v_stride, lane);
-    const unsigned c_lane = LC::lane_offset(CH, lane);
-    // The direct loads of chunk c + 1 are issued at the top of chunk c, as
-    // soon as the other buffer is free; they land while chunk c is computed.
-    auto issue_kq = [&](int c, int bi) {
-        const int n = min(CH, T - c * CH);
-        const size_t tok0 = ((size_t)b * T + c * CH) * H + h;
-        LK::load(buf[bi], k + tok0 * DK, kq_stride, kq_lane, n, wave, lane);
-        LK::load(buf[bi] + OFF_Q, q + tok0 * DK, kq_stride, kq_lane, n, wave, lane);
-    };
-    auto issue_rest = [&](int c, int bi) {
-        const int n = min(CH, T - c * CH);
-        const size_t tok0 = ((size_t)b * T + c * CH) * H + h;
-        const size_t chn = (size_t)bh * NC + c;
-        char* B = buf[bi];
-        LC::load(B + OFF_V, v + tok0 * DV + tile * TV, v_stride, v_lane, n, wave, lane);
-        LC::load(B + OFF_T, Tw + chn * CH * CH, CH, c_lane, CH, wave, lane);
-        LC::load(B + OFF_A, Aw + chn * CH * CH, CH, c_lane, CH, wave, lane);
-        // coefficient vectors: 6 x 64 floats = 96 chunks, plain layout
-        if (wave < 2 && (wave == 0 || lane < 32))
-            direct_load16(Vw + chn * NVEC * CH + 4 * (64 * wave + lane), vbuf[bi] + 256 * wave);
-    };
-    issue_kq(0, 0);
-    issue_rest(0, 0);
-
     // per-lane fragment row bases (bytes), the same every chunk
-    int kq_base[4], c_base[4], kt_base[RT];
+    int kq_base[4], c_base[4], kt_base[RT], orow[4];
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
         const int r = phys_row(16 * x + l16);
         kq_base[x] = LK::chunk(r, lg);
         c_base[x] = LC::chunk(r, lg);
+        orow[x] = r;
     }
 #pragma unroll
     for (int x = 0; x < RT; ++x) kt_base[x] = LC::chunk(phys_row(16 * x + l16), lg);
+    const unsigned ostride = (unsigned)(H * DV);
+    E* const Ocol = O + ((size_t)b * T * H + h) * DV + tile * TV + 16 * wave + 4 * lg;
 
+    __syncthreads();                           // chunk 0 staged
     for (int c = 0; c < NC; ++c) {
-        const int cur = c & 1;
         const int t0 = c * CH;
         const int n = min(CH, T - t0);
-        const size_t tok0 = ((size_t)b * T + t0) * H + h;
-        const char* Kb = buf[cur];
-        const char* Qb = Kb + OFF_Q;
-        const char* Vb = Kb + OFF_V;
-        const char* Tb = Kb + OFF_T;
-        const char* Ab = Kb + OFF_A;
-        const float* vec = vbuf[cur];
-
-        // this wavefront's direct loads for chunk c have landed; after the
-        // barrier everyone's have, and nobody still reads the other buffer
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (c + 1 < NC) {
-            issue_kq(c + 1, cur ^ 1);
-            issue_rest(c + 1, cur ^ 1);
-        }
-
-        // K^T[d][c] from K[c][d]: thread t takes chunk rows 4 (t % 16) .. + 3
-        // and d = 8 (t / 16) .. + 7: four 16-byte reads, then eight 8-byte
-        // writes (4 consecutive c of one K^T row each)
-        {
-            const int i4 = 4 * (tid & 15);
-            const int qd = tid >> 4;
-            if (qd < DK / 8) {
-                bf16x8 x[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    x[r] = *reinterpret_cast<const bf16x8*>(Kb + LK::chunk(i4 + r, qd));
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int d = 8 * qd + j;
-                    const bf16x4 w4 = {x[0][j], x[1][j], x[2][j], x[3][j]};
-                    *reinterpret_cast<bf16x4*>(KTs + LC::chunk(d, i4 >> 3) + 2 * (i4 & 7)) = w4;
-                }
-            }
-        }
-        __syncthreads();
+        const char* Kb = buf[c & 1];
+        const char* Qb = Kb + L::OFF_Q;
+        const char* Tb = Kb + L::OFF_T;
+        const char* Ab = Kb + L::OFF_A;
+        const char* KTb = Kb + L::OFF_KT;
+        const char* VTb = Kb + L::OFF_VT + wl * L::VT_LD;
+        const float* vec = reinterpret_cast<const float*>(Kb + L::OFF_VEC);
 
         // (1) X = K [S | M]: the critical path first (the state update below
         //     needs Vt, which needs R, which needs X)
@@ -876,19 +899,16 @@ __global__ __launch_bounds__(NT) void chunk_scan_bf16_kernel(
             }
             // (2) R = V - Diag(abar) K S0 + Diag(alpha b^-) K M0; slot (ct, lg, r)
             //     is chunk row phys_row(16 ct + 4 lg + r), four consecutive rows
-            //     per (ct, lg)
+            //     per (ct, lg), which V^T holds contiguously
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
                 const int p0 = phys_row(16 * ct + 4 * lg);
                 const f32x4 ab = *reinterpret_cast<const f32x4*>(vec + V_ABAR * CH + p0);
                 const f32x4 ab1 = *reinterpret_cast<const f32x4*>(vec + V_AB1 * CH + p0);
+                const bf16x4 vv = *reinterpret_cast<const bf16x4*>(VTb + 2 * p0);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int p = p0 + r;
-                    const float vv = static_cast<float>(*reinterpret_cast<const E*>(
-                        Vb + LC::chunk(p, wl >> 3) + 2 * (wl & 7)));
-                    R[ct][r] = vv - ab[r] * xs[ct][r] + ab1[r] * xm[ct][r];
-                }
+                for (int r = 0; r < 4; ++r)
+                    R[ct][r] = static_cast<float>(vv[r]) - ab[r] * xs[ct][r] + ab1[r] * xm[ct][r];
             }
         }
 
@@ -905,9 +925,9 @@ __global__ __launch_bounds__(NT) void chunk_scan_bf16_kernel(
                                  Vt[it]);
         }
 
-        // (4) O = Diag(abar) Q S0 - Diag(b) Q M0 + A Vt (off the critical path,
-        //     still from the entry state); rows < n to HBM
-        f32x4 Oa[4];
+        // (4) O^T = S0^T Q^T Diag(abar) - M0^T Q^T Diag(b) + Vt^T A^T (from the
+        //     entry state); lane: output row orow[ct], columns 4 lg .. + 3
+        f32x4 Ot[4];
         {
             f32x4 ys[4], ym[4];
 #pragma unroll
@@ -924,46 +944,32 @@ __global__ __launch_bounds__(NT) void chunk_scan_bf16_kernel(
                 const auto bM = MM::from_acc(Ma, s);
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
-                    ys[ct] = MM::mma(aQ[s][ct], bS, ys[ct]);
-                    ym[ct] = MM::mma(aQ[s][ct], bM, ym[ct]);
+                    ys[ct] = MM::mma(bS, aQ[s][ct], ys[ct]);
+                    ym[ct] = MM::mma(bM, aQ[s][ct], ym[ct]);
                 }
             }
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
-                const int p0 = phys_row(16 * ct + 4 * lg);
-                const f32x4 ab = *reinterpret_cast<const f32x4*>(vec + V_ABAR * CH + p0);
-                const f32x4 bb = *reinterpret_cast<const f32x4*>(vec + V_B * CH + p0);
-                Oa[ct] = ab * ys[ct] - bb * ym[ct];
+                const float ab = vec[V_ABAR * CH + orow[ct]];
+                const float bb = vec[V_B * CH + orow[ct]];
+                Ot[ct] = ab * ys[ct] - bb * ym[ct];
             }
         }
 #pragma unroll
         for (int s = 0; s < SC; ++s) {
-            const auto bV = MM::from_acc(Vt, s);
+            const auto aV = MM::from_acc(Vt, s);
 #pragma unroll
-            for (int it = 0; it < 4; ++it)
-                Oa[it] = MM::mma(*reinterpret_cast<const bf16x8*>(Ab + c_base[it] + 64 * s), bV,
-                                 Oa[it]);
+            for (int ct = 0; ct < 4; ++ct)
+                Ot[ct] = MM::mma(aV, *reinterpret_cast<const bf16x8*>(Ab + c_base[ct] + 64 * s),
+                                 Ot[ct]);
         }
         {
-            E* Ob = O + tok0 * DV + col;
-            const unsigned ostride = (unsigned)(H * DV);
-            if (n == CH) {
+            E* Ob = Ocol + (size_t)t0 * ostride;
 #pragma unroll
-                for (int it = 0; it < 4; ++it) {
-                    const int p0 = phys_row(16 * it + 4 * lg);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        Ob[(unsigned)(p0 + r) * ostride] = static_cast<E>(Oa[it][r]);
-                }
-            } else {
-#pragma unroll
-                for (int it = 0; it < 4; ++it) {
-                    const int p0 = phys_row(16 * it + 4 * lg);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (p0 + r < n) Ob[(unsigned)(p0 + r) * ostride] = static_cast<E>(Oa[it][r]);
-                }
-            }
+            for (int ct = 0; ct < 4; ++ct)
+                if (orow[ct] < n)
+                    store4<E>(Ob + (unsigned)orow[ct] * ostride, Ot[ct][0], Ot[ct][1], Ot[ct][2],
+                              Ot[ct][3]);
         }
 
         // (5) S' = abar_n S0 - b_n M0 + K^T Diag(eta gamma_n) Vt,
@@ -982,11 +988,13 @@ __global__ __launch_bounds__(NT) void chunk_scan_bf16_kernel(
             const auto bM = MM::from_acc_scaled8(Vt, s, vec + V_WM * CH + 32 * s + 8 * lg, -1.f);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                const auto aK = *reinterpret_cast<const bf16x8*>(KTs + kt_base[rt] + 64 * s);
+                const auto aK = *reinterpret_cast<const bf16x8*>(KTb + kt_base[rt] + 64 * s);
                 Sa[rt] = MM::mma(aK, bS, Sa[rt]);
                 Ma[rt] = MM::mma(aK, bM, Ma[rt]);
             }
         }
+        // this chunk's buffer is free and the next one is staged
+        __syncthreads();
     }
 
     auto store_state = [&](float* dst, const f32x4* X) {
@@ -1036,7 +1044,7 @@ static hipError_t launch_scan_t(const void* q, const void* k, const void* v, con
     const size_t nblk = (size_t)B * H * (DV / ScanSmem<E, DK, DV>::TV);
     const int xcd_groups = nblk % 8 == 0 ? (int)(nblk / 8) : 0;
     if constexpr (sizeof(E) == 2) {
-        hipLaunchKernelGGL((chunk_scan_bf16_kernel<DK, DV>), dim3((unsigned)nblk), dim3(NT), 0,
+        hipLaunchKernelGGL((chunk_scan_bf16_kernel<DK, DV>), dim3((unsigned)nblk), dim3(2 * NT), 0,
                            stream, static_cast<const E*>(q), static_cast<const E*>(k),
                            static_cast<const E*>(v), ws.T, ws.A, ws.vec, S0, M0,
                            static_cast<E*>(O), ST, MT, T, H, NC, xcd_groups);
