@@ -2,18 +2,20 @@
 
     python bench.py [--steps K] [--warmup W] [--decode-steps D] [--no-cpu-baseline]
 
-A step is one chunkwise forward (mdn_chunk_fwd: coefficients, T, A, residual
-solve, outputs and carried state) over the 1.3B-like layer B=8, H=16,
+A step is one chunkwise forward (mdn_chunk_fwd: coefficients, Gram products,
+residual solve, outputs and carried state, one fused kernel for bf16) over
+the 1.3B-like layer B=8, H=16,
 T=4096, d_k=d_v=128, chunk 64, bf16 q/k/v with fp32 gates and state, inputs
 resident in HBM.  `value` is tokens/s = B*T per step / time per step.
 
 The same JSON line carries:
-  roofline      the dominant kernel (the longest of the two phases) against the roof
-                its algorithmic work reaches last: bytes it must move vs the HBM peak,
-                or FLOP vs the bf16 MFMA peak; timed with HIP events on the launch
-                stream; `traffic` is its counter-measured HBM bytes per launch (null
-                once its sources differ from the profiled ones);
+  roofline      the step's kernel against the roof its algorithmic work reaches
+                last: bytes it must move vs the HBM peak, or FLOP vs the bf16 MFMA
+                peak; timed with HIP events on the launch stream; `traffic` is its
+                counter-measured HBM bytes per launch (null once its sources differ
+                from the profiled ones);
   kernels       the same record for every kernel of the step;
+  split_path    the same forward through mdn_chunk_fwd_prepare + mdn_chunk_fwd_scan;
   forward       the whole step against both roofs;
   decode        the recurrent decode step at 256 sequences x 16 heads, d 128
                 (GB/s of algorithmic state + token traffic);
@@ -66,6 +68,8 @@ TRAFFIC = {
     "chunk_prep_kernel": dict(sources=("chunk_fwd.hip", "mfma.hpp"), fetch_kib=134508.8,
                               write_kib=144424.5, sha256="ce4cdb1b7d771bebf9d9d234d79fb6a4"
                               "a5aceba658923136ff2908f83b55f9fb"),
+    "chunk_fwd_fused_kernel": dict(sources=("chunk_fused.hip", "chunk_common.hpp", "mfma.hpp"),
+                                   fetch_kib=None, write_kib=None, sha256=None),
     "decode_step_kernel": dict(sources=("decode.hip", "mfma.hpp"), fetch_kib=264253.5,
                                write_kib=525312.1, sha256="7efdc80c4829e435c48be8feda28c8ca"
                                "e49104e837fccc5b6cabe05d471b6e7f"),
@@ -84,7 +88,7 @@ def sources_sha256(names):
 def traffic_bytes(kernel):
     """Counter-derived HBM bytes per launch, or None when the kernel changed since."""
     t = TRAFFIC.get(kernel)
-    if t is None or sources_sha256(t["sources"]) != t["sha256"]:
+    if t is None or t["sha256"] is None or sources_sha256(t["sources"]) != t["sha256"]:
         return None
     return round(t["fetch_kib"] * 1024 * FETCH_FACTOR + t["write_kib"] * 1024 * WRITE_FACTOR)
 
@@ -127,6 +131,24 @@ def up(x, dtype):
     return torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(dtype)
 
 
+def time_calls(torch, fns, steps):
+    """Mean time (ms) of each of the callables in `fns`, launched in order
+    `steps` times on the current stream, from HIP events recorded between
+    them; also the span of the whole sequence per step."""
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s in range(steps):
+        ev[s][0].record()
+        for i, fn in enumerate(fns):
+            fn()
+            ev[s][i + 1].record()
+    torch.cuda.synchronize()
+    means = [sum(e[i].elapsed_time(e[i + 1]) for e in ev) / steps for i in range(len(fns))]
+    span = ev[0][0].elapsed_time(ev[-1][-1]) / steps
+    return means, span
+
+
 def bench_forward(args, torch, si, mdn):
     cfg = si.CONFIGS[2]
     t0 = time.time()
@@ -136,44 +158,43 @@ def bench_forward(args, torch, si, mdn):
     f32 = torch.float32
     plan = mdn.ChunkPlan(up(inp["q"], bf), up(inp["k"], bf), up(inp["v"], bf),
                          up(inp["alpha"], f32), up(inp["mu"], f32), up(inp["eta"], f32))
-    torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        plan.prepare()
-        plan.scan()
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for s in range(args.steps):
-        ev[s][0].record()
-        plan.prepare()
-        ev[s][1].record()
-        plan.scan()
-        ev[s][2].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    prep_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    scan_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
-    span_ms = ev[0][0].elapsed_time(ev[-1][2])
-    step_ms = span_ms / args.steps
-    tokens = cfg.B * cfg.T
     toh = cfg.B * cfg.T * cfg.H
-    log(f"forward: {step_ms * 1e3:.1f} us/step (prepare {prep_ms * 1e3:.1f} us, "
-        f"scan {scan_ms * 1e3:.1f} us), wall {wall / args.steps * 1e3:.1f} us/step")
     heads = cfg.B * cfg.H
+    tokens = cfg.B * cfg.T
+    # the step: one mdn_chunk_fwd, which for bf16 launches chunk_coef_kernel (a
+    # few microseconds) and then chunk_fwd_fused_kernel; the events bracket the
+    # call, so the fused kernel's rate below includes the coefficient kernel's
+    # time (it is understated, never overstated)
+    for _ in range(args.warmup):
+        plan.forward()
+    (fwd_ms,), step_ms = time_calls(torch, [plan.forward], args.steps)
+    log(f"forward: {step_ms * 1e3:.1f} us/step (call {fwd_ms * 1e3:.1f} us)")
     kernels = {
+        "chunk_fwd_fused_kernel": roofline_of("chunk_fwd_fused_kernel", fwd_ms * 1e3,
+                                              FLOP_FWD * toh,
+                                              BYTES_FWD * toh + STATE_BYTES_HEAD * heads),
+    }
+    kernels["chunk_fwd_fused_kernel"]["timed_with"] = "chunk_coef_kernel (same call)"
+    # the same forward through the exported two-phase entry points
+    for _ in range(2):
+        plan.prepare()
+        plan.scan()
+    (prep_ms, scan_ms), split_ms = time_calls(torch, [plan.prepare, plan.scan], args.steps)
+    log(f"split path: prepare {prep_ms * 1e3:.1f} us, scan {scan_ms * 1e3:.1f} us")
+    split = {
+        "us_per_step": split_ms * 1e3, "tokens_per_s": tokens / (split_ms * 1e-3),
         "chunk_prep_kernel": roofline_of("chunk_prep_kernel", prep_ms * 1e3, FLOP_PREP * toh,
                                          BYTES_PREP * toh),
         "chunk_scan_bf16_kernel": roofline_of("chunk_scan_bf16_kernel", scan_ms * 1e3,
                                               FLOP_SCAN * toh,
                                               BYTES_SCAN * toh + STATE_BYTES_HEAD * heads),
     }
-    dom = max(kernels, key=lambda n: kernels[n]["us"])
-    roofline = dict(kernels[dom])
+    roofline = dict(kernels["chunk_fwd_fused_kernel"])
     fwd = {"us_per_step": step_ms * 1e3, "tokens_per_s": tokens / (step_ms * 1e-3),
            "mfma_frac": FLOP_FWD * toh / (step_ms * 1e-3) / PEAK_BF16_FLOPS,
-           "hbm_frac_algorithmic": BYTES_FWD * toh / (step_ms * 1e-3) / PEAK_HBM_BPS}
-    return cfg, inp, step_ms, kernels, roofline, fwd
+           "hbm_frac_algorithmic": (BYTES_FWD * toh + STATE_BYTES_HEAD * heads)
+           / (step_ms * 1e-3) / PEAK_HBM_BPS}
+    return cfg, inp, step_ms, kernels, roofline, fwd, split
 
 
 def bench_decode(args, torch, si, mdn):
@@ -242,7 +263,7 @@ def main():
         from chunkwise_delta_rule_amd import build as libbuild
         libbuild.build()
     mdn.load_library()
-    cfg, inp, step_ms, kernels, roofline, fwd = bench_forward(args, torch, si, mdn)
+    cfg, inp, step_ms, kernels, roofline, fwd, split = bench_forward(args, torch, si, mdn)
     decode = None if args.no_decode else bench_decode(args, torch, si, mdn)
     base = None if args.no_cpu_baseline else cpu_baseline(inp, cfg)
     tokens = cfg.B * cfg.T
@@ -265,6 +286,7 @@ def main():
         "roofline": roofline,
         "forward": fwd,
         "kernels": kernels,
+        "split_path": split,
         "decode": decode,
         "cpu_baseline": base,
     }

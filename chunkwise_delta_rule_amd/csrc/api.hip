@@ -12,6 +12,11 @@ size_t chunk_workspace_bytes(int B, int T, int H, bool bf16);
 hipError_t launch_chunk_prepare(const void* q, const void* k, const float* alpha, const float* mu,
                                 const float* eta, int B, int T, int H, int Dk, bool bf16,
                                 void* workspace, hipStream_t stream);
+size_t chunk_fused_workspace_bytes(size_t nchunks);
+hipError_t launch_chunk_fused(const void* q, const void* k, const void* v, const float* alpha,
+                              const float* mu, const float* eta, const float* S0, const float* M0,
+                              void* O, float* ST, float* MT, int B, int T, int H, int Dk, int Dv,
+                              void* workspace, hipStream_t stream);
 hipError_t launch_chunk_scan(const void* q, const void* k, const void* v, const float* S0,
                              const float* M0, void* O, float* ST, float* MT, int B, int T, int H,
                              int Dk, int Dv, bool bf16, const void* workspace, hipStream_t stream);
@@ -77,8 +82,7 @@ const char* mdn_status_string(mdn_status s)
     return "unknown mdn_status";
 }
 
-size_t mdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
-                                     mdn_dtype dt)
+static size_t split_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, mdn_dtype dt)
 {
     if (B <= 0 || T <= 0 || H <= 0) return 0;
     if (!head_dim_ok(Dk) || !head_dim_ok(Dv) || chunk != 64) return 0;
@@ -86,6 +90,22 @@ size_t mdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int ch
     size_t tmp;
     if (!mul_ok((size_t)B, (size_t)T, (size_t)H, 1, &tmp)) return 0;
     return mdn::chunk_workspace_bytes(B, T, H, dt == MDN_BF16);
+}
+
+size_t mdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
+                                     mdn_dtype dt)
+{
+    // the bf16 forward keeps T and A on chip and needs only the per-chunk
+    // coefficient tables
+    const size_t split = split_workspace_bytes(B, T, H, Dk, Dv, chunk, dt);
+    if (split == 0 || dt != MDN_BF16) return split;
+    return mdn::chunk_fused_workspace_bytes((size_t)B * H * (((size_t)T + 63) / 64));
+}
+
+size_t mdn_chunk_fwd_split_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
+                                           mdn_dtype dt)
+{
+    return split_workspace_bytes(B, T, H, Dk, Dv, chunk, dt);
 }
 
 }  // extern "C"
@@ -137,7 +157,12 @@ mdn_status validate_fwd(const FwdArgs& a, int phase, bool* no_work)
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MDN_ERR_ALIGN;
 
-    const size_t need = tok ? mdn::chunk_workspace_bytes(a.B, a.T, a.H, a.dt == MDN_BF16) : 0;
+    // the bf16 forward runs fused and needs only the per-chunk coefficient tables
+    const bool fused = phase == BOTH && a.dt == MDN_BF16;
+    const size_t nchunks = (size_t)a.B * a.H * (((size_t)a.T + 63) / 64);
+    const size_t need = !tok ? 0
+                        : fused ? mdn::chunk_fused_workspace_bytes(nchunks)
+                                : mdn::chunk_workspace_bytes(a.B, a.T, a.H, a.dt == MDN_BF16);
     if (need > 0 && (!a.ws || a.ws_bytes < need)) return MDN_ERR_WORKSPACE;
 
     const size_t nt = tok ? 1 : 0;   // token arrays are empty when T == 0
@@ -174,7 +199,14 @@ mdn_status run_fwd(const FwdArgs& a, int phase, hipStream_t stream)
     const mdn_status st = validate_fwd(a, phase, &no_work);
     if (st != MDN_OK || no_work) return st;
     const bool bf16 = a.dt == MDN_BF16;
-    if (phase & PREPARE) {
+    if (phase == BOTH && bf16 && a.T > 0) {
+        const hipError_t err =
+            mdn::launch_chunk_fused(a.q, a.k, a.v, a.alpha, a.mu, a.eta, a.S0, a.M0, a.O, a.S_T,
+                                    a.M_T, a.B, a.T, a.H, a.Dk, a.Dv, const_cast<void*>(a.ws),
+                                    stream);
+        return err == hipSuccess ? MDN_OK : MDN_ERR_HIP;
+    }
+    if ((phase & PREPARE) && a.T > 0) {
         const hipError_t err =
             mdn::launch_chunk_prepare(a.q, a.k, a.alpha, a.mu, a.eta, a.B, a.T, a.H, a.Dk, bf16,
                                       const_cast<void*>(a.ws), stream);

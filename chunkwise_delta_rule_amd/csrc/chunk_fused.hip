@@ -1,0 +1,800 @@
+// chunk_fused.hip -- the chunkwise MDN forward for bf16 inputs on gfx950 as
+// two launches: a small coefficient kernel (per chunk, fully parallel) and
+// one fused kernel in which each chunk's Gram products, masks and triangular
+// solve are formed in the same workgroup that carries the state, so T, A
+// and the Gram matrices never leave LDS and q, k, v are read from HBM once.
+//
+// The method is the same as in chunk_fwd.hip ("MDN: Parallelizing Stepwise
+// Momentum for Delta Linear Attention", slides Eqs. (7)-(9), (15)-(18),
+// (40)-(42) in their Appendix C forms with the one-row-shifted residual mask;
+// the reading notes on the same paper, Secs. 2.3-2.5).  Per chunk of C = 64
+// rows with entry state (S0, M0), P = Diag(alpha) K, Khat = Diag(eta) K:
+//   L  = I + (P Khat^T) o Gamma^-,   A = (Q Khat^T) o Gamma
+//   R  = V - Diag(abar) K S0 + Diag(alpha_i b_{i-1}) K M0,   Vt = L^{-1} R
+//   O  = Diag(abar) Q S0 - Diag(b) Q M0 + A Vt
+//   S' = abar_C S0 - b_C M0 + K^T Diag(eta gamma_C) Vt
+//   M' = mubar_C M0 - K^T Diag(eta mubar_C / mubar) Vt
+//
+// Two ways of evaluating the same quantities differ from chunk_fwd.hip:
+//
+//  * Gamma by 16-row blocks.  For a column j left of block I (rows
+//    16 I .. 16 I + 15) the column recursion m_{i,j} = mu_i m_{i-1,j},
+//    gamma_{i,j} = alpha_i gamma_{i-1,j} + m_{i,j} is affine in its value at
+//    row 16 I - 1, so with the block-local products
+//        ra_i = prod_{u=16I}^{i} alpha_u,   rp_i = prod_{u=16I}^{i} mu_u,
+//        rg_i = alpha_i rg_{i-1} + rp_i     (rg_{16I-1} = 0)
+//    it is gamma_{i,j} = ra_i gb_{I,j} + rg_i mb_{I,j} and m_{i,j} =
+//    rp_i mb_{I,j}, where (gb, mb) are gamma and m at row 16 I - 1.  Only the
+//    16 x 16 diagonal blocks run the recursion itself; every quantity stays a
+//    sum of nonnegative products, with no division, so mu = 0 is exact.
+//  * Vt = L^{-1} R by block forward substitution over the four 16-row blocks:
+//        Vt_I = D_I (R_I - sum_{J<I} N_{IJ} Vt_J),  D_I = (I + N_{II})^{-1},
+//    with N = L - I strictly lower triangular, so N_{II}^16 = 0 and
+//    D_I = (I - N)(I + N^2)(I + N^4)(I + N^8): four levels of 16x16x16
+//    products, all operands in registers.
+//
+// chunk_coef_kernel (one wavefront per chunk, lane = row and column index)
+//   writes each chunk's tables: its gates, ra and rg of the rows, the
+//   diagonal blocks of Gamma, (gb, mb) for every block and column, and the
+//   six coefficient rows the scan reads.  Both value-column tiles of a head
+//   use the same tables, which is why they are computed once, here.
+//
+// chunk_fwd_fused_kernel: 8 wavefronts for one (batch, head, 64 value columns).
+//   compute 0..3  wavefront w keeps columns 16 w .. 16 w + 15 of S and M in
+//                 fp32 accumulators for the whole sequence (rows of S in the
+//                 permuted order phys_row(), as in chunk_fwd.hip) and works
+//                 through chunk c: X = K [S|M], R, Q [S|M], the substitution,
+//                 O^T (stored as 8-byte rows), the state update.
+//   helper 4..7   helper h owns row block h (rows 16 h .. 16 h + 15).  While
+//                 chunk c is scanned it prepares chunk c + 1 in the other LDS
+//                 buffer: its K, Q rows (loaded into registers one chunk
+//                 earlier, in MFMA fragment layout) to LDS, the V tile and
+//                 the coefficient rows by direct loads, row block h of the
+//                 Gram product P Khat^T masked into -N and D_h, column block
+//                 h of A; and it loads the tables of chunk c + 2.  No helper
+//                 waits for another.
+// Two workgroup barriers per chunk: B1 once K, Q of chunk c + 1 are in LDS
+// (the compute wavefronts have done their entry-state products by then), B0
+// once chunk c + 1 is complete.
+#include <hip/hip_runtime.h>
+
+#include "chunk_common.hpp"
+#include "mfma.hpp"
+
+namespace mdn {
+
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+
+template <int N>
+struct IConst {
+    static constexpr int value = N;
+};
+
+// Per-chunk coefficient tables (float offsets), as chunk_coef_kernel writes
+// them to the workspace and the fused kernel keeps them in LDS (all but the
+// coefficient rows, which go to the chunk's operand buffer).
+struct ChunkTables {
+    static constexpr int ALPHA = 0;           // gates of the rows
+    static constexpr int ETA = 64;
+    static constexpr int RA = 128;            // block-local products of the rows
+    static constexpr int RG = 192;
+    static constexpr int GB = 256;            // [4][64]: gamma at row 16 I - 1, column j (j < 16 I)
+    static constexpr int MB = 512;            // [4][64]: m at row 16 I - 1
+    static constexpr int GD = 768;            // [64][16]: row i, column 16 (i / 16) + jj of Gamma
+    static constexpr int VEC = 1792;          // the six coefficient rows (V_ABAR .. V_SCAL)
+    static constexpr int LDS_FLOATS = VEC;    // what the fused kernel keeps in LDS
+    static constexpr int FLOATS = VEC + 6 * CH;
+};
+
+size_t chunk_fused_workspace_bytes(size_t nchunks)
+{
+    return nchunks * ChunkTables::FLOATS * sizeof(float);
+}
+
+// two 4-element k-fragments as one 8-element fragment (k of the second after
+// the first's)
+__device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b)
+{
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+__device__ __forceinline__ bf16x4 to_bf4(const f32x4& x)
+{
+    return bf16x4{static_cast<__bf16>(x[0]), static_cast<__bf16>(x[1]),
+                  static_cast<__bf16>(x[2]), static_cast<__bf16>(x[3])};
+}
+
+// value of x in lane l (l uniform)
+__device__ __forceinline__ float readlane_f(float x, int l)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// A lane-dependent value the compiler must treat as new at this point: keeps
+// per-lane comparisons made from it inside the chunk loop instead of hoisted
+// out of it as lane masks (which would then live in spilled SGPRs).
+__device__ __forceinline__ int opaque(int x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// LDS ordering inside one wavefront (data written by other lanes of it)
+__device__ __forceinline__ void wave_lds_sync()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
+// Coefficient tables of every chunk.  Four chunks per workgroup, one per
+// wavefront; lane l is row l (for the row quantities) and column l (for the
+// column recursion); its 16-row block is l / 16.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT) void chunk_coef_kernel(const float* __restrict__ alpha,
+                                                        const float* __restrict__ mu,
+                                                        const float* __restrict__ eta,
+                                                        float* __restrict__ ws, int T, int H,
+                                                        int NC, size_t nchunks)
+{
+    using CTb = ChunkTables;
+    __shared__ __align__(16) float gates[4][2][CH];
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const size_t ch = (size_t)blockIdx.x * 4 + wv;
+    if (ch >= nchunks) return;   // whole wavefronts; this kernel has no barrier
+    const int c = (int)(ch % NC);
+    const size_t bh = ch / NC;
+    const int h = (int)(bh % H), b = (int)(bh / H);
+    const int n = min(CH, T - c * CH), last = n - 1;
+    const size_t gi = ((size_t)b * T + (size_t)c * CH + min(lane, last)) * H + h;
+    const float ga = alpha[gi], gm = mu[gi], ge = eta[gi];
+    float* tb = ws + ch * CTb::FLOATS;
+
+    const int blk = lane >> 4, off = lane & 15;
+    gates[wv][0][lane] = ga;
+    gates[wv][1][lane] = gm;
+    wave_lds_sync();
+    float ab[16], mbk[16];
+#pragma unroll
+    for (int t = 0; t < 16; t += 4) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(&gates[wv][0][16 * blk + t]);
+        const f32x4 m4 = *reinterpret_cast<const f32x4*>(&gates[wv][1][16 * blk + t]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ab[t + e] = a4[e];
+            mbk[t + e] = m4[e];
+        }
+    }
+    // block-local products of row `lane`, and the diagonal-block column
+    // recursion of column `lane`, side by side over the block's rows
+    float ra = 1.f, rp = 1.f, rg = 0.f;
+    float gam = 1.f, mm = 1.f, g_last = 0.f, m_last = 0.f;
+    float gd[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        const float a = ab[t], m = mbk[t];
+        const bool row_in = t <= off;      // block row t is at or above row `lane`
+        ra = row_in ? ra * a : ra;
+        rp = row_in ? rp * m : rp;
+        rg = row_in ? a * rg + rp : rg;
+        const bool below = t > off;        // below column `lane`'s diagonal
+        mm = below ? mm * m : mm;
+        gam = below ? a * gam + mm : gam;
+        gd[t] = t >= off ? gam : 0.f;
+        const bool at_last = 16 * blk + t == last;
+        g_last = at_last ? gd[t] : g_last;
+        m_last = at_last ? (t >= off ? mm : 0.f) : m_last;
+    }
+    // block summaries (values at each block's last row)
+    const float sa0 = readlane_f(ra, 15), sa1 = readlane_f(ra, 31), sa2 = readlane_f(ra, 47);
+    const float sp1 = readlane_f(rp, 31), sp2 = readlane_f(rp, 47);
+    const float sg1 = readlane_f(rg, 31), sg2 = readlane_f(rg, 47);
+    // gamma, m of column `lane` at rows 16 I - 1 for the blocks below its own
+    float gb = gam, mb = mm;
+    float gbI[4] = {0.f, 0.f, 0.f, 0.f}, mbI[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int I = 1; I < 4; ++I) {
+        if (I > 1) {   // through block I - 1 when the column lies left of it
+            const float ca = I == 2 ? sa1 : sa2, cg = I == 2 ? sg1 : sg2, cp = I == 2 ? sp1 : sp2;
+            const bool through = I > blk + 1;
+            const float gn = ca * gb + cg * mb, mn = cp * mb;
+            gb = through ? gn : gb;
+            mb = through ? mn : mb;
+        }
+        gbI[I] = I > blk ? gb : 0.f;
+        mbI[I] = I > blk ? mb : 0.f;
+    }
+    // coefficient rows
+    const float pre = blk == 0 ? 1.f : blk == 1 ? sa0 : blk == 2 ? sa0 * sa1 : sa0 * sa1 * sa2;
+    const float abar = ra * pre;
+    const float mu0 = readlane_f(gm, 0);
+    // gamma_{i,0}: block 0 from column 0's recursion, later blocks from the
+    // boundary values of column 0
+    float g0c[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) g0c[t] = readlane_f(gd[t], 0);
+    float g0 = 0.f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) g0 = (blk == 0 && off == t) ? g0c[t] : g0;
+    {
+        const float gb1 = readlane_f(gbI[1], 0), gb2 = readlane_f(gbI[2], 0), gb3 = readlane_f(gbI[3], 0);
+        const float mb1 = readlane_f(mbI[1], 0), mb2 = readlane_f(mbI[2], 0), mb3 = readlane_f(mbI[3], 0);
+        const float gbb = blk == 1 ? gb1 : blk == 2 ? gb2 : gb3;
+        const float mbb = blk == 1 ? mb1 : blk == 2 ? mb2 : mb3;
+        if (blk > 0) g0 = ra * gbb + rg * mbb;
+    }
+    const float bi = mu0 * g0;
+    const float bprev = __shfl_up(bi, 1);
+    const bool valid = lane < n;
+    // gamma and m at the last row, column `lane`
+    const int lb = last >> 4;
+    const float raL = readlane_f(ra, last), rgL = readlane_f(rg, last), rpL = readlane_f(rp, last);
+    const float gbl = lb == 1 ? gbI[1] : lb == 2 ? gbI[2] : gbI[3];
+    const float mbl = lb == 1 ? mbI[1] : lb == 2 ? mbI[2] : mbI[3];
+    const float gl = blk < lb ? raL * gbl + rgL * mbl : blk == lb ? g_last : 0.f;
+    const float ml = blk < lb ? rpL * mbl : blk == lb ? m_last : 0.f;
+    const float abar_n = readlane_f(abar, last);
+    const float b_n = readlane_f(bi, last);
+    const float mbar_n = mu0 * readlane_f(ml, 0);
+
+    // ---- stores
+    tb[CTb::ALPHA + lane] = ga;
+    tb[CTb::ETA + lane] = ge;
+    tb[CTb::RA + lane] = ra;
+    tb[CTb::RG + lane] = rg;
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        tb[CTb::GB + 64 * I + lane] = gbI[I];
+        tb[CTb::MB + 64 * I + lane] = mbI[I];
+    }
+    // diagonal block of Gamma, one column per lane (zero above the diagonal)
+#pragma unroll
+    for (int t = 0; t < 16; ++t) tb[CTb::GD + (16 * blk + t) * 16 + off] = gd[t];
+    float* vec = tb + CTb::VEC;
+    vec[V_ABAR * CH + lane] = valid ? abar : 0.f;
+    vec[V_AB1 * CH + lane] = valid && lane > 0 ? ga * bprev : 0.f;
+    vec[V_B * CH + lane] = valid ? bi : 0.f;
+    vec[V_WS * CH + lane] = ge * gl;
+    vec[V_WM * CH + lane] = ge * ml;
+    vec[V_SCAL * CH + lane] = lane == 0 ? abar_n : lane == 1 ? b_n : lane == 2 ? mbar_n : 0.f;
+}
+
+template <int DK>
+struct FusedLayout {
+    using LK = TileLayout<DK * 2>;          // K, Q: 64 rows x DK
+    using LC = TileLayout<CH * 2>;          // V tile, T (-N, D), A: 64 rows x 64
+    static constexpr int OFF_K = 0;
+    static constexpr int OFF_Q = LK::BYTES;
+    static constexpr int OFF_V = 2 * LK::BYTES;
+    static constexpr int OFF_T = OFF_V + LC::BYTES;
+    static constexpr int OFF_A = OFF_T + LC::BYTES;
+    static constexpr int OFF_VEC = OFF_A + LC::BYTES;
+    static constexpr int BUF = OFF_VEC + 6 * CH * 4;
+    static constexpr int TB_BYTES = ChunkTables::LDS_FLOATS * 4;
+    // two operand buffers, two table sets (chunks of even and odd index)
+    static constexpr int BYTES = 2 * BUF + 2 * TB_BYTES;
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const float* __restrict__ ctab, const float* S0, const float* M0, __bf16* __restrict__ O,
+    float* ST, float* MT, int T, int H, int NC, int xcd_groups)
+{
+    using E = __bf16;
+    using MM = Mma<E>;
+    using L = FusedLayout<DK>;
+    using LK = typename L::LK;
+    using LC = typename L::LC;
+    using CTb = ChunkTables;
+    constexpr int TV = 64;                  // value columns per workgroup
+    constexpr int NTILE = DV / TV;
+    constexpr int RT = DK / 16;             // state row tiles
+    constexpr int SK = DK / 32;             // 16x16x32 k-steps over d
+    static_assert(DV % TV == 0, "value tile");
+
+    __shared__ __align__(16) char smem[L::BYTES];
+    // coefficient tables of chunk c: set c & 1
+    auto tables = [&](int c) {
+        return reinterpret_cast<float*>(smem + 2 * L::BUF + (c & 1) * L::TB_BYTES);
+    };
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l16 = lane & 15;
+    const int lg = lane >> 4;
+
+    unsigned bid = blockIdx.x;
+    if (xcd_groups > 0) bid = (bid % 8u) * (unsigned)xcd_groups + bid / 8u;
+    const int tile = (int)(bid % NTILE);
+    const int bh = (int)(bid / NTILE);
+    const int h = bh % H;
+    const int b = bh / H;
+    // token index of row 0 of chunk c of this head (rows are H tokens apart)
+    auto tok_base = [&](int c) { return ((size_t)b * T + (size_t)c * CH) * H + h; };
+    auto chunk_rows = [&](int c) { return min(CH, T - c * CH); };
+
+    if (wave >= 4) {
+        // =================== helper wavefronts ===================
+        const int hw = wave - 4;
+        const int r0 = 16 * hw;                 // first row of this helper's block
+        MM::frag kf[2][SK], qf[2][SK];          // own K, Q rows; set = chunk parity
+        const unsigned v_lane = LC::lane_offset((unsigned)(H * DV), lane);
+        const MM::frag zfrag = __builtin_bit_cast(MM::frag, u32x4{0u, 0u, 0u, 0u});
+        // 16x16 product X Y from acc(X^T) and acc(Y), where acc(Z) is the
+        // accumulator layout (lane (l16, g), element r = Z[4 g + r][l16]): the
+        // A operand of a 16x16x16 step is then acc(X^T) and the B operand
+        // acc(Y), both straight from registers (operands rounded to bf16)
+        auto prod = [](const f32x4& XT, const f32x4& YB) {
+            return mma16(to_bf4(XT), to_bf4(YB), zero4());
+        };
+
+        auto load_kq = [&](int c, auto par) {
+            constexpr int P = decltype(par)::value;
+            const int n = chunk_rows(c);
+            const size_t row = tok_base(c) + (size_t)min(r0 + l16, n - 1) * H;
+#pragma unroll
+            for (int u = 0; u < SK; ++u) {
+                const size_t off = row * DK + 8 * (4 * u + lg);
+                kf[P][u] = *reinterpret_cast<const MM::frag*>(k + off);
+                qf[P][u] = *reinterpret_cast<const MM::frag*>(q + off);
+            }
+        };
+        // own rows of chunk c into buffer B (rows >= n become zero, in the
+        // registers too, so the Gram products, L and A vanish there)
+        auto store_kq = [&](int c, char* B, auto par) {
+            constexpr int P = decltype(par)::value;
+            const bool live = r0 + l16 < chunk_rows(c);
+#pragma unroll
+            for (int u = 0; u < SK; ++u) {
+                kf[P][u] = live ? kf[P][u] : zfrag;
+                qf[P][u] = live ? qf[P][u] : zfrag;
+                const int off = LK::chunk(r0 + l16, 4 * u + lg);
+                *reinterpret_cast<MM::frag*>(B + L::OFF_K + off) = kf[P][u];
+                *reinterpret_cast<MM::frag*>(B + L::OFF_Q + off) = qf[P][u];
+            }
+        };
+        // direct loads of chunk c's V tile and coefficient rows into buffer B
+        auto load_v = [&](int c, char* B) {
+            const int n = chunk_rows(c);
+            LC::load(B + L::OFF_V, v + tok_base(c) * DV + tile * TV, (unsigned)(H * DV), v_lane,
+                     n, hw, lane);
+            const float* src = ctab + ((size_t)bh * NC + c) * CTb::FLOATS + CTb::VEC;
+            if (hw == 0 || (hw == 1 && lane < 32))
+                direct_load16(src + 4 * (64 * hw + lane), B + L::OFF_VEC + 1024 * hw);
+        };
+        // direct loads of chunk c's tables into its table set: 7 pieces of
+        // 1 KB, helper h takes pieces h and h + 4
+        auto load_tables = [&](int c) {
+            const float* src = ctab + ((size_t)bh * NC + c) * CTb::FLOATS;
+            char* dst = reinterpret_cast<char*>(tables(c));
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int piece = hw + 4 * u;
+                if (piece < CTb::LDS_FLOATS / 256)
+                    direct_load16(src + 256 * piece + 4 * lane, dst + 1024 * piece);
+            }
+        };
+
+        // Row block W of L (-N_{W,J}, J < W, and D_W) into T, column block W
+        // of A into A; W is this helper's index, a compile-time constant in
+        // each copy.
+        auto prepare = [&](auto wc, char* B, const float* tb, auto par) {
+            constexpr int W = decltype(wc)::value;
+            constexpr int P = decltype(par)::value;
+            const int l16o = opaque(lane & 15), lgo = opaque(lane >> 4);
+            const char* Kb = B + L::OFF_K;
+            const char* Qb = B + L::OFF_Q;
+            // ---- table values for the masks
+            const int iL = 16 * W + l16o;
+            const float aiL = tb[CTb::ALPHA + iL];
+            const float raP = tb[CTb::RA + (l16o > 0 ? iL - 1 : iL)];
+            const float rgP = tb[CTb::RG + (l16o > 0 ? iL - 1 : iL)];
+            f32x4 eC[4], gbL[4], mbL[4];        // columns 16 J + 4 lg + r
+#pragma unroll
+            for (int J = 0; J <= W; ++J) {
+                eC[J] = *reinterpret_cast<const f32x4*>(tb + CTb::ETA + 16 * J + 4 * lgo);
+                if (J < W) {
+                    gbL[J] = *reinterpret_cast<const f32x4*>(tb + CTb::GB + 64 * W + 16 * J + 4 * lgo);
+                    mbL[J] = *reinterpret_cast<const f32x4*>(tb + CTb::MB + 64 * W + 16 * J + 4 * lgo);
+                }
+            }
+            const f32x4 gdT = *reinterpret_cast<const f32x4*>(
+                tb + CTb::GD + (16 * W + (l16o > 0 ? l16o - 1 : 0)) * 16 + 4 * lgo);
+            const f32x4 aD = *reinterpret_cast<const f32x4*>(tb + CTb::ALPHA + 16 * W + 4 * lgo);
+            const float eR = tb[CTb::ETA + 16 * W + l16o];
+            float gdB[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * lgo + r - 1;
+                gdB[r] = tb[CTb::GD + (16 * W + (row > 0 ? row : 0)) * 16 + l16o];
+            }
+            // A column block W: rows 16 I + l16 (I >= W), columns 16 W + 4 lg + r
+            float raA[4], rgA[4];
+            f32x4 gA[4], mA[4];
+#pragma unroll
+            for (int I = W + 1; I < 4; ++I) {
+                raA[I] = tb[CTb::RA + 16 * I + l16o];
+                rgA[I] = tb[CTb::RG + 16 * I + l16o];
+                gA[I] = *reinterpret_cast<const f32x4*>(tb + CTb::GB + 64 * I + 16 * W + 4 * lgo);
+                mA[I] = *reinterpret_cast<const f32x4*>(tb + CTb::MB + 64 * I + 16 * W + 4 * lgo);
+            }
+            const f32x4 gdA = *reinterpret_cast<const f32x4*>(tb + CTb::GD + (16 * W + l16o) * 16 + 4 * lgo);
+            // ---- Gram tiles, transposed (lane: row 16 I + l16, columns 16 J + 4 lg + r)
+            f32x4 Gt[W + 1], At[4];
+#pragma unroll
+            for (int J = 0; J <= W; ++J) Gt[J] = zero4();
+#pragma unroll
+            for (int I = W; I < 4; ++I) At[I] = zero4();
+#pragma unroll
+            for (int s = 0; s < SK; ++s) {
+#pragma unroll
+                for (int J = 0; J < W; ++J) {
+                    const auto aK =
+                        *reinterpret_cast<const MM::frag*>(Kb + LK::chunk(16 * J + l16, 4 * s + lg));
+                    Gt[J] = MM::mma(aK, kf[P][s], Gt[J]);
+                }
+                Gt[W] = MM::mma(kf[P][s], kf[P][s], Gt[W]);
+                At[W] = MM::mma(kf[P][s], qf[P][s], At[W]);
+#pragma unroll
+                for (int I = W + 1; I < 4; ++I) {
+                    const auto bQ =
+                        *reinterpret_cast<const MM::frag*>(Qb + LK::chunk(16 * I + l16, 4 * s + lg));
+                    At[I] = MM::mma(kf[P][s], bQ, At[I]);
+                }
+            }
+            // ---- masks: -N_{W,J} = -alpha_i eta_j G_ij gamma_{i-1,j} (J < W)
+            bf16x4 nOut[4];
+#pragma unroll
+            for (int J = 0; J < W; ++J)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float g = l16o == 0 ? gbL[J][r] : raP * gbL[J][r] + rgP * mbL[J][r];
+                    nOut[J][r] = static_cast<__bf16>(-(aiL * eC[J][r] * Gt[J][r] * g));
+                }
+            // N_WW in both accumulator layouts from the symmetric Gram tile:
+            // NT = acc(N^T) (lane: row l16, cols 4 lg + r), NB = acc(N)
+            f32x4 NT, NB, Id;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = 4 * lgo + r;
+                NT[r] = j < l16o ? aiL * eC[W][r] * Gt[W][r] * gdT[r] : 0.f;
+                NB[r] = l16o < j ? aD[r] * eR * Gt[W][r] * gdB[r] : 0.f;
+                Id[r] = j == l16o ? 1.f : 0.f;
+            }
+            // A_{I,W} = eta_j QK_ij gamma_{i,j} (j <= i)
+            bf16x4 aOut[4];
+#pragma unroll
+            for (int I = W; I < 4; ++I)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float g = I == W ? gdA[r] : raA[I] * gA[I][r] + rgA[I] * mA[I][r];
+                    aOut[I][r] = static_cast<__bf16>(eC[W][r] * At[I][r] * g);
+                }
+            // D_W = (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8) (N^16 = 0),
+            // formed transposed: D^T = (I + N8^T)(I + N4^T) P1^T
+            const f32x4 N2B = prod(NT, NB), N2T = prod(NB, NT);
+            const f32x4 N4B = prod(N2T, N2B), N4T = prod(N2B, N2T);
+            const f32x4 N8B = prod(N4T, N4B);
+            const f32x4 P1T = Id - NT + N2T - prod(N2B, NT);
+            const f32x4 QT = P1T + prod(N4B, P1T);
+            const f32x4 DT = QT + prod(N8B, QT);
+            // ---- stores
+            char* Tb = B + L::OFF_T;
+            char* Ab = B + L::OFF_A;
+#pragma unroll
+            for (int J = 0; J < W; ++J) {
+                const int j0 = 16 * J + 4 * lg;
+                *reinterpret_cast<bf16x4*>(Tb + LC::chunk(iL, j0 >> 3) + 2 * (j0 & 7)) = nOut[J];
+            }
+            const int j0 = 16 * W + 4 * lg;
+            *reinterpret_cast<bf16x4*>(Tb + LC::chunk(iL, j0 >> 3) + 2 * (j0 & 7)) = to_bf4(DT);
+#pragma unroll
+            for (int I = W; I < 4; ++I)
+                *reinterpret_cast<bf16x4*>(Ab + LC::chunk(16 * I + l16, j0 >> 3) + 2 * (j0 & 7)) =
+                    aOut[I];
+        };
+        auto prepare_any = [&](char* B, const float* tb, auto par) {
+            switch (hw) {
+            case 0: prepare(IConst<0>{}, B, tb, par); break;
+            case 1: prepare(IConst<1>{}, B, tb, par); break;
+            case 2: prepare(IConst<2>{}, B, tb, par); break;
+            default: prepare(IConst<3>{}, B, tb, par); break;
+            }
+        };
+
+        // The pipeline: in round c (c = -1 .. NC - 1) chunk nx = c + 1 is
+        // prepared into buffer nx & 1 while the compute wavefronts scan chunk
+        // c.  Its K, Q rows were loaded into registers and its tables into
+        // table set nx & 1 in round c - 1.  Per helper and round the loads
+        // are issued as: tables of nx + 1, V tile and coefficient rows of nx,
+        // K, Q rows of nx + 1 (2 SK), so waiting for all but the last 2 SK
+        // covers everything nx needs.
+        auto round = [&](int c, auto par) {      // par: parity of nx
+            constexpr int P = decltype(par)::value;
+            const int nx = c + 1;
+            char* B = smem + P * L::BUF;
+            const float* tb = tables(nx);
+            const bool live = nx < NC, more = nx + 1 < NC;
+            if (live) {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // K, Q and tables of nx
+                store_kq(nx, B, par);
+                if (more) load_tables(nx + 1);
+                load_v(nx, B);
+                if (more) load_kq(nx + 1, IConst<1 - P>{});
+            }
+            lds_barrier();   // B1: K, Q and the tables of nx visible
+            if (live) {
+                prepare_any(B, tb, par);
+                // the V tile and coefficient rows of nx have landed; the
+                // K, Q loads of nx + 1, issued after them, may still be in
+                // flight
+                if (more) {
+                    if constexpr (SK == 4)
+                        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+                    else
+                        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                } else {
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                }
+            }
+            lds_barrier();   // B0: chunk nx ready
+        };
+        load_kq(0, IConst<0>{});
+        load_tables(0);
+        for (int c = -1; c < NC; c += 2) {
+            round(c, IConst<0>{});
+            if (c + 1 < NC) round(c + 1, IConst<1>{});
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        return;
+    }
+
+    // =================== compute wavefronts ===================
+    const int wl = 16 * wave + l16;            // this lane's column inside the tile
+    const int col = tile * TV + wl;            // ... inside the head
+    f32x4 Sa[RT], Ma[RT];                      // slot (rt, lg, r): row phys_row(16 rt + 4 lg + r)
+    const size_t sbase = (size_t)bh * DK * DV;
+    auto load_state = [&](f32x4* X, const float* src) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                X[rt][r] = src ? src[sbase + (size_t)phys_row(16 * rt + 4 * lg + r) * DV + col] : 0.f;
+    };
+    if (S0) load_state(Sa, S0); else load_state(Sa, nullptr);
+    if (M0) load_state(Ma, M0); else load_state(Ma, nullptr);
+
+    // per-lane LDS offsets, the same every chunk
+    int kq_base[4];                            // row 16 x + l16, d-chunk lg
+#pragma unroll
+    for (int x = 0; x < 4; ++x) kq_base[x] = LK::chunk(16 * x + l16, lg);
+    // transposing reads: lane 4 j + m of a 16-lane group reads row base + j,
+    // 4 columns starting at 4 m of the wanted column block
+    const int trj = l16 >> 2, trm = l16 & 3;
+    int ktr_base[RT];                          // K rows 4 lg + j (+ 16 J), d = phys_row(16 rt + 4 m)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int d0 = phys_row(16 * rt + 4 * trm);
+        ktr_base[rt] = LK::chunk(4 * lg + trj, d0 >> 3) + 2 * (d0 & 7);
+    }
+    constexpr int KJ = 16 * DK * 2 + (16 / LK::G) * LK::PAD;   // 16 K rows further
+    const int vc = 16 * wave + 4 * trm;
+    const int vtr_base = LC::chunk(4 * lg + trj, vc >> 3) + 2 * (vc & 7);
+    constexpr int VJ = 16 * CH * 2 + (16 / LC::G) * LC::PAD;   // 16 V rows further
+    // 8-byte fragments of T and A: row 16 x + l16, columns 16 J + 4 lg .. + 3.
+    // The row's 16-byte chunks are XOR-permuted by (row & 3), which swaps
+    // column blocks J and J ^ 1 on some rows, so each row tile keeps the
+    // offsets of blocks 0 and 1; blocks 2 and 3 are 64 bytes further.
+    int tn_off[4][2];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int J = 0; J < 2; ++J)
+            tn_off[x][J] = LC::chunk(16 * x + l16, 2 * J + (lg >> 1)) + 8 * (lg & 1);
+    auto tn = [&](int x, int J) { return tn_off[x][J & 1] + 64 * (J >> 1); };
+    const unsigned ostride = (unsigned)(H * DV);
+    E* const Ocol = O + ((size_t)b * T * H + h) * DV + tile * TV + 16 * wave + 4 * lg;
+
+    lds_barrier();   // B1 of the preparation of chunk 0
+    lds_barrier();   // B0: chunk 0 ready
+    for (int c = 0; c < NC; ++c) {
+        const int t0 = c * CH;
+        const int n = min(CH, T - t0);
+        const char* B = smem + (c & 1) * L::BUF;
+        const char* Kb = B + L::OFF_K;
+        const char* Qb = B + L::OFF_Q;
+        const char* Vb = B + L::OFF_V;
+        const char* Tb = B + L::OFF_T;
+        const char* Ab = B + L::OFF_A;
+        const float* vec = reinterpret_cast<const float*>(B + L::OFF_VEC);
+
+        // (1) X = K [S | M]
+        f32x4 R[4];
+        {
+            f32x4 xs[4], xm[4];
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) xs[ct] = xm[ct] = zero4();
+#pragma unroll
+            for (int s = 0; s < SK; ++s) {
+                const auto bS = MM::from_acc(Sa, s);
+                const auto bM = MM::from_acc(Ma, s);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    const auto aK = *reinterpret_cast<const MM::frag*>(Kb + kq_base[ct] + 64 * s);
+                    xs[ct] = MM::mma(aK, bS, xs[ct]);
+                    xm[ct] = MM::mma(aK, bM, xm[ct]);
+                }
+            }
+            // (2) R = V - Diag(abar) K S0 + Diag(alpha b^-) K M0, rows 16 ct + 4 lg + r
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                const int p0 = 16 * ct + 4 * lg;
+                const f32x4 ab = *reinterpret_cast<const f32x4*>(vec + V_ABAR * CH + p0);
+                const f32x4 ab1 = *reinterpret_cast<const f32x4*>(vec + V_AB1 * CH + p0);
+                const bf16x4 vv = lds_read_tr4(Vb + vtr_base + ct * VJ);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    R[ct][r] = static_cast<float>(vv[r]) - ab[r] * xs[ct][r] + ab1[r] * xm[ct][r];
+            }
+        }
+        // (3) O^T = S0^T Q^T Diag(abar) - M0^T Q^T Diag(b) + Vt^T A^T, its
+        //     entry-state part now (it needs nothing the helpers produce);
+        //     lane: output row 16 ct + l16, columns 4 lg .. + 3 of this
+        //     wavefront's 16
+        f32x4 Ot[4];
+        {
+            f32x4 ys[4], ym[4];
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) ys[ct] = ym[ct] = zero4();
+#pragma unroll
+            for (int s = 0; s < SK; ++s) {
+                const auto bS = MM::from_acc(Sa, s);
+                const auto bM = MM::from_acc(Ma, s);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    const auto aQ = *reinterpret_cast<const MM::frag*>(Qb + kq_base[ct] + 64 * s);
+                    ys[ct] = MM::mma(bS, aQ, ys[ct]);
+                    ym[ct] = MM::mma(bM, aQ, ym[ct]);
+                }
+            }
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                const float ab = vec[V_ABAR * CH + 16 * ct + l16];
+                const float bb = vec[V_B * CH + 16 * ct + l16];
+                Ot[ct] = ab * ys[ct] - bb * ym[ct];
+            }
+        }
+        lds_barrier();   // B1
+
+        // (4) Vt = L^{-1} R by block substitution
+        f32x4 Vt[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const bf16x4 dI = *reinterpret_cast<const bf16x4*>(Tb + tn(I, I));
+            Vt[I] = mma16(dI, to_bf4(R[I]), zero4());
+            const bf16x4 vI = to_bf4(Vt[I]);
+#pragma unroll
+            for (int I2 = I + 1; I2 < 4; ++I2) {
+                const bf16x4 nIJ = *reinterpret_cast<const bf16x4*>(Tb + tn(I2, I));
+                R[I2] = mma16(nIJ, vI, R[I2]);
+            }
+        }
+
+        // ... and its chunk-local part, over the blocks J <= ct of A's row
+        //     tile ct; blocks 2 p and 2 p + 1 together make one 16x16x32 step
+        //     (k = their 32 rows), a lone block a 16x16x16 one
+        {
+            bf16x4 vb[4];
+#pragma unroll
+            for (int J = 0; J < 4; ++J) vb[J] = to_bf4(Vt[J]);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+                for (int p = 0; 2 * p <= ct; ++p) {
+                    const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(Ab + tn(ct, 2 * p));
+                    if (2 * p + 1 <= ct) {
+                        const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(Ab + tn(ct, 2 * p + 1));
+                        Ot[ct] = MM::mma(cat8(vb[2 * p], vb[2 * p + 1]), cat8(a0, a1), Ot[ct]);
+                    } else {
+                        Ot[ct] = mma16(vb[2 * p], a0, Ot[ct]);
+                    }
+                }
+            }
+        }
+        {
+            E* Ob = Ocol + (size_t)t0 * ostride;
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+                if (16 * ct + l16 < n)
+                    store4<E>(Ob + (unsigned)(16 * ct + l16) * ostride, Ot[ct][0], Ot[ct][1],
+                              Ot[ct][2], Ot[ct][3]);
+        }
+
+        // (5) S' = abar_n S0 - b_n M0 + K^T Diag(eta gamma_n) Vt,
+        //     M' = mubar_n M0 - K^T Diag(eta mubar_n / mubar) Vt
+        const float abn = vec[V_SCAL * CH + 0];
+        const float bn = vec[V_SCAL * CH + 1];
+        const float mbn = vec[V_SCAL * CH + 2];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            Sa[rt] = abn * Sa[rt] - bn * Ma[rt];
+            Ma[rt] = mbn * Ma[rt];
+        }
+        // K^T fragments by transposing reads, two 16-row blocks of the chunk
+        // per 16x16x32 step (k = chunk rows 32 p .. 32 p + 31)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            bf16x4 bS[2], bM[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int J = 2 * p + e;
+                const f32x4 ws = *reinterpret_cast<const f32x4*>(vec + V_WS * CH + 16 * J + 4 * lg);
+                const f32x4 wm = *reinterpret_cast<const f32x4*>(vec + V_WM * CH + 16 * J + 4 * lg);
+                bS[e] = to_bf4(ws * Vt[J]);
+                bM[e] = to_bf4(-(wm * Vt[J]));
+            }
+            const auto bS8 = cat8(bS[0], bS[1]), bM8 = cat8(bM[0], bM[1]);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const auto aK = cat8(lds_read_tr4(Kb + ktr_base[rt] + 2 * p * KJ),
+                                     lds_read_tr4(Kb + ktr_base[rt] + (2 * p + 1) * KJ));
+                Sa[rt] = MM::mma(aK, bS8, Sa[rt]);
+                Ma[rt] = MM::mma(aK, bM8, Ma[rt]);
+            }
+        }
+        lds_barrier();   // B0: chunk c + 1 ready, this buffer free
+    }
+
+    auto store_state = [&](float* dst, const f32x4* X) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dst[sbase + (size_t)phys_row(16 * rt + 4 * lg + r) * DV + col] = X[rt][r];
+    };
+    if (ST) store_state(ST, Sa);
+    if (MT) store_state(MT, Ma);
+}
+
+template <int DK, int DV>
+static hipError_t launch_fused_t(const void* q, const void* k, const void* v, const float* alpha,
+                                 const float* mu, const float* eta, const float* S0,
+                                 const float* M0, void* O, float* ST, float* MT, int B, int T,
+                                 int H, void* workspace, hipStream_t stream)
+{
+    const int NC = (T + CH - 1) / CH;
+    const size_t nchunks = (size_t)B * H * NC;
+    float* ctab = static_cast<float*>(workspace);
+    hipLaunchKernelGGL(chunk_coef_kernel, dim3((unsigned)((nchunks + 3) / 4)), dim3(NT), 0, stream,
+                       alpha, mu, eta, ctab, T, H, NC, nchunks);
+    const size_t nblk = (size_t)B * H * (DV / 64);
+    const int xcd_groups = nblk % 8 == 0 ? (int)(nblk / 8) : 0;
+    hipLaunchKernelGGL((chunk_fwd_fused_kernel<DK, DV>), dim3((unsigned)nblk), dim3(2 * NT), 0,
+                       stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                       static_cast<const __bf16*>(v), ctab, S0, M0, static_cast<__bf16*>(O), ST,
+                       MT, T, H, NC, xcd_groups);
+    return hipGetLastError();
+}
+
+// The whole bf16 forward for T >= 1: the coefficient kernel, then the fused
+// kernel.  `workspace` holds chunk_fused_workspace_bytes(B * H * ceil(T / 64)).
+hipError_t launch_chunk_fused(const void* q, const void* k, const void* v, const float* alpha,
+                              const float* mu, const float* eta, const float* S0, const float* M0,
+                              void* O, float* ST, float* MT, int B, int T, int H, int Dk, int Dv,
+                              void* workspace, hipStream_t stream)
+{
+    if (Dk == 128 && Dv == 128)
+        return launch_fused_t<128, 128>(q, k, v, alpha, mu, eta, S0, M0, O, ST, MT, B, T, H,
+                                        workspace, stream);
+    if (Dk == 128 && Dv == 64)
+        return launch_fused_t<128, 64>(q, k, v, alpha, mu, eta, S0, M0, O, ST, MT, B, T, H,
+                                       workspace, stream);
+    if (Dk == 64 && Dv == 128)
+        return launch_fused_t<64, 128>(q, k, v, alpha, mu, eta, S0, M0, O, ST, MT, B, T, H,
+                                       workspace, stream);
+    return launch_fused_t<64, 64>(q, k, v, alpha, mu, eta, S0, M0, O, ST, MT, B, T, H, workspace,
+                                  stream);
+}
+
+}  // namespace mdn

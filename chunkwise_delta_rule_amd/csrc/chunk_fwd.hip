@@ -37,21 +37,10 @@
 //                      into the next products directly from the accumulators.
 #include <hip/hip_runtime.h>
 
+#include "chunk_common.hpp"
 #include "mfma.hpp"
 
 namespace mdn {
-
-constexpr int CH = 64;    // chunk length
-constexpr int NT = 256;   // threads per workgroup (4 wavefronts)
-constexpr int NVEC = 8;   // coefficient vectors per chunk in the workspace
-
-// coefficient vector rows (each CH floats)
-constexpr int V_ABAR = 0;   // abar_i                      (rows >= n: 0)
-constexpr int V_AB1 = 1;    // alpha_i b_{i-1}             (rows >= n: 0)
-constexpr int V_B = 2;      // b_i                         (rows >= n: 0)
-constexpr int V_WS = 3;     // eta_j gamma_{n,j}           (cols >= n: 0)
-constexpr int V_WM = 4;     // eta_j prod_{u=j+1}^{n} mu_u (cols >= n: 0)
-constexpr int V_SCAL = 5;   // [abar_n, b_n, mubar_n]      (n = rows in this chunk)
 
 template <typename E>
 struct Workspace {
@@ -622,78 +611,6 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(
     if (MT) store_state(MT, Ma);
 }
 
-__device__ __forceinline__ int phys_row(int slot)
-{
-    const int q = slot & 31;
-    return (slot & ~31) + 8 * ((q & 15) >> 2) + 4 * (q >> 4) + (q & 3);
-}
-
-// One direct global-to-LDS load of 16 bytes per lane: lane l's bytes land at
-// lds_base + 16 l (lds_base is wave-uniform).
-__device__ __forceinline__ void direct_load16(const void* gsrc, void* lds_base)
-{
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
-                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
-
-// LDS layout of a 64-row bf16 tile with ROWB bytes per row (128 or 256).
-// Rows are unpadded; every 1 KB group of rows (one direct load of 64 lanes x
-// 16 bytes) is followed by PAD bytes, and inside a row the 16-byte chunks are
-// XOR-permuted by (row & 3).  A fragment read by 16 lanes of rows
-// phys_row(16 x + l16) -- rows r0 + {0..3, 8..11} or r0 + {4..7, 12..15} --
-// then touches 8 distinct 16-byte bank groups per 8 lanes, and the address of
-// step s is a per-row base plus 64 s bytes (an instruction immediate).
-template <int ROWB>
-struct TileLayout {
-    static constexpr int G = 1024 / ROWB;               // rows per 1 KB group
-    static constexpr int PAD = ROWB == 256 ? 32 : 64;   // bytes after each group
-    static constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
-    static constexpr int BYTES = CH * ROWB + (CH / G) * PAD;
-    __device__ __forceinline__ static int row_base(int row)
-    {
-        return row * ROWB + (row / G) * PAD;
-    }
-    // byte offset of 16-byte logical chunk qc of row
-    __device__ __forceinline__ static int chunk(int row, int qc)
-    {
-        return row_base(row) + 16 * (qc ^ (row & 3));
-    }
-    // Direct loads of rows [0, 64) of a row-major global tile (row stride in
-    // elements) for wavefront `wave` of 4: instruction u fills group
-    // 4 u + wave.  Since a group holds a multiple of 4 rows, the swizzle of a
-    // lane's row depends on the lane only, so each lane's source offset is
-    // one constant plus a wave-uniform group offset.  Rows >= n (a partial
-    // last chunk) read row n - 1 instead.
-    __device__ __forceinline__ static unsigned lane_offset(unsigned row_stride, int lane)
-    {
-        const int r = lane / CPR;
-        return (unsigned)r * row_stride + 8u * (unsigned)((lane % CPR) ^ (r & 3));
-    }
-    __device__ __forceinline__ static void load(char* lds, const __bf16* __restrict__ g,
-                                                unsigned row_stride, unsigned lane_off, int n,
-                                                int wave, int lane)
-    {
-        constexpr int GROUPS = CH / G;
-        static_assert(GROUPS % 4 == 0 && G % 4 == 0, "groups must split over 4 wavefronts");
-        if (n == CH) {
-#pragma unroll
-            for (int u = 0; u < GROUPS / 4; ++u) {
-                const int grp = 4 * u + wave;
-                direct_load16(g + (unsigned)(grp * G) * row_stride + lane_off,
-                              lds + grp * (1024 + PAD));
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < GROUPS / 4; ++u) {
-                const int grp = 4 * u + wave;
-                const int row = grp * G + lane / CPR;
-                const unsigned srow = (unsigned)min(row, n - 1);
-                direct_load16(g + srow * row_stride + 8 * ((lane % CPR) ^ (row & 3)),
-                              lds + grp * (1024 + PAD));
-            }
-        }
-    }
-};
 
 // ---------------------------------------------------------------------------
 // bf16 scan.  Same mathematics and column ownership as chunk_scan_kernel;
@@ -823,10 +740,10 @@ __global__ __launch_bounds__(2 * NT) void chunk_scan_bf16_kernel(
             }
         };
         stage(0, 0);
-        __syncthreads();
+        lds_barrier();
         for (int c = 0; c < NC; ++c) {
             if (c + 1 < NC) stage(c + 1, (c + 1) & 1);
-            __syncthreads();
+            lds_barrier();
         }
         return;
     }
@@ -862,7 +779,7 @@ __global__ __launch_bounds__(2 * NT) void chunk_scan_bf16_kernel(
     const unsigned ostride = (unsigned)(H * DV);
     E* const Ocol = O + ((size_t)b * T * H + h) * DV + tile * TV + 16 * wave + 4 * lg;
 
-    __syncthreads();                           // chunk 0 staged
+    lds_barrier();                           // chunk 0 staged
     for (int c = 0; c < NC; ++c) {
         const int t0 = c * CH;
         const int n = min(CH, T - t0);
@@ -994,7 +911,7 @@ __global__ __launch_bounds__(2 * NT) void chunk_scan_bf16_kernel(
             }
         }
         // this chunk's buffer is free and the next one is staged
-        __syncthreads();
+        lds_barrier();
     }
 
     auto store_state = [&](float* dst, const f32x4* X) {

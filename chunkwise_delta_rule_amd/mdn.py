@@ -35,7 +35,8 @@ STATUS_NAMES = {
 }
 
 # every symbol include/libmdn.h declares
-EXPORTED = ("mdn_chunk_fwd_workspace_bytes", "mdn_chunk_fwd", "mdn_chunk_fwd_prepare",
+EXPORTED = ("mdn_chunk_fwd_workspace_bytes", "mdn_chunk_fwd_split_workspace_bytes",
+            "mdn_chunk_fwd", "mdn_chunk_fwd_prepare",
             "mdn_chunk_fwd_scan", "mdn_decode_step", "mdn_status_string")
 
 
@@ -60,6 +61,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.mdn_chunk_fwd_workspace_bytes.restype = S
     lib.mdn_chunk_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.mdn_chunk_fwd_split_workspace_bytes.restype = S
+    lib.mdn_chunk_fwd_split_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.mdn_chunk_fwd.restype = I
     lib.mdn_chunk_fwd.argtypes = [P] * 11 + [I] * 7 + [P, S, P]
     lib.mdn_chunk_fwd_prepare.restype = I
@@ -105,9 +108,12 @@ def _stream(device: torch.device) -> int:
 
 
 def workspace_bytes(B: int, T: int, H: int, Dk: int, Dv: int, dtype: torch.dtype,
-                    chunk: int = CHUNK) -> int:
-    return int(load_library().mdn_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk,
-                                                             _dtype_code(dtype)))
+                    chunk: int = CHUNK, split: bool = False) -> int:
+    """Workspace bytes of mdn_chunk_fwd (split=False) or of the
+    mdn_chunk_fwd_prepare / mdn_chunk_fwd_scan pair (split=True)."""
+    lib = load_library()
+    fn = lib.mdn_chunk_fwd_split_workspace_bytes if split else lib.mdn_chunk_fwd_workspace_bytes
+    return int(fn(B, T, H, Dk, Dv, chunk, _dtype_code(dtype)))
 
 
 def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
@@ -175,7 +181,7 @@ class ChunkPlan:
         self.O = torch.empty((B, T, H, Dv), dtype=q.dtype, device=dev)
         self.S_T = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev) if final_state else None
         self.M_T = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev) if final_state else None
-        need = int(self.lib.mdn_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, self.code))
+        need = int(self.lib.mdn_chunk_fwd_split_workspace_bytes(B, T, H, Dk, Dv, chunk, self.code))
         self.workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
         self.ws_bytes = need
         # one full call validates every argument (and fills the outputs)

@@ -63,13 +63,27 @@ typedef enum {
 } mdn_dtype;
 
 /*
- * Bytes of device workspace mdn_chunk_fwd needs for this problem (per-chunk
- * coefficient vectors and the chunk-local matrices T and A of the slides'
- * Eqs. (15)-(18) and (40)-(42)).  Returns 0 for unsupported or invalid sizes
- * and when no work is needed (B, T or H is 0).
+ * Bytes of device workspace mdn_chunk_fwd needs for this problem.  With
+ * dt = MDN_BF16 the forward keeps the chunk-local matrices T and A on chip
+ * and needs only per-chunk coefficient tables (8704 bytes per chunk of 64
+ * tokens and head: the gates, the block products and boundary values of
+ * the slides' Gamma of Eqs. (7)-(9), its 16 x 16 diagonal blocks and the
+ * six coefficient rows the scan reads).  With MDN_F32 it runs as the two
+ * phases below and needs what mdn_chunk_fwd_split_workspace_bytes returns.
+ * Returns 0 for unsupported or invalid sizes and when no work is needed
+ * (B, T or H is 0).
  */
 size_t mdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
                                      mdn_dtype dt);
+
+/*
+ * Bytes of device workspace the split entry points mdn_chunk_fwd_prepare /
+ * mdn_chunk_fwd_scan exchange: per chunk the coefficient vectors and the
+ * chunk-local matrices T = L^{-1} and A of the slides' Eqs. (15)-(18) and
+ * (40)-(42).  0 for unsupported or invalid sizes and when B, T or H is 0.
+ */
+size_t mdn_chunk_fwd_split_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
+                                           mdn_dtype dt);
 
 /*
  * Chunkwise MDN forward over T tokens.
@@ -98,23 +112,26 @@ mdn_status mdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          hipStream_t stream);
 
 /*
- * The two phases mdn_chunk_fwd runs, exported so that a caller can time them
- * separately or run the chunk-local phase ahead of the scan (for instance on
- * another stream).  The reading notes on the MDN paper (Sec. 2.4) point out
+ * The forward as two separate phases, for callers that want to run the
+ * chunk-local phase ahead of the scan (for instance on another stream) or
+ * time them apart.  The reading notes on the MDN paper (Sec. 2.4) point out
  * that T = [I + (P Khat^T) o Gamma^-]^{-1} and the scalar coefficients depend
  * only on chunk-local inputs, while the carried state enters afterwards; the
- * split follows that.  mdn_chunk_fwd(...) is exactly
- *   mdn_chunk_fwd_prepare(...) followed by mdn_chunk_fwd_scan(...)
- * on one stream with one workspace.
+ * split follows that.  mdn_chunk_fwd_prepare(...) followed by
+ * mdn_chunk_fwd_scan(...) on one stream with one workspace computes what
+ * mdn_chunk_fwd(...) computes (for MDN_F32 it is exactly how mdn_chunk_fwd
+ * runs; for MDN_BF16 mdn_chunk_fwd runs a coefficient kernel and one fused
+ * kernel that evaluate the same equations, so the two agree to rounding,
+ * not bit for bit).
  *
  * mdn_chunk_fwd_prepare: per chunk, the coefficients (abar, mubar, b, Gamma;
  *   slides Eqs. (7)-(9)), T = L^{-1} (Eqs. (15)-(18)) and
  *   A = (Q Khat^T) o Gamma (Eqs. (40)-(42)), written to `workspace`.
  *   Reads q, k and the gates only (layouts as for mdn_chunk_fwd; Dk is the
  *   head size of q and k).  The workspace must hold at least
- *   mdn_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, dt) bytes for the Dv
- *   the scan will use (the size does not depend on Dk or Dv) and must not
- *   overlap any input.  T = 0, B = 0 or H = 0: nothing is launched.
+ *   mdn_chunk_fwd_split_workspace_bytes(B, T, H, Dk, Dv, chunk, dt) bytes
+ *   (the size does not depend on Dk or Dv) and must not overlap any input.
+ *   T = 0, B = 0 or H = 0: nothing is launched.
  *
  * mdn_chunk_fwd_scan: the sequential part (residuals, outputs and the
  *   carried state pair), reading q, k, v, S0/M0 and the workspace a previous

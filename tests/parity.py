@@ -47,6 +47,22 @@ def gpu_forward(inp, mu=None, S0=None, M0=None, io=None):
     return to_np(O), to_np(ST), to_np(MT)
 
 
+def split_forward(inp, io=None):
+    """The same forward through the two exported phases (prepare, then scan)."""
+    io = io or inp["cfg"].io_dtype
+    dt = TORCH_DT[io]
+    plan = mdn.ChunkPlan(to_dev(inp["q"], dt), to_dev(inp["k"], dt), to_dev(inp["v"], dt),
+                         to_dev(inp["alpha"]), to_dev(inp["mu"]), to_dev(inp["eta"]),
+                         to_dev(inp["S0"]), to_dev(inp["M0"]))
+    plan.O.fill_(float("nan"))
+    plan.S_T.fill_(float("nan"))
+    plan.M_T.fill_(float("nan"))
+    plan.prepare()
+    plan.scan()
+    torch.cuda.synchronize()
+    return to_np(plan.O), to_np(plan.S_T), to_np(plan.M_T)
+
+
 def gather_heads(x, pairs, state=False):
     """Stack the (b, h) pairs of a [B, T, H, ...] (or [B, H, ...] state)
     array along a new head axis of a batch of one."""

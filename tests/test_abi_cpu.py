@@ -45,15 +45,23 @@ def test_status_strings(lib):
 
 def test_workspace_bytes(lib):
     ws = lib.mdn_chunk_fwd_workspace_bytes
+    split = lib.mdn_chunk_fwd_split_workspace_bytes
     # per chunk: T and A (C x C in the I/O dtype) and 8 coefficient vectors
     per_bf16 = 2 * 64 * 64 * 2 + 8 * 64 * 4
     per_f32 = 2 * 64 * 64 * 4 + 8 * 64 * 4
-    assert ws(8, 4096, 16, 128, 128, 64, mdn.MDN_BF16) == 8 * 16 * 64 * per_bf16
-    assert ws(1, 65, 2, 64, 64, 64, mdn.MDN_F32) == 2 * 2 * per_f32      # ragged: 2 chunks
-    assert ws(1, 1, 1, 64, 128, 64, mdn.MDN_BF16) == per_bf16
+    assert split(8, 4096, 16, 128, 128, 64, mdn.MDN_BF16) == 8 * 16 * 64 * per_bf16
+    assert split(1, 65, 2, 64, 64, 64, mdn.MDN_F32) == 2 * 2 * per_f32     # ragged: 2 chunks
+    assert split(1, 1, 1, 64, 128, 64, mdn.MDN_BF16) == per_bf16
+    # the bf16 forward keeps T and A on chip and needs only per-chunk coefficient
+    # tables (gates, block products, boundary values, Gamma's diagonal blocks,
+    # six coefficient rows: 2176 floats); fp32 uses the split path
+    assert ws(8, 4096, 16, 128, 128, 64, mdn.MDN_BF16) == 8 * 16 * 64 * 2176 * 4
+    assert ws(1, 65, 2, 64, 64, 64, mdn.MDN_BF16) == 2 * 2 * 2176 * 4
+    assert ws(1, 65, 2, 64, 64, 64, mdn.MDN_F32) == 2 * 2 * per_f32
     for bad in [(0, 64, 1, 64, 64, 64, 1), (1, 0, 1, 64, 64, 64, 1), (1, 64, 1, 96, 64, 64, 1),
                 (1, 64, 1, 64, 64, 32, 1), (1, 64, 1, 64, 64, 64, 7), (-1, 64, 1, 64, 64, 64, 1)]:
         assert ws(*bad) == 0
+        assert split(*bad) == 0
 
 
 # fake, 16-byte aligned, non-overlapping "device" addresses
@@ -91,11 +99,13 @@ def call_fwd(lib, a):
     (dict(O=None), "MDN_ERR_NULL"),
     (dict(k=fake(1, 8)), "MDN_ERR_ALIGN"),
     (dict(S_T=fake(9, 4)), "MDN_ERR_ALIGN"),
+    (dict(ws=None, dt=mdn.MDN_F32), "MDN_ERR_WORKSPACE"),
+    (dict(wsb=1000, dt=mdn.MDN_F32), "MDN_ERR_WORKSPACE"),
     (dict(ws=None), "MDN_ERR_WORKSPACE"),
     (dict(wsb=1000), "MDN_ERR_WORKSPACE"),
     (dict(O=fake(0)), "MDN_ERR_ALIAS"),                 # output over q
     (dict(O=fake(2, 4096)), "MDN_ERR_ALIAS"),           # output inside v
-    (dict(ws=fake(8)), "MDN_ERR_ALIAS"),                # workspace over output
+    (dict(ws=fake(8), dt=mdn.MDN_F32), "MDN_ERR_ALIAS"),  # workspace over output
     (dict(S_T=fake(7)), "MDN_ERR_ALIAS"),               # final memory over initial momentum
     (dict(S_T=fake(6, 16)), "MDN_ERR_ALIAS"),           # shifted, not exactly in place
     (dict(M_T=fake(9)), "MDN_ERR_ALIAS"),               # both final states at one address

@@ -184,7 +184,9 @@ def test_bad_arguments_raise():
     with pytest.raises(mdn.MdnError) as ex:
         mdn.chunk_fwd(q, q, q, g, g, g, O=q)           # output over the inputs
     assert ex.value.status == 5
+    # the bf16 forward needs no workspace; the fp32 one (two phases) does
+    qf = to_dev(inp["q"], torch.float32)
     with pytest.raises(mdn.MdnError) as ex:
-        mdn.chunk_fwd(q, q, q, g, g, g, workspace=torch.empty(16, dtype=torch.uint8,
-                                                             device="cuda"))
+        mdn.chunk_fwd(qf, qf, qf, g, g, g, workspace=torch.empty(16, dtype=torch.uint8,
+                                                                device="cuda"))
     assert ex.value.status == 6
