@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -44,12 +45,35 @@ def hipcc() -> str:
     return path
 
 
+# Kernels whose explicit vmcnt waits count only their own loads: a register
+# spill would add scratch traffic to the same counter and break those waits,
+# so these must compile without scratch.
+NO_SCRATCH = {"chunk_fused.hip": ("chunk_fwd_fused_kernel",),
+              "chunk_fwd.hip": ("chunk_scan_bf16_kernel",)}
+
+
+def _check_no_scratch(src: str, remarks: str) -> None:
+    names = NO_SCRATCH.get(src, ())
+    current = None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            current = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and current and any(n in current for n in names) and int(m.group(1)) > 0:
+            raise RuntimeError(f"{src}: kernel {current} uses {m.group(1)} bytes/lane of scratch; "
+                               "its vmcnt waits assume it has none")
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")
+    _check_no_scratch(src, res.stderr)
     return obj
 
 
