@@ -54,8 +54,9 @@
 //                 h of A; and it loads the tables of chunk c + 2.  No helper
 //                 waits for another.
 // Two workgroup barriers per chunk: B1 once K, Q of chunk c + 1 are in LDS
-// (the compute wavefronts have done their entry-state products by then), B0
-// once chunk c + 1 is complete.
+// (the compute wavefronts have done their entry-state products by then, the
+// helpers their mask factors from the chunk's tables), B0 once chunk c + 1
+// is complete; one more at the start, for chunk 0's tables.
 #include <hip/hip_runtime.h>
 
 #include "chunk_common.hpp"
@@ -376,50 +377,70 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
             }
         };
 
-        // Row block W of L (-N_{W,J}, J < W, and D_W) into T, column block W
-        // of A into A; W is this helper's index, a compile-time constant in
-        // each copy.
-        auto prepare = [&](auto wc, char* B, const float* tb, auto par) {
+        // Elementwise factors of helper W's Gram tiles, from chunk tables tb
+        // (they need no K, Q, so they are formed before B1):
+        //   mL[J]: -N_{W,J} = mL[J] o G_{W,J} (J < W): -alpha_i eta_j gamma_{i-1,j}
+        //   mT, mB: N_{W,W} in both accumulator layouts (zero on and above the
+        //           diagonal): alpha_i eta_j gamma_{i-1,j}
+        //   mA[I]: A_{I,W} = mA[I] o (Q K^T)_{I,W} (I >= W): eta_j gamma_{i,j}
+        // Lane layout: the transposed tiles' (row 16 I + l16, columns
+        // 16 J + 4 lg + r); mB is N_{W,W}'s own layout (row 16 W + 4 lg + r,
+        // column 16 W + l16).
+        struct Mult {
+            f32x4 mL[3], mT, mB, mA[4];
+        };
+        auto multipliers = [&](auto wc, const float* tb) {
             constexpr int W = decltype(wc)::value;
-            constexpr int P = decltype(par)::value;
             const int l16o = opaque(lane & 15), lgo = opaque(lane >> 4);
-            const char* Kb = B + L::OFF_K;
-            const char* Qb = B + L::OFF_Q;
-            // ---- table values for the masks
+            Mult m;
             const int iL = 16 * W + l16o;
             const float aiL = tb[CTb::ALPHA + iL];
             const float raP = tb[CTb::RA + (l16o > 0 ? iL - 1 : iL)];
             const float rgP = tb[CTb::RG + (l16o > 0 ? iL - 1 : iL)];
-            f32x4 eC[4], gbL[4], mbL[4];        // columns 16 J + 4 lg + r
+            const f32x4 eW = *reinterpret_cast<const f32x4*>(tb + CTb::ETA + 16 * W + 4 * lgo);
 #pragma unroll
-            for (int J = 0; J <= W; ++J) {
-                eC[J] = *reinterpret_cast<const f32x4*>(tb + CTb::ETA + 16 * J + 4 * lgo);
-                if (J < W) {
-                    gbL[J] = *reinterpret_cast<const f32x4*>(tb + CTb::GB + 64 * W + 16 * J + 4 * lgo);
-                    mbL[J] = *reinterpret_cast<const f32x4*>(tb + CTb::MB + 64 * W + 16 * J + 4 * lgo);
+            for (int J = 0; J < W; ++J) {
+                const f32x4 e = *reinterpret_cast<const f32x4*>(tb + CTb::ETA + 16 * J + 4 * lgo);
+                const f32x4 gb = *reinterpret_cast<const f32x4*>(tb + CTb::GB + 64 * W + 16 * J + 4 * lgo);
+                const f32x4 mb = *reinterpret_cast<const f32x4*>(tb + CTb::MB + 64 * W + 16 * J + 4 * lgo);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float g = l16o == 0 ? gb[r] : raP * gb[r] + rgP * mb[r];
+                    m.mL[J][r] = -(aiL * e[r] * g);
                 }
             }
             const f32x4 gdT = *reinterpret_cast<const f32x4*>(
                 tb + CTb::GD + (16 * W + (l16o > 0 ? l16o - 1 : 0)) * 16 + 4 * lgo);
             const f32x4 aD = *reinterpret_cast<const f32x4*>(tb + CTb::ALPHA + 16 * W + 4 * lgo);
             const float eR = tb[CTb::ETA + 16 * W + l16o];
-            float gdB[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = 4 * lgo + r - 1;
-                gdB[r] = tb[CTb::GD + (16 * W + (row > 0 ? row : 0)) * 16 + l16o];
-            }
-            // A column block W: rows 16 I + l16 (I >= W), columns 16 W + 4 lg + r
-            float raA[4], rgA[4];
-            f32x4 gA[4], mA[4];
-#pragma unroll
-            for (int I = W + 1; I < 4; ++I) {
-                raA[I] = tb[CTb::RA + 16 * I + l16o];
-                rgA[I] = tb[CTb::RG + 16 * I + l16o];
-                gA[I] = *reinterpret_cast<const f32x4*>(tb + CTb::GB + 64 * I + 16 * W + 4 * lgo);
-                mA[I] = *reinterpret_cast<const f32x4*>(tb + CTb::MB + 64 * I + 16 * W + 4 * lgo);
+                const int j = 4 * lgo + r;
+                const float gdB = tb[CTb::GD + (16 * W + (j > 0 ? j - 1 : 0)) * 16 + l16o];
+                m.mT[r] = j < l16o ? aiL * eW[r] * gdT[r] : 0.f;
+                m.mB[r] = l16o < j ? aD[r] * eR * gdB : 0.f;
             }
             const f32x4 gdA = *reinterpret_cast<const f32x4*>(tb + CTb::GD + (16 * W + l16o) * 16 + 4 * lgo);
+            m.mA[W] = eW * gdA;
+#pragma unroll
+            for (int I = W + 1; I < 4; ++I) {
+                const float ra = tb[CTb::RA + 16 * I + l16o], rg = tb[CTb::RG + 16 * I + l16o];
+                const f32x4 gb = *reinterpret_cast<const f32x4*>(tb + CTb::GB + 64 * I + 16 * W + 4 * lgo);
+                const f32x4 mb = *reinterpret_cast<const f32x4*>(tb + CTb::MB + 64 * I + 16 * W + 4 * lgo);
+                m.mA[I] = eW * (ra * gb + rg * mb);
+            }
+            return m;
+        };
+
+        // Row block W of L (-N_{W,J}, J < W, and D_W) into T, column block W
+        // of A into A; W is this helper's index, a compile-time constant in
+        // each copy.
+        auto prepare = [&](auto wc, char* B, const Mult& m, auto par) {
+            constexpr int W = decltype(wc)::value;
+            constexpr int P = decltype(par)::value;
+            const int l16o = opaque(lane & 15), lgo = opaque(lane >> 4);
+            const char* Kb = B + L::OFF_K;
+            const char* Qb = B + L::OFF_Q;
             // ---- Gram tiles, transposed (lane: row 16 I + l16, columns 16 J + 4 lg + r)
             f32x4 Gt[W + 1], At[4];
 #pragma unroll
@@ -443,34 +464,12 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
                     At[I] = MM::mma(kf[P][s], bQ, At[I]);
                 }
             }
-            // ---- masks: -N_{W,J} = -alpha_i eta_j G_ij gamma_{i-1,j} (J < W)
-            bf16x4 nOut[4];
-#pragma unroll
-            for (int J = 0; J < W; ++J)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float g = l16o == 0 ? gbL[J][r] : raP * gbL[J][r] + rgP * mbL[J][r];
-                    nOut[J][r] = static_cast<__bf16>(-(aiL * eC[J][r] * Gt[J][r] * g));
-                }
             // N_WW in both accumulator layouts from the symmetric Gram tile:
             // NT = acc(N^T) (lane: row l16, cols 4 lg + r), NB = acc(N)
-            f32x4 NT, NB, Id;
+            const f32x4 NT = m.mT * Gt[W], NB = m.mB * Gt[W];
+            f32x4 Id;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = 4 * lgo + r;
-                NT[r] = j < l16o ? aiL * eC[W][r] * Gt[W][r] * gdT[r] : 0.f;
-                NB[r] = l16o < j ? aD[r] * eR * Gt[W][r] * gdB[r] : 0.f;
-                Id[r] = j == l16o ? 1.f : 0.f;
-            }
-            // A_{I,W} = eta_j QK_ij gamma_{i,j} (j <= i)
-            bf16x4 aOut[4];
-#pragma unroll
-            for (int I = W; I < 4; ++I)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float g = I == W ? gdA[r] : raA[I] * gA[I][r] + rgA[I] * mA[I][r];
-                    aOut[I][r] = static_cast<__bf16>(eC[W][r] * At[I][r] * g);
-                }
+            for (int r = 0; r < 4; ++r) Id[r] = 4 * lgo + r == l16o ? 1.f : 0.f;
             // D_W = (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8) (N^16 = 0),
             // formed transposed: D^T = (I + N8^T)(I + N4^T) P1^T
             const f32x4 N2B = prod(NT, NB), N2T = prod(NB, NT);
@@ -482,69 +481,75 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
             // ---- stores
             char* Tb = B + L::OFF_T;
             char* Ab = B + L::OFF_A;
+            const int iL = 16 * W + l16;
 #pragma unroll
             for (int J = 0; J < W; ++J) {
                 const int j0 = 16 * J + 4 * lg;
-                *reinterpret_cast<bf16x4*>(Tb + LC::chunk(iL, j0 >> 3) + 2 * (j0 & 7)) = nOut[J];
+                *reinterpret_cast<bf16x4*>(Tb + LC::chunk(iL, j0 >> 3) + 2 * (j0 & 7)) =
+                    to_bf4(m.mL[J] * Gt[J]);
             }
             const int j0 = 16 * W + 4 * lg;
-            *reinterpret_cast<bf16x4*>(Tb + LC::chunk(iL, j0 >> 3) + 2 * (j0 & 7)) = to_bf4(DT);
 #pragma unroll
             for (int I = W; I < 4; ++I)
                 *reinterpret_cast<bf16x4*>(Ab + LC::chunk(16 * I + l16, j0 >> 3) + 2 * (j0 & 7)) =
-                    aOut[I];
-        };
-        auto prepare_any = [&](char* B, const float* tb, auto par) {
-            switch (hw) {
-            case 0: prepare(IConst<0>{}, B, tb, par); break;
-            case 1: prepare(IConst<1>{}, B, tb, par); break;
-            case 2: prepare(IConst<2>{}, B, tb, par); break;
-            default: prepare(IConst<3>{}, B, tb, par); break;
-            }
+                    to_bf4(m.mA[I] * At[I]);
+            *reinterpret_cast<bf16x4*>(Tb + LC::chunk(iL, j0 >> 3) + 2 * (j0 & 7)) = to_bf4(DT);
         };
 
         // The pipeline: in round c (c = -1 .. NC - 1) chunk nx = c + 1 is
         // prepared into buffer nx & 1 while the compute wavefronts scan chunk
         // c.  Its K, Q rows were loaded into registers and its tables into
-        // table set nx & 1 in round c - 1.  Per helper and round the loads
-        // are issued as: tables of nx + 1, V tile and coefficient rows of nx,
-        // K, Q rows of nx + 1 (2 SK), so waiting for all but the last 2 SK
-        // covers everything nx needs.
-        auto round = [&](int c, auto par) {      // par: parity of nx
-            constexpr int P = decltype(par)::value;
-            const int nx = c + 1;
-            char* B = smem + P * L::BUF;
-            const float* tb = tables(nx);
-            const bool live = nx < NC, more = nx + 1 < NC;
-            if (live) {
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // K, Q and tables of nx
-                store_kq(nx, B, par);
-                if (more) load_tables(nx + 1);
-                load_v(nx, B);
-                if (more) load_kq(nx + 1, IConst<1 - P>{});
-            }
-            lds_barrier();   // B1: K, Q and the tables of nx visible
-            if (live) {
-                prepare_any(B, tb, par);
-                // the V tile and coefficient rows of nx have landed; the
-                // K, Q loads of nx + 1, issued after them, may still be in
-                // flight
-                if (more) {
-                    if constexpr (SK == 4)
-                        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-                    else
-                        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-                } else {
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // table set nx & 1 in round c - 1 (and waited for before the B0 that
+        // ended it).  Per helper and round the loads are issued as: tables of
+        // nx + 1, V tile and coefficient rows of nx, K, Q rows of nx + 1
+        // (2 SK), so waiting for all but the last 2 SK covers everything nx
+        // needs.
+        auto run = [&](auto wc) {
+            auto round = [&](int c, auto par) {      // par: parity of nx
+                constexpr int P = decltype(par)::value;
+                const int nx = c + 1;
+                char* B = smem + P * L::BUF;
+                const bool live = nx < NC, more = nx + 1 < NC;
+                Mult m;
+                if (live) {
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // K, Q of nx
+                    store_kq(nx, B, par);
+                    if (more) load_tables(nx + 1);
+                    load_v(nx, B);
+                    if (more) load_kq(nx + 1, IConst<1 - P>{});
+                    m = multipliers(wc, tables(nx));
                 }
+                lds_barrier();   // B1: K, Q of nx visible
+                if (live) {
+                    prepare(wc, B, m, par);
+                    // the tables of nx + 1, the V tile and coefficient rows of
+                    // nx have landed; the K, Q loads of nx + 1, issued after
+                    // them, may still be in flight
+                    if (more) {
+                        if constexpr (SK == 4)
+                            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+                        else
+                            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                    } else {
+                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    }
+                }
+                lds_barrier();   // B0: chunk nx ready
+            };
+            load_kq(0, IConst<0>{});
+            load_tables(0);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();       // chunk 0's tables visible
+            for (int c = -1; c < NC; c += 2) {
+                round(c, IConst<0>{});
+                if (c + 1 < NC) round(c + 1, IConst<1>{});
             }
-            lds_barrier();   // B0: chunk nx ready
         };
-        load_kq(0, IConst<0>{});
-        load_tables(0);
-        for (int c = -1; c < NC; c += 2) {
-            round(c, IConst<0>{});
-            if (c + 1 < NC) round(c + 1, IConst<1>{});
+        switch (hw) {
+        case 0: run(IConst<0>{}); break;
+        case 1: run(IConst<1>{}); break;
+        case 2: run(IConst<2>{}); break;
+        default: run(IConst<3>{}); break;
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         return;
@@ -596,6 +601,7 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
     const unsigned ostride = (unsigned)(H * DV);
     E* const Ocol = O + ((size_t)b * T * H + h) * DV + tile * TV + 16 * wave + 4 * lg;
 
+    lds_barrier();   // chunk 0's tables in LDS
     lds_barrier();   // B1 of the preparation of chunk 0
     lds_barrier();   // B0: chunk 0 ready
     for (int c = 0; c < NC; ++c) {
