@@ -259,9 +259,36 @@ __global__ __launch_bounds__(NT) void chunk_coef_kernel(const float* __restrict_
     vec[V_SCAL * CH + lane] = lane == 0 ? abar_n : lane == 1 ? b_n : lane == 2 ? mbar_n : 0.f;
 }
 
+// LDS layout of the K and Q tiles of the fused kernel (64 rows x DK bf16),
+// written by the helpers from registers.  Two reads must be free of bank
+// conflicts (64 banks of 4 bytes; a wavefront's access is served 32 lanes at
+// a time): 16-byte fragments of 16 consecutive rows at one 16-byte chunk, and
+// transposing reads in which each 16-lane group takes four 8-byte pieces from
+// each of 4 consecutive rows, the pieces lying in one 64-byte window of the
+// row.  Rows start 64 bytes apart modulo 256 (a 64-byte gap after every
+// row at DK = 128, after every second row at DK = 64), so 4 consecutive rows
+// fall in 4 different 64-byte bank windows; and the 16-byte chunks of a row
+// are XOR-permuted by bits 2..3 of the row, so 16 consecutive rows spread
+// over the 4 chunks of each window.  The permutation touches chunk-index
+// bits 0..1 only: step s of a fragment read is a fixed 64 s bytes further,
+// and 16 rows further is a fixed J16 bytes further.
+template <int DK>
+struct KQLayout {
+    static constexpr int ROWB = 2 * DK;
+    static constexpr int G = DK == 128 ? 1 : 2;         // rows per gap
+    static constexpr int GAP = 64;
+    static constexpr int BYTES = CH * ROWB + (CH / G) * GAP;
+    static constexpr int J16 = 16 * ROWB + (16 / G) * GAP;
+    static_assert(DK == 64 || DK == 128, "head size");
+    __device__ __forceinline__ static int chunk(int row, int qc)
+    {
+        return row * ROWB + (row / G) * GAP + 16 * (qc ^ ((row >> 2) & 3));
+    }
+};
+
 template <int DK>
 struct FusedLayout {
-    using LK = TileLayout<DK * 2>;          // K, Q: 64 rows x DK
+    using LK = KQLayout<DK>;                // K, Q: 64 rows x DK
     using LC = TileLayout<CH * 2>;          // V tile, T (-N, D), A: 64 rows x 64
     static constexpr int OFF_K = 0;
     static constexpr int OFF_Q = LK::BYTES;
@@ -583,7 +610,7 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
         const int d0 = phys_row(16 * rt + 4 * trm);
         ktr_base[rt] = LK::chunk(4 * lg + trj, d0 >> 3) + 2 * (d0 & 7);
     }
-    constexpr int KJ = 16 * DK * 2 + (16 / LK::G) * LK::PAD;   // 16 K rows further
+    constexpr int KJ = LK::J16;                // 16 K rows further
     const int vc = 16 * wave + 4 * trm;
     const int vtr_base = LC::chunk(4 * lg + trj, vc >> 3) + 2 * (vc & 7);
     constexpr int VJ = 16 * CH * 2 + (16 / LC::G) * LC::PAD;   // 16 V rows further
@@ -689,11 +716,17 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
 
         // ... and its chunk-local part, over the blocks J <= ct of A's row
         //     tile ct; blocks 2 p and 2 p + 1 together make one 16x16x32 step
-        //     (k = their 32 rows), a lone block a 16x16x16 one
+        //     (k = their 32 rows), a lone block a 16x16x32 step with zero
+        //     upper half.  Every step of an accumulator's chain has the same
+        //     shape: an MFMA that takes the result of an MFMA of another
+        //     shape as its accumulator input, with no instruction between,
+        //     has read a stale accumulator on gfx950 (the compiler inserts
+        //     no wait there), and the 16x16x16 form is no faster here.
         {
             bf16x4 vb[4];
 #pragma unroll
             for (int J = 0; J < 4; ++J) vb[J] = to_bf4(Vt[J]);
+            const bf16x4 zb = to_bf4(zero4());
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
@@ -703,7 +736,7 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
                         const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(Ab + tn(ct, 2 * p + 1));
                         Ot[ct] = MM::mma(cat8(vb[2 * p], vb[2 * p + 1]), cat8(a0, a1), Ot[ct]);
                     } else {
-                        Ot[ct] = mma16(vb[2 * p], a0, Ot[ct]);
+                        Ot[ct] = MM::mma(cat8(vb[2 * p], zb), cat8(a0, zb), Ot[ct]);
                     }
                 }
             }
