@@ -51,12 +51,13 @@
 //                 earlier, in MFMA fragment layout) to LDS, the V tile and
 //                 the coefficient rows by direct loads, row block h of the
 //                 Gram product P Khat^T masked into -N and D_h, column block
-//                 h of A; and it loads the tables of chunk c + 2.  No helper
-//                 waits for another.
-// Two workgroup barriers per chunk: B1 once K, Q of chunk c + 1 are in LDS
-// (the compute wavefronts have done their entry-state products by then, the
-// helpers their mask factors from the chunk's tables), B0 once chunk c + 1
-// is complete; one more at the start, for chunk 0's tables.
+//                 h of A; and it loads the tables of chunk c + 2.
+// Synchronisation per chunk: B1, among the helpers only, once K, Q of chunk
+// c + 1 are in LDS (each helper's Gram products read the other helpers'
+// rows; the compute wavefronts need nothing from it), and the workgroup
+// barrier B0 once chunk c + 1 is complete, after which the compute
+// wavefronts move on to it and its buffer stops being written.  One more
+// workgroup barrier at the start, for chunk 0's tables.
 #include <hip/hip_runtime.h>
 
 #include "chunk_common.hpp"
@@ -298,8 +299,10 @@ struct FusedLayout {
     static constexpr int OFF_VEC = OFF_A + LC::BYTES;
     static constexpr int BUF = OFF_VEC + 6 * CH * 4;
     static constexpr int TB_BYTES = ChunkTables::LDS_FLOATS * 4;
-    // two operand buffers, two table sets (chunks of even and odd index)
-    static constexpr int BYTES = 2 * BUF + 2 * TB_BYTES;
+    // two operand buffers, two table sets (chunks of even and odd index),
+    // the helpers' arrival counter
+    static constexpr int OFF_SYNC = 2 * BUF + 2 * TB_BYTES;
+    static constexpr int BYTES = OFF_SYNC + 16;
 };
 
 template <int DK, int DV>
@@ -341,6 +344,8 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
     // token index of row 0 of chunk c of this head (rows are H tokens apart)
     auto tok_base = [&](int c) { return ((size_t)b * T + (size_t)c * CH) * H + h; };
     auto chunk_rows = [&](int c) { return min(CH, T - c * CH); };
+    unsigned* const hsync = reinterpret_cast<unsigned*>(smem + L::OFF_SYNC);
+    if (tid == 0) *hsync = 0u;   // visible to all after the first barrier
 
     if (wave >= 4) {
         // =================== helper wavefronts ===================
@@ -372,11 +377,17 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
         // registers too, so the Gram products, L and A vanish there)
         auto store_kq = [&](int c, char* B, auto par) {
             constexpr int P = decltype(par)::value;
-            const bool live = r0 + l16 < chunk_rows(c);
+            const int n = chunk_rows(c);
+            if (n < CH) {   // the last chunk only
+                const bool live = r0 + l16 < n;
+#pragma unroll
+                for (int u = 0; u < SK; ++u) {
+                    kf[P][u] = live ? kf[P][u] : zfrag;
+                    qf[P][u] = live ? qf[P][u] : zfrag;
+                }
+            }
 #pragma unroll
             for (int u = 0; u < SK; ++u) {
-                kf[P][u] = live ? kf[P][u] : zfrag;
-                qf[P][u] = live ? qf[P][u] : zfrag;
                 const int off = LK::chunk(r0 + l16, 4 * u + lg);
                 *reinterpret_cast<MM::frag*>(B + L::OFF_K + off) = kf[P][u];
                 *reinterpret_cast<MM::frag*>(B + L::OFF_Q + off) = qf[P][u];
@@ -531,23 +542,47 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
         // nx + 1, V tile and coefficient rows of nx, K, Q rows of nx + 1
         // (2 SK), so waiting for all but the last 2 SK covers everything nx
         // needs.
+        // B1, a barrier of the four helpers only (the compute wavefronts do
+        // not need it): an LDS arrival counter that only grows, round r
+        // (r = 0 .. NC) waiting for 4 (r + 1) arrivals.  Each helper's LDS
+        // writes are complete before it arrives.  The wait is bounded, so a
+        // helper that never arrived could not hang the workgroup.
+        // The counter is touched by inline assembly: a plain LDS access there
+        // would make the compiler wait for every outstanding global load
+        // first (it cannot tell the counter from the direct-load targets).
+        const unsigned hsync_addr =
+            (unsigned)(uintptr_t)((__attribute__((address_space(3))) unsigned*)hsync);
+        auto helper_sync = [&](unsigned target) {
+            const unsigned one = 1u;
+            if (lane == 0)
+                asm volatile("s_waitcnt lgkmcnt(0)\n\tds_add_u32 %0, %1"
+                             :: "v"(hsync_addr), "v"(one) : "memory");
+            for (int spin = 0; spin < (1 << 22); ++spin) {
+                unsigned v;
+                asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                             : "=v"(v) : "v"(hsync_addr) : "memory");
+                if (__builtin_amdgcn_readfirstlane(v) >= target) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+        };
         auto run = [&](auto wc) {
             auto round = [&](int c, auto par) {      // par: parity of nx
                 constexpr int P = decltype(par)::value;
                 const int nx = c + 1;
                 char* B = smem + P * L::BUF;
-                const bool live = nx < NC, more = nx + 1 < NC;
-                Mult m;
-                if (live) {
+                const unsigned arrivals = 4u * (unsigned)(c + 2);
+                // one branch for both halves of a live round, so that the
+                // compiler sees prepare() reached only through the wait below
+                // (a path around it would make it wait for every load)
+                if (nx < NC) {
+                    const bool more = nx + 1 < NC;
                     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // K, Q of nx
                     store_kq(nx, B, par);
                     if (more) load_tables(nx + 1);
                     load_v(nx, B);
                     if (more) load_kq(nx + 1, IConst<1 - P>{});
-                    m = multipliers(wc, tables(nx));
-                }
-                lds_barrier();   // B1: K, Q of nx visible
-                if (live) {
+                    const Mult m = multipliers(wc, tables(nx));
+                    helper_sync(arrivals);   // B1: K, Q of nx visible
                     prepare(wc, B, m, par);
                     // the tables of nx + 1, the V tile and coefficient rows of
                     // nx have landed; the K, Q loads of nx + 1, issued after
@@ -560,6 +595,8 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
                     } else {
                         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                     }
+                } else {
+                    helper_sync(arrivals);
                 }
                 lds_barrier();   // B0: chunk nx ready
             };
@@ -629,7 +666,6 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
     E* const Ocol = O + ((size_t)b * T * H + h) * DV + tile * TV + 16 * wave + 4 * lg;
 
     lds_barrier();   // chunk 0's tables in LDS
-    lds_barrier();   // B1 of the preparation of chunk 0
     lds_barrier();   // B0: chunk 0 ready
     for (int c = 0; c < NC; ++c) {
         const int t0 = c * CH;
@@ -698,7 +734,6 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
                 Ot[ct] = ab * ys[ct] - bb * ym[ct];
             }
         }
-        lds_barrier();   // B1
 
         // (4) Vt = L^{-1} R by block substitution
         f32x4 Vt[4];
