@@ -99,6 +99,31 @@ __device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b)
 {
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
+__device__ __forceinline__ bf16x4 lo4(const bf16x8& v) { return bf16x4{v[0], v[1], v[2], v[3]}; }
+__device__ __forceinline__ bf16x4 hi4(const bf16x8& v) { return bf16x4{v[4], v[5], v[6], v[7]}; }
+
+// LDS placement of the 16x16 blocks (x, J), J <= x, of T (-N below the block
+// diagonal, D on it) and of A.  A block is stored in the lane order of the
+// MFMA operand that reads it -- lane (l16, g) holds row 16 x + l16, columns
+// 16 J + 4 g .. + 3, 8 bytes -- which is also the lane order of the helper
+// accumulator that produces it, so every access is linear and free of bank
+// conflicts.  Blocks read together share a 16-byte lane slot of a 1 KB pair
+// area: (1,0|1,1), (2,0|2,1), (3,0|3,1), (3,2|3,3); the lone blocks (0,0) and
+// (2,2) have 8-byte slots, 640 bytes apart, so that a read of both merged
+// into one instruction reaches different banks.
+struct FragSlot {
+    int off;      // byte offset of lane 0's 8 bytes
+    int stride;   // bytes from lane to lane
+};
+__host__ __device__ constexpr FragSlot frag_slot(int x, int J)
+{
+    return x == 0                ? FragSlot{4096, 8}
+           : (x == 2 && J == 2) ? FragSlot{4096 + 640, 8}
+                                : FragSlot{1024 * (x == 1 ? 0 : x == 2 ? 1 : J < 2 ? 2 : 3) + 8 * (J & 1), 16};
+}
+// bytes of one T or A area; 128 more than a multiple of 512, so that T and
+// A blocks at equal offsets are never merged into one two-address access
+constexpr int FRAG_AREA = 4096 + 640 + 512;
 
 __device__ __forceinline__ bf16x4 to_bf4(const f32x4& x)
 {
@@ -295,8 +320,8 @@ struct FusedLayout {
     static constexpr int OFF_Q = LK::BYTES;
     static constexpr int OFF_V = 2 * LK::BYTES;
     static constexpr int OFF_T = OFF_V + LC::BYTES;
-    static constexpr int OFF_A = OFF_T + LC::BYTES;
-    static constexpr int OFF_VEC = OFF_A + LC::BYTES;
+    static constexpr int OFF_A = OFF_T + FRAG_AREA;
+    static constexpr int OFF_VEC = OFF_A + FRAG_AREA;
     static constexpr int BUF = OFF_VEC + 6 * CH * 4;
     static constexpr int TB_BYTES = ChunkTables::LDS_FLOATS * 4;
     // two operand buffers, two table sets (chunks of even and odd index),
@@ -519,19 +544,27 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
             // ---- stores
             char* Tb = B + L::OFF_T;
             char* Ab = B + L::OFF_A;
-            const int iL = 16 * W + l16;
+            // T row block W: -N_{W,J} (J < W) and D_W; pairs (J, J + 1) as
+            // one 16-byte store
+            bf16x4 tW[W + 1];
 #pragma unroll
-            for (int J = 0; J < W; ++J) {
-                const int j0 = 16 * J + 4 * lg;
-                *reinterpret_cast<bf16x4*>(Tb + LC::chunk(iL, j0 >> 3) + 2 * (j0 & 7)) =
-                    to_bf4(m.mL[J] * Gt[J]);
+            for (int J = 0; J < W; ++J) tW[J] = to_bf4(m.mL[J] * Gt[J]);
+            tW[W] = to_bf4(DT);
+#pragma unroll
+            for (int J = 0; J <= W; ++J) {
+                const FragSlot f = frag_slot(W, J);
+                if (f.stride == 8) {
+                    *reinterpret_cast<bf16x4*>(Tb + f.off + 8 * lane) = tW[J];
+                } else if ((J & 1) == 0) {
+                    *reinterpret_cast<bf16x8*>(Tb + f.off + 16 * lane) = cat8(tW[J], tW[J + 1]);
+                }
             }
-            const int j0 = 16 * W + 4 * lg;
+            // A column block W: A_{I,W}, I >= W
 #pragma unroll
-            for (int I = W; I < 4; ++I)
-                *reinterpret_cast<bf16x4*>(Ab + LC::chunk(16 * I + l16, j0 >> 3) + 2 * (j0 & 7)) =
-                    to_bf4(m.mA[I] * At[I]);
-            *reinterpret_cast<bf16x4*>(Tb + LC::chunk(iL, j0 >> 3) + 2 * (j0 & 7)) = to_bf4(DT);
+            for (int I = W; I < 4; ++I) {
+                const FragSlot f = frag_slot(I, W);
+                *reinterpret_cast<bf16x4*>(Ab + f.off + f.stride * lane) = to_bf4(m.mA[I] * At[I]);
+            }
         };
 
         // The pipeline: in round c (c = -1 .. NC - 1) chunk nx = c + 1 is
@@ -651,17 +684,6 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
     const int vc = 16 * wave + 4 * trm;
     const int vtr_base = LC::chunk(4 * lg + trj, vc >> 3) + 2 * (vc & 7);
     constexpr int VJ = 16 * CH * 2 + (16 / LC::G) * LC::PAD;   // 16 V rows further
-    // 8-byte fragments of T and A: row 16 x + l16, columns 16 J + 4 lg .. + 3.
-    // The row's 16-byte chunks are XOR-permuted by (row & 3), which swaps
-    // column blocks J and J ^ 1 on some rows, so each row tile keeps the
-    // offsets of blocks 0 and 1; blocks 2 and 3 are 64 bytes further.
-    int tn_off[4][2];
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int J = 0; J < 2; ++J)
-            tn_off[x][J] = LC::chunk(16 * x + l16, 2 * J + (lg >> 1)) + 8 * (lg & 1);
-    auto tn = [&](int x, int J) { return tn_off[x][J & 1] + 64 * (J >> 1); };
     const unsigned ostride = (unsigned)(H * DV);
     E* const Ocol = O + ((size_t)b * T * H + h) * DV + tile * TV + 16 * wave + 4 * lg;
 
@@ -735,17 +757,26 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
             }
         }
 
-        // (4) Vt = L^{-1} R by block substitution
+        // (4) Vt = L^{-1} R by block substitution; T's blocks: D on the
+        //     diagonal, -N below it (pairs read as one 16-byte access)
         f32x4 Vt[4];
+        {
+            const bf16x8 t10 = *reinterpret_cast<const bf16x8*>(Tb + frag_slot(1, 0).off + 16 * lane);
+            const bf16x8 t20 = *reinterpret_cast<const bf16x8*>(Tb + frag_slot(2, 0).off + 16 * lane);
+            const bf16x8 t30 = *reinterpret_cast<const bf16x8*>(Tb + frag_slot(3, 0).off + 16 * lane);
+            const bf16x8 t32 = *reinterpret_cast<const bf16x8*>(Tb + frag_slot(3, 2).off + 16 * lane);
+            const bf16x4 t00 = *reinterpret_cast<const bf16x4*>(Tb + frag_slot(0, 0).off + 8 * lane);
+            const bf16x4 t22 = *reinterpret_cast<const bf16x4*>(Tb + frag_slot(2, 2).off + 8 * lane);
+            const bf16x4 tb[4][4] = {{t00, t00, t00, t00},
+                                     {lo4(t10), hi4(t10), t00, t00},
+                                     {lo4(t20), hi4(t20), t22, t00},
+                                     {lo4(t30), hi4(t30), lo4(t32), hi4(t32)}};
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            const bf16x4 dI = *reinterpret_cast<const bf16x4*>(Tb + tn(I, I));
-            Vt[I] = mma16(dI, to_bf4(R[I]), zero4());
-            const bf16x4 vI = to_bf4(Vt[I]);
+            for (int I = 0; I < 4; ++I) {
+                Vt[I] = mma16(tb[I][I], to_bf4(R[I]), zero4());
+                const bf16x4 vI = to_bf4(Vt[I]);
 #pragma unroll
-            for (int I2 = I + 1; I2 < 4; ++I2) {
-                const bf16x4 nIJ = *reinterpret_cast<const bf16x4*>(Tb + tn(I2, I));
-                R[I2] = mma16(nIJ, vI, R[I2]);
+                for (int I2 = I + 1; I2 < 4; ++I2) R[I2] = mma16(tb[I2][I], vI, R[I2]);
             }
         }
 
@@ -766,11 +797,12 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
             for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
                 for (int p = 0; 2 * p <= ct; ++p) {
-                    const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(Ab + tn(ct, 2 * p));
+                    const FragSlot f = frag_slot(ct, 2 * p);
                     if (2 * p + 1 <= ct) {
-                        const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(Ab + tn(ct, 2 * p + 1));
-                        Ot[ct] = MM::mma(cat8(vb[2 * p], vb[2 * p + 1]), cat8(a0, a1), Ot[ct]);
+                        const bf16x8 a01 = *reinterpret_cast<const bf16x8*>(Ab + f.off + 16 * lane);
+                        Ot[ct] = MM::mma(cat8(vb[2 * p], vb[2 * p + 1]), a01, Ot[ct]);
                     } else {
+                        const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(Ab + f.off + 8 * lane);
                         Ot[ct] = MM::mma(cat8(vb[2 * p], zb), cat8(a0, zb), Ot[ct]);
                     }
                 }
