@@ -286,29 +286,28 @@ __global__ __launch_bounds__(NT) void chunk_coef_kernel(const float* __restrict_
 }
 
 // LDS layout of the K and Q tiles of the fused kernel (64 rows x DK bf16),
-// written by the helpers from registers.  Two reads must be free of bank
-// conflicts (64 banks of 4 bytes; a wavefront's access is served 32 lanes at
-// a time): 16-byte fragments of 16 consecutive rows at one 16-byte chunk, and
-// transposing reads in which each 16-lane group takes four 8-byte pieces from
-// each of 4 consecutive rows, the pieces lying in one 64-byte window of the
-// row.  Rows start 64 bytes apart modulo 256 (a 64-byte gap after every
-// row at DK = 128, after every second row at DK = 64), so 4 consecutive rows
-// fall in 4 different 64-byte bank windows; and the 16-byte chunks of a row
-// are XOR-permuted by bits 2..3 of the row, so 16 consecutive rows spread
-// over the 4 chunks of each window.  The permutation touches chunk-index
-// bits 0..1 only: step s of a fragment read is a fixed 64 s bytes further,
-// and 16 rows further is a fixed J16 bytes further.
+// written by the helpers from registers.  Three accesses use it: 16-byte
+// fragments of 16 consecutive rows at one 16-byte chunk (both waves' Gram
+// and state products), transposing reads in which each 16-lane group takes
+// four 8-byte pieces from each of 4 consecutive rows within one 64-byte
+// window, and the helpers' 16-byte stores.  Rows are 2 DK + 32 bytes apart
+// and the 16-byte chunks of a row are XOR-permuted by bits 2..3 of the row.
+// Measured on gfx950 with every wavefront of a workgroup issuing each
+// access, all three then run at the rate of a linear access of the same
+// width; plain row strides of 2 DK or 2 DK + 64 bytes do not (the 16-row
+// reads or the transposing reads take 1.6x to 3.7x as long).  The
+// permutation touches chunk-index bits 0..1 only: step s of a fragment read
+// is a fixed 64 s bytes further, and 16 rows further is a fixed J16 bytes.
 template <int DK>
 struct KQLayout {
     static constexpr int ROWB = 2 * DK;
-    static constexpr int G = DK == 128 ? 1 : 2;         // rows per gap
-    static constexpr int GAP = 64;
-    static constexpr int BYTES = CH * ROWB + (CH / G) * GAP;
-    static constexpr int J16 = 16 * ROWB + (16 / G) * GAP;
+    static constexpr int STRIDE = ROWB + 32;            // bytes from row to row
+    static constexpr int BYTES = CH * STRIDE;
+    static constexpr int J16 = 16 * STRIDE;
     static_assert(DK == 64 || DK == 128, "head size");
     __device__ __forceinline__ static int chunk(int row, int qc)
     {
-        return row * ROWB + (row / G) * GAP + 16 * (qc ^ ((row >> 2) & 3));
+        return row * STRIDE + 16 * (qc ^ ((row >> 2) & 3));
     }
 };
 
