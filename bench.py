@@ -1,12 +1,14 @@
 """Benchmark of the MDN hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--decode-steps D] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--settle SEC] [--decode-steps D] [--no-cpu-baseline]
 
 A step is one chunkwise forward (mdn_chunk_fwd: coefficients, Gram products,
 residual solve, outputs and carried state, one fused kernel for bf16) over
 the 1.3B-like layer B=8, H=16,
 T=4096, d_k=d_v=128, chunk 64, bf16 q/k/v with fp32 gates and state, inputs
 resident in HBM.  `value` is tokens/s = B*T per step / time per step.
+Each timed section is preceded by about SEC seconds of untimed calls (the
+GPU clock leaves its idle state) and W warm-up steps; then K steps are timed.
 
 The same JSON line carries:
   roofline      the step's kernel against the roof its algorithmic work reaches
@@ -118,8 +120,10 @@ def roofline_of(kernel, us, flop, nbytes):
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--settle", type=float, default=0.3,
+                   help="seconds of untimed calls before each timed section")
     p.add_argument("--decode-steps", type=int, default=64)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
@@ -134,6 +138,20 @@ def up(x, dtype):
     import numpy as np
     import torch
     return torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(dtype)
+
+
+def settle(torch, fns, seconds):
+    """Untimed repetitions of the callables for about `seconds` of wall time,
+    so that the GPU clock has left its idle state before anything is timed
+    (a few steps from idle run up to 20% slower than the steady state)."""
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(10):
+            for fn in fns:
+                fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
 
 
 def time_calls(torch, fns, steps):
@@ -170,6 +188,7 @@ def bench_forward(args, torch, si, mdn):
     # (about 6% of the call) and then chunk_fwd_fused_kernel; the events bracket the
     # call, so the fused kernel's rate below includes the coefficient kernel's
     # time (it is understated, never overstated)
+    settle(torch, [plan.forward], args.settle)
     for _ in range(args.warmup):
         plan.forward()
     (fwd_ms,), step_ms = time_calls(torch, [plan.forward], args.steps)
@@ -181,9 +200,7 @@ def bench_forward(args, torch, si, mdn):
     }
     kernels["chunk_fwd_fused_kernel"]["timed_with"] = "chunk_coef_kernel (same call)"
     # the same forward through the exported two-phase entry points
-    for _ in range(2):
-        plan.prepare()
-        plan.scan()
+    settle(torch, [plan.prepare, plan.scan], args.settle)
     (prep_ms, scan_ms), split_ms = time_calls(torch, [plan.prepare, plan.scan], args.steps)
     log(f"split path: prepare {prep_ms * 1e3:.1f} us, scan {scan_ms * 1e3:.1f} us")
     split = {
@@ -220,9 +237,7 @@ def bench_decode(args, torch, si, mdn):
                      up(t["mu"], f32), up(t["eta"], f32)))
     o = torch.empty((cfg.N, cfg.H, cfg.Dv), dtype=bf, device="cuda")
     log(f"decode inputs ({dcfg.steps} steps) drawn in {time.time() - t0:.1f}s")
-    for i in range(min(3, dcfg.steps)):
-        mdn.decode_step(*toks[i], S, M, o)
-    torch.cuda.synchronize()
+    settle(torch, [lambda: mdn.decode_step(*toks[0], S, M, o)], args.settle)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
