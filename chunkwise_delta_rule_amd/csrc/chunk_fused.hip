@@ -311,22 +311,25 @@ struct KQLayout {
     }
 };
 
+// LDS of the fused kernel.  Q, the V tile, T, A and the coefficient rows of
+// a chunk live in operand buffer c & 1; K in K buffer c % 3, since the
+// helpers store a chunk's K rows a round before they build its Gram products
+// from them (so that no helper waits for another's rows); the tables of a
+// chunk in table set c & 1.
 template <int DK>
 struct FusedLayout {
     using LK = KQLayout<DK>;                // K, Q: 64 rows x DK
-    using LC = TileLayout<CH * 2>;          // V tile, T (-N, D), A: 64 rows x 64
-    static constexpr int OFF_K = 0;
-    static constexpr int OFF_Q = LK::BYTES;
-    static constexpr int OFF_V = 2 * LK::BYTES;
+    using LC = TileLayout<CH * 2>;          // V tile: 64 rows x 64
+    static constexpr int OFF_Q = 0;
+    static constexpr int OFF_V = LK::BYTES;
     static constexpr int OFF_T = OFF_V + LC::BYTES;
     static constexpr int OFF_A = OFF_T + FRAG_AREA;
     static constexpr int OFF_VEC = OFF_A + FRAG_AREA;
     static constexpr int BUF = OFF_VEC + 6 * CH * 4;
+    static constexpr int OFF_K = 2 * BUF;                 // three K buffers
     static constexpr int TB_BYTES = ChunkTables::LDS_FLOATS * 4;
-    // two operand buffers, two table sets (chunks of even and odd index),
-    // the helpers' arrival counter
-    static constexpr int OFF_SYNC = 2 * BUF + 2 * TB_BYTES;
-    static constexpr int BYTES = OFF_SYNC + 16;
+    static constexpr int OFF_TB = OFF_K + 3 * LK::BYTES;  // two table sets
+    static constexpr int BYTES = OFF_TB + 2 * TB_BYTES;
 };
 
 template <int DK, int DV>
@@ -350,8 +353,9 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
     __shared__ __align__(16) char smem[L::BYTES];
     // coefficient tables of chunk c: set c & 1
     auto tables = [&](int c) {
-        return reinterpret_cast<float*>(smem + 2 * L::BUF + (c & 1) * L::TB_BYTES);
+        return reinterpret_cast<float*>(smem + L::OFF_TB + (c & 1) * L::TB_BYTES);
     };
+    auto kbuf = [&](int c) { return smem + L::OFF_K + (c % 3) * LK::BYTES; };
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -368,14 +372,17 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
     // token index of row 0 of chunk c of this head (rows are H tokens apart)
     auto tok_base = [&](int c) { return ((size_t)b * T + (size_t)c * CH) * H + h; };
     auto chunk_rows = [&](int c) { return min(CH, T - c * CH); };
-    unsigned* const hsync = reinterpret_cast<unsigned*>(smem + L::OFF_SYNC);
-    if (tid == 0) *hsync = 0u;   // visible to all after the first barrier
 
     if (wave >= 4) {
         // =================== helper wavefronts ===================
+        // Helper W builds row block W of T and row block X = 3 - W of A (five
+        // 16x16 Gram tiles for every helper).  It loads K rows of block W
+        // and Q rows of block X into registers, one chunk ahead, and stores
+        // them to LDS for everyone.
         const int hw = wave - 4;
-        const int r0 = 16 * hw;                 // first row of this helper's block
-        MM::frag kf[2][SK], qf[2][SK];          // own K, Q rows; set = chunk parity
+        const int rK = 16 * hw, rQ = 16 * (3 - hw);   // its K and Q rows
+        MM::frag kf[SK];                        // K rows of block W, next to store
+        MM::frag qf[2][SK];                     // Q rows of block X; set = chunk parity
         const unsigned v_lane = LC::lane_offset((unsigned)(H * DV), lane);
         const MM::frag zfrag = __builtin_bit_cast(MM::frag, u32x4{0u, 0u, 0u, 0u});
         // 16x16 product X Y from acc(X^T) and acc(Y), where acc(Z) is the
@@ -385,37 +392,34 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
         auto prod = [](const f32x4& XT, const f32x4& YB) {
             return mma16(to_bf4(XT), to_bf4(YB), zero4());
         };
-
-        auto load_kq = [&](int c, auto par) {
-            constexpr int P = decltype(par)::value;
-            const int n = chunk_rows(c);
-            const size_t row = tok_base(c) + (size_t)min(r0 + l16, n - 1) * H;
-#pragma unroll
-            for (int u = 0; u < SK; ++u) {
-                const size_t off = row * DK + 8 * (4 * u + lg);
-                kf[P][u] = *reinterpret_cast<const MM::frag*>(k + off);
-                qf[P][u] = *reinterpret_cast<const MM::frag*>(q + off);
-            }
+        auto row_off = [&](int c, int r) {      // element offset of row r of chunk c
+            return (tok_base(c) + (size_t)min(r, chunk_rows(c) - 1) * H) * DK;
         };
-        // own rows of chunk c into buffer B (rows >= n become zero, in the
-        // registers too, so the Gram products, L and A vanish there)
-        auto store_kq = [&](int c, char* B, auto par) {
+        auto load_k = [&](int c) {
+            const size_t off = row_off(c, rK + l16) + 8 * lg;
+#pragma unroll
+            for (int u = 0; u < SK; ++u) kf[u] = *reinterpret_cast<const MM::frag*>(k + off + 32 * u);
+        };
+        auto load_q = [&](int c, auto par) {
             constexpr int P = decltype(par)::value;
+            const size_t off = row_off(c, rQ + l16) + 8 * lg;
+#pragma unroll
+            for (int u = 0; u < SK; ++u) qf[P][u] = *reinterpret_cast<const MM::frag*>(q + off + 32 * u);
+        };
+        // rows >= n of a partial last chunk become zero (in the registers
+        // too), so that the Gram products, L and A vanish there
+        auto zero_tail = [&](int c, int r0, MM::frag* f) {
             const int n = chunk_rows(c);
-            if (n < CH) {   // the last chunk only
+            if (n < CH) {
                 const bool live = r0 + l16 < n;
 #pragma unroll
-                for (int u = 0; u < SK; ++u) {
-                    kf[P][u] = live ? kf[P][u] : zfrag;
-                    qf[P][u] = live ? qf[P][u] : zfrag;
-                }
+                for (int u = 0; u < SK; ++u) f[u] = live ? f[u] : zfrag;
             }
+        };
+        auto store_rows = [&](char* dst, int r0, const MM::frag* f) {
 #pragma unroll
-            for (int u = 0; u < SK; ++u) {
-                const int off = LK::chunk(r0 + l16, 4 * u + lg);
-                *reinterpret_cast<MM::frag*>(B + L::OFF_K + off) = kf[P][u];
-                *reinterpret_cast<MM::frag*>(B + L::OFF_Q + off) = qf[P][u];
-            }
+            for (int u = 0; u < SK; ++u)
+                *reinterpret_cast<MM::frag*>(dst + LK::chunk(r0 + l16, 4 * u + lg)) = f[u];
         };
         // direct loads of chunk c's V tile and coefficient rows into buffer B
         auto load_v = [&](int c, char* B) {
@@ -439,36 +443,38 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
             }
         };
 
-        // Elementwise factors of helper W's Gram tiles, from chunk tables tb
-        // (they need no K, Q, so they are formed before B1):
+        // Elementwise factors of helper W's Gram tiles, from chunk tables tb.
+        // Lane layout of the tiles: (row 16 x + l16, columns 16 J + 4 lg + r).
         //   mL[J]: -N_{W,J} = mL[J] o G_{W,J} (J < W): -alpha_i eta_j gamma_{i-1,j}
         //   mT, mB: N_{W,W} in both accumulator layouts (zero on and above the
-        //           diagonal): alpha_i eta_j gamma_{i-1,j}
-        //   mA[I]: A_{I,W} = mA[I] o (Q K^T)_{I,W} (I >= W): eta_j gamma_{i,j}
-        // Lane layout: the transposed tiles' (row 16 I + l16, columns
-        // 16 J + 4 lg + r); mB is N_{W,W}'s own layout (row 16 W + 4 lg + r,
-        // column 16 W + l16).
+        //           diagonal): alpha_i eta_j gamma_{i-1,j}; mB is N_{W,W}'s own
+        //           layout (row 16 W + 4 lg + r, column 16 W + l16)
+        //   mA[J]: A_{X,J} = mA[J] o (Q K^T)_{X,J} (J <= X): eta_j gamma_{i,j}
         struct Mult {
             f32x4 mL[3], mT, mB, mA[4];
         };
         auto multipliers = [&](auto wc, const float* tb) {
             constexpr int W = decltype(wc)::value;
+            constexpr int X = 3 - W;
             const int l16o = opaque(lane & 15), lgo = opaque(lane >> 4);
             Mult m;
             const int iL = 16 * W + l16o;
             const float aiL = tb[CTb::ALPHA + iL];
             const float raP = tb[CTb::RA + (l16o > 0 ? iL - 1 : iL)];
             const float rgP = tb[CTb::RG + (l16o > 0 ? iL - 1 : iL)];
-            const f32x4 eW = *reinterpret_cast<const f32x4*>(tb + CTb::ETA + 16 * W + 4 * lgo);
+            f32x4 eJ[4];
+#pragma unroll
+            for (int J = 0; J < 4; ++J)
+                if (J <= W || J <= X)
+                    eJ[J] = *reinterpret_cast<const f32x4*>(tb + CTb::ETA + 16 * J + 4 * lgo);
 #pragma unroll
             for (int J = 0; J < W; ++J) {
-                const f32x4 e = *reinterpret_cast<const f32x4*>(tb + CTb::ETA + 16 * J + 4 * lgo);
                 const f32x4 gb = *reinterpret_cast<const f32x4*>(tb + CTb::GB + 64 * W + 16 * J + 4 * lgo);
                 const f32x4 mb = *reinterpret_cast<const f32x4*>(tb + CTb::MB + 64 * W + 16 * J + 4 * lgo);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float g = l16o == 0 ? gb[r] : raP * gb[r] + rgP * mb[r];
-                    m.mL[J][r] = -(aiL * e[r] * g);
+                    m.mL[J][r] = -(aiL * eJ[J][r] * g);
                 }
             }
             const f32x4 gdT = *reinterpret_cast<const f32x4*>(
@@ -479,52 +485,62 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
             for (int r = 0; r < 4; ++r) {
                 const int j = 4 * lgo + r;
                 const float gdB = tb[CTb::GD + (16 * W + (j > 0 ? j - 1 : 0)) * 16 + l16o];
-                m.mT[r] = j < l16o ? aiL * eW[r] * gdT[r] : 0.f;
+                m.mT[r] = j < l16o ? aiL * eJ[W][r] * gdT[r] : 0.f;
                 m.mB[r] = l16o < j ? aD[r] * eR * gdB : 0.f;
             }
-            const f32x4 gdA = *reinterpret_cast<const f32x4*>(tb + CTb::GD + (16 * W + l16o) * 16 + 4 * lgo);
-            m.mA[W] = eW * gdA;
+            const int iA = 16 * X + l16o;
+            const float ra = tb[CTb::RA + iA], rg = tb[CTb::RG + iA];
 #pragma unroll
-            for (int I = W + 1; I < 4; ++I) {
-                const float ra = tb[CTb::RA + 16 * I + l16o], rg = tb[CTb::RG + 16 * I + l16o];
-                const f32x4 gb = *reinterpret_cast<const f32x4*>(tb + CTb::GB + 64 * I + 16 * W + 4 * lgo);
-                const f32x4 mb = *reinterpret_cast<const f32x4*>(tb + CTb::MB + 64 * I + 16 * W + 4 * lgo);
-                m.mA[I] = eW * (ra * gb + rg * mb);
+            for (int J = 0; J < X; ++J) {
+                const f32x4 gb = *reinterpret_cast<const f32x4*>(tb + CTb::GB + 64 * X + 16 * J + 4 * lgo);
+                const f32x4 mb = *reinterpret_cast<const f32x4*>(tb + CTb::MB + 64 * X + 16 * J + 4 * lgo);
+                m.mA[J] = eJ[J] * (ra * gb + rg * mb);
             }
+            const f32x4 gdA = *reinterpret_cast<const f32x4*>(tb + CTb::GD + iA * 16 + 4 * lgo);
+            m.mA[X] = eJ[X] * gdA;
             return m;
         };
 
-        // Row block W of L (-N_{W,J}, J < W, and D_W) into T, column block W
-        // of A into A; W is this helper's index, a compile-time constant in
+        // One row block x of T or A into its fragment slots: pairs
+        // (J, J + 1) as one 16-byte store, lone blocks as 8 bytes
+        auto store_block_row = [&](auto xc, char* area, const bf16x4* f) {
+            constexpr int x = decltype(xc)::value;
+#pragma unroll
+            for (int J = 0; J <= x; ++J) {
+                const FragSlot sl = frag_slot(x, J);
+                if (sl.stride == 8)
+                    *reinterpret_cast<bf16x4*>(area + sl.off + 8 * lane) = f[J];
+                else if ((J & 1) == 0)
+                    *reinterpret_cast<bf16x8*>(area + sl.off + 16 * lane) = cat8(f[J], f[J + 1]);
+            }
+        };
+
+        // Row block W of L (-N_{W,J}, J < W, and D_W) into T, row block X
+        // of A into A, for the chunk whose K tile is Kt and Q rows (block X)
+        // are in qf[P]; W is this helper's index, a compile-time constant in
         // each copy.
-        auto prepare = [&](auto wc, char* B, const Mult& m, auto par) {
+        auto prepare = [&](auto wc, char* B, const char* Kt, const Mult& m, auto par) {
             constexpr int W = decltype(wc)::value;
+            constexpr int X = 3 - W;
+            constexpr int JN = W > X ? W : X;     // K blocks 0 .. JN are read
             constexpr int P = decltype(par)::value;
             const int l16o = opaque(lane & 15), lgo = opaque(lane >> 4);
-            const char* Kb = B + L::OFF_K;
-            const char* Qb = B + L::OFF_Q;
-            // ---- Gram tiles, transposed (lane: row 16 I + l16, columns 16 J + 4 lg + r)
-            f32x4 Gt[W + 1], At[4];
+            // ---- Gram tiles, transposed (lane: row 16 x + l16, columns 16 J + 4 lg + r)
+            f32x4 Gt[W + 1], At[X + 1];
 #pragma unroll
             for (int J = 0; J <= W; ++J) Gt[J] = zero4();
 #pragma unroll
-            for (int I = W; I < 4; ++I) At[I] = zero4();
+            for (int J = 0; J <= X; ++J) At[J] = zero4();
 #pragma unroll
             for (int s = 0; s < SK; ++s) {
+                MM::frag aK[JN + 1];
 #pragma unroll
-                for (int J = 0; J < W; ++J) {
-                    const auto aK =
-                        *reinterpret_cast<const MM::frag*>(Kb + LK::chunk(16 * J + l16, 4 * s + lg));
-                    Gt[J] = MM::mma(aK, kf[P][s], Gt[J]);
-                }
-                Gt[W] = MM::mma(kf[P][s], kf[P][s], Gt[W]);
-                At[W] = MM::mma(kf[P][s], qf[P][s], At[W]);
+                for (int J = 0; J <= JN; ++J)
+                    aK[J] = *reinterpret_cast<const MM::frag*>(Kt + LK::chunk(16 * J + l16, 4 * s + lg));
 #pragma unroll
-                for (int I = W + 1; I < 4; ++I) {
-                    const auto bQ =
-                        *reinterpret_cast<const MM::frag*>(Qb + LK::chunk(16 * I + l16, 4 * s + lg));
-                    At[I] = MM::mma(kf[P][s], bQ, At[I]);
-                }
+                for (int J = 0; J <= W; ++J) Gt[J] = MM::mma(aK[J], aK[W], Gt[J]);
+#pragma unroll
+                for (int J = 0; J <= X; ++J) At[J] = MM::mma(aK[J], qf[P][s], At[J]);
             }
             // N_WW in both accumulator layouts from the symmetric Gram tile:
             // NT = acc(N^T) (lane: row l16, cols 4 lg + r), NB = acc(N)
@@ -541,101 +557,80 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
             const f32x4 QT = P1T + prod(N4B, P1T);
             const f32x4 DT = QT + prod(N8B, QT);
             // ---- stores
-            char* Tb = B + L::OFF_T;
-            char* Ab = B + L::OFF_A;
-            // T row block W: -N_{W,J} (J < W) and D_W; pairs (J, J + 1) as
-            // one 16-byte store
-            bf16x4 tW[W + 1];
+            bf16x4 tW[W + 1], aX[X + 1];
 #pragma unroll
             for (int J = 0; J < W; ++J) tW[J] = to_bf4(m.mL[J] * Gt[J]);
             tW[W] = to_bf4(DT);
 #pragma unroll
-            for (int J = 0; J <= W; ++J) {
-                const FragSlot f = frag_slot(W, J);
-                if (f.stride == 8) {
-                    *reinterpret_cast<bf16x4*>(Tb + f.off + 8 * lane) = tW[J];
-                } else if ((J & 1) == 0) {
-                    *reinterpret_cast<bf16x8*>(Tb + f.off + 16 * lane) = cat8(tW[J], tW[J + 1]);
-                }
-            }
-            // A column block W: A_{I,W}, I >= W
-#pragma unroll
-            for (int I = W; I < 4; ++I) {
-                const FragSlot f = frag_slot(I, W);
-                *reinterpret_cast<bf16x4*>(Ab + f.off + f.stride * lane) = to_bf4(m.mA[I] * At[I]);
-            }
+            for (int J = 0; J <= X; ++J) aX[J] = to_bf4(m.mA[J] * At[J]);
+            store_block_row(IConst<W>{}, B + L::OFF_T, tW);
+            store_block_row(IConst<X>{}, B + L::OFF_A, aX);
         };
 
         // The pipeline: in round c (c = -1 .. NC - 1) chunk nx = c + 1 is
         // prepared into buffer nx & 1 while the compute wavefronts scan chunk
-        // c.  Its K, Q rows were loaded into registers and its tables into
-        // table set nx & 1 in round c - 1 (and waited for before the B0 that
-        // ended it).  Per helper and round the loads are issued as: tables of
-        // nx + 1, V tile and coefficient rows of nx, K, Q rows of nx + 1
-        // (2 SK), so waiting for all but the last 2 SK covers everything nx
-        // needs.
-        // B1, a barrier of the four helpers only (the compute wavefronts do
-        // not need it): an LDS arrival counter that only grows, round r
-        // (r = 0 .. NC) waiting for 4 (r + 1) arrivals.  Each helper's LDS
-        // writes are complete before it arrives.  The wait is bounded, so a
-        // helper that never arrived could not hang the workgroup.
-        // The counter is touched by inline assembly: a plain LDS access there
-        // would make the compiler wait for every outstanding global load
-        // first (it cannot tell the counter from the direct-load targets).
-        const unsigned hsync_addr =
-            (unsigned)(uintptr_t)((__attribute__((address_space(3))) unsigned*)hsync);
-        auto helper_sync = [&](unsigned target) {
-            const unsigned one = 1u;
-            if (lane == 0)
-                asm volatile("s_waitcnt lgkmcnt(0)\n\tds_add_u32 %0, %1"
-                             :: "v"(hsync_addr), "v"(one) : "memory");
-            for (int spin = 0; spin < (1 << 22); ++spin) {
-                unsigned v;
-                asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
-                             : "=v"(v) : "v"(hsync_addr) : "memory");
-                if (__builtin_amdgcn_readfirstlane(v) >= target) break;
-                __builtin_amdgcn_s_sleep(1);
-            }
-        };
+        // c.  At the start of the round the registers hold the K rows of
+        // nx + 1 and the Q rows of nx, loaded in round c - 1; the K tile of
+        // nx is in LDS since round c - 1 and the tables of nx since its B0.
+        // Per helper and round the loads are issued as: tables of nx + 1, V
+        // tile and coefficient rows of nx, then the register loads (K rows of
+        // nx + 2, Q rows of nx + 1), so waiting for all but the register loads
+        // covers everything nx needs.
         auto run = [&](auto wc) {
             auto round = [&](int c, auto par) {      // par: parity of nx
                 constexpr int P = decltype(par)::value;
                 const int nx = c + 1;
                 char* B = smem + P * L::BUF;
-                const unsigned arrivals = 4u * (unsigned)(c + 2);
-                // one branch for both halves of a live round, so that the
+                // one branch for the whole of a live round, so that the
                 // compiler sees prepare() reached only through the wait below
                 // (a path around it would make it wait for every load)
                 if (nx < NC) {
-                    const bool more = nx + 1 < NC;
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // K, Q of nx
-                    store_kq(nx, B, par);
+                    const bool more = nx + 1 < NC, more2 = nx + 2 < NC;
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    if (more) {
+                        zero_tail(nx + 1, rK, kf);
+                        store_rows(kbuf(nx + 1), rK, kf);
+                    }
+                    zero_tail(nx, rQ, qf[P]);
+                    store_rows(B + L::OFF_Q, rQ, qf[P]);
                     if (more) load_tables(nx + 1);
                     load_v(nx, B);
-                    if (more) load_kq(nx + 1, IConst<1 - P>{});
+                    // keep the register loads after the direct loads: the
+                    // wait below counts on that order
+                    asm volatile("" ::: "memory");
+                    if (more2) load_k(nx + 2);
+                    if (more) load_q(nx + 1, IConst<1 - P>{});
                     const Mult m = multipliers(wc, tables(nx));
-                    helper_sync(arrivals);   // B1: K, Q of nx visible
-                    prepare(wc, B, m, par);
+                    prepare(wc, B, kbuf(nx), m, par);
                     // the tables of nx + 1, the V tile and coefficient rows of
-                    // nx have landed; the K, Q loads of nx + 1, issued after
-                    // them, may still be in flight
-                    if (more) {
+                    // nx have landed; the register loads, issued after them,
+                    // may still be in flight
+                    if (more2) {
                         if constexpr (SK == 4)
                             asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
                         else
                             asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                    } else if (more) {
+                        if constexpr (SK == 4)
+                            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                        else
+                            asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
                     } else {
                         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                     }
-                } else {
-                    helper_sync(arrivals);
                 }
                 lds_barrier();   // B0: chunk nx ready
             };
-            load_kq(0, IConst<0>{});
+            // K tile of chunk 0, then the registers for round -1
+            load_k(0);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            zero_tail(0, rK, kf);
+            store_rows(kbuf(0), rK, kf);
+            if (NC > 1) load_k(1);
+            load_q(0, IConst<0>{});
             load_tables(0);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            lds_barrier();       // chunk 0's tables visible
+            lds_barrier();       // chunk 0's K tile and tables visible
             for (int c = -1; c < NC; c += 2) {
                 round(c, IConst<0>{});
                 if (c + 1 < NC) round(c + 1, IConst<1>{});
@@ -692,7 +687,7 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
         const int t0 = c * CH;
         const int n = min(CH, T - t0);
         const char* B = smem + (c & 1) * L::BUF;
-        const char* Kb = B + L::OFF_K;
+        const char* Kb = kbuf(c);
         const char* Qb = B + L::OFF_Q;
         const char* Vb = B + L::OFF_V;
         const char* Tb = B + L::OFF_T;
