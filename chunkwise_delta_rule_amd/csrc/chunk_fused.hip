@@ -137,6 +137,20 @@ __device__ __forceinline__ float readlane_f(float x, int l)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
 
+// x of lane i - d within each row of 16 lanes; lanes i < d of a row get
+// `fill` (DPP row_shr:d)
+__device__ __forceinline__ float dpp_shr(float x, int d, float fill)
+{
+    int r = __float_as_int(fill);
+    switch (d) {
+    case 1: r = __builtin_amdgcn_update_dpp(r, __float_as_int(x), 0x111, 0xf, 0xf, false); break;
+    case 2: r = __builtin_amdgcn_update_dpp(r, __float_as_int(x), 0x112, 0xf, 0xf, false); break;
+    case 4: r = __builtin_amdgcn_update_dpp(r, __float_as_int(x), 0x114, 0xf, 0xf, false); break;
+    default: r = __builtin_amdgcn_update_dpp(r, __float_as_int(x), 0x118, 0xf, 0xf, false); break;
+    }
+    return __int_as_float(r);
+}
+
 // A lane-dependent value the compiler must treat as new at this point: keeps
 // per-lane comparisons made from it inside the chunk loop instead of hoisted
 // out of it as lane masks (which would then live in spilled SGPRs).
@@ -191,30 +205,35 @@ __global__ __launch_bounds__(NT) void chunk_coef_kernel(const float* __restrict_
             mbk[t + e] = m4[e];
         }
     }
-    // block-local products of row `lane`, and the diagonal-block column
-    // recursion of column `lane`, side by side over the block's rows
-    float ra = 1.f, rp = 1.f, rg = 0.f;
-    float gam = 1.f, mm = 1.f, g_last = 0.f, m_last = 0.f;
+    // Block-local products of row `lane` (from its block's first row, row
+    // included): ra = prod alpha, rp = prod mu, rg_t = alpha_t rg_{t-1} + rp_t.
+    // A range's triple composes associatively -- earlier range L, later R:
+    // (ra, rp, rg) = (ra_L ra_R, rp_L rp_R, ra_R rg_L + rp_L rg_R) -- so the
+    // prefixes are a 4-step scan across the 16 lanes of the block.
+    float ra = ga, rp = gm, rg = gm;
+#pragma unroll
+    for (int d = 1; d < 16; d *= 2) {
+        const float pa = dpp_shr(ra, d, 1.f), pp = dpp_shr(rp, d, 1.f), pg = dpp_shr(rg, d, 0.f);
+        rg = ra * pg + pp * rg;
+        ra = pa * ra;
+        rp = pp * rp;
+    }
+    // the diagonal-block column recursion of column `lane` over its block's
+    // rows: gamma_jj = 1, m_jj = 1; below the diagonal m_t = mu_t m_{t-1},
+    // gamma_t = alpha_t gamma_{t-1} + m_t
+    float gam = 1.f, mm = 1.f;
     float gd[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-        const float a = ab[t], m = mbk[t];
-        const bool row_in = t <= off;      // block row t is at or above row `lane`
-        ra = row_in ? ra * a : ra;
-        rp = row_in ? rp * m : rp;
-        rg = row_in ? a * rg + rp : rg;
-        const bool below = t > off;        // below column `lane`'s diagonal
-        mm = below ? mm * m : mm;
-        gam = below ? a * gam + mm : gam;
+        const bool below = t > off;
+        mm = below ? mm * mbk[t] : mm;
+        gam = below ? ab[t] * gam + mm : gam;
         gd[t] = t >= off ? gam : 0.f;
-        const bool at_last = 16 * blk + t == last;
-        g_last = at_last ? gd[t] : g_last;
-        m_last = at_last ? (t >= off ? mm : 0.f) : m_last;
     }
     // block summaries (values at each block's last row)
     const float sa0 = readlane_f(ra, 15), sa1 = readlane_f(ra, 31), sa2 = readlane_f(ra, 47);
-    const float sp1 = readlane_f(rp, 31), sp2 = readlane_f(rp, 47);
-    const float sg1 = readlane_f(rg, 31), sg2 = readlane_f(rg, 47);
+    const float sp0 = readlane_f(rp, 15), sp1 = readlane_f(rp, 31), sp2 = readlane_f(rp, 47);
+    const float sg0 = readlane_f(rg, 15), sg1 = readlane_f(rg, 31), sg2 = readlane_f(rg, 47);
     // gamma, m of column `lane` at rows 16 I - 1 for the blocks below its own
     float gb = gam, mb = mm;
     float gbI[4] = {0.f, 0.f, 0.f, 0.f}, mbI[4] = {0.f, 0.f, 0.f, 0.f};
@@ -230,30 +249,33 @@ __global__ __launch_bounds__(NT) void chunk_coef_kernel(const float* __restrict_
         gbI[I] = I > blk ? gb : 0.f;
         mbI[I] = I > blk ? mb : 0.f;
     }
-    // coefficient rows
-    const float pre = blk == 0 ? 1.f : blk == 1 ? sa0 : blk == 2 ? sa0 * sa1 : sa0 * sa1 * sa2;
-    const float abar = ra * pre;
-    const float mu0 = readlane_f(gm, 0);
-    // gamma_{i,0}: block 0 from column 0's recursion, later blocks from the
-    // boundary values of column 0
-    float g0c[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) g0c[t] = readlane_f(gd[t], 0);
-    float g0 = 0.f;
-#pragma unroll
-    for (int t = 0; t < 16; ++t) g0 = (blk == 0 && off == t) ? g0c[t] : g0;
-    {
-        const float gb1 = readlane_f(gbI[1], 0), gb2 = readlane_f(gbI[2], 0), gb3 = readlane_f(gbI[3], 0);
-        const float mb1 = readlane_f(mbI[1], 0), mb2 = readlane_f(mbI[2], 0), mb3 = readlane_f(mbI[3], 0);
-        const float gbb = blk == 1 ? gb1 : blk == 2 ? gb2 : gb3;
-        const float mbb = blk == 1 ? mb1 : blk == 2 ? mb2 : mb3;
-        if (blk > 0) g0 = ra * gbb + rg * mbb;
-    }
-    const float bi = mu0 * g0;
+    // chunk-level prefixes of row `lane`: the whole blocks before its own,
+    // composed, then its block-local prefix; abar = prod alpha, mubar =
+    // prod mu and b = the rg of the whole chunk (b_i = alpha_i b_{i-1} +
+    // mubar_i is exactly rg's recursion from the chunk's first row)
+    const float A1 = sa0, P1 = sp0, G1 = sg0;
+    const float A2 = A1 * sa1, P2 = P1 * sp1, G2 = sa1 * G1 + P1 * sg1;
+    const float A3 = A2 * sa2, P3 = P2 * sp2, G3 = sa2 * G2 + P2 * sg2;
+    const float Ap = blk == 0 ? 1.f : blk == 1 ? A1 : blk == 2 ? A2 : A3;
+    const float Pp = blk == 0 ? 1.f : blk == 1 ? P1 : blk == 2 ? P2 : P3;
+    const float Gp = blk == 0 ? 0.f : blk == 1 ? G1 : blk == 2 ? G2 : G3;
+    const float abar = Ap * ra;
+    const float mubar = Pp * rp;
+    const float bi = ra * Gp + Pp * rg;
     const float bprev = __shfl_up(bi, 1);
     const bool valid = lane < n;
-    // gamma and m at the last row, column `lane`
-    const int lb = last >> 4;
+    // gamma and m of column `lane` at the last row
+    const int lb = last >> 4, tl = last & 15;
+    float g_last = gd[15], m_last = mm;   // a full chunk: row 15 of block 3
+    if (n < CH) {                         // the last chunk only
+        float m2 = 1.f;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            m2 = t > off && t <= tl ? m2 * mbk[t] : m2;
+            g_last = t == tl ? gd[t] : g_last;
+        }
+        m_last = tl >= off ? m2 : 0.f;
+    }
     const float raL = readlane_f(ra, last), rgL = readlane_f(rg, last), rpL = readlane_f(rp, last);
     const float gbl = lb == 1 ? gbI[1] : lb == 2 ? gbI[2] : gbI[3];
     const float mbl = lb == 1 ? mbI[1] : lb == 2 ? mbI[2] : mbI[3];
@@ -261,7 +283,7 @@ __global__ __launch_bounds__(NT) void chunk_coef_kernel(const float* __restrict_
     const float ml = blk < lb ? rpL * mbl : blk == lb ? m_last : 0.f;
     const float abar_n = readlane_f(abar, last);
     const float b_n = readlane_f(bi, last);
-    const float mbar_n = mu0 * readlane_f(ml, 0);
+    const float mbar_n = readlane_f(mubar, last);
 
     // ---- stores
     tb[CTb::ALPHA + lane] = ga;
