@@ -414,19 +414,25 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
         auto prod = [](const f32x4& XT, const f32x4& YB) {
             return mma16(to_bf4(XT), to_bf4(YB), zero4());
         };
-        auto row_off = [&](int c, int r) {      // element offset of row r of chunk c
-            return (tok_base(c) + (size_t)min(r, chunk_rows(c) - 1) * H) * DK;
+        // element offsets of this lane's K and Q rows inside a chunk (rows
+        // past the end of a partial last chunk repeat its last row)
+        const unsigned rowstride = (unsigned)(H * DK);
+        const unsigned offK = (unsigned)(rK + l16) * rowstride + 8u * (unsigned)lg;
+        const unsigned offQ = (unsigned)(rQ + l16) * rowstride + 8u * (unsigned)lg;
+        auto lane_off = [&](int c, int r, unsigned full) {
+            const int n = chunk_rows(c);
+            return n == CH ? full : (unsigned)min(r + l16, n - 1) * rowstride + 8u * (unsigned)lg;
         };
         auto load_k = [&](int c) {
-            const size_t off = row_off(c, rK + l16) + 8 * lg;
+            const __bf16* src = k + tok_base(c) * DK + lane_off(c, rK, offK);
 #pragma unroll
-            for (int u = 0; u < SK; ++u) kf[u] = *reinterpret_cast<const MM::frag*>(k + off + 32 * u);
+            for (int u = 0; u < SK; ++u) kf[u] = *reinterpret_cast<const MM::frag*>(src + 32 * u);
         };
         auto load_q = [&](int c, auto par) {
             constexpr int P = decltype(par)::value;
-            const size_t off = row_off(c, rQ + l16) + 8 * lg;
+            const __bf16* src = q + tok_base(c) * DK + lane_off(c, rQ, offQ);
 #pragma unroll
-            for (int u = 0; u < SK; ++u) qf[P][u] = *reinterpret_cast<const MM::frag*>(q + off + 32 * u);
+            for (int u = 0; u < SK; ++u) qf[P][u] = *reinterpret_cast<const MM::frag*>(src + 32 * u);
         };
         // rows >= n of a partial last chunk become zero (in the registers
         // too), so that the Gram products, L and A vanish there
@@ -475,50 +481,69 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
         struct Mult {
             f32x4 mL[3], mT, mB, mA[4];
         };
-        auto multipliers = [&](auto wc, const float* tb) {
+        // the lane's table offsets and 0/1 masks, the same every chunk
+        struct MultLane {
+            int oP;          // row iL - 1 (iL itself on the block's first row)
+            int oGdT;        // GD row iL - 1 (clamped), columns 4 lg ..
+            int oGdB;        // GD row 16 W + 4 lg - 1, column l16 (+ 16 per r)
+            float z0;        // 1 on the block's first row
+            f32x4 fT, fB;    // strictly below the diagonal in either layout
+            f32x4 id;        // the identity in the accumulator layout
+        };
+        auto mult_lane = [&](auto wc) {
+            constexpr int W = decltype(wc)::value;
+            MultLane ml;
+            const int iL = 16 * W + l16;
+            ml.oP = l16 > 0 ? iL - 1 : iL;
+            ml.oGdT = (16 * W + (l16 > 0 ? l16 - 1 : 0)) * 16 + 4 * lg;
+            ml.oGdB = (16 * W + 4 * lg - 1) * 16 + l16;   // (r = 0, lg = 0): masked
+            ml.z0 = l16 == 0 ? 1.f : 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = 4 * lg + r;
+                ml.fT[r] = j < l16 ? 1.f : 0.f;
+                ml.fB[r] = l16 < j ? 1.f : 0.f;
+                ml.id[r] = j == l16 ? 1.f : 0.f;
+            }
+            return ml;
+        };
+        auto multipliers = [&](auto wc, const float* tb, const MultLane& ml) {
             constexpr int W = decltype(wc)::value;
             constexpr int X = 3 - W;
-            const int l16o = opaque(lane & 15), lgo = opaque(lane >> 4);
             Mult m;
-            const int iL = 16 * W + l16o;
+            const int iL = 16 * W + l16;
             const float aiL = tb[CTb::ALPHA + iL];
-            const float raP = tb[CTb::RA + (l16o > 0 ? iL - 1 : iL)];
-            const float rgP = tb[CTb::RG + (l16o > 0 ? iL - 1 : iL)];
+            const float raP = tb[CTb::RA + ml.oP], rgP = tb[CTb::RG + ml.oP];
+            // gamma_{i-1,j} = raP gb + rgP mb, and gb itself on the first row
+            const float raZ = raP + ml.z0 * (1.f - raP), rgZ = rgP - ml.z0 * rgP;
             f32x4 eJ[4];
 #pragma unroll
             for (int J = 0; J < 4; ++J)
                 if (J <= W || J <= X)
-                    eJ[J] = *reinterpret_cast<const f32x4*>(tb + CTb::ETA + 16 * J + 4 * lgo);
+                    eJ[J] = *reinterpret_cast<const f32x4*>(tb + CTb::ETA + 16 * J + 4 * lg);
 #pragma unroll
             for (int J = 0; J < W; ++J) {
-                const f32x4 gb = *reinterpret_cast<const f32x4*>(tb + CTb::GB + 64 * W + 16 * J + 4 * lgo);
-                const f32x4 mb = *reinterpret_cast<const f32x4*>(tb + CTb::MB + 64 * W + 16 * J + 4 * lgo);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float g = l16o == 0 ? gb[r] : raP * gb[r] + rgP * mb[r];
-                    m.mL[J][r] = -(aiL * eJ[J][r] * g);
-                }
+                const f32x4 gb = *reinterpret_cast<const f32x4*>(tb + CTb::GB + 64 * W + 16 * J + 4 * lg);
+                const f32x4 mb = *reinterpret_cast<const f32x4*>(tb + CTb::MB + 64 * W + 16 * J + 4 * lg);
+                m.mL[J] = (-aiL) * eJ[J] * (raZ * gb + rgZ * mb);
             }
-            const f32x4 gdT = *reinterpret_cast<const f32x4*>(
-                tb + CTb::GD + (16 * W + (l16o > 0 ? l16o - 1 : 0)) * 16 + 4 * lgo);
-            const f32x4 aD = *reinterpret_cast<const f32x4*>(tb + CTb::ALPHA + 16 * W + 4 * lgo);
-            const float eR = tb[CTb::ETA + 16 * W + l16o];
+            const f32x4 gdT = *reinterpret_cast<const f32x4*>(tb + CTb::GD + ml.oGdT);
+            const f32x4 aD = *reinterpret_cast<const f32x4*>(tb + CTb::ALPHA + 16 * W + 4 * lg);
+            const float eR = tb[CTb::ETA + iL];
+            f32x4 gdB;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = 4 * lgo + r;
-                const float gdB = tb[CTb::GD + (16 * W + (j > 0 ? j - 1 : 0)) * 16 + l16o];
-                m.mT[r] = j < l16o ? aiL * eJ[W][r] * gdT[r] : 0.f;
-                m.mB[r] = l16o < j ? aD[r] * eR * gdB : 0.f;
-            }
-            const int iA = 16 * X + l16o;
+            for (int r = 0; r < 4; ++r) gdB[r] = tb[CTb::GD + ml.oGdB + 16 * r];
+            m.mT = ml.fT * (aiL * (eJ[W] * gdT));
+            m.mB = ml.fB * (eR * (aD * gdB));
+            const int iA = 16 * X + l16;
             const float ra = tb[CTb::RA + iA], rg = tb[CTb::RG + iA];
 #pragma unroll
             for (int J = 0; J < X; ++J) {
-                const f32x4 gb = *reinterpret_cast<const f32x4*>(tb + CTb::GB + 64 * X + 16 * J + 4 * lgo);
-                const f32x4 mb = *reinterpret_cast<const f32x4*>(tb + CTb::MB + 64 * X + 16 * J + 4 * lgo);
+                const f32x4 gb = *reinterpret_cast<const f32x4*>(tb + CTb::GB + 64 * X + 16 * J + 4 * lg);
+                const f32x4 mb = *reinterpret_cast<const f32x4*>(tb + CTb::MB + 64 * X + 16 * J + 4 * lg);
                 m.mA[J] = eJ[J] * (ra * gb + rg * mb);
             }
-            const f32x4 gdA = *reinterpret_cast<const f32x4*>(tb + CTb::GD + iA * 16 + 4 * lgo);
+            const f32x4 gdA = *reinterpret_cast<const f32x4*>(tb + CTb::GD + iA * 16 + 4 * lg);
             m.mA[X] = eJ[X] * gdA;
             return m;
         };
@@ -541,12 +566,12 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
         // of A into A, for the chunk whose K tile is Kt and Q rows (block X)
         // are in qf[P]; W is this helper's index, a compile-time constant in
         // each copy.
-        auto prepare = [&](auto wc, char* B, const char* Kt, const Mult& m, auto par) {
+        auto prepare = [&](auto wc, char* B, const char* Kt, const Mult& m, const f32x4& Id,
+                           auto par) {
             constexpr int W = decltype(wc)::value;
             constexpr int X = 3 - W;
             constexpr int JN = W > X ? W : X;     // K blocks 0 .. JN are read
             constexpr int P = decltype(par)::value;
-            const int l16o = opaque(lane & 15), lgo = opaque(lane >> 4);
             // ---- Gram tiles, transposed (lane: row 16 x + l16, columns 16 J + 4 lg + r)
             f32x4 Gt[W + 1], At[X + 1];
 #pragma unroll
@@ -567,9 +592,6 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
             // N_WW in both accumulator layouts from the symmetric Gram tile:
             // NT = acc(N^T) (lane: row l16, cols 4 lg + r), NB = acc(N)
             const f32x4 NT = m.mT * Gt[W], NB = m.mB * Gt[W];
-            f32x4 Id;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Id[r] = 4 * lgo + r == l16o ? 1.f : 0.f;
             // D_W = (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8) (N^16 = 0),
             // formed transposed: D^T = (I + N8^T)(I + N4^T) P1^T
             const f32x4 N2B = prod(NT, NB), N2T = prod(NB, NT);
@@ -599,6 +621,7 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
         // nx + 2, Q rows of nx + 1), so waiting for all but the register loads
         // covers everything nx needs.
         auto run = [&](auto wc) {
+            const MultLane ml = mult_lane(wc);
             auto round = [&](int c, auto par) {      // par: parity of nx
                 constexpr int P = decltype(par)::value;
                 const int nx = c + 1;
@@ -622,8 +645,8 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
                     asm volatile("" ::: "memory");
                     if (more2) load_k(nx + 2);
                     if (more) load_q(nx + 1, IConst<1 - P>{});
-                    const Mult m = multipliers(wc, tables(nx));
-                    prepare(wc, B, kbuf(nx), m, par);
+                    const Mult m = multipliers(wc, tables(nx), ml);
+                    prepare(wc, B, kbuf(nx), m, ml.id, par);
                     // the tables of nx + 1, the V tile and coefficient rows of
                     // nx have landed; the register loads, issued after them,
                     // may still be in flight
