@@ -16,7 +16,11 @@
 // loaded once with 16-byte coalesced loads (a wavefront covers two full rows
 // per load), reduced twice through LDS (S^T k before the update, S^T q after
 // it) and stored once.  The columns of S and M are independent, which is why
-// the only cross-thread traffic is the two column reductions over Dk.
+// the only cross-thread traffic is the two column reductions over Dk.  The
+// state is read and written with non-temporal accesses: it is streamed once
+// per step and does not fit the caches at serving sizes (512 MiB at 256
+// sequences x 16 heads), and on gfx950 that measured 7% faster than plain
+// accesses for this read-modify-write stream.
 #include <hip/hip_runtime.h>
 
 #include "mfma.hpp"
@@ -51,8 +55,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
         const int row = ty + RPP * j;
-        s_reg[j] = *reinterpret_cast<const f32x4*>(Sh + (size_t)row * DV + 4 * tx);
-        m_reg[j] = *reinterpret_cast<const f32x4*>(Mh + (size_t)row * DV + 4 * tx);
+        s_reg[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sh + (size_t)row * DV + 4 * tx));
+        m_reg[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Mh + (size_t)row * DV + 4 * tx));
     }
     for (int i = tid; i < DK; i += 256) {
         ks[i] = to_f32(k[head * DK + i]);
@@ -85,8 +89,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         const float kr = ks[row];
         const f32x4 mn = m * m_reg[j] - (e * kr) * vt;
         const f32x4 sn = a * s_reg[j] - mn;
-        *reinterpret_cast<f32x4*>(Mh + (size_t)row * DV + 4 * tx) = mn;
-        *reinterpret_cast<f32x4*>(Sh + (size_t)row * DV + 4 * tx) = sn;
+        __builtin_nontemporal_store(mn, reinterpret_cast<f32x4*>(Mh + (size_t)row * DV + 4 * tx));
+        __builtin_nontemporal_store(sn, reinterpret_cast<f32x4*>(Sh + (size_t)row * DV + 4 * tx));
         acc_o += sn * qs[row];
     }
     __syncthreads();   // every thread has read red[] for S^T k
