@@ -21,6 +21,7 @@ The same JSON line carries:
   forward       the whole step against both roofs;
   decode        the recurrent decode step at 256 sequences x 16 heads, d 128
                 (GB/s of algorithmic state + token traffic);
+  sweep         tokens/s at T x B = 16384 tokens per call for T = 2K .. 16K;
   cpu_baseline  the fp64 oracle timed on this host's cores.
 Rank 0 prints one JSON line; only one GPU is supported.
 """
@@ -127,6 +128,7 @@ def parse():
     p.add_argument("--decode-steps", type=int, default=64)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-sweep", action="store_true")
     return p.parse_args()
 
 
@@ -255,6 +257,50 @@ def bench_decode(args, torch, si, mdn):
             "kernel": "decode_step_kernel", "traffic": traffic_bytes("decode_step_kernel")}
 
 
+# tokens/s against sequence length at a fixed 16,384 tokens per call (T x B), H = 16, d = 128,
+# gates as in the headline layer; the last point is the 16K-context layer
+SWEEP = [(2048, 8), (4096, 4), (8192, 2), (16384, 1)]
+
+
+def bench_sweep(args, torch, si, mdn):
+    import dataclasses
+    base = si.CONFIGS[2]
+    out = []
+    for T, B in SWEEP:
+        cfg = dataclasses.replace(base, name=f"sweep-bf16-B{B}H16T{T}d128", B=B, T=T,
+                                  seed=si.SEED_BASE + 100 + T // 1024)
+        inp = si.make_forward(cfg)
+        bf, f32 = torch.bfloat16, torch.float32
+        plan = mdn.ChunkPlan(up(inp["q"], bf), up(inp["k"], bf), up(inp["v"], bf),
+                             up(inp["alpha"], f32), up(inp["mu"], f32), up(inp["eta"], f32))
+        del inp
+        settle(torch, [plan.forward], args.settle)
+        for _ in range(args.warmup):
+            plan.forward()
+        (call_ms,), step_ms = time_calls(torch, [plan.forward], args.steps)
+        wg = B * cfg.H * (cfg.Dv // 64)
+        out.append({"T": T, "B": B, "H": cfg.H, "us_per_step": step_ms * 1e3,
+                    "tokens_per_s": B * T / (step_ms * 1e-3), "workgroups": wg})
+        log(f"sweep T{T} B{B}: {step_ms * 1e3:.1f} us/step, {B * T / (step_ms * 1e-3):.3e} tokens/s, "
+            f"{wg} workgroups")
+        del plan
+    return {"workload": "mdn_chunk_fwd, T x B = 16384 tokens per call, H16 d128, bf16",
+            "bound": "one workgroup per (b, h, 64 value columns) scans its chunks in sequence, "
+                     "so fewer than 256 workgroups leave CUs idle",
+            "points": out}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(inp, cfg):
     import oracle
     lib = oracle.load()
@@ -264,6 +310,7 @@ def cpu_baseline(inp, cfg):
     sec = time.perf_counter() - t0
     log(f"oracle: {sec:.1f}s on {cores} threads")
     return {"value": cfg.B * cfg.T / sec, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu": cpu_model(), "nproc": os.cpu_count(),
             "sample": f"the whole {cfg.name} workload (B{cfg.B} H{cfg.H} T{cfg.T} d{cfg.Dk}), "
                       f"fp64 token recurrence, one pass, {sec:.1f}s"}
 
@@ -285,6 +332,7 @@ def main():
     mdn.load_library()
     cfg, inp, step_ms, kernels, roofline, fwd, split = bench_forward(args, torch, si, mdn)
     decode = None if args.no_decode else bench_decode(args, torch, si, mdn)
+    sweep = None if args.no_sweep else bench_sweep(args, torch, si, mdn)
     base = None if args.no_cpu_baseline else cpu_baseline(inp, cfg)
     tokens = cfg.B * cfg.T
     line = {
@@ -308,6 +356,7 @@ def main():
         "kernels": kernels,
         "split_path": split,
         "decode": decode,
+        "sweep": sweep,
         "cpu_baseline": base,
     }
     print(json.dumps(line), flush=True)
