@@ -66,6 +66,7 @@
 namespace mdn {
 
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 
 template <int N>
 struct IConst {
@@ -848,12 +849,28 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
             }
         }
         {
-            E* Ob = Ocol + (size_t)t0 * ostride;
+            // One 16-byte store per lane per pair of row tiles: lane groups
+            // lg and lg ^ 1 (lg = 2 x, 2 x + 1) swap halves of row tiles 2 p and
+            // 2 p + 1 (permlane16_swap exchanges group 1 of its first operand
+            // with group 0 of its second, and group 3 with group 2), after which
+            // each lane holds 8 consecutive columns, 8 x .. 8 x + 7 of this
+            // wave's 16, of row 16 (2 p + (lg & 1)) + l16.  Half the store
+            // instructions of one 8-byte store per row tile.
+            E* Ob = Ocol - 4 * lg + 8 * (lg >> 1) + (size_t)t0 * ostride;
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
-                if (16 * ct + l16 < n)
-                    store4<E>(Ob + (unsigned)(16 * ct + l16) * ostride, Ot[ct][0], Ot[ct][1],
-                              Ot[ct][2], Ot[ct][3]);
+            for (int p = 0; p < 2; ++p) {
+                u32x2 ua = __builtin_bit_cast(u32x2, to_bf4(Ot[2 * p]));
+                u32x2 ub = __builtin_bit_cast(u32x2, to_bf4(Ot[2 * p + 1]));
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    const auto r = __builtin_amdgcn_permlane16_swap(ua[d], ub[d], false, false);
+                    ua[d] = r[0];
+                    ub[d] = r[1];
+                }
+                const int row = 16 * (2 * p + (lg & 1)) + l16;
+                if (row < n)
+                    *reinterpret_cast<u32x4*>(Ob + (unsigned)row * ostride) = u32x4{ua[0], ua[1], ub[0], ub[1]};
+            }
         }
 
         // (5) S' = abar_n S0 - b_n M0 + K^T Diag(eta gamma_n) Vt,
