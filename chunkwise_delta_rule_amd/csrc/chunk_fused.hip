@@ -126,10 +126,19 @@ __host__ __device__ constexpr FragSlot frag_slot(int x, int J)
 // A blocks at equal offsets are never merged into one two-address access
 constexpr int FRAG_AREA = 4096 + 640 + 512;
 
+// x rounded to bf16 (nearest even).  Built from two packed 32-bit words: a
+// 4-element bf16 vector built element by element and fed to a 16x16x16 MFMA
+// is converted one element at a time (four conversions and two byte
+// permutes instead of two packed conversions).
+__device__ __forceinline__ unsigned pack_bf16(float a, float b)
+{
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    return __builtin_bit_cast(unsigned, bf16x2{static_cast<__bf16>(a), static_cast<__bf16>(b)});
+}
 __device__ __forceinline__ bf16x4 to_bf4(const f32x4& x)
 {
-    return bf16x4{static_cast<__bf16>(x[0]), static_cast<__bf16>(x[1]),
-                  static_cast<__bf16>(x[2]), static_cast<__bf16>(x[3])};
+    typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+    return __builtin_bit_cast(bf16x4, u32x2_t{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])});
 }
 
 // value of x in lane l (l uniform)
@@ -708,18 +717,20 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
     if (M0) load_state(Ma, M0); else load_state(Ma, nullptr);
 
     // per-lane LDS offsets, the same every chunk
-    int kq_base[4];                            // row 16 x + l16, d-chunk lg
-#pragma unroll
-    for (int x = 0; x < 4; ++x) kq_base[x] = LK::chunk(16 * x + l16, lg);
+    // row 16 x + l16, d-chunk lg: rows 16 apart share the swizzle, so the
+    // four row blocks are one lane offset plus a constant
+    const int kq0 = LK::chunk(l16, lg);
+    auto kq_base = [&](int x) { return kq0 + x * LK::J16; };
     // transposing reads: lane 4 j + m of a 16-lane group reads row base + j,
     // 4 columns starting at 4 m of the wanted column block
     const int trj = l16 >> 2, trm = l16 & 3;
-    int ktr_base[RT];                          // K rows 4 lg + j (+ 16 J), d = phys_row(16 rt + 4 m)
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const int d0 = phys_row(16 * rt + 4 * trm);
-        ktr_base[rt] = LK::chunk(4 * lg + trj, d0 >> 3) + 2 * (d0 & 7);
-    }
+    // K rows 4 lg + j (+ 16 J), columns d0 = phys_row(16 rt + 4 m) .. + 3,
+    // with d0 = 32 (rt >> 1) + 8 m + 4 (rt & 1): the d-chunk is
+    // 4 (rt >> 1) + m, whose swizzle with key (row >> 2) & 3 = lg leaves
+    // 4 (rt >> 1) alone, so every rt is one lane offset plus a constant
+    // (instruction immediates instead of an address add per read)
+    const int ktr0 = LK::chunk(4 * lg + trj, trm);
+    auto ktr_base = [&](int rt) { return ktr0 + 64 * (rt >> 1) + 8 * (rt & 1); };
     constexpr int KJ = LK::J16;                // 16 K rows further
     const int vc = 16 * wave + 4 * trm;
     const int vtr_base = LC::chunk(4 * lg + trj, vc >> 3) + 2 * (vc & 7);
@@ -752,7 +763,7 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
                 const auto bM = MM::from_acc(Ma, s);
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
-                    const auto aK = *reinterpret_cast<const MM::frag*>(Kb + kq_base[ct] + 64 * s);
+                    const auto aK = *reinterpret_cast<const MM::frag*>(Kb + kq_base(ct) + 64 * s);
                     xs[ct] = MM::mma(aK, bS, xs[ct]);
                     xm[ct] = MM::mma(aK, bM, xm[ct]);
                 }
@@ -784,7 +795,7 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
                 const auto bM = MM::from_acc(Ma, s);
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
-                    const auto aQ = *reinterpret_cast<const MM::frag*>(Qb + kq_base[ct] + 64 * s);
+                    const auto aQ = *reinterpret_cast<const MM::frag*>(Qb + kq_base(ct) + 64 * s);
                     ys[ct] = MM::mma(bS, aQ, ys[ct]);
                     ym[ct] = MM::mma(bM, aQ, ym[ct]);
                 }
@@ -884,7 +895,12 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
             Ma[rt] = mbn * Ma[rt];
         }
         // K^T fragments by transposing reads, two 16-row blocks of the chunk
-        // per 16x16x32 step (k = chunk rows 32 p .. 32 p + 31)
+        // per 16x16x32 step (k = chunk rows 32 p .. 32 p + 31).  The lane's
+        // base address is fixed here, so that every read is that base plus an
+        // instruction immediate (left to itself the compiler rebases on a
+        // later block and pays an address add per read for the negative
+        // offsets of the others).
+        const int ktb = opaque((int)(Kb - smem) + ktr0);
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             bf16x4 bS[2], bM[2];
@@ -899,8 +915,9 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
             const auto bS8 = cat8(bS[0], bS[1]), bM8 = cat8(bM[0], bM[1]);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                const auto aK = cat8(lds_read_tr4(Kb + ktr_base[rt] + 2 * p * KJ),
-                                     lds_read_tr4(Kb + ktr_base[rt] + (2 * p + 1) * KJ));
+                const int off = ktr_base(rt) - ktr0;   // a constant
+                const auto aK = cat8(lds_read_tr4(smem + ktb + off + 2 * p * KJ),
+                                     lds_read_tr4(smem + ktb + off + (2 * p + 1) * KJ));
                 Sa[rt] = MM::mma(aK, bS8, Sa[rt]);
                 Ma[rt] = MM::mma(aK, bM8, Ma[rt]);
             }
