@@ -81,6 +81,7 @@ struct ChunkTables {
     static constexpr int ETA = 64;
     static constexpr int RA = 128;            // block-local products of the rows
     static constexpr int RG = 192;
+    // the three below are scaled by eta_j of their column j
     static constexpr int GB = 256;            // [4][64]: gamma at row 16 I - 1, column j (j < 16 I)
     static constexpr int MB = 512;            // [4][64]: m at row 16 I - 1
     static constexpr int GD = 768;            // [64][16]: row i, column 16 (i / 16) + jj of Gamma
@@ -161,9 +162,10 @@ __device__ __forceinline__ float dpp_shr(float x, int d, float fill)
     return __int_as_float(r);
 }
 
-// A lane-dependent value the compiler must treat as new at this point: keeps
-// per-lane comparisons made from it inside the chunk loop instead of hoisted
-// out of it as lane masks (which would then live in spilled SGPRs).
+// x in a VGPR, as a value the compiler must treat as new at this point.  An
+// LDS address made this way stays the base of the accesses after it (their
+// constant offsets become instruction immediates), instead of being
+// re-derived, or rebased on a later access, from its parts.
 __device__ __forceinline__ int opaque(int x)
 {
     asm volatile("" : "+v"(x));
@@ -300,14 +302,16 @@ __global__ __launch_bounds__(NT) void chunk_coef_kernel(const float* __restrict_
     tb[CTb::ETA + lane] = ge;
     tb[CTb::RA + lane] = ra;
     tb[CTb::RG + lane] = rg;
+    // the Gamma tables carry the eta of their column (column `lane`), the
+    // factor every use of them applies
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-        tb[CTb::GB + 64 * I + lane] = gbI[I];
-        tb[CTb::MB + 64 * I + lane] = mbI[I];
+        tb[CTb::GB + 64 * I + lane] = ge * gbI[I];
+        tb[CTb::MB + 64 * I + lane] = ge * mbI[I];
     }
     // diagonal block of Gamma, one column per lane (zero above the diagonal)
 #pragma unroll
-    for (int t = 0; t < 16; ++t) tb[CTb::GD + (16 * blk + t) * 16 + off] = gd[t];
+    for (int t = 0; t < 16; ++t) tb[CTb::GD + (16 * blk + t) * 16 + off] = ge * gd[t];
     float* vec = tb + CTb::VEC;
     vec[V_ABAR * CH + lane] = valid ? abar : 0.f;
     vec[V_AB1 * CH + lane] = valid && lane > 0 ? ga * bprev : 0.f;
@@ -424,25 +428,28 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
         auto prod = [](const f32x4& XT, const f32x4& YB) {
             return mma16(to_bf4(XT), to_bf4(YB), zero4());
         };
-        // element offsets of this lane's K and Q rows inside a chunk (rows
-        // past the end of a partial last chunk repeat its last row)
-        const unsigned rowstride = (unsigned)(H * DK);
-        const unsigned offK = (unsigned)(rK + l16) * rowstride + 8u * (unsigned)lg;
-        const unsigned offQ = (unsigned)(rQ + l16) * rowstride + 8u * (unsigned)lg;
-        auto lane_off = [&](int c, int r, unsigned full) {
-            const int n = chunk_rows(c);
-            return n == CH ? full : (unsigned)min(r + l16, n - 1) * rowstride + 8u * (unsigned)lg;
-        };
+        // byte offsets of this lane's K and Q rows inside a chunk, for full
+        // chunks and for a partial last chunk (whose rows past its end repeat
+        // its last row); 32-bit offsets from a uniform base let the loads use
+        // the scalar-base address form
+        const unsigned rowbytes = (unsigned)(H * DK) * 2u;
+        const int n_last = T - (NC - 1) * CH;
+        auto row_off = [&](int r) { return (unsigned)r * rowbytes + 16u * (unsigned)lg; };
+        const unsigned offK = row_off(rK + l16), offQ = row_off(rQ + l16);
+        const unsigned offK_last = row_off(min(rK + l16, n_last - 1));
+        const unsigned offQ_last = row_off(min(rQ + l16, n_last - 1));
         auto load_k = [&](int c) {
-            const __bf16* src = k + tok_base(c) * DK + lane_off(c, rK, offK);
+            const char* src = reinterpret_cast<const char*>(k + tok_base(c) * DK);
+            const unsigned o = c == NC - 1 ? offK_last : offK;
 #pragma unroll
-            for (int u = 0; u < SK; ++u) kf[u] = *reinterpret_cast<const MM::frag*>(src + 32 * u);
+            for (int u = 0; u < SK; ++u) kf[u] = *reinterpret_cast<const MM::frag*>(src + o + 64 * u);
         };
         auto load_q = [&](int c, auto par) {
             constexpr int P = decltype(par)::value;
-            const __bf16* src = q + tok_base(c) * DK + lane_off(c, rQ, offQ);
+            const char* src = reinterpret_cast<const char*>(q + tok_base(c) * DK);
+            const unsigned o = c == NC - 1 ? offQ_last : offQ;
 #pragma unroll
-            for (int u = 0; u < SK; ++u) qf[P][u] = *reinterpret_cast<const MM::frag*>(src + 32 * u);
+            for (int u = 0; u < SK; ++u) qf[P][u] = *reinterpret_cast<const MM::frag*>(src + o + 64 * u);
         };
         // rows >= n of a partial last chunk become zero (in the registers
         // too), so that the Gram products, L and A vanish there
@@ -454,10 +461,14 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
                 for (int u = 0; u < SK; ++u) f[u] = live ? f[u] : zfrag;
             }
         };
-        auto store_rows = [&](char* dst, int r0, const MM::frag* f) {
+        // the rows' LDS offsets: rows 16 apart share the swizzle, and d-chunk
+        // 4 u + lg lies 64 u bytes after d-chunk lg, so one lane offset plus
+        // immediates covers the four stores; the buffer's base is added once
+        const int stK = LK::chunk(rK + l16, lg), stQ = LK::chunk(rQ + l16, lg);
+        auto store_rows = [&](const char* dst, int st, const MM::frag* f) {
+            const int a = opaque((int)(dst - smem) + st);
 #pragma unroll
-            for (int u = 0; u < SK; ++u)
-                *reinterpret_cast<MM::frag*>(dst + LK::chunk(r0 + l16, 4 * u + lg)) = f[u];
+            for (int u = 0; u < SK; ++u) *reinterpret_cast<MM::frag*>(smem + a + 64 * u) = f[u];
         };
         // direct loads of chunk c's V tile and coefficient rows into buffer B
         auto load_v = [&](int c, char* B) {
@@ -524,37 +535,32 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
             const int iL = 16 * W + l16;
             const float aiL = tb[CTb::ALPHA + iL];
             const float raP = tb[CTb::RA + ml.oP], rgP = tb[CTb::RG + ml.oP];
-            // gamma_{i-1,j} = raP gb + rgP mb, and gb itself on the first row
+            // gamma_{i-1,j} = raP gb + rgP mb, and gb itself on the first row;
+            // -alpha_i folded into the two row factors (the tables carry eta_j)
             const float raZ = raP + ml.z0 * (1.f - raP), rgZ = rgP - ml.z0 * rgP;
-            f32x4 eJ[4];
-#pragma unroll
-            for (int J = 0; J < 4; ++J)
-                if (J <= W || J <= X)
-                    eJ[J] = *reinterpret_cast<const f32x4*>(tb + CTb::ETA + 16 * J + 4 * lg);
+            const float cL = -aiL * raZ, dL = -aiL * rgZ;
 #pragma unroll
             for (int J = 0; J < W; ++J) {
                 const f32x4 gb = *reinterpret_cast<const f32x4*>(tb + CTb::GB + 64 * W + 16 * J + 4 * lg);
                 const f32x4 mb = *reinterpret_cast<const f32x4*>(tb + CTb::MB + 64 * W + 16 * J + 4 * lg);
-                m.mL[J] = (-aiL) * eJ[J] * (raZ * gb + rgZ * mb);
+                m.mL[J] = cL * gb + dL * mb;
             }
             const f32x4 gdT = *reinterpret_cast<const f32x4*>(tb + CTb::GD + ml.oGdT);
             const f32x4 aD = *reinterpret_cast<const f32x4*>(tb + CTb::ALPHA + 16 * W + 4 * lg);
-            const float eR = tb[CTb::ETA + iL];
             f32x4 gdB;
 #pragma unroll
             for (int r = 0; r < 4; ++r) gdB[r] = tb[CTb::GD + ml.oGdB + 16 * r];
-            m.mT = ml.fT * (aiL * (eJ[W] * gdT));
-            m.mB = ml.fB * (eR * (aD * gdB));
+            m.mT = ml.fT * (aiL * gdT);
+            m.mB = ml.fB * (aD * gdB);
             const int iA = 16 * X + l16;
             const float ra = tb[CTb::RA + iA], rg = tb[CTb::RG + iA];
 #pragma unroll
             for (int J = 0; J < X; ++J) {
                 const f32x4 gb = *reinterpret_cast<const f32x4*>(tb + CTb::GB + 64 * X + 16 * J + 4 * lg);
                 const f32x4 mb = *reinterpret_cast<const f32x4*>(tb + CTb::MB + 64 * X + 16 * J + 4 * lg);
-                m.mA[J] = eJ[J] * (ra * gb + rg * mb);
+                m.mA[J] = ra * gb + rg * mb;
             }
-            const f32x4 gdA = *reinterpret_cast<const f32x4*>(tb + CTb::GD + iA * 16 + 4 * lg);
-            m.mA[X] = eJ[X] * gdA;
+            m.mA[X] = *reinterpret_cast<const f32x4*>(tb + CTb::GD + iA * 16 + 4 * lg);
             return m;
         };
 
@@ -644,10 +650,10 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
                     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                     if (more) {
                         zero_tail(nx + 1, rK, kf);
-                        store_rows(kbuf(nx + 1), rK, kf);
+                        store_rows(kbuf(nx + 1), stK, kf);
                     }
                     zero_tail(nx, rQ, qf[P]);
-                    store_rows(B + L::OFF_Q, rQ, qf[P]);
+                    store_rows(B + L::OFF_Q, stQ, qf[P]);
                     if (more) load_tables(nx + 1);
                     load_v(nx, B);
                     // keep the register loads after the direct loads: the
@@ -680,7 +686,7 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
             load_k(0);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             zero_tail(0, rK, kf);
-            store_rows(kbuf(0), rK, kf);
+            store_rows(kbuf(0), stK, kf);
             if (NC > 1) load_k(1);
             load_q(0, IConst<0>{});
             load_tables(0);
