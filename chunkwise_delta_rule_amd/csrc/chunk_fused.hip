@@ -78,17 +78,30 @@ struct IConst {
 // coefficient rows, which go to the chunk's operand buffer).
 struct ChunkTables {
     static constexpr int ALPHA = 0;           // gates of the rows
-    static constexpr int ETA = 64;
-    static constexpr int RA = 128;            // block-local products of the rows
-    static constexpr int RG = 192;
+    static constexpr int RA = 64;             // block-local products of the rows
+    static constexpr int RG = 128;
     // the three below are scaled by eta_j of their column j
-    static constexpr int GB = 256;            // [4][64]: gamma at row 16 I - 1, column j (j < 16 I)
-    static constexpr int MB = 512;            // [4][64]: m at row 16 I - 1
-    static constexpr int GD = 768;            // [64][16]: row i, column 16 (i / 16) + jj of Gamma
-    static constexpr int VEC = 1792;          // the six coefficient rows (V_ABAR .. V_SCAL)
-    static constexpr int LDS_FLOATS = VEC;    // what the fused kernel keeps in LDS
+    static constexpr int GB = 192;            // [3][64]: gamma at row 16 I - 1, column j (j < 16 I), I = 1..3
+    static constexpr int MB = 384;            // [3][64]: m at row 16 I - 1
+    static constexpr int GD = 576;            // Gamma's diagonal blocks, rows packed (gd_row)
+    static constexpr int GD_ZERO = GD + 4 * 160;   // four zeros
+    static constexpr int VEC = 1280;          // the six coefficient rows
+    static constexpr int LDS_FLOATS = VEC;    // what the fused kernel keeps in LDS (5 KB)
     static constexpr int FLOATS = VEC + 6 * CH;
 };
+
+// Offset from ChunkTables::GD of row i (0..63) of Gamma's diagonal blocks.
+// Block-local row r keeps columns 0 .. 4 ((r >> 2) + 1) - 1 of its block: the
+// lower triangle, rounded up to whole 16-byte pieces (the entries above the
+// diagonal in them are zero), 160 floats per block.
+__host__ __device__ constexpr int gd_row(int i)
+{
+    const int r = i & 15, q = r >> 2;
+    return 160 * (i >> 4) + 4 * (2 * q * (q + 1) + (r & 3) * (q + 1));
+}
+__host__ __device__ constexpr int gd_len(int i) { return 4 * (((i & 15) >> 2) + 1); }
+static_assert(gd_row(15) + gd_len(15) == 160 && gd_row(63) + gd_len(63) == 640, "packed rows");
+static_assert(ChunkTables::GD_ZERO + 4 <= ChunkTables::VEC, "tables overlap");
 
 size_t chunk_fused_workspace_bytes(size_t nchunks)
 {
@@ -191,7 +204,9 @@ __global__ __launch_bounds__(NT) void chunk_coef_kernel(const float* __restrict_
 {
     using CTb = ChunkTables;
     __shared__ __align__(16) float gates[4][2][CH];
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the wavefront index as a uniform value, so that the chunk's indices
+    // and addresses are scalar arithmetic
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const size_t ch = (size_t)blockIdx.x * 4 + wv;
     if (ch >= nchunks) return;   // whole wavefronts; this kernel has no barrier
     const int c = (int)(ch % NC);
@@ -232,15 +247,16 @@ __global__ __launch_bounds__(NT) void chunk_coef_kernel(const float* __restrict_
     }
     // the diagonal-block column recursion of column `lane` over its block's
     // rows: gamma_jj = 1, m_jj = 1; below the diagonal m_t = mu_t m_{t-1},
-    // gamma_t = alpha_t gamma_{t-1} + m_t
-    float gam = 1.f, mm = 1.f;
+    // gamma_t = alpha_t gamma_{t-1} + m_t.  Every lane runs all 16 rows from
+    // m = gamma = 0 and gets a 1 added to m on its diagonal row, which starts
+    // the recursion there and leaves the rows above it at zero.
+    float gam = 0.f, mm = 0.f;
     float gd[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-        const bool below = t > off;
-        mm = below ? mm * mbk[t] : mm;
-        gam = below ? ab[t] * gam + mm : gam;
-        gd[t] = t >= off ? gam : 0.f;
+        mm = mbk[t] * mm + (t == off ? 1.f : 0.f);
+        gam = ab[t] * gam + mm;
+        gd[t] = gam;
     }
     // block summaries (values at each block's last row)
     const float sa0 = readlane_f(ra, 15), sa1 = readlane_f(ra, 31), sa2 = readlane_f(ra, 47);
@@ -299,19 +315,21 @@ __global__ __launch_bounds__(NT) void chunk_coef_kernel(const float* __restrict_
 
     // ---- stores
     tb[CTb::ALPHA + lane] = ga;
-    tb[CTb::ETA + lane] = ge;
     tb[CTb::RA + lane] = ra;
     tb[CTb::RG + lane] = rg;
     // the Gamma tables carry the eta of their column (column `lane`), the
     // factor every use of them applies
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
-        tb[CTb::GB + 64 * I + lane] = ge * gbI[I];
-        tb[CTb::MB + 64 * I + lane] = ge * mbI[I];
+    for (int I = 1; I < 4; ++I) {
+        tb[CTb::GB + 64 * (I - 1) + lane] = ge * gbI[I];
+        tb[CTb::MB + 64 * (I - 1) + lane] = ge * mbI[I];
     }
-    // diagonal block of Gamma, one column per lane (zero above the diagonal)
+    // diagonal block of Gamma, one column per lane (zero above the diagonal),
+    // the stored part of each row
 #pragma unroll
-    for (int t = 0; t < 16; ++t) tb[CTb::GD + (16 * blk + t) * 16 + off] = ge * gd[t];
+    for (int t = 0; t < 16; ++t)
+        if (off < gd_len(t)) tb[CTb::GD + gd_row(16 * blk + t) + off] = ge * gd[t];
+    if (lane < 4) tb[CTb::GD_ZERO + lane] = 0.f;
     float* vec = tb + CTb::VEC;
     vec[V_ABAR * CH + lane] = valid ? abar : 0.f;
     vec[V_AB1 * CH + lane] = valid && lane > 0 ? ga * bprev : 0.f;
@@ -479,7 +497,7 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
             if (hw == 0 || (hw == 1 && lane < 32))
                 direct_load16(src + 4 * (64 * hw + lane), B + L::OFF_VEC + 1024 * hw);
         };
-        // direct loads of chunk c's tables into its table set: 7 pieces of
+        // direct loads of chunk c's tables into its table set: 5 pieces of
         // 1 KB, helper h takes pieces h and h + 4
         auto load_tables = [&](int c) {
             const float* src = ctab + ((size_t)bh * NC + c) * CTb::FLOATS;
@@ -506,7 +524,8 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
         struct MultLane {
             int oP;          // row iL - 1 (iL itself on the block's first row)
             int oGdT;        // GD row iL - 1 (clamped), columns 4 lg ..
-            int oGdB;        // GD row 16 W + 4 lg - 1, column l16 (+ 16 per r)
+            int oGdB[4];     // GD row 16 W + 4 lg + r - 1, column l16
+            int oGdA;        // GD row 16 X + l16, columns 4 lg .. (the zeros past its stored part)
             float z0;        // 1 on the block's first row
             f32x4 fT, fB;    // strictly below the diagonal in either layout
             f32x4 id;        // the identity in the accumulator layout
@@ -516,8 +535,17 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
             MultLane ml;
             const int iL = 16 * W + l16;
             ml.oP = l16 > 0 ? iL - 1 : iL;
-            ml.oGdT = (16 * W + (l16 > 0 ? l16 - 1 : 0)) * 16 + 4 * lg;
-            ml.oGdB = (16 * W + 4 * lg - 1) * 16 + l16;   // (r = 0, lg = 0): masked
+            // entries read past a row's stored part are masked below (fT, fB)
+            // and finite; A's diagonal block has no mask, so its lanes past
+            // the stored part read the zeros
+            ml.oGdT = CTb::GD + gd_row(16 * W + (l16 > 0 ? l16 - 1 : 0)) + 4 * lg;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * W + 4 * lg + r - 1;      // -1 (W = 0): masked
+                ml.oGdB[r] = row < 0 ? CTb::GD_ZERO : CTb::GD + gd_row(row) + l16;
+            }
+            const int iA = 16 * (3 - W) + l16;
+            ml.oGdA = 4 * lg < gd_len(iA) ? CTb::GD + gd_row(iA) + 4 * lg : CTb::GD_ZERO;
             ml.z0 = l16 == 0 ? 1.f : 0.f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -541,26 +569,26 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
             const float cL = -aiL * raZ, dL = -aiL * rgZ;
 #pragma unroll
             for (int J = 0; J < W; ++J) {
-                const f32x4 gb = *reinterpret_cast<const f32x4*>(tb + CTb::GB + 64 * W + 16 * J + 4 * lg);
-                const f32x4 mb = *reinterpret_cast<const f32x4*>(tb + CTb::MB + 64 * W + 16 * J + 4 * lg);
+                const f32x4 gb = *reinterpret_cast<const f32x4*>(tb + CTb::GB + 64 * (W - 1) + 16 * J + 4 * lg);
+                const f32x4 mb = *reinterpret_cast<const f32x4*>(tb + CTb::MB + 64 * (W - 1) + 16 * J + 4 * lg);
                 m.mL[J] = cL * gb + dL * mb;
             }
-            const f32x4 gdT = *reinterpret_cast<const f32x4*>(tb + CTb::GD + ml.oGdT);
+            const f32x4 gdT = *reinterpret_cast<const f32x4*>(tb + ml.oGdT);
             const f32x4 aD = *reinterpret_cast<const f32x4*>(tb + CTb::ALPHA + 16 * W + 4 * lg);
             f32x4 gdB;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) gdB[r] = tb[CTb::GD + ml.oGdB + 16 * r];
+            for (int r = 0; r < 4; ++r) gdB[r] = tb[ml.oGdB[r]];
             m.mT = ml.fT * (aiL * gdT);
             m.mB = ml.fB * (aD * gdB);
             const int iA = 16 * X + l16;
             const float ra = tb[CTb::RA + iA], rg = tb[CTb::RG + iA];
 #pragma unroll
             for (int J = 0; J < X; ++J) {
-                const f32x4 gb = *reinterpret_cast<const f32x4*>(tb + CTb::GB + 64 * X + 16 * J + 4 * lg);
-                const f32x4 mb = *reinterpret_cast<const f32x4*>(tb + CTb::MB + 64 * X + 16 * J + 4 * lg);
+                const f32x4 gb = *reinterpret_cast<const f32x4*>(tb + CTb::GB + 64 * (X - 1) + 16 * J + 4 * lg);
+                const f32x4 mb = *reinterpret_cast<const f32x4*>(tb + CTb::MB + 64 * (X - 1) + 16 * J + 4 * lg);
                 m.mA[J] = ra * gb + rg * mb;
             }
-            m.mA[X] = *reinterpret_cast<const f32x4*>(tb + CTb::GD + iA * 16 + 4 * lg);
+            m.mA[X] = *reinterpret_cast<const f32x4*>(tb + ml.oGdA);
             return m;
         };
 

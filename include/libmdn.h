@@ -65,10 +65,10 @@ typedef enum {
 /*
  * Bytes of device workspace mdn_chunk_fwd needs for this problem.  With
  * dt = MDN_BF16 the forward keeps the chunk-local matrices T and A on chip
- * and needs only per-chunk coefficient tables (8704 bytes per chunk of 64
+ * and needs only per-chunk coefficient tables (6656 bytes per chunk of 64
  * tokens and head: the gates, the block products and boundary values of
- * the slides' Gamma of Eqs. (7)-(9), its 16 x 16 diagonal blocks and the
- * six coefficient rows the scan reads).  With MDN_F32 it runs as the two
+ * the slides' Gamma of Eqs. (7)-(9), the lower triangles of its 16 x 16
+ * diagonal blocks and the six coefficient rows the scan reads).  With MDN_F32 it runs as the two
  * phases below and needs what mdn_chunk_fwd_split_workspace_bytes returns.
  * Returns 0 for unsupported or invalid sizes and when no work is needed
  * (B, T or H is 0).

@@ -53,10 +53,11 @@ def test_workspace_bytes(lib):
     assert split(1, 65, 2, 64, 64, 64, mdn.MDN_F32) == 2 * 2 * per_f32     # ragged: 2 chunks
     assert split(1, 1, 1, 64, 128, 64, mdn.MDN_BF16) == per_bf16
     # the bf16 forward keeps T and A on chip and needs only per-chunk coefficient
-    # tables (gates, block products, boundary values, Gamma's diagonal blocks,
-    # six coefficient rows: 2176 floats); fp32 uses the split path
-    assert ws(8, 4096, 16, 128, 128, 64, mdn.MDN_BF16) == 8 * 16 * 64 * 2176 * 4
-    assert ws(1, 65, 2, 64, 64, 64, mdn.MDN_BF16) == 2 * 2 * 2176 * 4
+    # tables (gates, block products, boundary values, Gamma's diagonal blocks
+    # packed to their lower triangles, six coefficient rows: 1664 floats); fp32
+    # uses the split path
+    assert ws(8, 4096, 16, 128, 128, 64, mdn.MDN_BF16) == 8 * 16 * 64 * 1664 * 4
+    assert ws(1, 65, 2, 64, 64, 64, mdn.MDN_BF16) == 2 * 2 * 1664 * 4
     assert ws(1, 65, 2, 64, 64, 64, mdn.MDN_F32) == 2 * 2 * per_f32
     for bad in [(0, 64, 1, 64, 64, 64, 1), (1, 0, 1, 64, 64, 64, 1), (1, 64, 1, 96, 64, 64, 1),
                 (1, 64, 1, 64, 64, 32, 1), (1, 64, 1, 64, 64, 64, 7), (-1, 64, 1, 64, 64, 64, 1)]:
