@@ -185,47 +185,61 @@ __device__ __forceinline__ int opaque(int x)
     return x;
 }
 
-// LDS ordering inside one wavefront (data written by other lanes of it)
-__device__ __forceinline__ void wave_lds_sync()
-{
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-}
-
 // ---------------------------------------------------------------------------
-// Coefficient tables of every chunk.  Four chunks per workgroup, one per
-// wavefront; lane l is row l (for the row quantities) and column l (for the
-// column recursion); its 16-row block is l / 16.
+// Coefficient tables of every chunk.  A workgroup takes one chunk of up to
+// 16 heads (workgroup g: chunk g % NC of batch row (g / NC) / NHG, heads
+// 16 ((g / NC) % NHG) ..): it reads the gates of those heads and rows as
+// contiguous memory (a head's own gates are H floats apart), stages them in
+// LDS by head, and wavefront w then builds the tables of head w; lane l is
+// row l (for the row quantities) and column l (for the column recursion);
+// its 16-row block is l / 16.
+constexpr int COEF_HEADS = 16;   // heads per workgroup, one wavefront each
+constexpr int COEF_PITCH = CH + 4;   // LDS floats per head row (16-byte aligned, spreads banks)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(NT) void chunk_coef_kernel(const float* __restrict__ alpha,
-                                                        const float* __restrict__ mu,
-                                                        const float* __restrict__ eta,
-                                                        float* __restrict__ ws, int T, int H,
-                                                        int NC, size_t nchunks)
+__global__ __launch_bounds__(COEF_HEADS * 64) void chunk_coef_kernel(
+    const float* __restrict__ alpha, const float* __restrict__ mu, const float* __restrict__ eta,
+    float* __restrict__ ws, int T, int H, int NC, unsigned NHG)
 {
     using CTb = ChunkTables;
-    __shared__ __align__(16) float gates[4][2][CH];
+    __shared__ __align__(16) float gates[3][COEF_HEADS][COEF_PITCH];
+    // 32-bit indices: B NC NHG is below 2^32 (the entry points check it)
+    const unsigned g = blockIdx.x / (unsigned)NC;
+    const int c = (int)(blockIdx.x - g * (unsigned)NC);
+    const int b = (int)(g / NHG), h0 = (int)(g - (unsigned)b * NHG) * COEF_HEADS;
+    const int hg = min(COEF_HEADS, H - h0);            // heads of this workgroup
+    const int n = min(CH, T - c * CH), last = n - 1;
+    {
+        // element e = row (e / hg) of head h0 + e % hg: consecutive threads read
+        // consecutive floats; rows past a partial chunk's end repeat its last
+        const size_t g0 = ((size_t)b * T + (size_t)c * CH) * H + h0;
+        for (int e = threadIdx.x; e < CH * hg; e += COEF_HEADS * 64) {
+            const int t = e / hg, hh = e - t * hg;
+            const size_t gi = g0 + (size_t)min(t, last) * H + hh;
+            gates[0][hh][t] = alpha[gi];
+            gates[1][hh][t] = mu[gi];
+            gates[2][hh][t] = eta[gi];
+        }
+    }
+    __syncthreads();
     // the wavefront index as a uniform value, so that the chunk's indices
     // and addresses are scalar arithmetic
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const size_t ch = (size_t)blockIdx.x * 4 + wv;
-    if (ch >= nchunks) return;   // whole wavefronts; this kernel has no barrier
-    const int c = (int)(ch % NC);
-    const size_t bh = ch / NC;
-    const int h = (int)(bh % H), b = (int)(bh / H);
-    const int n = min(CH, T - c * CH), last = n - 1;
-    const size_t gi = ((size_t)b * T + (size_t)c * CH + min(lane, last)) * H + h;
-    const float ga = alpha[gi], gm = mu[gi], ge = eta[gi];
-    float* tb = ws + ch * CTb::FLOATS;
+    if (wv >= hg) return;   // whole wavefronts; no barrier follows
+    const int h = h0 + wv;
+    const float ga = gates[0][wv][lane], gm = gates[1][wv][lane], ge = gates[2][wv][lane];
+    float* tb = ws + (((size_t)b * H + h) * NC + c) * CTb::FLOATS;
 
+    // Each table is stored as soon as it is known: every wavefront of the
+    // grid is resident at once and runs the same steps in step, so stores
+    // left to the end would leave the whole table write to one burst after
+    // all the arithmetic instead of overlapping it.
+    tb[CTb::ALPHA + lane] = ga;
     const int blk = lane >> 4, off = lane & 15;
-    gates[wv][0][lane] = ga;
-    gates[wv][1][lane] = gm;
-    wave_lds_sync();
     float ab[16], mbk[16];
 #pragma unroll
     for (int t = 0; t < 16; t += 4) {
-        const f32x4 a4 = *reinterpret_cast<const f32x4*>(&gates[wv][0][16 * blk + t]);
-        const f32x4 m4 = *reinterpret_cast<const f32x4*>(&gates[wv][1][16 * blk + t]);
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(&gates[0][wv][16 * blk + t]);
+        const f32x4 m4 = *reinterpret_cast<const f32x4*>(&gates[1][wv][16 * blk + t]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             ab[t + e] = a4[e];
@@ -245,11 +259,15 @@ __global__ __launch_bounds__(NT) void chunk_coef_kernel(const float* __restrict_
         ra = pa * ra;
         rp = pp * rp;
     }
+    tb[CTb::RA + lane] = ra;
+    tb[CTb::RG + lane] = rg;
     // the diagonal-block column recursion of column `lane` over its block's
     // rows: gamma_jj = 1, m_jj = 1; below the diagonal m_t = mu_t m_{t-1},
     // gamma_t = alpha_t gamma_{t-1} + m_t.  Every lane runs all 16 rows from
     // m = gamma = 0 and gets a 1 added to m on its diagonal row, which starts
     // the recursion there and leaves the rows above it at zero.
+    // Stored (times the column's eta, as every use of the Gamma tables
+    // wants) for the stored part of each row.
     float gam = 0.f, mm = 0.f;
     float gd[16];
 #pragma unroll
@@ -257,7 +275,9 @@ __global__ __launch_bounds__(NT) void chunk_coef_kernel(const float* __restrict_
         mm = mbk[t] * mm + (t == off ? 1.f : 0.f);
         gam = ab[t] * gam + mm;
         gd[t] = gam;
+        if (off < gd_len(t)) tb[CTb::GD + gd_row(16 * blk + t) + off] = ge * gam;
     }
+    if (lane < 4) tb[CTb::GD_ZERO + lane] = 0.f;
     // block summaries (values at each block's last row)
     const float sa0 = readlane_f(ra, 15), sa1 = readlane_f(ra, 31), sa2 = readlane_f(ra, 47);
     const float sp0 = readlane_f(rp, 15), sp1 = readlane_f(rp, 31), sp2 = readlane_f(rp, 47);
@@ -276,6 +296,8 @@ __global__ __launch_bounds__(NT) void chunk_coef_kernel(const float* __restrict_
         }
         gbI[I] = I > blk ? gb : 0.f;
         mbI[I] = I > blk ? mb : 0.f;
+        tb[CTb::GB + 64 * (I - 1) + lane] = ge * gbI[I];
+        tb[CTb::MB + 64 * (I - 1) + lane] = ge * mbI[I];
     }
     // chunk-level prefixes of row `lane`: the whole blocks before its own,
     // composed, then its block-local prefix; abar = prod alpha, mubar =
@@ -313,23 +335,6 @@ __global__ __launch_bounds__(NT) void chunk_coef_kernel(const float* __restrict_
     const float b_n = readlane_f(bi, last);
     const float mbar_n = readlane_f(mubar, last);
 
-    // ---- stores
-    tb[CTb::ALPHA + lane] = ga;
-    tb[CTb::RA + lane] = ra;
-    tb[CTb::RG + lane] = rg;
-    // the Gamma tables carry the eta of their column (column `lane`), the
-    // factor every use of them applies
-#pragma unroll
-    for (int I = 1; I < 4; ++I) {
-        tb[CTb::GB + 64 * (I - 1) + lane] = ge * gbI[I];
-        tb[CTb::MB + 64 * (I - 1) + lane] = ge * mbI[I];
-    }
-    // diagonal block of Gamma, one column per lane (zero above the diagonal),
-    // the stored part of each row
-#pragma unroll
-    for (int t = 0; t < 16; ++t)
-        if (off < gd_len(t)) tb[CTb::GD + gd_row(16 * blk + t) + off] = ge * gd[t];
-    if (lane < 4) tb[CTb::GD_ZERO + lane] = 0.f;
     float* vec = tb + CTb::VEC;
     vec[V_ABAR * CH + lane] = valid ? abar : 0.f;
     vec[V_AB1 * CH + lane] = valid && lane > 0 ? ga * bprev : 0.f;
@@ -977,10 +982,10 @@ static hipError_t launch_fused_t(const void* q, const void* k, const void* v, co
                                  int H, void* workspace, hipStream_t stream)
 {
     const int NC = (T + CH - 1) / CH;
-    const size_t nchunks = (size_t)B * H * NC;
     float* ctab = static_cast<float*>(workspace);
-    hipLaunchKernelGGL(chunk_coef_kernel, dim3((unsigned)((nchunks + 3) / 4)), dim3(NT), 0, stream,
-                       alpha, mu, eta, ctab, T, H, NC, nchunks);
+    const unsigned nhg = (unsigned)((H + COEF_HEADS - 1) / COEF_HEADS);   // head groups
+    hipLaunchKernelGGL(chunk_coef_kernel, dim3((unsigned)B * nhg * (unsigned)NC),
+                       dim3(COEF_HEADS * 64), 0, stream, alpha, mu, eta, ctab, T, H, NC, nhg);
     const size_t nblk = (size_t)B * H * (DV / 64);
     const int xcd_groups = nblk % 8 == 0 ? (int)(nblk / 8) : 0;
     hipLaunchKernelGGL((chunk_fwd_fused_kernel<DK, DV>), dim3((unsigned)nblk), dim3(2 * NT), 0,

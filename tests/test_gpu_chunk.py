@@ -51,6 +51,15 @@ def test_small_shapes_with_initial_state(io, dk, dv, T):
     check_all(io, gpu_forward(inp), oracle_forward(inp), f"{io} dk{dk} dv{dv} T{T}")
 
 
+def test_more_heads_than_one_coefficient_group():
+    """H = 20 with bf16 I/O: the coefficient tables are built 16 heads per
+    workgroup, so this takes a full and a partial head group; ragged T."""
+    cfg = dataclasses.replace(si.CONFIGS[1], B=2, T=130, H=20, Dk=64, Dv=64, io_dtype="bf16",
+                              init_state_std=0.3, seed=4242)
+    inp = si.make_forward(cfg)
+    check_all("bf16", gpu_forward(inp), oracle_forward(inp), "bf16 B2 H20 T130 d64")
+
+
 def test_gated_delta_rule_special_case():
     """mu = 0 exactly: the operator is the gated delta rule; the final
     momentum is then rank one, -eta_T k_T vt_T^T (checked on the oracle side
