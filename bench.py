@@ -58,29 +58,29 @@ DEC_BYTES_HEAD = 4 * D * D * 4 + 3 * D * 2 + D * 2 + 3 * 4   # S, M in+out; q k 
 # HBM traffic per launch from rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, KiB per dispatch,
 # means over the profiled dispatches), recorded with the kernel sources whose sha256 is given;
 # the factors scale each counter to bytes as measured on torch's fp32 -> bf16 copy of
-# 67,108,864 elements (reads 262,144 KiB, FETCH_SIZE 131,093.4; writes 131,072 KiB, WRITE_SIZE
+# 67,108,864 elements (reads 262,144 KiB, FETCH_SIZE 131,093.9; writes 131,072 KiB, WRITE_SIZE
 # 131,072.0).  An entry that covers several kernels of one call sums their dispatches.
 # Figures and commands: profiles/chunk_fwd_fused_B8H16T4096d128.md,
 # profiles/chunk_fwd_split_B8H16T4096d128.md and profiles/decode_step_N256H16d128.md.
 # A kernel whose sources changed reports traffic null.
-FETCH_FACTOR = 262144.0 / 131093.4
+FETCH_FACTOR = 262144.0 / 131093.9
 WRITE_FACTOR = 131072.0 / 131072.0
 CSRC = os.path.join(ROOT, "chunkwise_delta_rule_amd", "csrc")
 _SPLIT_SHA = "6ea3e22bf2bc709479a8cca404573f1481629250d972d28b07290b1075ce920e"
 TRAFFIC = {
-    # chunk_coef_kernel (3,269.1 / 69,632.5) + chunk_fwd_fused_kernel (231,723.1 / 147,456.1):
+    # chunk_coef_kernel (3,100.5 / 51,458.4) + chunk_fwd_fused_kernel (223,505.3 / 147,456.2):
     # one mdn_chunk_fwd call, the unit the bench times
     "chunk_fwd_fused_kernel": dict(sources=("chunk_fused.hip", "chunk_common.hpp", "mfma.hpp"),
-                                   fetch_kib=3269.1 + 231723.1, write_kib=69632.5 + 147456.1,
-                                   sha256="173e7c3860e52f7653cea9d7b78b81db"
-                                   "0537eb28acc2262d5e812bb0f6fded87"),
+                                   fetch_kib=3100.5 + 223505.3, write_kib=51458.4 + 147456.2,
+                                   sha256="3241b1f9d44525f44a8a4253f91e7b1f"
+                                   "1fea3195bc2489a2132bdb95f7575180"),
     "chunk_scan_bf16_kernel": dict(sources=("chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
                                    fetch_kib=268385.5, write_kib=147456.2, sha256=_SPLIT_SHA),
     "chunk_prep_kernel": dict(sources=("chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
                               fetch_kib=134752.5, write_kib=144936.3, sha256=_SPLIT_SHA),
-    "decode_step_kernel": dict(sources=("decode.hip", "mfma.hpp"), fetch_kib=264253.5,
-                               write_kib=525312.2, sha256="7efdc80c4829e435c48be8feda28c8ca"
-                               "e49104e837fccc5b6cabe05d471b6e7f"),
+    "decode_step_kernel": dict(sources=("decode.hip", "mfma.hpp"), fetch_kib=264106.5,
+                               write_kib=525516.0, sha256="98626040b43b57d258352e14f9c2d2cd"
+                               "5f1e54ed58653cb636924adc441e3670"),
 }
 
 
