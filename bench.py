@@ -47,6 +47,7 @@ FLOP_SCAN = 12 * D * D + 4 * C * D       # K[S|M], Q[S|M], K^T[Vt], T R, A Vt
 FLOP_PREP = 4 * C * D                    # K K^T, Q K^T
 FLOP_FWD = FLOP_SCAN + FLOP_PREP         # 12 d^2 + 8 C d
 BYTES_FWD = 3 * D * 2 + D * 2 + 3 * 4    # q, k, v, O (bf16) + three gates (fp32)
+BYTES_FWD_BETA = BYTES_FWD + 4            # ... + the optional update-step gate beta
 # per kernel, per token and head: what each phase must read and write once
 BYTES_TA = 2 * C * C * 2 // C            # T and A, two C x C bf16 matrices per C tokens
 BYTES_VEC = 6 * 4                        # six coefficient rows (fp32) the scan reads
@@ -218,6 +219,21 @@ def bench_forward(args, torch, si, mdn):
            "mfma_frac": FLOP_FWD * toh / (step_ms * 1e-3) / PEAK_BF16_FLOPS,
            "hbm_frac_algorithmic": (BYTES_FWD * toh + STATE_BYTES_HEAD * heads)
            / (step_ms * 1e-3) / PEAK_HBM_BPS}
+    # the same layer in the four-gate form: an explicit update-step gate beta
+    # (one more fp32 gate per token and head to read)
+    beta = si.make_forward(cfg, beta="logit")["beta"]
+    plan_b = mdn.ChunkPlan(*plan.args, beta=up(beta, f32))
+    del beta
+    settle(torch, [plan_b.forward], args.settle)
+    for _ in range(args.warmup):
+        plan_b.forward()
+    _, beta_ms = time_calls(torch, [plan_b.forward], args.steps)
+    log(f"forward with a beta gate: {beta_ms * 1e3:.1f} us/step")
+    fwd["beta_gate"] = {"workload": "the same layer with beta = sigmoid(z), z ~ N(0, 1)",
+                        "us_per_step": beta_ms * 1e3, "tokens_per_s": tokens / (beta_ms * 1e-3),
+                        "hbm_frac_algorithmic": (BYTES_FWD_BETA * toh + STATE_BYTES_HEAD * heads)
+                        / (beta_ms * 1e-3) / PEAK_HBM_BPS}
+    del plan_b
     return cfg, inp, step_ms, kernels, roofline, fwd, split
 
 

@@ -10,19 +10,20 @@
 namespace mdn {
 size_t chunk_workspace_bytes(int B, int T, int H, bool bf16);
 hipError_t launch_chunk_prepare(const void* q, const void* k, const float* alpha, const float* mu,
-                                const float* eta, int B, int T, int H, int Dk, bool bf16,
-                                void* workspace, hipStream_t stream);
+                                const float* eta, const float* beta, int B, int T, int H, int Dk,
+                                bool bf16, void* workspace, hipStream_t stream);
 size_t chunk_fused_workspace_bytes(size_t nchunks);
 hipError_t launch_chunk_fused(const void* q, const void* k, const void* v, const float* alpha,
-                              const float* mu, const float* eta, const float* S0, const float* M0,
-                              void* O, float* ST, float* MT, int B, int T, int H, int Dk, int Dv,
-                              void* workspace, hipStream_t stream);
+                              const float* mu, const float* eta, const float* beta,
+                              const float* S0, const float* M0, void* O, float* ST, float* MT,
+                              int B, int T, int H, int Dk, int Dv, void* workspace,
+                              hipStream_t stream);
 hipError_t launch_chunk_scan(const void* q, const void* k, const void* v, const float* S0,
                              const float* M0, void* O, float* ST, float* MT, int B, int T, int H,
                              int Dk, int Dv, bool bf16, const void* workspace, hipStream_t stream);
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* alpha,
-                         const float* mu, const float* eta, float* S, float* M, void* o,
-                         int heads, int Dk, int Dv, bool bf16, hipStream_t stream);
+                         const float* mu, const float* eta, const float* beta, float* S, float* M,
+                         void* o, int heads, int Dk, int Dv, bool bf16, hipStream_t stream);
 }  // namespace mdn
 
 namespace {
@@ -116,7 +117,7 @@ enum Phase { PREPARE = 1, SCAN = 2, BOTH = 3 };
 
 struct FwdArgs {
     const void *q, *k, *v;
-    const float *alpha, *mu, *eta, *S0, *M0;
+    const float *alpha, *mu, *eta, *beta, *S0, *M0;   // beta may be NULL
     void* O;
     float *S_T, *M_T;
     int B, T, H, Dk, Dv, chunk;
@@ -153,7 +154,8 @@ mdn_status validate_fwd(const FwdArgs& a, int phase, bool* no_work)
     if (tok && (phase & PREPARE) && (!a.alpha || !a.mu || !a.eta)) return MDN_ERR_NULL;
     if (tok && (phase & SCAN) && (!a.v || !a.O)) return MDN_ERR_NULL;
 
-    const void* ptrs[] = {a.q, a.k, a.v, a.alpha, a.mu, a.eta, a.S0, a.M0, a.O, a.S_T, a.M_T, a.ws};
+    const void* ptrs[] = {a.q, a.k, a.v, a.alpha, a.mu, a.eta, a.beta, a.S0, a.M0, a.O, a.S_T,
+                          a.M_T, a.ws};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MDN_ERR_ALIGN;
 
@@ -172,12 +174,13 @@ mdn_status validate_fwd(const FwdArgs& a, int phase, bool* no_work)
                sa = span(prep ? a.alpha : nullptr, nt * ngate * 4),
                sm = span(prep ? a.mu : nullptr, nt * ngate * 4),
                se = span(prep ? a.eta : nullptr, nt * ngate * 4),
+               sb = span(prep ? a.beta : nullptr, nt * ngate * 4),
                sS0 = span(scan ? a.S0 : nullptr, nstate * 4),
                sM0 = span(scan ? a.M0 : nullptr, nstate * 4),
                sO = span(scan ? a.O : nullptr, nt * nv * esz),
                sST = span(scan ? a.S_T : nullptr, nstate * 4),
                sMT = span(scan ? a.M_T : nullptr, nstate * 4), sW = span(a.ws, need);
-    const Span inputs[] = {sq, sk, sv, sa, sm, se, sS0, sM0};
+    const Span inputs[] = {sq, sk, sv, sa, sm, se, sb, sS0, sM0};
     // O and the workspace overlap nothing
     for (const Span& x : inputs)
         if (overlap(sO, x) || overlap(sW, x)) return MDN_ERR_ALIAS;
@@ -186,9 +189,9 @@ mdn_status validate_fwd(const FwdArgs& a, int phase, bool* no_work)
         return MDN_ERR_ALIAS;
     // final states overlap no input, except exactly in place over their own
     // initial state
-    for (int i = 0; i < 8; ++i) {
-        if (overlap(sST, inputs[i]) && !(i == 6 && a.S_T == a.S0)) return MDN_ERR_ALIAS;
-        if (overlap(sMT, inputs[i]) && !(i == 7 && a.M_T == a.M0)) return MDN_ERR_ALIAS;
+    for (int i = 0; i < 9; ++i) {
+        if (overlap(sST, inputs[i]) && !(i == 7 && a.S_T == a.S0)) return MDN_ERR_ALIAS;
+        if (overlap(sMT, inputs[i]) && !(i == 8 && a.M_T == a.M0)) return MDN_ERR_ALIAS;
     }
     return MDN_OK;
 }
@@ -201,15 +204,15 @@ mdn_status run_fwd(const FwdArgs& a, int phase, hipStream_t stream)
     const bool bf16 = a.dt == MDN_BF16;
     if (phase == BOTH && bf16 && a.T > 0) {
         const hipError_t err =
-            mdn::launch_chunk_fused(a.q, a.k, a.v, a.alpha, a.mu, a.eta, a.S0, a.M0, a.O, a.S_T,
-                                    a.M_T, a.B, a.T, a.H, a.Dk, a.Dv, const_cast<void*>(a.ws),
-                                    stream);
+            mdn::launch_chunk_fused(a.q, a.k, a.v, a.alpha, a.mu, a.eta, a.beta, a.S0, a.M0, a.O,
+                                    a.S_T, a.M_T, a.B, a.T, a.H, a.Dk, a.Dv,
+                                    const_cast<void*>(a.ws), stream);
         return err == hipSuccess ? MDN_OK : MDN_ERR_HIP;
     }
     if ((phase & PREPARE) && a.T > 0) {
         const hipError_t err =
-            mdn::launch_chunk_prepare(a.q, a.k, a.alpha, a.mu, a.eta, a.B, a.T, a.H, a.Dk, bf16,
-                                      const_cast<void*>(a.ws), stream);
+            mdn::launch_chunk_prepare(a.q, a.k, a.alpha, a.mu, a.eta, a.beta, a.B, a.T, a.H, a.Dk,
+                                      bf16, const_cast<void*>(a.ws), stream);
         if (err != hipSuccess) return MDN_ERR_HIP;
     }
     if (phase & SCAN) {
@@ -226,25 +229,25 @@ mdn_status run_fwd(const FwdArgs& a, int phase, hipStream_t stream)
 extern "C" {
 
 mdn_status mdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
-                         const float* mu, const float* eta, const float* S0, const float* M0,
-                         void* O, float* S_T, float* M_T, int B, int T, int H, int Dk, int Dv,
-                         int chunk, mdn_dtype dt, void* workspace, size_t workspace_bytes,
-                         hipStream_t stream)
+                         const float* mu, const float* eta, const float* beta, const float* S0,
+                         const float* M0, void* O, float* S_T, float* M_T, int B, int T, int H,
+                         int Dk, int Dv, int chunk, mdn_dtype dt, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream)
 {
-    const FwdArgs a{q, k, v, alpha, mu, eta, S0, M0, O, S_T, M_T, B, T, H, Dk, Dv, chunk, dt,
-                    workspace, workspace_bytes};
+    const FwdArgs a{q, k, v, alpha, mu, eta, beta, S0, M0, O, S_T, M_T, B, T, H, Dk, Dv, chunk,
+                    dt, workspace, workspace_bytes};
     return run_fwd(a, BOTH, stream);
 }
 
 mdn_status mdn_chunk_fwd_prepare(const void* q, const void* k, const float* alpha,
-                                 const float* mu, const float* eta, int B, int T, int H, int Dk,
-                                 int chunk, mdn_dtype dt, void* workspace, size_t workspace_bytes,
-                                 hipStream_t stream)
+                                 const float* mu, const float* eta, const float* beta, int B,
+                                 int T, int H, int Dk, int chunk, mdn_dtype dt, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream)
 {
     // the scan's Dv does not change the prepared data; any supported value
     // validates the same
-    const FwdArgs a{q, k, nullptr, alpha, mu, eta, nullptr, nullptr, nullptr, nullptr, nullptr,
-                    B, T, H, Dk, 64, chunk, dt, workspace, workspace_bytes};
+    const FwdArgs a{q, k, nullptr, alpha, mu, eta, beta, nullptr, nullptr, nullptr, nullptr,
+                    nullptr, B, T, H, Dk, 64, chunk, dt, workspace, workspace_bytes};
     return run_fwd(a, PREPARE, stream);
 }
 
@@ -253,14 +256,15 @@ mdn_status mdn_chunk_fwd_scan(const void* q, const void* k, const void* v, const
                               int H, int Dk, int Dv, int chunk, mdn_dtype dt,
                               const void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    const FwdArgs a{q, k, v, nullptr, nullptr, nullptr, S0, M0, O, S_T, M_T, B, T, H, Dk, Dv,
-                    chunk, dt, workspace, workspace_bytes};
+    const FwdArgs a{q, k, v, nullptr, nullptr, nullptr, nullptr, S0, M0, O, S_T, M_T, B, T, H,
+                    Dk, Dv, chunk, dt, workspace, workspace_bytes};
     return run_fwd(a, SCAN, stream);
 }
 
 mdn_status mdn_decode_step(const void* q, const void* k, const void* v, const float* alpha,
-                           const float* mu, const float* eta, float* S, float* M, void* o,
-                           int N, int H, int Dk, int Dv, mdn_dtype dt, hipStream_t stream)
+                           const float* mu, const float* eta, const float* beta, float* S,
+                           float* M, void* o, int N, int H, int Dk, int Dv, mdn_dtype dt,
+                           hipStream_t stream)
 {
     if (N < 0 || H < 0) return MDN_ERR_SHAPE;
     if (!head_dim_ok(Dk) || !head_dim_ok(Dv)) return MDN_ERR_UNSUPPORTED;
@@ -275,17 +279,18 @@ mdn_status mdn_decode_step(const void* q, const void* k, const void* v, const fl
     const void* ptrs[] = {q, k, v, alpha, mu, eta, S, M, o};
     for (const void* p : ptrs)
         if (!aligned16(p)) return MDN_ERR_ALIGN;
+    if (beta && !aligned16(beta)) return MDN_ERR_ALIGN;   // optional
     const size_t esz = dt == MDN_BF16 ? 2 : 4;
     const Span sq = span(q, heads * Dk * esz), sk = span(k, heads * Dk * esz),
                sv = span(v, heads * Dv * esz), sa = span(alpha, heads * 4),
-               sm = span(mu, heads * 4), se = span(eta, heads * 4), sS = span(S, nstate * 4),
-               sM = span(M, nstate * 4), so = span(o, heads * Dv * esz);
-    const Span inputs[] = {sq, sk, sv, sa, sm, se};
+               sm = span(mu, heads * 4), se = span(eta, heads * 4), sb = span(beta, heads * 4),
+               sS = span(S, nstate * 4), sM = span(M, nstate * 4), so = span(o, heads * Dv * esz);
+    const Span inputs[] = {sq, sk, sv, sa, sm, se, sb};
     for (const Span& x : inputs)
         if (overlap(so, x) || overlap(sS, x) || overlap(sM, x)) return MDN_ERR_ALIAS;
     if (overlap(so, sS) || overlap(so, sM) || overlap(sS, sM)) return MDN_ERR_ALIAS;
-    const hipError_t err = mdn::launch_decode(q, k, v, alpha, mu, eta, S, M, o, (int)heads, Dk,
-                                              Dv, dt == MDN_BF16, stream);
+    const hipError_t err = mdn::launch_decode(q, k, v, alpha, mu, eta, beta, S, M, o, (int)heads,
+                                              Dk, Dv, dt == MDN_BF16, stream);
     return err == hipSuccess ? MDN_OK : MDN_ERR_HIP;
 }
 

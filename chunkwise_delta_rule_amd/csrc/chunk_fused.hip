@@ -198,10 +198,10 @@ constexpr int COEF_PITCH = CH + 4;   // LDS floats per head row (16-byte aligned
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(COEF_HEADS * 64) void chunk_coef_kernel(
     const float* __restrict__ alpha, const float* __restrict__ mu, const float* __restrict__ eta,
-    float* __restrict__ ws, int T, int H, int NC, unsigned NHG)
+    const float* __restrict__ beta, float* __restrict__ ws, int T, int H, int NC, unsigned NHG)
 {
     using CTb = ChunkTables;
-    __shared__ __align__(16) float gates[3][COEF_HEADS][COEF_PITCH];
+    __shared__ __align__(16) float gates[4][COEF_HEADS][COEF_PITCH];   // alpha, mu, eta, beta
     // 32-bit indices: B NC NHG is below 2^32 (the entry points check it)
     const unsigned g = blockIdx.x / (unsigned)NC;
     const int c = (int)(blockIdx.x - g * (unsigned)NC);
@@ -218,6 +218,7 @@ __global__ __launch_bounds__(COEF_HEADS * 64) void chunk_coef_kernel(
             gates[0][hh][t] = alpha[gi];
             gates[1][hh][t] = mu[gi];
             gates[2][hh][t] = eta[gi];
+            gates[3][hh][t] = beta ? beta[gi] : 1.f;
         }
     }
     __syncthreads();
@@ -227,6 +228,7 @@ __global__ __launch_bounds__(COEF_HEADS * 64) void chunk_coef_kernel(
     if (wv >= hg) return;   // whole wavefronts; no barrier follows
     const int h = h0 + wv;
     const float ga = gates[0][wv][lane], gm = gates[1][wv][lane], ge = gates[2][wv][lane];
+    const float gs = gates[3][wv][lane];
     float* tb = ws + (((size_t)b * H + h) * NC + c) * CTb::FLOATS;
 
     // Each table is stored as soon as it is known: every wavefront of the
@@ -235,23 +237,27 @@ __global__ __launch_bounds__(COEF_HEADS * 64) void chunk_coef_kernel(
     // all the arithmetic instead of overlapping it.
     tb[CTb::ALPHA + lane] = ga;
     const int blk = lane >> 4, off = lane & 15;
-    float ab[16], mbk[16];
+    float ab[16], mbk[16], sbk[16];
 #pragma unroll
     for (int t = 0; t < 16; t += 4) {
         const f32x4 a4 = *reinterpret_cast<const f32x4*>(&gates[0][wv][16 * blk + t]);
         const f32x4 m4 = *reinterpret_cast<const f32x4*>(&gates[1][wv][16 * blk + t]);
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(&gates[3][wv][16 * blk + t]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             ab[t + e] = a4[e];
             mbk[t + e] = m4[e];
+            sbk[t + e] = s4[e];
         }
     }
     // Block-local products of row `lane` (from its block's first row, row
-    // included): ra = prod alpha, rp = prod mu, rg_t = alpha_t rg_{t-1} + rp_t.
-    // A range's triple composes associatively -- earlier range L, later R:
-    // (ra, rp, rg) = (ra_L ra_R, rp_L rp_R, ra_R rg_L + rp_L rg_R) -- so the
-    // prefixes are a 4-step scan across the 16 lanes of the block.
-    float ra = ga, rp = gm, rg = gm;
+    // included): ra = prod alpha, rp = prod mu,
+    // rg_t = alpha_t rg_{t-1} + beta_t rp_t.  A range's triple composes
+    // associatively -- earlier range L, later R:
+    // (ra, rp, rg) = (ra_L ra_R, rp_L rp_R, ra_R rg_L + rp_L rg_R), a single
+    // row being (alpha, mu, beta mu) -- so the prefixes are a 4-step scan
+    // across the 16 lanes of the block.
+    float ra = ga, rp = gm, rg = gs * gm;
 #pragma unroll
     for (int d = 1; d < 16; d *= 2) {
         const float pa = dpp_shr(ra, d, 1.f), pp = dpp_shr(rp, d, 1.f), pg = dpp_shr(rg, d, 0.f);
@@ -262,10 +268,10 @@ __global__ __launch_bounds__(COEF_HEADS * 64) void chunk_coef_kernel(
     tb[CTb::RA + lane] = ra;
     tb[CTb::RG + lane] = rg;
     // the diagonal-block column recursion of column `lane` over its block's
-    // rows: gamma_jj = 1, m_jj = 1; below the diagonal m_t = mu_t m_{t-1},
-    // gamma_t = alpha_t gamma_{t-1} + m_t.  Every lane runs all 16 rows from
-    // m = gamma = 0 and gets a 1 added to m on its diagonal row, which starts
-    // the recursion there and leaves the rows above it at zero.
+    // rows: gamma_jj = beta_j, m_jj = 1; below the diagonal m_t = mu_t m_{t-1},
+    // gamma_t = alpha_t gamma_{t-1} + beta_t m_t.  Every lane runs all 16 rows
+    // from m = gamma = 0 and gets a 1 added to m on its diagonal row, which
+    // starts the recursion there and leaves the rows above it at zero.
     // Stored (times the column's eta, as every use of the Gamma tables
     // wants) for the stored part of each row.
     float gam = 0.f, mm = 0.f;
@@ -273,7 +279,7 @@ __global__ __launch_bounds__(COEF_HEADS * 64) void chunk_coef_kernel(
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
         mm = mbk[t] * mm + (t == off ? 1.f : 0.f);
-        gam = ab[t] * gam + mm;
+        gam = ab[t] * gam + sbk[t] * mm;
         gd[t] = gam;
         if (off < gd_len(t)) tb[CTb::GD + gd_row(16 * blk + t) + off] = ge * gam;
     }
@@ -977,15 +983,16 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
 
 template <int DK, int DV>
 static hipError_t launch_fused_t(const void* q, const void* k, const void* v, const float* alpha,
-                                 const float* mu, const float* eta, const float* S0,
-                                 const float* M0, void* O, float* ST, float* MT, int B, int T,
-                                 int H, void* workspace, hipStream_t stream)
+                                 const float* mu, const float* eta, const float* beta,
+                                 const float* S0, const float* M0, void* O, float* ST, float* MT,
+                                 int B, int T, int H, void* workspace, hipStream_t stream)
 {
     const int NC = (T + CH - 1) / CH;
     float* ctab = static_cast<float*>(workspace);
     const unsigned nhg = (unsigned)((H + COEF_HEADS - 1) / COEF_HEADS);   // head groups
     hipLaunchKernelGGL(chunk_coef_kernel, dim3((unsigned)B * nhg * (unsigned)NC),
-                       dim3(COEF_HEADS * 64), 0, stream, alpha, mu, eta, ctab, T, H, NC, nhg);
+                       dim3(COEF_HEADS * 64), 0, stream, alpha, mu, eta, beta, ctab, T, H, NC,
+                       nhg);
     const size_t nblk = (size_t)B * H * (DV / 64);
     const int xcd_groups = nblk % 8 == 0 ? (int)(nblk / 8) : 0;
     hipLaunchKernelGGL((chunk_fwd_fused_kernel<DK, DV>), dim3((unsigned)nblk), dim3(2 * NT), 0,
@@ -998,21 +1005,22 @@ static hipError_t launch_fused_t(const void* q, const void* k, const void* v, co
 // The whole bf16 forward for T >= 1: the coefficient kernel, then the fused
 // kernel.  `workspace` holds chunk_fused_workspace_bytes(B * H * ceil(T / 64)).
 hipError_t launch_chunk_fused(const void* q, const void* k, const void* v, const float* alpha,
-                              const float* mu, const float* eta, const float* S0, const float* M0,
-                              void* O, float* ST, float* MT, int B, int T, int H, int Dk, int Dv,
-                              void* workspace, hipStream_t stream)
+                              const float* mu, const float* eta, const float* beta,
+                              const float* S0, const float* M0, void* O, float* ST, float* MT,
+                              int B, int T, int H, int Dk, int Dv, void* workspace,
+                              hipStream_t stream)
 {
     if (Dk == 128 && Dv == 128)
-        return launch_fused_t<128, 128>(q, k, v, alpha, mu, eta, S0, M0, O, ST, MT, B, T, H,
-                                        workspace, stream);
+        return launch_fused_t<128, 128>(q, k, v, alpha, mu, eta, beta, S0, M0, O, ST, MT, B, T,
+                                        H, workspace, stream);
     if (Dk == 128 && Dv == 64)
-        return launch_fused_t<128, 64>(q, k, v, alpha, mu, eta, S0, M0, O, ST, MT, B, T, H,
+        return launch_fused_t<128, 64>(q, k, v, alpha, mu, eta, beta, S0, M0, O, ST, MT, B, T, H,
                                        workspace, stream);
     if (Dk == 64 && Dv == 128)
-        return launch_fused_t<64, 128>(q, k, v, alpha, mu, eta, S0, M0, O, ST, MT, B, T, H,
+        return launch_fused_t<64, 128>(q, k, v, alpha, mu, eta, beta, S0, M0, O, ST, MT, B, T, H,
                                        workspace, stream);
-    return launch_fused_t<64, 64>(q, k, v, alpha, mu, eta, S0, M0, O, ST, MT, B, T, H, workspace,
-                                  stream);
+    return launch_fused_t<64, 64>(q, k, v, alpha, mu, eta, beta, S0, M0, O, ST, MT, B, T, H,
+                                  workspace, stream);
 }
 
 }  // namespace mdn

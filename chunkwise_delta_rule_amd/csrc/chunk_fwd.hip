@@ -7,8 +7,8 @@
 // with entry state (S0, M0), P = Diag(alpha) K and Khat = Diag(eta) K:
 //
 //   abar_i = prod_{r<=i} alpha_r        mubar_i = prod_{r<=i} mu_r
-//   b_i    = alpha_i b_{i-1} + mubar_i  (= abar_i c_i, beta = 1)
-//   gamma_{i,j} = sum_{r=j}^{i} (prod_{u=r+1}^{i} alpha_u)(prod_{u=j+1}^{r} mu_u)
+//   b_i    = alpha_i b_{i-1} + beta_i mubar_i  (= abar_i c_i)
+//   gamma_{i,j} = sum_{r=j}^{i} beta_r (prod_{u=r+1}^{i} alpha_u)(prod_{u=j+1}^{r} mu_u)
 //   L  = I + (P Khat^T) o Gamma^-       (Gamma^-: Gamma shifted down one row)
 //   T  = L^{-1}
 //   Vt = T [V - Diag(abar^-) P S0 + Diag(b^-) P M0]
@@ -16,9 +16,11 @@
 //   S' = abar_C S0 - b_C M0 + [Diag(Gamma_C,:) Khat]^T Vt
 //   M' = mubar_C M0 - [Diag(mubar_C / mubar) Khat]^T Vt
 //
-// Gamma is formed by the division-free column recursion
-//   gamma_{j,j} = 1,  m_{j,j} = 1,  m_{i,j} = mu_i m_{i-1,j},
-//   gamma_{i,j} = alpha_i gamma_{i-1,j} + m_{i,j},
+// with beta the gate of the memory update S_t = alpha_t S_{t-1} - beta_t M_t
+// (beta = 1 when the caller gives none).  Gamma is formed by the
+// division-free column recursion
+//   gamma_{j,j} = beta_j,  m_{j,j} = 1,  m_{i,j} = mu_i m_{i-1,j},
+//   gamma_{i,j} = alpha_i gamma_{i-1,j} + beta_i m_{i,j},
 // which is the product-sum definition evaluated left to right; it needs no
 // exp(-U_j) and no division by mubar, so mu = 0 is exact.  Note that
 // Diag(abar^-) P = Diag(abar) K (alpha_i abar_{i-1} = abar_i).
@@ -156,8 +158,8 @@ struct PrepSmem {
 template <typename E, int DK>
 __global__ __launch_bounds__(NT) void chunk_prep_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const float* __restrict__ alpha,
-    const float* __restrict__ mu, const float* __restrict__ eta, E* __restrict__ Tw,
-    E* __restrict__ Aw, float* __restrict__ Vw, int T, int H, int NC)
+    const float* __restrict__ mu, const float* __restrict__ eta, const float* __restrict__ beta,
+    E* __restrict__ Tw, E* __restrict__ Aw, float* __restrict__ Vw, int T, int H, int NC)
 {
     using MM = Mma<E>;
     using MF = Mma<float>;
@@ -171,6 +173,7 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
     __shared__ __align__(16) float al[CH];
     __shared__ __align__(16) float mus[CH];
     __shared__ __align__(16) float et[CH];
+    __shared__ __align__(16) float bts[CH];
     E* Ks = reinterpret_cast<E*>(smem0);
     E* Qs = Ks + CH * LDK;
     float* Ls = reinterpret_cast<float*>(smem0);
@@ -198,18 +201,21 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
         kt.template store<LDK>(Ks, tid);
         qt.template store<LDK>(Qs, tid);
     }
-    // gates of this chunk, one row per lane (rows >= n: alpha 1, mu 0, eta 0)
-    float a_l = 1.f, m_l = 0.f, e_l = 0.f;
+    // gates of this chunk, one row per lane (rows >= n: alpha 1, mu 0, eta 0,
+    // beta 0); beta is 1 when no beta gate is given
+    float a_l = 1.f, m_l = 0.f, e_l = 0.f, s_l = 0.f;
     if (lane < n) {
         const size_t g = tok0 + (size_t)lane * H;
         a_l = alpha[g];
         m_l = mu[g];
         e_l = eta[g];
+        s_l = beta ? beta[g] : 1.f;
     }
     if (wave == 0) {
         al[lane] = a_l;
         mus[lane] = m_l;
         et[lane] = e_l;
+        bts[lane] = s_l;
     }
     __syncthreads();
 
@@ -219,20 +225,23 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
     //      and the pass is straight-line (rows >= n are masked, not branched
     //      over), so the reads run ahead of the arithmetic.  Since
     //      mubar_r = mu_0 prod_{u=1..r} mu_u, column 0 gives b_i = mu_0 gamma_{i,0}
-    //      and mubar_{n-1} = mu_0 m_{n-1,0}.
+    //      and mubar_{n-1} = mu_0 m_{n-1,0}.  With a beta gate, gamma_jj = beta_j
+    //      and gamma_{r,j} = alpha_r gamma_{r-1,j} + beta_r m_{r,j}.
     float* Vch = Vw + ch * NVEC * CH;
     if (wave == 0) {
         float g = 0.f, mj = 1.f, ab = 1.f;
         // blocks of 16 rows: the block's gates arrive in four 16-byte reads
         // and its rows are unrolled; rows >= n are masked inside a block
         for (int r0 = 0; r0 < n; r0 += 16) {
-            float ga[16], gm[16];
+            float ga[16], gm[16], gs[16];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const float4 a4 = *reinterpret_cast<const float4*>(al + r0 + 4 * u);
                 const float4 m4 = *reinterpret_cast<const float4*>(mus + r0 + 4 * u);
+                const float4 s4 = *reinterpret_cast<const float4*>(bts + r0 + 4 * u);
                 ga[4 * u + 0] = a4.x; ga[4 * u + 1] = a4.y; ga[4 * u + 2] = a4.z; ga[4 * u + 3] = a4.w;
                 gm[4 * u + 0] = m4.x; gm[4 * u + 1] = m4.y; gm[4 * u + 2] = m4.z; gm[4 * u + 3] = m4.w;
+                gs[4 * u + 0] = s4.x; gs[4 * u + 1] = s4.y; gs[4 * u + 2] = s4.z; gs[4 * u + 3] = s4.w;
             }
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
@@ -240,7 +249,7 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
                 const bool act = r < n;
                 const bool below = r > lane;
                 const float mj_n = below ? mj * gm[u] : 1.f;
-                const float g_n = below ? ga[u] * g + mj_n : (r == lane ? 1.f : 0.f);
+                const float g_n = below ? ga[u] * g + gs[u] * mj_n : (r == lane ? gs[u] : 0.f);
                 mj = act ? mj_n : mj;
                 g = act ? g_n : g;
                 ab = (act && r <= lane) ? ab * ga[u] : ab;
@@ -938,15 +947,15 @@ __global__ __launch_bounds__(NT) void state_passthrough_kernel(const float* __re
 // ---------------------------------------------------------------------------
 template <typename E, int DK>
 static hipError_t launch_prepare_t(const void* q, const void* k, const float* alpha,
-                                   const float* mu, const float* eta, int B, int T, int H,
-                                   void* workspace, hipStream_t stream)
+                                   const float* mu, const float* eta, const float* beta, int B,
+                                   int T, int H, void* workspace, hipStream_t stream)
 {
     const int NC = (T + CH - 1) / CH;
     const size_t nchunks = (size_t)B * H * NC;
     Workspace<E> ws = ws_carve<E>(workspace, nchunks);
     hipLaunchKernelGGL((chunk_prep_kernel<E, DK>), dim3((unsigned)nchunks), dim3(NT), 0, stream,
-                       static_cast<const E*>(q), static_cast<const E*>(k), alpha, mu, eta, ws.T,
-                       ws.A, ws.vec, T, H, NC);
+                       static_cast<const E*>(q), static_cast<const E*>(k), alpha, mu, eta, beta,
+                       ws.T, ws.A, ws.vec, T, H, NC);
     return hipGetLastError();
 }
 
@@ -982,12 +991,13 @@ size_t chunk_workspace_bytes(int B, int T, int H, bool bf16)
 }
 
 hipError_t launch_chunk_prepare(const void* q, const void* k, const float* alpha, const float* mu,
-                                const float* eta, int B, int T, int H, int Dk, bool bf16,
-                                void* workspace, hipStream_t stream)
+                                const float* eta, const float* beta, int B, int T, int H, int Dk,
+                                bool bf16, void* workspace, hipStream_t stream)
 {
     if (T == 0) return hipSuccess;
 #define MDN_PREP(E, DK)                                                                          \
-    if (Dk == DK) return launch_prepare_t<E, DK>(q, k, alpha, mu, eta, B, T, H, workspace, stream);
+    if (Dk == DK)                                                                                \
+        return launch_prepare_t<E, DK>(q, k, alpha, mu, eta, beta, B, T, H, workspace, stream);
     if (bf16) {
         MDN_PREP(__bf16, 64) MDN_PREP(__bf16, 128)
     } else {

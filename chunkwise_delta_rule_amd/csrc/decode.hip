@@ -6,7 +6,7 @@
 // combine incoming states and local writes"):
 //     vt = v - alpha S^T k
 //     M  = mu M - eta k vt^T
-//     S  = alpha S - M
+//     S  = alpha S - beta M      (beta = 1 when no beta gate is given)
 //     o  = S^T q
 //
 // The step is bound by HBM traffic: each head reads and writes its two fp32
@@ -31,7 +31,8 @@ template <typename E, int DK, int DV>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ mu, const float* __restrict__ eta,
-    float* __restrict__ S, float* __restrict__ M, E* __restrict__ o)
+    const float* __restrict__ beta, float* __restrict__ S, float* __restrict__ M,
+    E* __restrict__ o)
 {
     constexpr int CPR = DV / 4;       // threads across one row (4 columns each)
     constexpr int RPP = 256 / CPR;    // rows covered by one pass of the block
@@ -65,6 +66,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     const float a = alpha[head];
     const float m = mu[head];
     const float e = eta[head];
+    const float bt = beta ? beta[head] : 1.f;
     f32x4 vv;
 #pragma unroll
     for (int c = 0; c < 4; ++c) vv[c] = to_f32(v[head * DV + 4 * tx + c]);
@@ -88,7 +90,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         const int row = ty + RPP * j;
         const float kr = ks[row];
         const f32x4 mn = m * m_reg[j] - (e * kr) * vt;
-        const f32x4 sn = a * s_reg[j] - mn;
+        const f32x4 sn = a * s_reg[j] - bt * mn;
         __builtin_nontemporal_store(mn, reinterpret_cast<f32x4*>(Mh + (size_t)row * DV + 4 * tx));
         __builtin_nontemporal_store(sn, reinterpret_cast<f32x4*>(Sh + (size_t)row * DV + 4 * tx));
         acc_o += sn * qs[row];
@@ -106,23 +108,24 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 
 template <typename E, int DK, int DV>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* alpha,
-                                  const float* mu, const float* eta, float* S, float* M, void* o,
-                                  int heads, hipStream_t stream)
+                                  const float* mu, const float* eta, const float* beta, float* S,
+                                  float* M, void* o, int heads, hipStream_t stream)
 {
     hipLaunchKernelGGL((decode_step_kernel<E, DK, DV>), dim3(heads), dim3(256), 0, stream,
                        static_cast<const E*>(q), static_cast<const E*>(k),
-                       static_cast<const E*>(v), alpha, mu, eta, S, M, static_cast<E*>(o));
+                       static_cast<const E*>(v), alpha, mu, eta, beta, S, M,
+                       static_cast<E*>(o));
     return hipGetLastError();
 }
 
 // Host entry used by the C ABI layer; shapes are validated there.
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* alpha,
-                         const float* mu, const float* eta, float* S, float* M, void* o,
-                         int heads, int Dk, int Dv, bool bf16, hipStream_t stream)
+                         const float* mu, const float* eta, const float* beta, float* S, float* M,
+                         void* o, int heads, int Dk, int Dv, bool bf16, hipStream_t stream)
 {
 #define MDN_DEC(E, DK, DV)                                                                       \
     if (Dk == DK && Dv == DV)                                                                    \
-        return launch_decode_t<E, DK, DV>(q, k, v, alpha, mu, eta, S, M, o, heads, stream);
+        return launch_decode_t<E, DK, DV>(q, k, v, alpha, mu, eta, beta, S, M, o, heads, stream);
     if (bf16) {
         MDN_DEC(__bf16, 64, 64) MDN_DEC(__bf16, 64, 128) MDN_DEC(__bf16, 128, 64)
         MDN_DEC(__bf16, 128, 128)

@@ -64,13 +64,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mdn_chunk_fwd_split_workspace_bytes.restype = S
     lib.mdn_chunk_fwd_split_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.mdn_chunk_fwd.restype = I
-    lib.mdn_chunk_fwd.argtypes = [P] * 11 + [I] * 7 + [P, S, P]
+    lib.mdn_chunk_fwd.argtypes = [P] * 12 + [I] * 7 + [P, S, P]
     lib.mdn_chunk_fwd_prepare.restype = I
-    lib.mdn_chunk_fwd_prepare.argtypes = [P] * 5 + [I] * 6 + [P, S, P]
+    lib.mdn_chunk_fwd_prepare.argtypes = [P] * 6 + [I] * 6 + [P, S, P]
     lib.mdn_chunk_fwd_scan.restype = I
     lib.mdn_chunk_fwd_scan.argtypes = [P] * 8 + [I] * 7 + [P, S, P]
     lib.mdn_decode_step.restype = I
-    lib.mdn_decode_step.argtypes = [P] * 9 + [I] * 5 + [P]
+    lib.mdn_decode_step.argtypes = [P] * 10 + [I] * 5 + [P]
     lib.mdn_status_string.restype = ctypes.c_char_p
     lib.mdn_status_string.argtypes = [I]
     if path == LIB_PATH:
@@ -118,13 +118,14 @@ def workspace_bytes(B: int, T: int, H: int, Dk: int, Dv: int, dtype: torch.dtype
 
 def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
               mu: torch.Tensor, eta: torch.Tensor, S0: Optional[torch.Tensor] = None,
-              M0: Optional[torch.Tensor] = None, *, chunk: int = CHUNK,
-              O: Optional[torch.Tensor] = None, S_T: Optional[torch.Tensor] = None,
-              M_T: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-              final_state: bool = True
+              M0: Optional[torch.Tensor] = None, *, beta: Optional[torch.Tensor] = None,
+              chunk: int = CHUNK, O: Optional[torch.Tensor] = None,
+              S_T: Optional[torch.Tensor] = None, M_T: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None, final_state: bool = True
               ) -> Tuple[torch.Tensor, Optional[torch.Tensor], Optional[torch.Tensor]]:
     """Chunkwise MDN forward.  q, k [B, T, H, Dk], v [B, T, H, Dv] (bf16 or
-    fp32), gates [B, T, H] fp32, S0/M0 [B, H, Dk, Dv] fp32 or None.
+    fp32), gates [B, T, H] fp32 (beta optional: None means beta = 1),
+    S0/M0 [B, H, Dk, Dv] fp32 or None.
     Returns (O, S_T, M_T); S_T/M_T are None when ``final_state`` is False and
     none were passed in."""
     lib = load_library()
@@ -138,6 +139,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
     _check(v, "v", (B, T, H, Dv), dt, dev)
     for name, g in (("alpha", alpha), ("mu", mu), ("eta", eta)):
         _check(g, name, (B, T, H), torch.float32, dev)
+    if beta is not None:
+        _check(beta, "beta", (B, T, H), torch.float32, dev)
     for name, s in (("S0", S0), ("M0", M0)):
         if s is not None:
             _check(s, name, (B, H, Dk, Dv), torch.float32, dev)
@@ -155,9 +158,9 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.mdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(mu), _ptr(eta), _ptr(S0),
-                           _ptr(M0), _ptr(O), _ptr(S_T), _ptr(M_T), B, T, H, Dk, Dv, chunk, code,
-                           _ptr(workspace), wbytes, _stream(dev))
+    st = lib.mdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(mu), _ptr(eta),
+                           _ptr(beta), _ptr(S0), _ptr(M0), _ptr(O), _ptr(S_T), _ptr(M_T), B, T, H,
+                           Dk, Dv, chunk, code, _ptr(workspace), wbytes, _stream(dev))
     if st != 0:
         raise MdnError(st, "mdn_chunk_fwd")
     return O, S_T, M_T
@@ -168,10 +171,11 @@ class ChunkPlan:
     the phases can then be launched (and timed) one by one.  Holds the
     outputs and the workspace; launching performs no allocation."""
 
-    def __init__(self, q, k, v, alpha, mu, eta, S0=None, M0=None, *, chunk: int = CHUNK,
-                 final_state: bool = True):
+    def __init__(self, q, k, v, alpha, mu, eta, S0=None, M0=None, *, beta=None,
+                 chunk: int = CHUNK, final_state: bool = True):
         self.lib = load_library()
         self.args = (q, k, v, alpha, mu, eta, S0, M0)
+        self.beta = beta
         B, T, H, Dk = q.shape
         Dv = v.shape[-1]
         self.shape = (B, T, H, Dk, Dv)
@@ -185,16 +189,16 @@ class ChunkPlan:
         self.workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
         self.ws_bytes = need
         # one full call validates every argument (and fills the outputs)
-        chunk_fwd(*self.args, chunk=chunk, O=self.O, S_T=self.S_T, M_T=self.M_T,
+        chunk_fwd(*self.args, beta=beta, chunk=chunk, O=self.O, S_T=self.S_T, M_T=self.M_T,
                   workspace=self.workspace)
         self.stream = _stream(dev)
 
     def prepare(self):
         q, k, _, a, m, e, _, _ = self.args
         B, T, H, Dk, _ = self.shape
-        st = self.lib.mdn_chunk_fwd_prepare(_ptr(q), _ptr(k), _ptr(a), _ptr(m), _ptr(e), B, T, H,
-                                            Dk, self.chunk, self.code, _ptr(self.workspace),
-                                            self.ws_bytes, self.stream)
+        st = self.lib.mdn_chunk_fwd_prepare(_ptr(q), _ptr(k), _ptr(a), _ptr(m), _ptr(e),
+                                            _ptr(self.beta), B, T, H, Dk, self.chunk, self.code,
+                                            _ptr(self.workspace), self.ws_bytes, self.stream)
         if st != 0:
             raise MdnError(st, "mdn_chunk_fwd_prepare")
 
@@ -212,7 +216,8 @@ class ChunkPlan:
         q, k, v, a, m, e, S0, M0 = self.args
         B, T, H, Dk, Dv = self.shape
         st = self.lib.mdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(m), _ptr(e),
-                                    _ptr(S0), _ptr(M0), _ptr(self.O), _ptr(self.S_T),
+                                    _ptr(self.beta), _ptr(S0), _ptr(M0), _ptr(self.O),
+                                    _ptr(self.S_T),
                                     _ptr(self.M_T), B, T, H, Dk, Dv, self.chunk, self.code,
                                     _ptr(self.workspace), self.ws_bytes, self.stream)
         if st != 0:
@@ -221,9 +226,11 @@ class ChunkPlan:
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
                 mu: torch.Tensor, eta: torch.Tensor, S: torch.Tensor, M: torch.Tensor,
-                o: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """One decode step: q, k [N, H, Dk], v [N, H, Dv], gates [N, H]; S, M
-    [N, H, Dk, Dv] fp32 updated in place.  Returns o [N, H, Dv]."""
+                o: Optional[torch.Tensor] = None, *,
+                beta: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step: q, k [N, H, Dk], v [N, H, Dv], gates [N, H] (beta
+    optional: None means beta = 1); S, M [N, H, Dk, Dv] fp32 updated in
+    place.  Returns o [N, H, Dv]."""
     lib = load_library()
     dev = q.device
     N, H, Dk = q.shape
@@ -235,13 +242,16 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.
     _check(v, "v", (N, H, Dv), dt, dev)
     for name, g in (("alpha", alpha), ("mu", mu), ("eta", eta)):
         _check(g, name, (N, H), torch.float32, dev)
+    if beta is not None:
+        _check(beta, "beta", (N, H), torch.float32, dev)
     _check(S, "S", (N, H, Dk, Dv), torch.float32, dev)
     _check(M, "M", (N, H, Dk, Dv), torch.float32, dev)
     if o is None:
         o = torch.empty((N, H, Dv), dtype=dt, device=dev)
     _check(o, "o", (N, H, Dv), dt, dev)
     st = lib.mdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(mu), _ptr(eta),
-                             _ptr(S), _ptr(M), _ptr(o), N, H, Dk, Dv, code, _stream(dev))
+                             _ptr(beta), _ptr(S), _ptr(M), _ptr(o), N, H, Dk, Dv, code,
+                             _stream(dev))
     if st != 0:
         raise MdnError(st, "mdn_decode_step")
     return o

@@ -6,11 +6,13 @@
  * The operation (per batch entry b and head h, tokens t = 1..T):
  *     vt_t = v_t - alpha_t S_{t-1}^T k_t
  *     M_t  = mu_t M_{t-1} - eta_t k_t vt_t^T
- *     S_t  = alpha_t S_{t-1} - M_t                 (update step beta = 1)
+ *     S_t  = alpha_t S_{t-1} - beta_t M_t
  *     o_t  = S_t^T q_t
  * with S, M in R^{Dk x Dv}.  This is the two-state recurrence of "MDN:
  * Parallelizing Stepwise Momentum for Delta Linear Attention" (slides),
- * Sec. 3.1 Eqs. (3)-(5), with the update step beta fixed to 1.  The forward
+ * Sec. 3.1 Eqs. (3)-(5); the update-step gate beta is optional (a NULL beta
+ * means beta = 1, the form the slides' chunk equations are written in, and
+ * then runs exactly the arithmetic an all-ones beta runs).  The forward
  * pass evaluates it chunk by chunk as in the same slides' Eqs. (7)-(9),
  * (15)-(18) and (40)-(42) (Appendix C forms, residual mask shifted one row
  * as in the backup frame "a one-row shift is essential for causality"),
@@ -32,7 +34,7 @@
  * Layouts (row-major, C order):
  *    q, k    [B, T, H, Dk]     dtype `dt`
  *    v, O    [B, T, H, Dv]     dtype `dt`
- *    alpha, mu, eta  [B, T, H] float32
+ *    alpha, mu, eta, beta  [B, T, H] float32 (beta may be NULL)
  *    S0, M0, S_T, M_T [B, H, Dk, Dv] float32
  *  Decode: q, k [N, H, Dk]; v, o [N, H, Dv]; gates [N, H]; S, M [N, H, Dk, Dv].
  */
@@ -91,6 +93,8 @@ size_t mdn_chunk_fwd_split_workspace_bytes(int B, int T, int H, int Dk, int Dv, 
  *   alpha, mu, eta   per-token, per-head gates (float32).  Any finite values
  *                    are accepted; mu = 0 is the gated delta rule and
  *                    additionally alpha = 1 is DeltaNet.
+ *   beta             the update-step gate (float32, same layout), or NULL for
+ *                    beta = 1.
  *   S0, M0           initial memory and momentum (float32); NULL = zero.
  *   O                output o_t for every token (dtype dt); must not overlap
  *                    any input.
@@ -106,10 +110,10 @@ size_t mdn_chunk_fwd_split_workspace_bytes(int B, int T, int H, int Dk, int Dv, 
  * and O is untouched; with B = 0 or H = 0 nothing is launched.
  */
 mdn_status mdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
-                         const float* mu, const float* eta, const float* S0, const float* M0,
-                         void* O, float* S_T, float* M_T, int B, int T, int H, int Dk, int Dv,
-                         int chunk, mdn_dtype dt, void* workspace, size_t workspace_bytes,
-                         hipStream_t stream);
+                         const float* mu, const float* eta, const float* beta, const float* S0,
+                         const float* M0, void* O, float* S_T, float* M_T, int B, int T, int H,
+                         int Dk, int Dv, int chunk, mdn_dtype dt, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
 
 /*
  * The forward as two separate phases, for callers that want to run the
@@ -127,7 +131,8 @@ mdn_status mdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
  * mdn_chunk_fwd_prepare: per chunk, the coefficients (abar, mubar, b, Gamma;
  *   slides Eqs. (7)-(9)), T = L^{-1} (Eqs. (15)-(18)) and
  *   A = (Q Khat^T) o Gamma (Eqs. (40)-(42)), written to `workspace`.
- *   Reads q, k and the gates only (layouts as for mdn_chunk_fwd; Dk is the
+ *   Reads q, k and the gates only (layouts and the optional beta as for
+ *   mdn_chunk_fwd; Dk is the
  *   head size of q and k).  The workspace must hold at least
  *   mdn_chunk_fwd_split_workspace_bytes(B, T, H, Dk, Dv, chunk, dt) bytes
  *   (the size does not depend on Dk or Dv) and must not overlap any input.
@@ -141,9 +146,9 @@ mdn_status mdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
  * Both return the same status codes as mdn_chunk_fwd for the same errors.
  */
 mdn_status mdn_chunk_fwd_prepare(const void* q, const void* k, const float* alpha,
-                                 const float* mu, const float* eta, int B, int T, int H, int Dk,
-                                 int chunk, mdn_dtype dt, void* workspace, size_t workspace_bytes,
-                                 hipStream_t stream);
+                                 const float* mu, const float* eta, const float* beta, int B,
+                                 int T, int H, int Dk, int chunk, mdn_dtype dt, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
 mdn_status mdn_chunk_fwd_scan(const void* q, const void* k, const void* v, const float* S0,
                               const float* M0, void* O, float* S_T, float* M_T, int B, int T,
@@ -156,14 +161,16 @@ mdn_status mdn_chunk_fwd_scan(const void* q, const void* k, const void* v, const
  * fixed-size pair S, M).
  *   q, k [N, H, Dk], v [N, H, Dv]    this step's token (dtype dt).
  *   alpha, mu, eta [N, H]            this step's gates (float32).
+ *   beta [N, H] or NULL              this step's update-step gate (NULL: 1).
  *   S, M [N, H, Dk, Dv]              state, read and updated IN PLACE (float32).
  *   o [N, H, Dv]                     output (dtype dt); must not overlap any
  *                                    other argument.
  * N, H >= 0; N = 0 or H = 0 launches nothing.
  */
 mdn_status mdn_decode_step(const void* q, const void* k, const void* v, const float* alpha,
-                           const float* mu, const float* eta, float* S, float* M, void* o,
-                           int N, int H, int Dk, int Dv, mdn_dtype dt, hipStream_t stream);
+                           const float* mu, const float* eta, const float* beta, float* S,
+                           float* M, void* o, int N, int H, int Dk, int Dv, mdn_dtype dt,
+                           hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char* mdn_status_string(mdn_status s);

@@ -12,6 +12,9 @@ Recipe (every array is drawn whole, in C order of its layout, from one
    standard-normal arrays z_alpha, z_mu, z_eta mapped as
    alpha = exp(-0.1 softplus(z)), mu = 0.9 sigmoid(z), eta = sigmoid(z).
 3. Initial states S0 then M0 when the workload has them.
+3b. The update-step gate beta, last, when the workload has one: uniform
+   U(0.2, 1) or sigmoid(z) of a standard normal z.  Workloads without it
+   draw exactly what they drew before beta existed.
 4. q and k are L2-normalised per (token, head) in float64; this mirrors the
    model placing the normalisation in front of the memory core.
 5. q, k, v are rounded once to the I/O dtype (round to nearest even);
@@ -48,6 +51,7 @@ class ForwardConfig:
     gates: str               # "uniform" or "logit"
     seed: int
     init_state_std: float = 0.0   # 0 => S0 = M0 = 0 (None)
+    beta: str = "none"            # "none" (beta = 1, None), "uniform" or "logit"
 
 
 @dataclass(frozen=True)
@@ -61,6 +65,7 @@ class DecodeConfig:
     state_std: float
     seed: int
     io_dtype: str = "bf16"
+    beta: str = "none"            # as for ForwardConfig
 
 
 # The workloads: a small fp32 correctness case, a 400M-like layer, the
@@ -156,6 +161,16 @@ def _gates(rng: np.random.Generator, shape, kind: str):
     return a.astype(np.float32), m.astype(np.float32), e.astype(np.float32)
 
 
+def _beta(rng: np.random.Generator, shape, kind: str) -> Optional[np.ndarray]:
+    if kind == "none":
+        return None
+    if kind == "uniform":
+        return rng.uniform(0.2, 1.0, size=shape).astype(np.float32)
+    if kind == "logit":
+        return _sigmoid(rng.standard_normal(shape)).astype(np.float32)
+    raise ValueError(kind)
+
+
 def make_forward(cfg: ForwardConfig, **overrides) -> Dict[str, Optional[np.ndarray]]:
     """Draw one forward workload.  ``overrides`` may replace any field of the
     config (B, T, H, Dk, Dv, seed, init_state_std, ...) to make a smaller or
@@ -172,7 +187,8 @@ def make_forward(cfg: ForwardConfig, **overrides) -> Dict[str, Optional[np.ndarr
     if cfg.init_state_std > 0:
         S0 = _normal_rows(rng, (B, H, Dk, Dv), "f32", False, cfg.init_state_std)
         M0 = _normal_rows(rng, (B, H, Dk, Dv), "f32", False, cfg.init_state_std)
-    return dict(q=q, k=k, v=v, alpha=alpha, mu=mu, eta=eta, S0=S0, M0=M0, cfg=cfg)
+    beta = _beta(rng, (B, T, H), cfg.beta)
+    return dict(q=q, k=k, v=v, alpha=alpha, mu=mu, eta=eta, beta=beta, S0=S0, M0=M0, cfg=cfg)
 
 
 def decode_initial_state(cfg: DecodeConfig, rng: np.random.Generator):
@@ -190,7 +206,8 @@ def decode_token(cfg: DecodeConfig, rng: np.random.Generator) -> Dict[str, np.nd
     k = _normal_rows(rng, (N, H, cfg.Dk), cfg.io_dtype, normalise=True)
     v = _normal_rows(rng, (N, H, cfg.Dv), cfg.io_dtype, normalise=False)
     alpha, mu, eta = _gates(rng, (N, H), "logit")
-    return dict(q=q, k=k, v=v, alpha=alpha, mu=mu, eta=eta)
+    beta = _beta(rng, (N, H), cfg.beta)
+    return dict(q=q, k=k, v=v, alpha=alpha, mu=mu, eta=eta, beta=beta)
 
 
 def decode_stream(cfg: DecodeConfig, **overrides) -> Iterator:

@@ -35,14 +35,17 @@ def to_np(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def gpu_forward(inp, mu=None, S0=None, M0=None, io=None):
+def gpu_forward(inp, mu=None, S0=None, M0=None, io=None, beta="inp"):
+    """beta: "inp" passes the workload's own beta (None if it has none), or
+    give an array or None explicitly."""
     io = io or inp["cfg"].io_dtype
     dt = TORCH_DT[io]
+    beta = inp.get("beta") if isinstance(beta, str) else beta
     O, ST, MT = mdn.chunk_fwd(to_dev(inp["q"], dt), to_dev(inp["k"], dt), to_dev(inp["v"], dt),
                               to_dev(inp["alpha"]), to_dev(inp["mu"] if mu is None else mu),
                               to_dev(inp["eta"]),
                               to_dev(inp["S0"] if S0 is None else S0),
-                              to_dev(inp["M0"] if M0 is None else M0))
+                              to_dev(inp["M0"] if M0 is None else M0), beta=to_dev(beta))
     torch.cuda.synchronize()
     return to_np(O), to_np(ST), to_np(MT)
 
@@ -53,7 +56,7 @@ def split_forward(inp, io=None):
     dt = TORCH_DT[io]
     plan = mdn.ChunkPlan(to_dev(inp["q"], dt), to_dev(inp["k"], dt), to_dev(inp["v"], dt),
                          to_dev(inp["alpha"]), to_dev(inp["mu"]), to_dev(inp["eta"]),
-                         to_dev(inp["S0"]), to_dev(inp["M0"]))
+                         to_dev(inp["S0"]), to_dev(inp["M0"]), beta=to_dev(inp.get("beta")))
     plan.O.fill_(float("nan"))
     plan.S_T.fill_(float("nan"))
     plan.M_T.fill_(float("nan"))
@@ -75,12 +78,13 @@ def gather_heads(x, pairs, state=False):
 
 def oracle_forward(inp, pairs=None, mu=None):
     mu = inp["mu"] if mu is None else mu
+    beta = inp.get("beta")
     if pairs is None:
-        return oracle.recurrence(inp["q"], inp["k"], inp["v"], inp["alpha"], mu, inp["eta"], None,
+        return oracle.recurrence(inp["q"], inp["k"], inp["v"], inp["alpha"], mu, inp["eta"], beta,
                                  inp["S0"], inp["M0"])
     g = lambda x: gather_heads(x, pairs)
     return oracle.recurrence(g(inp["q"]), g(inp["k"]), g(inp["v"]), g(inp["alpha"]), g(mu),
-                             g(inp["eta"]), None, gather_heads(inp["S0"], pairs, True),
+                             g(inp["eta"]), g(beta), gather_heads(inp["S0"], pairs, True),
                              gather_heads(inp["M0"], pairs, True))
 
 

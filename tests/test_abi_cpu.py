@@ -75,17 +75,17 @@ def fake(i, off=0):
 
 
 def fwd_args(**over):
-    a = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), mu=fake(4), eta=fake(5), S0=fake(6),
-             M0=fake(7), O=fake(8), S_T=fake(9), M_T=fake(10), B=2, T=100, H=3, Dk=64, Dv=128,
-             chunk=64, dt=mdn.MDN_BF16, ws=fake(11), wsb=1 << 31, stream=None)
+    a = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), mu=fake(4), eta=fake(5), beta=None,
+             S0=fake(6), M0=fake(7), O=fake(8), S_T=fake(9), M_T=fake(10), B=2, T=100, H=3,
+             Dk=64, Dv=128, chunk=64, dt=mdn.MDN_BF16, ws=fake(11), wsb=1 << 31, stream=None)
     a.update(over)
     return a
 
 
 def call_fwd(lib, a):
-    return lib.mdn_chunk_fwd(a["q"], a["k"], a["v"], a["alpha"], a["mu"], a["eta"], a["S0"],
-                             a["M0"], a["O"], a["S_T"], a["M_T"], a["B"], a["T"], a["H"], a["Dk"],
-                             a["Dv"], a["chunk"], a["dt"], a["ws"], a["wsb"], a["stream"])
+    return lib.mdn_chunk_fwd(a["q"], a["k"], a["v"], a["alpha"], a["mu"], a["eta"], a["beta"],
+                             a["S0"], a["M0"], a["O"], a["S_T"], a["M_T"], a["B"], a["T"], a["H"],
+                             a["Dk"], a["Dv"], a["chunk"], a["dt"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("over,status", [
@@ -110,9 +110,19 @@ def call_fwd(lib, a):
     (dict(S_T=fake(7)), "MDN_ERR_ALIAS"),               # final memory over initial momentum
     (dict(S_T=fake(6, 16)), "MDN_ERR_ALIAS"),           # shifted, not exactly in place
     (dict(M_T=fake(9)), "MDN_ERR_ALIAS"),               # both final states at one address
+    (dict(beta=fake(12, 8)), "MDN_ERR_ALIGN"),          # the optional gate is checked too
+    (dict(beta=fake(8)), "MDN_ERR_ALIAS"),              # output over beta
+    (dict(beta=fake(12), M_T=fake(12)), "MDN_ERR_ALIAS"),  # final momentum over beta
 ])
 def test_chunk_fwd_rejects(lib, over, status):
     assert mdn.STATUS_NAMES[call_fwd(lib, fwd_args(**over))] == status
+
+
+def test_chunk_fwd_beta_is_optional(lib):
+    # a NULL beta (the default above) and a valid one both pass validation;
+    # B = 0 keeps the calls from launching anything
+    assert call_fwd(lib, fwd_args(B=0)) == 0
+    assert call_fwd(lib, fwd_args(B=0, beta=fake(12))) == 0
 
 
 def test_chunk_fwd_no_work_returns_ok_without_launch(lib):
@@ -122,15 +132,16 @@ def test_chunk_fwd_no_work_returns_ok_without_launch(lib):
 
 
 def dec_args(**over):
-    a = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), mu=fake(4), eta=fake(5), S=fake(6),
-             M=fake(7), o=fake(8), N=4, H=2, Dk=128, Dv=128, dt=mdn.MDN_BF16, stream=None)
+    a = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), mu=fake(4), eta=fake(5), beta=None,
+             S=fake(6), M=fake(7), o=fake(8), N=4, H=2, Dk=128, Dv=128, dt=mdn.MDN_BF16,
+             stream=None)
     a.update(over)
     return a
 
 
 def call_dec(lib, a):
-    return lib.mdn_decode_step(a["q"], a["k"], a["v"], a["alpha"], a["mu"], a["eta"], a["S"],
-                               a["M"], a["o"], a["N"], a["H"], a["Dk"], a["Dv"], a["dt"],
+    return lib.mdn_decode_step(a["q"], a["k"], a["v"], a["alpha"], a["mu"], a["eta"], a["beta"],
+                               a["S"], a["M"], a["o"], a["N"], a["H"], a["Dk"], a["Dv"], a["dt"],
                                a["stream"])
 
 
@@ -144,6 +155,8 @@ def call_dec(lib, a):
     (dict(o=fake(0)), "MDN_ERR_ALIAS"),
     (dict(M=fake(6, 1024)), "MDN_ERR_ALIAS"),
     (dict(S=fake(1)), "MDN_ERR_ALIAS"),
+    (dict(beta=fake(9, 4)), "MDN_ERR_ALIGN"),
+    (dict(beta=fake(9), o=fake(9)), "MDN_ERR_ALIAS"),   # output over beta
 ])
 def test_decode_rejects(lib, over, status):
     assert mdn.STATUS_NAMES[call_dec(lib, dec_args(**over))] == status
@@ -160,8 +173,8 @@ def test_missing_library_fails_loudly(tmp_path):
 
 
 def call_prepare(lib, a):
-    return lib.mdn_chunk_fwd_prepare(a["q"], a["k"], a["alpha"], a["mu"], a["eta"], a["B"],
-                                     a["T"], a["H"], a["Dk"], a["chunk"], a["dt"], a["ws"],
+    return lib.mdn_chunk_fwd_prepare(a["q"], a["k"], a["alpha"], a["mu"], a["eta"], a["beta"],
+                                     a["B"], a["T"], a["H"], a["Dk"], a["chunk"], a["dt"], a["ws"],
                                      a["wsb"], a["stream"])
 
 
@@ -179,6 +192,8 @@ def call_scan(lib, a):
     (dict(alpha=fake(3, 4)), "MDN_ERR_ALIGN"),
     (dict(ws=None), "MDN_ERR_WORKSPACE"),
     (dict(ws=fake(1)), "MDN_ERR_ALIAS"),            # workspace over k
+    (dict(beta=fake(12, 4)), "MDN_ERR_ALIGN"),
+    (dict(beta=fake(12), ws=fake(12)), "MDN_ERR_ALIAS"),   # workspace over beta
 ])
 def test_prepare_rejects(lib, over, status):
     assert mdn.STATUS_NAMES[call_prepare(lib, fwd_args(**over))] == status

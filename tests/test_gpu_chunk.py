@@ -13,8 +13,8 @@ import torch
 
 import synthetic_inputs as si
 from chunkwise_delta_rule_amd import mdn
-from parity import (TORCH_DT, assert_close, gather_heads, gpu_forward, oracle_forward, to_dev,
-                    to_np)
+from parity import (TORCH_DT, assert_close, gather_heads, gpu_forward, oracle_forward,
+                    split_forward, to_dev, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -58,6 +58,41 @@ def test_more_heads_than_one_coefficient_group():
                               init_state_std=0.3, seed=4242)
     inp = si.make_forward(cfg)
     check_all("bf16", gpu_forward(inp), oracle_forward(inp), "bf16 B2 H20 T130 d64")
+
+
+BETA = [(io, dk, dv, T) for io in ("f32", "bf16") for (dk, dv) in ((64, 64), (128, 128))
+        for T in (37, 200)]
+
+
+@pytest.mark.parametrize("io,dk,dv,T", BETA, ids=[f"{a}-dk{b}-dv{c}-T{d}" for a, b, c, d in BETA])
+def test_beta_gate(io, dk, dv, T):
+    """The four-gate form: an explicit update-step gate beta (uniform in
+    [0.2, 1]) against the oracle's beta recurrence; ragged T, nonzero S0, M0."""
+    cfg = dataclasses.replace(si.CONFIGS[1], B=2, T=T, H=3, Dk=dk, Dv=dv, io_dtype=io,
+                              init_state_std=0.3, beta="uniform", seed=5000 + T + dk + dv)
+    inp = si.make_forward(cfg)
+    check_all(io, gpu_forward(inp), oracle_forward(inp), f"beta {io} dk{dk} dv{dv} T{T}")
+
+
+def test_beta_gate_split_phases():
+    """beta through the two exported phases (prepare, then scan) in bf16."""
+    cfg = dataclasses.replace(si.CONFIGS[1], B=1, T=150, H=4, io_dtype="bf16",
+                              init_state_std=0.3, beta="logit", seed=5555)
+    inp = si.make_forward(cfg)
+    check_all("bf16", split_forward(inp), oracle_forward(inp), "beta split bf16")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_beta_ones_matches_no_beta_bitwise(io):
+    """An all-ones beta runs exactly the arithmetic of no beta (fused bf16
+    path and fp32 split path)."""
+    cfg = dataclasses.replace(si.CONFIGS[1], B=1, T=130, H=2, io_dtype=io, init_state_std=0.3,
+                              seed=5600)
+    inp = si.make_forward(cfg)
+    a = gpu_forward(inp, beta=None)
+    b = gpu_forward(inp, beta=np.ones_like(inp["alpha"]))
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
 
 
 def test_gated_delta_rule_special_case():

@@ -38,12 +38,14 @@ def run_decode(cfg, pairs=None, steps=None):
     worst = (0.0, 0.0, 0.0)
     for step in range(steps):
         tok = next(stream)
+        beta = tok.get("beta")
         o = mdn.decode_step(to_dev(tok["q"], dt), to_dev(tok["k"], dt), to_dev(tok["v"], dt),
-                            to_dev(tok["alpha"]), to_dev(tok["mu"]), to_dev(tok["eta"]), S, M)
-        sel = lambda x: x[ni, hi][:, None]
+                            to_dev(tok["alpha"]), to_dev(tok["mu"]), to_dev(tok["eta"]), S, M,
+                            beta=to_dev(beta))
+        sel = lambda x: None if x is None else x[ni, hi][:, None]
         o_ref, Sr, Mr = oracle.decode_step(sel(tok["q"]), sel(tok["k"]), sel(tok["v"]),
                                            sel(tok["alpha"]), sel(tok["mu"]), sel(tok["eta"]),
-                                           Sr, Mr)
+                                           Sr, Mr, sel(beta))
         o_got = to_np(o)[ni, hi][:, None]
         err = errors(o_got, o_ref)
         if err[0] > worst[0]:
@@ -70,6 +72,37 @@ def test_decode_small(io, dk, dv):
     print(f"[decode {io} dk{dk} dv{dv}] worst o err {worst[0]:.3e} (max|o| {worst[1]:.3e})")
     assert_close(got[0], ref[0], io, "S")
     assert_close(got[1], ref[1], io, "M")
+
+
+@pytest.mark.parametrize("io,d", [("f32", 64), ("bf16", 128)])
+def test_decode_beta_gate(io, d):
+    """The four-gate form: a fresh update-step gate beta = sigmoid(z) each
+    step, against the oracle's beta recurrence."""
+    cfg = dataclasses.replace(si.CONFIGS[4], N=3, H=5, Dk=d, Dv=d, steps=20, state_std=0.3,
+                              io_dtype=io, beta="logit", seed=4500 + d)
+    worst, got, ref = run_decode(cfg)
+    print(f"[decode beta {io} d{d}] worst o err {worst[0]:.3e} (max|o| {worst[1]:.3e})")
+    assert_close(got[0], ref[0], io, "S")
+    assert_close(got[1], ref[1], io, "M")
+
+
+def test_decode_beta_ones_matches_no_beta_bitwise():
+    """An all-ones beta runs exactly the arithmetic of no beta."""
+    cfg = dataclasses.replace(si.CONFIGS[4], N=2, H=3, steps=1, state_std=0.3)
+    stream = si.decode_stream(cfg)
+    S0, M0 = next(stream)
+    tok = next(stream)
+    dt = torch.bfloat16
+    outs = []
+    for beta in (None, np.ones_like(tok["alpha"])):
+        S, M = to_dev(S0), to_dev(M0)
+        o = mdn.decode_step(to_dev(tok["q"], dt), to_dev(tok["k"], dt), to_dev(tok["v"], dt),
+                            to_dev(tok["alpha"]), to_dev(tok["mu"]), to_dev(tok["eta"]), S, M,
+                            beta=to_dev(beta))
+        torch.cuda.synchronize()
+        outs.append((to_np(o), to_np(S), to_np(M)))
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
 
 
 def test_decode_full_config_sampled_heads():
