@@ -55,6 +55,7 @@ BYTES_SCAN = 3 * D * 2 + D * 2 + BYTES_TA + BYTES_VEC     # + final S, M per (b,
 BYTES_PREP = 2 * D * 2 + 3 * 4 + BYTES_TA + BYTES_VEC
 STATE_BYTES_HEAD = 2 * D * D * 4         # S_T and M_T written once per (b, h)
 DEC_BYTES_HEAD = 4 * D * D * 4 + 3 * D * 2 + D * 2 + 3 * 4   # S, M in+out; q k v o; gates
+DEC_BYTES_HEAD_GDN = 2 * D * D * 4 + 3 * D * 2 + D * 2 + 2 * 4   # mu = 0: S only; two gates
 
 # HBM traffic per launch from rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, KiB per dispatch,
 # means over the profiled dispatches), recorded with the kernel sources whose sha256 is given;
@@ -234,6 +235,17 @@ def bench_forward(args, torch, si, mdn):
                         "hbm_frac_algorithmic": (BYTES_FWD_BETA * toh + STATE_BYTES_HEAD * heads)
                         / (beta_ms * 1e-3) / PEAK_HBM_BPS}
     del plan_b
+    # the gated delta rule: no mu (mu = 0), the momentum-free kernel
+    a_, e_ = plan.args[3], plan.args[5]
+    plan_g = mdn.ChunkPlan(plan.args[0], plan.args[1], plan.args[2], a_, None, e_)
+    settle(torch, [plan_g.forward], args.settle)
+    for _ in range(args.warmup):
+        plan_g.forward()
+    _, gdn_ms = time_calls(torch, [plan_g.forward], args.steps)
+    log(f"forward with no mu (gated delta rule): {gdn_ms * 1e3:.1f} us/step")
+    fwd["no_mu"] = {"workload": "the same layer with mu = 0 (no mu given): the gated delta rule",
+                    "us_per_step": gdn_ms * 1e3, "tokens_per_s": tokens / (gdn_ms * 1e-3)}
+    del plan_g
     return cfg, inp, step_ms, kernels, roofline, fwd, split
 
 
@@ -267,10 +279,25 @@ def bench_decode(args, torch, si, mdn):
     heads = cfg.N * cfg.H
     gbs = DEC_BYTES_HEAD * heads / (us * 1e-6) / 1e9
     log(f"decode: {us:.1f} us/step, {gbs:.0f} GB/s algorithmic")
+    # the gated delta rule: no mu and no momentum state, S alone streams
+    settle(torch, [lambda: mdn.decode_step(*toks[0][:4], None, toks[0][5], S, None, o)],
+           args.settle)
+    e0.record()
+    for t in toks:
+        mdn.decode_step(*t[:4], None, t[5], S, None, o)
+    e1.record()
+    torch.cuda.synchronize()
+    us_g = e0.elapsed_time(e1) / dcfg.steps * 1e3
+    gbs_g = DEC_BYTES_HEAD_GDN * heads / (us_g * 1e-6) / 1e9
+    log(f"decode with no mu and no M: {us_g:.1f} us/step, {gbs_g:.0f} GB/s algorithmic")
     return {"workload": f"decode N{cfg.N} H{cfg.H} d{cfg.Dk} fp32 state, bf16 tokens",
             "us_per_step": us, "GB_per_s": gbs, "hbm_frac": gbs * 1e9 / PEAK_HBM_BPS,
             "bytes_per_step": DEC_BYTES_HEAD * heads, "steps_timed": dcfg.steps,
-            "kernel": "decode_step_kernel", "traffic": traffic_bytes("decode_step_kernel")}
+            "kernel": "decode_step_kernel", "traffic": traffic_bytes("decode_step_kernel"),
+            "no_mu": {"workload": "the same steps with mu = 0 and no momentum state",
+                      "us_per_step": us_g, "GB_per_s": gbs_g,
+                      "hbm_frac": gbs_g * 1e9 / PEAK_HBM_BPS,
+                      "bytes_per_step": DEC_BYTES_HEAD_GDN * heads}}
 
 
 # tokens/s against sequence length at a fixed 16,384 tokens per call (T x B), H = 16, d = 128,

@@ -151,7 +151,8 @@ mdn_status validate_fwd(const FwdArgs& a, int phase, bool* no_work)
     if ((size_t)a.B * a.H * (((size_t)a.T + 63) / 64) > 0xffffffffu) return MDN_ERR_SHAPE;
     const bool tok = a.T > 0;
     if (tok && (!a.q || !a.k)) return MDN_ERR_NULL;
-    if (tok && (phase & PREPARE) && (!a.alpha || !a.mu || !a.eta)) return MDN_ERR_NULL;
+    // mu may be NULL: mu = 0 (the gated delta rule)
+    if (tok && (phase & PREPARE) && (!a.alpha || !a.eta)) return MDN_ERR_NULL;
     if (tok && (phase & SCAN) && (!a.v || !a.O)) return MDN_ERR_NULL;
 
     const void* ptrs[] = {a.q, a.k, a.v, a.alpha, a.mu, a.eta, a.beta, a.S0, a.M0, a.O, a.S_T,
@@ -275,11 +276,11 @@ mdn_status mdn_decode_step(const void* q, const void* k, const void* v, const fl
         !mul_ok((size_t)N, (size_t)H, (size_t)Dk, (size_t)Dv, &nstate))
         return MDN_ERR_SHAPE;
     if (heads > 0x7fffffffu) return MDN_ERR_SHAPE;
-    if (!q || !k || !v || !alpha || !mu || !eta || !S || !M || !o) return MDN_ERR_NULL;
-    const void* ptrs[] = {q, k, v, alpha, mu, eta, S, M, o};
+    // mu may be NULL (mu = 0, the gated delta rule), and then M may be too
+    if (!q || !k || !v || !alpha || !eta || !S || !o || (mu && !M)) return MDN_ERR_NULL;
+    const void* ptrs[] = {q, k, v, alpha, mu, eta, beta, S, M, o};
     for (const void* p : ptrs)
-        if (!aligned16(p)) return MDN_ERR_ALIGN;
-    if (beta && !aligned16(beta)) return MDN_ERR_ALIGN;   // optional
+        if (p && !aligned16(p)) return MDN_ERR_ALIGN;
     const size_t esz = dt == MDN_BF16 ? 2 : 4;
     const Span sq = span(q, heads * Dk * esz), sk = span(k, heads * Dk * esz),
                sv = span(v, heads * Dv * esz), sa = span(alpha, heads * 4),

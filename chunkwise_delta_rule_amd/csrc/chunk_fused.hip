@@ -216,7 +216,7 @@ __global__ __launch_bounds__(COEF_HEADS * 64) void chunk_coef_kernel(
             const int t = e / hg, hh = e - t * hg;
             const size_t gi = g0 + (size_t)min(t, last) * H + hh;
             gates[0][hh][t] = alpha[gi];
-            gates[1][hh][t] = mu[gi];
+            gates[1][hh][t] = mu ? mu[gi] : 0.f;
             gates[2][hh][t] = eta[gi];
             gates[3][hh][t] = beta ? beta[gi] : 1.f;
         }
@@ -397,7 +397,12 @@ struct FusedLayout {
     static constexpr int BYTES = OFF_TB + 2 * TB_BYTES;
 };
 
-template <int DK, int DV>
+// MOM = false is the momentum-free case mu = 0 (the gated delta rule): then
+// b = 0 and mubar = 0, so the momentum never feeds the memory, and the
+// final momentum is the last token's own write, -eta_T k_T vt_T^T (the last
+// chunk's update with the weights eta m_n, which are zero but on its last
+// row); the compute waves skip every product with M.
+template <int DK, int DV, bool MOM>
 __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const float* __restrict__ ctab, const float* S0, const float* M0, __bf16* __restrict__ O,
@@ -759,7 +764,7 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
                 X[rt][r] = src ? src[sbase + (size_t)phys_row(16 * rt + 4 * lg + r) * DV + col] : 0.f;
     };
     if (S0) load_state(Sa, S0); else load_state(Sa, nullptr);
-    if (M0) load_state(Ma, M0); else load_state(Ma, nullptr);
+    if (MOM && M0) load_state(Ma, M0); else load_state(Ma, nullptr);
 
     // per-lane LDS offsets, the same every chunk
     // row 16 x + l16, d-chunk lg: rows 16 apart share the swizzle, so the
@@ -805,12 +810,11 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
 #pragma unroll
             for (int s = 0; s < SK; ++s) {
                 const auto bS = MM::from_acc(Sa, s);
-                const auto bM = MM::from_acc(Ma, s);
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
                     const auto aK = *reinterpret_cast<const MM::frag*>(Kb + kq_base(ct) + 64 * s);
                     xs[ct] = MM::mma(aK, bS, xs[ct]);
-                    xm[ct] = MM::mma(aK, bM, xm[ct]);
+                    if constexpr (MOM) xm[ct] = MM::mma(aK, MM::from_acc(Ma, s), xm[ct]);
                 }
             }
             // (2) R = V - Diag(abar) K S0 + Diag(alpha b^-) K M0, rows 16 ct + 4 lg + r
@@ -821,8 +825,10 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
                 const f32x4 ab1 = *reinterpret_cast<const f32x4*>(vec + V_AB1 * CH + p0);
                 const bf16x4 vv = lds_read_tr4(Vb + vtr_base + ct * VJ);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    R[ct][r] = static_cast<float>(vv[r]) - ab[r] * xs[ct][r] + ab1[r] * xm[ct][r];
+                for (int r = 0; r < 4; ++r) {
+                    R[ct][r] = static_cast<float>(vv[r]) - ab[r] * xs[ct][r];
+                    if constexpr (MOM) R[ct][r] += ab1[r] * xm[ct][r];
+                }
             }
         }
         // (3) O^T = S0^T Q^T Diag(abar) - M0^T Q^T Diag(b) + Vt^T A^T, its
@@ -837,19 +843,18 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
 #pragma unroll
             for (int s = 0; s < SK; ++s) {
                 const auto bS = MM::from_acc(Sa, s);
-                const auto bM = MM::from_acc(Ma, s);
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
                     const auto aQ = *reinterpret_cast<const MM::frag*>(Qb + kq_base(ct) + 64 * s);
                     ys[ct] = MM::mma(bS, aQ, ys[ct]);
-                    ym[ct] = MM::mma(bM, aQ, ym[ct]);
+                    if constexpr (MOM) ym[ct] = MM::mma(MM::from_acc(Ma, s), aQ, ym[ct]);
                 }
             }
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
                 const float ab = vec[V_ABAR * CH + 16 * ct + l16];
-                const float bb = vec[V_B * CH + 16 * ct + l16];
-                Ot[ct] = ab * ys[ct] - bb * ym[ct];
+                Ot[ct] = ab * ys[ct];
+                if constexpr (MOM) Ot[ct] -= vec[V_B * CH + 16 * ct + l16] * ym[ct];
             }
         }
 
@@ -936,9 +941,15 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
         const float mbn = vec[V_SCAL * CH + 2];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            Sa[rt] = abn * Sa[rt] - bn * Ma[rt];
-            Ma[rt] = mbn * Ma[rt];
+            if constexpr (MOM) {
+                Sa[rt] = abn * Sa[rt] - bn * Ma[rt];
+                Ma[rt] = mbn * Ma[rt];
+            } else {
+                (void)bn, (void)mbn;
+                Sa[rt] = abn * Sa[rt];
+            }
         }
+
         // K^T fragments by transposing reads, two 16-row blocks of the chunk
         // per 16x16x32 step (k = chunk rows 32 p .. 32 p + 31).  The lane's
         // base address is fixed here, so that every read is that base plus an
@@ -946,26 +957,39 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
         // later block and pays an address add per read for the negative
         // offsets of the others).
         const int ktb = opaque((int)(Kb - smem) + ktr0);
+        // the products with K^T; `with_m` also updates M
+        auto update = [&](auto with_m) {
+            constexpr bool WM = decltype(with_m)::value != 0;
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            bf16x4 bS[2], bM[2];
+            for (int p = 0; p < 2; ++p) {
+                bf16x4 bS[2], bM[2];
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int J = 2 * p + e;
-                const f32x4 ws = *reinterpret_cast<const f32x4*>(vec + V_WS * CH + 16 * J + 4 * lg);
-                const f32x4 wm = *reinterpret_cast<const f32x4*>(vec + V_WM * CH + 16 * J + 4 * lg);
-                bS[e] = to_bf4(ws * Vt[J]);
-                bM[e] = to_bf4(-(wm * Vt[J]));
+                for (int e = 0; e < 2; ++e) {
+                    const int J = 2 * p + e;
+                    const f32x4 ws = *reinterpret_cast<const f32x4*>(vec + V_WS * CH + 16 * J + 4 * lg);
+                    const f32x4 wm = *reinterpret_cast<const f32x4*>(vec + V_WM * CH + 16 * J + 4 * lg);
+                    bS[e] = to_bf4(ws * Vt[J]);
+                    if constexpr (WM) bM[e] = to_bf4(-(wm * Vt[J]));
+                }
+                const auto bS8 = cat8(bS[0], bS[1]);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const int off = ktr_base(rt) - ktr0;   // a constant
+                    const auto aK = cat8(lds_read_tr4(smem + ktb + off + 2 * p * KJ),
+                                         lds_read_tr4(smem + ktb + off + (2 * p + 1) * KJ));
+                    Sa[rt] = MM::mma(aK, bS8, Sa[rt]);
+                    if constexpr (WM) Ma[rt] = MM::mma(aK, cat8(bM[0], bM[1]), Ma[rt]);
+                }
             }
-            const auto bS8 = cat8(bS[0], bS[1]), bM8 = cat8(bM[0], bM[1]);
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                const int off = ktr_base(rt) - ktr0;   // a constant
-                const auto aK = cat8(lds_read_tr4(smem + ktb + off + 2 * p * KJ),
-                                     lds_read_tr4(smem + ktb + off + (2 * p + 1) * KJ));
-                Sa[rt] = MM::mma(aK, bS8, Sa[rt]);
-                Ma[rt] = MM::mma(aK, bM8, Ma[rt]);
-            }
+        };
+        if constexpr (MOM) {
+            update(IConst<1>{});
+        } else if (MT && c == NC - 1) {
+            // without momentum M' is the last token's own write; it is
+            // formed once, with the last chunk (M is zero before it)
+            update(IConst<1>{});
+        } else {
+            update(IConst<0>{});
         }
         lds_barrier();   // B0: chunk c + 1 ready, this buffer free
     }
@@ -995,8 +1019,10 @@ static hipError_t launch_fused_t(const void* q, const void* k, const void* v, co
                        nhg);
     const size_t nblk = (size_t)B * H * (DV / 64);
     const int xcd_groups = nblk % 8 == 0 ? (int)(nblk / 8) : 0;
-    hipLaunchKernelGGL((chunk_fwd_fused_kernel<DK, DV>), dim3((unsigned)nblk), dim3(2 * NT), 0,
-                       stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+    // mu = NULL: mu = 0, the momentum-free kernel
+    auto kern = mu ? chunk_fwd_fused_kernel<DK, DV, true> : chunk_fwd_fused_kernel<DK, DV, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(2 * NT), 0, stream,
+                       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                        static_cast<const __bf16*>(v), ctab, S0, M0, static_cast<__bf16*>(O), ST,
                        MT, T, H, NC, xcd_groups);
     return hipGetLastError();

@@ -207,7 +207,7 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
     if (lane < n) {
         const size_t g = tok0 + (size_t)lane * H;
         a_l = alpha[g];
-        m_l = mu[g];
+        m_l = mu ? mu[g] : 0.f;   // NULL: mu = 0
         e_l = eta[g];
         s_l = beta ? beta[g] : 1.f;
     }

@@ -27,7 +27,10 @@
 
 namespace mdn {
 
-template <typename E, int DK, int DV>
+// MOM = false: mu = 0 (the gated delta rule).  M_{t-1} is then not read (it
+// does not enter the step); M may be NULL, and if it is not, it receives the
+// step's own write -eta k vt^T.
+template <typename E, int DK, int DV, bool MOM>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ mu, const float* __restrict__ eta,
@@ -49,7 +52,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     const size_t head = blockIdx.x;                    // n * H + h
     const size_t sbase = head * DK * DV;
     float* Sh = S + sbase;
-    float* Mh = M + sbase;
+    float* Mh = M ? M + sbase : nullptr;
 
     // the whole strip of S and M is requested before anything waits on it
     f32x4 s_reg[RPT], m_reg[RPT];
@@ -57,14 +60,17 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     for (int j = 0; j < RPT; ++j) {
         const int row = ty + RPP * j;
         s_reg[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sh + (size_t)row * DV + 4 * tx));
-        m_reg[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Mh + (size_t)row * DV + 4 * tx));
+        if constexpr (MOM)
+            m_reg[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Mh + (size_t)row * DV + 4 * tx));
+        else
+            m_reg[j] = zero4();
     }
     for (int i = tid; i < DK; i += 256) {
         ks[i] = to_f32(k[head * DK + i]);
         qs[i] = to_f32(q[head * DK + i]);
     }
     const float a = alpha[head];
-    const float m = mu[head];
+    const float m = MOM ? mu[head] : 0.f;
     const float e = eta[head];
     const float bt = beta ? beta[head] : 1.f;
     f32x4 vv;
@@ -89,9 +95,10 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     for (int j = 0; j < RPT; ++j) {
         const int row = ty + RPP * j;
         const float kr = ks[row];
-        const f32x4 mn = m * m_reg[j] - (e * kr) * vt;
+        const f32x4 mn = MOM ? m * m_reg[j] - (e * kr) * vt : -((e * kr) * vt);
         const f32x4 sn = a * s_reg[j] - bt * mn;
-        __builtin_nontemporal_store(mn, reinterpret_cast<f32x4*>(Mh + (size_t)row * DV + 4 * tx));
+        if (MOM || M)
+            __builtin_nontemporal_store(mn, reinterpret_cast<f32x4*>(Mh + (size_t)row * DV + 4 * tx));
         __builtin_nontemporal_store(sn, reinterpret_cast<f32x4*>(Sh + (size_t)row * DV + 4 * tx));
         acc_o += sn * qs[row];
     }
@@ -111,10 +118,11 @@ static hipError_t launch_decode_t(const void* q, const void* k, const void* v, c
                                   const float* mu, const float* eta, const float* beta, float* S,
                                   float* M, void* o, int heads, hipStream_t stream)
 {
-    hipLaunchKernelGGL((decode_step_kernel<E, DK, DV>), dim3(heads), dim3(256), 0, stream,
-                       static_cast<const E*>(q), static_cast<const E*>(k),
-                       static_cast<const E*>(v), alpha, mu, eta, beta, S, M,
-                       static_cast<E*>(o));
+    // mu = NULL: mu = 0, the momentum-free kernel
+    auto kern = mu ? decode_step_kernel<E, DK, DV, true> : decode_step_kernel<E, DK, DV, false>;
+    hipLaunchKernelGGL(kern, dim3(heads), dim3(256), 0, stream, static_cast<const E*>(q),
+                       static_cast<const E*>(k), static_cast<const E*>(v), alpha, mu, eta, beta,
+                       S, M, static_cast<E*>(o));
     return hipGetLastError();
 }
 

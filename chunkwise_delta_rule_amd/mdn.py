@@ -93,6 +93,8 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 
 def _check(t: torch.Tensor, name: str, shape, dtype, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
     if t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if t.dtype != dtype:
@@ -124,8 +126,9 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
               workspace: Optional[torch.Tensor] = None, final_state: bool = True
               ) -> Tuple[torch.Tensor, Optional[torch.Tensor], Optional[torch.Tensor]]:
     """Chunkwise MDN forward.  q, k [B, T, H, Dk], v [B, T, H, Dv] (bf16 or
-    fp32), gates [B, T, H] fp32 (beta optional: None means beta = 1),
-    S0/M0 [B, H, Dk, Dv] fp32 or None.
+    fp32), gates [B, T, H] fp32 (beta optional: None means beta = 1; mu may
+    be None, meaning mu = 0, the gated delta rule), S0/M0 [B, H, Dk, Dv] fp32
+    or None.
     Returns (O, S_T, M_T); S_T/M_T are None when ``final_state`` is False and
     none were passed in."""
     lib = load_library()
@@ -137,10 +140,9 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
     _check(q, "q", (B, T, H, Dk), dt, dev)
     _check(k, "k", (B, T, H, Dk), dt, dev)
     _check(v, "v", (B, T, H, Dv), dt, dev)
-    for name, g in (("alpha", alpha), ("mu", mu), ("eta", eta)):
-        _check(g, name, (B, T, H), torch.float32, dev)
-    if beta is not None:
-        _check(beta, "beta", (B, T, H), torch.float32, dev)
+    for name, g in (("alpha", alpha), ("mu", mu), ("eta", eta), ("beta", beta)):
+        if g is not None or name in ("alpha", "eta"):
+            _check(g, name, (B, T, H), torch.float32, dev)
     for name, s in (("S0", S0), ("M0", M0)):
         if s is not None:
             _check(s, name, (B, H, Dk, Dv), torch.float32, dev)
@@ -225,12 +227,12 @@ class ChunkPlan:
 
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
-                mu: torch.Tensor, eta: torch.Tensor, S: torch.Tensor, M: torch.Tensor,
-                o: Optional[torch.Tensor] = None, *,
+                mu: Optional[torch.Tensor], eta: torch.Tensor, S: torch.Tensor,
+                M: Optional[torch.Tensor], o: Optional[torch.Tensor] = None, *,
                 beta: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One decode step: q, k [N, H, Dk], v [N, H, Dv], gates [N, H] (beta
-    optional: None means beta = 1); S, M [N, H, Dk, Dv] fp32 updated in
-    place.  Returns o [N, H, Dv]."""
+    optional: None means beta = 1; mu None means mu = 0, and then M may be
+    None); S, M [N, H, Dk, Dv] fp32 updated in place.  Returns o [N, H, Dv]."""
     lib = load_library()
     dev = q.device
     N, H, Dk = q.shape
@@ -240,12 +242,12 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.
     _check(q, "q", (N, H, Dk), dt, dev)
     _check(k, "k", (N, H, Dk), dt, dev)
     _check(v, "v", (N, H, Dv), dt, dev)
-    for name, g in (("alpha", alpha), ("mu", mu), ("eta", eta)):
-        _check(g, name, (N, H), torch.float32, dev)
-    if beta is not None:
-        _check(beta, "beta", (N, H), torch.float32, dev)
+    for name, g in (("alpha", alpha), ("mu", mu), ("eta", eta), ("beta", beta)):
+        if g is not None or name in ("alpha", "eta"):
+            _check(g, name, (N, H), torch.float32, dev)
     _check(S, "S", (N, H, Dk, Dv), torch.float32, dev)
-    _check(M, "M", (N, H, Dk, Dv), torch.float32, dev)
+    if M is not None or mu is not None:
+        _check(M, "M", (N, H, Dk, Dv), torch.float32, dev)
     if o is None:
         o = torch.empty((N, H, Dv), dtype=dt, device=dev)
     _check(o, "o", (N, H, Dv), dt, dev)

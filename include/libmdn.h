@@ -92,7 +92,11 @@ size_t mdn_chunk_fwd_split_workspace_bytes(int B, int T, int H, int Dk, int Dv, 
  *   q, k, v          inputs, layouts above, dtype dt.
  *   alpha, mu, eta   per-token, per-head gates (float32).  Any finite values
  *                    are accepted; mu = 0 is the gated delta rule and
- *                    additionally alpha = 1 is DeltaNet.
+ *                    additionally alpha = 1 is DeltaNet.  mu may be NULL,
+ *                    meaning mu = 0: the momentum then never feeds the memory
+ *                    and a kernel without the momentum products runs (M0 is
+ *                    not read; M_T receives the last token's own write
+ *                    -eta_T k_T vt_T^T).
  *   beta             the update-step gate (float32, same layout), or NULL for
  *                    beta = 1.
  *   S0, M0           initial memory and momentum (float32); NULL = zero.
@@ -160,7 +164,10 @@ mdn_status mdn_chunk_fwd_scan(const void* q, const void* k, const void* v, const
  * above with T = 1; the slides' Sec. 3.1 notes that decoding keeps the
  * fixed-size pair S, M).
  *   q, k [N, H, Dk], v [N, H, Dv]    this step's token (dtype dt).
- *   alpha, mu, eta [N, H]            this step's gates (float32).
+ *   alpha, mu, eta [N, H]            this step's gates (float32).  mu may be
+ *                                    NULL, meaning mu = 0: M is then not
+ *                                    read and may be NULL; if it is not, it
+ *                                    receives the step's -eta k vt^T.
  *   beta [N, H] or NULL              this step's update-step gate (NULL: 1).
  *   S, M [N, H, Dk, Dv]              state, read and updated IN PLACE (float32).
  *   o [N, H, Dv]                     output (dtype dt); must not overlap any

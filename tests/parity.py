@@ -35,14 +35,15 @@ def to_np(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def gpu_forward(inp, mu=None, S0=None, M0=None, io=None, beta="inp"):
+def gpu_forward(inp, mu=None, S0=None, M0=None, io=None, beta="inp", mu_null=False):
     """beta: "inp" passes the workload's own beta (None if it has none), or
-    give an array or None explicitly."""
+    give an array or None explicitly.  mu_null passes no mu (mu = 0)."""
     io = io or inp["cfg"].io_dtype
     dt = TORCH_DT[io]
     beta = inp.get("beta") if isinstance(beta, str) else beta
+    mu_dev = None if mu_null else to_dev(inp["mu"] if mu is None else mu)
     O, ST, MT = mdn.chunk_fwd(to_dev(inp["q"], dt), to_dev(inp["k"], dt), to_dev(inp["v"], dt),
-                              to_dev(inp["alpha"]), to_dev(inp["mu"] if mu is None else mu),
+                              to_dev(inp["alpha"]), mu_dev,
                               to_dev(inp["eta"]),
                               to_dev(inp["S0"] if S0 is None else S0),
                               to_dev(inp["M0"] if M0 is None else M0), beta=to_dev(beta))
@@ -50,12 +51,13 @@ def gpu_forward(inp, mu=None, S0=None, M0=None, io=None, beta="inp"):
     return to_np(O), to_np(ST), to_np(MT)
 
 
-def split_forward(inp, io=None):
+def split_forward(inp, io=None, mu_null=False):
     """The same forward through the two exported phases (prepare, then scan)."""
     io = io or inp["cfg"].io_dtype
     dt = TORCH_DT[io]
     plan = mdn.ChunkPlan(to_dev(inp["q"], dt), to_dev(inp["k"], dt), to_dev(inp["v"], dt),
-                         to_dev(inp["alpha"]), to_dev(inp["mu"]), to_dev(inp["eta"]),
+                         to_dev(inp["alpha"]), None if mu_null else to_dev(inp["mu"]),
+                         to_dev(inp["eta"]),
                          to_dev(inp["S0"]), to_dev(inp["M0"]), beta=to_dev(inp.get("beta")))
     plan.O.fill_(float("nan"))
     plan.S_T.fill_(float("nan"))

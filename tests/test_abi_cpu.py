@@ -111,6 +111,7 @@ def call_fwd(lib, a):
     (dict(S_T=fake(6, 16)), "MDN_ERR_ALIAS"),           # shifted, not exactly in place
     (dict(M_T=fake(9)), "MDN_ERR_ALIAS"),               # both final states at one address
     (dict(beta=fake(12, 8)), "MDN_ERR_ALIGN"),          # the optional gate is checked too
+    (dict(mu=None, M0=None, k=fake(1, 8)), "MDN_ERR_ALIGN"),  # NULL mu (mu = 0) is allowed
     (dict(beta=fake(8)), "MDN_ERR_ALIAS"),              # output over beta
     (dict(beta=fake(12), M_T=fake(12)), "MDN_ERR_ALIAS"),  # final momentum over beta
 ])
@@ -156,6 +157,8 @@ def call_dec(lib, a):
     (dict(M=fake(6, 1024)), "MDN_ERR_ALIAS"),
     (dict(S=fake(1)), "MDN_ERR_ALIAS"),
     (dict(beta=fake(9, 4)), "MDN_ERR_ALIGN"),
+    (dict(M=None), "MDN_ERR_NULL"),                      # M is required when mu is given
+    (dict(mu=None, M=None, v=fake(2, 2)), "MDN_ERR_ALIGN"),   # ... not when mu = 0 (NULL)
     (dict(beta=fake(9), o=fake(9)), "MDN_ERR_ALIAS"),   # output over beta
 ])
 def test_decode_rejects(lib, over, status):
@@ -188,8 +191,9 @@ def call_scan(lib, a):
     (dict(Dk=32), "MDN_ERR_UNSUPPORTED"),
     (dict(T=-1), "MDN_ERR_SHAPE"),
     (dict(k=None), "MDN_ERR_NULL"),
-    (dict(mu=None), "MDN_ERR_NULL"),
+    (dict(alpha=None), "MDN_ERR_NULL"),
     (dict(alpha=fake(3, 4)), "MDN_ERR_ALIGN"),
+    (dict(mu=None, k=fake(1, 8)), "MDN_ERR_ALIGN"),   # a NULL mu (mu = 0) passes the NULL check
     (dict(ws=None), "MDN_ERR_WORKSPACE"),
     (dict(ws=fake(1)), "MDN_ERR_ALIAS"),            # workspace over k
     (dict(beta=fake(12, 4)), "MDN_ERR_ALIGN"),

@@ -95,6 +95,32 @@ def test_beta_ones_matches_no_beta_bitwise(io):
         assert np.array_equal(x, y)
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_mu_null_runs_the_gated_delta_rule(io):
+    """No mu (mu = 0): the momentum-free kernel (bf16) and the split path
+    (fp32) against the oracle at mu = 0, with S0 and M0 given (M0 cannot
+    matter) and a beta gate; M_T is the last token's own write."""
+    cfg = dataclasses.replace(si.CONFIGS[1], B=2, T=150, H=3, io_dtype=io, init_state_std=0.3,
+                              beta="uniform", seed=5700)
+    inp = si.make_forward(cfg)
+    mu0 = np.zeros_like(inp["mu"])
+    got = gpu_forward(inp, mu_null=True)
+    check_all(io, got, oracle_forward(inp, mu=mu0), f"mu NULL {io}")
+    # against the general kernel given mu = 0 explicitly
+    ref = gpu_forward(inp, mu=mu0)
+    for x, y, name in zip(got, ref, ("O", "S_T", "M_T")):
+        assert_close(x, y, io, name + " (mu NULL vs mu = 0)")
+
+
+def test_mu_null_split_phases():
+    """No mu through the exported phases in bf16."""
+    cfg = dataclasses.replace(si.CONFIGS[1], B=1, T=100, H=4, io_dtype="bf16",
+                              init_state_std=0.3, seed=5800)
+    inp = si.make_forward(cfg)
+    check_all("bf16", split_forward(inp, mu_null=True),
+              oracle_forward(inp, mu=np.zeros_like(inp["mu"])), "mu NULL split bf16")
+
+
 def test_gated_delta_rule_special_case():
     """mu = 0 exactly: the operator is the gated delta rule; the final
     momentum is then rank one, -eta_T k_T vt_T^T (checked on the oracle side

@@ -105,6 +105,35 @@ def test_decode_beta_ones_matches_no_beta_bitwise():
         assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("keep_m", [False, True])
+def test_decode_mu_null(keep_m):
+    """No mu (mu = 0): the momentum-free step over 20 tokens against the
+    oracle at mu = 0; without M only S is kept, with M it receives each
+    step's own write."""
+    cfg = dataclasses.replace(si.CONFIGS[4], N=3, H=5, steps=20, state_std=0.3, seed=4600)
+    stream = si.decode_stream(cfg)
+    S0, M0 = next(stream)
+    S = to_dev(S0)
+    M = to_dev(M0) if keep_m else None
+    Sr = S0.reshape(cfg.N * cfg.H, 1, cfg.Dk, cfg.Dv).astype(np.float64)
+    Mr = M0.reshape(cfg.N * cfg.H, 1, cfg.Dk, cfg.Dv).astype(np.float64)
+    dt = torch.bfloat16
+    flat = lambda x: x.reshape(cfg.N * cfg.H, 1, *x.shape[2:])
+    for step in range(cfg.steps):
+        tok = next(stream)
+        o = mdn.decode_step(to_dev(tok["q"], dt), to_dev(tok["k"], dt), to_dev(tok["v"], dt),
+                            to_dev(tok["alpha"]), None, to_dev(tok["eta"]), S, M)
+        zero = np.zeros((cfg.N * cfg.H, 1), np.float32)
+        o_ref, Sr, Mr = oracle.decode_step(flat(tok["q"]), flat(tok["k"]), flat(tok["v"]),
+                                           tok["alpha"].reshape(-1, 1), zero,
+                                           tok["eta"].reshape(-1, 1), Sr, Mr)
+        assert_close(to_np(o).reshape(o_ref.shape), o_ref, "bf16", f"o step {step}")
+    torch.cuda.synchronize()
+    assert_close(to_np(S).reshape(Sr.shape), Sr, "bf16", "S")
+    if keep_m:
+        assert_close(to_np(M).reshape(Mr.shape), Mr, "bf16", "M")
+
+
 def test_decode_full_config_sampled_heads():
     """256 x 16 heads, d = 128, 512 steps (the benchmarked launch); 32 sampled
     heads followed by the oracle through every step."""
