@@ -18,6 +18,7 @@ The same JSON line carries:
                 from the profiled ones);
   kernels       the same record for every kernel of the step;
   split_path    the same forward through mdn_chunk_fwd_prepare + mdn_chunk_fwd_scan;
+  forward.from_logits  mdn_gates_from_logits, then the four-gate forward on its gates;
   forward       the whole step against both roofs;
   decode        the recurrent decode step at 256 sequences x 16 heads, d 128
                 (GB/s of algorithmic state + token traffic);
@@ -56,6 +57,8 @@ BYTES_PREP = 2 * D * 2 + 3 * 4 + BYTES_TA + BYTES_VEC
 STATE_BYTES_HEAD = 2 * D * D * 4         # S_T and M_T written once per (b, h)
 DEC_BYTES_HEAD = 4 * D * D * 4 + 3 * D * 2 + D * 2 + 3 * 4   # S, M in+out; q k v o; gates
 DEC_BYTES_HEAD_GDN = 2 * D * D * 4 + 3 * D * 2 + D * 2 + 2 * 4   # mu = 0: S only; two gates
+BYTES_GATES = 4 * 4 + 4 * 4              # four fp32 logits in, four fp32 gates out
+GATE_TAU = (2048 / 16) ** 0.5            # the temperature sqrt(d_in / h) at d_in 2048, 16 heads
 
 # HBM traffic per launch from rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, KiB per dispatch,
 # means over the profiled dispatches), recorded with the kernel sources whose sha256 is given;
@@ -63,26 +66,30 @@ DEC_BYTES_HEAD_GDN = 2 * D * D * 4 + 3 * D * 2 + D * 2 + 2 * 4   # mu = 0: S onl
 # 67,108,864 elements (reads 262,144 KiB, FETCH_SIZE 131,093.9; writes 131,072 KiB, WRITE_SIZE
 # 131,072.0).  An entry that covers several kernels of one call sums their dispatches.
 # Figures and commands: profiles/chunk_fwd_fused_B8H16T4096d128.md,
-# profiles/chunk_fwd_split_B8H16T4096d128.md and profiles/decode_step_N256H16d128.md.
+# profiles/chunk_fwd_split_B8H16T4096d128.md, profiles/decode_step_N256H16d128.md and
+# profiles/gates_from_logits_B8H16T4096.md.
 # A kernel whose sources changed reports traffic null.
 FETCH_FACTOR = 262144.0 / 131093.9
 WRITE_FACTOR = 131072.0 / 131072.0
 CSRC = os.path.join(ROOT, "chunkwise_delta_rule_amd", "csrc")
-_SPLIT_SHA = "6ea3e22bf2bc709479a8cca404573f1481629250d972d28b07290b1075ce920e"
+_SPLIT_SHA = "350d9d1fdd4d8c52823618a5f4545940c3716fc90611689eb634f3e80eab581a"
 TRAFFIC = {
-    # chunk_coef_kernel (3,100.5 / 51,458.4) + chunk_fwd_fused_kernel (223,505.3 / 147,456.2):
+    # chunk_coef_kernel (3,109.0 / 51,461.7) + chunk_fwd_fused_kernel (223,496.4 / 147,456.1):
     # one mdn_chunk_fwd call, the unit the bench times
     "chunk_fwd_fused_kernel": dict(sources=("chunk_fused.hip", "chunk_common.hpp", "mfma.hpp"),
-                                   fetch_kib=3100.5 + 223505.3, write_kib=51458.4 + 147456.2,
-                                   sha256="3241b1f9d44525f44a8a4253f91e7b1f"
-                                   "1fea3195bc2489a2132bdb95f7575180"),
+                                   fetch_kib=3109.0 + 223496.4, write_kib=51461.7 + 147456.1,
+                                   sha256="606172cabe668f8521453009dba7525a"
+                                   "7acf9d7156fa31b51ed5b4de8104de16"),
     "chunk_scan_bf16_kernel": dict(sources=("chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
-                                   fetch_kib=268385.5, write_kib=147456.2, sha256=_SPLIT_SHA),
+                                   fetch_kib=268392.0, write_kib=147456.4, sha256=_SPLIT_SHA),
     "chunk_prep_kernel": dict(sources=("chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
-                              fetch_kib=134752.5, write_kib=144936.3, sha256=_SPLIT_SHA),
-    "decode_step_kernel": dict(sources=("decode.hip", "mfma.hpp"), fetch_kib=264106.5,
-                               write_kib=525516.0, sha256="98626040b43b57d258352e14f9c2d2cd"
-                               "5f1e54ed58653cb636924adc441e3670"),
+                              fetch_kib=134528.7, write_kib=144054.7, sha256=_SPLIT_SHA),
+    "decode_step_kernel": dict(sources=("decode.hip", "mfma.hpp"), fetch_kib=264109.0,
+                               write_kib=525523.8, sha256="8fa39113008b99235e1abe57028f0d81"
+                               "9b837f475aa87000a6b4e46e3ea6c4e5"),
+    "gates_kernel": dict(sources=("gates.hip",), fetch_kib=4114.0, write_kib=8192.0,
+                         sha256="2bde382d2f924a1318325130cdb94dab"
+                         "7d2b47dcae9f102ec3b939b9dde52ce6"),
 }
 
 
@@ -246,6 +253,31 @@ def bench_forward(args, torch, si, mdn):
     fwd["no_mu"] = {"workload": "the same layer with mu = 0 (no mu given): the gated delta rule",
                     "us_per_step": gdn_ms * 1e3, "tokens_per_s": tokens / (gdn_ms * 1e-3)}
     del plan_g
+    # the coupled gates from logits (one mdn_gates_from_logits call), then the
+    # four-gate forward on its outputs: the whole layer core from projections
+    z = si.gate_logits(toh, seed=3, scale=1.0)
+    shape = (cfg.B, cfg.T, cfg.H)
+    zt = [up(z[n], f32).reshape(shape) for n in ("z_eta", "z_alpha", "z_beta", "z_mu")]
+    del z
+    gp = dict(tau=GATE_TAU, s=1.0, a=1.0, b=0.0, log_mu_min=-2.0)
+    gates = mdn.gates_from_logits(*zt, **gp)
+    gfn = lambda: mdn.gates_from_logits(*zt, **gp, out=gates)
+    plan_z = mdn.ChunkPlan(*plan.args[:3], gates[0], gates[1], gates[2], beta=gates[3])
+    settle(torch, [gfn, plan_z.forward], args.settle)
+    for _ in range(args.warmup):
+        gfn()
+        plan_z.forward()
+    (g_ms, _), gz_ms = time_calls(torch, [gfn, plan_z.forward], args.steps)
+    gbs = BYTES_GATES * toh / (g_ms * 1e-3) / 1e9
+    log(f"gates from logits: {g_ms * 1e3:.1f} us ({gbs:.0f} GB/s); with the forward "
+        f"{gz_ms * 1e3:.1f} us/step")
+    kernels["gates_kernel"] = roofline_of("gates_kernel", g_ms * 1e3, 0, BYTES_GATES * toh)
+    fwd["from_logits"] = {"workload": "mdn_gates_from_logits (tau = sqrt(2048 / 16), s = a = 1, "
+                                      "b = 0, log mu floor -2, logits ~ N(0, 1)) then the "
+                                      "four-gate forward",
+                          "us_per_step": gz_ms * 1e3, "tokens_per_s": tokens / (gz_ms * 1e-3),
+                          "gates_us": g_ms * 1e3, "gates_GB_per_s": gbs}
+    del plan_z, gates, zt
     return cfg, inp, step_ms, kernels, roofline, fwd, split
 
 

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
+
 #include "../../include/libmdn.h"
 
 namespace mdn {
@@ -24,6 +26,10 @@ hipError_t launch_chunk_scan(const void* q, const void* k, const void* v, const 
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* alpha,
                          const float* mu, const float* eta, const float* beta, float* S, float* M,
                          void* o, int heads, int Dk, int Dv, bool bf16, hipStream_t stream);
+hipError_t launch_gates(const float* z_eta, const float* z_alpha, const float* z_beta,
+                        const float* z_mu, size_t n, float tau, float s, float a, float b,
+                        float log_mu_min, float* alpha, float* mu, float* eta, float* beta,
+                        hipStream_t stream);
 }  // namespace mdn
 
 namespace {
@@ -292,6 +298,41 @@ mdn_status mdn_decode_step(const void* q, const void* k, const void* v, const fl
     if (overlap(so, sS) || overlap(so, sM) || overlap(sS, sM)) return MDN_ERR_ALIAS;
     const hipError_t err = mdn::launch_decode(q, k, v, alpha, mu, eta, beta, S, M, o, (int)heads,
                                               Dk, Dv, dt == MDN_BF16, stream);
+    return err == hipSuccess ? MDN_OK : MDN_ERR_HIP;
+}
+
+mdn_status mdn_gates_from_logits(const float* z_eta, const float* z_alpha, const float* z_beta,
+                                 const float* z_mu, size_t n, mdn_gate_params params,
+                                 float* alpha, float* mu, float* eta, float* beta,
+                                 hipStream_t stream)
+{
+    if (n == 0) return MDN_OK;
+    const float* ins[] = {z_eta, z_alpha, z_beta, z_mu};
+    float* outs[] = {alpha, mu, eta, beta};
+    for (const float* p : ins)
+        if (!p) return MDN_ERR_NULL;
+    for (const float* p : outs)
+        if (!p) return MDN_ERR_NULL;
+    for (const float* p : ins)
+        if (!aligned16(p)) return MDN_ERR_ALIGN;
+    for (const float* p : outs)
+        if (!aligned16(p)) return MDN_ERR_ALIGN;
+    if (n > (size_t)-1 / 4) return MDN_ERR_SHAPE;
+    const float pv[] = {params.tau, params.s, params.a, params.b, params.log_mu_min};
+    for (float x : pv)
+        if (!std::isfinite(x)) return MDN_ERR_UNSUPPORTED;
+    if (!(params.tau > 0.f)) return MDN_ERR_UNSUPPORTED;
+    Span sp[8];
+    for (int i = 0; i < 4; ++i) {
+        sp[i] = span(ins[i], n * 4);
+        sp[4 + i] = span(outs[i], n * 4);
+    }
+    for (int i = 0; i < 8; ++i)
+        for (int j = i + 1; j < 8; ++j)
+            if ((i >= 4 || j >= 4) && overlap(sp[i], sp[j])) return MDN_ERR_ALIAS;
+    const hipError_t err = mdn::launch_gates(z_eta, z_alpha, z_beta, z_mu, n, params.tau, params.s,
+                                             params.a, params.b, params.log_mu_min, alpha, mu,
+                                             eta, beta, stream);
     return err == hipSuccess ? MDN_OK : MDN_ERR_HIP;
 }
 

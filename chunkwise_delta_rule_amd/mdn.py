@@ -37,7 +37,14 @@ STATUS_NAMES = {
 # every symbol include/libmdn.h declares
 EXPORTED = ("mdn_chunk_fwd_workspace_bytes", "mdn_chunk_fwd_split_workspace_bytes",
             "mdn_chunk_fwd", "mdn_chunk_fwd_prepare",
-            "mdn_chunk_fwd_scan", "mdn_decode_step", "mdn_status_string")
+            "mdn_chunk_fwd_scan", "mdn_decode_step", "mdn_gates_from_logits",
+            "mdn_status_string")
+
+
+class GateParams(ctypes.Structure):
+    """mdn_gate_params, passed by value: f(z) = -a softplus(z + b)."""
+    _fields_ = [("tau", ctypes.c_float), ("s", ctypes.c_float), ("a", ctypes.c_float),
+                ("b", ctypes.c_float), ("log_mu_min", ctypes.c_float)]
 
 
 class MdnError(RuntimeError):
@@ -71,6 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mdn_chunk_fwd_scan.argtypes = [P] * 8 + [I] * 7 + [P, S, P]
     lib.mdn_decode_step.restype = I
     lib.mdn_decode_step.argtypes = [P] * 10 + [I] * 5 + [P]
+    lib.mdn_gates_from_logits.restype = I
+    lib.mdn_gates_from_logits.argtypes = [P] * 4 + [S, GateParams] + [P] * 4 + [P]
     lib.mdn_status_string.restype = ctypes.c_char_p
     lib.mdn_status_string.argtypes = [I]
     if path == LIB_PATH:
@@ -257,3 +266,29 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.
     if st != 0:
         raise MdnError(st, "mdn_decode_step")
     return o
+
+
+def gates_from_logits(z_eta: torch.Tensor, z_alpha: torch.Tensor, z_beta: torch.Tensor,
+                      z_mu: torch.Tensor, *, tau: float, s: float, a: float, b: float,
+                      log_mu_min: float = -2.0,
+                      out: Optional[Tuple[torch.Tensor, ...]] = None
+                      ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
+    """MDN's coupled gates from logits (float32, one shape for all four, e.g.
+    [B, T, H]).  Returns (alpha, mu, eta, beta) of that shape, float32, in
+    the form chunk_fwd and decode_step take them."""
+    lib = load_library()
+    dev = z_eta.device
+    shape = tuple(z_eta.shape)
+    for name, z in (("z_eta", z_eta), ("z_alpha", z_alpha), ("z_beta", z_beta), ("z_mu", z_mu)):
+        _check(z, name, shape, torch.float32, dev)
+    if out is None:
+        out = tuple(torch.empty(shape, dtype=torch.float32, device=dev) for _ in range(4))
+    for name, g in zip(("alpha", "mu", "eta", "beta"), out):
+        _check(g, name, shape, torch.float32, dev)
+    n = z_eta.numel()
+    p = GateParams(tau, s, a, b, log_mu_min)
+    st = lib.mdn_gates_from_logits(_ptr(z_eta), _ptr(z_alpha), _ptr(z_beta), _ptr(z_mu), n, p,
+                                   *(_ptr(g) for g in out), _stream(dev))
+    if st != 0:
+        raise MdnError(st, "mdn_gates_from_logits")
+    return tuple(out)

@@ -179,6 +179,43 @@ mdn_status mdn_decode_step(const void* q, const void* k, const void* v, const fl
                            float* M, void* o, int N, int H, int Dk, int Dv, mdn_dtype dt,
                            hipStream_t stream);
 
+/*
+ * MDN's coupled gate parameterisation ("MDN: Parallelizing Stepwise Momentum
+ * for Delta Linear Attention" (slides), frame "Coupled gates restrict the
+ * spectral region", the paper's Sec. 3.3), from logits the caller computes
+ * (its projections W x_t of the layer input) to the gates of the recurrence:
+ *     eta   = 1 + tanh(z_eta / tau)
+ *     theta = arctan(s eta),  alpha_max = cos^2 theta,  beta_max = sin^2 theta
+ *     log alpha = f(z_alpha) + log alpha_max
+ *     beta      = sigmoid(z_beta) beta_max
+ *     log mu    = max(f(z_mu), log_mu_min),      f(z) = -a softplus(z + b)
+ * so that eta is in (0, 2) and, for a >= 0, alpha + beta <= 1.  The slides
+ * give tau = sqrt(d_in / h) as the paper's default and log_mu_min = -2 for
+ * the reported experiments; a, b and s are the caller's.
+ *   z_eta, z_alpha, z_beta, z_mu    n logits each (float32, any layout, one
+ *                                   value per token and head).
+ *   alpha, mu, eta, beta            n gates each (float32, same order), in
+ *                                   the form mdn_chunk_fwd and
+ *                                   mdn_decode_step take them.
+ * All eight are device pointers aligned to 16 bytes (MDN_ERR_ALIGN), none
+ * NULL (MDN_ERR_NULL) unless n = 0, which launches nothing.  No output may
+ * overlap another output or an input (MDN_ERR_ALIAS); inputs may share
+ * memory.  tau must be positive and every parameter finite
+ * (MDN_ERR_UNSUPPORTED otherwise).  Enqueued on `stream`; the caller owns
+ * every buffer.
+ */
+typedef struct {
+    float tau;          /* temperature of eta                              */
+    float s;            /* angle scale of theta                            */
+    float a, b;         /* f(z) = -a softplus(z + b), for alpha and mu     */
+    float log_mu_min;   /* floor of log mu                                 */
+} mdn_gate_params;
+
+mdn_status mdn_gates_from_logits(const float* z_eta, const float* z_alpha, const float* z_beta,
+                                 const float* z_mu, size_t n, mdn_gate_params params,
+                                 float* alpha, float* mu, float* eta, float* beta,
+                                 hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* mdn_status_string(mdn_status s);
 

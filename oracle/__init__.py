@@ -170,3 +170,28 @@ def chunk_gamma(alpha, mu, beta=None, *, form: int = 0, lib: Optional[ctypes.CDL
     if rc != 0:
         raise RuntimeError(f"mdn_oracle_chunk_gamma failed with code {rc}")
     return G
+
+
+def gates_from_logits(z_eta, z_alpha, z_beta, z_mu, *, tau: float, s: float, a: float, b: float,
+                      log_mu_min: float):
+    """MDN's coupled gate parameterisation in float64, term by term as
+    [MDN slides] frame "Coupled gates restrict the spectral region" (the
+    paper's Sec. 3.3; [MDN notes] Sec. 2.8) writes it:
+        eta = 1 + tanh(z_eta / tau),  theta = arctan(s eta),
+        alpha_max = cos^2 theta,  beta_max = sin^2 theta,
+        log alpha = f(z_alpha) + log alpha_max,  beta = sigmoid(z_beta) beta_max,
+        log mu = max(f(z_mu), log_mu_min),  f(z) = -a softplus(z + b).
+    Plain numpy; softplus(x) = log(1 + e^x) as numpy's logaddexp(0, x).
+    Returns (alpha, mu, eta, beta)."""
+    z = lambda x: np.asarray(x, dtype=np.float64)
+    f = lambda x: -a * np.logaddexp(0.0, x + b)
+    eta = 1.0 + np.tanh(z(z_eta) / tau)
+    theta = np.arctan(s * eta)
+    alpha_max = np.cos(theta) ** 2
+    beta_max = np.sin(theta) ** 2
+    alpha = np.exp(f(z(z_alpha)) + np.log(alpha_max))
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-z(z_beta)))
+    beta = sig * beta_max
+    mu = np.exp(np.maximum(f(z(z_mu)), log_mu_min))
+    return alpha, mu, eta, beta

@@ -222,3 +222,19 @@ def decode_stream(cfg: DecodeConfig, **overrides) -> Iterator:
 
 def tokens_per_call(cfg: ForwardConfig) -> int:
     return cfg.B * cfg.T
+
+
+def gate_logits(n: int, seed: int, scale: float = 3.0) -> Dict[str, np.ndarray]:
+    """Four float32 logit arrays of n values each (z_eta, z_alpha, z_beta,
+    z_mu, drawn in this order) ~ N(0, scale^2), the first 16 entries of each
+    replaced by fixed extremes (+-1e3, +-100, +-30, +-10, +-1, +-1e-3, 0 and
+    -0) so that the saturated ends are always covered."""
+    rng = np.random.default_rng(SEED_BASE + seed)
+    ext = np.array([1e3, -1e3, 100, -100, 30, -30, 10, -10, 1, -1, 1e-3, -1e-3, 0.0, -0.0, 5, -5])
+    out = {}
+    for name in ("z_eta", "z_alpha", "z_beta", "z_mu"):
+        z = rng.normal(0.0, scale, size=n)
+        m = min(n, ext.size)
+        z[:m] = np.roll(ext, len(out) * 3)[:m]
+        out[name] = z.astype(np.float32)
+    return out

@@ -407,6 +407,49 @@ def pin_deltanet_chunk(lib):
 # P9: structural invariants of the operator ([MDN slides] "Chunk outputs
 # combine incoming states and local writes": two final states pass onward)
 # --------------------------------------------------------------------------
+def pin_gate_parameterisation(lib):
+    """The coupled gates ([MDN slides] frame "Coupled gates restrict the
+    spectral region"):
+      - z_eta = 0 gives eta = 1, so alpha_max = 1 / (1 + s^2) and
+        beta_max = s^2 / (1 + s^2) (cos^2 and sin^2 of arctan s);
+      - z_alpha = -b gives softplus(0) = log 2, so alpha = alpha_max 2^-a;
+        z_beta = 0 gives beta = beta_max / 2; z_mu = -b gives
+        mu = max(2^-a, e^floor);
+      - for any logits: 0 < eta < 2, alpha + beta <= 1, alpha <= alpha_max,
+        mu <= 1 and log mu >= the floor;
+      - z_mu -> -inf gives mu -> 1 and z_mu -> +inf gives mu = e^floor."""
+    del lib
+    tau, s, a, b, fl = 2.5, 1.7, 0.8, 0.3, -2.0
+    kw = dict(tau=tau, s=s, a=a, b=b, log_mu_min=fl)
+    al, mu, eta, be = oracle.gates_from_logits([0.0], [-b], [0.0], [-b], **kw)
+    amax, bmax = 1.0 / (1.0 + s * s), s * s / (1.0 + s * s)
+    assert abs(eta[0] - 1.0) < 1e-15
+    assert _rel(al, [amax * 2.0 ** -a]) < 1e-14
+    assert _rel(be, [bmax / 2.0]) < 1e-14
+    assert _rel(mu, [max(2.0 ** -a, np.exp(fl))]) < 1e-14
+    # off the centre: z_eta = tau artanh(1/2) gives eta = 3/2; z_alpha with
+    # softplus(z_alpha + b) = 1 gives alpha = alpha_max e^-a; z_beta = log 3
+    # gives sigmoid = 3/4
+    al, mu, eta, be = oracle.gates_from_logits([tau * np.arctanh(0.5)], [np.log(np.e - 1) - b],
+                                               [np.log(3.0)], [-b], **kw)
+    x2 = (1.5 * s) ** 2
+    assert _rel(eta, [1.5]) < 1e-14
+    assert _rel(al, [np.exp(-a) / (1.0 + x2)]) < 1e-14
+    assert _rel(be, [0.75 * x2 / (1.0 + x2)]) < 1e-14
+    rng = np.random.default_rng(31)
+    zs = [rng.normal(0.0, 4.0, 10000) for _ in range(4)]
+    al, mu, eta, be = oracle.gates_from_logits(*zs, **kw)
+    assert np.all(eta > 0.0) and np.all(eta < 2.0)
+    assert np.all(al + be <= 1.0 + 1e-15)
+    th = np.arctan(s * eta)
+    assert np.all(al <= np.cos(th) ** 2 * (1 + 1e-15))
+    assert np.all(mu <= 1.0) and np.all(np.log(mu) >= fl - 1e-12)
+    _, mu_lo, _, _ = oracle.gates_from_logits([0.0], [0.0], [0.0], [-60.0], **kw)
+    _, mu_hi, _, _ = oracle.gates_from_logits([0.0], [0.0], [0.0], [60.0], **kw)
+    assert abs(mu_lo[0] - 1.0) < 1e-20 + a * np.exp(-60 + b) * 2
+    assert _rel(mu_hi, [np.exp(fl)]) < 1e-15
+
+
 def pin_invariants(lib):
     rng = np.random.default_rng(21)
     B, T, H, Dk, Dv = 2, 29, 2, 6, 7
@@ -451,7 +494,7 @@ def pin_invariants(lib):
     assert _rel(S, ST) < TOL and _rel(M, MT) < TOL
 
 
-ALL_PINS = [
+ALL_PINS = [pin_gate_parameterisation, 
     pin_one_token,
     pin_two_tokens,
     pin_gdn_reduction,

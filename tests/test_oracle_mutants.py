@@ -73,3 +73,38 @@ def test_pins_catch_mutant(name, old, new, tmp_path):
                 __import__("numpy").linalg.LinAlgError):
             caught.append(pin.__name__)
     assert caught, f"no pin caught the planted mistake '{name}'"
+
+
+# the gate parameterisation is numpy code in oracle/__init__.py: mutate the
+# function's own source text and run the pins against the mutated copy
+GATE_MUTANTS = [
+    ("eta offset dropped", "eta = 1.0 + np.tanh(", "eta = np.tanh("),
+    ("eta temperature multiplies", "np.tanh(z(z_eta) / tau)", "np.tanh(z(z_eta) * tau)"),
+    ("cos and sin swapped", "alpha_max = np.cos(theta) ** 2", "alpha_max = np.sin(theta) ** 2"),
+    ("softplus shift sign", "np.logaddexp(0.0, x + b)", "np.logaddexp(0.0, x - b)"),
+    ("decay scale dropped", "f = lambda x: -a * np.logaddexp", "f = lambda x: -np.logaddexp"),
+    ("alpha_max dropped", "alpha = np.exp(f(z(z_alpha)) + np.log(alpha_max))",
+     "alpha = np.exp(f(z(z_alpha)))"),
+    ("sigmoid sign", "sig = 1.0 / (1.0 + np.exp(-z(z_beta)))",
+     "sig = 1.0 / (1.0 + np.exp(z(z_beta)))"),
+    ("beta_max dropped", "beta = sig * beta_max", "beta = sig"),
+    ("momentum floor as a ceiling", "np.maximum(f(z(z_mu)), log_mu_min)",
+     "np.minimum(f(z(z_mu)), log_mu_min)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", GATE_MUTANTS, ids=[m[0] for m in GATE_MUTANTS])
+def test_gate_pin_catches_mutant(name, old, new, monkeypatch):
+    import inspect
+    import textwrap
+
+    import numpy as np
+    from oracle_pins import pin_gate_parameterisation
+
+    src = textwrap.dedent(inspect.getsource(oracle.gates_from_logits))
+    assert src.count(old) == 1, f"mutation site for '{name}' not found exactly once"
+    ns = {"np": np}
+    exec(compile(src.replace(old, new), "<gate mutant>", "exec"), ns)
+    monkeypatch.setattr(oracle, "gates_from_logits", ns["gates_from_logits"])
+    with pytest.raises(AssertionError):
+        pin_gate_parameterisation(None)
