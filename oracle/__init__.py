@@ -15,6 +15,12 @@ Sources:
                 Eqs. (7)-(9), (15)-(18), (40)-(42) and the backup frames for
                 the chunkwise equations.
   [MDN notes]   reading notes on the same paper, Secs. 2.2-2.6.
+
+The backward pass (``recurrence_backward``) is the reverse-mode derivative of
+the recurrence: the pages give its strategy (save the residuals, rebuild the
+states; [MDN slides] frame "The implementation trades saved residuals for
+throughput", [MDN notes] Sec. 2.6) but no gradient
+formulas, so the definition of the derivative is the reference.
 """
 from __future__ import annotations
 
@@ -56,6 +62,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.mdn_oracle_chunk_bruteforce.argtypes = [dp] * 12 + [ctypes.c_int] * 8
     lib.mdn_oracle_chunk_gamma.restype = ctypes.c_int
     lib.mdn_oracle_chunk_gamma.argtypes = [dp, dp, dp, ctypes.c_int, ctypes.c_int, dp]
+    lib.mdn_oracle_recurrence_backward.restype = ctypes.c_int
+    lib.mdn_oracle_recurrence_backward.argtypes = [dp] * 21 + [ctypes.c_int] * 7
     lib.mdn_oracle_max_threads.restype = ctypes.c_int
     lib.mdn_oracle_max_threads.argtypes = []
     return lib
@@ -116,6 +124,40 @@ def recurrence(q, k, v, alpha, mu, eta, beta=None, S0=None, M0=None, *,
     if rc != 0:
         raise RuntimeError(f"mdn_oracle_recurrence failed with code {rc}")
     return O, ST, MT
+
+
+def recurrence_backward(q, k, v, alpha, mu, eta, beta=None, S0=None, M0=None, *, dO,
+                        dST=None, dMT=None, col_block: int = 16, nthreads: int = 0,
+                        lib: Optional[ctypes.CDLL] = None):
+    """Reverse-mode derivative of :func:`recurrence` in fp64: the gradients of
+    a loss L given dO = dL/dO and dST, dMT = dL/dS_T, dL/dM_T (None: zero).
+    Returns a dict with dq, dk, dv, dalpha, dmu, deta, dbeta (None when beta
+    is None: beta = 1 is then not an input), dS0 and dM0."""
+    lib = lib or load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    alpha, mu, eta, beta = _f64(alpha), _f64(mu), _f64(eta), _f64(beta)
+    S0, M0, dO, dST, dMT = _f64(S0), _f64(M0), _f64(dO), _f64(dST), _f64(dMT)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    assert k.shape == q.shape and v.shape == (B, T, H, Dv) and dO.shape == v.shape
+    for g in (alpha, mu, eta) + ((beta,) if beta is not None else ()):
+        assert g.shape == (B, T, H)
+    for st in (S0, M0, dST, dMT):
+        assert st is None or st.shape == (B, H, Dk, Dv)
+    out = dict(dq=np.zeros((B, T, H, Dk)), dk=np.zeros((B, T, H, Dk)),
+               dv=np.zeros((B, T, H, Dv)), dalpha=np.zeros((B, T, H)),
+               dbeta=None if beta is None else np.zeros((B, T, H)), dmu=np.zeros((B, T, H)),
+               deta=np.zeros((B, T, H)), dS0=np.zeros((B, H, Dk, Dv)),
+               dM0=np.zeros((B, H, Dk, Dv)))
+    rc = lib.mdn_oracle_recurrence_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(mu), _ptr(eta), _ptr(S0),
+        _ptr(M0), _ptr(dO), _ptr(dST), _ptr(dMT), _ptr(out["dq"]), _ptr(out["dk"]),
+        _ptr(out["dv"]), _ptr(out["dalpha"]), _ptr(out["dbeta"]), _ptr(out["dmu"]),
+        _ptr(out["deta"]), _ptr(out["dS0"]), _ptr(out["dM0"]), B, T, H, Dk, Dv, col_block,
+        nthreads)
+    if rc != 0:
+        raise RuntimeError(f"mdn_oracle_recurrence_backward failed with code {rc}")
+    return out
 
 
 def decode_step(q, k, v, alpha, mu, eta, S, M, beta=None, *, nthreads: int = 0,

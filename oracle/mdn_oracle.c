@@ -185,6 +185,219 @@ int mdn_oracle_max_threads(void)
 }
 
 /* ------------------------------------------------------------------------ */
+/* Reverse-mode derivative of the token recurrence                           */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The pages give the backward pass's strategy but no gradient formulas, so
+ * this is the plain reverse-mode derivative of the recurrence above (the
+ * chain rule applied to each line of the token step, last token first).
+ * Given dO = dL/dO, dST = dL/dS_T and dMT = dL/dM_T, and writing Sh and Mh for
+ * the running gradients dL/dS_t and dL/dM_t (from the later tokens), token t
+ * (a = alpha_t, m = mu_t, e = eta_t, s = beta_t) contributes:
+ *     o_t = S_t^T q_t:              Sh += q_t do_t^T;  dq_t = S_t do_t
+ *     S_t = a S_{t-1} - s M_t:      dalpha_t += <S_{t-1}, Sh>;  dbeta_t = -<M_t, Sh>
+ *                                   P = Mh - s Sh  (the whole dL/dM_t)
+ *     M_t = m M_{t-1} - e k_t vt^T: dmu_t = <M_{t-1}, P>;  deta_t = -k_t^T P vt
+ *                                   dk_t = -e P vt;  dvt = -e P^T k_t
+ *     vt = v_t - a S_{t-1}^T k_t:   dv_t = dvt;  dk_t += -a S_{t-1} dvt
+ *                                   dalpha_t += -k_t^T S_{t-1} dvt
+ * and hands on Sh <- a Sh - a k_t dvt^T, Mh <- m P.  After token 1,
+ * dS0 = Sh and dM0 = Mh.  <X, Y> is the sum of X .* Y over d_k x d_v.
+ *
+ * A work unit is one (b, h); it runs column blocks one after another, each
+ * with its forward states S_t, M_t (t = 0..T) stored, and adds the column
+ * sums (dq, dk and the gate gradients) into the unit's own slices.
+ */
+static void backward_unit(const double* q, const double* k, const double* v,
+                          const double* alpha, const double* beta, const double* mu,
+                          const double* eta, const double* S0, const double* M0,
+                          const double* dO, const double* dST, const double* dMT, double* dq,
+                          double* dk, double* dv, double* dalpha, double* dbeta, double* dmu,
+                          double* deta, double* dS0, double* dM0, int b, int h, int T, int H,
+                          int Dk, int Dv, int col_block, double* Ss, double* Ms, double* vts,
+                          double* Sh, double* Mh, double* P, double* dvt)
+{
+    for (int t = 0; t < T; ++t) {
+        const size_t g = IDX_GATE(b, t, h, T, H);
+        dalpha[g] = 0.0;
+        dmu[g] = 0.0;
+        deta[g] = 0.0;
+        if (dbeta) dbeta[g] = 0.0;
+        for (int i = 0; i < Dk; ++i) {
+            dq[IDX_TOK(b, t, h, i, T, H, Dk)] = 0.0;
+            dk[IDX_TOK(b, t, h, i, T, H, Dk)] = 0.0;
+        }
+    }
+    for (int c0 = 0; c0 < Dv; c0 += col_block) {
+        const int nc = (c0 + col_block <= Dv) ? col_block : Dv - c0;
+        const size_t st = (size_t)Dk * nc;   /* one stored state */
+        /* forward, keeping S_t, M_t for t = 0..T and vt_t */
+        for (int i = 0; i < Dk; ++i)
+            for (int c = 0; c < nc; ++c) {
+                Ss[(size_t)i * nc + c] = S0 ? S0[IDX_STATE(b, h, i, c0 + c, H, Dk, Dv)] : 0.0;
+                Ms[(size_t)i * nc + c] = M0 ? M0[IDX_STATE(b, h, i, c0 + c, H, Dk, Dv)] : 0.0;
+            }
+        for (int t = 0; t < T; ++t) {
+            const size_t g = IDX_GATE(b, t, h, T, H);
+            const double a = alpha[g], m = mu[g], e = eta[g], s = beta ? beta[g] : 1.0;
+            const double* kt = k + IDX_TOK(b, t, h, 0, T, H, Dk);
+            const double* vv = v + IDX_TOK(b, t, h, c0, T, H, Dv);
+            const double* Sp = Ss + st * t;
+            const double* Mp = Ms + st * t;
+            double* Sn = Ss + st * (t + 1);
+            double* Mn = Ms + st * (t + 1);
+            double* vt = vts + (size_t)nc * t;
+            for (int c = 0; c < nc; ++c) vt[c] = 0.0;
+            for (int i = 0; i < Dk; ++i)
+                for (int c = 0; c < nc; ++c) vt[c] += Sp[(size_t)i * nc + c] * kt[i];
+            for (int c = 0; c < nc; ++c) vt[c] = vv[c] - a * vt[c];
+            for (int i = 0; i < Dk; ++i)
+                for (int c = 0; c < nc; ++c) {
+                    const size_t x = (size_t)i * nc + c;
+                    Mn[x] = m * Mp[x] - e * kt[i] * vt[c];
+                    Sn[x] = a * Sp[x] - s * Mn[x];
+                }
+        }
+        /* backward, last token first */
+        for (int i = 0; i < Dk; ++i)
+            for (int c = 0; c < nc; ++c) {
+                Sh[(size_t)i * nc + c] = dST ? dST[IDX_STATE(b, h, i, c0 + c, H, Dk, Dv)] : 0.0;
+                Mh[(size_t)i * nc + c] = dMT ? dMT[IDX_STATE(b, h, i, c0 + c, H, Dk, Dv)] : 0.0;
+            }
+        for (int t = T - 1; t >= 0; --t) {
+            const size_t g = IDX_GATE(b, t, h, T, H);
+            const double a = alpha[g], m = mu[g], e = eta[g], s = beta ? beta[g] : 1.0;
+            const double* kt = k + IDX_TOK(b, t, h, 0, T, H, Dk);
+            const double* qt = q + IDX_TOK(b, t, h, 0, T, H, Dk);
+            const double* dot = dO + IDX_TOK(b, t, h, c0, T, H, Dv);
+            const double* Sp = Ss + st * t;         /* S_{t-1} */
+            const double* Mp = Ms + st * t;         /* M_{t-1} */
+            const double* Sn = Ss + st * (t + 1);   /* S_t */
+            const double* Mn = Ms + st * (t + 1);   /* M_t */
+            const double* vt = vts + (size_t)nc * t;
+            double* dqt = dq + IDX_TOK(b, t, h, 0, T, H, Dk);
+            double* dkt = dk + IDX_TOK(b, t, h, 0, T, H, Dk);
+            double* dvv = dv + IDX_TOK(b, t, h, c0, T, H, Dv);
+            double ga = 0.0, gb = 0.0, gm = 0.0, ge = 0.0;
+            /* read-out */
+            for (int i = 0; i < Dk; ++i) {
+                double acc = 0.0;
+                for (int c = 0; c < nc; ++c) {
+                    const size_t x = (size_t)i * nc + c;
+                    Sh[x] += qt[i] * dot[c];
+                    acc += Sn[x] * dot[c];
+                }
+                dqt[i] += acc;
+            }
+            /* memory step */
+            for (size_t x = 0; x < st; ++x) {
+                ga += Sp[x] * Sh[x];
+                gb -= Mn[x] * Sh[x];
+                P[x] = Mh[x] - s * Sh[x];
+            }
+            /* momentum step */
+            for (int c = 0; c < nc; ++c) dvt[c] = 0.0;
+            for (int i = 0; i < Dk; ++i) {
+                double acc = 0.0;
+                for (int c = 0; c < nc; ++c) {
+                    const size_t x = (size_t)i * nc + c;
+                    gm += Mp[x] * P[x];
+                    acc += P[x] * vt[c];
+                    dvt[c] += P[x] * kt[i];
+                }
+                ge -= kt[i] * acc;
+                dkt[i] -= e * acc;
+            }
+            for (int c = 0; c < nc; ++c) dvt[c] *= -e;
+            /* residual */
+            for (int c = 0; c < nc; ++c) dvv[c] = dvt[c];
+            for (int i = 0; i < Dk; ++i) {
+                double acc = 0.0;
+                for (int c = 0; c < nc; ++c) acc += Sp[(size_t)i * nc + c] * dvt[c];
+                dkt[i] -= a * acc;
+                ga -= kt[i] * acc;
+            }
+            /* hand on to token t-1 */
+            for (int i = 0; i < Dk; ++i)
+                for (int c = 0; c < nc; ++c) {
+                    const size_t x = (size_t)i * nc + c;
+                    Sh[x] = a * Sh[x] - a * kt[i] * dvt[c];
+                    Mh[x] = m * P[x];
+                }
+            dalpha[g] += ga;
+            dmu[g] += gm;
+            deta[g] += ge;
+            if (dbeta) dbeta[g] += gb;
+        }
+        for (int i = 0; i < Dk; ++i)
+            for (int c = 0; c < nc; ++c) {
+                if (dS0) dS0[IDX_STATE(b, h, i, c0 + c, H, Dk, Dv)] = Sh[(size_t)i * nc + c];
+                if (dM0) dM0[IDX_STATE(b, h, i, c0 + c, H, Dk, Dv)] = Mh[(size_t)i * nc + c];
+            }
+    }
+}
+
+/*
+ * Gradients of a loss L through the recurrence, given dO [B,T,H,Dv] and
+ * optional dST, dMT [B,H,Dk,Dv] (NULL: zero).  Outputs: dq, dk [B,T,H,Dk];
+ * dv [B,T,H,Dv]; dalpha, dmu, deta [B,T,H]; dbeta [B,T,H] or NULL (then
+ * not computed); dS0, dM0 [B,H,Dk,Dv] or NULL.  beta NULL means beta = 1.
+ * Memory: 2 (T + 1) Dk col_block doubles per thread.  Returns 0 on success.
+ */
+int mdn_oracle_recurrence_backward(const double* q, const double* k, const double* v,
+                                   const double* alpha, const double* beta, const double* mu,
+                                   const double* eta, const double* S0, const double* M0,
+                                   const double* dO, const double* dST, const double* dMT,
+                                   double* dq, double* dk, double* dv, double* dalpha,
+                                   double* dbeta, double* dmu, double* deta, double* dS0,
+                                   double* dM0, int B, int T, int H, int Dk, int Dv,
+                                   int col_block, int nthreads)
+{
+    if (!q || !k || !v || !alpha || !mu || !eta || !dO) return 1;
+    if (!dq || !dk || !dv || !dalpha || !dmu || !deta) return 1;
+    if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return 2;
+    if (col_block <= 0 || col_block > Dv) col_block = Dv;
+    const long units = (long)B * H;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel reduction(| : failed)
+    {
+        const size_t st = (size_t)Dk * col_block;
+        double* Ss = (double*)malloc(sizeof(double) * st * ((size_t)T + 1));
+        double* Ms = (double*)malloc(sizeof(double) * st * ((size_t)T + 1));
+        double* vts = (double*)malloc(sizeof(double) * (size_t)col_block * (T > 0 ? T : 1));
+        double* Sh = (double*)malloc(sizeof(double) * st);
+        double* Mh = (double*)malloc(sizeof(double) * st);
+        double* P = (double*)malloc(sizeof(double) * st);
+        double* dvt = (double*)malloc(sizeof(double) * (size_t)col_block);
+        const int ok = Ss && Ms && vts && Sh && Mh && P && dvt;
+        if (!ok) failed = 1;
+#pragma omp for schedule(dynamic, 1)
+        for (long u = 0; u < units; ++u) {
+            if (!ok) continue;
+            const int h = (int)(u % H);
+            const int b = (int)(u / H);
+            backward_unit(q, k, v, alpha, beta, mu, eta, S0, M0, dO, dST, dMT, dq, dk, dv,
+                          dalpha, dbeta, dmu, deta, dS0, dM0, b, h, T, H, Dk, Dv, col_block,
+                          Ss, Ms, vts, Sh, Mh, P, dvt);
+        }
+        free(Ss);
+        free(Ms);
+        free(vts);
+        free(Sh);
+        free(Mh);
+        free(P);
+        free(dvt);
+    }
+    return failed ? 3 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Brute-force chunkwise evaluator (tiny inputs only)                        */
 /* ------------------------------------------------------------------------ */
 

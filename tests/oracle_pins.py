@@ -450,6 +450,61 @@ def pin_gate_parameterisation(lib):
     assert _rel(mu_hi, [np.exp(fl)]) < 1e-15
 
 
+def _fd_check(lib, inp, dO, dST, dMT, col_block, h=1e-6, tol=1e-8):
+    """Central differences of L = <dO, O> + <dST, S_T> + <dMT, M_T> in every
+    input element against recurrence_backward's gradient."""
+    def loss(**over):
+        x = dict(inp)
+        x.update(over)
+        O, ST, MT = oracle.recurrence(x["q"], x["k"], x["v"], x["alpha"], x["mu"], x["eta"],
+                                      x["beta"], x["S0"], x["M0"], lib=lib)
+        val = float(np.sum(O * dO))
+        if dST is not None:
+            val += float(np.sum(ST * dST))
+        if dMT is not None:
+            val += float(np.sum(MT * dMT))
+        return val
+    g = oracle.recurrence_backward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["mu"],
+                                   inp["eta"], inp["beta"], inp["S0"], inp["M0"], dO=dO,
+                                   dST=dST, dMT=dMT, col_block=col_block, lib=lib)
+    for name, x in inp.items():
+        if x is None:
+            continue
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = x.copy()
+            xp[idx] += h
+            xm = x.copy()
+            xm[idx] -= h
+            fd[idx] = (loss(**{name: xp}) - loss(**{name: xm})) / (2 * h)
+        got = g["d" + name]
+        assert got is not None, name
+        err = _rel(got, fd)
+        assert err < tol, f"d{name}: finite differences disagree ({err:.2e})"
+
+
+def pin_backward_finite_differences(lib):
+    """The pages state the backward pass's strategy (save the residuals,
+    rebuild the states) but no gradient formulas, so the reverse-mode
+    derivative is pinned by its definition: central differences of a random
+    linear functional of (O, S_T, M_T), element by element, for every input.
+    Two cases: all four gates with initial states, terminal gradients and a
+    ragged column block; beta = 1 (None), mu = 0, zero initial state and no
+    terminal gradient."""
+    rng = np.random.default_rng(41)
+    B, T, H, Dk, Dv = 1, 5, 2, 3, 4
+    a, m, e = _gates(rng, (B, T, H))
+    inp = dict(q=rng.standard_normal((B, T, H, Dk)), k=rng.standard_normal((B, T, H, Dk)),
+               v=rng.standard_normal((B, T, H, Dv)), alpha=a, mu=m, eta=e,
+               beta=rng.uniform(0.2, 1.0, (B, T, H)), S0=rng.standard_normal((B, H, Dk, Dv)),
+               M0=rng.standard_normal((B, H, Dk, Dv)))
+    _fd_check(lib, inp, rng.standard_normal((B, T, H, Dv)),
+              rng.standard_normal((B, H, Dk, Dv)), rng.standard_normal((B, H, Dk, Dv)),
+              col_block=3)
+    inp.update(beta=None, mu=np.zeros((B, T, H)), S0=None, M0=None)
+    _fd_check(lib, inp, rng.standard_normal((B, T, H, Dv)), None, None, col_block=16)
+
+
 def pin_invariants(lib):
     rng = np.random.default_rng(21)
     B, T, H, Dk, Dv = 2, 29, 2, 6, 7
@@ -494,7 +549,7 @@ def pin_invariants(lib):
     assert _rel(S, ST) < TOL and _rel(M, MT) < TOL
 
 
-ALL_PINS = [pin_gate_parameterisation, 
+ALL_PINS = [pin_gate_parameterisation, pin_backward_finite_differences, 
     pin_one_token,
     pin_two_tokens,
     pin_gdn_reduction,

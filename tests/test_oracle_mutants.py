@@ -54,6 +54,19 @@ MUTANTS = [
      "if (j < i) x = G[(size_t)(i - 1) * n + j];", "if (j < i) x = G[(size_t)i * n + j];"),
     ("brute force: carry uses old momentum sign",
      "Mn[x] = mbar[n] * M[x] - wm;", "Mn[x] = mbar[n] * M[x] + wm;"),
+    ("backward: read-out gradient uses the key",
+     "Sh[x] += qt[i] * dot[c];", "Sh[x] += kt[i] * dot[c];"),
+    ("backward: memory step drops beta",
+     "P[x] = Mh[x] - s * Sh[x];", "P[x] = Mh[x] - Sh[x];"),
+    ("backward: memory gradient not decayed",
+     "Sh[x] = a * Sh[x] - a * kt[i] * dvt[c];", "Sh[x] = Sh[x] - a * kt[i] * dvt[c];"),
+    ("backward: residual gradient sign",
+     "for (int c = 0; c < nc; ++c) dvt[c] *= -e;", "for (int c = 0; c < nc; ++c) dvt[c] *= e;"),
+    ("backward: momentum gradient skips the memory step",
+     "Mh[x] = m * P[x];", "Mh[x] = m * Mh[x];"),
+    ("backward: dalpha misses the residual term",
+     "ga -= kt[i] * acc;", "ga -= 0.0 * kt[i] * acc;"),
+    ("backward: deta sign", "ge -= kt[i] * acc;", "ge += kt[i] * acc;"),
 ]
 
 
