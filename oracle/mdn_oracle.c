@@ -57,6 +57,27 @@
 /* Token recurrence                                                          */
 /* ------------------------------------------------------------------------ */
 
+/* One token's update of a column block of S and M, in place (the step
+ * recurrence_unit describes); vt receives the residual. */
+static void token_step(const double* kt, const double* vv, double a, double m, double e,
+                       double s, double* S, double* M, double* vt, int Dk, int nc)
+{
+    /* S_{t-1}^T k_t, column by column */
+    for (int c = 0; c < nc; ++c) vt[c] = 0.0;
+    for (int i = 0; i < Dk; ++i)
+        for (int c = 0; c < nc; ++c) vt[c] += S[(size_t)i * nc + c] * kt[i];
+    for (int c = 0; c < nc; ++c) vt[c] = vv[c] - a * vt[c];
+
+    /* momentum, then memory (which reads the new momentum) */
+    for (int i = 0; i < Dk; ++i) {
+        for (int c = 0; c < nc; ++c) {
+            const size_t x = (size_t)i * nc + c;
+            M[x] = m * M[x] - e * kt[i] * vt[c];
+            S[x] = a * S[x] - s * M[x];
+        }
+    }
+}
+
 /*
  * One (b, h, column block) work unit.  Columns of S and M evolve
  * independently given q, k and the gates: every step below acts on each
@@ -93,20 +114,7 @@ static void recurrence_unit(const double* q, const double* k, const double* v,
         const double* qt = q + IDX_TOK(b, t, h, 0, T, H, Dk);
         const double* vv = v + IDX_TOK(b, t, h, c0, T, H, Dv);
 
-        /* S_{t-1}^T k_t, column by column */
-        for (int c = 0; c < nc; ++c) vt[c] = 0.0;
-        for (int i = 0; i < Dk; ++i)
-            for (int c = 0; c < nc; ++c) vt[c] += S[(size_t)i * nc + c] * kt[i];
-        for (int c = 0; c < nc; ++c) vt[c] = vv[c] - a * vt[c];
-
-        /* momentum, then memory (which reads the new momentum) */
-        for (int i = 0; i < Dk; ++i) {
-            for (int c = 0; c < nc; ++c) {
-                const size_t x = (size_t)i * nc + c;
-                M[x] = m * M[x] - e * kt[i] * vt[c];
-                S[x] = a * S[x] - s * M[x];
-            }
-        }
+        token_step(kt, vv, a, m, e, s, S, M, vt, Dk, nc);
 
         /* o_t = S_t^T q_t */
         for (int c = 0; c < nc; ++c) o[c] = 0.0;
@@ -242,22 +250,12 @@ static void backward_unit(const double* q, const double* k, const double* v,
             const size_t g = IDX_GATE(b, t, h, T, H);
             const double a = alpha[g], m = mu[g], e = eta[g], s = beta ? beta[g] : 1.0;
             const double* kt = k + IDX_TOK(b, t, h, 0, T, H, Dk);
-            const double* vv = v + IDX_TOK(b, t, h, c0, T, H, Dv);
-            const double* Sp = Ss + st * t;
-            const double* Mp = Ms + st * t;
             double* Sn = Ss + st * (t + 1);
             double* Mn = Ms + st * (t + 1);
-            double* vt = vts + (size_t)nc * t;
-            for (int c = 0; c < nc; ++c) vt[c] = 0.0;
-            for (int i = 0; i < Dk; ++i)
-                for (int c = 0; c < nc; ++c) vt[c] += Sp[(size_t)i * nc + c] * kt[i];
-            for (int c = 0; c < nc; ++c) vt[c] = vv[c] - a * vt[c];
-            for (int i = 0; i < Dk; ++i)
-                for (int c = 0; c < nc; ++c) {
-                    const size_t x = (size_t)i * nc + c;
-                    Mn[x] = m * Mp[x] - e * kt[i] * vt[c];
-                    Sn[x] = a * Sp[x] - s * Mn[x];
-                }
+            memcpy(Sn, Ss + st * t, sizeof(double) * st);
+            memcpy(Mn, Ms + st * t, sizeof(double) * st);
+            token_step(kt, v + IDX_TOK(b, t, h, c0, T, H, Dv), a, m, e, s, Sn, Mn,
+                       vts + (size_t)nc * t, Dk, nc);
         }
         /* backward, last token first */
         for (int i = 0; i < Dk; ++i)

@@ -28,14 +28,14 @@ MUTANTS = [
     ("memory decay dropped",
      "S[x] = a * S[x] - s * M[x];", "S[x] = S[x] - s * M[x];"),
     ("memory reads old momentum",
-     "                M[x] = m * M[x] - e * kt[i] * vt[c];\n"
-     "                S[x] = a * S[x] - s * M[x];",
-     "                S[x] = a * S[x] - s * M[x];\n"
-     "                M[x] = m * M[x] - e * kt[i] * vt[c];"),
+     "            M[x] = m * M[x] - e * kt[i] * vt[c];\n"
+     "            S[x] = a * S[x] - s * M[x];",
+     "            S[x] = a * S[x] - s * M[x];\n"
+     "            M[x] = m * M[x] - e * kt[i] * vt[c];"),
     ("read-out uses key",
      "o[c] += S[(size_t)i * nc + c] * qt[i];", "o[c] += S[(size_t)i * nc + c] * kt[i];"),
-    ("residual uses query",
-     "vt[c] += S[(size_t)i * nc + c] * kt[i];", "vt[c] += S[(size_t)i * nc + c] * qt[i];"),
+    ("residual reads the momentum",
+     "vt[c] += S[(size_t)i * nc + c] * kt[i];", "vt[c] += M[(size_t)i * nc + c] * kt[i];"),
     ("gates swapped",
      "const double a = alpha[g];\n        const double m = mu[g];",
      "const double a = mu[g];\n        const double m = alpha[g];"),
