@@ -20,6 +20,7 @@ The same JSON line carries:
   split_path    the same forward through mdn_chunk_fwd_prepare + mdn_chunk_fwd_scan;
   forward.from_logits  mdn_gates_from_logits, then the four-gate forward on its gates;
   forward       the whole step against both roofs;
+  backward      mdn_chunk_bwd on the same layer (all gradients), against the fp32 MFMA peak;
   decode        the recurrent decode step at 256 sequences x 16 heads, d 128
                 (GB/s of algorithmic state + token traffic);
   sweep         tokens/s at T x B = 16384 tokens per call for T = 2K .. 16K;
@@ -58,6 +59,13 @@ STATE_BYTES_HEAD = 2 * D * D * 4         # S_T and M_T written once per (b, h)
 DEC_BYTES_HEAD = 4 * D * D * 4 + 3 * D * 2 + D * 2 + 3 * 4   # S, M in+out; q k v o; gates
 DEC_BYTES_HEAD_GDN = 2 * D * D * 4 + 3 * D * 2 + D * 2 + 2 * 4   # mu = 0: S only; two gates
 BYTES_GATES = 4 * 4 + 4 * 4              # four fp32 logits in, four fp32 gates out
+# backward (mdn_chunk_bwd), dense products per token and head: prepare 4 C d; reverse scan
+# 12 d^2 + 4 C d; re-scan 8 d^2 + 2 C d; per-chunk gradients 12 d^2 + 16 C d
+FLOP_BWD = 32 * D * D + 30 * C * D
+# what it must read and write once: q, k, v, dO (bf16), three gates in, dq, dk, dv (fp32)
+# and three gate gradients out, plus S0, M0 read / dS0, dM0 written per (b, h) (zero here)
+BYTES_BWD = 4 * D * 2 + 3 * 4 + 3 * D * 4 + 3 * 4
+PEAK_FP32_MFMA = 157.3e12       # MI355X dense fp32 matrix
 GATE_TAU = (2048 / 16) ** 0.5            # the temperature sqrt(d_in / h) at d_in 2048, 16 heads
 
 # HBM traffic per launch from rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, KiB per dispatch,
@@ -137,6 +145,7 @@ def parse():
     p.add_argument("--decode-steps", type=int, default=64)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-backward", action="store_true")
     p.add_argument("--no-sweep", action="store_true")
     return p.parse_args()
 
@@ -281,6 +290,38 @@ def bench_forward(args, torch, si, mdn):
     return cfg, inp, step_ms, kernels, roofline, fwd, split
 
 
+def bench_backward(args, torch, si, mdn, cfg, inp):
+    """mdn_chunk_bwd on the headline layer with dO ~ N(0, 1) and no terminal
+    state gradients; every gradient (q, k, v, alpha, mu, eta) computed."""
+    bf, f32 = torch.bfloat16, torch.float32
+    cot = si.backward_cotangents(cfg, 12, terminal=False)
+    args_ = (up(inp["q"], bf), up(inp["k"], bf), up(inp["v"], bf), up(inp["alpha"], f32),
+             up(inp["mu"], f32), up(inp["eta"], f32), None, None, up(cot["dO"], bf))
+    del cot
+    B, T, H = cfg.B, cfg.T, cfg.H
+    ws = torch.empty(mdn.workspace_bytes_bwd(B, T, H, cfg.Dk, cfg.Dv, bf), dtype=torch.uint8,
+                     device="cuda")
+    fn = lambda: mdn.chunk_bwd(*args_, workspace=ws, state_grads=False)
+    settle(torch, [fn], args.settle)
+    for _ in range(max(1, args.warmup // 2)):
+        fn()
+    steps = max(1, args.steps // 5)
+    (_,), span = time_calls(torch, [fn], steps)
+    toh = B * T * H
+    us = span * 1e3
+    flop = FLOP_BWD * toh
+    tf = flop / (us * 1e-6) / 1e12
+    log(f"backward: {us:.1f} us/step ({tf:.1f} TFLOP/s dense fp32 work)")
+    return {"workload": f"mdn_chunk_bwd on {cfg.name}: dO ~ N(0, 1), all gradients, fp32 "
+                        "arithmetic (fp32 MFMA)",
+            "us_per_step": us, "tokens_per_s": B * T / (us * 1e-6), "steps_timed": steps,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP32_MFMA / 1e12,
+                         "unit": "TFLOP/s", "frac": flop / (us * 1e-6) / PEAK_FP32_MFMA,
+                         "traffic": None, "algorithmic_flop": flop,
+                         "algorithmic_bytes": BYTES_BWD * toh,
+                         "hbm_frac": BYTES_BWD * toh / (us * 1e-6) / PEAK_HBM_BPS}}
+
+
 def bench_decode(args, torch, si, mdn):
     cfg = si.CONFIGS[4]
     import dataclasses
@@ -406,6 +447,7 @@ def main():
         libbuild.build()
     mdn.load_library()
     cfg, inp, step_ms, kernels, roofline, fwd, split = bench_forward(args, torch, si, mdn)
+    backward = None if args.no_backward else bench_backward(args, torch, si, mdn, cfg, inp)
     decode = None if args.no_decode else bench_decode(args, torch, si, mdn)
     sweep = None if args.no_sweep else bench_sweep(args, torch, si, mdn)
     base = None if args.no_cpu_baseline else cpu_baseline(inp, cfg)
@@ -430,6 +472,7 @@ def main():
         "forward": fwd,
         "kernels": kernels,
         "split_path": split,
+        "backward": backward,
         "decode": decode,
         "sweep": sweep,
         "cpu_baseline": base,

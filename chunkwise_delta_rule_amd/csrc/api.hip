@@ -26,6 +26,14 @@ hipError_t launch_chunk_scan(const void* q, const void* k, const void* v, const 
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* alpha,
                          const float* mu, const float* eta, const float* beta, float* S, float* M,
                          void* o, int heads, int Dk, int Dv, bool bf16, hipStream_t stream);
+size_t chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, bool bf16);
+hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
+                            const float* mu, const float* eta, const float* beta, const float* S0,
+                            const float* M0, const void* dO, const float* dST, const float* dMT,
+                            float* dq, float* dk, float* dv, float* dalpha, float* dmu,
+                            float* deta, float* dbeta, float* dS0, float* dM0, int B, int T,
+                            int H, int Dk, int Dv, bool bf16, void* workspace, hipStream_t stream);
+hipError_t launch_state_copy(const float* src, float* dst, size_t count, hipStream_t stream);
 hipError_t launch_gates(const float* z_eta, const float* z_alpha, const float* z_beta,
                         const float* z_mu, size_t n, float tau, float s, float a, float b,
                         float log_mu_min, float* alpha, float* mu, float* eta, float* beta,
@@ -333,6 +341,83 @@ mdn_status mdn_gates_from_logits(const float* z_eta, const float* z_alpha, const
     const hipError_t err = mdn::launch_gates(z_eta, z_alpha, z_beta, z_mu, n, params.tau, params.s,
                                              params.a, params.b, params.log_mu_min, alpha, mu,
                                              eta, beta, stream);
+    return err == hipSuccess ? MDN_OK : MDN_ERR_HIP;
+}
+
+size_t mdn_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
+                                     mdn_dtype dt)
+{
+    if (B <= 0 || T <= 0 || H <= 0) return 0;
+    if (!head_dim_ok(Dk) || !head_dim_ok(Dv) || chunk != 64) return 0;
+    if (dt != MDN_F32 && dt != MDN_BF16) return 0;
+    size_t tmp;
+    if (!mul_ok((size_t)B, (size_t)T, (size_t)H, 1, &tmp)) return 0;
+    return mdn::chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, dt == MDN_BF16);
+}
+
+mdn_status mdn_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
+                         const float* mu, const float* eta, const float* beta, const float* S0,
+                         const float* M0, const void* dO, const float* dS_T, const float* dM_T,
+                         float* dq, float* dk, float* dv, float* dalpha, float* dmu, float* deta,
+                         float* dbeta, float* dS0, float* dM0, int B, int T, int H, int Dk,
+                         int Dv, int chunk, mdn_dtype dt, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream)
+{
+    if (B < 0 || T < 0 || H < 0) return MDN_ERR_SHAPE;
+    if (!head_dim_ok(Dk) || !head_dim_ok(Dv) || chunk != 64) return MDN_ERR_UNSUPPORTED;
+    if (dt != MDN_F32 && dt != MDN_BF16) return MDN_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0) return MDN_OK;
+    const size_t esz = dt == MDN_BF16 ? 2 : 4;
+    size_t nqk, nv, ngate, nstate;
+    if (!mul_ok((size_t)B, (size_t)T, (size_t)H, (size_t)Dk, &nqk) ||
+        !mul_ok((size_t)B, (size_t)T, (size_t)H, (size_t)Dv, &nv) ||
+        !mul_ok((size_t)B, (size_t)T, (size_t)H, 1, &ngate) ||
+        !mul_ok((size_t)B, (size_t)H, (size_t)Dk, (size_t)Dv, &nstate))
+        return MDN_ERR_SHAPE;
+    if ((size_t)B * H * (((size_t)T + 63) / 64) > 0xffffffffu) return MDN_ERR_SHAPE;
+    const bool tok = T > 0;
+    if (tok && (!q || !k || !v || !alpha || !eta || !dO || !dq || !dk || !dv || !dalpha || !deta))
+        return MDN_ERR_NULL;
+    const void* ptrs[] = {q, k, v, alpha, mu, eta, beta, S0, M0, dO, dS_T, dM_T, dq, dk, dv,
+                          dalpha, dmu, deta, dbeta, dS0, dM0, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MDN_ERR_ALIGN;
+    const size_t need = tok ? mdn::chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, dt == MDN_BF16) : 0;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return MDN_ERR_WORKSPACE;
+
+    const size_t nt = tok ? 1 : 0;
+    // gradients of absent gates are not written
+    float* dmu_w = mu ? dmu : nullptr;
+    float* dbeta_w = beta ? dbeta : nullptr;
+    const Span inputs[] = {span(q, nt * nqk * esz),     span(k, nt * nqk * esz),
+                           span(v, nt * nv * esz),      span(alpha, nt * ngate * 4),
+                           span(mu, nt * ngate * 4),    span(eta, nt * ngate * 4),
+                           span(beta, nt * ngate * 4),  span(S0, nstate * 4),
+                           span(M0, nstate * 4),        span(dO, nt * nv * esz),
+                           span(dS_T, nstate * 4),      span(dM_T, nstate * 4)};
+    const Span outputs[] = {span(dq, nt * nqk * 4),        span(dk, nt * nqk * 4),
+                            span(dv, nt * nv * 4),         span(dalpha, nt * ngate * 4),
+                            span(dmu_w, nt * ngate * 4),   span(deta, nt * ngate * 4),
+                            span(dbeta_w, nt * ngate * 4), span(dS0, nstate * 4),
+                            span(dM0, nstate * 4),         span(workspace, need)};
+    constexpr int NO = sizeof(outputs) / sizeof(outputs[0]);
+    for (int i = 0; i < NO; ++i) {
+        for (const Span& x : inputs)
+            if (overlap(outputs[i], x)) return MDN_ERR_ALIAS;
+        for (int j = i + 1; j < NO; ++j)
+            if (overlap(outputs[i], outputs[j])) return MDN_ERR_ALIAS;
+    }
+
+    if (!tok) {
+        // no tokens: the state gradients pass straight through
+        hipError_t err = hipSuccess;
+        if (dS0) err = mdn::launch_state_copy(dS_T, dS0, nstate, stream);
+        if (err == hipSuccess && dM0) err = mdn::launch_state_copy(dM_T, dM0, nstate, stream);
+        return err == hipSuccess ? MDN_OK : MDN_ERR_HIP;
+    }
+    const hipError_t err = mdn::launch_chunk_bwd(
+        q, k, v, alpha, mu, eta, beta, S0, M0, dO, dS_T, dM_T, dq, dk, dv, dalpha, dmu_w, deta,
+        dbeta_w, dS0, dM0, B, T, H, Dk, Dv, dt == MDN_BF16, workspace, stream);
     return err == hipSuccess ? MDN_OK : MDN_ERR_HIP;
 }
 

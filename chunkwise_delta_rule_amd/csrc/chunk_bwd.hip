@@ -1,0 +1,1091 @@
+// chunk_bwd.hip -- chunkwise MDN backward pass on gfx950.
+//
+// The pages ("MDN: Parallelizing Stepwise Momentum for Delta Linear
+// Attention" (slides), frame "The implementation trades saved residuals for
+// throughput"; the reading notes on the same paper, Sec. 2.6) give the
+// backward pass's strategy -- keep the residuals Vt, rebuild the states from
+// them, store no full state pair per chunk between the passes -- but no
+// gradient formulas.  The formulas below are the chain rule applied to the
+// chunk equations of the forward (chunk_fwd.hip), per chunk of C = 64 tokens
+// with entry state (S0, M0), exit-state gradients (dS', dM') and the same
+// coefficients (abar, b, ab1_i = alpha_i b_{i-1}, Gamma, m, ws = eta o
+// Gamma_{n,:}, wm = eta o m_{n,:}; P = Diag(alpha) K, Khat = Diag(eta) K):
+//
+//   dVt  = A^T dO + Diag(ws) K dS' - Diag(wm) K dM'
+//   dR   = T^T dVt                                  (= dV)
+//   dS0  = abar_n dS' + Q^T Diag(abar) dO - K^T Diag(abar) dR
+//   dM0  = mubar_n dM' - b_n dS' - Q^T Diag(b) dO + K^T Diag(ab1) dR
+//   dA   = tril(dO Vt^T),  dL = -stril(dR Vt^T)
+//   dQ   = Diag(abar) dO S0^T - Diag(b) dO M0^T + (dA o Gamma) Khat
+//   dKhat = (dA o Gamma)^T Q + (dL o Gamma^-)^T P,  dP = (dL o Gamma^-) Khat
+//   dK   = Diag(eta) dKhat + Diag(alpha) dP - Diag(abar) dR S0^T + Diag(ab1) dR M0^T
+//          + Diag(ws) Vt dS'^T - Diag(wm) Vt dM'^T
+// and, for the gates, the gradients of the coefficients
+//   dabar_i = q_i.(dO S0^T)_i - k_i.(dR S0^T)_i,  db_i = -q_i.(dO M0^T)_i,
+//   d(ab1)_i = k_i.(dR M0^T)_i,  plus <dS', S0>, -<dS', M0>, <dM', M0> on the
+//   last row's abar_n, b_n, mubar_n;
+//   dGamma = dA o (Q Khat^T) + (dL o (P Khat^T)) shifted up one row, plus
+//   eta_j k_j.(Vt dS'^T)_j on the last row;  dm_{n,j} = -eta_j k_j.(Vt dM'^T)_j
+// carried back through the coefficient recursions (abar_i = alpha_i abar_{i-1},
+// mubar_i = mu_i mubar_{i-1}, b_i = alpha_i b_{i-1} + beta_i mubar_i,
+// gamma_{i,j} = alpha_i gamma_{i-1,j} + beta_i m_{i,j}, m_{i,j} = mu_i m_{i-1,j})
+// and the direct uses of eta (Khat, ws, wm) and alpha (P, ab1).
+//
+// Kernels, in launch order (after chunk_prep_kernel has written T, A and the
+// coefficient rows of every chunk):
+//   bwd_scan_kernel     one workgroup per (b, h, 64 value columns), chunks last
+//                       to first: dVt, dR (written as dv), the state gradients
+//                       carried back, and each chunk's exit-state gradients
+//                       stored for the last kernel.
+//   bwd_rescan_kernel   the same grid, chunks first to last: the forward's
+//                       R, Vt = T R and state update again, storing each
+//                       chunk's entry state and Vt.
+//   bwd_grad_kernel     one workgroup per chunk, all columns: dq, dk and the
+//                       gate gradients.
+// All arithmetic is fp32 (v_mfma_f32_16x16x4_f32 and VALU); bf16 inputs are
+// widened when they are staged into LDS.
+#include <hip/hip_runtime.h>
+
+#include "chunk_common.hpp"
+#include "mfma.hpp"
+
+namespace mdn {
+
+hipError_t launch_chunk_prepare(const void* q, const void* k, const float* alpha, const float* mu,
+                                const float* eta, const float* beta, int B, int T, int H, int Dk,
+                                bool bf16, void* workspace, hipStream_t stream);
+
+namespace {
+
+using MF = Mma<float>;
+
+__device__ __forceinline__ float ldf(const float* p) { return *p; }
+__device__ __forceinline__ float ldf(const __bf16* p) { return static_cast<float>(*p); }
+
+// A C x D tile of a row-major array (row stride in elements) on its way to
+// fp32 LDS with row stride LD: fetch() issues every 16-byte load of this
+// thread into registers (rows >= n read as zero), commit() widens and stores
+// them, so that the loads of several tiles (or of the next chunk) are in
+// flight together.
+template <typename E, int D, int LD>
+struct Tile {
+    static constexpr int VE = 16 / sizeof(E);    // elements per load
+    static constexpr int VPR = D / VE;           // loads per row
+    static constexpr int NV = CH * VPR / NT;     // loads per thread
+    static_assert(CH * VPR % NT == 0, "tile must split evenly over the workgroup");
+    uint4 buf[NV];
+    __device__ __forceinline__ void fetch(const E* __restrict__ src, size_t stride, int n, int tid)
+    {
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int idx = tid + u * NT;
+            const int row = idx / VPR;
+            const int cv = idx % VPR;
+            buf[u] = row < n ? *reinterpret_cast<const uint4*>(src + (size_t)row * stride + cv * VE)
+                             : uint4{0u, 0u, 0u, 0u};
+        }
+    }
+    __device__ __forceinline__ void commit(float* dst, int tid) const
+    {
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int idx = tid + u * NT;
+            float* d = dst + (idx / VPR) * LD + (idx % VPR) * VE;
+            if constexpr (sizeof(E) == 2) {
+                const unsigned w[4] = {buf[u].x, buf[u].y, buf[u].z, buf[u].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    d[2 * e] = __uint_as_float(w[e] << 16);
+                    d[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+                }
+            } else {
+                d[0] = __uint_as_float(buf[u].x);
+                d[1] = __uint_as_float(buf[u].y);
+                d[2] = __uint_as_float(buf[u].z);
+                d[3] = __uint_as_float(buf[u].w);
+            }
+        }
+    }
+};
+
+template <int D, int LD, typename E>
+__device__ __forceinline__ void stage(float* dst, const E* __restrict__ src, size_t stride, int n,
+                                      int tid)
+{
+    Tile<E, D, LD> t;
+    t.fetch(src, stride, n, tid);
+    t.commit(dst, tid);
+}
+
+// sum over the 16 lanes of a lane group (lanes 16 g .. 16 g + 15)
+__device__ __forceinline__ float sum16(float x)
+{
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    return x;
+}
+
+// ---------------------------------------------------------------------------
+// Reverse scan.  Wavefront w keeps 16 columns of dS and dM in fp32 MFMA
+// accumulators (rows 16 rt + 4 lg + r, column wcol + l16), as the forward
+// scan keeps S and M.
+// ---------------------------------------------------------------------------
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(NT) void bwd_scan_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ dO,
+    const E* __restrict__ Tw, const E* __restrict__ Aw, const float* __restrict__ Vw,
+    const float* dST, const float* dMT, float* __restrict__ Hd, float* __restrict__ dv,
+    float* dS0, float* dM0, int T, int H, int NC)
+{
+    constexpr int TV = 64;
+    constexpr int NTILE = DV / TV;
+    constexpr int RT = DK / 16;
+    constexpr int LDK = DK + 1;
+    constexpr int LDV = TV + 1;
+    constexpr int LDC = CH + 1;
+    __shared__ float Qs[CH * LDK];
+    __shared__ float Ks[CH * LDK];
+    __shared__ float Gs[CH * LDV];   // dO, this workgroup's columns
+    __shared__ float Ts[CH * LDC];
+    __shared__ float As[CH * LDC];
+    __shared__ float vecs[6 * CH];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l16 = lane & 15;
+    const int lg = lane >> 4;
+    const int tile = (int)(blockIdx.x % NTILE);
+    const int bh = (int)(blockIdx.x / NTILE);
+    const int h = bh % H;
+    const int b = bh / H;
+    const int lcol = 16 * wave + l16;        // column inside the workgroup's 64
+    const int wcol = tile * TV + 16 * wave;  // first column of this wavefront
+
+    f32x4 Sa[RT], Ma[RT];
+    const size_t sbase = (size_t)bh * DK * DV;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const size_t x = sbase + (size_t)(16 * rt + 4 * lg + r) * DV + wcol + l16;
+            Sa[rt][r] = dST ? dST[x] : 0.f;
+            Ma[rt][r] = dMT ? dMT[x] : 0.f;
+        }
+
+    Tile<E, DK, LDK> pq, pk;
+    Tile<E, TV, LDV> pg;
+    Tile<E, CH, LDC> pt, pa;
+    float pvec[2];
+    auto fetch = [&](int c) {
+        const int t0 = c * CH;
+        const int n = min(CH, T - t0);
+        const size_t tok0 = ((size_t)b * T + t0) * H + h;
+        const size_t chn = (size_t)bh * NC + c;
+        pq.fetch(q + tok0 * DK, (size_t)H * DK, n, tid);
+        pk.fetch(k + tok0 * DK, (size_t)H * DK, n, tid);
+        pg.fetch(dO + tok0 * DV + tile * TV, (size_t)H * DV, n, tid);
+        pt.fetch(Tw + chn * CH * CH, CH, CH, tid);
+        pa.fetch(Aw + chn * CH * CH, CH, CH, tid);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            pvec[u] = tid + u * NT < 6 * CH ? Vw[chn * NVEC * CH + tid + u * NT] : 0.f;
+    };
+    fetch(NC - 1);
+
+    for (int c = NC - 1; c >= 0; --c) {
+        const int t0 = c * CH;
+        const int n = min(CH, T - t0);
+        const size_t tok0 = ((size_t)b * T + t0) * H + h;
+        const size_t chn = (size_t)bh * NC + c;
+
+        __syncthreads();
+        pq.commit(Qs, tid);
+        pk.commit(Ks, tid);
+        pg.commit(Gs, tid);
+        pt.commit(Ts, tid);
+        pa.commit(As, tid);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            if (tid + u * NT < 6 * CH) vecs[tid + u * NT] = pvec[u];
+        __syncthreads();
+        if (c > 0) fetch(c - 1);
+
+        // the exit-state gradients of this chunk, for bwd_grad_kernel
+        {
+            float* hd = Hd + chn * 2 * DK * DV;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const size_t x = (size_t)(16 * rt + 4 * lg + r) * DV + wcol + l16;
+                    hd[x] = Sa[rt][r];
+                    hd[(size_t)DK * DV + x] = Ma[rt][r];
+                }
+        }
+
+        // K dS', K dM' (rows i, this wavefront's columns)
+        f32x4 xs[4], xm[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) xs[ct] = xm[ct] = zero4();
+#pragma unroll
+        for (int s = 0; s < DK / 4; ++s) {
+            const float bS = MF::from_acc(Sa, s);
+            const float bM = MF::from_acc(Ma, s);
+            const int kd = MF::perm_row(s, lg, 0);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                const float aK = Ks[(16 * ct + l16) * LDK + kd];
+                xs[ct] = MF::mma(aK, bS, xs[ct]);
+                xm[ct] = MF::mma(aK, bM, xm[ct]);
+            }
+        }
+
+        // dVt = A^T dO + Diag(ws) K dS' - Diag(wm) K dM'
+        f32x4 dVt[4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * it + 4 * lg + r;
+                dVt[it][r] = vecs[V_WS * CH + i] * xs[it][r] - vecs[V_WM * CH + i] * xm[it][r];
+            }
+#pragma unroll 4
+        for (int s = 0; s < CH / 4; ++s) {
+            const int kr = 4 * s + lg;
+            const float bO = Gs[kr * LDV + lcol];
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                dVt[it] = MF::mma(As[kr * LDC + 16 * it + l16], bO, dVt[it]);
+        }
+
+        // dR = T^T dVt, written as dv
+        f32x4 dR[4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) dR[it] = zero4();
+#pragma unroll
+        for (int s = 0; s < CH / 4; ++s) {
+            const float bV = MF::from_acc(dVt, s);
+            const int kr = MF::perm_row(s, lg, 0);
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                dR[it] = MF::mma(Ts[kr * LDC + 16 * it + l16], bV, dR[it]);
+        }
+        {
+            float* dvb = dv + tok0 * DV + wcol + l16;
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * it + 4 * lg + r;
+                    if (i < n) dvb[(size_t)i * H * DV] = dR[it][r];
+                }
+        }
+
+        // carry back: dS <- abar_n dS' + Q^T Diag(abar) dO - K^T Diag(abar) dR,
+        //             dM <- mubar_n dM' - b_n dS' - Q^T Diag(b) dO + K^T Diag(ab1) dR
+        const float abn = vecs[V_SCAL * CH + 0];
+        const float bn = vecs[V_SCAL * CH + 1];
+        const float mbn = vecs[V_SCAL * CH + 2];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const f32x4 so = Sa[rt];
+            Sa[rt] = abn * so;
+            Ma[rt] = mbn * Ma[rt] - bn * so;
+        }
+#pragma unroll 4
+        for (int s = 0; s < CH / 4; ++s) {
+            const int kr = 4 * s + lg;
+            const float g = Gs[kr * LDV + lcol];
+            const float bS = vecs[V_ABAR * CH + kr] * g;
+            const float bM = -vecs[V_B * CH + kr] * g;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const float aQ = Qs[kr * LDK + 16 * rt + l16];
+                Sa[rt] = MF::mma(aQ, bS, Sa[rt]);
+                Ma[rt] = MF::mma(aQ, bM, Ma[rt]);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < CH / 4; ++s) {
+            const float bS = MF::from_acc_scaled(dR, s, lg, vecs + V_ABAR * CH, -1.f);
+            const float bM = MF::from_acc_scaled(dR, s, lg, vecs + V_AB1 * CH, 1.f);
+            const int kr = MF::perm_row(s, lg, 0);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const float aK = Ks[kr * LDK + 16 * rt + l16];
+                Sa[rt] = MF::mma(aK, bS, Sa[rt]);
+                Ma[rt] = MF::mma(aK, bM, Ma[rt]);
+            }
+        }
+    }
+
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const size_t x = sbase + (size_t)(16 * rt + 4 * lg + r) * DV + wcol + l16;
+            if (dS0) dS0[x] = Sa[rt][r];
+            if (dM0) dM0[x] = Ma[rt][r];
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Forward re-scan: the chunk-entry states and Vt of every chunk.
+// ---------------------------------------------------------------------------
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(NT) void bwd_rescan_kernel(
+    const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ Tw,
+    const float* __restrict__ Vw, const float* S0, const float* M0, float* __restrict__ Hs,
+    float* __restrict__ Vts, int T, int H, int NC)
+{
+    constexpr int TV = 64;
+    constexpr int NTILE = DV / TV;
+    constexpr int RT = DK / 16;
+    constexpr int LDK = DK + 1;
+    constexpr int LDV = TV + 1;
+    constexpr int LDC = CH + 1;
+    __shared__ float Ks[CH * LDK];
+    __shared__ float Vs[CH * LDV];
+    __shared__ float Ts[CH * LDC];
+    __shared__ float vecs[6 * CH];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l16 = lane & 15;
+    const int lg = lane >> 4;
+    const int tile = (int)(blockIdx.x % NTILE);
+    const int bh = (int)(blockIdx.x / NTILE);
+    const int h = bh % H;
+    const int b = bh / H;
+    const int lcol = 16 * wave + l16;
+    const int wcol = tile * TV + 16 * wave;
+
+    f32x4 Sa[RT], Ma[RT];
+    const size_t sbase = (size_t)bh * DK * DV;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const size_t x = sbase + (size_t)(16 * rt + 4 * lg + r) * DV + wcol + l16;
+            Sa[rt][r] = S0 ? S0[x] : 0.f;
+            Ma[rt][r] = M0 ? M0[x] : 0.f;
+        }
+
+    Tile<E, DK, LDK> pk;
+    Tile<E, TV, LDV> pv;
+    Tile<E, CH, LDC> pt;
+    float pvec[2];
+    auto fetch = [&](int c) {
+        const int t0 = c * CH;
+        const int n = min(CH, T - t0);
+        const size_t tok0 = ((size_t)b * T + t0) * H + h;
+        const size_t chn = (size_t)bh * NC + c;
+        pk.fetch(k + tok0 * DK, (size_t)H * DK, n, tid);
+        pv.fetch(v + tok0 * DV + tile * TV, (size_t)H * DV, n, tid);
+        pt.fetch(Tw + chn * CH * CH, CH, CH, tid);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            pvec[u] = tid + u * NT < 6 * CH ? Vw[chn * NVEC * CH + tid + u * NT] : 0.f;
+    };
+    fetch(0);
+
+    for (int c = 0; c < NC; ++c) {
+        const int t0 = c * CH;
+        const int n = min(CH, T - t0);
+        const size_t tok0 = ((size_t)b * T + t0) * H + h;
+        const size_t chn = (size_t)bh * NC + c;
+        (void)tok0;
+
+        __syncthreads();
+        pk.commit(Ks, tid);
+        pv.commit(Vs, tid);
+        pt.commit(Ts, tid);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            if (tid + u * NT < 6 * CH) vecs[tid + u * NT] = pvec[u];
+        __syncthreads();
+        if (c + 1 < NC) fetch(c + 1);
+
+        {
+            float* hs = Hs + chn * 2 * DK * DV;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const size_t x = (size_t)(16 * rt + 4 * lg + r) * DV + wcol + l16;
+                    hs[x] = Sa[rt][r];
+                    hs[(size_t)DK * DV + x] = Ma[rt][r];
+                }
+        }
+
+        f32x4 xs[4], xm[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) xs[ct] = xm[ct] = zero4();
+#pragma unroll
+        for (int s = 0; s < DK / 4; ++s) {
+            const float bS = MF::from_acc(Sa, s);
+            const float bM = MF::from_acc(Ma, s);
+            const int kd = MF::perm_row(s, lg, 0);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                const float aK = Ks[(16 * ct + l16) * LDK + kd];
+                xs[ct] = MF::mma(aK, bS, xs[ct]);
+                xm[ct] = MF::mma(aK, bM, xm[ct]);
+            }
+        }
+        f32x4 R[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ct + 4 * lg + r;
+                R[ct][r] = Vs[i * LDV + lcol] - vecs[V_ABAR * CH + i] * xs[ct][r] +
+                           vecs[V_AB1 * CH + i] * xm[ct][r];
+            }
+        f32x4 Vt[4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) Vt[it] = zero4();
+#pragma unroll
+        for (int s = 0; s < CH / 4; ++s) {
+            const float bR = MF::from_acc(R, s);
+            const int kr = MF::perm_row(s, lg, 0);
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                Vt[it] = MF::mma(Ts[(16 * it + l16) * LDC + kr], bR, Vt[it]);
+        }
+        {
+            float* vb = Vts + chn * CH * DV + wcol + l16;
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vb[(size_t)(16 * it + 4 * lg + r) * DV] = Vt[it][r];
+        }
+
+        const float abn = vecs[V_SCAL * CH + 0];
+        const float bn = vecs[V_SCAL * CH + 1];
+        const float mbn = vecs[V_SCAL * CH + 2];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            Sa[rt] = abn * Sa[rt] - bn * Ma[rt];
+            Ma[rt] = mbn * Ma[rt];
+        }
+#pragma unroll
+        for (int s = 0; s < CH / 4; ++s) {
+            const float bS = MF::from_acc_scaled(Vt, s, lg, vecs + V_WS * CH, 1.f);
+            const float bM = MF::from_acc_scaled(Vt, s, lg, vecs + V_WM * CH, -1.f);
+            const int kr = MF::perm_row(s, lg, 0);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const float aK = Ks[kr * LDK + 16 * rt + l16];
+                Sa[rt] = MF::mma(aK, bS, Sa[rt]);
+                Ma[rt] = MF::mma(aK, bM, Ma[rt]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-chunk gradients: one workgroup per (b, h, chunk), all columns.
+//
+// C x DK results (dq, dk and the state products) are split over the four
+// wavefronts by column tiles: wavefront w owns d-tiles w * DT .. w * DT + DT - 1
+// (DT = DK / 64) and all four row tiles.  C x C results: wavefront w owns row
+// tile w and all four column tiles.
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+struct GradSmem {
+    static constexpr int LDK = DK + 1;
+    static constexpr int LDV = DV + 1;
+    static constexpr int LD = LDK > LDV ? LDK : LDV;
+    static constexpr int SLOT = CH * LD;     // floats of one C x D tile
+    static constexpr int LDC = CH + 1;
+    static constexpr int CM = CH * LDC;      // floats of one C x C matrix
+    static constexpr int NV = 24;            // vectors of CH floats
+    static constexpr int FLOATS = 3 * SLOT + 3 * CM + NV * CH + 8;
+};
+
+// vector rows of GradSmem
+constexpr int G_A = 0, G_M = 1, G_E = 2, G_S = 3;          // gates alpha, mu, eta, beta
+constexpr int G_AB = 4, G_MB = 5, G_B = 6;                   // abar, mubar, b
+constexpr int G_RX1 = 7, G_RX2 = 8, G_RY1 = 9, G_RY2 = 10;   // row dots
+constexpr int G_RZ1 = 11, G_RZ2 = 12, G_RKH = 13, G_RP = 14;
+constexpr int G_DA = 15, G_DM = 16, G_DE = 17, G_DS = 18;    // gate gradients
+constexpr int G_DAB = 19, G_DMB = 20, G_DB = 21;             // coefficient gradients
+constexpr int G_RED = 22;                                    // 2 rows: reduction scratch
+
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(NT) void bwd_grad_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ dO,
+    const float* __restrict__ dv, const float* __restrict__ Vts, const float* __restrict__ Hs,
+    const float* __restrict__ Hd, const float* __restrict__ alpha, const float* __restrict__ mu,
+    const float* __restrict__ eta, const float* __restrict__ beta, float* __restrict__ dq,
+    float* __restrict__ dk, float* __restrict__ dalpha, float* __restrict__ dmu,
+    float* __restrict__ deta, float* __restrict__ dbeta, int T, int H, int NC)
+{
+    using SM = GradSmem<DK, DV>;
+    constexpr int LD = SM::LD;
+    constexpr int LDC = SM::LDC;
+    constexpr int DT = DK / 64;   // d-tiles per wavefront
+    __shared__ float smem[SM::FLOATS];
+    float* slot0 = smem;
+    float* slot1 = smem + SM::SLOT;
+    float* slot2 = smem + 2 * SM::SLOT;
+    float* Gm = smem + 3 * SM::SLOT;     // Gamma
+    float* Cm1 = Gm + SM::CM;
+    float* Cm2 = Cm1 + SM::CM;
+    float* vec = Cm2 + SM::CM;
+    float* scal = vec + SM::NV * CH;     // 3 state inner products
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l16 = lane & 15;
+    const int lg = lane >> 4;
+    const int c = (int)(blockIdx.x % NC);
+    const int bh = (int)(blockIdx.x / NC);
+    const int h = bh % H;
+    const int b = bh / H;
+    const int t0 = c * CH;
+    const int n = min(CH, T - t0);
+    const size_t tok0 = ((size_t)b * T + t0) * H + h;
+    const size_t chn = (size_t)bh * NC + c;
+    const float* S0 = Hs + chn * 2 * DK * DV;
+    const float* M0 = S0 + DK * DV;
+    const float* dS = Hd + chn * 2 * DK * DV;
+    const float* dM = dS + DK * DV;
+    auto V = [&](int row) { return vec + row * CH; };
+
+    // ---- gates, coefficient vectors, Gamma ----------------------------------
+    for (int i = tid; i < CH; i += NT) {
+        const bool in = i < n;
+        const size_t g = tok0 + (size_t)i * H;
+        V(G_A)[i] = in ? alpha[g] : 1.f;
+        V(G_M)[i] = in && mu ? mu[g] : 0.f;
+        V(G_E)[i] = in ? eta[g] : 0.f;
+        V(G_S)[i] = in ? (beta ? beta[g] : 1.f) : 0.f;
+    }
+    for (int i = tid; i < (SM::NV - G_RX1) * CH; i += NT) vec[G_RX1 * CH + i] = 0.f;
+    __syncthreads();
+    if (tid == 0) {
+        float ab = 1.f, mb = 1.f, bp = 0.f;
+        for (int i = 0; i < CH; ++i) {
+            ab *= V(G_A)[i];
+            mb *= V(G_M)[i];
+            bp = V(G_A)[i] * bp + V(G_S)[i] * mb;
+            V(G_AB)[i] = ab;
+            V(G_MB)[i] = mb;
+            V(G_B)[i] = bp;
+        }
+    }
+    // Gamma by columns (thread j < CH): rows < j are zero; m lives in Cm1 for now
+    if (tid < CH) {
+        const int j = tid;
+        float g = 0.f, m = 1.f;
+        for (int i = 0; i < CH; ++i) {
+            if (i == j) {
+                g = V(G_S)[j];
+                m = 1.f;
+            } else if (i > j) {
+                m = V(G_M)[i] * m;
+                g = V(G_A)[i] * g + V(G_S)[i] * m;
+            }
+            Gm[i * LDC + j] = i >= j ? g : 0.f;
+            Cm1[i * LDC + j] = i >= j ? m : 0.f;
+        }
+    }
+    __syncthreads();
+    // last-row weights ws_j = eta_j gamma_{n-1,j}, wm_j = eta_j m_{n-1,j}
+    // (kept in the reduction rows until the state products are done)
+    float* ws = V(G_RED);
+    float* wm = V(G_RED + 1);
+    for (int j = tid; j < CH; j += NT) {
+        ws[j] = V(G_E)[j] * Gm[(n - 1) * LDC + j];
+        wm[j] = V(G_E)[j] * Cm1[(n - 1) * LDC + j];
+    }
+    // the three state inner products (each thread a strided share, then a
+    // fixed-order reduction over the four wavefronts)
+    {
+        float a0 = 0.f, a1 = 0.f, a2 = 0.f;
+        for (int x = tid; x < DK * DV; x += NT) {
+            const float s0 = S0[x], m0 = M0[x], ds = dS[x];
+            a0 += ds * s0;
+            a1 += ds * m0;
+            a2 += dM[x] * m0;
+        }
+        for (int o = 32; o >= 1; o >>= 1) {
+            a0 += __shfl_xor(a0, o);
+            a1 += __shfl_xor(a1, o);
+            a2 += __shfl_xor(a2, o);
+        }
+        __shared__ float part[3][4];
+        if (lane == 0) {
+            part[0][wave] = a0;
+            part[1][wave] = a1;
+            part[2][wave] = a2;
+        }
+        __syncthreads();
+        if (tid < 3) scal[tid] = (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]);
+    }
+
+    // ---- state products ------------------------------------------------------
+    // For a C x DV row operand X in LDS and a DK x DV state St in HBM, the
+    // product X St^T (C x DK): this wavefront's tiles, k over the DV columns
+    // in the fp32 k-permuted order, 4 state values per 16-byte load.
+    auto state_product = [&](const float* X, const float* St, f32x4 (*acc)[DT]) {
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[it][dt] = zero4();
+        // this wavefront's rows of the state, all DV columns, loaded at once
+        float4 sva[DV / 16][DT];
+#pragma unroll
+        for (int kb = 0; kb < DV / 16; ++kb)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int d = 16 * (wave * DT + dt) + l16;
+                sva[kb][dt] =
+                    *reinterpret_cast<const float4*>(St + (size_t)d * DV + 16 * kb + 4 * lg);
+            }
+#pragma unroll
+        for (int kb = 0; kb < DV / 16; ++kb) {
+            const float4* sv = sva[kb];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int kc = 16 * kb + 4 * lg + e;
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const float a = X[(16 * it + l16) * LD + kc];
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) {
+                        const float bv = e == 0 ? sv[dt].x : e == 1 ? sv[dt].y
+                                       : e == 2 ? sv[dt].z : sv[dt].w;
+                        acc[it][dt] = MF::mma(a, bv, acc[it][dt]);
+                    }
+                }
+            }
+        }
+    };
+    // row dot of a C x DK accumulator set with a C x DK LDS operand Y: adds
+    // this wavefront's share into red[wave][i]; the caller sums the four
+    float* red = Cm2;   // [4][CH] scratch (Cm2 is free until the C x C phase)
+    auto row_dot = [&](const f32x4 (*acc)[DT], const float* Y, float* out_row) {
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * it + 4 * lg + r;
+                float p = 0.f;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+                    p += acc[it][dt][r] * Y[i * LD + 16 * (wave * DT + dt) + l16];
+                p = sum16(p);
+                if (l16 == 0) red[wave * CH + i] = p;
+            }
+        __syncthreads();
+        for (int i = tid; i < CH; i += NT)
+            out_row[i] = (red[i] + red[CH + i]) + (red[2 * CH + i] + red[3 * CH + i]);
+        __syncthreads();
+    };
+
+    f32x4 dQa[4][DT], dKa[4][DT], P1[4][DT], P2[4][DT];
+    f32x4 cA[4], cL[4], cK[4];   // C x C tiles: dA, dL, K K^T (row tile = wave)
+
+    // phase 1: slot0 = Vt, slot1 = dO, slot2 = Q
+    {
+        Tile<float, DV, LD> t0_;
+        Tile<E, DV, LD> t1_;
+        Tile<E, DK, LD> t2_;
+        t0_.fetch(Vts + chn * CH * DV, DV, n, tid);
+        t1_.fetch(dO + tok0 * DV, (size_t)H * DV, n, tid);
+        t2_.fetch(q + tok0 * DK, (size_t)H * DK, n, tid);
+        __syncthreads();
+        t0_.commit(slot0, tid);
+        t1_.commit(slot1, tid);
+        t2_.commit(slot2, tid);
+    }
+    __syncthreads();
+    // dA = dO Vt^T (lower triangle with the diagonal kept below)
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) cA[jt] = zero4();
+    for (int kc = lg; kc < DV; kc += 4) {
+        const float a = slot1[(16 * wave + l16) * LD + kc];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) cA[jt] = MF::mma(a, slot0[(16 * jt + l16) * LD + kc], cA[jt]);
+    }
+    state_product(slot1, S0, P1);   // dO S0^T
+    state_product(slot1, M0, P2);   // dO M0^T
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * it + 4 * lg + r;
+                dQa[it][dt][r] = V(G_AB)[i] * P1[it][dt][r] - V(G_B)[i] * P2[it][dt][r];
+            }
+    row_dot(P1, slot2, V(G_RX1));
+    row_dot(P2, slot2, V(G_RX2));
+
+    // phase 2: slot1 = dR, slot2 = K (Vt stays in slot0)
+    {
+        Tile<float, DV, LD> t1_;
+        Tile<E, DK, LD> t2_;
+        t1_.fetch(dv + tok0 * DV, (size_t)H * DV, n, tid);
+        t2_.fetch(k + tok0 * DK, (size_t)H * DK, n, tid);
+        t1_.commit(slot1, tid);
+        t2_.commit(slot2, tid);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) cL[jt] = cK[jt] = zero4();
+    for (int kc = lg; kc < DV; kc += 4) {
+        const float a = slot1[(16 * wave + l16) * LD + kc];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) cL[jt] = MF::mma(-a, slot0[(16 * jt + l16) * LD + kc], cL[jt]);
+    }
+    for (int kd = lg; kd < DK; kd += 4) {
+        const float a = slot2[(16 * wave + l16) * LD + kd];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) cK[jt] = MF::mma(a, slot2[(16 * jt + l16) * LD + kd], cK[jt]);
+    }
+    state_product(slot1, S0, P1);   // dR S0^T
+    state_product(slot1, M0, P2);   // dR M0^T
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * it + 4 * lg + r;
+                const float ab1 = i > 0 ? V(G_A)[i] * V(G_B)[i - 1] : 0.f;
+                dKa[it][dt][r] = -V(G_AB)[i] * P1[it][dt][r] + ab1 * P2[it][dt][r];
+            }
+    row_dot(P1, slot2, V(G_RY1));
+    row_dot(P2, slot2, V(G_RY2));
+    state_product(slot0, dS, P1);   // Vt dS'^T
+    state_product(slot0, dM, P2);   // Vt dM'^T
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * it + 4 * lg + r;
+                dKa[it][dt][r] += ws[i] * P1[it][dt][r] - wm[i] * P2[it][dt][r];
+            }
+    row_dot(P1, slot2, V(G_RZ1));
+    row_dot(P2, slot2, V(G_RZ2));
+
+    // phase 3: slot1 = Q (K stays in slot2); Q K^T, then the masked products
+    stage<DK, LD>(slot1, q + tok0 * DK, (size_t)H * DK, n, tid);
+    __syncthreads();
+    f32x4 cQ[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) cQ[jt] = zero4();
+    for (int kd = lg; kd < DK; kd += 4) {
+        const float a = slot1[(16 * wave + l16) * LD + kd];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) cQ[jt] = MF::mma(a, slot2[(16 * jt + l16) * LD + kd], cQ[jt]);
+    }
+    // dGamma from A (dA o Q Khat^T) now, G_L = dL o (P Khat^T) into Cm2 for the
+    // one-row shift; dA o Gamma into Cm1, dL o Gamma^- into slot0 (Vt is done)
+    float* dAG = Cm1;
+    float* dLG = slot0;   // C x C with row stride LDC
+    float* GL = Cm2;
+    f32x4 dG[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * wave + 4 * lg + r;
+            const int j = 16 * jt + l16;
+            const float ej = V(G_E)[j];
+            const float da = j <= i ? cA[jt][r] : 0.f;
+            const float dl = j < i ? cL[jt][r] : 0.f;
+            dG[jt][r] = da * cQ[jt][r] * ej;
+            GL[i * LDC + j] = dl * V(G_A)[i] * cK[jt][r] * ej;
+            dAG[i * LDC + j] = da * Gm[i * LDC + j];
+            dLG[i * LDC + j] = j < i ? dl * Gm[(i - 1) * LDC + j] : 0.f;
+        }
+    __syncthreads();
+    // dGamma_{i,j} += G_L_{i+1,j}; the last row also gets eta_j k_j.(Vt dS'^T)_j
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * wave + 4 * lg + r;
+            const int j = 16 * jt + l16;
+            if (i + 1 < n) dG[jt][r] += GL[(i + 1) * LDC + j];
+            if (i == n - 1 && j < n) dG[jt][r] += V(G_E)[j] * V(G_RZ1)[j];
+            if (j > i || i >= n) dG[jt][r] = 0.f;
+        }
+
+    // masked products: dQ += dAG Khat;  dKhat = dAG^T Q + dLG^T P;  dP = dLG Khat
+    f32x4 dKh[4][DT];
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) P1[it][dt] = dKh[it][dt] = zero4();
+    for (int kr = lg; kr < CH; kr += 4) {
+        const float ek = V(G_E)[kr];
+        const float ak = V(G_A)[kr];
+        float kh[DT], qv[DT], kv[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int d = 16 * (wave * DT + dt) + l16;
+            kv[dt] = slot2[kr * LD + d];
+            kh[dt] = ek * kv[dt];
+            qv[dt] = slot1[kr * LD + d];
+        }
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int i = 16 * it + l16;
+            const float aAG = dAG[i * LDC + kr];      // dAG[i][k]
+            const float aAGt = dAG[kr * LDC + i];     // dAG^T[i][k]
+            const float aLGt = dLG[kr * LDC + i];     // dLG^T[i][k]
+            const float aLG = dLG[i * LDC + kr];      // dLG[i][k]
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                dQa[it][dt] = MF::mma(aAG, kh[dt], dQa[it][dt]);
+                dKh[it][dt] = MF::mma(aAGt, qv[dt], dKh[it][dt]);
+                dKh[it][dt] = MF::mma(aLGt, ak * kv[dt], dKh[it][dt]);
+                P1[it][dt] = MF::mma(aLG, kh[dt], P1[it][dt]);
+            }
+        }
+    }
+    // dK += Diag(eta) dKhat + Diag(alpha) dP
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * it + 4 * lg + r;
+                dKa[it][dt][r] += V(G_E)[i] * dKh[it][dt][r] + V(G_A)[i] * P1[it][dt][r];
+            }
+    // GL (Cm2) is read: reuse it for the row-dot scratch, then store dGamma there
+    __syncthreads();
+    row_dot(dKh, slot2, V(G_RKH));
+    row_dot(P1, slot2, V(G_RP));
+
+    // dq, dk (rows < n)
+    {
+        float* dqb = dq + tok0 * DK;
+        float* dkb = dk + tok0 * DK;
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * it + 4 * lg + r;
+                    const int d = 16 * (wave * DT + dt) + l16;
+                    if (i < n) {
+                        dqb[(size_t)i * H * DK + d] = dQa[it][dt][r];
+                        dkb[(size_t)i * H * DK + d] = dKa[it][dt][r];
+                    }
+                }
+    }
+
+    // ---- coefficient gradients back to the gates ----------------------------
+    float* dGm = Cm2;   // dGamma, row stride LDC
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dGm[(16 * wave + 4 * lg + r) * LDC + 16 * jt + l16] = dG[jt][r];
+    // scratch, all with row stride LDC: the m table (K is done) and the
+    // per-(i, j) contributions to dalpha_i, dbeta_i, dmu_i (dLG, Q and dAG
+    // are done)
+    float* Mt = slot2;
+    float* cA_ = slot0;
+    float* cS_ = slot1;
+    float* cM_ = Cm1;
+    __syncthreads();
+    // direct terms per row
+    for (int i = tid; i < CH; i += NT) {
+        const float bp = i > 0 ? V(G_B)[i - 1] : 0.f;
+        V(G_DAB)[i] = V(G_RX1)[i] - V(G_RY1)[i];
+        V(G_DB)[i] = -V(G_RX2)[i];
+        V(G_DMB)[i] = 0.f;
+        // alpha: through P = Diag(alpha) K and ab1 = alpha_i b_{i-1}
+        V(G_DA)[i] = V(G_RP)[i] + V(G_RY2)[i] * bp;
+        // eta: through Khat and ws (wm follows with the m table)
+        V(G_DE)[i] = V(G_RKH)[i] + (i < n ? Gm[(n - 1) * LDC + i] * V(G_RZ1)[i] : 0.f);
+        V(G_DS)[i] = 0.f;
+        V(G_DM)[i] = 0.f;
+    }
+    __syncthreads();
+    // d(ab1)_i also reaches b_{i-1} through alpha_i; the last row's scalars
+    if (tid == 0) {
+        for (int i = 1; i < n; ++i) V(G_DB)[i - 1] += V(G_RY2)[i] * V(G_A)[i];
+        V(G_DAB)[n - 1] += scal[0];
+        V(G_DB)[n - 1] -= scal[1];
+        V(G_DMB)[n - 1] += scal[2];
+    }
+    // m table and the column recursions (thread j < n)
+    if (tid < CH) {
+        const int j = tid;
+        float m = 1.f;
+        for (int i = 0; i < CH; ++i) {
+            if (i > j) m = V(G_M)[i] * m;
+            Mt[i * LDC + j] = i >= j ? m : 0.f;
+            cA_[i * LDC + j] = 0.f;
+            cS_[i * LDC + j] = 0.f;
+            cM_[i * LDC + j] = 0.f;
+        }
+        if (j < n) {
+            // eta_j through wm: -m_{n-1,j} k_j.(Vt dM'^T)_j
+            const float dml = -V(G_E)[j] * V(G_RZ2)[j];
+            float gcar = 0.f;      // dGamma_{i,j} carried down the column
+            float mcar = 0.f;      // dm_{i,j} carried down the column
+            for (int i = n - 1; i > j; --i) {
+                const float g = dGm[i * LDC + j] + gcar;
+                const float dm = (i == n - 1 ? dml : 0.f) + mcar;
+                const float ai = V(G_A)[i], si = V(G_S)[i], mi = V(G_M)[i];
+                const float mij = Mt[i * LDC + j];
+                cA_[i * LDC + j] = g * Gm[(i - 1) * LDC + j];
+                cS_[i * LDC + j] = g * mij;
+                const float dmt = dm + g * si;          // total dm_{i,j}
+                cM_[i * LDC + j] = dmt * Mt[(i - 1) * LDC + j];
+                gcar = g * ai;
+                mcar = dmt * mi;
+            }
+            // gamma_{j,j} = beta_j
+            cS_[j * LDC + j] = dGm[j * LDC + j] + gcar;
+            // the eta_j m_{n-1,j} weight: its eta part
+            V(G_DE)[j] += -Mt[(n - 1) * LDC + j] * V(G_RZ2)[j];
+        }
+    }
+    __syncthreads();
+    // sum the column contributions per row, then the b, abar and mubar recursions
+    for (int i = tid; i < CH; i += NT) {
+        float sa = 0.f, ss = 0.f, sm = 0.f;
+        for (int j = 0; j < CH; ++j) {
+            sa += cA_[i * LDC + j];
+            ss += cS_[i * LDC + j];
+            sm += cM_[i * LDC + j];
+        }
+        V(G_DA)[i] += sa;
+        V(G_DS)[i] += ss;
+        V(G_DM)[i] += sm;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        // b_i = alpha_i b_{i-1} + beta_i mubar_i
+        for (int i = n - 1; i >= 0; --i) {
+            const float g = V(G_DB)[i];
+            const float bp = i > 0 ? V(G_B)[i - 1] : 0.f;
+            V(G_DA)[i] += g * bp;
+            if (i > 0) V(G_DB)[i - 1] += g * V(G_A)[i];
+            V(G_DS)[i] += g * V(G_MB)[i];
+            V(G_DMB)[i] += g * V(G_S)[i];
+        }
+        // abar_i = alpha_i abar_{i-1},  mubar_i = mu_i mubar_{i-1}
+        for (int i = n - 1; i >= 0; --i) {
+            const float ga = V(G_DAB)[i];
+            const float gm = V(G_DMB)[i];
+            V(G_DA)[i] += ga * (i > 0 ? V(G_AB)[i - 1] : 1.f);
+            V(G_DM)[i] += gm * (i > 0 ? V(G_MB)[i - 1] : 1.f);
+            if (i > 0) {
+                V(G_DAB)[i - 1] += ga * V(G_A)[i];
+                V(G_DMB)[i - 1] += gm * V(G_M)[i];
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += NT) {
+        const size_t g = tok0 + (size_t)i * H;
+        dalpha[g] = V(G_DA)[i];
+        deta[g] = V(G_DE)[i];
+        if (dmu) dmu[g] = V(G_DM)[i];
+        if (dbeta) dbeta[g] = V(G_DS)[i];
+    }
+}
+
+}  // namespace
+}  // namespace mdn
+
+namespace mdn {
+
+size_t chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, bool bf16)
+{
+    const size_t NC = ((size_t)T + CH - 1) / CH;
+    const size_t nchunks = (size_t)B * H * NC;
+    const size_t prep = nchunks * (2 * CH * CH * (bf16 ? 2 : 4) + NVEC * CH * 4);
+    return prep + nchunks * (4 * (size_t)Dk * Dv + (size_t)CH * Dv) * 4;
+}
+
+template <typename E, int DK, int DV>
+static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const float* alpha,
+                               const float* mu, const float* eta, const float* beta,
+                               const float* S0, const float* M0, const void* dO,
+                               const float* dST, const float* dMT, float* dq, float* dk,
+                               float* dv, float* dalpha, float* dmu, float* deta, float* dbeta,
+                               float* dS0, float* dM0, int B, int T, int H, void* workspace,
+                               hipStream_t stream)
+{
+    const int NC = (T + CH - 1) / CH;
+    const size_t nchunks = (size_t)B * H * NC;
+    char* p = static_cast<char*>(workspace);
+    E* Tw = reinterpret_cast<E*>(p);
+    p += nchunks * CH * CH * sizeof(E);
+    E* Aw = reinterpret_cast<E*>(p);
+    p += nchunks * CH * CH * sizeof(E);
+    float* Vw = reinterpret_cast<float*>(p);
+    p += nchunks * NVEC * CH * sizeof(float);
+    float* Hs = reinterpret_cast<float*>(p);
+    p += nchunks * 2 * DK * DV * sizeof(float);
+    float* Hd = reinterpret_cast<float*>(p);
+    p += nchunks * 2 * DK * DV * sizeof(float);
+    float* Vts = reinterpret_cast<float*>(p);
+
+    hipError_t err = launch_chunk_prepare(q, k, alpha, mu, eta, beta, B, T, H, DK,
+                                          sizeof(E) == 2, workspace, stream);
+    if (err != hipSuccess) return err;
+    const unsigned nblk = (unsigned)((size_t)B * H * (DV / 64));
+    hipLaunchKernelGGL((bwd_scan_kernel<E, DK, DV>), dim3(nblk), dim3(NT), 0, stream,
+                       static_cast<const E*>(q), static_cast<const E*>(k),
+                       static_cast<const E*>(dO), Tw, Aw, Vw, dST, dMT, Hd, dv, dS0, dM0, T, H,
+                       NC);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((bwd_rescan_kernel<E, DK, DV>), dim3(nblk), dim3(NT), 0, stream,
+                       static_cast<const E*>(k), static_cast<const E*>(v), Tw, Vw, S0, M0, Hs,
+                       Vts, T, H, NC);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((bwd_grad_kernel<E, DK, DV>), dim3((unsigned)nchunks), dim3(NT), 0, stream,
+                       static_cast<const E*>(q), static_cast<const E*>(k),
+                       static_cast<const E*>(dO), dv, Vts, Hs, Hd, alpha, mu, eta, beta, dq, dk,
+                       dalpha, dmu, deta, dbeta, T, H, NC);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
+                            const float* mu, const float* eta, const float* beta, const float* S0,
+                            const float* M0, const void* dO, const float* dST, const float* dMT,
+                            float* dq, float* dk, float* dv, float* dalpha, float* dmu,
+                            float* deta, float* dbeta, float* dS0, float* dM0, int B, int T,
+                            int H, int Dk, int Dv, bool bf16, void* workspace, hipStream_t stream)
+{
+#define MDN_BWD(E, DK, DV)                                                                        \
+    if (Dk == DK && Dv == DV)                                                                     \
+        return launch_bwd_t<E, DK, DV>(q, k, v, alpha, mu, eta, beta, S0, M0, dO, dST, dMT, dq,   \
+                                       dk, dv, dalpha, dmu, deta, dbeta, dS0, dM0, B, T, H,       \
+                                       workspace, stream);
+    if (bf16) {
+        MDN_BWD(__bf16, 64, 64) MDN_BWD(__bf16, 64, 128)
+        MDN_BWD(__bf16, 128, 64) MDN_BWD(__bf16, 128, 128)
+    } else {
+        MDN_BWD(float, 64, 64) MDN_BWD(float, 64, 128)
+        MDN_BWD(float, 128, 64) MDN_BWD(float, 128, 128)
+    }
+#undef MDN_BWD
+    return hipErrorInvalidValue;
+}
+
+}  // namespace mdn

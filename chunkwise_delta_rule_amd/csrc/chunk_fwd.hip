@@ -983,6 +983,15 @@ static hipError_t launch_scan_t(const void* q, const void* k, const void* v, con
     return hipGetLastError();
 }
 
+// dst = src (src NULL: zero), count floats
+hipError_t launch_state_copy(const float* src, float* dst, size_t count, hipStream_t stream)
+{
+    if (count == 0) return hipSuccess;
+    const unsigned grid = (unsigned)((count + NT - 1) / NT);
+    hipLaunchKernelGGL(state_passthrough_kernel, dim3(grid), dim3(NT), 0, stream, src, dst, count);
+    return hipGetLastError();
+}
+
 size_t chunk_workspace_bytes(int B, int T, int H, bool bf16)
 {
     const size_t NC = ((size_t)T + CH - 1) / CH;

@@ -38,7 +38,7 @@ STATUS_NAMES = {
 EXPORTED = ("mdn_chunk_fwd_workspace_bytes", "mdn_chunk_fwd_split_workspace_bytes",
             "mdn_chunk_fwd", "mdn_chunk_fwd_prepare",
             "mdn_chunk_fwd_scan", "mdn_decode_step", "mdn_gates_from_logits",
-            "mdn_status_string")
+            "mdn_chunk_bwd_workspace_bytes", "mdn_chunk_bwd", "mdn_status_string")
 
 
 class GateParams(ctypes.Structure):
@@ -78,6 +78,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mdn_chunk_fwd_scan.argtypes = [P] * 8 + [I] * 7 + [P, S, P]
     lib.mdn_decode_step.restype = I
     lib.mdn_decode_step.argtypes = [P] * 10 + [I] * 5 + [P]
+    lib.mdn_chunk_bwd_workspace_bytes.restype = S
+    lib.mdn_chunk_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.mdn_chunk_bwd.restype = I
+    lib.mdn_chunk_bwd.argtypes = [P] * 21 + [I] * 7 + [P, S, P]
     lib.mdn_gates_from_logits.restype = I
     lib.mdn_gates_from_logits.argtypes = [P] * 4 + [S, GateParams] + [P] * 4 + [P]
     lib.mdn_status_string.restype = ctypes.c_char_p
@@ -292,3 +296,58 @@ def gates_from_logits(z_eta: torch.Tensor, z_alpha: torch.Tensor, z_beta: torch.
     if st != 0:
         raise MdnError(st, "mdn_gates_from_logits")
     return tuple(out)
+
+
+def workspace_bytes_bwd(B: int, T: int, H: int, Dk: int, Dv: int, dtype: torch.dtype,
+                        chunk: int = CHUNK) -> int:
+    """Workspace bytes of mdn_chunk_bwd."""
+    return int(load_library().mdn_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, chunk,
+                                                            _dtype_code(dtype)))
+
+
+def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+              mu: Optional[torch.Tensor], eta: torch.Tensor, S0: Optional[torch.Tensor],
+              M0: Optional[torch.Tensor], dO: torch.Tensor, dS_T: Optional[torch.Tensor] = None,
+              dM_T: Optional[torch.Tensor] = None, *, beta: Optional[torch.Tensor] = None,
+              chunk: int = CHUNK, workspace: Optional[torch.Tensor] = None,
+              state_grads: bool = True) -> dict:
+    """Gradients through mdn_chunk_fwd given dO (and optionally dS_T, dM_T).
+    Arguments as for chunk_fwd; returns a dict of float32 tensors dq, dk, dv,
+    dalpha, dmu (None without mu), deta, dbeta (None without beta), dS0, dM0
+    (None when state_grads is False)."""
+    lib = load_library()
+    dev = q.device
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    code = _dtype_code(dt)
+    _check(q, "q", (B, T, H, Dk), dt, dev)
+    _check(k, "k", (B, T, H, Dk), dt, dev)
+    _check(v, "v", (B, T, H, Dv), dt, dev)
+    _check(dO, "dO", (B, T, H, Dv), dt, dev)
+    for name, g in (("alpha", alpha), ("mu", mu), ("eta", eta), ("beta", beta)):
+        if g is not None or name in ("alpha", "eta"):
+            _check(g, name, (B, T, H), torch.float32, dev)
+    for name, st in (("S0", S0), ("M0", M0), ("dS_T", dS_T), ("dM_T", dM_T)):
+        if st is not None:
+            _check(st, name, (B, H, Dk, Dv), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dq=torch.empty((B, T, H, Dk), **f32), dk=torch.empty((B, T, H, Dk), **f32),
+               dv=torch.empty((B, T, H, Dv), **f32), dalpha=torch.empty((B, T, H), **f32),
+               dmu=torch.empty((B, T, H), **f32) if mu is not None else None,
+               deta=torch.empty((B, T, H), **f32),
+               dbeta=torch.empty((B, T, H), **f32) if beta is not None else None,
+               dS0=torch.empty((B, H, Dk, Dv), **f32) if state_grads else None,
+               dM0=torch.empty((B, H, Dk, Dv), **f32) if state_grads else None)
+    need = int(lib.mdn_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, chunk, code))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    st = lib.mdn_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(mu), _ptr(eta),
+                           _ptr(beta), _ptr(S0), _ptr(M0), _ptr(dO), _ptr(dS_T), _ptr(dM_T),
+                           *(_ptr(out[n]) for n in ("dq", "dk", "dv", "dalpha", "dmu", "deta",
+                                                    "dbeta", "dS0", "dM0")),
+                           B, T, H, Dk, Dv, chunk, code, _ptr(workspace), workspace.numel(),
+                           _stream(dev))
+    if st != 0:
+        raise MdnError(st, "mdn_chunk_bwd")
+    return out

@@ -180,6 +180,45 @@ mdn_status mdn_decode_step(const void* q, const void* k, const void* v, const fl
                            hipStream_t stream);
 
 /*
+ * Backward pass of mdn_chunk_fwd: the gradients of a loss L through the
+ * forward, given dO = dL/dO and dS_T, dM_T = dL/dS_T, dL/dM_T.  The pages
+ * ("MDN: Parallelizing Stepwise Momentum for Delta Linear Attention"
+ * (slides), frame "The implementation trades saved residuals for
+ * throughput"; the paper's Sec. 3.1 and Appendix E) describe the strategy --
+ * rebuild the states for the gradients instead of storing every state pair --
+ * but print no gradient formulas; these are the chain rule through the chunk
+ * equations of mdn_chunk_fwd, chunk by chunk from the last.  The call
+ * recomputes the residuals Vt from (q, k, v, gates, S0, M0) and keeps each
+ * chunk's entry state and exit-state gradients in the workspace while it
+ * runs; nothing from the forward call is needed.
+ *   q, k, v, alpha, mu, eta, beta, S0, M0, B, T, H, Dk, Dv, chunk, dt:
+ *                         exactly as given to mdn_chunk_fwd (mu, beta, S0, M0
+ *                         may be NULL with the same meaning).
+ *   dO [B, T, H, Dv]       dtype dt.
+ *   dS_T, dM_T [B, H, Dk, Dv] or NULL (zero), float32.
+ * Outputs, all float32, each overwritten:
+ *   dq, dk [B, T, H, Dk]; dv [B, T, H, Dv];
+ *   dalpha, deta [B, T, H]; dmu [B, T, H] (only when mu is given; may be
+ *   NULL otherwise); dbeta [B, T, H] (only when beta is given; may be NULL
+ *   otherwise); dS0, dM0 [B, H, Dk, Dv] or NULL (not returned).
+ * Every pointer is a device pointer aligned to 16 bytes; no output may
+ * overlap an input, another output or the workspace.  Workspace:
+ * mdn_chunk_bwd_workspace_bytes (T and A of every chunk, the coefficient
+ * rows, two state pairs and the residuals of every chunk, in float32 but for
+ * T and A).  T = 0 copies dS_T, dM_T to dS0, dM0.  Enqueued on `stream`.
+ */
+size_t mdn_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
+                                     mdn_dtype dt);
+
+mdn_status mdn_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
+                         const float* mu, const float* eta, const float* beta, const float* S0,
+                         const float* M0, const void* dO, const float* dS_T, const float* dM_T,
+                         float* dq, float* dk, float* dv, float* dalpha, float* dmu, float* deta,
+                         float* dbeta, float* dS0, float* dM0, int B, int T, int H, int Dk,
+                         int Dv, int chunk, mdn_dtype dt, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/*
  * MDN's coupled gate parameterisation ("MDN: Parallelizing Stepwise Momentum
  * for Delta Linear Attention" (slides), frame "Coupled gates restrict the
  * spectral region", the paper's Sec. 3.3), from logits the caller computes

@@ -238,3 +238,21 @@ def gate_logits(n: int, seed: int, scale: float = 3.0) -> Dict[str, np.ndarray]:
         z[:m] = np.roll(ext, len(out) * 3)[:m]
         out[name] = z.astype(np.float32)
     return out
+
+
+def backward_cotangents(cfg: ForwardConfig, seed: int, terminal: bool = True,
+                        **overrides) -> Dict[str, Optional[np.ndarray]]:
+    """Gradients arriving at the forward's outputs, for a backward run on the
+    workload ``make_forward(cfg, **overrides)``: dO ~ N(0, 1) rounded to the
+    I/O dtype, then (when ``terminal``) dS_T, dM_T ~ N(0, 1) in float32, drawn
+    in this order from their own generator (seed ``SEED_BASE + seed``)."""
+    if overrides:
+        cfg = replace(cfg, **overrides)
+    rng = np.random.Generator(np.random.PCG64(SEED_BASE + seed))
+    B, T, H, Dk, Dv = cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv
+    dO = _normal_rows(rng, (B, T, H, Dv), cfg.io_dtype, normalise=False)
+    dS = dM = None
+    if terminal:
+        dS = _normal_rows(rng, (B, H, Dk, Dv), "f32", False)
+        dM = _normal_rows(rng, (B, H, Dk, Dv), "f32", False)
+    return dict(dO=dO, dS_T=dS, dM_T=dM)
