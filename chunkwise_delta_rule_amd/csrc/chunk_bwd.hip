@@ -87,22 +87,20 @@ struct Tile {
     }
     __device__ __forceinline__ void commit(float* dst, int tid) const
     {
+        static_assert(LD % 4 == 0, "16-byte LDS rows");
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             const int idx = tid + u * NT;
-            float* d = dst + (idx / VPR) * LD + (idx % VPR) * VE;
+            float4* d = reinterpret_cast<float4*>(dst + (idx / VPR) * LD + (idx % VPR) * VE);
             if constexpr (sizeof(E) == 2) {
                 const unsigned w[4] = {buf[u].x, buf[u].y, buf[u].z, buf[u].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    d[2 * e] = __uint_as_float(w[e] << 16);
-                    d[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-                }
+                d[0] = float4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                              __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+                d[1] = float4{__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xffff0000u),
+                              __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xffff0000u)};
             } else {
-                d[0] = __uint_as_float(buf[u].x);
-                d[1] = __uint_as_float(buf[u].y);
-                d[2] = __uint_as_float(buf[u].z);
-                d[3] = __uint_as_float(buf[u].w);
+                d[0] = float4{__uint_as_float(buf[u].x), __uint_as_float(buf[u].y),
+                              __uint_as_float(buf[u].z), __uint_as_float(buf[u].w)};
             }
         }
     }
@@ -127,6 +125,36 @@ __device__ __forceinline__ float sum16(float x)
     return x;
 }
 
+// Scans over the 64 lanes of a wavefront, lane i holding row i: the affine
+// recurrence x_i = m_i x_{i-1} + c_i from x_{-1} = 0 (prefix), and
+// y_i = c_i + m_i y_{i+1} from y_64 = 0 (suffix).  Six shuffle steps each.
+__device__ __forceinline__ float prefix_affine(float m, float c, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const float mp = __shfl_up(m, d);
+        const float cp = __shfl_up(c, d);
+        if (lane >= d) {
+            c = m * cp + c;
+            m = m * mp;
+        }
+    }
+    return c;
+}
+__device__ __forceinline__ float suffix_affine(float m, float c, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const float mn = __shfl_down(m, d);
+        const float cn = __shfl_down(c, d);
+        if (lane + d < 64) {
+            c = c + m * cn;
+            m = m * mn;
+        }
+    }
+    return c;
+}
+
 // ---------------------------------------------------------------------------
 // Reverse scan.  Wavefront w keeps 16 columns of dS and dM in fp32 MFMA
 // accumulators (rows 16 rt + 4 lg + r, column wcol + l16), as the forward
@@ -142,14 +170,14 @@ __global__ __launch_bounds__(NT) void bwd_scan_kernel(
     constexpr int TV = 64;
     constexpr int NTILE = DV / TV;
     constexpr int RT = DK / 16;
-    constexpr int LDK = DK + 1;
-    constexpr int LDV = TV + 1;
-    constexpr int LDC = CH + 1;
-    __shared__ float Qs[CH * LDK];
-    __shared__ float Ks[CH * LDK];
-    __shared__ float Gs[CH * LDV];   // dO, this workgroup's columns
-    __shared__ float Ts[CH * LDC];
-    __shared__ float As[CH * LDC];
+    constexpr int LDK = DK + 4;
+    constexpr int LDV = TV + 4;
+    constexpr int LDC = CH + 4;
+    __shared__ __align__(16) float Qs[CH * LDK];
+    __shared__ __align__(16) float Ks[CH * LDK];
+    __shared__ __align__(16) float Gs[CH * LDV];   // dO, this workgroup's columns
+    __shared__ __align__(16) float Ts[CH * LDC];
+    __shared__ __align__(16) float As[CH * LDC];
     __shared__ float vecs[6 * CH];
 
     const int tid = threadIdx.x;
@@ -231,15 +259,22 @@ __global__ __launch_bounds__(NT) void bwd_scan_kernel(
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) xs[ct] = xm[ct] = zero4();
 #pragma unroll
-        for (int s = 0; s < DK / 4; ++s) {
-            const float bS = MF::from_acc(Sa, s);
-            const float bM = MF::from_acc(Ma, s);
-            const int kd = MF::perm_row(s, lg, 0);
+        for (int sb = 0; sb < DK / 16; ++sb) {
+            float4 a4[4];
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-                const float aK = Ks[(16 * ct + l16) * LDK + kd];
-                xs[ct] = MF::mma(aK, bS, xs[ct]);
-                xm[ct] = MF::mma(aK, bM, xm[ct]);
+            for (int ct = 0; ct < 4; ++ct)
+                a4[ct] = *reinterpret_cast<const float4*>(Ks + (16 * ct + l16) * LDK + 16 * sb + 4 * lg);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // k = perm_row(4 sb + e, lg) = 16 sb + 4 lg + e
+                const float bS = Sa[sb][e];
+                const float bM = Ma[sb][e];
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    const float aK = e == 0 ? a4[ct].x : e == 1 ? a4[ct].y : e == 2 ? a4[ct].z : a4[ct].w;
+                    xs[ct] = MF::mma(aK, bS, xs[ct]);
+                    xm[ct] = MF::mma(aK, bM, xm[ct]);
+                }
             }
         }
 
@@ -252,9 +287,9 @@ __global__ __launch_bounds__(NT) void bwd_scan_kernel(
                 const int i = 16 * it + 4 * lg + r;
                 dVt[it][r] = vecs[V_WS * CH + i] * xs[it][r] - vecs[V_WM * CH + i] * xm[it][r];
             }
-#pragma unroll 4
+#pragma unroll
         for (int s = 0; s < CH / 4; ++s) {
-            const int kr = 4 * s + lg;
+            const int kr = MF::perm_row(s, lg, 0);
             const float bO = Gs[kr * LDV + lcol];
 #pragma unroll
             for (int it = 0; it < 4; ++it)
@@ -295,9 +330,9 @@ __global__ __launch_bounds__(NT) void bwd_scan_kernel(
             Sa[rt] = abn * so;
             Ma[rt] = mbn * Ma[rt] - bn * so;
         }
-#pragma unroll 4
+#pragma unroll
         for (int s = 0; s < CH / 4; ++s) {
-            const int kr = 4 * s + lg;
+            const int kr = MF::perm_row(s, lg, 0);
             const float g = Gs[kr * LDV + lcol];
             const float bS = vecs[V_ABAR * CH + kr] * g;
             const float bM = -vecs[V_B * CH + kr] * g;
@@ -344,12 +379,12 @@ __global__ __launch_bounds__(NT) void bwd_rescan_kernel(
     constexpr int TV = 64;
     constexpr int NTILE = DV / TV;
     constexpr int RT = DK / 16;
-    constexpr int LDK = DK + 1;
-    constexpr int LDV = TV + 1;
-    constexpr int LDC = CH + 1;
-    __shared__ float Ks[CH * LDK];
-    __shared__ float Vs[CH * LDV];
-    __shared__ float Ts[CH * LDC];
+    constexpr int LDK = DK + 4;
+    constexpr int LDV = TV + 4;
+    constexpr int LDC = CH + 4;
+    __shared__ __align__(16) float Ks[CH * LDK];
+    __shared__ __align__(16) float Vs[CH * LDV];
+    __shared__ __align__(16) float Ts[CH * LDC];
     __shared__ float vecs[6 * CH];
 
     const int tid = threadIdx.x;
@@ -426,15 +461,22 @@ __global__ __launch_bounds__(NT) void bwd_rescan_kernel(
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) xs[ct] = xm[ct] = zero4();
 #pragma unroll
-        for (int s = 0; s < DK / 4; ++s) {
-            const float bS = MF::from_acc(Sa, s);
-            const float bM = MF::from_acc(Ma, s);
-            const int kd = MF::perm_row(s, lg, 0);
+        for (int sb = 0; sb < DK / 16; ++sb) {
+            float4 a4[4];
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-                const float aK = Ks[(16 * ct + l16) * LDK + kd];
-                xs[ct] = MF::mma(aK, bS, xs[ct]);
-                xm[ct] = MF::mma(aK, bM, xm[ct]);
+            for (int ct = 0; ct < 4; ++ct)
+                a4[ct] = *reinterpret_cast<const float4*>(Ks + (16 * ct + l16) * LDK + 16 * sb + 4 * lg);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // k = perm_row(4 sb + e, lg) = 16 sb + 4 lg + e
+                const float bS = Sa[sb][e];
+                const float bM = Ma[sb][e];
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    const float aK = e == 0 ? a4[ct].x : e == 1 ? a4[ct].y : e == 2 ? a4[ct].z : a4[ct].w;
+                    xs[ct] = MF::mma(aK, bS, xs[ct]);
+                    xm[ct] = MF::mma(aK, bM, xm[ct]);
+                }
             }
         }
         f32x4 R[4];
@@ -450,12 +492,20 @@ __global__ __launch_bounds__(NT) void bwd_rescan_kernel(
 #pragma unroll
         for (int it = 0; it < 4; ++it) Vt[it] = zero4();
 #pragma unroll
-        for (int s = 0; s < CH / 4; ++s) {
-            const float bR = MF::from_acc(R, s);
-            const int kr = MF::perm_row(s, lg, 0);
+        for (int sb = 0; sb < CH / 16; ++sb) {
+            float4 t4[4];
 #pragma unroll
             for (int it = 0; it < 4; ++it)
-                Vt[it] = MF::mma(Ts[(16 * it + l16) * LDC + kr], bR, Vt[it]);
+                t4[it] = *reinterpret_cast<const float4*>(Ts + (16 * it + l16) * LDC + 16 * sb + 4 * lg);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float bR = R[sb][e];
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const float aT = e == 0 ? t4[it].x : e == 1 ? t4[it].y : e == 2 ? t4[it].z : t4[it].w;
+                    Vt[it] = MF::mma(aT, bR, Vt[it]);
+                }
+            }
         }
         {
             float* vb = Vts + chn * CH * DV + wcol + l16;
@@ -498,11 +548,11 @@ __global__ __launch_bounds__(NT) void bwd_rescan_kernel(
 // ---------------------------------------------------------------------------
 template <int DK, int DV>
 struct GradSmem {
-    static constexpr int LDK = DK + 1;
-    static constexpr int LDV = DV + 1;
+    static constexpr int LDK = DK + 4;
+    static constexpr int LDV = DV + 4;
     static constexpr int LD = LDK > LDV ? LDK : LDV;
     static constexpr int SLOT = CH * LD;     // floats of one C x D tile
-    static constexpr int LDC = CH + 1;
+    static constexpr int LDC = CH + 4;
     static constexpr int CM = CH * LDC;      // floats of one C x C matrix
     static constexpr int NV = 24;            // vectors of CH floats
     static constexpr int FLOATS = 3 * SLOT + 3 * CM + NV * CH + 8;
@@ -530,7 +580,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
     constexpr int LD = SM::LD;
     constexpr int LDC = SM::LDC;
     constexpr int DT = DK / 64;   // d-tiles per wavefront
-    __shared__ float smem[SM::FLOATS];
+    __shared__ __align__(16) float smem[SM::FLOATS];
     float* slot0 = smem;
     float* slot1 = smem + SM::SLOT;
     float* slot2 = smem + 2 * SM::SLOT;
@@ -570,16 +620,21 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
     }
     for (int i = tid; i < (SM::NV - G_RX1) * CH; i += NT) vec[G_RX1 * CH + i] = 0.f;
     __syncthreads();
-    if (tid == 0) {
-        float ab = 1.f, mb = 1.f, bp = 0.f;
-        for (int i = 0; i < CH; ++i) {
-            ab *= V(G_A)[i];
-            mb *= V(G_M)[i];
-            bp = V(G_A)[i] * bp + V(G_S)[i] * mb;
-            V(G_AB)[i] = ab;
-            V(G_MB)[i] = mb;
-            V(G_B)[i] = bp;
+    if (wave == 0) {
+        // abar, mubar (prefix products) and b_i = alpha_i b_{i-1} + beta_i mubar_i
+        const float a = V(G_A)[lane], m = V(G_M)[lane];
+        float pa = a, pm = m;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const float ua = __shfl_up(pa, d), um = __shfl_up(pm, d);
+            if (lane >= d) {
+                pa *= ua;
+                pm *= um;
+            }
         }
+        V(G_AB)[lane] = pa;
+        V(G_MB)[lane] = pm;
+        V(G_B)[lane] = prefix_affine(a, V(G_S)[lane] * pm, lane);
     }
     // Gamma by columns (thread j < CH): rows < j are zero; m lives in Cm1 for now
     if (tid < CH) {
@@ -610,11 +665,24 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
     // fixed-order reduction over the four wavefronts)
     {
         float a0 = 0.f, a1 = 0.f, a2 = 0.f;
-        for (int x = tid; x < DK * DV; x += NT) {
-            const float s0 = S0[x], m0 = M0[x], ds = dS[x];
-            a0 += ds * s0;
-            a1 += ds * m0;
-            a2 += dM[x] * m0;
+        constexpr int NF = DK * DV / 4 / NT;   // 16-byte loads per thread and array
+        constexpr int BATCH = NF < 4 ? NF : 4;
+        for (int u0 = 0; u0 < NF; u0 += BATCH) {
+            float4 s0[BATCH], m0[BATCH], ds[BATCH], dm[BATCH];
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+                const int x = 4 * (tid + (u0 + u) * NT);
+                s0[u] = *reinterpret_cast<const float4*>(S0 + x);
+                m0[u] = *reinterpret_cast<const float4*>(M0 + x);
+                ds[u] = *reinterpret_cast<const float4*>(dS + x);
+                dm[u] = *reinterpret_cast<const float4*>(dM + x);
+            }
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+                a0 += ds[u].x * s0[u].x + ds[u].y * s0[u].y + ds[u].z * s0[u].z + ds[u].w * s0[u].w;
+                a1 += ds[u].x * m0[u].x + ds[u].y * m0[u].y + ds[u].z * m0[u].z + ds[u].w * m0[u].w;
+                a2 += dm[u].x * m0[u].x + dm[u].y * m0[u].y + dm[u].z * m0[u].z + dm[u].w * m0[u].w;
+            }
         }
         for (int o = 32; o >= 1; o >>= 1) {
             a0 += __shfl_xor(a0, o);
@@ -653,12 +721,15 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
 #pragma unroll
         for (int kb = 0; kb < DV / 16; ++kb) {
             const float4* sv = sva[kb];
+            float4 xa[4];
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                xa[it] = *reinterpret_cast<const float4*>(X + (16 * it + l16) * LD + 16 * kb + 4 * lg);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int kc = 16 * kb + 4 * lg + e;
 #pragma unroll
                 for (int it = 0; it < 4; ++it) {
-                    const float a = X[(16 * it + l16) * LD + kc];
+                    const float a = e == 0 ? xa[it].x : e == 1 ? xa[it].y : e == 2 ? xa[it].z : xa[it].w;
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) {
                         const float bv = e == 0 ? sv[dt].x : e == 1 ? sv[dt].y
@@ -691,31 +762,55 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
         __syncthreads();
     };
 
+    // this wavefront's row tile of X Y^T (C x C), k over KD columns of both,
+    // 16-byte k-permuted reads
+    auto cc_product = [&](const float* X, const float* Y, int KD, float sign, f32x4* acc) {
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) acc[jt] = zero4();
+        for (int kb = 0; kb < KD / 16; ++kb) {
+            const float4 a4 =
+                *reinterpret_cast<const float4*>(X + (16 * wave + l16) * LD + 16 * kb + 4 * lg);
+            float4 b4[4];
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt)
+                b4[jt] = *reinterpret_cast<const float4*>(Y + (16 * jt + l16) * LD + 16 * kb + 4 * lg);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a = sign * (e == 0 ? a4.x : e == 1 ? a4.y : e == 2 ? a4.z : a4.w);
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt) {
+                    const float bv = e == 0 ? b4[jt].x : e == 1 ? b4[jt].y : e == 2 ? b4[jt].z : b4[jt].w;
+                    acc[jt] = MF::mma(a, bv, acc[jt]);
+                }
+            }
+        }
+    };
+
     f32x4 dQa[4][DT], dKa[4][DT], P1[4][DT], P2[4][DT];
     f32x4 cA[4], cL[4], cK[4];   // C x C tiles: dA, dL, K K^T (row tile = wave)
 
-    // phase 1: slot0 = Vt, slot1 = dO, slot2 = Q
-    {
+    // phase 1: slot0 = Vt, slot1 = dO, slot2 = Q.  The three fetches are in
+    // flight together for bf16 inputs; fp32 inputs stage one tile at a time
+    // (three fp32 tiles in registers at once overflow the register file).
+    __syncthreads();
+    if constexpr (sizeof(E) == 2) {
         Tile<float, DV, LD> t0_;
         Tile<E, DV, LD> t1_;
         Tile<E, DK, LD> t2_;
         t0_.fetch(Vts + chn * CH * DV, DV, n, tid);
         t1_.fetch(dO + tok0 * DV, (size_t)H * DV, n, tid);
         t2_.fetch(q + tok0 * DK, (size_t)H * DK, n, tid);
-        __syncthreads();
         t0_.commit(slot0, tid);
         t1_.commit(slot1, tid);
         t2_.commit(slot2, tid);
+    } else {
+        stage<DV, LD>(slot0, Vts + chn * CH * DV, DV, n, tid);
+        stage<DV, LD>(slot1, dO + tok0 * DV, (size_t)H * DV, n, tid);
+        stage<DK, LD>(slot2, q + tok0 * DK, (size_t)H * DK, n, tid);
     }
     __syncthreads();
     // dA = dO Vt^T (lower triangle with the diagonal kept below)
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) cA[jt] = zero4();
-    for (int kc = lg; kc < DV; kc += 4) {
-        const float a = slot1[(16 * wave + l16) * LD + kc];
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) cA[jt] = MF::mma(a, slot0[(16 * jt + l16) * LD + kc], cA[jt]);
-    }
+    cc_product(slot1, slot0, DV, 1.f, cA);
     state_product(slot1, S0, P1);   // dO S0^T
     state_product(slot1, M0, P2);   // dO M0^T
 #pragma unroll
@@ -731,27 +826,20 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
     row_dot(P2, slot2, V(G_RX2));
 
     // phase 2: slot1 = dR, slot2 = K (Vt stays in slot0)
-    {
+    if constexpr (sizeof(E) == 2) {
         Tile<float, DV, LD> t1_;
         Tile<E, DK, LD> t2_;
         t1_.fetch(dv + tok0 * DV, (size_t)H * DV, n, tid);
         t2_.fetch(k + tok0 * DK, (size_t)H * DK, n, tid);
         t1_.commit(slot1, tid);
         t2_.commit(slot2, tid);
+    } else {
+        stage<DV, LD>(slot1, dv + tok0 * DV, (size_t)H * DV, n, tid);
+        stage<DK, LD>(slot2, k + tok0 * DK, (size_t)H * DK, n, tid);
     }
     __syncthreads();
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) cL[jt] = cK[jt] = zero4();
-    for (int kc = lg; kc < DV; kc += 4) {
-        const float a = slot1[(16 * wave + l16) * LD + kc];
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) cL[jt] = MF::mma(-a, slot0[(16 * jt + l16) * LD + kc], cL[jt]);
-    }
-    for (int kd = lg; kd < DK; kd += 4) {
-        const float a = slot2[(16 * wave + l16) * LD + kd];
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) cK[jt] = MF::mma(a, slot2[(16 * jt + l16) * LD + kd], cK[jt]);
-    }
+    cc_product(slot1, slot0, DV, -1.f, cL);
+    cc_product(slot2, slot2, DK, 1.f, cK);
     state_product(slot1, S0, P1);   // dR S0^T
     state_product(slot1, M0, P2);   // dR M0^T
 #pragma unroll
@@ -784,13 +872,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
     stage<DK, LD>(slot1, q + tok0 * DK, (size_t)H * DK, n, tid);
     __syncthreads();
     f32x4 cQ[4];
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) cQ[jt] = zero4();
-    for (int kd = lg; kd < DK; kd += 4) {
-        const float a = slot1[(16 * wave + l16) * LD + kd];
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) cQ[jt] = MF::mma(a, slot2[(16 * jt + l16) * LD + kd], cQ[jt]);
-    }
+    cc_product(slot1, slot2, DK, 1.f, cQ);
     // dGamma from A (dA o Q Khat^T) now, G_L = dL o (P Khat^T) into Cm2 for the
     // one-row shift; dA o Gamma into Cm1, dL o Gamma^- into slot0 (Vt is done)
     float* dAG = Cm1;
@@ -830,30 +912,43 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
     for (int it = 0; it < 4; ++it)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) P1[it][dt] = dKh[it][dt] = zero4();
-    for (int kr = lg; kr < CH; kr += 4) {
-        const float ek = V(G_E)[kr];
-        const float ak = V(G_A)[kr];
-        float kh[DT], qv[DT], kv[DT];
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const int d = 16 * (wave * DT + dt) + l16;
-            kv[dt] = slot2[kr * LD + d];
-            kh[dt] = ek * kv[dt];
-            qv[dt] = slot1[kr * LD + d];
-        }
+    // k runs over the chunk rows in the k-permuted order 16 kb + 4 lg + e:
+    // row reads of dAG, dLG as 16-byte vectors, column reads and the K, Q
+    // rows as single values (both conflict-free with row strides 4 mod 32)
+    for (int kb = 0; kb < CH / 16; ++kb) {
+        float4 ag4[4], lg4[4];
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            const int i = 16 * it + l16;
-            const float aAG = dAG[i * LDC + kr];      // dAG[i][k]
-            const float aAGt = dAG[kr * LDC + i];     // dAG^T[i][k]
-            const float aLGt = dLG[kr * LDC + i];     // dLG^T[i][k]
-            const float aLG = dLG[i * LDC + kr];      // dLG[i][k]
+            ag4[it] = *reinterpret_cast<const float4*>(dAG + (16 * it + l16) * LDC + 16 * kb + 4 * lg);
+            lg4[it] = *reinterpret_cast<const float4*>(dLG + (16 * it + l16) * LDC + 16 * kb + 4 * lg);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int kr = 16 * kb + 4 * lg + e;
+            const float ek = V(G_E)[kr];
+            const float ak = V(G_A)[kr];
+            float kh[DT], qv[DT], kv[DT];
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                dQa[it][dt] = MF::mma(aAG, kh[dt], dQa[it][dt]);
-                dKh[it][dt] = MF::mma(aAGt, qv[dt], dKh[it][dt]);
-                dKh[it][dt] = MF::mma(aLGt, ak * kv[dt], dKh[it][dt]);
-                P1[it][dt] = MF::mma(aLG, kh[dt], P1[it][dt]);
+                const int d = 16 * (wave * DT + dt) + l16;
+                kv[dt] = slot2[kr * LD + d];
+                kh[dt] = ek * kv[dt];
+                qv[dt] = slot1[kr * LD + d];
+            }
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int i = 16 * it + l16;
+                const float aAG = e == 0 ? ag4[it].x : e == 1 ? ag4[it].y : e == 2 ? ag4[it].z : ag4[it].w;
+                const float aLG = e == 0 ? lg4[it].x : e == 1 ? lg4[it].y : e == 2 ? lg4[it].z : lg4[it].w;
+                const float aAGt = dAG[kr * LDC + i];     // dAG^T[i][k]
+                const float aLGt = dLG[kr * LDC + i];     // dLG^T[i][k]
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    dQa[it][dt] = MF::mma(aAG, kh[dt], dQa[it][dt]);
+                    dKh[it][dt] = MF::mma(aAGt, qv[dt], dKh[it][dt]);
+                    dKh[it][dt] = MF::mma(aLGt, ak * kv[dt], dKh[it][dt]);
+                    P1[it][dt] = MF::mma(aLG, kh[dt], P1[it][dt]);
+                }
             }
         }
     }
@@ -920,11 +1015,13 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
     }
     __syncthreads();
     // d(ab1)_i also reaches b_{i-1} through alpha_i; the last row's scalars
-    if (tid == 0) {
-        for (int i = 1; i < n; ++i) V(G_DB)[i - 1] += V(G_RY2)[i] * V(G_A)[i];
-        V(G_DAB)[n - 1] += scal[0];
-        V(G_DB)[n - 1] -= scal[1];
-        V(G_DMB)[n - 1] += scal[2];
+    for (int i = tid; i < n; i += NT) {
+        if (i + 1 < n) V(G_DB)[i] += V(G_RY2)[i + 1] * V(G_A)[i + 1];
+        if (i == n - 1) {
+            V(G_DAB)[i] += scal[0];
+            V(G_DB)[i] -= scal[1];
+            V(G_DMB)[i] += scal[2];
+        }
     }
     // m table and the column recursions (thread j < n)
     if (tid < CH) {
@@ -974,27 +1071,27 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
         V(G_DM)[i] += sm;
     }
     __syncthreads();
-    if (tid == 0) {
-        // b_i = alpha_i b_{i-1} + beta_i mubar_i
-        for (int i = n - 1; i >= 0; --i) {
-            const float g = V(G_DB)[i];
-            const float bp = i > 0 ? V(G_B)[i - 1] : 0.f;
-            V(G_DA)[i] += g * bp;
-            if (i > 0) V(G_DB)[i - 1] += g * V(G_A)[i];
-            V(G_DS)[i] += g * V(G_MB)[i];
-            V(G_DMB)[i] += g * V(G_S)[i];
-        }
-        // abar_i = alpha_i abar_{i-1},  mubar_i = mu_i mubar_{i-1}
-        for (int i = n - 1; i >= 0; --i) {
-            const float ga = V(G_DAB)[i];
-            const float gm = V(G_DMB)[i];
-            V(G_DA)[i] += ga * (i > 0 ? V(G_AB)[i - 1] : 1.f);
-            V(G_DM)[i] += gm * (i > 0 ? V(G_MB)[i - 1] : 1.f);
-            if (i > 0) {
-                V(G_DAB)[i - 1] += ga * V(G_A)[i];
-                V(G_DMB)[i - 1] += gm * V(G_M)[i];
-            }
-        }
+    if (wave == 0) {
+        // Through b_i = alpha_i b_{i-1} + beta_i mubar_i: the total gradient of
+        // b_i is db_i + alpha_{i+1} (total of b_{i+1}), a suffix recursion; then
+        // abar_i = alpha_i abar_{i-1} and mubar_i = mu_i mubar_{i-1} likewise.
+        // Rows >= n carry nothing (their seeds are zero and the chain is cut).
+        const int i = lane;
+        const bool in = i < n;
+        const float anext = i + 1 < n ? V(G_A)[i + 1] : 0.f;
+        const float mnext = i + 1 < n ? V(G_M)[i + 1] : 0.f;
+        const float gb = suffix_affine(anext, in ? V(G_DB)[i] : 0.f, lane);
+        const float bp = i > 0 ? V(G_B)[i - 1] : 0.f;
+        float da = V(G_DA)[i] + gb * bp;
+        const float ds = V(G_DS)[i] + gb * V(G_MB)[i];
+        const float gmb0 = (in ? V(G_DMB)[i] : 0.f) + gb * V(G_S)[i];
+        const float gab = suffix_affine(anext, in ? V(G_DAB)[i] : 0.f, lane);
+        const float gmb = suffix_affine(mnext, in ? gmb0 : 0.f, lane);
+        da += gab * (i > 0 ? V(G_AB)[i - 1] : 1.f);
+        const float dm = V(G_DM)[i] + gmb * (i > 0 ? V(G_MB)[i - 1] : 1.f);
+        V(G_DA)[i] = da;
+        V(G_DS)[i] = ds;
+        V(G_DM)[i] = dm;
     }
     __syncthreads();
     for (int i = tid; i < n; i += NT) {
