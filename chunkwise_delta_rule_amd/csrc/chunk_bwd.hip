@@ -31,6 +31,10 @@
 // gamma_{i,j} = alpha_i gamma_{i-1,j} + beta_i m_{i,j}, m_{i,j} = mu_i m_{i-1,j})
 // and the direct uses of eta (Khat, ws, wm) and alpha (P, ab1).
 //
+// This version takes nothing from the forward call: it recomputes Vt (the
+// re-scan below runs the forward's solve again) and keeps each chunk's entry
+// state and exit-state gradients in its workspace only while it runs.
+//
 // Kernels, in launch order (after chunk_prep_kernel has written T, A and the
 // coefficient rows of every chunk):
 //   bwd_scan_kernel     one workgroup per (b, h, 64 value columns), chunks last
