@@ -75,7 +75,7 @@ GATE_TAU = (2048 / 16) ** 0.5            # the temperature sqrt(d_in / h) at d_i
 # 131,072.0).  An entry that covers several kernels of one call sums their dispatches.
 # Figures and commands: profiles/chunk_fwd_fused_B8H16T4096d128.md,
 # profiles/chunk_fwd_split_B8H16T4096d128.md, profiles/decode_step_N256H16d128.md and
-# profiles/gates_from_logits_B8H16T4096.md.
+# profiles/gates_from_logits_B8H16T4096.md and profiles/chunk_bwd_B8H16T4096d128.md.
 # A kernel whose sources changed reports traffic null.
 FETCH_FACTOR = 262144.0 / 131093.9
 WRITE_FACTOR = 131072.0 / 131072.0
@@ -95,6 +95,14 @@ TRAFFIC = {
     "decode_step_kernel": dict(sources=("decode.hip", "mfma.hpp"), fetch_kib=264109.0,
                                write_kib=525523.8, sha256="8fa39113008b99235e1abe57028f0d81"
                                "9b837f475aa87000a6b4e46e3ea6c4e5"),
+    # chunk_prep_kernel (134,557.9 / 144,101.2) + bwd_scan_kernel (471,264.1 / 1,310,723.9) +
+    # bwd_rescan_kernel (274,559.5 / 1,310,720.5) + bwd_grad_kernel (3,453,358.1 / 982,657.3):
+    # one mdn_chunk_bwd call
+    "chunk_bwd": dict(sources=("chunk_bwd.hip", "chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
+                      fetch_kib=134557.9 + 471264.1 + 274559.5 + 3453358.1,
+                      write_kib=144101.2 + 1310723.9 + 1310720.5 + 982657.3,
+                      sha256="6c75187aa75d4ad6450fa082c40bcdf7"
+                      "1cf7ab7c4821ae8842e177540bd3530c"),
     "gates_kernel": dict(sources=("gates.hip",), fetch_kib=4114.0, write_kib=8192.0,
                          sha256="2bde382d2f924a1318325130cdb94dab"
                          "7d2b47dcae9f102ec3b939b9dde52ce6"),
@@ -317,7 +325,7 @@ def bench_backward(args, torch, si, mdn, cfg, inp):
             "us_per_step": us, "tokens_per_s": B * T / (us * 1e-6), "steps_timed": steps,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP32_MFMA / 1e12,
                          "unit": "TFLOP/s", "frac": flop / (us * 1e-6) / PEAK_FP32_MFMA,
-                         "traffic": None, "algorithmic_flop": flop,
+                         "traffic": traffic_bytes("chunk_bwd"), "algorithmic_flop": flop,
                          "algorithmic_bytes": BYTES_BWD * toh,
                          "hbm_frac": BYTES_BWD * toh / (us * 1e-6) / PEAK_HBM_BPS}}
 
