@@ -168,7 +168,7 @@ template <typename E, int DK, int DV>
 __global__ __launch_bounds__(NT) void bwd_scan_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ dO,
     const E* __restrict__ Tw, const E* __restrict__ Aw, const float* __restrict__ Vw,
-    const float* dST, const float* dMT, float* __restrict__ Hd, float* __restrict__ dv,
+    const float* dST, const float* dMT, E* __restrict__ Hd, float* __restrict__ dv,
     float* dS0, float* dM0, int T, int H, int NC)
 {
     constexpr int TV = 64;
@@ -247,14 +247,14 @@ __global__ __launch_bounds__(NT) void bwd_scan_kernel(
 
         // the exit-state gradients of this chunk, for bwd_grad_kernel
         {
-            float* hd = Hd + chn * 2 * DK * DV;
+            E* hd = Hd + chn * 2 * DK * DV;
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const size_t x = (size_t)(16 * rt + 4 * lg + r) * DV + wcol + l16;
-                    hd[x] = Sa[rt][r];
-                    hd[(size_t)DK * DV + x] = Ma[rt][r];
+                    hd[x] = to_elem<E>(Sa[rt][r]);
+                    hd[(size_t)DK * DV + x] = to_elem<E>(Ma[rt][r]);
                 }
         }
 
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(NT) void bwd_scan_kernel(
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(NT) void bwd_rescan_kernel(
     const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ Tw,
-    const float* __restrict__ Vw, const float* S0, const float* M0, float* __restrict__ Hs,
+    const float* __restrict__ Vw, const float* S0, const float* M0, E* __restrict__ Hs,
     float* __restrict__ Vts, int T, int H, int NC)
 {
     constexpr int TV = 64;
@@ -450,14 +450,14 @@ __global__ __launch_bounds__(NT) void bwd_rescan_kernel(
         if (c + 1 < NC) fetch(c + 1);
 
         {
-            float* hs = Hs + chn * 2 * DK * DV;
+            E* hs = Hs + chn * 2 * DK * DV;
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const size_t x = (size_t)(16 * rt + 4 * lg + r) * DV + wcol + l16;
-                    hs[x] = Sa[rt][r];
-                    hs[(size_t)DK * DV + x] = Ma[rt][r];
+                    hs[x] = to_elem<E>(Sa[rt][r]);
+                    hs[(size_t)DK * DV + x] = to_elem<E>(Ma[rt][r]);
                 }
         }
 
@@ -574,8 +574,8 @@ constexpr int G_RED = 22;                                    // 2 rows: reductio
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(NT) void bwd_grad_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ dO,
-    const float* __restrict__ dv, const float* __restrict__ Vts, const float* __restrict__ Hs,
-    const float* __restrict__ Hd, const float* __restrict__ alpha, const float* __restrict__ mu,
+    const float* __restrict__ dv, const float* __restrict__ Vts, const E* __restrict__ Hs,
+    const E* __restrict__ Hd, const float* __restrict__ alpha, const float* __restrict__ mu,
     const float* __restrict__ eta, const float* __restrict__ beta, float* __restrict__ dq,
     float* __restrict__ dk, float* __restrict__ dalpha, float* __restrict__ dmu,
     float* __restrict__ deta, float* __restrict__ dbeta, int T, int H, int NC)
@@ -607,10 +607,28 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
     const int n = min(CH, T - t0);
     const size_t tok0 = ((size_t)b * T + t0) * H + h;
     const size_t chn = (size_t)bh * NC + c;
-    const float* S0 = Hs + chn * 2 * DK * DV;
-    const float* M0 = S0 + DK * DV;
-    const float* dS = Hd + chn * 2 * DK * DV;
-    const float* dM = dS + DK * DV;
+    // the chunk's states, stored in the I/O type (bf16 states are the rounding
+    // the forward's MFMA operands make too)
+    const E* S0 = Hs + chn * 2 * DK * DV;
+    const E* M0 = S0 + DK * DV;
+    const E* dS = Hd + chn * 2 * DK * DV;
+    const E* dM = dS + DK * DV;
+    constexpr int SV = 16 / sizeof(E);   // state values per 16-byte load
+    auto unpack = [](const uint4& w, float* f) {
+        if constexpr (sizeof(E) == 2) {
+            const unsigned u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[2 * e] = __uint_as_float(u[e] << 16);
+                f[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+            }
+        } else {
+            f[0] = __uint_as_float(w.x);
+            f[1] = __uint_as_float(w.y);
+            f[2] = __uint_as_float(w.z);
+            f[3] = __uint_as_float(w.w);
+        }
+    };
     auto V = [&](int row) { return vec + row * CH; };
 
     // ---- gates, coefficient vectors, Gamma ----------------------------------
@@ -669,23 +687,31 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
     // fixed-order reduction over the four wavefronts)
     {
         float a0 = 0.f, a1 = 0.f, a2 = 0.f;
-        constexpr int NF = DK * DV / 4 / NT;   // 16-byte loads per thread and array
+        constexpr int NF = DK * DV / SV / NT;   // 16-byte loads per thread and array
         constexpr int BATCH = NF < 4 ? NF : 4;
         for (int u0 = 0; u0 < NF; u0 += BATCH) {
-            float4 s0[BATCH], m0[BATCH], ds[BATCH], dm[BATCH];
+            uint4 s0[BATCH], m0[BATCH], ds[BATCH], dm[BATCH];
 #pragma unroll
             for (int u = 0; u < BATCH; ++u) {
-                const int x = 4 * (tid + (u0 + u) * NT);
-                s0[u] = *reinterpret_cast<const float4*>(S0 + x);
-                m0[u] = *reinterpret_cast<const float4*>(M0 + x);
-                ds[u] = *reinterpret_cast<const float4*>(dS + x);
-                dm[u] = *reinterpret_cast<const float4*>(dM + x);
+                const int x = SV * (tid + (u0 + u) * NT);
+                s0[u] = *reinterpret_cast<const uint4*>(S0 + x);
+                m0[u] = *reinterpret_cast<const uint4*>(M0 + x);
+                ds[u] = *reinterpret_cast<const uint4*>(dS + x);
+                dm[u] = *reinterpret_cast<const uint4*>(dM + x);
             }
 #pragma unroll
             for (int u = 0; u < BATCH; ++u) {
-                a0 += ds[u].x * s0[u].x + ds[u].y * s0[u].y + ds[u].z * s0[u].z + ds[u].w * s0[u].w;
-                a1 += ds[u].x * m0[u].x + ds[u].y * m0[u].y + ds[u].z * m0[u].z + ds[u].w * m0[u].w;
-                a2 += dm[u].x * m0[u].x + dm[u].y * m0[u].y + dm[u].z * m0[u].z + dm[u].w * m0[u].w;
+                float fs[SV], fm[SV], fd[SV], fe[SV];
+                unpack(s0[u], fs);
+                unpack(m0[u], fm);
+                unpack(ds[u], fd);
+                unpack(dm[u], fe);
+#pragma unroll
+                for (int e = 0; e < SV; ++e) {
+                    a0 += fd[e] * fs[e];
+                    a1 += fd[e] * fm[e];
+                    a2 += fe[e] * fm[e];
+                }
             }
         }
         for (int o = 32; o >= 1; o >>= 1) {
@@ -707,40 +733,46 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
     // For a C x DV row operand X in LDS and a DK x DV state St in HBM, the
     // product X St^T (C x DK): this wavefront's tiles, k over the DV columns
     // in the fp32 k-permuted order, 4 state values per 16-byte load.
-    auto state_product = [&](const float* X, const float* St, f32x4 (*acc)[DT]) {
+    auto state_product = [&](const float* X, const E* St, f32x4 (*acc)[DT]) {
+        // k order: block kb of KB = 4 SV columns, lane group lg takes columns
+        // KB kb + SV lg + e (e < SV) from one 16-byte load of the state row
+        constexpr int KB = 4 * SV;
 #pragma unroll
         for (int it = 0; it < 4; ++it)
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) acc[it][dt] = zero4();
         // this wavefront's rows of the state, all DV columns, loaded at once
-        float4 sva[DV / 16][DT];
+        uint4 sva[DV / KB][DT];
 #pragma unroll
-        for (int kb = 0; kb < DV / 16; ++kb)
+        for (int kb = 0; kb < DV / KB; ++kb)
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const int d = 16 * (wave * DT + dt) + l16;
                 sva[kb][dt] =
-                    *reinterpret_cast<const float4*>(St + (size_t)d * DV + 16 * kb + 4 * lg);
+                    *reinterpret_cast<const uint4*>(St + (size_t)d * DV + KB * kb + SV * lg);
             }
 #pragma unroll
-        for (int kb = 0; kb < DV / 16; ++kb) {
-            const float4* sv = sva[kb];
-            float4 xa[4];
+        for (int kb = 0; kb < DV / KB; ++kb) {
+            float sv[DT][SV];
 #pragma unroll
-            for (int it = 0; it < 4; ++it)
-                xa[it] = *reinterpret_cast<const float4*>(X + (16 * it + l16) * LD + 16 * kb + 4 * lg);
+            for (int dt = 0; dt < DT; ++dt) unpack(sva[kb][dt], sv[dt]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+            for (int h4 = 0; h4 < SV / 4; ++h4) {
+                float4 xa[4];
 #pragma unroll
-                for (int it = 0; it < 4; ++it) {
-                    const float a = e == 0 ? xa[it].x : e == 1 ? xa[it].y : e == 2 ? xa[it].z : xa[it].w;
+                for (int it = 0; it < 4; ++it)
+                    xa[it] = *reinterpret_cast<const float4*>(
+                        X + (16 * it + l16) * LD + KB * kb + SV * lg + 4 * h4);
 #pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) {
-                        const float bv = e == 0 ? sv[dt].x : e == 1 ? sv[dt].y
-                                       : e == 2 ? sv[dt].z : sv[dt].w;
-                        acc[it][dt] = MF::mma(a, bv, acc[it][dt]);
+                for (int e4 = 0; e4 < 4; ++e4)
+#pragma unroll
+                    for (int it = 0; it < 4; ++it) {
+                        const float a = e4 == 0 ? xa[it].x : e4 == 1 ? xa[it].y
+                                      : e4 == 2 ? xa[it].z : xa[it].w;
+#pragma unroll
+                        for (int dt = 0; dt < DT; ++dt)
+                            acc[it][dt] = MF::mma(a, sv[dt][4 * h4 + e4], acc[it][dt]);
                     }
-                }
             }
         }
     };
@@ -1117,7 +1149,8 @@ size_t chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, bool bf16)
     const size_t NC = ((size_t)T + CH - 1) / CH;
     const size_t nchunks = (size_t)B * H * NC;
     const size_t prep = nchunks * (2 * CH * CH * (bf16 ? 2 : 4) + NVEC * CH * 4);
-    return prep + nchunks * (4 * (size_t)Dk * Dv + (size_t)CH * Dv) * 4;
+    // state pairs in the I/O type, residuals in fp32
+    return prep + nchunks * (4 * (size_t)Dk * Dv * (bf16 ? 2 : 4) + (size_t)CH * Dv * 4);
 }
 
 template <typename E, int DK, int DV>
@@ -1138,10 +1171,10 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
     p += nchunks * CH * CH * sizeof(E);
     float* Vw = reinterpret_cast<float*>(p);
     p += nchunks * NVEC * CH * sizeof(float);
-    float* Hs = reinterpret_cast<float*>(p);
-    p += nchunks * 2 * DK * DV * sizeof(float);
-    float* Hd = reinterpret_cast<float*>(p);
-    p += nchunks * 2 * DK * DV * sizeof(float);
+    E* Hs = reinterpret_cast<E*>(p);
+    p += nchunks * 2 * DK * DV * sizeof(E);
+    E* Hd = reinterpret_cast<E*>(p);
+    p += nchunks * 2 * DK * DV * sizeof(E);
     float* Vts = reinterpret_cast<float*>(p);
 
     hipError_t err = launch_chunk_prepare(q, k, alpha, mu, eta, beta, B, T, H, DK,
