@@ -19,6 +19,7 @@ The same JSON line carries:
   kernels       the same record for every kernel of the step;
   split_path    the same forward through mdn_chunk_fwd_prepare + mdn_chunk_fwd_scan;
   forward.from_logits  mdn_gates_from_logits, then the four-gate forward on its gates;
+  forward.with_prologue_epilogue  mdn_qk_prologue, the forward, mdn_output_epilogue;
   forward       the whole step against both roofs;
   backward      mdn_chunk_bwd on the same layer (all gradients), against the fp32 MFMA peak;
   decode        the recurrent decode step at 256 sequences x 16 heads, d 128
@@ -59,6 +60,8 @@ STATE_BYTES_HEAD = 2 * D * D * 4         # S_T and M_T written once per (b, h)
 DEC_BYTES_HEAD = 4 * D * D * 4 + 3 * D * 2 + D * 2 + 3 * 4   # S, M in+out; q k v o; gates
 DEC_BYTES_HEAD_GDN = 2 * D * D * 4 + 3 * D * 2 + D * 2 + 2 * 4   # mu = 0: S only; two gates
 BYTES_GATES = 4 * 4 + 4 * 4              # four fp32 logits in, four fp32 gates out
+BYTES_PROLOGUE = 2 * D * 2 + 2 * D * 2   # q, k in and out (bf16)
+BYTES_EPILOGUE = 2 * D * 2 + D * 2       # o, gate in, y out (bf16)
 # backward (mdn_chunk_bwd), dense products per token and head: prepare 4 C d; reverse scan
 # 12 d^2 + 4 C d; re-scan 8 d^2 + 2 C d; per-chunk gradients 12 d^2 + 16 C d
 FLOP_BWD = 32 * D * D + 30 * C * D
@@ -201,6 +204,7 @@ def time_calls(torch, fns, steps):
 
 
 def bench_forward(args, torch, si, mdn):
+    import numpy as np
     cfg = si.CONFIGS[2]
     t0 = time.time()
     inp = si.make_forward(cfg)
@@ -295,6 +299,34 @@ def bench_forward(args, torch, si, mdn):
                           "us_per_step": gz_ms * 1e3, "tokens_per_s": tokens / (gz_ms * 1e-3),
                           "gates_us": g_ms * 1e3, "gates_GB_per_s": gbs}
     del plan_z, gates, zt
+    # the layer's elementwise steps around the core: the query correction and
+    # q, k normalisation before it, the gated RMSNorm after it
+    q_, k_ = plan.args[0], plan.args[1]
+    qn, kn = torch.empty_like(q_), torch.empty_like(k_)
+    dcorr = torch.full((cfg.H,), 0.5, dtype=f32, device="cuda")
+    gt = up(si.round_io(np.random.default_rng(5).standard_normal(plan.O.shape), "bf16"), bf)
+    wn = torch.ones(cfg.Dv, dtype=f32, device="cuda")
+    yo = torch.empty_like(plan.O)
+    pro = lambda: mdn.qk_prologue(q_, k_, dcorr, out=(qn, kn))
+    epi = lambda: mdn.output_epilogue(plan.O, gt, wn, out=yo)
+    plan_n = mdn.ChunkPlan(qn, kn, *plan.args[2:6])
+    settle(torch, [pro, plan_n.forward, epi], args.settle)
+    (p_ms, _, e_ms), layer_ms = time_calls(torch, [pro, plan_n.forward, epi], args.steps)
+    p_gbs = BYTES_PROLOGUE * toh / (p_ms * 1e-3) / 1e9
+    e_gbs = BYTES_EPILOGUE * toh / (e_ms * 1e-3) / 1e9
+    log(f"prologue {p_ms * 1e3:.1f} us ({p_gbs:.0f} GB/s), epilogue {e_ms * 1e3:.1f} us "
+        f"({e_gbs:.0f} GB/s); prologue + forward + epilogue {layer_ms * 1e3:.1f} us/step")
+    kernels["qk_prologue_kernel"] = roofline_of("qk_prologue_kernel", p_ms * 1e3, 0,
+                                                BYTES_PROLOGUE * toh)
+    kernels["output_epilogue_kernel"] = roofline_of("output_epilogue_kernel", e_ms * 1e3, 0,
+                                                    BYTES_EPILOGUE * toh)
+    fwd["with_prologue_epilogue"] = {
+        "workload": "mdn_qk_prologue (d = 0.5 per head), the forward on its outputs, "
+                    "mdn_output_epilogue (gate ~ N(0, 1), unit weight)",
+        "us_per_step": layer_ms * 1e3, "tokens_per_s": tokens / (layer_ms * 1e-3),
+        "prologue_us": p_ms * 1e3, "prologue_GB_per_s": p_gbs,
+        "epilogue_us": e_ms * 1e3, "epilogue_GB_per_s": e_gbs}
+    del plan_n, qn, kn, gt, yo
     return cfg, inp, step_ms, kernels, roofline, fwd, split
 
 

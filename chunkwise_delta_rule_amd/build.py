@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmdn.so")
-SOURCES = ["api.hip", "chunk_bwd.hip", "chunk_fwd.hip", "chunk_fused.hip", "decode.hip", "gates.hip"]
+SOURCES = ["api.hip", "chunk_bwd.hip", "chunk_fwd.hip", "chunk_fused.hip", "decode.hip", "gates.hip", "layer_io.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <cmath>
+#include <initializer_list>
 
 #include "../../include/libmdn.h"
 
@@ -34,6 +35,11 @@ hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const f
                             float* deta, float* dbeta, float* dS0, float* dM0, int B, int T,
                             int H, int Dk, int Dv, bool bf16, void* workspace, hipStream_t stream);
 hipError_t launch_state_copy(const float* src, float* dst, size_t count, hipStream_t stream);
+hipError_t launch_qk_prologue(const void* q, const void* k, const float* dcorr, void* qo,
+                              void* ko, size_t rows, int H, int D, bool bf16, float eps,
+                              hipStream_t stream);
+hipError_t launch_output_epilogue(const void* o, const void* g, const float* w, void* y,
+                                  size_t rows, int D, bool bf16, float eps, hipStream_t stream);
 hipError_t launch_gates(const float* z_eta, const float* z_alpha, const float* z_beta,
                         const float* z_mu, size_t n, float tau, float s, float a, float b,
                         float log_mu_min, float* alpha, float* mu, float* eta, float* beta,
@@ -418,6 +424,70 @@ mdn_status mdn_chunk_bwd(const void* q, const void* k, const void* v, const floa
     const hipError_t err = mdn::launch_chunk_bwd(
         q, k, v, alpha, mu, eta, beta, S0, M0, dO, dS_T, dM_T, dq, dk, dv, dalpha, dmu_w, deta,
         dbeta_w, dS0, dM0, B, T, H, Dk, Dv, dt == MDN_BF16, workspace, stream);
+    return err == hipSuccess ? MDN_OK : MDN_ERR_HIP;
+}
+
+static mdn_status check_rows(size_t rows, int H, int D, mdn_dtype dt, float eps, size_t* bytes)
+{
+    if (H < 0) return MDN_ERR_SHAPE;
+    if (!head_dim_ok(D)) return MDN_ERR_UNSUPPORTED;
+    if (dt != MDN_F32 && dt != MDN_BF16) return MDN_ERR_UNSUPPORTED;
+    if (!std::isfinite(eps) || !(eps > 0.f)) return MDN_ERR_UNSUPPORTED;
+    size_t n;
+    if (!mul_ok(rows, (size_t)H, (size_t)D, dt == MDN_BF16 ? 2 : 4, &n)) return MDN_ERR_SHAPE;
+    *bytes = n;
+    return MDN_OK;
+}
+
+// true when `out` overlaps none of `others`
+static bool disjoint(const Span& out, std::initializer_list<Span> others)
+{
+    for (const Span& x : others)
+        if (overlap(out, x)) return false;
+    return true;
+}
+
+mdn_status mdn_qk_prologue(const void* q, const void* k, const float* d, void* q_out,
+                           void* k_out, size_t rows, int H, int Dk, float eps, mdn_dtype dt,
+                           hipStream_t stream)
+{
+    size_t bytes = 0;
+    const mdn_status st = check_rows(rows, H, Dk, dt, eps, &bytes);
+    if (st != MDN_OK) return st;
+    if (bytes == 0) return MDN_OK;
+    if (!q || !k || !q_out || !k_out) return MDN_ERR_NULL;
+    for (const void* p : {(const void*)q, (const void*)k, (const void*)d, (const void*)q_out,
+                          (const void*)k_out})
+        if (p && !aligned16(p)) return MDN_ERR_ALIGN;
+    const Span sq = span(q, bytes), sk = span(k, bytes), sd = span(d, (size_t)H * 4),
+               sqo = span(q_out, bytes), sko = span(k_out, bytes);
+    // q_out may be q itself and k_out k itself; nothing else may overlap
+    if (!(q_out == q ? disjoint(sqo, {sk, sd, sko}) : disjoint(sqo, {sq, sk, sd, sko})))
+        return MDN_ERR_ALIAS;
+    if (!(k_out == k ? disjoint(sko, {sq, sd}) : disjoint(sko, {sq, sk, sd})))
+        return MDN_ERR_ALIAS;
+    const hipError_t err = mdn::launch_qk_prologue(q, k, d, q_out, k_out, rows * (size_t)H, H,
+                                                   Dk, dt == MDN_BF16, eps, stream);
+    return err == hipSuccess ? MDN_OK : MDN_ERR_HIP;
+}
+
+mdn_status mdn_output_epilogue(const void* o, const void* g, const float* w, void* y,
+                               size_t rows, int H, int Dv, float eps, mdn_dtype dt,
+                               hipStream_t stream)
+{
+    size_t bytes = 0;
+    const mdn_status st = check_rows(rows, H, Dv, dt, eps, &bytes);
+    if (st != MDN_OK) return st;
+    if (bytes == 0) return MDN_OK;
+    if (!o || !g || !y) return MDN_ERR_NULL;
+    for (const void* p : {(const void*)o, (const void*)g, (const void*)w, (const void*)y})
+        if (p && !aligned16(p)) return MDN_ERR_ALIGN;
+    const Span so = span(o, bytes), sg = span(g, bytes), sw = span(w, (size_t)Dv * 4),
+               sy = span(y, bytes);
+    // y may be o itself; nothing else may overlap it
+    if (!(y == o ? disjoint(sy, {sg, sw}) : disjoint(sy, {so, sg, sw}))) return MDN_ERR_ALIAS;
+    const hipError_t err = mdn::launch_output_epilogue(o, g, w, y, rows * (size_t)H, Dv,
+                                                       dt == MDN_BF16, eps, stream);
     return err == hipSuccess ? MDN_OK : MDN_ERR_HIP;
 }
 

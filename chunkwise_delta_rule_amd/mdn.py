@@ -38,7 +38,8 @@ STATUS_NAMES = {
 EXPORTED = ("mdn_chunk_fwd_workspace_bytes", "mdn_chunk_fwd_split_workspace_bytes",
             "mdn_chunk_fwd", "mdn_chunk_fwd_prepare",
             "mdn_chunk_fwd_scan", "mdn_decode_step", "mdn_gates_from_logits",
-            "mdn_chunk_bwd_workspace_bytes", "mdn_chunk_bwd", "mdn_status_string")
+            "mdn_chunk_bwd_workspace_bytes", "mdn_chunk_bwd", "mdn_qk_prologue",
+            "mdn_output_epilogue", "mdn_status_string")
 
 
 class GateParams(ctypes.Structure):
@@ -82,6 +83,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mdn_chunk_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.mdn_chunk_bwd.restype = I
     lib.mdn_chunk_bwd.argtypes = [P] * 21 + [I] * 7 + [P, S, P]
+    F = ctypes.c_float
+    lib.mdn_qk_prologue.restype = I
+    lib.mdn_qk_prologue.argtypes = [P] * 5 + [S, I, I, F, I, P]
+    lib.mdn_output_epilogue.restype = I
+    lib.mdn_output_epilogue.argtypes = [P] * 4 + [S, I, I, F, I, P]
     lib.mdn_gates_from_logits.restype = I
     lib.mdn_gates_from_logits.argtypes = [P] * 4 + [S, GateParams] + [P] * 4 + [P]
     lib.mdn_status_string.restype = ctypes.c_char_p
@@ -351,3 +357,50 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
     if st != 0:
         raise MdnError(st, "mdn_chunk_bwd")
     return out
+
+
+def qk_prologue(q: torch.Tensor, k: torch.Tensor, d: Optional[torch.Tensor] = None, *,
+                eps: float = 1e-6, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None
+                ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Comba correction q - d_h k and L2 normalisation of q and k (per token
+    and head).  q, k [..., H, Dk] contiguous, one dtype; d [H] float32 or
+    None.  Returns (q_out, k_out); pass out=(q, k) to work in place."""
+    lib = load_library()
+    dev = q.device
+    shape = tuple(q.shape)
+    H, Dk = shape[-2], shape[-1]
+    rows = q.numel() // (H * Dk) if q.numel() else 0
+    _check(q, "q", shape, q.dtype, dev)
+    _check(k, "k", shape, q.dtype, dev)
+    if d is not None:
+        _check(d, "d", (H,), torch.float32, dev)
+    qo, ko = out if out is not None else (torch.empty_like(q), torch.empty_like(k))
+    _check(qo, "q_out", shape, q.dtype, dev)
+    _check(ko, "k_out", shape, q.dtype, dev)
+    st = lib.mdn_qk_prologue(_ptr(q), _ptr(k), _ptr(d), _ptr(qo), _ptr(ko), rows, H, Dk, eps,
+                             _dtype_code(q.dtype), _stream(dev))
+    if st != 0:
+        raise MdnError(st, "mdn_qk_prologue")
+    return qo, ko
+
+
+def output_epilogue(o: torch.Tensor, g: torch.Tensor, w: Optional[torch.Tensor] = None, *,
+                    eps: float = 1e-6, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = sigmoid(g) * RMSNorm(o) * w per token and head over Dv.  o, g
+    [..., H, Dv] contiguous, one dtype; w [Dv] float32 or None."""
+    lib = load_library()
+    dev = o.device
+    shape = tuple(o.shape)
+    H, Dv = shape[-2], shape[-1]
+    rows = o.numel() // (H * Dv) if o.numel() else 0
+    _check(o, "o", shape, o.dtype, dev)
+    _check(g, "g", shape, o.dtype, dev)
+    if w is not None:
+        _check(w, "w", (Dv,), torch.float32, dev)
+    y = out if out is not None else torch.empty_like(o)
+    _check(y, "y", shape, o.dtype, dev)
+    st = lib.mdn_output_epilogue(_ptr(o), _ptr(g), _ptr(w), _ptr(y), rows, H, Dv, eps,
+                                 _dtype_code(o.dtype), _stream(dev))
+    if st != 0:
+        raise MdnError(st, "mdn_output_epilogue")
+    return y

@@ -219,6 +219,36 @@ mdn_status mdn_chunk_bwd(const void* q, const void* k, const void* v, const floa
                          size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The elementwise steps around the core, each one pass over HBM ("MDN:
+ * Parallelizing Stepwise Momentum for Delta Linear Attention" (slides), frame
+ * "The memory sits inside a familiar language-model block"; the paper's
+ * Sec. 3.3 and Fig. 3).
+ *
+ * mdn_qk_prologue: the Comba query correction and the L2 normalisation of
+ * queries and keys, per token and head over Dk:
+ *     q' = q - d_h k,   q_out = q' / sqrt(|q'|^2 + eps),   k_out = k / sqrt(|k|^2 + eps)
+ *   q, k, q_out, k_out [rows, H, Dk] (dtype dt; rows = tokens, e.g. B T);
+ *   d [H] float32 or NULL (no correction).
+ * mdn_output_epilogue: the gated output norm before the output projection,
+ * per token and head over Dv:
+ *     y = sigmoid(g) * (o / sqrt(mean(o^2) + eps)) * w
+ *   o, g, y [rows, H, Dv] (dtype dt; g is the caller's gate projection);
+ *   w [Dv] float32 shared by the heads, or NULL (ones).
+ * Dk, Dv in {64, 128}; eps finite and > 0 (MDN_ERR_UNSUPPORTED otherwise).
+ * Device pointers aligned to 16 bytes.  An output may be its own input
+ * exactly (q_out = q, k_out = k, y = o: in place) and must overlap nothing
+ * else (MDN_ERR_ALIAS).  rows = 0 or H = 0 launches nothing.  Enqueued on
+ * `stream`; the caller owns every buffer.
+ */
+mdn_status mdn_qk_prologue(const void* q, const void* k, const float* d, void* q_out,
+                           void* k_out, size_t rows, int H, int Dk, float eps, mdn_dtype dt,
+                           hipStream_t stream);
+
+mdn_status mdn_output_epilogue(const void* o, const void* g, const float* w, void* y,
+                               size_t rows, int H, int Dv, float eps, mdn_dtype dt,
+                               hipStream_t stream);
+
+/*
  * MDN's coupled gate parameterisation ("MDN: Parallelizing Stepwise Momentum
  * for Delta Linear Attention" (slides), frame "Coupled gates restrict the
  * spectral region", the paper's Sec. 3.3), from logits the caller computes

@@ -237,3 +237,31 @@ def gates_from_logits(z_eta, z_alpha, z_beta, z_mu, *, tau: float, s: float, a: 
     beta = sig * beta_max
     mu = np.exp(np.maximum(f(z(z_mu)), log_mu_min))
     return alpha, mu, eta, beta
+
+
+def qk_prologue(q, k, d=None, *, eps: float):
+    """The Comba query correction and L2 normalisation around the core
+    ([MDN slides] frame "The memory sits inside a familiar language-model
+    block"; [MDN notes] Sec. 2.9), in float64, per token and head over the
+    last axis: q' = q - d_h k, q' / sqrt(|q'|^2 + eps), k / sqrt(|k|^2 + eps).
+    q, k [..., H, Dk]; d [H] or None."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    if d is not None:
+        q = q - np.asarray(d, dtype=np.float64)[:, None] * k
+    nq = np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + eps)
+    nk = np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + eps)
+    return q / nq, k / nk
+
+
+def output_epilogue(o, g, w=None, *, eps: float):
+    """The gated output norm before the output projection ([MDN notes]
+    Sec. 2.9: y = W_o[sigmoid(W_g x) * RMSNorm(o)]), in float64 per token and
+    head over the last axis: sigmoid(g) * o / sqrt(mean(o^2) + eps) * w."""
+    o = np.asarray(o, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    y = (1.0 / (1.0 + np.exp(-g))) * (o / rms)
+    if w is not None:
+        y = y * np.asarray(w, dtype=np.float64)
+    return y

@@ -505,6 +505,48 @@ def pin_backward_finite_differences(lib):
     _fd_check(lib, inp, rng.standard_normal((B, T, H, Dv)), None, None, col_block=16)
 
 
+def pin_layer_prologue_epilogue(lib):
+    """The elementwise steps around the core ([MDN notes] Sec. 2.9):
+      - prologue: q = (3, 4, 0, ..) normalises to (0.6, 0.8, 0, ..) as eps -> 0,
+        and |x / sqrt(|x|^2 + eps)|^2 = |x|^2 / (|x|^2 + eps) exactly; the
+        correction with d_h = 1 and q = k gives a zero query; d = 0 is no
+        correction; the output keeps the direction of q - d_h k;
+      - epilogue: o = (3, 4) has mean square 12.5, so g = 0 and w = (1, 2)
+        give (0.5 * 3 / sqrt(12.5 + eps), 0.5 * 2 * 4 / sqrt(12.5 + eps));
+        sigmoid(g) -> 1 for large g; RMSNorm is invariant to o -> c o (c > 0)
+        as eps -> 0."""
+    del lib
+    q = np.zeros((1, 1, 8))
+    q[0, 0, :2] = (3.0, 4.0)
+    qo, ko = oracle.qk_prologue(q, q, None, eps=0.0)
+    assert _rel(qo[0, 0, :2], [0.6, 0.8]) < 1e-15 and _rel(ko, qo) < 1e-15
+    rng = np.random.default_rng(51)
+    x = rng.standard_normal((5, 3, 16))
+    kx = rng.standard_normal((5, 3, 16))
+    eps = 0.37
+    qo, ko = oracle.qk_prologue(x, kx, None, eps=eps)
+    n2 = np.sum(x * x, axis=-1)
+    assert _rel(np.sum(qo * qo, axis=-1), n2 / (n2 + eps)) < 1e-14
+    d = np.array([1.0, 0.0, -0.5])
+    qo, _ = oracle.qk_prologue(kx, kx, d, eps=1e-6)
+    assert np.max(np.abs(qo[:, 0])) < 1e-12                     # d_h = 1, q = k
+    qd, _ = oracle.qk_prologue(x, kx, d, eps=1e-9)
+    want = x - d[:, None] * kx
+    cos = np.sum(qd * want, -1) / (np.linalg.norm(qd, axis=-1) * np.linalg.norm(want, axis=-1))
+    assert np.max(np.abs(cos - 1.0)) < 1e-12
+    q0, _ = oracle.qk_prologue(x, kx, np.zeros(3), eps=eps)
+    q1, _ = oracle.qk_prologue(x, kx, None, eps=eps)
+    assert _rel(q0, q1) == 0.0
+    y = oracle.output_epilogue([[3.0, 4.0]], [[0.0, 0.0]], [1.0, 2.0], eps=eps)
+    r = np.sqrt(12.5 + eps)
+    assert _rel(y, [[0.5 * 3.0 / r, 0.5 * 2.0 * 4.0 / r]]) < 1e-15
+    o = rng.standard_normal((4, 2, 16))
+    y1 = oracle.output_epilogue(o, np.full(o.shape, 40.0), None, eps=1e-12)
+    y2 = oracle.output_epilogue(3.5 * o, np.full(o.shape, 40.0), None, eps=1e-12)
+    assert _rel(y1, y2) < 1e-10
+    assert _rel(np.mean(y1 * y1, axis=-1), np.ones((4, 2))) < 1e-10
+
+
 def pin_invariants(lib):
     rng = np.random.default_rng(21)
     B, T, H, Dk, Dv = 2, 29, 2, 6, 7
@@ -549,7 +591,7 @@ def pin_invariants(lib):
     assert _rel(S, ST) < TOL and _rel(M, MT) < TOL
 
 
-ALL_PINS = [pin_gate_parameterisation, pin_backward_finite_differences, 
+ALL_PINS = [pin_gate_parameterisation, pin_layer_prologue_epilogue, pin_backward_finite_differences, 
     pin_one_token,
     pin_two_tokens,
     pin_gdn_reduction,

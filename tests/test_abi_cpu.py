@@ -262,3 +262,49 @@ def test_gates_empty_is_ok_and_outputs_never_cover_inputs(lib):
     # that passes validation would launch, so only the rejection is checked)
     a = gate_args(za=fake(0), zb=fake(0), zm=fake(0), beta=fake(0, 256))
     assert mdn.STATUS_NAMES[call_gates(lib, a)] == "MDN_ERR_ALIAS"
+
+
+def call_pro(lib, q=fake(0), k=fake(1), d=None, qo=fake(2), ko=fake(3), rows=10, H=2, D=64,
+             eps=1e-6, dt=mdn.MDN_BF16):
+    return lib.mdn_qk_prologue(q, k, d, qo, ko, rows, H, D, eps, dt, None)
+
+
+def call_epi(lib, o=fake(0), g=fake(1), w=None, y=fake(2), rows=10, H=2, D=64, eps=1e-6,
+             dt=mdn.MDN_BF16):
+    return lib.mdn_output_epilogue(o, g, w, y, rows, H, D, eps, dt, None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(D=96), "MDN_ERR_UNSUPPORTED"),
+    (dict(eps=0.0), "MDN_ERR_UNSUPPORTED"),
+    (dict(eps=float("nan")), "MDN_ERR_UNSUPPORTED"),
+    (dict(dt=7), "MDN_ERR_UNSUPPORTED"),
+    (dict(H=-1), "MDN_ERR_SHAPE"),
+    (dict(q=None), "MDN_ERR_NULL"),
+    (dict(ko=None), "MDN_ERR_NULL"),
+    (dict(k=fake(1, 8)), "MDN_ERR_ALIGN"),
+    (dict(d=fake(4, 4)), "MDN_ERR_ALIGN"),
+    (dict(qo=fake(1)), "MDN_ERR_ALIAS"),            # q_out over k
+    (dict(qo=fake(0, 16)), "MDN_ERR_ALIAS"),        # q_out shifted over q, not in place
+    (dict(ko=fake(2)), "MDN_ERR_ALIAS"),            # both outputs at one address
+])
+def test_prologue_rejects(lib, over, status):
+    assert mdn.STATUS_NAMES[call_pro(lib, **over)] == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(D=32), "MDN_ERR_UNSUPPORTED"),
+    (dict(eps=-1.0), "MDN_ERR_UNSUPPORTED"),
+    (dict(o=None), "MDN_ERR_NULL"),
+    (dict(w=fake(4, 8)), "MDN_ERR_ALIGN"),
+    (dict(y=fake(1)), "MDN_ERR_ALIAS"),             # y over the gate
+    (dict(y=fake(0, 32)), "MDN_ERR_ALIAS"),         # y shifted over o
+    (dict(rows=1 << 62), "MDN_ERR_SHAPE"),
+])
+def test_epilogue_rejects(lib, over, status):
+    assert mdn.STATUS_NAMES[call_epi(lib, **over)] == status
+
+
+def test_prologue_epilogue_no_rows(lib):
+    assert call_pro(lib, rows=0, q=None) == 0
+    assert call_epi(lib, H=0, o=None) == 0

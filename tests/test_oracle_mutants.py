@@ -121,3 +121,33 @@ def test_gate_pin_catches_mutant(name, old, new, monkeypatch):
     monkeypatch.setattr(oracle, "gates_from_logits", ns["gates_from_logits"])
     with pytest.raises(AssertionError):
         pin_gate_parameterisation(None)
+
+
+LAYER_MUTANTS = [
+    ("prologue", "correction sign", "q = q - np.asarray(d", "q = q + np.asarray(d"),
+    ("prologue", "eps dropped from the query norm", "nq = np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + eps)",
+     "nq = np.sqrt(np.sum(q * q, axis=-1, keepdims=True))"),
+    ("prologue", "keys not normalised", "return q / nq, k / nk", "return q / nq, k"),
+    ("epilogue", "sum instead of mean", "rms = np.sqrt(np.mean(o * o", "rms = np.sqrt(np.sum(o * o"),
+    ("epilogue", "gate sign", "y = (1.0 / (1.0 + np.exp(-g)))", "y = (1.0 / (1.0 + np.exp(g)))"),
+    ("epilogue", "weight ignored", "y = y * np.asarray(w, dtype=np.float64)", "y = y"),
+]
+
+
+@pytest.mark.parametrize("fn,name,old,new", LAYER_MUTANTS, ids=[m[1] for m in LAYER_MUTANTS])
+def test_layer_pin_catches_mutant(fn, name, old, new, monkeypatch):
+    import inspect
+    import textwrap
+
+    import numpy as np
+    from oracle_pins import pin_layer_prologue_epilogue
+
+    f = oracle.qk_prologue if fn == "prologue" else oracle.output_epilogue
+    src = textwrap.dedent(inspect.getsource(f))
+    assert src.count(old) == 1, f"mutation site for '{name}' not found exactly once"
+    ns = {"np": np}
+    exec(compile(src.replace(old, new), "<layer mutant>", "exec"), ns)
+    monkeypatch.setattr(oracle, "qk_prologue" if fn == "prologue" else "output_epilogue",
+                        ns["qk_prologue" if fn == "prologue" else "output_epilogue"])
+    with pytest.raises(AssertionError):
+        pin_layer_prologue_epilogue(None)
