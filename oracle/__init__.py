@@ -58,6 +58,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     dp = ctypes.POINTER(ctypes.c_double)
     lib.mdn_oracle_recurrence.restype = ctypes.c_int
     lib.mdn_oracle_recurrence.argtypes = [dp] * 12 + [ctypes.c_int] * 7
+    lib.mdn_oracle_recurrence_vt.restype = ctypes.c_int
+    lib.mdn_oracle_recurrence_vt.argtypes = [dp] * 13 + [ctypes.c_int] * 7
     lib.mdn_oracle_chunk_bruteforce.restype = ctypes.c_int
     lib.mdn_oracle_chunk_bruteforce.argtypes = [dp] * 12 + [ctypes.c_int] * 8
     lib.mdn_oracle_chunk_gamma.restype = ctypes.c_int
@@ -98,7 +100,8 @@ def max_threads(lib: Optional[ctypes.CDLL] = None) -> int:
 
 
 def recurrence(q, k, v, alpha, mu, eta, beta=None, S0=None, M0=None, *,
-               col_block: int = 16, nthreads: int = 0, lib: Optional[ctypes.CDLL] = None):
+               col_block: int = 16, nthreads: int = 0, lib: Optional[ctypes.CDLL] = None,
+               return_vt: bool = False):
     """Token-by-token MDN recurrence in fp64.
 
     q, k: [B, T, H, Dk]; v: [B, T, H, Dv]; alpha, mu, eta (, beta): [B, T, H];
@@ -118,6 +121,15 @@ def recurrence(q, k, v, alpha, mu, eta, beta=None, S0=None, M0=None, *,
     O = np.zeros((B, T, H, Dv))
     ST = np.zeros((B, H, Dk, Dv))
     MT = np.zeros((B, H, Dk, Dv))
+    if return_vt:
+        VT = np.zeros((B, T, H, Dv))
+        rc = lib.mdn_oracle_recurrence_vt(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                          _ptr(mu), _ptr(eta), _ptr(S0), _ptr(M0), _ptr(O),
+                                          _ptr(ST), _ptr(MT), _ptr(VT), B, T, H, Dk, Dv,
+                                          col_block, nthreads)
+        if rc != 0:
+            raise RuntimeError(f"mdn_oracle_recurrence_vt failed with code {rc}")
+        return O, ST, MT, VT
     rc = lib.mdn_oracle_recurrence(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(mu),
                                    _ptr(eta), _ptr(S0), _ptr(M0), _ptr(O), _ptr(ST), _ptr(MT),
                                    B, T, H, Dk, Dv, col_block, nthreads)

@@ -94,7 +94,8 @@ static void token_step(const double* kt, const double* vv, double a, double m, d
 static void recurrence_unit(const double* q, const double* k, const double* v,
                             const double* alpha, const double* beta, const double* mu,
                             const double* eta, const double* S0, const double* M0,
-                            double* O, double* ST, double* MT, int b, int h, int c0, int nc,
+                            double* O, double* ST, double* MT, double* VT, int b, int h, int c0,
+                            int nc,
                             int T, int H, int Dk, int Dv, double* S, double* M, double* vt,
                             double* o)
 {
@@ -122,6 +123,10 @@ static void recurrence_unit(const double* q, const double* k, const double* v,
             for (int c = 0; c < nc; ++c) o[c] += S[(size_t)i * nc + c] * qt[i];
         double* ot = O + IDX_TOK(b, t, h, c0, T, H, Dv);
         for (int c = 0; c < nc; ++c) ot[c] = o[c];
+        if (VT) {
+            double* vo = VT + IDX_TOK(b, t, h, c0, T, H, Dv);
+            for (int c = 0; c < nc; ++c) vo[c] = vt[c];
+        }
     }
     for (int i = 0; i < Dk; ++i) {
         for (int c = 0; c < nc; ++c) {
@@ -136,11 +141,11 @@ static void recurrence_unit(const double* q, const double* k, const double* v,
  * columns.  nthreads <= 0 leaves OpenMP's default.  Returns 0 on success,
  * nonzero on bad arguments or allocation failure.
  */
-int mdn_oracle_recurrence(const double* q, const double* k, const double* v,
+static int recurrence_all(const double* q, const double* k, const double* v,
                           const double* alpha, const double* beta, const double* mu,
                           const double* eta, const double* S0, const double* M0, double* O,
-                          double* ST, double* MT, int B, int T, int H, int Dk, int Dv,
-                          int col_block, int nthreads)
+                          double* ST, double* MT, double* VT, int B, int T, int H, int Dk,
+                          int Dv, int col_block, int nthreads)
 {
     if (!q || !k || !v || !alpha || !mu || !eta || !O) return 1;
     if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return 2;
@@ -171,7 +176,7 @@ int mdn_oracle_recurrence(const double* q, const double* k, const double* v,
             const int b = (int)(u / ((long)nblk * H));
             const int c0 = blk * col_block;
             const int nc = (c0 + col_block <= Dv) ? col_block : Dv - c0;
-            recurrence_unit(q, k, v, alpha, beta, mu, eta, S0, M0, O, ST, MT, b, h, c0, nc, T,
+            recurrence_unit(q, k, v, alpha, beta, mu, eta, S0, M0, O, ST, MT, VT, b, h, c0, nc, T,
                             H, Dk, Dv, S, M, vt, o);
         }
         free(S);
@@ -180,6 +185,29 @@ int mdn_oracle_recurrence(const double* q, const double* k, const double* v,
         free(o);
     }
     return failed ? 3 : 0;
+}
+
+int mdn_oracle_recurrence(const double* q, const double* k, const double* v,
+                          const double* alpha, const double* beta, const double* mu,
+                          const double* eta, const double* S0, const double* M0, double* O,
+                          double* ST, double* MT, int B, int T, int H, int Dk, int Dv,
+                          int col_block, int nthreads)
+{
+    return recurrence_all(q, k, v, alpha, beta, mu, eta, S0, M0, O, ST, MT, NULL, B, T, H, Dk,
+                          Dv, col_block, nthreads);
+}
+
+/* The same recurrence, also returning every token's residual vt_t [B,T,H,Dv]
+ * (the quantity the chunk form calls Vt). */
+int mdn_oracle_recurrence_vt(const double* q, const double* k, const double* v,
+                             const double* alpha, const double* beta, const double* mu,
+                             const double* eta, const double* S0, const double* M0, double* O,
+                             double* ST, double* MT, double* VT, int B, int T, int H, int Dk,
+                             int Dv, int col_block, int nthreads)
+{
+    if (!VT) return 1;
+    return recurrence_all(q, k, v, alpha, beta, mu, eta, S0, M0, O, ST, MT, VT, B, T, H, Dk, Dv,
+                          col_block, nthreads);
 }
 
 /* Number of threads OpenMP would use for a parallel region (for reporting). */

@@ -79,6 +79,29 @@ def pin_one_token(lib):
 # P2: two tokens, the two propagation paths ([MDN slides] "One error can affect
 # several future writes"; [MDN notes] Sec. 2.2 two-step example)
 # --------------------------------------------------------------------------
+def pin_residuals(lib):
+    """The residual the recurrence reports is vt_t = v_t - alpha_t S_{t-1}^T k_t
+    ([MDN slides] Sec. 3.1 Eq. (3)): at T = 1 from arbitrary S0 it is the
+    closed form; at T = 2 the second one is taken against S_1, rebuilt from
+    the first residual as S_1 = alpha_1 S0 - beta_1 (mu_1 M0 - eta_1 k_1 vt_1^T)."""
+    rng = np.random.default_rng(12)
+    B, H, Dk, Dv = 1, 2, 4, 3
+    q = rng.standard_normal((B, 2, H, Dk))
+    k = rng.standard_normal((B, 2, H, Dk))
+    v = rng.standard_normal((B, 2, H, Dv))
+    a, m, e = _gates(rng, (B, 2, H))
+    s = rng.uniform(0.2, 1.0, (B, 2, H))
+    S0 = rng.standard_normal((B, H, Dk, Dv))
+    M0 = rng.standard_normal((B, H, Dk, Dv))
+    _, _, _, VT = oracle.recurrence(q, k, v, a, m, e, s, S0, M0, lib=lib, return_vt=True)
+    for h in range(H):
+        vt1 = v[0, 0, h] - a[0, 0, h] * S0[0, h].T @ k[0, 0, h]
+        assert _rel(VT[0, 0, h], vt1) < TOL
+        M1 = m[0, 0, h] * M0[0, h] - e[0, 0, h] * np.outer(k[0, 0, h], vt1)
+        S1 = a[0, 0, h] * S0[0, h] - s[0, 0, h] * M1
+        assert _rel(VT[0, 1, h], v[0, 1, h] - a[0, 1, h] * S1.T @ k[0, 1, h]) < TOL
+
+
 def pin_two_tokens(lib):
     """From zero state, the first residual reaches S_2 with weight
     (alpha_2 beta_1 + beta_2 mu_2):
@@ -591,7 +614,7 @@ def pin_invariants(lib):
     assert _rel(S, ST) < TOL and _rel(M, MT) < TOL
 
 
-ALL_PINS = [pin_gate_parameterisation, pin_layer_prologue_epilogue, pin_backward_finite_differences, 
+ALL_PINS = [pin_gate_parameterisation, pin_residuals, pin_layer_prologue_epilogue, pin_backward_finite_differences, 
     pin_one_token,
     pin_two_tokens,
     pin_gdn_reduction,

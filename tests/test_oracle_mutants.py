@@ -54,6 +54,8 @@ MUTANTS = [
      "if (j < i) x = G[(size_t)(i - 1) * n + j];", "if (j < i) x = G[(size_t)i * n + j];"),
     ("brute force: carry uses old momentum sign",
      "Mn[x] = mbar[n] * M[x] - wm;", "Mn[x] = mbar[n] * M[x] + wm;"),
+    ("residual output reports the read-out",
+     "for (int c = 0; c < nc; ++c) vo[c] = vt[c];", "for (int c = 0; c < nc; ++c) vo[c] = o[c];"),
     ("backward: read-out gradient uses the key",
      "Sh[x] += qt[i] * dot[c];", "Sh[x] += kt[i] * dot[c];"),
     ("backward: memory step drops beta",
