@@ -68,6 +68,10 @@ FLOP_BWD = 32 * D * D + 30 * C * D
 # what it must read and write once: q, k, v, dO (bf16), three gates in, dq, dk, dv (fp32)
 # and three gate gradients out, plus S0, M0 read / dS0, dM0 written per (b, h) (zero here)
 BYTES_BWD = 4 * D * 2 + 3 * 4 + 3 * D * 4 + 3 * 4
+# with the forward's saved residuals the re-scan only rebuilds the states (4 d^2 instead of
+# 8 d^2 + 2 C d) and reads Vt (bf16) instead of v
+FLOP_BWD_SAVED = FLOP_BWD - 4 * D * D - 2 * C * D
+BYTES_BWD_SAVED = BYTES_BWD + D * 2
 PEAK_FP32_MFMA = 157.3e12       # MI355X dense fp32 matrix
 GATE_TAU = (2048 / 16) ** 0.5            # the temperature sqrt(d_in / h) at d_in 2048, 16 heads
 
@@ -263,6 +267,17 @@ def bench_forward(args, torch, si, mdn):
                         "hbm_frac_algorithmic": (BYTES_FWD_BETA * toh + STATE_BYTES_HEAD * heads)
                         / (beta_ms * 1e-3) / PEAK_HBM_BPS}
     del plan_b
+    # the same layer saving every token's residual for a backward pass
+    plan_s = mdn.ChunkPlan(*plan.args, save_vt=True)
+    settle(torch, [plan_s.forward], args.settle)
+    for _ in range(args.warmup):
+        plan_s.forward()
+    _, save_ms = time_calls(torch, [plan_s.forward], args.steps)
+    log(f"forward saving the residuals: {save_ms * 1e3:.1f} us/step")
+    fwd["save_residuals"] = {"workload": "the same layer also writing Vt [B, T, H, Dv] (bf16)",
+                             "us_per_step": save_ms * 1e3,
+                             "tokens_per_s": tokens / (save_ms * 1e-3)}
+    del plan_s
     # the gated delta rule: no mu (mu = 0), the momentum-free kernel
     a_, e_ = plan.args[3], plan.args[5]
     plan_g = mdn.ChunkPlan(plan.args[0], plan.args[1], plan.args[2], a_, None, e_)
@@ -332,7 +347,9 @@ def bench_forward(args, torch, si, mdn):
 
 def bench_backward(args, torch, si, mdn, cfg, inp):
     """mdn_chunk_bwd on the headline layer with dO ~ N(0, 1) and no terminal
-    state gradients; every gradient (q, k, v, alpha, mu, eta) computed."""
+    state gradients; every gradient (q, k, v, alpha, mu, eta) computed.  The
+    main figure takes the residuals the forward saved (the pages' trade); the
+    recompute figure passes none and re-solves for them."""
     bf, f32 = torch.bfloat16, torch.float32
     cot = si.backward_cotangents(cfg, 12, terminal=False)
     args_ = (up(inp["q"], bf), up(inp["k"], bf), up(inp["v"], bf), up(inp["alpha"], f32),
@@ -341,25 +358,40 @@ def bench_backward(args, torch, si, mdn, cfg, inp):
     B, T, H = cfg.B, cfg.T, cfg.H
     ws = torch.empty(mdn.workspace_bytes_bwd(B, T, H, cfg.Dk, cfg.Dv, bf), dtype=torch.uint8,
                      device="cuda")
-    fn = lambda: mdn.chunk_bwd(*args_, workspace=ws, state_grads=False)
-    settle(torch, [fn], args.settle)
-    for _ in range(max(1, args.warmup // 2)):
-        fn()
+    Vt = torch.empty_like(args_[2])
+    mdn.chunk_fwd(*args_[:8], Vt=Vt)
     steps = max(1, args.steps // 5)
-    (_,), span = time_calls(torch, [fn], steps)
     toh = B * T * H
-    us = span * 1e3
+    flop_saved = FLOP_BWD_SAVED * toh
     flop = FLOP_BWD * toh
-    tf = flop / (us * 1e-6) / 1e12
-    log(f"backward: {us:.1f} us/step ({tf:.1f} TFLOP/s dense fp32 work)")
-    return {"workload": f"mdn_chunk_bwd on {cfg.name}: dO ~ N(0, 1), all gradients, fp32 "
-                        "arithmetic (fp32 MFMA)",
+    out = {}
+    for name, kw in (("saved", dict(Vt=Vt)), ("recompute", {})):
+        fn = lambda: mdn.chunk_bwd(*args_, workspace=ws, state_grads=False, **kw)
+        settle(torch, [fn], args.settle)
+        for _ in range(max(1, args.warmup // 2)):
+            fn()
+        (_,), span = time_calls(torch, [fn], steps)
+        out[name] = span * 1e3
+    us, us_re = out["saved"], out["recompute"]
+    tf = flop_saved / (us * 1e-6) / 1e12
+    log(f"backward: {us:.1f} us/step with saved residuals ({tf:.1f} TFLOP/s dense fp32 work), "
+        f"{us_re:.1f} us/step recomputing them")
+    return {"workload": f"mdn_chunk_bwd on {cfg.name}: dO ~ N(0, 1), all gradients, the "
+                        "forward's saved residuals, fp32 arithmetic (fp32 MFMA)",
             "us_per_step": us, "tokens_per_s": B * T / (us * 1e-6), "steps_timed": steps,
+            "recompute_us_per_step": us_re,
+            "recompute_tokens_per_s": B * T / (us_re * 1e-6),
             "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP32_MFMA / 1e12,
-                         "unit": "TFLOP/s", "frac": flop / (us * 1e-6) / PEAK_FP32_MFMA,
-                         "traffic": traffic_bytes("chunk_bwd"), "algorithmic_flop": flop,
-                         "algorithmic_bytes": BYTES_BWD * toh,
-                         "hbm_frac": BYTES_BWD * toh / (us * 1e-6) / PEAK_HBM_BPS}}
+                         "unit": "TFLOP/s", "frac": flop_saved / (us * 1e-6) / PEAK_FP32_MFMA,
+                         "traffic": None, "algorithmic_flop": flop_saved,
+                         "algorithmic_bytes": BYTES_BWD_SAVED * toh,
+                         "hbm_frac": BYTES_BWD_SAVED * toh / (us * 1e-6) / PEAK_HBM_BPS},
+            "recompute_roofline": {"bound": "mfma", "achieved": flop / (us_re * 1e-6) / 1e12,
+                                   "peak": PEAK_FP32_MFMA / 1e12, "unit": "TFLOP/s",
+                                   "frac": flop / (us_re * 1e-6) / PEAK_FP32_MFMA,
+                                   "traffic": traffic_bytes("chunk_bwd"),
+                                   "algorithmic_flop": flop,
+                                   "algorithmic_bytes": BYTES_BWD * toh}}
 
 
 def bench_decode(args, torch, si, mdn):

@@ -18,12 +18,13 @@ hipError_t launch_chunk_prepare(const void* q, const void* k, const float* alpha
 size_t chunk_fused_workspace_bytes(size_t nchunks);
 hipError_t launch_chunk_fused(const void* q, const void* k, const void* v, const float* alpha,
                               const float* mu, const float* eta, const float* beta,
-                              const float* S0, const float* M0, void* O, float* ST, float* MT,
-                              int B, int T, int H, int Dk, int Dv, void* workspace,
+                              const float* S0, const float* M0, void* O, void* Vto, float* ST,
+                              float* MT, int B, int T, int H, int Dk, int Dv, void* workspace,
                               hipStream_t stream);
 hipError_t launch_chunk_scan(const void* q, const void* k, const void* v, const float* S0,
-                             const float* M0, void* O, float* ST, float* MT, int B, int T, int H,
-                             int Dk, int Dv, bool bf16, const void* workspace, hipStream_t stream);
+                             const float* M0, void* O, void* Vto, float* ST, float* MT, int B,
+                             int T, int H, int Dk, int Dv, bool bf16, const void* workspace,
+                             hipStream_t stream);
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* alpha,
                          const float* mu, const float* eta, const float* beta, float* S, float* M,
                          void* o, int heads, int Dk, int Dv, bool bf16, hipStream_t stream);
@@ -31,9 +32,10 @@ size_t chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, bool bf16)
 hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
                             const float* mu, const float* eta, const float* beta, const float* S0,
                             const float* M0, const void* dO, const float* dST, const float* dMT,
-                            float* dq, float* dk, float* dv, float* dalpha, float* dmu,
-                            float* deta, float* dbeta, float* dS0, float* dM0, int B, int T,
-                            int H, int Dk, int Dv, bool bf16, void* workspace, hipStream_t stream);
+                            const void* Vsaved, float* dq, float* dk, float* dv, float* dalpha,
+                            float* dmu, float* deta, float* dbeta, float* dS0, float* dM0, int B,
+                            int T, int H, int Dk, int Dv, bool bf16, void* workspace,
+                            hipStream_t stream);
 hipError_t launch_state_copy(const float* src, float* dst, size_t count, hipStream_t stream);
 hipError_t launch_qk_prologue(const void* q, const void* k, const float* dcorr, void* qo,
                               void* ko, size_t rows, int H, int D, bool bf16, float eps,
@@ -139,6 +141,7 @@ struct FwdArgs {
     const void *q, *k, *v;
     const float *alpha, *mu, *eta, *beta, *S0, *M0;   // beta may be NULL
     void* O;
+    void* Vt;   // optional: the residuals of every token (mdn_chunk_fwd only)
     float *S_T, *M_T;
     int B, T, H, Dk, Dv, chunk;
     mdn_dtype dt;
@@ -175,8 +178,8 @@ mdn_status validate_fwd(const FwdArgs& a, int phase, bool* no_work)
     if (tok && (phase & PREPARE) && (!a.alpha || !a.eta)) return MDN_ERR_NULL;
     if (tok && (phase & SCAN) && (!a.v || !a.O)) return MDN_ERR_NULL;
 
-    const void* ptrs[] = {a.q, a.k, a.v, a.alpha, a.mu, a.eta, a.beta, a.S0, a.M0, a.O, a.S_T,
-                          a.M_T, a.ws};
+    const void* ptrs[] = {a.q, a.k, a.v, a.alpha, a.mu, a.eta, a.beta, a.S0, a.M0, a.O, a.Vt,
+                          a.S_T, a.M_T, a.ws};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MDN_ERR_ALIGN;
 
@@ -199,14 +202,17 @@ mdn_status validate_fwd(const FwdArgs& a, int phase, bool* no_work)
                sS0 = span(scan ? a.S0 : nullptr, nstate * 4),
                sM0 = span(scan ? a.M0 : nullptr, nstate * 4),
                sO = span(scan ? a.O : nullptr, nt * nv * esz),
+               sVt = span(scan ? a.Vt : nullptr, nt * nv * esz),
                sST = span(scan ? a.S_T : nullptr, nstate * 4),
                sMT = span(scan ? a.M_T : nullptr, nstate * 4), sW = span(a.ws, need);
     const Span inputs[] = {sq, sk, sv, sa, sm, se, sb, sS0, sM0};
     // O and the workspace overlap nothing
     for (const Span& x : inputs)
-        if (overlap(sO, x) || overlap(sW, x)) return MDN_ERR_ALIAS;
+        if (overlap(sO, x) || overlap(sW, x) || overlap(sVt, x)) return MDN_ERR_ALIAS;
     if (overlap(sO, sW) || overlap(sO, sST) || overlap(sO, sMT) || overlap(sW, sST) ||
         overlap(sW, sMT) || overlap(sST, sMT))
+        return MDN_ERR_ALIAS;
+    if (overlap(sVt, sO) || overlap(sVt, sW) || overlap(sVt, sST) || overlap(sVt, sMT))
         return MDN_ERR_ALIAS;
     // final states overlap no input, except exactly in place over their own
     // initial state
@@ -226,7 +232,7 @@ mdn_status run_fwd(const FwdArgs& a, int phase, hipStream_t stream)
     if (phase == BOTH && bf16 && a.T > 0) {
         const hipError_t err =
             mdn::launch_chunk_fused(a.q, a.k, a.v, a.alpha, a.mu, a.eta, a.beta, a.S0, a.M0, a.O,
-                                    a.S_T, a.M_T, a.B, a.T, a.H, a.Dk, a.Dv,
+                                    a.Vt, a.S_T, a.M_T, a.B, a.T, a.H, a.Dk, a.Dv,
                                     const_cast<void*>(a.ws), stream);
         return err == hipSuccess ? MDN_OK : MDN_ERR_HIP;
     }
@@ -238,8 +244,8 @@ mdn_status run_fwd(const FwdArgs& a, int phase, hipStream_t stream)
     }
     if (phase & SCAN) {
         const hipError_t err =
-            mdn::launch_chunk_scan(a.q, a.k, a.v, a.S0, a.M0, a.O, a.S_T, a.M_T, a.B, a.T, a.H,
-                                   a.Dk, a.Dv, bf16, a.ws, stream);
+            mdn::launch_chunk_scan(a.q, a.k, a.v, a.S0, a.M0, a.O, a.Vt, a.S_T, a.M_T, a.B, a.T,
+                                   a.H, a.Dk, a.Dv, bf16, a.ws, stream);
         if (err != hipSuccess) return MDN_ERR_HIP;
     }
     return MDN_OK;
@@ -251,12 +257,12 @@ extern "C" {
 
 mdn_status mdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
                          const float* mu, const float* eta, const float* beta, const float* S0,
-                         const float* M0, void* O, float* S_T, float* M_T, int B, int T, int H,
-                         int Dk, int Dv, int chunk, mdn_dtype dt, void* workspace,
+                         const float* M0, void* O, void* Vt, float* S_T, float* M_T, int B,
+                         int T, int H, int Dk, int Dv, int chunk, mdn_dtype dt, void* workspace,
                          size_t workspace_bytes, hipStream_t stream)
 {
-    const FwdArgs a{q, k, v, alpha, mu, eta, beta, S0, M0, O, S_T, M_T, B, T, H, Dk, Dv, chunk,
-                    dt, workspace, workspace_bytes};
+    const FwdArgs a{q, k, v, alpha, mu, eta, beta, S0, M0, O, Vt, S_T, M_T, B, T, H, Dk, Dv,
+                    chunk, dt, workspace, workspace_bytes};
     return run_fwd(a, BOTH, stream);
 }
 
@@ -268,7 +274,7 @@ mdn_status mdn_chunk_fwd_prepare(const void* q, const void* k, const float* alph
     // the scan's Dv does not change the prepared data; any supported value
     // validates the same
     const FwdArgs a{q, k, nullptr, alpha, mu, eta, beta, nullptr, nullptr, nullptr, nullptr,
-                    nullptr, B, T, H, Dk, 64, chunk, dt, workspace, workspace_bytes};
+                    nullptr, nullptr, B, T, H, Dk, 64, chunk, dt, workspace, workspace_bytes};
     return run_fwd(a, PREPARE, stream);
 }
 
@@ -277,8 +283,8 @@ mdn_status mdn_chunk_fwd_scan(const void* q, const void* k, const void* v, const
                               int H, int Dk, int Dv, int chunk, mdn_dtype dt,
                               const void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    const FwdArgs a{q, k, v, nullptr, nullptr, nullptr, nullptr, S0, M0, O, S_T, M_T, B, T, H,
-                    Dk, Dv, chunk, dt, workspace, workspace_bytes};
+    const FwdArgs a{q, k, v, nullptr, nullptr, nullptr, nullptr, S0, M0, O, nullptr, S_T, M_T, B,
+                    T, H, Dk, Dv, chunk, dt, workspace, workspace_bytes};
     return run_fwd(a, SCAN, stream);
 }
 
@@ -364,7 +370,8 @@ size_t mdn_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int ch
 mdn_status mdn_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
                          const float* mu, const float* eta, const float* beta, const float* S0,
                          const float* M0, const void* dO, const float* dS_T, const float* dM_T,
-                         float* dq, float* dk, float* dv, float* dalpha, float* dmu, float* deta,
+                         const void* Vt, float* dq, float* dk, float* dv, float* dalpha,
+                         float* dmu, float* deta,
                          float* dbeta, float* dS0, float* dM0, int B, int T, int H, int Dk,
                          int Dv, int chunk, mdn_dtype dt, void* workspace,
                          size_t workspace_bytes, hipStream_t stream)
@@ -384,7 +391,7 @@ mdn_status mdn_chunk_bwd(const void* q, const void* k, const void* v, const floa
     const bool tok = T > 0;
     if (tok && (!q || !k || !v || !alpha || !eta || !dO || !dq || !dk || !dv || !dalpha || !deta))
         return MDN_ERR_NULL;
-    const void* ptrs[] = {q, k, v, alpha, mu, eta, beta, S0, M0, dO, dS_T, dM_T, dq, dk, dv,
+    const void* ptrs[] = {q, k, v, alpha, mu, eta, beta, S0, M0, dO, dS_T, dM_T, Vt, dq, dk, dv,
                           dalpha, dmu, deta, dbeta, dS0, dM0, workspace};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MDN_ERR_ALIGN;
@@ -400,7 +407,8 @@ mdn_status mdn_chunk_bwd(const void* q, const void* k, const void* v, const floa
                            span(mu, nt * ngate * 4),    span(eta, nt * ngate * 4),
                            span(beta, nt * ngate * 4),  span(S0, nstate * 4),
                            span(M0, nstate * 4),        span(dO, nt * nv * esz),
-                           span(dS_T, nstate * 4),      span(dM_T, nstate * 4)};
+                           span(dS_T, nstate * 4),      span(dM_T, nstate * 4),
+                           span(Vt, nt * nv * esz)};
     const Span outputs[] = {span(dq, nt * nqk * 4),        span(dk, nt * nqk * 4),
                             span(dv, nt * nv * 4),         span(dalpha, nt * ngate * 4),
                             span(dmu_w, nt * ngate * 4),   span(deta, nt * ngate * 4),
@@ -422,7 +430,7 @@ mdn_status mdn_chunk_bwd(const void* q, const void* k, const void* v, const floa
         return err == hipSuccess ? MDN_OK : MDN_ERR_HIP;
     }
     const hipError_t err = mdn::launch_chunk_bwd(
-        q, k, v, alpha, mu, eta, beta, S0, M0, dO, dS_T, dM_T, dq, dk, dv, dalpha, dmu_w, deta,
+        q, k, v, alpha, mu, eta, beta, S0, M0, dO, dS_T, dM_T, Vt, dq, dk, dv, dalpha, dmu_w, deta,
         dbeta_w, dS0, dM0, B, T, H, Dk, Dv, dt == MDN_BF16, workspace, stream);
     return err == hipSuccess ? MDN_OK : MDN_ERR_HIP;
 }

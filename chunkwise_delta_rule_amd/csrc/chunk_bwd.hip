@@ -374,12 +374,14 @@ __global__ __launch_bounds__(NT) void bwd_scan_kernel(
 // ---------------------------------------------------------------------------
 // Forward re-scan: the chunk-entry states and Vt of every chunk.
 // ---------------------------------------------------------------------------
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, bool SAVED>
 __global__ __launch_bounds__(NT) void bwd_rescan_kernel(
     const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ Tw,
     const float* __restrict__ Vw, const float* S0, const float* M0, E* __restrict__ Hs,
     float* __restrict__ Vts, int T, int H, int NC)
 {
+    // SAVED: v holds the forward's residuals Vt ([B, T, H, DV]); the chunk's
+    // Vt is then read instead of solved for, and only the states are rebuilt
     constexpr int TV = 64;
     constexpr int NTILE = DV / TV;
     constexpr int RT = DK / 16;
@@ -425,7 +427,7 @@ __global__ __launch_bounds__(NT) void bwd_rescan_kernel(
         const size_t chn = (size_t)bh * NC + c;
         pk.fetch(k + tok0 * DK, (size_t)H * DK, n, tid);
         pv.fetch(v + tok0 * DV + tile * TV, (size_t)H * DV, n, tid);
-        pt.fetch(Tw + chn * CH * CH, CH, CH, tid);
+        if (!SAVED) pt.fetch(Tw + chn * CH * CH, CH, CH, tid);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
             pvec[u] = tid + u * NT < 6 * CH ? Vw[chn * NVEC * CH + tid + u * NT] : 0.f;
@@ -442,7 +444,7 @@ __global__ __launch_bounds__(NT) void bwd_rescan_kernel(
         __syncthreads();
         pk.commit(Ks, tid);
         pv.commit(Vs, tid);
-        pt.commit(Ts, tid);
+        if (!SAVED) pt.commit(Ts, tid);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
             if (tid + u * NT < 6 * CH) vecs[tid + u * NT] = pvec[u];
@@ -461,6 +463,8 @@ __global__ __launch_bounds__(NT) void bwd_rescan_kernel(
                 }
         }
 
+        f32x4 Vt[4];
+        if constexpr (!SAVED) {
         f32x4 xs[4], xm[4];
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) xs[ct] = xm[ct] = zero4();
@@ -492,7 +496,6 @@ __global__ __launch_bounds__(NT) void bwd_rescan_kernel(
                 R[ct][r] = Vs[i * LDV + lcol] - vecs[V_ABAR * CH + i] * xs[ct][r] +
                            vecs[V_AB1 * CH + i] * xm[ct][r];
             }
-        f32x4 Vt[4];
 #pragma unroll
         for (int it = 0; it < 4; ++it) Vt[it] = zero4();
 #pragma unroll
@@ -519,6 +522,7 @@ __global__ __launch_bounds__(NT) void bwd_rescan_kernel(
                 for (int r = 0; r < 4; ++r) vb[(size_t)(16 * it + 4 * lg + r) * DV] = Vt[it][r];
         }
 
+        }
         const float abn = vecs[V_SCAL * CH + 0];
         const float bn = vecs[V_SCAL * CH + 1];
         const float mbn = vecs[V_SCAL * CH + 2];
@@ -529,9 +533,16 @@ __global__ __launch_bounds__(NT) void bwd_rescan_kernel(
         }
 #pragma unroll
         for (int s = 0; s < CH / 4; ++s) {
-            const float bS = MF::from_acc_scaled(Vt, s, lg, vecs + V_WS * CH, 1.f);
-            const float bM = MF::from_acc_scaled(Vt, s, lg, vecs + V_WM * CH, -1.f);
             const int kr = MF::perm_row(s, lg, 0);
+            float bS, bM;
+            if constexpr (SAVED) {
+                const float vt = Vs[kr * LDV + lcol];
+                bS = vecs[V_WS * CH + kr] * vt;
+                bM = -(vecs[V_WM * CH + kr] * vt);
+            } else {
+                bS = MF::from_acc_scaled(Vt, s, lg, vecs + V_WS * CH, 1.f);
+                bM = MF::from_acc_scaled(Vt, s, lg, vecs + V_WM * CH, -1.f);
+            }
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 const float aK = Ks[kr * LDK + 16 * rt + l16];
@@ -574,7 +585,8 @@ constexpr int G_RED = 22;                                    // 2 rows: reductio
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(NT) void bwd_grad_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ dO,
-    const float* __restrict__ dv, const float* __restrict__ Vts, const E* __restrict__ Hs,
+    const float* __restrict__ dv, const float* __restrict__ Vts, const E* __restrict__ Vsaved,
+    const E* __restrict__ Hs,
     const E* __restrict__ Hd, const float* __restrict__ alpha, const float* __restrict__ mu,
     const float* __restrict__ eta, const float* __restrict__ beta, float* __restrict__ dq,
     float* __restrict__ dk, float* __restrict__ dalpha, float* __restrict__ dmu,
@@ -833,14 +845,16 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
         Tile<float, DV, LD> t0_;
         Tile<E, DV, LD> t1_;
         Tile<E, DK, LD> t2_;
-        t0_.fetch(Vts + chn * CH * DV, DV, n, tid);
+        if (!Vsaved) t0_.fetch(Vts + chn * CH * DV, DV, n, tid);
         t1_.fetch(dO + tok0 * DV, (size_t)H * DV, n, tid);
         t2_.fetch(q + tok0 * DK, (size_t)H * DK, n, tid);
-        t0_.commit(slot0, tid);
+        if (Vsaved) stage<DV, LD>(slot0, Vsaved + tok0 * DV, (size_t)H * DV, n, tid);
+        else t0_.commit(slot0, tid);
         t1_.commit(slot1, tid);
         t2_.commit(slot2, tid);
     } else {
-        stage<DV, LD>(slot0, Vts + chn * CH * DV, DV, n, tid);
+        if (Vsaved) stage<DV, LD>(slot0, Vsaved + tok0 * DV, (size_t)H * DV, n, tid);
+        else stage<DV, LD>(slot0, Vts + chn * CH * DV, DV, n, tid);
         stage<DV, LD>(slot1, dO + tok0 * DV, (size_t)H * DV, n, tid);
         stage<DK, LD>(slot2, q + tok0 * DK, (size_t)H * DK, n, tid);
     }
@@ -1157,7 +1171,8 @@ template <typename E, int DK, int DV>
 static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const float* alpha,
                                const float* mu, const float* eta, const float* beta,
                                const float* S0, const float* M0, const void* dO,
-                               const float* dST, const float* dMT, float* dq, float* dk,
+                               const float* dST, const float* dMT, const void* Vsaved, float* dq,
+                               float* dk,
                                float* dv, float* dalpha, float* dmu, float* deta, float* dbeta,
                                float* dS0, float* dM0, int B, int T, int H, void* workspace,
                                hipStream_t stream)
@@ -1187,14 +1202,20 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
                        NC);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((bwd_rescan_kernel<E, DK, DV>), dim3(nblk), dim3(NT), 0, stream,
-                       static_cast<const E*>(k), static_cast<const E*>(v), Tw, Vw, S0, M0, Hs,
-                       Vts, T, H, NC);
+    if (Vsaved)
+        hipLaunchKernelGGL((bwd_rescan_kernel<E, DK, DV, true>), dim3(nblk), dim3(NT), 0, stream,
+                           static_cast<const E*>(k), static_cast<const E*>(Vsaved), Tw, Vw, S0,
+                           M0, Hs, Vts, T, H, NC);
+    else
+        hipLaunchKernelGGL((bwd_rescan_kernel<E, DK, DV, false>), dim3(nblk), dim3(NT), 0,
+                           stream, static_cast<const E*>(k), static_cast<const E*>(v), Tw, Vw,
+                           S0, M0, Hs, Vts, T, H, NC);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((bwd_grad_kernel<E, DK, DV>), dim3((unsigned)nchunks), dim3(NT), 0, stream,
                        static_cast<const E*>(q), static_cast<const E*>(k),
-                       static_cast<const E*>(dO), dv, Vts, Hs, Hd, alpha, mu, eta, beta, dq, dk,
+                       static_cast<const E*>(dO), dv, Vts, static_cast<const E*>(Vsaved), Hs, Hd,
+                       alpha, mu, eta, beta, dq, dk,
                        dalpha, dmu, deta, dbeta, T, H, NC);
     return hipGetLastError();
 }
@@ -1202,13 +1223,15 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
 hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
                             const float* mu, const float* eta, const float* beta, const float* S0,
                             const float* M0, const void* dO, const float* dST, const float* dMT,
-                            float* dq, float* dk, float* dv, float* dalpha, float* dmu,
-                            float* deta, float* dbeta, float* dS0, float* dM0, int B, int T,
-                            int H, int Dk, int Dv, bool bf16, void* workspace, hipStream_t stream)
+                            const void* Vsaved, float* dq, float* dk, float* dv, float* dalpha,
+                            float* dmu, float* deta, float* dbeta, float* dS0, float* dM0, int B,
+                            int T, int H, int Dk, int Dv, bool bf16, void* workspace,
+                            hipStream_t stream)
 {
 #define MDN_BWD(E, DK, DV)                                                                        \
     if (Dk == DK && Dv == DV)                                                                     \
-        return launch_bwd_t<E, DK, DV>(q, k, v, alpha, mu, eta, beta, S0, M0, dO, dST, dMT, dq,   \
+        return launch_bwd_t<E, DK, DV>(q, k, v, alpha, mu, eta, beta, S0, M0, dO, dST, dMT,       \
+                                       Vsaved, dq,                                                \
                                        dk, dv, dalpha, dmu, deta, dbeta, dS0, dM0, B, T, H,       \
                                        workspace, stream);
     if (bf16) {

@@ -402,11 +402,11 @@ struct FusedLayout {
 // final momentum is the last token's own write, -eta_T k_T vt_T^T (the last
 // chunk's update with the weights eta m_n, which are zero but on its last
 // row); the compute waves skip every product with M.
-template <int DK, int DV, bool MOM>
+template <int DK, int DV, bool MOM, bool SAVE>
 __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const float* __restrict__ ctab, const float* S0, const float* M0, __bf16* __restrict__ O,
-    float* ST, float* MT, int T, int H, int NC, int xcd_groups)
+    __bf16* __restrict__ Vto, float* ST, float* MT, int T, int H, int NC, int xcd_groups)
 {
     using E = __bf16;
     using MM = Mma<E>;
@@ -787,6 +787,13 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
     constexpr int VJ = 16 * CH * 2 + (16 / LC::G) * LC::PAD;   // 16 V rows further
     const unsigned ostride = (unsigned)(H * DV);
     E* const Ocol = O + ((size_t)b * T * H + h) * DV + tile * TV + 16 * wave + 4 * lg;
+    // SAVE: the residuals Vt of every token, [B, T, H, DV] like O (a backward
+    // pass can then rebuild the states without the solve)
+    E* const Vcol = SAVE ? Vto + ((size_t)b * T * H + h) * DV + tile * TV + 16 * wave + 4 * lg : nullptr;
+    // the 16 x 16 identity as a B fragment of mma16: B[4 lg + j][l16] = (4 lg + j == l16)
+    bf16x4 eye;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) eye[j] = static_cast<__bf16>(4 * lg + j == l16 ? 1.f : 0.f);
 
     lds_barrier();   // chunk 0's tables in LDS
     lds_barrier();   // B0: chunk 0 ready
@@ -933,6 +940,30 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
                     *reinterpret_cast<u32x4*>(Ob + (unsigned)row * ostride) = u32x4{ua[0], ua[1], ub[0], ub[1]};
             }
         }
+        if constexpr (SAVE) {
+            // Vt[I] element r is row 16 I + 4 lg + r, column l16 of this wave's
+            // 16.  One MFMA per block with the identity, Vt_I^T I, puts it in
+            // O's layout (element r: row 16 I + l16, column 4 lg + r) with the
+            // same bf16 values; then O's two 16-byte stores per lane.
+            f32x4 Vtt[4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) Vtt[I] = mma16(to_bf4(Vt[I]), eye, zero4());
+            E* Vb = Vcol - 4 * lg + 8 * (lg >> 1) + (size_t)t0 * ostride;
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                u32x2 ua = __builtin_bit_cast(u32x2, to_bf4(Vtt[2 * p]));
+                u32x2 ub = __builtin_bit_cast(u32x2, to_bf4(Vtt[2 * p + 1]));
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    const auto r = __builtin_amdgcn_permlane16_swap(ua[d], ub[d], false, false);
+                    ua[d] = r[0];
+                    ub[d] = r[1];
+                }
+                const int row = 16 * (2 * p + (lg & 1)) + l16;
+                if (row < n)
+                    *reinterpret_cast<u32x4*>(Vb + (unsigned)row * ostride) = u32x4{ua[0], ua[1], ub[0], ub[1]};
+            }
+        }
 
         // (5) S' = abar_n S0 - b_n M0 + K^T Diag(eta gamma_n) Vt,
         //     M' = mubar_n M0 - K^T Diag(eta mubar_n / mubar) Vt
@@ -1008,8 +1039,9 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
 template <int DK, int DV>
 static hipError_t launch_fused_t(const void* q, const void* k, const void* v, const float* alpha,
                                  const float* mu, const float* eta, const float* beta,
-                                 const float* S0, const float* M0, void* O, float* ST, float* MT,
-                                 int B, int T, int H, void* workspace, hipStream_t stream)
+                                 const float* S0, const float* M0, void* O, void* Vto, float* ST,
+                                 float* MT, int B, int T, int H, void* workspace,
+                                 hipStream_t stream)
 {
     const int NC = (T + CH - 1) / CH;
     float* ctab = static_cast<float*>(workspace);
@@ -1020,11 +1052,15 @@ static hipError_t launch_fused_t(const void* q, const void* k, const void* v, co
     const size_t nblk = (size_t)B * H * (DV / 64);
     const int xcd_groups = nblk % 8 == 0 ? (int)(nblk / 8) : 0;
     // mu = NULL: mu = 0, the momentum-free kernel
-    auto kern = mu ? chunk_fwd_fused_kernel<DK, DV, true> : chunk_fwd_fused_kernel<DK, DV, false>;
+    // Vto != NULL: the variant that also stores the residuals
+    auto kern = mu ? (Vto ? chunk_fwd_fused_kernel<DK, DV, true, true>
+                          : chunk_fwd_fused_kernel<DK, DV, true, false>)
+                   : (Vto ? chunk_fwd_fused_kernel<DK, DV, false, true>
+                          : chunk_fwd_fused_kernel<DK, DV, false, false>);
     hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(2 * NT), 0, stream,
                        static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-                       static_cast<const __bf16*>(v), ctab, S0, M0, static_cast<__bf16*>(O), ST,
-                       MT, T, H, NC, xcd_groups);
+                       static_cast<const __bf16*>(v), ctab, S0, M0, static_cast<__bf16*>(O),
+                       static_cast<__bf16*>(Vto), ST, MT, T, H, NC, xcd_groups);
     return hipGetLastError();
 }
 
@@ -1032,20 +1068,20 @@ static hipError_t launch_fused_t(const void* q, const void* k, const void* v, co
 // kernel.  `workspace` holds chunk_fused_workspace_bytes(B * H * ceil(T / 64)).
 hipError_t launch_chunk_fused(const void* q, const void* k, const void* v, const float* alpha,
                               const float* mu, const float* eta, const float* beta,
-                              const float* S0, const float* M0, void* O, float* ST, float* MT,
-                              int B, int T, int H, int Dk, int Dv, void* workspace,
+                              const float* S0, const float* M0, void* O, void* Vto, float* ST,
+                              float* MT, int B, int T, int H, int Dk, int Dv, void* workspace,
                               hipStream_t stream)
 {
     if (Dk == 128 && Dv == 128)
-        return launch_fused_t<128, 128>(q, k, v, alpha, mu, eta, beta, S0, M0, O, ST, MT, B, T,
+        return launch_fused_t<128, 128>(q, k, v, alpha, mu, eta, beta, S0, M0, O, Vto, ST, MT, B, T,
                                         H, workspace, stream);
     if (Dk == 128 && Dv == 64)
-        return launch_fused_t<128, 64>(q, k, v, alpha, mu, eta, beta, S0, M0, O, ST, MT, B, T, H,
+        return launch_fused_t<128, 64>(q, k, v, alpha, mu, eta, beta, S0, M0, O, Vto, ST, MT, B, T, H,
                                        workspace, stream);
     if (Dk == 64 && Dv == 128)
-        return launch_fused_t<64, 128>(q, k, v, alpha, mu, eta, beta, S0, M0, O, ST, MT, B, T, H,
+        return launch_fused_t<64, 128>(q, k, v, alpha, mu, eta, beta, S0, M0, O, Vto, ST, MT, B, T, H,
                                        workspace, stream);
-    return launch_fused_t<64, 64>(q, k, v, alpha, mu, eta, beta, S0, M0, O, ST, MT, B, T, H,
+    return launch_fused_t<64, 64>(q, k, v, alpha, mu, eta, beta, S0, M0, O, Vto, ST, MT, B, T, H,
                                   workspace, stream);
 }
 

@@ -409,8 +409,8 @@ template <typename E, int DK, int DV>
 __global__ __launch_bounds__(NT) void chunk_scan_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ Tw, const E* __restrict__ Aw, const float* __restrict__ Vw,
-    const float* S0, const float* M0, E* __restrict__ O, float* ST, float* MT, int T, int H,
-    int NC, int xcd_groups)
+    const float* S0, const float* M0, E* __restrict__ O, E* __restrict__ Vto, float* ST,
+    float* MT, int T, int H, int NC, int xcd_groups)
 {
     using MM = Mma<E>;
     using SM = ScanSmem<E, DK, DV>;
@@ -547,6 +547,18 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(
 #pragma unroll
             for (int it = 0; it < 4; ++it)
                 Vt[it] = MM::mma(MM::load_perm(Ts + (16 * it + l16) * LDC, s, lg), bR, Vt[it]);
+        }
+
+        // the residuals of every token, when asked for (Vto: [B, T, H, DV] like O)
+        if (Vto) {
+            E* Vb = Vto + tok0 * DV + wcol + l16;
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * it + 4 * lg + r;
+                    if (i < n) Vb[(size_t)i * H * DV] = to_elem<E>(Vt[it][r]);
+                }
         }
 
         // (4) O = entry-state part + A Vt; rows < n to HBM
@@ -961,14 +973,15 @@ static hipError_t launch_prepare_t(const void* q, const void* k, const float* al
 
 template <typename E, int DK, int DV>
 static hipError_t launch_scan_t(const void* q, const void* k, const void* v, const float* S0,
-                                const float* M0, void* O, float* ST, float* MT, int B, int T,
-                                int H, const void* workspace, hipStream_t stream)
+                                const float* M0, void* O, void* Vto, float* ST, float* MT, int B,
+                                int T, int H, const void* workspace, hipStream_t stream)
 {
     const int NC = (T + CH - 1) / CH;
     const size_t nchunks = (size_t)B * H * NC;
     Workspace<E> ws = ws_carve<E>(const_cast<void*>(workspace), nchunks);
     const size_t nblk = (size_t)B * H * (DV / ScanSmem<E, DK, DV>::TV);
     const int xcd_groups = nblk % 8 == 0 ? (int)(nblk / 8) : 0;
+    if (sizeof(E) == 2 && Vto) return hipErrorInvalidValue;   // not stored by this path
     if constexpr (sizeof(E) == 2) {
         hipLaunchKernelGGL((chunk_scan_bf16_kernel<DK, DV>), dim3((unsigned)nblk), dim3(2 * NT), 0,
                            stream, static_cast<const E*>(q), static_cast<const E*>(k),
@@ -978,7 +991,8 @@ static hipError_t launch_scan_t(const void* q, const void* k, const void* v, con
         hipLaunchKernelGGL((chunk_scan_kernel<E, DK, DV>), dim3((unsigned)nblk), dim3(NT), 0,
                            stream, static_cast<const E*>(q), static_cast<const E*>(k),
                            static_cast<const E*>(v), ws.T, ws.A, ws.vec, S0, M0,
-                           static_cast<E*>(O), ST, MT, T, H, NC, xcd_groups);
+                           static_cast<E*>(O), static_cast<E*>(Vto), ST, MT, T, H, NC,
+                           xcd_groups);
     }
     return hipGetLastError();
 }
@@ -1017,8 +1031,9 @@ hipError_t launch_chunk_prepare(const void* q, const void* k, const float* alpha
 }
 
 hipError_t launch_chunk_scan(const void* q, const void* k, const void* v, const float* S0,
-                             const float* M0, void* O, float* ST, float* MT, int B, int T, int H,
-                             int Dk, int Dv, bool bf16, const void* workspace, hipStream_t stream)
+                             const float* M0, void* O, void* Vto, float* ST, float* MT, int B,
+                             int T, int H, int Dk, int Dv, bool bf16, const void* workspace,
+                             hipStream_t stream)
 {
     if (T == 0) {
         const size_t count = (size_t)B * H * Dk * Dv;
@@ -1038,7 +1053,7 @@ hipError_t launch_chunk_scan(const void* q, const void* k, const void* v, const 
     }
 #define MDN_SCAN(E, DK, DV)                                                                      \
     if (Dk == DK && Dv == DV)                                                                    \
-        return launch_scan_t<E, DK, DV>(q, k, v, S0, M0, O, ST, MT, B, T, H, workspace, stream);
+        return launch_scan_t<E, DK, DV>(q, k, v, S0, M0, O, Vto, ST, MT, B, T, H, workspace, stream);
     if (bf16) {
         MDN_SCAN(__bf16, 64, 64) MDN_SCAN(__bf16, 64, 128)
         MDN_SCAN(__bf16, 128, 64) MDN_SCAN(__bf16, 128, 128)

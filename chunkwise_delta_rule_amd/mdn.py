@@ -72,7 +72,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mdn_chunk_fwd_split_workspace_bytes.restype = S
     lib.mdn_chunk_fwd_split_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.mdn_chunk_fwd.restype = I
-    lib.mdn_chunk_fwd.argtypes = [P] * 12 + [I] * 7 + [P, S, P]
+    lib.mdn_chunk_fwd.argtypes = [P] * 13 + [I] * 7 + [P, S, P]
     lib.mdn_chunk_fwd_prepare.restype = I
     lib.mdn_chunk_fwd_prepare.argtypes = [P] * 6 + [I] * 6 + [P, S, P]
     lib.mdn_chunk_fwd_scan.restype = I
@@ -82,7 +82,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mdn_chunk_bwd_workspace_bytes.restype = S
     lib.mdn_chunk_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.mdn_chunk_bwd.restype = I
-    lib.mdn_chunk_bwd.argtypes = [P] * 21 + [I] * 7 + [P, S, P]
+    lib.mdn_chunk_bwd.argtypes = [P] * 22 + [I] * 7 + [P, S, P]
     F = ctypes.c_float
     lib.mdn_qk_prologue.restype = I
     lib.mdn_qk_prologue.argtypes = [P] * 5 + [S, I, I, F, I, P]
@@ -142,12 +142,15 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
               M0: Optional[torch.Tensor] = None, *, beta: Optional[torch.Tensor] = None,
               chunk: int = CHUNK, O: Optional[torch.Tensor] = None,
               S_T: Optional[torch.Tensor] = None, M_T: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None, final_state: bool = True
+              workspace: Optional[torch.Tensor] = None, final_state: bool = True,
+              Vt: Optional[torch.Tensor] = None
               ) -> Tuple[torch.Tensor, Optional[torch.Tensor], Optional[torch.Tensor]]:
     """Chunkwise MDN forward.  q, k [B, T, H, Dk], v [B, T, H, Dv] (bf16 or
     fp32), gates [B, T, H] fp32 (beta optional: None means beta = 1; mu may
     be None, meaning mu = 0, the gated delta rule), S0/M0 [B, H, Dk, Dv] fp32
-    or None.
+    or None.  Vt, when given ([B, T, H, Dv], q's dtype), receives every
+    token's residual (the activations mdn_chunk_bwd can take instead of
+    recomputing them).
     Returns (O, S_T, M_T); S_T/M_T are None when ``final_state`` is False and
     none were passed in."""
     lib = load_library()
@@ -168,6 +171,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
     if O is None:
         O = torch.empty((B, T, H, Dv), dtype=dt, device=dev)
     _check(O, "O", (B, T, H, Dv), dt, dev)
+    if Vt is not None:
+        _check(Vt, "Vt", (B, T, H, Dv), dt, dev)
     if final_state and S_T is None:
         S_T = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
     if final_state and M_T is None:
@@ -180,8 +185,9 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.mdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(mu), _ptr(eta),
-                           _ptr(beta), _ptr(S0), _ptr(M0), _ptr(O), _ptr(S_T), _ptr(M_T), B, T, H,
-                           Dk, Dv, chunk, code, _ptr(workspace), wbytes, _stream(dev))
+                           _ptr(beta), _ptr(S0), _ptr(M0), _ptr(O), _ptr(Vt), _ptr(S_T),
+                           _ptr(M_T), B, T, H, Dk, Dv, chunk, code, _ptr(workspace), wbytes,
+                           _stream(dev))
     if st != 0:
         raise MdnError(st, "mdn_chunk_fwd")
     return O, S_T, M_T
@@ -193,7 +199,7 @@ class ChunkPlan:
     outputs and the workspace; launching performs no allocation."""
 
     def __init__(self, q, k, v, alpha, mu, eta, S0=None, M0=None, *, beta=None,
-                 chunk: int = CHUNK, final_state: bool = True):
+                 chunk: int = CHUNK, final_state: bool = True, save_vt: bool = False):
         self.lib = load_library()
         self.args = (q, k, v, alpha, mu, eta, S0, M0)
         self.beta = beta
@@ -204,6 +210,7 @@ class ChunkPlan:
         self.code = _dtype_code(q.dtype)
         dev = q.device
         self.O = torch.empty((B, T, H, Dv), dtype=q.dtype, device=dev)
+        self.Vt = torch.empty((B, T, H, Dv), dtype=q.dtype, device=dev) if save_vt else None
         self.S_T = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev) if final_state else None
         self.M_T = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev) if final_state else None
         need = int(self.lib.mdn_chunk_fwd_split_workspace_bytes(B, T, H, Dk, Dv, chunk, self.code))
@@ -211,7 +218,7 @@ class ChunkPlan:
         self.ws_bytes = need
         # one full call validates every argument (and fills the outputs)
         chunk_fwd(*self.args, beta=beta, chunk=chunk, O=self.O, S_T=self.S_T, M_T=self.M_T,
-                  workspace=self.workspace)
+                  workspace=self.workspace, Vt=self.Vt)
         self.stream = _stream(dev)
 
     def prepare(self):
@@ -238,7 +245,7 @@ class ChunkPlan:
         B, T, H, Dk, Dv = self.shape
         st = self.lib.mdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(m), _ptr(e),
                                     _ptr(self.beta), _ptr(S0), _ptr(M0), _ptr(self.O),
-                                    _ptr(self.S_T),
+                                    _ptr(self.Vt), _ptr(self.S_T),
                                     _ptr(self.M_T), B, T, H, Dk, Dv, self.chunk, self.code,
                                     _ptr(self.workspace), self.ws_bytes, self.stream)
         if st != 0:
@@ -316,11 +323,12 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
               M0: Optional[torch.Tensor], dO: torch.Tensor, dS_T: Optional[torch.Tensor] = None,
               dM_T: Optional[torch.Tensor] = None, *, beta: Optional[torch.Tensor] = None,
               chunk: int = CHUNK, workspace: Optional[torch.Tensor] = None,
-              state_grads: bool = True) -> dict:
+              state_grads: bool = True, Vt: Optional[torch.Tensor] = None) -> dict:
     """Gradients through mdn_chunk_fwd given dO (and optionally dS_T, dM_T).
     Arguments as for chunk_fwd; returns a dict of float32 tensors dq, dk, dv,
     dalpha, dmu (None without mu), deta, dbeta (None without beta), dS0, dM0
-    (None when state_grads is False)."""
+    (None when state_grads is False).  Vt: the residuals chunk_fwd saved for
+    these inputs (the states are then rebuilt without the solve)."""
     lib = load_library()
     dev = q.device
     B, T, H, Dk = q.shape
@@ -331,6 +339,8 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
     _check(k, "k", (B, T, H, Dk), dt, dev)
     _check(v, "v", (B, T, H, Dv), dt, dev)
     _check(dO, "dO", (B, T, H, Dv), dt, dev)
+    if Vt is not None:
+        _check(Vt, "Vt", (B, T, H, Dv), dt, dev)
     for name, g in (("alpha", alpha), ("mu", mu), ("eta", eta), ("beta", beta)):
         if g is not None or name in ("alpha", "eta"):
             _check(g, name, (B, T, H), torch.float32, dev)
@@ -350,6 +360,7 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     st = lib.mdn_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(mu), _ptr(eta),
                            _ptr(beta), _ptr(S0), _ptr(M0), _ptr(dO), _ptr(dS_T), _ptr(dM_T),
+                           _ptr(Vt),
                            *(_ptr(out[n]) for n in ("dq", "dk", "dv", "dalpha", "dmu", "deta",
                                                     "dbeta", "dS0", "dM0")),
                            B, T, H, Dk, Dv, chunk, code, _ptr(workspace), workspace.numel(),

@@ -102,6 +102,13 @@ size_t mdn_chunk_fwd_split_workspace_bytes(int B, int T, int H, int Dk, int Dv, 
  *   S0, M0           initial memory and momentum (float32); NULL = zero.
  *   O                output o_t for every token (dtype dt); must not overlap
  *                    any input.
+ *   Vt               NULL, or [B, T, H, Dv] (dtype dt): receives every token's
+ *                    residual vt_t = v_t - alpha_t S_{t-1}^T k_t (the chunk
+ *                    form's Vt = L^{-1} R), the activations the slides' frame
+ *                    "The implementation trades saved residuals for
+ *                    throughput" keeps for the backward pass (mdn_chunk_bwd
+ *                    then rebuilds the states from them without the solve).
+ *                    Overlaps nothing.
  *   S_T, M_T         final memory and momentum (float32); NULL = not written.
  *                    S_T may be exactly S0 and M_T exactly M0 (in place); any
  *                    other overlap is MDN_ERR_ALIAS.
@@ -115,8 +122,8 @@ size_t mdn_chunk_fwd_split_workspace_bytes(int B, int T, int H, int Dk, int Dv, 
  */
 mdn_status mdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
                          const float* mu, const float* eta, const float* beta, const float* S0,
-                         const float* M0, void* O, float* S_T, float* M_T, int B, int T, int H,
-                         int Dk, int Dv, int chunk, mdn_dtype dt, void* workspace,
+                         const float* M0, void* O, void* Vt, float* S_T, float* M_T, int B,
+                         int T, int H, int Dk, int Dv, int chunk, mdn_dtype dt, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
 
 /*
@@ -187,15 +194,18 @@ mdn_status mdn_decode_step(const void* q, const void* k, const void* v, const fl
  * throughput"; the paper's Sec. 3.1 and Appendix E) describe the strategy --
  * rebuild the states for the gradients instead of storing every state pair --
  * but print no gradient formulas; these are the chain rule through the chunk
- * equations of mdn_chunk_fwd, chunk by chunk from the last.  The call
- * recomputes the residuals Vt from (q, k, v, gates, S0, M0) and keeps each
- * chunk's entry state and exit-state gradients in the workspace while it
- * runs; nothing from the forward call is needed.
+ * equations of mdn_chunk_fwd, chunk by chunk from the last.  The call takes
+ * the residuals Vt the forward saved (or recomputes them when Vt is NULL) and
+ * keeps each chunk's entry state and exit-state gradients in the workspace
+ * while it runs.
  *   q, k, v, alpha, mu, eta, beta, S0, M0, B, T, H, Dk, Dv, chunk, dt:
  *                         exactly as given to mdn_chunk_fwd (mu, beta, S0, M0
  *                         may be NULL with the same meaning).
  *   dO [B, T, H, Dv]       dtype dt.
  *   dS_T, dM_T [B, H, Dk, Dv] or NULL (zero), float32.
+ *   Vt [B, T, H, Dv] (dtype dt) or NULL: the residuals mdn_chunk_fwd saved
+ *                          for these inputs.  Given, the states are rebuilt
+ *                          from them (no solve); NULL recomputes them.
  * Outputs, all float32, each overwritten:
  *   dq, dk [B, T, H, Dk]; dv [B, T, H, Dv];
  *   dalpha, deta [B, T, H]; dmu [B, T, H] (only when mu is given; may be
@@ -213,7 +223,8 @@ size_t mdn_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int ch
 mdn_status mdn_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
                          const float* mu, const float* eta, const float* beta, const float* S0,
                          const float* M0, const void* dO, const float* dS_T, const float* dM_T,
-                         float* dq, float* dk, float* dv, float* dalpha, float* dmu, float* deta,
+                         const void* Vt, float* dq, float* dk, float* dv, float* dalpha,
+                         float* dmu, float* deta,
                          float* dbeta, float* dS0, float* dM0, int B, int T, int H, int Dk,
                          int Dv, int chunk, mdn_dtype dt, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);

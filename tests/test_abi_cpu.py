@@ -76,16 +76,18 @@ def fake(i, off=0):
 
 def fwd_args(**over):
     a = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), mu=fake(4), eta=fake(5), beta=None,
-             S0=fake(6), M0=fake(7), O=fake(8), S_T=fake(9), M_T=fake(10), B=2, T=100, H=3,
-             Dk=64, Dv=128, chunk=64, dt=mdn.MDN_BF16, ws=fake(11), wsb=1 << 31, stream=None)
+             S0=fake(6), M0=fake(7), O=fake(8), Vt=None, S_T=fake(9), M_T=fake(10), B=2, T=100,
+             H=3, Dk=64, Dv=128, chunk=64, dt=mdn.MDN_BF16, ws=fake(11), wsb=1 << 31,
+             stream=None)
     a.update(over)
     return a
 
 
 def call_fwd(lib, a):
     return lib.mdn_chunk_fwd(a["q"], a["k"], a["v"], a["alpha"], a["mu"], a["eta"], a["beta"],
-                             a["S0"], a["M0"], a["O"], a["S_T"], a["M_T"], a["B"], a["T"], a["H"],
-                             a["Dk"], a["Dv"], a["chunk"], a["dt"], a["ws"], a["wsb"], a["stream"])
+                             a["S0"], a["M0"], a["O"], a["Vt"], a["S_T"], a["M_T"], a["B"], a["T"],
+                             a["H"], a["Dk"], a["Dv"], a["chunk"], a["dt"], a["ws"], a["wsb"],
+                             a["stream"])
 
 
 @pytest.mark.parametrize("over,status", [
@@ -114,6 +116,9 @@ def call_fwd(lib, a):
     (dict(mu=None, M0=None, k=fake(1, 8)), "MDN_ERR_ALIGN"),  # NULL mu (mu = 0) is allowed
     (dict(beta=fake(8)), "MDN_ERR_ALIAS"),              # output over beta
     (dict(beta=fake(12), M_T=fake(12)), "MDN_ERR_ALIAS"),  # final momentum over beta
+    (dict(Vt=fake(13, 8)), "MDN_ERR_ALIGN"),            # the optional residual output
+    (dict(Vt=fake(8)), "MDN_ERR_ALIAS"),                # residuals over O
+    (dict(Vt=fake(2)), "MDN_ERR_ALIAS"),                # residuals over v
 ])
 def test_chunk_fwd_rejects(lib, over, status):
     assert mdn.STATUS_NAMES[call_fwd(lib, fwd_args(**over))] == status

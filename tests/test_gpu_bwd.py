@@ -30,7 +30,7 @@ NAMES = ("dq", "dk", "dv", "dalpha", "dmu", "deta", "dbeta", "dS0", "dM0")
 
 
 def run_case(cfg, *, seed=5, terminal=True, mu_null=False, with_beta=False, label="",
-             heads=None):
+             heads=None, saved=False):
     """heads: (b, h) pairs to compare (all when None); the GPU always runs the
     whole workload."""
     inp = si.make_forward(cfg)
@@ -40,13 +40,19 @@ def run_case(cfg, *, seed=5, terminal=True, mu_null=False, with_beta=False, labe
             0.2, 1.0, inp["alpha"].shape).astype(np.float32)
     mu = None if mu_null else inp["mu"]
     dt = TORCH_DT[cfg.io_dtype]
-    print(f"bwd {label} B{cfg.B} T{cfg.T} H{cfg.H} d{cfg.Dk}x{cfg.Dv} {cfg.io_dtype} "
+    print(f"bwd {label}{' saved' if saved else ''} B{cfg.B} T{cfg.T} H{cfg.H} d{cfg.Dk}x{cfg.Dv} {cfg.io_dtype} "
           f"mu={'no' if mu_null else 'yes'} beta={'yes' if inp['beta'] is not None else 'no'} "
           f"S0={'yes' if inp['S0'] is not None else 'no'} terminal={terminal}", flush=True)
-    g = mdn.chunk_bwd(to_dev(inp["q"], dt), to_dev(inp["k"], dt), to_dev(inp["v"], dt),
-                      to_dev(inp["alpha"]), None if mu_null else to_dev(mu), to_dev(inp["eta"]),
-                      to_dev(inp["S0"]), to_dev(inp["M0"]), to_dev(cot["dO"], dt),
-                      to_dev(cot["dS_T"]), to_dev(cot["dM_T"]), beta=to_dev(inp["beta"]))
+    fargs = (to_dev(inp["q"], dt), to_dev(inp["k"], dt), to_dev(inp["v"], dt),
+             to_dev(inp["alpha"]), None if mu_null else to_dev(mu), to_dev(inp["eta"]),
+             to_dev(inp["S0"]), to_dev(inp["M0"]))
+    Vt = None
+    if saved:
+        # the residuals the forward saves, then the backward that rebuilds from them
+        Vt = torch.empty_like(fargs[2])
+        mdn.chunk_fwd(*fargs, beta=to_dev(inp["beta"]), Vt=Vt)
+    g = mdn.chunk_bwd(*fargs, to_dev(cot["dO"], dt), to_dev(cot["dS_T"]), to_dev(cot["dM_T"]),
+                      beta=to_dev(inp["beta"]), Vt=Vt)
     torch.cuda.synchronize()
     mu_ref = np.zeros_like(inp["alpha"]) if mu_null else mu
     tok = lambda x: None if x is None else (x if heads is None else gather_heads(x, heads))
@@ -156,3 +162,61 @@ def test_bwd_deterministic():
     for name in NAMES:
         if g1[name] is not None:
             assert torch.equal(g1[name], g2[name]), name
+
+
+@pytest.mark.parametrize("T", [37, 200])
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (64, 128)])
+def test_bwd_saved_residuals_fp32(T, dims):
+    """The forward saves Vt (fp32 split path); the backward rebuilds the
+    states from it."""
+    cfg = si.replace(SMALL, B=2, T=T, H=2, Dk=dims[0], Dv=dims[1], init_state_std=0.5,
+                     seed=si.SEED_BASE + 350 + T)
+    run_case(cfg, label="small", saved=True)
+
+
+@pytest.mark.parametrize("T", [65, 200])
+def test_bwd_saved_residuals_bf16(T):
+    """The fused bf16 forward saves Vt; beta and no mu as well."""
+    cfg = si.replace(SMALL, B=1, T=T, H=2, Dk=128, Dv=128, io_dtype="bf16",
+                     init_state_std=0.5, seed=si.SEED_BASE + 360 + T)
+    run_case(cfg, label="bf16", saved=True)
+    run_case(cfg, label="bf16 mu0 beta", saved=True, mu_null=True, with_beta=True)
+
+
+def test_bwd_saved_residuals_config2_sampled_heads():
+    heads = [(0, 3), (3, 12), (7, 6)]
+    run_case(si.CONFIGS[2], seed=13, label="config 2", heads=heads, saved=True)
+
+
+@pytest.mark.parametrize("io,dims,T", [("f32", (64, 64), 200), ("f32", (128, 64), 65),
+                                       ("bf16", (128, 128), 200), ("bf16", (64, 128), 37)])
+def test_forward_saves_residuals(io, dims, T):
+    """The residuals mdn_chunk_fwd saves against the oracle's vt_t, and the
+    other outputs unchanged (bitwise) by saving them."""
+    from parity import assert_close
+
+    cfg = si.replace(SMALL, B=2, T=T, H=3, Dk=dims[0], Dv=dims[1], io_dtype=io,
+                     init_state_std=0.3, seed=si.SEED_BASE + 370 + T)
+    inp = si.make_forward(cfg)
+    dt = TORCH_DT[io]
+    args = (to_dev(inp["q"], dt), to_dev(inp["k"], dt), to_dev(inp["v"], dt), to_dev(inp["alpha"]),
+            to_dev(inp["mu"]), to_dev(inp["eta"]), to_dev(inp["S0"]), to_dev(inp["M0"]))
+    print(f"residuals {io} d{dims} T{T}", flush=True)
+    Vt = torch.empty_like(args[2])
+    O1, S1, M1 = mdn.chunk_fwd(*args, Vt=Vt)
+    O2, S2, M2 = mdn.chunk_fwd(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(S1, S2) and torch.equal(M1, M2)
+    _, _, _, VT = oracle.recurrence(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["mu"],
+                                    inp["eta"], None, inp["S0"], inp["M0"], return_vt=True)
+    if io == "f32":
+        assert_close(to_np(Vt), VT, io, "Vt")
+    else:
+        # bf16: the residuals reach several units (v is unit scale), and storing
+        # one in bf16 alone moves it by up to 2^-8 of itself; with the forward's
+        # bf16-operand arithmetic: |x - x*| <= 1e-2 max|x*| (measured <= 4e-3)
+        x = to_np(Vt)
+        err = float(np.max(np.abs(x - VT)))
+        mx = float(np.max(np.abs(VT)))
+        print(f"  Vt: max|err|={err:.3e} max|ref|={mx:.3e} rel={err / mx:.3e} (tol 1e-2)")
+        assert np.all(np.isfinite(x)) and err <= 1e-2 * mx
