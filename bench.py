@@ -82,34 +82,45 @@ GATE_TAU = (2048 / 16) ** 0.5            # the temperature sqrt(d_in / h) at d_i
 # 131,072.0).  An entry that covers several kernels of one call sums their dispatches.
 # Figures and commands: profiles/chunk_fwd_fused_B8H16T4096d128.md,
 # profiles/chunk_fwd_split_B8H16T4096d128.md, profiles/decode_step_N256H16d128.md and
-# profiles/gates_from_logits_B8H16T4096.md and profiles/chunk_bwd_B8H16T4096d128.md.
+# profiles/gates_from_logits_B8H16T4096.md, profiles/chunk_bwd_B8H16T4096d128.md and
+# profiles/layer_prologue_epilogue_B8H16T4096d128.md.
 # A kernel whose sources changed reports traffic null.
 FETCH_FACTOR = 262144.0 / 131093.9
 WRITE_FACTOR = 131072.0 / 131072.0
 CSRC = os.path.join(ROOT, "chunkwise_delta_rule_amd", "csrc")
-_SPLIT_SHA = "350d9d1fdd4d8c52823618a5f4545940c3716fc90611689eb634f3e80eab581a"
+_SPLIT_SHA = "8af5c737255c1507ac8eae24ed24c172deed445ad75cc8377ea217c8d71e70d4"
+_BWD_SHA = "0038cd3499bfe9d730ffa62cb0de3214e8f4c1f96d79d50262b66c405717f21c"
+_LIO_SHA = "627a8009335ec269a3313bb348dbbb8e2230dded01b1dfc19a85d20d78a2a663"
 TRAFFIC = {
-    # chunk_coef_kernel (3,109.0 / 51,461.7) + chunk_fwd_fused_kernel (223,496.4 / 147,456.1):
+    # chunk_coef_kernel (3,109.0 / 51,459.4) + chunk_fwd_fused_kernel (223,498.9 / 147,456.1):
     # one mdn_chunk_fwd call, the unit the bench times
     "chunk_fwd_fused_kernel": dict(sources=("chunk_fused.hip", "chunk_common.hpp", "mfma.hpp"),
-                                   fetch_kib=3109.0 + 223496.4, write_kib=51461.7 + 147456.1,
-                                   sha256="606172cabe668f8521453009dba7525a"
-                                   "7acf9d7156fa31b51ed5b4de8104de16"),
+                                   fetch_kib=3109.0 + 223498.9, write_kib=51459.4 + 147456.1,
+                                   sha256="6974036122debe9ff2a7e566310281d9"
+                                   "cf59d301d216a22c7c443e2b7b4b602e"),
     "chunk_scan_bf16_kernel": dict(sources=("chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
-                                   fetch_kib=268392.0, write_kib=147456.4, sha256=_SPLIT_SHA),
+                                   fetch_kib=268388.0, write_kib=147457.8, sha256=_SPLIT_SHA),
     "chunk_prep_kernel": dict(sources=("chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
-                              fetch_kib=134528.7, write_kib=144054.7, sha256=_SPLIT_SHA),
+                              fetch_kib=134785.1, write_kib=144779.8, sha256=_SPLIT_SHA),
     "decode_step_kernel": dict(sources=("decode.hip", "mfma.hpp"), fetch_kib=264109.0,
-                               write_kib=525523.8, sha256="8fa39113008b99235e1abe57028f0d81"
+                               write_kib=525524.5, sha256="8fa39113008b99235e1abe57028f0d81"
                                "9b837f475aa87000a6b4e46e3ea6c4e5"),
-    # chunk_prep_kernel (134,557.9 / 144,101.2) + bwd_scan_kernel (471,264.1 / 1,310,723.9) +
-    # bwd_rescan_kernel (274,559.5 / 1,310,720.5) + bwd_grad_kernel (3,453,358.1 / 982,657.3):
-    # one mdn_chunk_bwd call
+    # one mdn_chunk_bwd call with the forward's saved residuals: chunk_prep_kernel
+    # (134,785.1 / 144,779.8) + bwd_scan_kernel (471,265.3 / 786,432.2) + bwd_rescan_kernel
+    # with saved residuals (208,988.2 / 524,288.1) + bwd_grad_kernel (1,943,813.0 / 917,881.7)
     "chunk_bwd": dict(sources=("chunk_bwd.hip", "chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
-                      fetch_kib=134557.9 + 471264.1 + 274559.5 + 3453358.1,
-                      write_kib=144101.2 + 1310723.9 + 1310720.5 + 982657.3,
-                      sha256="6c75187aa75d4ad6450fa082c40bcdf7"
-                      "1cf7ab7c4821ae8842e177540bd3530c"),
+                      fetch_kib=134785.1 + 471265.3 + 208988.2 + 1943813.0,
+                      write_kib=144779.8 + 786432.2 + 524288.1 + 917881.7, sha256=_BWD_SHA),
+    # the same recomputing the residuals: bwd_rescan_kernel (274,564.2 / 786,432.3)
+    "chunk_bwd_recompute": dict(sources=("chunk_bwd.hip", "chunk_fwd.hip", "chunk_common.hpp",
+                                         "mfma.hpp"),
+                                fetch_kib=134785.1 + 471265.3 + 274564.2 + 1943813.0,
+                                write_kib=144779.8 + 786432.2 + 786432.3 + 917881.7,
+                                sha256=_BWD_SHA),
+    "qk_prologue_kernel": dict(sources=("layer_io.hip", "mfma.hpp"), fetch_kib=131099.8,
+                               write_kib=262144.0, sha256=_LIO_SHA),
+    "output_epilogue_kernel": dict(sources=("layer_io.hip", "mfma.hpp"), fetch_kib=131096.9,
+                                   write_kib=131072.0, sha256=_LIO_SHA),
     "gates_kernel": dict(sources=("gates.hip",), fetch_kib=4114.0, write_kib=8192.0,
                          sha256="2bde382d2f924a1318325130cdb94dab"
                          "7d2b47dcae9f102ec3b939b9dde52ce6"),
@@ -383,13 +394,13 @@ def bench_backward(args, torch, si, mdn, cfg, inp):
             "recompute_tokens_per_s": B * T / (us_re * 1e-6),
             "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP32_MFMA / 1e12,
                          "unit": "TFLOP/s", "frac": flop_saved / (us * 1e-6) / PEAK_FP32_MFMA,
-                         "traffic": None, "algorithmic_flop": flop_saved,
+                         "traffic": traffic_bytes("chunk_bwd"), "algorithmic_flop": flop_saved,
                          "algorithmic_bytes": BYTES_BWD_SAVED * toh,
                          "hbm_frac": BYTES_BWD_SAVED * toh / (us * 1e-6) / PEAK_HBM_BPS},
             "recompute_roofline": {"bound": "mfma", "achieved": flop / (us_re * 1e-6) / 1e12,
                                    "peak": PEAK_FP32_MFMA / 1e12, "unit": "TFLOP/s",
                                    "frac": flop / (us_re * 1e-6) / PEAK_FP32_MFMA,
-                                   "traffic": traffic_bytes("chunk_bwd"),
+                                   "traffic": traffic_bytes("chunk_bwd_recompute"),
                                    "algorithmic_flop": flop,
                                    "algorithmic_bytes": BYTES_BWD * toh}}
 
