@@ -31,9 +31,10 @@
 // gamma_{i,j} = alpha_i gamma_{i-1,j} + beta_i m_{i,j}, m_{i,j} = mu_i m_{i-1,j})
 // and the direct uses of eta (Khat, ws, wm) and alpha (P, ab1).
 //
-// This version takes nothing from the forward call: it recomputes Vt (the
-// re-scan below runs the forward's solve again) and keeps each chunk's entry
-// state and exit-state gradients in its workspace only while it runs.
+// Given the residuals Vt that the forward saved, the re-scan below rebuilds
+// the chunk-entry states from them with no solve; given none, it runs the
+// forward's solve again.  Each chunk's entry state and exit-state gradients
+// are kept in the workspace (in the I/O type) only while the call runs.
 //
 // Kernels, in launch order (after chunk_prep_kernel has written T, A and the
 // coefficient rows of every chunk):
@@ -41,13 +42,17 @@
 //                       to first: dVt, dR (written as dv), the state gradients
 //                       carried back, and each chunk's exit-state gradients
 //                       stored for the last kernel.
-//   bwd_rescan_kernel   the same grid, chunks first to last: the forward's
-//                       R, Vt = T R and state update again, storing each
-//                       chunk's entry state and Vt.
+//   bwd_rescan_kernel   the same grid, chunks first to last: the state update
+//                       again (with R and Vt = T R unless Vt was saved),
+//                       storing each chunk's entry state (and Vt).
 //   bwd_grad_kernel     one workgroup per chunk, all columns: dq, dk and the
 //                       gate gradients.
-// All arithmetic is fp32 (v_mfma_f32_16x16x4_f32 and VALU); bf16 inputs are
-// widened when they are staged into LDS.
+// Arithmetic is fp32 (v_mfma_f32_16x16x4_f32 and VALU; bf16 inputs are
+// widened when they are staged into LDS), except that with bf16 I/O
+// bwd_grad_kernel runs on v_mfma_f32_16x16x32_bf16 the six products of a row
+// operand with a stored bf16 state (the row operand rounded to bf16: exact
+// for dO and for saved Vt) and the chunk products dO Vt^T, K K^T and Q K^T
+// (exact operands, but for a recomputed Vt).
 #include <hip/hip_runtime.h>
 
 #include "chunk_common.hpp"
@@ -763,6 +768,30 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
                 sva[kb][dt] =
                     *reinterpret_cast<const uint4*>(St + (size_t)d * DV + KB * kb + SV * lg);
             }
+        if constexpr (sizeof(E) == 2) {
+            // bf16 states: one 16x16x32 bf16 step per block of 32 columns.  The
+            // lane's 16-byte load of a state row is its B fragment as it stands
+            // (k = 32 kb + 8 lg + j); the A fragment is the same 8 columns of
+            // X's row, rounded to bf16 (exact for dO and for saved Vt).
+#pragma unroll
+            for (int kb = 0; kb < DV / KB; ++kb) {
+                bf16x8 bv[DT];
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) bv[dt] = __builtin_bit_cast(bf16x8, sva[kb][dt]);
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const float* xr = X + (16 * it + l16) * LD + KB * kb + SV * lg;
+                    const float4 x0 = *reinterpret_cast<const float4*>(xr);
+                    const float4 x1 = *reinterpret_cast<const float4*>(xr + 4);
+                    const bf16x8 a = {(__bf16)x0.x, (__bf16)x0.y, (__bf16)x0.z, (__bf16)x0.w,
+                                      (__bf16)x1.x, (__bf16)x1.y, (__bf16)x1.z, (__bf16)x1.w};
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt)
+                        acc[it][dt] = Mma<__bf16>::mma(a, bv[dt], acc[it][dt]);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int kb = 0; kb < DV / KB; ++kb) {
             float sv[DT][SV];
@@ -834,6 +863,28 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
         }
     };
 
+    // the same on bf16 MFMA, for operands that hold bf16 values (inputs in the
+    // I/O type and saved Vt): one 16x16x32 step per 32 columns, lane group lg
+    // taking columns 32 kb + 8 lg .. 32 kb + 8 lg + 7 of both rows
+    auto cc_product_bf16 = [&](const float* X, const float* Y, int KD, f32x4* acc) {
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) acc[jt] = zero4();
+        auto frag = [](const float* p) {
+            const float4 u = *reinterpret_cast<const float4*>(p);
+            const float4 w = *reinterpret_cast<const float4*>(p + 4);
+            return bf16x8{(__bf16)u.x, (__bf16)u.y, (__bf16)u.z, (__bf16)u.w,
+                          (__bf16)w.x, (__bf16)w.y, (__bf16)w.z, (__bf16)w.w};
+        };
+        for (int kb = 0; kb < KD / 32; ++kb) {
+            const bf16x8 a = frag(X + (16 * wave + l16) * LD + 32 * kb + 8 * lg);
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt)
+                acc[jt] = Mma<__bf16>::mma(a, frag(Y + (16 * jt + l16) * LD + 32 * kb + 8 * lg),
+                                           acc[jt]);
+        }
+    };
+    constexpr bool BF = sizeof(E) == 2;
+
     f32x4 dQa[4][DT], dKa[4][DT], P1[4][DT], P2[4][DT];
     f32x4 cA[4], cL[4], cK[4];   // C x C tiles: dA, dL, K K^T (row tile = wave)
 
@@ -860,7 +911,9 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
     }
     __syncthreads();
     // dA = dO Vt^T (lower triangle with the diagonal kept below)
-    cc_product(slot1, slot0, DV, 1.f, cA);
+    // (Vt recomputed in fp32 is rounded here, as in its state products)
+    if constexpr (BF) cc_product_bf16(slot1, slot0, DV, cA);
+    else cc_product(slot1, slot0, DV, 1.f, cA);
     state_product(slot1, S0, P1);   // dO S0^T
     state_product(slot1, M0, P2);   // dO M0^T
 #pragma unroll
@@ -889,7 +942,8 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
     }
     __syncthreads();
     cc_product(slot1, slot0, DV, -1.f, cL);
-    cc_product(slot2, slot2, DK, 1.f, cK);
+    if constexpr (BF) cc_product_bf16(slot2, slot2, DK, cK);
+    else cc_product(slot2, slot2, DK, 1.f, cK);
     state_product(slot1, S0, P1);   // dR S0^T
     state_product(slot1, M0, P2);   // dR M0^T
 #pragma unroll
@@ -922,7 +976,8 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
     stage<DK, LD>(slot1, q + tok0 * DK, (size_t)H * DK, n, tid);
     __syncthreads();
     f32x4 cQ[4];
-    cc_product(slot1, slot2, DK, 1.f, cQ);
+    if constexpr (BF) cc_product_bf16(slot1, slot2, DK, cQ);
+    else cc_product(slot1, slot2, DK, 1.f, cQ);
     // dGamma from A (dA o Q Khat^T) now, G_L = dL o (P Khat^T) into Cm2 for the
     // one-row shift; dA o Gamma into Cm1, dL o Gamma^- into slot0 (Vt is done)
     float* dAG = Cm1;
