@@ -73,9 +73,10 @@ BYTES_BWD = 4 * D * 2 + 3 * 4 + 3 * D * 4 + 3 * 4
 FLOP_BWD_SAVED = FLOP_BWD - 4 * D * D - 2 * C * D
 BYTES_BWD_SAVED = BYTES_BWD + D * 2
 PEAK_FP32_MFMA = 157.3e12       # MI355X dense fp32 matrix
-# for bf16 I/O the per-chunk kernel's six state products (2 d^2 each per token and head)
-# run on bf16 MFMA against the bf16-stored states; the rest of the backward is fp32
-FLOP_BWD_BF16 = 12 * D * D
+# for bf16 I/O these run on bf16 MFMA: the reverse scan's products (12 d^2 + 4 C d), the
+# per-chunk kernel's six state products (12 d^2) and its chunk products dO Vt^T, K K^T,
+# Q K^T (6 C d); the rest of the backward (prepare, re-scan, masked products) is fp32
+FLOP_BWD_BF16 = 24 * D * D + 10 * C * D
 
 
 def mixed_peak(flop, flop_bf16):
@@ -399,15 +400,15 @@ def bench_backward(args, torch, si, mdn, cfg, inp):
     log(f"backward: {us:.1f} us/step with saved residuals ({tf:.1f} TFLOP/s of dense work, "
         f"mixed peak {peak_saved / 1e12:.1f}), {us_re:.1f} us/step recomputing them")
     return {"workload": f"mdn_chunk_bwd on {cfg.name}: dO ~ N(0, 1), all gradients, the "
-                        "forward's saved residuals; fp32 arithmetic (fp32 MFMA) except the "
-                        "six state products per chunk (bf16 MFMA on the bf16-stored states)",
+                        "forward's saved residuals; the reverse scan and most per-chunk products on "
+                        "bf16 MFMA, the rest fp32 (fp32 MFMA)",
             "us_per_step": us, "tokens_per_s": B * T / (us * 1e-6), "steps_timed": steps,
             "recompute_us_per_step": us_re,
             "recompute_tokens_per_s": B * T / (us_re * 1e-6),
             "roofline": {"bound": "mfma", "achieved": tf, "peak": peak_saved / 1e12,
                          "unit": "TFLOP/s", "frac": flop_saved / (us * 1e-6) / peak_saved,
-                         "peak_of": "mix: state products at the bf16 peak (2.5 PFLOP/s), the "
-                                    "rest at the fp32 matrix peak (157.3 TFLOP/s)",
+                         "peak_of": "mix: the bf16 products at the bf16 peak (2.5 PFLOP/s), "
+                                    "the rest at the fp32 matrix peak (157.3 TFLOP/s)",
                          "algorithmic_flop_bf16": fb,
                          "traffic": traffic_bytes("chunk_bwd"), "algorithmic_flop": flop_saved,
                          "algorithmic_bytes": BYTES_BWD_SAVED * toh,

@@ -187,7 +187,23 @@ __global__ __launch_bounds__(NT) void bwd_scan_kernel(
     __shared__ __align__(16) float Gs[CH * LDV];   // dO, this workgroup's columns
     __shared__ __align__(16) float Ts[CH * LDC];
     __shared__ __align__(16) float As[CH * LDC];
-    __shared__ float vecs[6 * CH];
+    __shared__ __align__(16) float vecs[6 * CH];
+    // bf16 I/O: every product below runs on 16x16x32 bf16 steps in the k
+    // order of Mma<__bf16>::perm_row.  q, k, dO, T and A are exact in bf16;
+    // the carried dS', dM' are rounded to bf16 in K dS', K dM' (the rounding
+    // their copies in Hd get); the fp32 intermediates (dVt and the gate-scaled
+    // rows of dO and dR) are split into a bf16 head and a bf16 remainder, two
+    // steps each, about 16 bits.  All sums and the carried state gradients
+    // stay fp32.
+    constexpr bool BF = sizeof(E) == 2;
+    using MB = Mma<__bf16>;
+    auto split8 = [](const float* x, bf16x8& hd, bf16x8& rs) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            hd[j] = static_cast<__bf16>(x[j]);
+            rs[j] = static_cast<__bf16>(x[j] - static_cast<float>(hd[j]));
+        }
+    };
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -267,6 +283,24 @@ __global__ __launch_bounds__(NT) void bwd_scan_kernel(
         f32x4 xs[4], xm[4];
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) xs[ct] = xm[ct] = zero4();
+        if constexpr (BF) {
+            // (dS' and dM' get the rounding their copies in Hd get)
+#pragma unroll
+            for (int s2 = 0; s2 < DK / 32; ++s2) {
+                const bf16x8 bS = Mma<__bf16>::from_acc(Sa, s2);
+                const bf16x8 bM = Mma<__bf16>::from_acc(Ma, s2);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    const float* kp = Ks + (16 * ct + l16) * LDK + 32 * s2 + 4 * lg;
+                    const float4 u = *reinterpret_cast<const float4*>(kp);
+                    const float4 w = *reinterpret_cast<const float4*>(kp + 16);
+                    const bf16x8 aK = {(__bf16)u.x, (__bf16)u.y, (__bf16)u.z, (__bf16)u.w,
+                                       (__bf16)w.x, (__bf16)w.y, (__bf16)w.z, (__bf16)w.w};
+                    xs[ct] = Mma<__bf16>::mma(aK, bS, xs[ct]);
+                    xm[ct] = Mma<__bf16>::mma(aK, bM, xm[ct]);
+                }
+            }
+        } else
 #pragma unroll
         for (int sb = 0; sb < DK / 16; ++sb) {
             float4 a4[4];
@@ -296,6 +330,22 @@ __global__ __launch_bounds__(NT) void bwd_scan_kernel(
                 const int i = 16 * it + 4 * lg + r;
                 dVt[it][r] = vecs[V_WS * CH + i] * xs[it][r] - vecs[V_WM * CH + i] * xm[it][r];
             }
+        if constexpr (BF) {
+#pragma unroll
+            for (int s2 = 0; s2 < CH / 32; ++s2) {
+                bf16x8 bO;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) bO[j] = (__bf16)Gs[MB::perm_row(s2, lg, j) * LDV + lcol];
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    bf16x8 aA;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        aA[j] = (__bf16)As[MB::perm_row(s2, lg, j) * LDC + 16 * it + l16];
+                    dVt[it] = MB::mma(aA, bO, dVt[it]);
+                }
+            }
+        } else
 #pragma unroll
         for (int s = 0; s < CH / 4; ++s) {
             const int kr = MF::perm_row(s, lg, 0);
@@ -309,6 +359,28 @@ __global__ __launch_bounds__(NT) void bwd_scan_kernel(
         f32x4 dR[4];
 #pragma unroll
         for (int it = 0; it < 4; ++it) dR[it] = zero4();
+        if constexpr (BF) {
+#pragma unroll
+            for (int s2 = 0; s2 < CH / 32; ++s2) {
+                float x[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    x[j] = dVt[2 * s2][j];
+                    x[4 + j] = dVt[2 * s2 + 1][j];
+                }
+                bf16x8 vh, vr;
+                split8(x, vh, vr);
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    bf16x8 aT;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        aT[j] = (__bf16)Ts[MB::perm_row(s2, lg, j) * LDC + 16 * it + l16];
+                    dR[it] = MB::mma(aT, vh, dR[it]);
+                    dR[it] = MB::mma(aT, vr, dR[it]);
+                }
+            }
+        } else
 #pragma unroll
         for (int s = 0; s < CH / 4; ++s) {
             const float bV = MF::from_acc(dVt, s);
@@ -339,6 +411,58 @@ __global__ __launch_bounds__(NT) void bwd_scan_kernel(
             Sa[rt] = abn * so;
             Ma[rt] = mbn * Ma[rt] - bn * so;
         }
+        if constexpr (BF) {
+#pragma unroll
+            for (int s2 = 0; s2 < CH / 32; ++s2) {
+                float xs8[8], xm8[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int kr = MB::perm_row(s2, lg, j);
+                    const float g = Gs[kr * LDV + lcol];
+                    xs8[j] = vecs[V_ABAR * CH + kr] * g;
+                    xm8[j] = -vecs[V_B * CH + kr] * g;
+                }
+                bf16x8 sh, sr, mh, mr;
+                split8(xs8, sh, sr);
+                split8(xm8, mh, mr);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    bf16x8 aQ;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        aQ[j] = (__bf16)Qs[MB::perm_row(s2, lg, j) * LDK + 16 * rt + l16];
+                    Sa[rt] = MB::mma(aQ, sh, Sa[rt]);
+                    Sa[rt] = MB::mma(aQ, sr, Sa[rt]);
+                    Ma[rt] = MB::mma(aQ, mh, Ma[rt]);
+                    Ma[rt] = MB::mma(aQ, mr, Ma[rt]);
+                }
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < CH / 32; ++s2) {
+                float xs8[8], xm8[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int kr = MB::perm_row(s2, lg, j);
+                    const float r = j < 4 ? dR[2 * s2][j] : dR[2 * s2 + 1][j - 4];
+                    xs8[j] = -vecs[V_ABAR * CH + kr] * r;
+                    xm8[j] = vecs[V_AB1 * CH + kr] * r;
+                }
+                bf16x8 sh, sr, mh, mr;
+                split8(xs8, sh, sr);
+                split8(xm8, mh, mr);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    bf16x8 aK;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        aK[j] = (__bf16)Ks[MB::perm_row(s2, lg, j) * LDK + 16 * rt + l16];
+                    Sa[rt] = MB::mma(aK, sh, Sa[rt]);
+                    Sa[rt] = MB::mma(aK, sr, Sa[rt]);
+                    Ma[rt] = MB::mma(aK, mh, Ma[rt]);
+                    Ma[rt] = MB::mma(aK, mr, Ma[rt]);
+                }
+            }
+        } else {
 #pragma unroll
         for (int s = 0; s < CH / 4; ++s) {
             const int kr = MF::perm_row(s, lg, 0);
@@ -363,6 +487,7 @@ __global__ __launch_bounds__(NT) void bwd_scan_kernel(
                 Sa[rt] = MF::mma(aK, bS, Sa[rt]);
                 Ma[rt] = MF::mma(aK, bM, Ma[rt]);
             }
+        }
         }
     }
 
