@@ -64,7 +64,7 @@ BYTES_PROLOGUE = 2 * D * 2 + 2 * D * 2   # q, k in and out (bf16)
 BYTES_EPILOGUE = 2 * D * 2 + D * 2       # o, gate in, y out (bf16)
 # backward (mdn_chunk_bwd), dense products per token and head: prepare 4 C d; reverse scan
 # 12 d^2 + 4 C d; re-scan 8 d^2 + 2 C d; per-chunk gradients 12 d^2 + 16 C d
-FLOP_BWD = 32 * D * D + 30 * C * D
+FLOP_BWD = 32 * D * D + 26 * C * D
 # what it must read and write once: q, k, v, dO (bf16), three gates in, dq, dk, dv (fp32)
 # and three gate gradients out, plus S0, M0 read / dS0, dM0 written per (b, h) (zero here)
 BYTES_BWD = 4 * D * 2 + 3 * 4 + 3 * D * 4 + 3 * 4
@@ -74,9 +74,11 @@ FLOP_BWD_SAVED = FLOP_BWD - 4 * D * D - 2 * C * D
 BYTES_BWD_SAVED = BYTES_BWD + D * 2
 PEAK_FP32_MFMA = 157.3e12       # MI355X dense fp32 matrix
 # for bf16 I/O these run on bf16 MFMA: the reverse scan's products (12 d^2 + 4 C d), the
-# per-chunk kernel's six state products (12 d^2) and its chunk products dO Vt^T, K K^T,
-# Q K^T (6 C d); the rest of the backward (prepare, re-scan, masked products) is fp32
-FLOP_BWD_BF16 = 24 * D * D + 10 * C * D
+# re-scan's (8 d^2 + 2 C d; 4 d^2 with saved residuals), the per-chunk kernel's six state
+# products (12 d^2) and its chunk products dO Vt^T, K K^T, Q K^T (6 C d); the rest (prepare,
+# the chunk product dR Vt^T and the masked products, 14 C d) is fp32
+FLOP_BWD_BF16 = 32 * D * D + 12 * C * D
+FLOP_BWD_BF16_SAVED = 28 * D * D + 10 * C * D
 
 
 def mixed_peak(flop, flop_bf16):
@@ -395,13 +397,13 @@ def bench_backward(args, torch, si, mdn, cfg, inp):
         out[name] = span * 1e3
     us, us_re = out["saved"], out["recompute"]
     tf = flop_saved / (us * 1e-6) / 1e12
-    fb = FLOP_BWD_BF16 * toh
-    peak_saved, peak_re = mixed_peak(flop_saved, fb), mixed_peak(flop, fb)
+    fb = FLOP_BWD_BF16_SAVED * toh
+    peak_saved, peak_re = mixed_peak(flop_saved, fb), mixed_peak(flop, FLOP_BWD_BF16 * toh)
     log(f"backward: {us:.1f} us/step with saved residuals ({tf:.1f} TFLOP/s of dense work, "
         f"mixed peak {peak_saved / 1e12:.1f}), {us_re:.1f} us/step recomputing them")
     return {"workload": f"mdn_chunk_bwd on {cfg.name}: dO ~ N(0, 1), all gradients, the "
-                        "forward's saved residuals; the reverse scan and most per-chunk products on "
-                        "bf16 MFMA, the rest fp32 (fp32 MFMA)",
+                        "forward's saved residuals; both scans and most per-chunk products on bf16 "
+                        "MFMA, the rest fp32 (fp32 MFMA)",
             "us_per_step": us, "tokens_per_s": B * T / (us * 1e-6), "steps_timed": steps,
             "recompute_us_per_step": us_re,
             "recompute_tokens_per_s": B * T / (us_re * 1e-6),

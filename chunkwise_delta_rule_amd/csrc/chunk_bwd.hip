@@ -48,11 +48,13 @@
 //   bwd_grad_kernel     one workgroup per chunk, all columns: dq, dk and the
 //                       gate gradients.
 // Arithmetic is fp32 (v_mfma_f32_16x16x4_f32 and VALU; bf16 inputs are
-// widened when they are staged into LDS), except that with bf16 I/O
-// bwd_grad_kernel runs on v_mfma_f32_16x16x32_bf16 the six products of a row
-// operand with a stored bf16 state (the row operand rounded to bf16: exact
-// for dO and for saved Vt) and the chunk products dO Vt^T, K K^T and Q K^T
-// (exact operands, but for a recomputed Vt).
+// widened when they are staged into LDS), except that with bf16 I/O the two
+// scans run all their products on v_mfma_f32_16x16x32_bf16 (each kernel
+// states which operands are exact in bf16, which are rounded and which are
+// split into two bf16 parts), and bwd_grad_kernel runs the six products of a
+// row operand with a stored bf16 state (the row operand rounded to bf16:
+// exact for dO and for saved Vt) and the chunk products dO Vt^T, K K^T and
+// Q K^T (exact operands, but for a recomputed Vt) on it.
 #include <hip/hip_runtime.h>
 
 #include "chunk_common.hpp"
@@ -522,6 +524,20 @@ __global__ __launch_bounds__(NT) void bwd_rescan_kernel(
     __shared__ __align__(16) float Vs[CH * LDV];
     __shared__ __align__(16) float Ts[CH * LDC];
     __shared__ float vecs[6 * CH];
+    // bf16 I/O: the products run on 16x16x32 bf16 steps in the k order of
+    // Mma<__bf16>::perm_row with fp32 sums.  k and T are exact in bf16; S and M
+    // are rounded to bf16 in K S, K M, as in the forward; R and the
+    // weight-scaled rows of Vt are split into a bf16 head and a bf16
+    // remainder, two steps each, about 16 bits.  The carried states stay fp32.
+    constexpr bool BF = sizeof(E) == 2;
+    using MB = Mma<__bf16>;
+    auto split8 = [](const float* x, bf16x8& hd, bf16x8& rs) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            hd[j] = static_cast<__bf16>(x[j]);
+            rs[j] = static_cast<__bf16>(x[j] - static_cast<float>(hd[j]));
+        }
+    };
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -598,6 +614,23 @@ __global__ __launch_bounds__(NT) void bwd_rescan_kernel(
         f32x4 xs[4], xm[4];
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) xs[ct] = xm[ct] = zero4();
+        if constexpr (BF) {
+#pragma unroll
+            for (int s2 = 0; s2 < DK / 32; ++s2) {
+                const bf16x8 bS = MB::from_acc(Sa, s2);
+                const bf16x8 bM = MB::from_acc(Ma, s2);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    const float* kp = Ks + (16 * ct + l16) * LDK + 32 * s2 + 4 * lg;
+                    const float4 u = *reinterpret_cast<const float4*>(kp);
+                    const float4 w = *reinterpret_cast<const float4*>(kp + 16);
+                    const bf16x8 aK = {(__bf16)u.x, (__bf16)u.y, (__bf16)u.z, (__bf16)u.w,
+                                       (__bf16)w.x, (__bf16)w.y, (__bf16)w.z, (__bf16)w.w};
+                    xs[ct] = MB::mma(aK, bS, xs[ct]);
+                    xm[ct] = MB::mma(aK, bM, xm[ct]);
+                }
+            }
+        } else
 #pragma unroll
         for (int sb = 0; sb < DK / 16; ++sb) {
             float4 a4[4];
@@ -628,6 +661,29 @@ __global__ __launch_bounds__(NT) void bwd_rescan_kernel(
             }
 #pragma unroll
         for (int it = 0; it < 4; ++it) Vt[it] = zero4();
+        if constexpr (BF) {
+#pragma unroll
+            for (int s2 = 0; s2 < CH / 32; ++s2) {
+                float x[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    x[j] = R[2 * s2][j];
+                    x[4 + j] = R[2 * s2 + 1][j];
+                }
+                bf16x8 rh, rr;
+                split8(x, rh, rr);
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const float* tp = Ts + (16 * it + l16) * LDC + 32 * s2 + 4 * lg;
+                    const float4 u = *reinterpret_cast<const float4*>(tp);
+                    const float4 w = *reinterpret_cast<const float4*>(tp + 16);
+                    const bf16x8 aT = {(__bf16)u.x, (__bf16)u.y, (__bf16)u.z, (__bf16)u.w,
+                                       (__bf16)w.x, (__bf16)w.y, (__bf16)w.z, (__bf16)w.w};
+                    Vt[it] = MB::mma(aT, rh, Vt[it]);
+                    Vt[it] = MB::mma(aT, rr, Vt[it]);
+                }
+            }
+        } else
 #pragma unroll
         for (int sb = 0; sb < CH / 16; ++sb) {
             float4 t4[4];
@@ -661,6 +717,35 @@ __global__ __launch_bounds__(NT) void bwd_rescan_kernel(
             Sa[rt] = abn * Sa[rt] - bn * Ma[rt];
             Ma[rt] = mbn * Ma[rt];
         }
+        if constexpr (BF) {
+#pragma unroll
+            for (int s2 = 0; s2 < CH / 32; ++s2) {
+                float xs8[8], xm8[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int kr = MB::perm_row(s2, lg, j);
+                    float vt;
+                    if constexpr (SAVED) vt = Vs[kr * LDV + lcol];
+                    else vt = j < 4 ? Vt[2 * s2][j] : Vt[2 * s2 + 1][j - 4];
+                    xs8[j] = vecs[V_WS * CH + kr] * vt;
+                    xm8[j] = -(vecs[V_WM * CH + kr] * vt);
+                }
+                bf16x8 sh, sr, mh, mr;
+                split8(xs8, sh, sr);
+                split8(xm8, mh, mr);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    bf16x8 aK;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        aK[j] = (__bf16)Ks[MB::perm_row(s2, lg, j) * LDK + 16 * rt + l16];
+                    Sa[rt] = MB::mma(aK, sh, Sa[rt]);
+                    Sa[rt] = MB::mma(aK, sr, Sa[rt]);
+                    Ma[rt] = MB::mma(aK, mh, Ma[rt]);
+                    Ma[rt] = MB::mma(aK, mr, Ma[rt]);
+                }
+            }
+        } else
 #pragma unroll
         for (int s = 0; s < CH / 4; ++s) {
             const int kr = MF::perm_row(s, lg, 0);
