@@ -101,7 +101,7 @@ FETCH_FACTOR = 262144.0 / 131093.9
 WRITE_FACTOR = 131072.0 / 131072.0
 CSRC = os.path.join(ROOT, "chunkwise_delta_rule_amd", "csrc")
 _SPLIT_SHA = "8af5c737255c1507ac8eae24ed24c172deed445ad75cc8377ea217c8d71e70d4"
-_BWD_SHA = "0038cd3499bfe9d730ffa62cb0de3214e8f4c1f96d79d50262b66c405717f21c"
+_BWD_SHA = "f902fbd7770cba646f9196b3bd96960b5abf9f88195739e2a05ade050015a2a0"
 _LIO_SHA = "627a8009335ec269a3313bb348dbbb8e2230dded01b1dfc19a85d20d78a2a663"
 TRAFFIC = {
     # chunk_coef_kernel (3,109.0 / 51,459.4) + chunk_fwd_fused_kernel (223,498.9 / 147,456.1):
@@ -118,16 +118,16 @@ TRAFFIC = {
                                write_kib=525524.5, sha256="8fa39113008b99235e1abe57028f0d81"
                                "9b837f475aa87000a6b4e46e3ea6c4e5"),
     # one mdn_chunk_bwd call with the forward's saved residuals: chunk_prep_kernel
-    # (134,785.1 / 144,779.8) + bwd_scan_kernel (471,265.3 / 786,432.2) + bwd_rescan_kernel
-    # with saved residuals (208,988.2 / 524,288.1) + bwd_grad_kernel (1,943,813.0 / 917,881.7)
+    # (134,555.6 / 144,240.5) + bwd_scan_kernel (471,250.7 / 786,432.2) + bwd_rescan_kernel
+    # with saved residuals (208,988.7 / 524,291.0) + bwd_grad_kernel (1,688,671.1 / 552,350.9)
     "chunk_bwd": dict(sources=("chunk_bwd.hip", "chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
-                      fetch_kib=134785.1 + 471265.3 + 208988.2 + 1943813.0,
-                      write_kib=144779.8 + 786432.2 + 524288.1 + 917881.7, sha256=_BWD_SHA),
-    # the same recomputing the residuals: bwd_rescan_kernel (274,564.2 / 786,432.3)
+                      fetch_kib=134555.6 + 471250.7 + 208988.7 + 1688671.1,
+                      write_kib=144240.5 + 786432.2 + 524291.0 + 552350.9, sha256=_BWD_SHA),
+    # the same recomputing the residuals: bwd_rescan_kernel (274,556.1 / 786,432.1)
     "chunk_bwd_recompute": dict(sources=("chunk_bwd.hip", "chunk_fwd.hip", "chunk_common.hpp",
                                          "mfma.hpp"),
-                                fetch_kib=134785.1 + 471265.3 + 274564.2 + 1943813.0,
-                                write_kib=144779.8 + 786432.2 + 786432.3 + 917881.7,
+                                fetch_kib=134555.6 + 471250.7 + 274556.1 + 1688671.1,
+                                write_kib=144240.5 + 786432.2 + 786432.1 + 552350.9,
                                 sha256=_BWD_SHA),
     "qk_prologue_kernel": dict(sources=("layer_io.hip", "mfma.hpp"), fetch_kib=131099.8,
                                write_kib=262144.0, sha256=_LIO_SHA),
