@@ -197,7 +197,12 @@ mdn_status mdn_decode_step(const void* q, const void* k, const void* v, const fl
  * equations of mdn_chunk_fwd, chunk by chunk from the last.  The call takes
  * the residuals Vt the forward saved (or recomputes them when Vt is NULL) and
  * keeps each chunk's entry state and exit-state gradients in the workspace
- * while it runs.
+ * while it runs.  All sums are fp32.  For dt = MDN_F32 every product is
+ * fp32; for dt = MDN_BF16 the stored states are bf16 and most products run on
+ * bf16 matrix instructions, with operands that are bf16 inputs, rounded to
+ * bf16, or split into a bf16 head and remainder (each kernel's comments say
+ * which), so each gradient tensor is accurate to about 1e-2 of its largest
+ * magnitude.
  *   q, k, v, alpha, mu, eta, beta, S0, M0, B, T, H, Dk, Dv, chunk, dt:
  *                         exactly as given to mdn_chunk_fwd (mu, beta, S0, M0
  *                         may be NULL with the same meaning).
