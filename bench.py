@@ -1,6 +1,7 @@
 """Benchmark of the MDN hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--settle SEC] [--decode-steps D] [--no-cpu-baseline]
+                    [--no-backward] [--no-decode] [--no-sweep] [--no-configs] [--no-peaks]
 
 A step is one chunkwise forward (mdn_chunk_fwd: coefficients, Gram products,
 residual solve, outputs and carried state, one fused kernel for bf16) over
@@ -21,10 +22,17 @@ The same JSON line carries:
   forward.from_logits  mdn_gates_from_logits, then the four-gate forward on its gates;
   forward.with_prologue_epilogue  mdn_qk_prologue, the forward, mdn_output_epilogue;
   forward       the whole step against both roofs;
-  backward      mdn_chunk_bwd on the same layer (all gradients), against the fp32 MFMA peak;
+  backward      mdn_chunk_bwd on the same layer (all gradients), against the matrix
+                peak of its mix (bf16 products at the bf16 peak, the rest at fp32's);
   decode        the recurrent decode step at 256 sequences x 16 heads, d 128
                 (GB/s of algorithmic state + token traffic);
+  timing_ab     the headline call timed one call at a time: median of 20 back to
+                back, and median of 20 with a 1 GiB write between calls;
+  other_configs the 400M-like layer (B4 H8 T2048) and the 16K-context layer
+                (B1 H16 T16384) as drawn and with no mu, each with its roofline;
   sweep         tokens/s at T x B = 16384 tokens per call for T = 2K .. 16K;
+  measured_peaks  a dense bf16 MFMA loop and a 2 GiB streaming copy on this GPU,
+                beside the datasheet peaks;
   cpu_baseline  the fp64 oracle timed on this host's cores.
 Rank 0 prints one JSON line; only one GPU is supported.
 """
@@ -150,7 +158,7 @@ def sources_sha256(names):
 
 def traffic_bytes(kernel):
     """Counter-derived HBM bytes per launch, or None when the kernel changed since."""
-    t = TRAFFIC.get(kernel)
+    t = TRAFFIC.get(kernel) if kernel else None
     if t is None or t["sha256"] is None or sources_sha256(t["sources"]) != t["sha256"]:
         return None
     return round(t["fetch_kib"] * 1024 * FETCH_FACTOR + t["write_kib"] * 1024 * WRITE_FACTOR)
@@ -185,6 +193,8 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-backward", action="store_true")
     p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--no-peaks", action="store_true")
+    p.add_argument("--no-configs", action="store_true")
     return p.parse_args()
 
 
@@ -252,6 +262,7 @@ def bench_forward(args, torch, si, mdn):
         plan.forward()
     (fwd_ms,), step_ms = time_calls(torch, [plan.forward], args.steps)
     log(f"forward: {step_ms * 1e3:.1f} us/step (call {fwd_ms * 1e3:.1f} us)")
+    flush_ab = bench_flush_ab(args, torch, plan)
     kernels = {
         "chunk_fwd_fused_kernel": roofline_of("chunk_fwd_fused_kernel", fwd_ms * 1e3,
                                               FLOP_FWD * toh,
@@ -274,7 +285,7 @@ def bench_forward(args, torch, si, mdn):
     fwd = {"us_per_step": step_ms * 1e3, "tokens_per_s": tokens / (step_ms * 1e-3),
            "mfma_frac": FLOP_FWD * toh / (step_ms * 1e-3) / PEAK_BF16_FLOPS,
            "hbm_frac_algorithmic": (BYTES_FWD * toh + STATE_BYTES_HEAD * heads)
-           / (step_ms * 1e-3) / PEAK_HBM_BPS}
+           / (step_ms * 1e-3) / PEAK_HBM_BPS, "_flush_ab": flush_ab}
     # the same layer in the four-gate form: an explicit update-step gate beta
     # (one more fp32 gate per token and head to read)
     beta = si.make_forward(cfg, beta="logit")["beta"]
@@ -507,6 +518,114 @@ def bench_sweep(args, torch, si, mdn):
             "points": out}
 
 
+def bench_peaks(args, torch):
+    """Measured ceilings on this GPU: a dense bf16 MFMA loop (8 independent
+    16x16x32 chains per wavefront, 4 wavefronts per workgroup) and a 2 GiB
+    streaming copy (cached and non-temporal accesses)."""
+    from chunkwise_delta_rule_amd import peaks
+    out = torch.empty(4096 * 256, dtype=torch.float32, device="cuda")
+    wg, iters = 4096, 2048
+    fn = lambda: peaks.mfma_bf16(wg, iters, out)
+    flop = fn()
+    settle(torch, [fn], args.settle)
+    (ms,), _ = time_calls(torch, [fn], 10)
+    mfma = flop / (ms * 1e-3)
+    n = 1 << 31
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    copy = {}
+    for nt in (True, False):
+        cf = lambda: peaks.copy(src, dst, nontemporal=nt)
+        nbytes = cf()
+        settle(torch, [cf], args.settle)
+        (cms,), _ = time_calls(torch, [cf], 10)
+        copy["nontemporal" if nt else "cached"] = nbytes / (cms * 1e-3)
+    del src, dst
+    best = max(copy.values())
+    log(f"measured peaks: bf16 MFMA {mfma / 1e12:.0f} TFLOP/s ({mfma / PEAK_BF16_FLOPS:.1%} of "
+        f"the datasheet), copy {copy['nontemporal'] / 1e9:.0f} GB/s non-temporal, "
+        f"{copy['cached'] / 1e9:.0f} GB/s cached ({best / PEAK_HBM_BPS:.1%})")
+    return {"mfma_bf16_TFLOP_per_s": mfma / 1e12,
+            "mfma_bf16_frac_of_datasheet": mfma / PEAK_BF16_FLOPS,
+            "mfma_workload": f"{wg} workgroups x 4 wavefronts x {iters} rounds of 8 independent "
+                             "v_mfma_f32_16x16x32_bf16",
+            "copy_GB_per_s": {k: v / 1e9 for k, v in copy.items()},
+            "copy_frac_of_datasheet": best / PEAK_HBM_BPS,
+            "copy_workload": "2 GiB read + 2 GiB written, 16 B per lane, grid-stride",
+            "datasheet": {"mfma_bf16_TFLOP_per_s": PEAK_BF16_FLOPS / 1e12,
+                          "hbm_GB_per_s": PEAK_HBM_BPS / 1e9}}
+
+
+def time_calls_each(torch, fn, steps, flush=None):
+    """Median and mean time (ms) of single calls, each bracketed by its own
+    events; with `flush`, that callable runs between the calls (outside the
+    events)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        if flush is not None:
+            flush()
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    return t[len(t) // 2], sum(t) / len(t)
+
+
+def bench_flush_ab(args, torch, plan):
+    """The headline call timed one call at a time, back to back and with a
+    1 GiB write between calls (evicting the 256 MB last-level cache), median
+    of 20 each: whether data left in the cache by the previous call helps."""
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = lambda: buf.fill_(0)
+    settle(torch, [plan.forward], args.settle)
+    med, mean = time_calls_each(torch, plan.forward, 20)
+    settle(torch, [flush, plan.forward], args.settle)
+    fmed, fmean = time_calls_each(torch, plan.forward, 20, flush=flush)
+    del buf
+    log(f"one call at a time: median {med * 1e3:.1f} us back to back, {fmed * 1e3:.1f} us "
+        f"after a 1 GiB write")
+    return {"median_us_back_to_back": med * 1e3, "mean_us_back_to_back": mean * 1e3,
+            "median_us_after_1GiB_write": fmed * 1e3, "mean_us_after_1GiB_write": fmean * 1e3,
+            "calls": 20}
+
+
+def bench_configs(args, torch, si, mdn):
+    """The other forward configurations at their own sizes: the 400M-like
+    layer (B4 H8 T2048) and the 16K-context layer (B1 H16 T16384) as drawn
+    and with no mu (the gated delta rule on the same inputs)."""
+    bf, f32 = torch.bfloat16, torch.float32
+    out = {}
+    for key, cfg, mu_null in (("config1", si.CONFIGS[1], False),
+                              ("config3_runA", si.CONFIGS[3], False),
+                              ("config3_runB_no_mu", si.CONFIGS[3], True)):
+        inp = si.make_forward(cfg)
+        plan = mdn.ChunkPlan(up(inp["q"], bf), up(inp["k"], bf), up(inp["v"], bf),
+                             up(inp["alpha"], f32), None if mu_null else up(inp["mu"], f32),
+                             up(inp["eta"], f32))
+        del inp
+        settle(torch, [plan.forward], args.settle)
+        for _ in range(args.warmup):
+            plan.forward()
+        (call_ms,), step_ms = time_calls(torch, [plan.forward], args.steps)
+        toh = cfg.B * cfg.T * cfg.H
+        heads = cfg.B * cfg.H
+        r = roofline_of(None, call_ms * 1e3, FLOP_FWD * toh,
+                        BYTES_FWD * toh + STATE_BYTES_HEAD * heads)
+        r["kernel"] = "chunk_fwd_fused_kernel" + ("<no mu>" if mu_null else "")
+        r["timed_with"] = "chunk_coef_kernel (same call)"
+        out[key] = {"workload": f"{cfg.name}{' with mu = 0 (no mu given)' if mu_null else ''}",
+                    "B": cfg.B, "T": cfg.T, "H": cfg.H, "us_per_step": step_ms * 1e3,
+                    "tokens_per_s": cfg.B * cfg.T / (step_ms * 1e-3),
+                    "workgroups": heads * (cfg.Dv // 64), "roofline": r}
+        log(f"{key}: {step_ms * 1e3:.1f} us/step, {cfg.B * cfg.T / (step_ms * 1e-3):.3e} tokens/s")
+        del plan
+    return out
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -554,9 +673,12 @@ def main():
         libbuild.build()
     mdn.load_library()
     cfg, inp, step_ms, kernels, roofline, fwd, split = bench_forward(args, torch, si, mdn)
+    flush_ab = fwd.pop("_flush_ab")
     backward = None if args.no_backward else bench_backward(args, torch, si, mdn, cfg, inp)
     decode = None if args.no_decode else bench_decode(args, torch, si, mdn)
     sweep = None if args.no_sweep else bench_sweep(args, torch, si, mdn)
+    configs = None if args.no_configs else bench_configs(args, torch, si, mdn)
+    peaks = None if args.no_peaks else bench_peaks(args, torch)
     base = None if args.no_cpu_baseline else cpu_baseline(inp, cfg)
     tokens = cfg.B * cfg.T
     line = {
@@ -581,7 +703,10 @@ def main():
         "split_path": split,
         "backward": backward,
         "decode": decode,
+        "timing_ab": flush_ab,
+        "other_configs": configs,
         "sweep": sweep,
+        "measured_peaks": peaks,
         "cpu_baseline": base,
     }
     print(json.dumps(line), flush=True)

@@ -3,8 +3,9 @@
     python -m chunkwise_delta_rule_amd.build
 
 Each HIP source is compiled to an object (in parallel), then linked into
-``chunkwise_delta_rule_amd/libmdn.so``.  Packed-fp32 instructions are
-disabled for all device code.
+``chunkwise_delta_rule_amd/libmdn.so``; the benchmark's ceiling kernels
+(``csrc/peaks.hip``) go into ``libmdn_peaks.so`` beside it.  Packed-fp32
+instructions are disabled for all device code.
 """
 from __future__ import annotations
 
@@ -20,7 +21,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmdn.so")
-SOURCES = ["api.hip", "chunk_bwd.hip", "chunk_fwd.hip", "chunk_fused.hip", "decode.hip", "gates.hip", "layer_io.hip"]
+PEAKS_LIB = os.path.join(PKG, "libmdn_peaks.so")
+SOURCES = ["api.hip", "chunk_bwd.hip", "chunk_fwd.hip", "chunk_fused.hip", "decode.hip", "gates.hip",
+           "layer_io.hip"]
+PEAKS_SOURCES = ["peaks.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -77,19 +81,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libmdn.so.  Returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link libmdn.so and libmdn_peaks.so.
+    Returns the path of libmdn.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PEAKS_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PEAKS_SOURCES], PEAKS_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PEAKS_LIB}")
     return LIB
 
 

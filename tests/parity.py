@@ -7,7 +7,12 @@ Tolerances (written here once, used by every parity test):
             max|X - X*| / max|X*| <= 1e-4     (relative to the tensor's scale;
             elementwise relative error is ill-posed where X* crosses 0)
   bf16 I/O: max|X - X*| <= 2e-2 * max(1, rms(X*)) per tensor; the outputs are
-            unit scale, so this is an absolute 2e-2 bound.
+            unit scale, so this is an absolute 2e-2 bound.  Beside it, a
+            companion bound relative to the tensor's own scale:
+            max|X - X*| <= 2e-2 * max|X*|.  The final states (and the decode
+            state and early decode outputs) are far below unit scale (M_T has
+            an rms of a few 1e-2), where the absolute bound alone would let an
+            error of the size of the signal pass.
 """
 from __future__ import annotations
 
@@ -20,6 +25,7 @@ from chunkwise_delta_rule_amd import mdn
 TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 FP32_REL_TOL = 1e-4
 BF16_ABS_TOL = 2e-2
+BF16_REL_TOL = 2e-2
 
 
 def to_dev(x, dtype=torch.float32):
@@ -109,5 +115,8 @@ def assert_close(x, ref, io, name):
         assert rel <= FP32_REL_TOL, f"{name}: relative error {rel:.3e} > {FP32_REL_TOL}"
     else:
         bound = BF16_ABS_TOL * max(1.0, rms)
-        print(f"  {name}: max|err|={err:.3e} bound={bound:.3e} max|ref|={mx:.3e} rms={rms:.3e}")
+        rel = err / mx if mx > 0 else err
+        print(f"  {name}: max|err|={err:.3e} bound={bound:.3e} rel={rel:.3e} "
+              f"(tol {BF16_REL_TOL}) max|ref|={mx:.3e} rms={rms:.3e}")
         assert err <= bound, f"{name}: max abs error {err:.3e} > {bound:.3e}"
+        assert rel <= BF16_REL_TOL, f"{name}: error {rel:.3e} of max|ref| > {BF16_REL_TOL}"

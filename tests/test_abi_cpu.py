@@ -313,3 +313,26 @@ def test_epilogue_rejects(lib, over, status):
 def test_prologue_epilogue_no_rows(lib):
     assert call_pro(lib, rows=0, q=None) == 0
     assert call_epi(lib, H=0, o=None) == 0
+
+
+def test_peaks_library_exports_its_header():
+    """libmdn_peaks.so (the benchmark's ceiling kernels) exports every
+    function include/libmdn_peaks.h declares; its argument checks run on the
+    host before any launch."""
+    from chunkwise_delta_rule_amd import peaks
+
+    plib = peaks.load_library()
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "libmdn_peaks.h")).read(),
+                  flags=re.S)
+    names = sorted(set(re.findall(r"\b(mdn_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["mdn_peak_copy", "mdn_peak_mfma_bf16", "mdn_peak_mfma_bf16_flop"]
+    for name in names:
+        assert ctypes.cast(getattr(plib, name), ctypes.c_void_p).value
+    assert plib.mdn_peak_mfma_bf16_flop(3, 5) == 3 * 4 * 5 * 8 * 16 * 16 * 32 * 2
+    assert plib.mdn_peak_mfma_bf16_flop(0, 5) == 0
+    assert plib.mdn_peak_mfma_bf16(4, 1, None, None) == 1
+    assert plib.mdn_peak_mfma_bf16(0, 1, 16, None) == 2
+    assert plib.mdn_peak_copy(None, 16, 16, 1, None) == 1
+    assert plib.mdn_peak_copy(16, 32, 15, 1, None) == 2
+    assert plib.mdn_peak_copy(8, 32, 16, 1, None) == 4
+    assert plib.mdn_peak_copy(16, 32, 0, 1, None) == 0

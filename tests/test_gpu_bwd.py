@@ -7,12 +7,14 @@ Tolerance, per result tensor X with oracle X* (the whole tensor's scale:
 elementwise relative error is ill-posed where X* crosses 0):
   fp32 I/O:  max|X - X*| <= 2e-5 max|X*|
   bf16 I/O:  max|X - X*| <= 1e-2 max|X*|
-The backward computes in fp32 throughout (measured: under 1e-6 of the scale
-on the small cases).  The bf16 case also carries the bf16 rounding (2^-9
-relative) of the T = L^-1 and A that the split path's prepare phase stores and
-of the per-chunk state pairs the backward keeps, which moves every gradient by
-a few 1e-3 of its scale (measured up to 2.5e-3); the bound leaves a margin of
-about 4 for longer sequences.
+For fp32 I/O the backward computes in fp32 (measured: under 1e-6 of the
+scale on the small cases).  For bf16 I/O its products run on bf16 MFMA with
+fp32 sums: the inputs, T = L^-1 and A (stored in bf16 by the prepare phase)
+and the saved residuals are exact as operands; the per-chunk state pairs the
+backward keeps are stored in bf16, and its fp32 row operands are split into a
+bf16 head and remainder or rounded once.  That moves every gradient by a few
+1e-3 of its scale (measured up to about 9e-3 with saved residuals on a
+65-token case); the full-size cases print their worst ratio to the bound.
 """
 import numpy as np
 import pytest
@@ -68,6 +70,7 @@ def run_case(cfg, *, seed=5, terminal=True, mu_null=False, with_beta=False, labe
                 x = to_np(g[name])
                 g[name] = gather_heads(x, heads, state=name in ("dS0", "dM0"))
     tol = TOL[cfg.io_dtype]
+    worst = (0.0, "")
     for name in NAMES:
         x = g[name]
         r = ref[name]
@@ -84,7 +87,9 @@ def run_case(cfg, *, seed=5, terminal=True, mu_null=False, with_beta=False, labe
         mx = float(np.max(np.abs(r))) if r.size else 0.0
         rel = err / mx if mx > 0 else err
         print(f"  {name}: max|err|={err:.3e} max|ref|={mx:.3e} rel={rel:.3e} (tol {tol})")
+        worst = max(worst, (rel / tol, name))
         assert rel <= tol, f"{name}: relative error {rel:.3e} > {tol}"
+    print(f"  worst ratio to the bound: {worst[0]:.3f} ({worst[1]})")
 
 
 SMALL = si.CONFIGS[0]
@@ -112,7 +117,7 @@ def test_bwd_mu_null(T):
 
 
 @pytest.mark.parametrize("T", [65, 200])
-@pytest.mark.parametrize("dims", [(64, 64), (128, 128)])
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (64, 128), (128, 64)])
 def test_bwd_small_bf16(T, dims):
     cfg = si.replace(SMALL, B=1, T=T, H=2, Dk=dims[0], Dv=dims[1], io_dtype="bf16",
                      init_state_std=0.5, seed=si.SEED_BASE + 330 + T)
@@ -140,11 +145,10 @@ def test_bwd_config1_full():
     run_case(si.CONFIGS[1], seed=11, label="config 1")
 
 
-def test_bwd_config2_sampled_heads():
+def test_bwd_config2_full():
     """The 1.3B-like layer at full size (B8 H16 T4096 d128, bf16) in one
-    call, as the benchmark runs it; eight heads compared."""
-    heads = [(0, 0), (1, 5), (2, 15), (3, 7), (4, 2), (5, 11), (6, 9), (7, 14)]
-    run_case(si.CONFIGS[2], seed=12, label="config 2", heads=heads)
+    call, as the benchmark runs it; every head and element."""
+    run_case(si.CONFIGS[2], seed=12, label="config 2 all heads")
 
 
 def test_bwd_deterministic():
@@ -175,17 +179,22 @@ def test_bwd_saved_residuals_fp32(T, dims):
 
 
 @pytest.mark.parametrize("T", [65, 200])
-def test_bwd_saved_residuals_bf16(T):
-    """The fused bf16 forward saves Vt; beta and no mu as well."""
-    cfg = si.replace(SMALL, B=1, T=T, H=2, Dk=128, Dv=128, io_dtype="bf16",
-                     init_state_std=0.5, seed=si.SEED_BASE + 360 + T)
-    run_case(cfg, label="bf16", saved=True)
-    run_case(cfg, label="bf16 mu0 beta", saved=True, mu_null=True, with_beta=True)
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (64, 128), (128, 64)])
+@pytest.mark.parametrize("gates", ["mu", "mu0-beta"])
+def test_bwd_saved_residuals_bf16(T, dims, gates):
+    """The fused bf16 forward saves Vt; the backward rebuilds the states
+    from it; with mu, and with no mu and a beta gate."""
+    cfg = si.replace(SMALL, B=1, T=T, H=2, Dk=dims[0], Dv=dims[1], io_dtype="bf16",
+                     init_state_std=0.5, seed=si.SEED_BASE + 360 + T + dims[0] + 2 * dims[1])
+    if gates == "mu":
+        run_case(cfg, label="bf16", saved=True)
+    else:
+        run_case(cfg, label="bf16 mu0 beta", saved=True, mu_null=True, with_beta=True)
 
 
-def test_bwd_saved_residuals_config2_sampled_heads():
-    heads = [(0, 3), (3, 12), (7, 6)]
-    run_case(si.CONFIGS[2], seed=13, label="config 2", heads=heads, saved=True)
+def test_bwd_saved_residuals_config2_full():
+    """Config 2 at full size from the forward's saved residuals, every head."""
+    run_case(si.CONFIGS[2], seed=13, label="config 2 all heads", saved=True)
 
 
 @pytest.mark.parametrize("io,dims,T", [("f32", (64, 64), 200), ("f32", (128, 64), 65),
