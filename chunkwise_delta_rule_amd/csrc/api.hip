@@ -5,8 +5,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <cmath>
 #include <initializer_list>
+#include <mutex>
 
 #include "../../include/libmdn.h"
 
@@ -147,6 +149,10 @@ struct FwdArgs {
     mdn_dtype dt;
     const void* ws;
     size_t ws_bytes;
+    // the workspace is the library's own per-device scratch array, resolved
+    // after validation: ws_bytes is its capacity, and it overlaps no
+    // caller buffer
+    bool static_ws = false;
 };
 
 // Every host-side check of the forward entry points.  `phase` says which
@@ -189,7 +195,8 @@ mdn_status validate_fwd(const FwdArgs& a, int phase, bool* no_work)
     const size_t need = !tok ? 0
                         : fused ? mdn::chunk_fused_workspace_bytes(nchunks)
                                 : mdn::chunk_workspace_bytes(a.B, a.T, a.H, a.dt == MDN_BF16);
-    if (need > 0 && (!a.ws || a.ws_bytes < need)) return MDN_ERR_WORKSPACE;
+    if (need > 0 && (a.static_ws ? need > a.ws_bytes : (!a.ws || a.ws_bytes < need)))
+        return MDN_ERR_WORKSPACE;
 
     const size_t nt = tok ? 1 : 0;   // token arrays are empty when T == 0
     const bool prep = phase & PREPARE, scan = phase & SCAN;
@@ -204,7 +211,8 @@ mdn_status validate_fwd(const FwdArgs& a, int phase, bool* no_work)
                sO = span(scan ? a.O : nullptr, nt * nv * esz),
                sVt = span(scan ? a.Vt : nullptr, nt * nv * esz),
                sST = span(scan ? a.S_T : nullptr, nstate * 4),
-               sMT = span(scan ? a.M_T : nullptr, nstate * 4), sW = span(a.ws, need);
+               sMT = span(scan ? a.M_T : nullptr, nstate * 4),
+               sW = span(a.static_ws ? nullptr : a.ws, need);
     const Span inputs[] = {sq, sk, sv, sa, sm, se, sb, sS0, sM0};
     // O and the workspace overlap nothing
     for (const Span& x : inputs)
@@ -223,11 +231,9 @@ mdn_status validate_fwd(const FwdArgs& a, int phase, bool* no_work)
     return MDN_OK;
 }
 
-mdn_status run_fwd(const FwdArgs& a, int phase, hipStream_t stream)
+// Launches the forward's kernels for arguments validate_fwd accepted.
+mdn_status launch_fwd(const FwdArgs& a, int phase, hipStream_t stream)
 {
-    bool no_work = false;
-    const mdn_status st = validate_fwd(a, phase, &no_work);
-    if (st != MDN_OK || no_work) return st;
     const bool bf16 = a.dt == MDN_BF16;
     if (phase == BOTH && bf16 && a.T > 0) {
         const hipError_t err =
@@ -251,6 +257,51 @@ mdn_status run_fwd(const FwdArgs& a, int phase, hipStream_t stream)
     return MDN_OK;
 }
 
+mdn_status run_fwd(const FwdArgs& a, int phase, hipStream_t stream)
+{
+    bool no_work = false;
+    const mdn_status st = validate_fwd(a, phase, &no_work);
+    if (st != MDN_OK || no_work) return st;
+    return launch_fwd(a, phase, stream);
+}
+
+// The forward's workspace for callers that cannot allocate: one array per
+// device in the library's code object, loaded with it and held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not
+// device memory; its device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address is ever
+// passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[MDN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<void*> scratch_ptr[MAX_DEVICES];
+std::mutex scratch_mutex;
+
+// The device address of `scratch` on the device `stream` belongs to (the
+// current device for the null stream).
+mdn_status scratch_for_stream(hipStream_t stream, void** out)
+{
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return MDN_ERR_HIP;
+    int dev = cur;
+    if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) return MDN_ERR_HIP;
+    if (dev < 0 || dev >= MAX_DEVICES) return MDN_ERR_UNSUPPORTED;
+    void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(scratch_mutex);
+        p = scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            if (dev != cur && hipSetDevice(dev) != hipSuccess) return MDN_ERR_HIP;
+            const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (dev != cur && hipSetDevice(cur) != hipSuccess) return MDN_ERR_HIP;
+            if (err != hipSuccess || p == nullptr) return MDN_ERR_HIP;
+            scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return MDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -264,6 +315,27 @@ mdn_status mdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
     const FwdArgs a{q, k, v, alpha, mu, eta, beta, S0, M0, O, Vt, S_T, M_T, B, T, H, Dk, Dv,
                     chunk, dt, workspace, workspace_bytes};
     return run_fwd(a, BOTH, stream);
+}
+
+mdn_status mdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                 const float* alpha, const float* mu, const float* eta,
+                                 const float* beta, const float* S0, const float* M0, void* O,
+                                 void* Vt, float* S_T, float* M_T, int B, int T, int H, int Dk,
+                                 int Dv, int chunk, mdn_dtype dt, hipStream_t stream)
+{
+    FwdArgs a{q, k, v, alpha, mu, eta, beta, S0, M0, O, Vt, S_T, M_T, B, T, H, Dk, Dv,
+              chunk, dt, nullptr, MDN_NOALLOC_SCRATCH_BYTES};
+    a.static_ws = true;
+    bool no_work = false;
+    mdn_status st = validate_fwd(a, BOTH, &no_work);
+    if (st != MDN_OK || no_work) return st;
+    if (mdn_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, dt) > 0) {
+        void* p = nullptr;
+        st = scratch_for_stream(stream, &p);
+        if (st != MDN_OK) return st;
+        a.ws = p;
+    }
+    return launch_fwd(a, BOTH, stream);
 }
 
 mdn_status mdn_chunk_fwd_prepare(const void* q, const void* k, const float* alpha,

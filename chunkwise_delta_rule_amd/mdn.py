@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libmdn.so")
 MDN_F32 = 0
 MDN_BF16 = 1
 CHUNK = 64
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MDN_NOALLOC_SCRATCH_BYTES
 HEAD_DIMS = (64, 128)
 
 STATUS_NAMES = {
@@ -36,7 +37,7 @@ STATUS_NAMES = {
 
 # every symbol include/libmdn.h declares
 EXPORTED = ("mdn_chunk_fwd_workspace_bytes", "mdn_chunk_fwd_split_workspace_bytes",
-            "mdn_chunk_fwd", "mdn_chunk_fwd_prepare",
+            "mdn_chunk_fwd", "mdn_chunk_fwd_noalloc", "mdn_chunk_fwd_prepare",
             "mdn_chunk_fwd_scan", "mdn_decode_step", "mdn_gates_from_logits",
             "mdn_chunk_bwd_workspace_bytes", "mdn_chunk_bwd", "mdn_qk_prologue",
             "mdn_output_epilogue", "mdn_status_string")
@@ -73,6 +74,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mdn_chunk_fwd_split_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.mdn_chunk_fwd.restype = I
     lib.mdn_chunk_fwd.argtypes = [P] * 13 + [I] * 7 + [P, S, P]
+    lib.mdn_chunk_fwd_noalloc.restype = I
+    lib.mdn_chunk_fwd_noalloc.argtypes = [P] * 13 + [I] * 7 + [P]
     lib.mdn_chunk_fwd_prepare.restype = I
     lib.mdn_chunk_fwd_prepare.argtypes = [P] * 6 + [I] * 6 + [P, S, P]
     lib.mdn_chunk_fwd_scan.restype = I
@@ -143,7 +146,7 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
               chunk: int = CHUNK, O: Optional[torch.Tensor] = None,
               S_T: Optional[torch.Tensor] = None, M_T: Optional[torch.Tensor] = None,
               workspace: Optional[torch.Tensor] = None, final_state: bool = True,
-              Vt: Optional[torch.Tensor] = None
+              Vt: Optional[torch.Tensor] = None, noalloc: bool = False
               ) -> Tuple[torch.Tensor, Optional[torch.Tensor], Optional[torch.Tensor]]:
     """Chunkwise MDN forward.  q, k [B, T, H, Dk], v [B, T, H, Dv] (bf16 or
     fp32), gates [B, T, H] fp32 (beta optional: None means beta = 1; mu may
@@ -152,7 +155,9 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
     token's residual (the activations mdn_chunk_bwd can take instead of
     recomputing them).
     Returns (O, S_T, M_T); S_T/M_T are None when ``final_state`` is False and
-    none were passed in."""
+    none were passed in.  ``noalloc`` calls mdn_chunk_fwd_noalloc, which runs
+    on the library's own per-device scratch array instead of a workspace (the
+    outputs are still allocated here unless passed in)."""
     lib = load_library()
     dev = q.device
     B, T, H, Dk = q.shape
@@ -180,6 +185,16 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
     for name, s in (("S_T", S_T), ("M_T", M_T)):
         if s is not None:
             _check(s, name, (B, H, Dk, Dv), torch.float32, dev)
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc runs on the library's own scratch array; pass no workspace")
+        st = lib.mdn_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(mu),
+                                       _ptr(eta), _ptr(beta), _ptr(S0), _ptr(M0), _ptr(O),
+                                       _ptr(Vt), _ptr(S_T), _ptr(M_T), B, T, H, Dk, Dv, chunk,
+                                       code, _stream(dev))
+        if st != 0:
+            raise MdnError(st, "mdn_chunk_fwd_noalloc")
+        return O, S_T, M_T
     need = int(lib.mdn_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, code))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

@@ -127,6 +127,36 @@ mdn_status mdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * mdn_chunk_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, rules and results as
+ * mdn_chunk_fwd (the same kernels run, so the outputs are bitwise those of
+ * mdn_chunk_fwd); the workspace is instead a file-scope device array of
+ * MDN_NOALLOC_SCRATCH_BYTES (64 MiB) in the library, one per GPU, loaded with
+ * the library's code on that GPU and held until the process ends.  Its
+ * address is looked up once per GPU on the first call there.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ * Limits and errors:
+ *   - a problem whose mdn_chunk_fwd_workspace_bytes(...) exceeds
+ *     MDN_NOALLOC_SCRATCH_BYTES returns MDN_ERR_WORKSPACE before anything is
+ *     enqueued (bf16: 6,656 bytes per chunk of 64 tokens and head, so up to
+ *     10,082 chunks, e.g. B8 H16 T4096; fp32: the two-phase workspace);
+ *   - MDN_ERR_HIP if the array's address cannot be looked up.
+ * Every call on one GPU shares that GPU's array, and a call leaves its
+ * contents behind: calls that overlap in time on one GPU (on different
+ * streams, or from different threads without ordering) race and give wrong
+ * results.  Calls ordered on one stream are safe.  No kernel relies on the
+ * array's contents on entry.
+ */
+#define MDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+mdn_status mdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                 const float* alpha, const float* mu, const float* eta,
+                                 const float* beta, const float* S0, const float* M0, void* O,
+                                 void* Vt, float* S_T, float* M_T, int B, int T, int H, int Dk,
+                                 int Dv, int chunk, mdn_dtype dt, hipStream_t stream);
+
+/*
  * The forward as two separate phases, for callers that want to run the
  * chunk-local phase ahead of the scan (for instance on another stream) or
  * time them apart.  The reading notes on the MDN paper (Sec. 2.4) point out

@@ -336,3 +336,24 @@ def test_peaks_library_exports_its_header():
     assert plib.mdn_peak_copy(16, 32, 15, 1, None) == 2
     assert plib.mdn_peak_copy(8, 32, 16, 1, None) == 4
     assert plib.mdn_peak_copy(16, 32, 0, 1, None) == 0
+
+
+def test_noalloc_validates_before_touching_a_device(lib):
+    """mdn_chunk_fwd_noalloc checks its arguments like mdn_chunk_fwd, and a
+    problem whose workspace exceeds the library's scratch array is refused
+    with MDN_ERR_WORKSPACE, all before any HIP call (fake pointers here)."""
+    P = 1 << 20
+    ptrs = [P * (i + 1) for i in range(13)]
+    call = lambda ptrs, B, T, H, dt: lib.mdn_chunk_fwd_noalloc(*ptrs, B, T, H, 128, 128, 64, dt,
+                                                                None)
+    B, T, H = 8, 8192, 16
+    assert lib.mdn_chunk_fwd_workspace_bytes(B, T, H, 128, 128, 64, mdn.MDN_BF16) > \
+        mdn.NOALLOC_SCRATCH_BYTES
+    big = [(1 << 40) * (i + 1) for i in range(13)]
+    assert call(big, B, T, H, mdn.MDN_BF16) == 6
+    assert call(big, B, T, H, mdn.MDN_F32) == 6
+    assert call([None] + big[1:], B, T, H, mdn.MDN_BF16) == 1
+    assert call(ptrs, -1, T, H, mdn.MDN_BF16) == 2
+    assert call(ptrs, 0, T, H, mdn.MDN_BF16) == 0          # nothing to do
+    assert lib.mdn_chunk_fwd_noalloc(*ptrs, 1, 64, 1, 96, 128, 64, mdn.MDN_BF16, None) == 3
+    assert call([p + 8 for p in ptrs], 1, 64, 1, mdn.MDN_BF16) == 4
