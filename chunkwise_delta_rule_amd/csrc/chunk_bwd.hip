@@ -1418,6 +1418,626 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Per-chunk gradients for bf16 I/O: the quantities of bwd_grad_kernel (same
+// formulas, same order of the coefficient recursions), laid out for eight
+// wavefronts and bf16 matrix cores.
+//
+// Every C x DK result is computed transposed, as [d][i]: lane (l16, lg) of
+// the wavefront owning d-tile dt holds d = 16 dt + 4 lg + r (r < 4) of chunk
+// row i = 16 it + l16.  Then
+//   * the six state products X St^T take the state rows as A operands straight
+//     from registers: each wavefront loads its 16 rows of S0, M0, dS', dM'
+//     once, at the start, and they also give the three inner products;
+//   * the masked products take K and Q as A operands by transposing LDS
+//     reads (columns of the row-major tiles), and the masked C x C matrices
+//     as B operands from bf16 planes holding each value as a head and a
+//     remainder (x = hi + lo to about 2^-16), formed once where the masks
+//     are applied: two products per operand, fp32 sums.
+// Row operands of the state products are rounded to bf16 as in
+// bwd_grad_kernel (exact for dO and saved Vt); dR enters dR Vt^T as a head
+// and remainder; a recomputed Vt is rounded to bf16 for its chunk products.
+// C x C results: wavefront w owns row tile w % 4 and column tiles
+// 2 (w / 4), 2 (w / 4) + 1.
+// ---------------------------------------------------------------------------
+
+// last-row weights of the bf16 kernel (the rows bwd_grad_kernel uses as
+// scratch for them)
+constexpr int G_WS = G_RED, G_WM = G_RED + 1;
+
+// x rounded to bf16 (nearest even), two per 32-bit word
+__device__ __forceinline__ unsigned bwd_pack_bf16(float a, float b)
+{
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    return __builtin_bit_cast(unsigned, bf16x2{static_cast<__bf16>(a), static_cast<__bf16>(b)});
+}
+__device__ __forceinline__ bf16x8 bwd_cat8(const bf16x4& a, const bf16x4& b)
+{
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+constexpr int NT8 = 512;
+
+template <int DK, int DV>
+struct GradBfSmem {
+    static constexpr int LQ = DK + 8;   // bf16 row stride of Q, K (16-byte pad)
+    static constexpr int LV = DV + 8;   // bf16 row stride of dO, Vt
+    static constexpr int LR = DV + 4;   // fp32 row stride of dR
+    static constexpr int LDC = CH + 4;  // fp32 row stride of C x C matrices
+    static constexpr int LP = CH + 8;   // bf16 row stride of a C x C plane
+    static constexpr int CM = CH * LDC * 4;       // bytes of one fp32 C x C matrix
+    static constexpr int PLANE = CH * LP * 2;     // bytes of one bf16 C x C plane
+    static constexpr int OFF_Q = 0;
+    static constexpr int OFF_K = OFF_Q + CH * LQ * 2;
+    static constexpr int OFF_DO = OFF_K + CH * LQ * 2;
+    static constexpr int OFF_VT = OFF_DO + CH * LV * 2;
+    static constexpr int OFF_DR = OFF_VT + CH * LV * 2;
+    static constexpr int END_TILES = OFF_DR + CH * LR * 4;
+    // the tiles' area also holds seven of the eight bf16 planes of the masked
+    // operands (from the dO tile on) once the chunk products are done
+    static constexpr int END_A = END_TILES > OFF_DO + 7 * PLANE ? END_TILES : OFF_DO + 7 * PLANE;
+    static constexpr int OFF_GM = END_A;          // Gamma
+    static constexpr int OFF_C1 = OFF_GM + CM;    // m, then planes
+    static constexpr int OFF_C2 = OFF_C1 + CM;    // row-dot partials, G_L, dGamma
+    static constexpr int OFF_VEC = OFF_C2 + CM;
+    static constexpr int NV = 24;
+    static constexpr int BYTES = OFF_VEC + (NV * CH + 32) * 4;
+    static constexpr int OFF_PL = OFF_DO;
+    static_assert(PLANE <= CM, "the eighth plane goes to C1");
+};
+
+// plane p of the masked operands: 0/1 dAG o eta (hi, lo), 2/3 dAG^T,
+// 4/5 (alpha dLG)^T, 6/7 dLG o eta
+template <int DK, int DV>
+__device__ __forceinline__ int plane_off(int p)
+{
+    using SM = GradBfSmem<DK, DV>;
+    // seven in the tiles' area after Q and K, the last in C1 (free once the
+    // m table has given the last-row weights)
+    return p < 7 ? SM::OFF_PL + p * SM::PLANE : SM::OFF_C1;
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ dO,
+    const float* __restrict__ dv, const float* __restrict__ Vts, const __bf16* __restrict__ Vsaved,
+    const __bf16* __restrict__ Hs, const __bf16* __restrict__ Hd, const float* __restrict__ alpha,
+    const float* __restrict__ mu, const float* __restrict__ eta, const float* __restrict__ beta,
+    float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dalpha,
+    float* __restrict__ dmu, float* __restrict__ deta, float* __restrict__ dbeta, int T, int H,
+    int NC)
+{
+    using SM = GradBfSmem<DK, DV>;
+    using BM = Mma<__bf16>;
+    constexpr int LQ = SM::LQ, LV = SM::LV, LR = SM::LR, LDC = SM::LDC, LP = SM::LP;
+    constexpr int NDT = DK / 16;             // d-tiles: 8 or 4
+    constexpr int NIT = 4 * NDT / 8;         // row tiles per wavefront: 4 or 2
+    constexpr int KSV = DV / 32;             // 32-column k-steps over DV
+    constexpr int KSK = DK / 32;             // ... over DK
+    static_assert(NDT == 8 || NDT == 4, "head size");
+    __shared__ __align__(16) char smem[SM::BYTES];
+    __bf16* Qs = reinterpret_cast<__bf16*>(smem + SM::OFF_Q);
+    __bf16* Ks = reinterpret_cast<__bf16*>(smem + SM::OFF_K);
+    __bf16* dOs = reinterpret_cast<__bf16*>(smem + SM::OFF_DO);
+    __bf16* Vs = reinterpret_cast<__bf16*>(smem + SM::OFF_VT);
+    float* dRs = reinterpret_cast<float*>(smem + SM::OFF_DR);
+    float* Gm = reinterpret_cast<float*>(smem + SM::OFF_GM);
+    float* Cm1 = reinterpret_cast<float*>(smem + SM::OFF_C1);
+    float* Cm2 = reinterpret_cast<float*>(smem + SM::OFF_C2);
+    float* vec = reinterpret_cast<float*>(smem + SM::OFF_VEC);
+    float* scal = vec + SM::NV * CH;     // 3 inner products, then 3 x 8 partials
+    auto V = [&](int row) { return vec + row * CH; };
+    auto plane = [&](int p) { return reinterpret_cast<__bf16*>(smem + plane_off<DK, DV>(p)); };
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l16 = lane & 15;
+    const int lg = lane >> 4;
+    const int c = (int)(blockIdx.x % NC);
+    const int bh = (int)(blockIdx.x / NC);
+    const int h = bh % H;
+    const int b = bh / H;
+    const int t0 = c * CH;
+    const int n = min(CH, T - t0);
+    const size_t tok0 = ((size_t)b * T + t0) * H + h;
+    const size_t chn = (size_t)bh * NC + c;
+    const int dt = wave % NDT;               // this wavefront's d-tile
+    const int it0 = (wave / NDT) * NIT;      // ... and first row tile
+    const bool owner = wave < NDT;           // counts the inner products once
+
+    // ---- loads: this wavefront's state rows, then the chunk's tiles --------
+    // state row d = 16 dt + l16, columns 32 s + 8 lg .. + 7: an A fragment
+    uint4 st[4][KSV];
+    {
+        const __bf16* S0 = Hs + chn * 2 * DK * DV;
+        const __bf16* Sd = Hd + chn * 2 * DK * DV;
+        const __bf16* base[4] = {S0, S0 + DK * DV, Sd, Sd + DK * DV};   // S0, M0, dS', dM'
+        const int d = 16 * dt + l16;
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int s = 0; s < KSV; ++s)
+                st[x][s] = *reinterpret_cast<const uint4*>(base[x] + (size_t)d * DV + 32 * s + 8 * lg);
+    }
+    // the chunk's rows into LDS: bf16 tiles as bf16 (a recomputed fp32 Vt is
+    // rounded), dR as fp32; rows >= n are zero
+    {
+        constexpr int PQ = CH * DK / 8 / NT8;    // 16-byte pieces per thread
+        constexpr int PV = CH * DV / 8 / NT8;
+        constexpr int PR = CH * DV / 4 / NT8;
+        static_assert(PQ >= 1 && PV >= 1 && PR >= 1, "tiles split over the workgroup");
+        uint4 bq[PQ], bk[PQ], bo[PV], bvt[PV], bvf[2 * PV];
+        float4 br[PR];
+        const bool saved = Vsaved != nullptr;
+#pragma unroll
+        for (int u = 0; u < PQ; ++u) {
+            const int idx = tid + u * NT8, row = idx / (DK / 8), c8 = idx % (DK / 8);
+            const bool in = row < n;
+            const size_t g = (tok0 + (size_t)row * H) * DK + 8 * c8;
+            bq[u] = in ? *reinterpret_cast<const uint4*>(q + g) : uint4{0u, 0u, 0u, 0u};
+            bk[u] = in ? *reinterpret_cast<const uint4*>(k + g) : uint4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < PV; ++u) {
+            const int idx = tid + u * NT8, row = idx / (DV / 8), c8 = idx % (DV / 8);
+            const bool in = row < n;
+            const size_t g = (tok0 + (size_t)row * H) * DV + 8 * c8;
+            bo[u] = in ? *reinterpret_cast<const uint4*>(dO + g) : uint4{0u, 0u, 0u, 0u};
+            if (saved) {
+                bvt[u] = in ? *reinterpret_cast<const uint4*>(Vsaved + g) : uint4{0u, 0u, 0u, 0u};
+            } else {
+                const float* src = Vts + (chn * CH + row) * DV + 8 * c8;
+                bvf[2 * u] = in ? *reinterpret_cast<const uint4*>(src) : uint4{0u, 0u, 0u, 0u};
+                bvf[2 * u + 1] = in ? *reinterpret_cast<const uint4*>(src + 4) : uint4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < PR; ++u) {
+            const int idx = tid + u * NT8, row = idx / (DV / 4), c4 = idx % (DV / 4);
+            br[u] = row < n ? *reinterpret_cast<const float4*>(dv + (tok0 + (size_t)row * H) * DV + 4 * c4)
+                            : float4{0.f, 0.f, 0.f, 0.f};
+        }
+        // gates (rows >= n: alpha 1, mu, eta, beta 0)
+        if (tid < CH) {
+            const int i = tid;
+            const bool in = i < n;
+            const size_t g = tok0 + (size_t)i * H;
+            V(G_A)[i] = in ? alpha[g] : 1.f;
+            V(G_M)[i] = in && mu ? mu[g] : 0.f;
+            V(G_E)[i] = in ? eta[g] : 0.f;
+            V(G_S)[i] = in ? (beta ? beta[g] : 1.f) : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < PQ; ++u) {
+            const int idx = tid + u * NT8, row = idx / (DK / 8), c8 = idx % (DK / 8);
+            *reinterpret_cast<uint4*>(Qs + row * LQ + 8 * c8) = bq[u];
+            *reinterpret_cast<uint4*>(Ks + row * LQ + 8 * c8) = bk[u];
+        }
+#pragma unroll
+        for (int u = 0; u < PV; ++u) {
+            const int idx = tid + u * NT8, row = idx / (DV / 8), c8 = idx % (DV / 8);
+            *reinterpret_cast<uint4*>(dOs + row * LV + 8 * c8) = bo[u];
+            if (saved) {
+                *reinterpret_cast<uint4*>(Vs + row * LV + 8 * c8) = bvt[u];
+            } else {
+                const uint4 a = bvf[2 * u], e = bvf[2 * u + 1];
+                *reinterpret_cast<uint4*>(Vs + row * LV + 8 * c8) =
+                    uint4{bwd_pack_bf16(__uint_as_float(a.x), __uint_as_float(a.y)),
+                          bwd_pack_bf16(__uint_as_float(a.z), __uint_as_float(a.w)),
+                          bwd_pack_bf16(__uint_as_float(e.x), __uint_as_float(e.y)),
+                          bwd_pack_bf16(__uint_as_float(e.z), __uint_as_float(e.w))};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < PR; ++u) {
+            const int idx = tid + u * NT8, row = idx / (DV / 4), c4 = idx % (DV / 4);
+            *reinterpret_cast<float4*>(dRs + row * LR + 4 * c4) = br[u];
+        }
+    }
+    for (int i = tid; i < (SM::NV - G_RX1) * CH; i += NT8) vec[G_RX1 * CH + i] = 0.f;
+    __syncthreads();
+
+    // ---- coefficients: abar, mubar, b; Gamma and m by columns ---------------
+    if (wave == 0) {
+        const float a = V(G_A)[lane], m = V(G_M)[lane];
+        float pa = a, pm = m;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const float ua = __shfl_up(pa, d), um = __shfl_up(pm, d);
+            if (lane >= d) {
+                pa *= ua;
+                pm *= um;
+            }
+        }
+        V(G_AB)[lane] = pa;
+        V(G_MB)[lane] = pm;
+        V(G_B)[lane] = prefix_affine(a, V(G_S)[lane] * pm, lane);
+    } else if (wave == 1) {
+        const int j = lane;
+        float g = 0.f, m = 1.f;
+        for (int i = 0; i < CH; ++i) {
+            if (i == j) {
+                g = V(G_S)[j];
+                m = 1.f;
+            } else if (i > j) {
+                m = V(G_M)[i] * m;
+                g = V(G_A)[i] * g + V(G_S)[i] * m;
+            }
+            Gm[i * LDC + j] = i >= j ? g : 0.f;
+            Cm1[i * LDC + j] = i >= j ? m : 0.f;
+        }
+    }
+    // the three inner products <dS', S0>, <dS', M0>, <dM', M0> from the
+    // registers (each state element counted by one wavefront)
+    {
+        float a0 = 0.f, a1 = 0.f, a2 = 0.f;
+        if (owner) {
+#pragma unroll
+            for (int s = 0; s < KSV; ++s) {
+                const unsigned w0[4] = {st[0][s].x, st[0][s].y, st[0][s].z, st[0][s].w};
+                const unsigned w1[4] = {st[1][s].x, st[1][s].y, st[1][s].z, st[1][s].w};
+                const unsigned w2[4] = {st[2][s].x, st[2][s].y, st[2][s].z, st[2][s].w};
+                const unsigned w3[4] = {st[3][s].x, st[3][s].y, st[3][s].z, st[3][s].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float s0a = __uint_as_float(w0[e] << 16), s0b = __uint_as_float(w0[e] & 0xffff0000u);
+                    const float m0a = __uint_as_float(w1[e] << 16), m0b = __uint_as_float(w1[e] & 0xffff0000u);
+                    const float dsa = __uint_as_float(w2[e] << 16), dsb = __uint_as_float(w2[e] & 0xffff0000u);
+                    const float dma = __uint_as_float(w3[e] << 16), dmb = __uint_as_float(w3[e] & 0xffff0000u);
+                    a0 += dsa * s0a + dsb * s0b;
+                    a1 += dsa * m0a + dsb * m0b;
+                    a2 += dma * m0a + dmb * m0b;
+                }
+            }
+        }
+        for (int o = 32; o >= 1; o >>= 1) {
+            a0 += __shfl_xor(a0, o);
+            a1 += __shfl_xor(a1, o);
+            a2 += __shfl_xor(a2, o);
+        }
+        if (lane == 0) {
+            scal[8 + wave] = a0;
+            scal[16 + wave] = a1;
+            scal[24 + wave] = a2;
+        }
+    }
+    __syncthreads();
+    // last-row weights ws_j = eta_j gamma_{n-1,j}, wm_j = eta_j m_{n-1,j}
+    if (tid < CH) {
+        const int j = tid;
+        V(G_WS)[j] = V(G_E)[j] * Gm[(n - 1) * LDC + j];
+        V(G_WM)[j] = V(G_E)[j] * Cm1[(n - 1) * LDC + j];
+    } else if (tid < CH + 3) {
+        const int x = tid - CH;
+        const float* p = scal + 8 * (x + 1);
+        scal[x] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    }
+    __syncthreads();
+
+    // ---- state products, transposed: P[x]^T = St X^T ----------------------
+    // (P1 dO S0^T, P2 dO M0^T, P3 dR S0^T, P4 dR M0^T, P5 Vt dS'^T, P6 Vt dM'^T)
+    f32x4 P[6][NIT];
+#pragma unroll
+    for (int x = 0; x < 6; ++x)
+#pragma unroll
+        for (int u = 0; u < NIT; ++u) P[x][u] = zero4();
+#pragma unroll
+    for (int s = 0; s < KSV; ++s) {
+        const bf16x8 aS0 = __builtin_bit_cast(bf16x8, st[0][s]);
+        const bf16x8 aM0 = __builtin_bit_cast(bf16x8, st[1][s]);
+        const bf16x8 adS = __builtin_bit_cast(bf16x8, st[2][s]);
+        const bf16x8 adM = __builtin_bit_cast(bf16x8, st[3][s]);
+#pragma unroll
+        for (int u = 0; u < NIT; ++u) {
+            const int i = 16 * (it0 + u) + l16;
+            const bf16x8 bO = *reinterpret_cast<const bf16x8*>(dOs + i * LV + 32 * s + 8 * lg);
+            const bf16x8 bV = *reinterpret_cast<const bf16x8*>(Vs + i * LV + 32 * s + 8 * lg);
+            const float4 r0 = *reinterpret_cast<const float4*>(dRs + i * LR + 32 * s + 8 * lg);
+            const float4 r1 = *reinterpret_cast<const float4*>(dRs + i * LR + 32 * s + 8 * lg + 4);
+            const bf16x8 bR = __builtin_bit_cast(
+                bf16x8, uint4{bwd_pack_bf16(r0.x, r0.y), bwd_pack_bf16(r0.z, r0.w), bwd_pack_bf16(r1.x, r1.y),
+                              bwd_pack_bf16(r1.z, r1.w)});
+            P[0][u] = BM::mma(aS0, bO, P[0][u]);
+            P[1][u] = BM::mma(aM0, bO, P[1][u]);
+            P[2][u] = BM::mma(aS0, bR, P[2][u]);
+            P[3][u] = BM::mma(aM0, bR, P[3][u]);
+            P[4][u] = BM::mma(adS, bV, P[4][u]);
+            P[5][u] = BM::mma(adM, bV, P[5][u]);
+        }
+    }
+    // dQ, dK state parts and the six row dots (q with P1, P2; k with P3..P6),
+    // partial over this d-tile: red[x][dt][i] in C2
+    float* red = Cm2;
+    f32x4 dQa[NIT], dKa[NIT];
+#pragma unroll
+    for (int u = 0; u < NIT; ++u) {
+        const int i = 16 * (it0 + u) + l16;
+        const float ab = V(G_AB)[i], bb = V(G_B)[i];
+        const float ab1 = i > 0 ? V(G_A)[i] * V(G_B)[i - 1] : 0.f;
+        const float wsv = V(G_WS)[i], wmv = V(G_WM)[i];
+        dQa[u] = ab * P[0][u] - bb * P[1][u];
+        dKa[u] = -ab * P[2][u] + ab1 * P[3][u] + wsv * P[4][u] - wmv * P[5][u];
+        const bf16x4 qd = *reinterpret_cast<const bf16x4*>(Qs + i * LQ + 16 * dt + 4 * lg);
+        const bf16x4 kd = *reinterpret_cast<const bf16x4*>(Ks + i * LQ + 16 * dt + 4 * lg);
+#pragma unroll
+        for (int x = 0; x < 6; ++x) {
+            const bf16x4 y = x < 2 ? qd : kd;
+            float p = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p += P[x][u][r] * static_cast<float>(y[r]);
+            p += __shfl_xor(p, 16);
+            p += __shfl_xor(p, 32);
+            if (lg == 0) red[(x * NDT + dt) * CH + i] = p;
+        }
+    }
+
+    // ---- chunk products (row tile rw, column tiles cw, cw + 1) -------------
+    const int rw = wave & 3, cw = 2 * (wave >> 2);
+    f32x4 cA[2], cL[2], cK[2], cQ[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) cA[e] = cL[e] = cK[e] = cQ[e] = zero4();
+    {
+        const int ia = 16 * rw + l16;
+#pragma unroll
+        for (int s = 0; s < KSV; ++s) {
+            const bf16x8 aO = *reinterpret_cast<const bf16x8*>(dOs + ia * LV + 32 * s + 8 * lg);
+            const float4 r0 = *reinterpret_cast<const float4*>(dRs + ia * LR + 32 * s + 8 * lg);
+            const float4 r1 = *reinterpret_cast<const float4*>(dRs + ia * LR + 32 * s + 8 * lg + 4);
+            // -dR as a bf16 head and remainder
+            const float rr[8] = {-r0.x, -r0.y, -r0.z, -r0.w, -r1.x, -r1.y, -r1.z, -r1.w};
+            bf16x8 rh, rl;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                rh[j] = static_cast<__bf16>(rr[j]);
+                rl[j] = static_cast<__bf16>(rr[j] - static_cast<float>(rh[j]));
+            }
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int jb = 16 * (cw + e) + l16;
+                const bf16x8 bV = *reinterpret_cast<const bf16x8*>(Vs + jb * LV + 32 * s + 8 * lg);
+                cA[e] = BM::mma(aO, bV, cA[e]);
+                cL[e] = BM::mma(rh, bV, cL[e]);
+                cL[e] = BM::mma(rl, bV, cL[e]);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < KSK; ++s) {
+            const bf16x8 aK = *reinterpret_cast<const bf16x8*>(Ks + ia * LQ + 32 * s + 8 * lg);
+            const bf16x8 aQ = *reinterpret_cast<const bf16x8*>(Qs + ia * LQ + 32 * s + 8 * lg);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int jb = 16 * (cw + e) + l16;
+                const bf16x8 bK = *reinterpret_cast<const bf16x8*>(Ks + jb * LQ + 32 * s + 8 * lg);
+                cK[e] = BM::mma(aK, bK, cK[e]);
+                cQ[e] = BM::mma(aQ, bK, cQ[e]);
+            }
+        }
+    }
+    __syncthreads();   // red complete; dO, Vt, dR read for the last time
+    for (int i = tid; i < 6 * CH; i += NT8) {
+        const int x = i / CH, r = i % CH;
+        float sum = 0.f;
+#pragma unroll
+        for (int u = 0; u < NDT; ++u) sum += red[(x * NDT + u) * CH + r];
+        V(G_RX1 + x)[r] = sum;   // RX1, RX2, RY1, RY2, RZ1, RZ2 are consecutive rows
+    }
+    __syncthreads();   // red consumed: C2 free for G_L
+
+    // ---- masks: dGamma, G_L, and the masked operands as bf16 planes --------
+    float* GL = Cm2;
+    f32x4 dG[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * rw + 4 * lg + r;
+            const int j = 16 * (cw + e) + l16;
+            const float ej = V(G_E)[j], ai = V(G_A)[i];
+            const float da = j <= i ? cA[e][r] : 0.f;
+            const float dl = j < i ? cL[e][r] : 0.f;
+            dG[e][r] = da * cQ[e][r] * ej;
+            GL[i * LDC + j] = dl * ai * cK[e][r] * ej;
+            const float dag = da * Gm[i * LDC + j];
+            const float dlg = j < i ? dl * Gm[(i - 1) * LDC + j] : 0.f;
+            // x = hi + lo for each of the four operands
+            const float xs[4] = {dag * ej, dag, ai * dlg, dlg * ej};
+            const int rowp[4] = {i, j, j, i};
+            const int colp[4] = {j, i, i, j};
+#pragma unroll
+            for (int o = 0; o < 4; ++o) {
+                const __bf16 hi = static_cast<__bf16>(xs[o]);
+                const __bf16 lo = static_cast<__bf16>(xs[o] - static_cast<float>(hi));
+                plane(2 * o)[rowp[o] * LP + colp[o]] = hi;
+                plane(2 * o + 1)[rowp[o] * LP + colp[o]] = lo;
+            }
+        }
+    __syncthreads();
+    // dGamma_{i,j} += G_L_{i+1,j}; the last row also gets eta_j k_j.(Vt dS'^T)_j
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * rw + 4 * lg + r;
+            const int j = 16 * (cw + e) + l16;
+            if (i + 1 < n) dG[e][r] += GL[(i + 1) * LDC + j];
+            if (i == n - 1 && j < n) dG[e][r] += V(G_E)[j] * V(G_RZ1)[j];
+            if (j > i || i >= n) dG[e][r] = 0.f;
+        }
+
+    // ---- masked products, transposed, k over the chunk rows ---------------
+    //   dQ^T   += K^T (dAG o eta)^T          dKh^T = Q^T dAG + K^T (alpha dLG)
+    //   dP^T    = K^T (dLG o eta)^T
+    // A: columns d of K, Q by transposing reads (k order 32 p + 4 lg + j and
+    // 32 p + 16 + 4 lg + j); B: row i of the planes in the same k order.
+    f32x4 dKh[NIT], dPa[NIT];
+#pragma unroll
+    for (int u = 0; u < NIT; ++u) dKh[u] = dPa[u] = zero4();
+    {
+        const int trow = 4 * lg + (l16 >> 2), tcol = 16 * dt + 4 * (l16 & 3);
+        const char* kt = reinterpret_cast<const char*>(Ks + trow * LQ + tcol);
+        const char* qt = reinterpret_cast<const char*>(Qs + trow * LQ + tcol);
+        constexpr int R16 = 16 * LQ * 2;   // 16 rows further, bytes
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const bf16x8 aK = bwd_cat8(lds_read_tr4(kt + 2 * p * R16), lds_read_tr4(kt + (2 * p + 1) * R16));
+            const bf16x8 aQ = bwd_cat8(lds_read_tr4(qt + 2 * p * R16), lds_read_tr4(qt + (2 * p + 1) * R16));
+#pragma unroll
+            for (int u = 0; u < NIT; ++u) {
+                const int i = 16 * (it0 + u) + l16;
+                auto bfr = [&](int pl) {
+                    const __bf16* row = plane(pl) + i * LP + 32 * p + 4 * lg;
+                    return bwd_cat8(*reinterpret_cast<const bf16x4*>(row),
+                                *reinterpret_cast<const bf16x4*>(row + 16));
+                };
+                dQa[u] = BM::mma(aK, bfr(0), dQa[u]);
+                dQa[u] = BM::mma(aK, bfr(1), dQa[u]);
+                dKh[u] = BM::mma(aQ, bfr(2), dKh[u]);
+                dKh[u] = BM::mma(aQ, bfr(3), dKh[u]);
+                dKh[u] = BM::mma(aK, bfr(4), dKh[u]);
+                dKh[u] = BM::mma(aK, bfr(5), dKh[u]);
+                dPa[u] = BM::mma(aK, bfr(6), dPa[u]);
+                dPa[u] = BM::mma(aK, bfr(7), dPa[u]);
+            }
+        }
+    }
+    __syncthreads();   // G_L read: C2 takes the last row-dot partials
+    // dK += Diag(eta) dKhat + Diag(alpha) dP; row dots k.dKhat, k.dP
+#pragma unroll
+    for (int u = 0; u < NIT; ++u) {
+        const int i = 16 * (it0 + u) + l16;
+        dKa[u] += V(G_E)[i] * dKh[u] + V(G_A)[i] * dPa[u];
+        const bf16x4 kd = *reinterpret_cast<const bf16x4*>(Ks + i * LQ + 16 * dt + 4 * lg);
+        float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            p0 += dKh[u][r] * static_cast<float>(kd[r]);
+            p1 += dPa[u][r] * static_cast<float>(kd[r]);
+        }
+        p0 += __shfl_xor(p0, 16);
+        p0 += __shfl_xor(p0, 32);
+        p1 += __shfl_xor(p1, 16);
+        p1 += __shfl_xor(p1, 32);
+        if (lg == 0) {
+            red[(0 * NDT + dt) * CH + i] = p0;
+            red[(1 * NDT + dt) * CH + i] = p1;
+        }
+        // dq, dk rows < n: 4 consecutive d per lane
+        if (i < n) {
+            const size_t g = (tok0 + (size_t)i * H) * DK + 16 * dt + 4 * lg;
+            *reinterpret_cast<f32x4*>(dq + g) = dQa[u];
+            *reinterpret_cast<f32x4*>(dk + g) = dKa[u];
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < 2 * CH; i += NT8) {
+        const int x = i / CH, r = i % CH;
+        float sum = 0.f;
+#pragma unroll
+        for (int u = 0; u < NDT; ++u) sum += red[(x * NDT + u) * CH + r];
+        V(x == 0 ? G_RKH : G_RP)[r] = sum;
+    }
+    __syncthreads();
+
+    // ---- coefficient gradients back to the gates (as in bwd_grad_kernel) ---
+    float* dGm = Cm2;   // dGamma, row stride LDC
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            dGm[(16 * rw + 4 * lg + r) * LDC + 16 * (cw + e) + l16] = dG[e][r];
+    // scratch with row stride LDC in the tiles' area (all read by now)
+    float* Mt = reinterpret_cast<float*>(smem);
+    float* cA_ = Mt + CH * LDC;
+    float* cS_ = cA_ + CH * LDC;
+    float* cM_ = cS_ + CH * LDC;
+    static_assert(4 * SM::CM <= SM::END_A, "tail scratch");
+    for (int i = tid; i < CH; i += NT8) {
+        const float bp = i > 0 ? V(G_B)[i - 1] : 0.f;
+        V(G_DAB)[i] = V(G_RX1)[i] - V(G_RY1)[i];
+        V(G_DB)[i] = -V(G_RX2)[i];
+        V(G_DMB)[i] = 0.f;
+        V(G_DA)[i] = V(G_RP)[i] + V(G_RY2)[i] * bp;
+        V(G_DE)[i] = V(G_RKH)[i] + (i < n ? Gm[(n - 1) * LDC + i] * V(G_RZ1)[i] : 0.f);
+        V(G_DS)[i] = 0.f;
+        V(G_DM)[i] = 0.f;
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += NT8) {
+        if (i + 1 < n) V(G_DB)[i] += V(G_RY2)[i + 1] * V(G_A)[i + 1];
+        if (i == n - 1) {
+            V(G_DAB)[i] += scal[0];
+            V(G_DB)[i] -= scal[1];
+            V(G_DMB)[i] += scal[2];
+        }
+    }
+    if (tid < CH) {
+        const int j = tid;
+        float m = 1.f;
+        for (int i = 0; i < CH; ++i) {
+            if (i > j) m = V(G_M)[i] * m;
+            Mt[i * LDC + j] = i >= j ? m : 0.f;
+            cA_[i * LDC + j] = 0.f;
+            cS_[i * LDC + j] = 0.f;
+            cM_[i * LDC + j] = 0.f;
+        }
+        if (j < n) {
+            const float dml = -V(G_E)[j] * V(G_RZ2)[j];
+            float gcar = 0.f, mcar = 0.f;
+            for (int i = n - 1; i > j; --i) {
+                const float g = dGm[i * LDC + j] + gcar;
+                const float dm = (i == n - 1 ? dml : 0.f) + mcar;
+                const float ai = V(G_A)[i], si = V(G_S)[i], mi = V(G_M)[i];
+                const float mij = Mt[i * LDC + j];
+                cA_[i * LDC + j] = g * Gm[(i - 1) * LDC + j];
+                cS_[i * LDC + j] = g * mij;
+                const float dmt = dm + g * si;
+                cM_[i * LDC + j] = dmt * Mt[(i - 1) * LDC + j];
+                gcar = g * ai;
+                mcar = dmt * mi;
+            }
+            cS_[j * LDC + j] = dGm[j * LDC + j] + gcar;
+            V(G_DE)[j] += -Mt[(n - 1) * LDC + j] * V(G_RZ2)[j];
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < CH; i += NT8) {
+        float sa = 0.f, ss = 0.f, sm = 0.f;
+        for (int j = 0; j < CH; ++j) {
+            sa += cA_[i * LDC + j];
+            ss += cS_[i * LDC + j];
+            sm += cM_[i * LDC + j];
+        }
+        V(G_DA)[i] += sa;
+        V(G_DS)[i] += ss;
+        V(G_DM)[i] += sm;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const int i = lane;
+        const bool in = i < n;
+        const float anext = i + 1 < n ? V(G_A)[i + 1] : 0.f;
+        const float mnext = i + 1 < n ? V(G_M)[i + 1] : 0.f;
+        const float gb = suffix_affine(anext, in ? V(G_DB)[i] : 0.f, lane);
+        const float bp = i > 0 ? V(G_B)[i - 1] : 0.f;
+        float da = V(G_DA)[i] + gb * bp;
+        const float ds = V(G_DS)[i] + gb * V(G_MB)[i];
+        const float gmb0 = (in ? V(G_DMB)[i] : 0.f) + gb * V(G_S)[i];
+        const float gab = suffix_affine(anext, in ? V(G_DAB)[i] : 0.f, lane);
+        const float gmb = suffix_affine(mnext, in ? gmb0 : 0.f, lane);
+        da += gab * (i > 0 ? V(G_AB)[i - 1] : 1.f);
+        const float dm = V(G_DM)[i] + gmb * (i > 0 ? V(G_MB)[i - 1] : 1.f);
+        if (in) {
+            const size_t g = tok0 + (size_t)i * H;
+            dalpha[g] = da;
+            deta[g] = V(G_DE)[i];
+            if (dmu) dmu[g] = dm;
+            if (dbeta) dbeta[g] = ds;
+        }
+    }
+}
+
 }  // namespace
 }  // namespace mdn
 
@@ -1477,11 +2097,17 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
                            S0, M0, Hs, Vts, T, H, NC);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((bwd_grad_kernel<E, DK, DV>), dim3((unsigned)nchunks), dim3(NT), 0, stream,
-                       static_cast<const E*>(q), static_cast<const E*>(k),
-                       static_cast<const E*>(dO), dv, Vts, static_cast<const E*>(Vsaved), Hs, Hd,
-                       alpha, mu, eta, beta, dq, dk,
-                       dalpha, dmu, deta, dbeta, T, H, NC);
+    if constexpr (sizeof(E) == 2)
+        hipLaunchKernelGGL((bwd_grad_bf16_kernel<DK, DV>), dim3((unsigned)nchunks), dim3(NT8), 0,
+                           stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                           static_cast<const __bf16*>(dO), dv, Vts,
+                           static_cast<const __bf16*>(Vsaved), Hs, Hd, alpha, mu, eta, beta, dq,
+                           dk, dalpha, dmu, deta, dbeta, T, H, NC);
+    else
+        hipLaunchKernelGGL((bwd_grad_kernel<E, DK, DV>), dim3((unsigned)nchunks), dim3(NT), 0,
+                           stream, static_cast<const E*>(q), static_cast<const E*>(k),
+                           static_cast<const E*>(dO), dv, Vts, static_cast<const E*>(Vsaved), Hs,
+                           Hd, alpha, mu, eta, beta, dq, dk, dalpha, dmu, deta, dbeta, T, H, NC);
     return hipGetLastError();
 }
 
