@@ -1452,6 +1452,27 @@ __device__ __forceinline__ unsigned bwd_pack_bf16(float a, float b)
     typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
     return __builtin_bit_cast(unsigned, bf16x2{static_cast<__bf16>(a), static_cast<__bf16>(b)});
 }
+// Column of the masked-operand planes holding chunk row k: inside each 32
+// columns, the k order of a 16x16x32 step whose lane group g takes rows
+// 32 p + 4 g .. + 3 and 32 p + 16 + 4 g .. + 3, so that they are 8 adjacent
+// columns.
+__device__ __forceinline__ int kperm(int k)
+{
+    return (k & ~31) | ((k & 12) << 1) | ((k & 16) >> 2) | (k & 3);
+}
+
+// a if c else b, on values (a conditional between two named vectors would
+// select between their addresses and put both in memory)
+__device__ __forceinline__ uint4 sel4(bool c, uint4 a, uint4 b)
+{
+    return uint4{c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w};
+}
+
+// value of x in lane l (l uniform)
+__device__ __forceinline__ float readlane_f(float x, int l)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
 __device__ __forceinline__ bf16x8 bwd_cat8(const bf16x4& a, const bf16x4& b)
 {
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -1498,7 +1519,9 @@ __device__ __forceinline__ int plane_off(int p)
     return p < 7 ? SM::OFF_PL + p * SM::PLANE : SM::OFF_C1;
 }
 
-template <int DK, int DV>
+// SAVED: the forward saved the residuals (Vsaved, bf16 tokens); otherwise
+// the re-scan wrote them in fp32 to Vts.
+template <int DK, int DV, bool SAVED>
 __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ dO,
     const float* __restrict__ dv, const float* __restrict__ Vts, const __bf16* __restrict__ Vsaved,
@@ -1547,20 +1570,11 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
     const int it0 = (wave / NDT) * NIT;      // ... and first row tile
     const bool owner = wave < NDT;           // counts the inner products once
 
-    // ---- loads: this wavefront's state rows, then the chunk's tiles --------
+    // ---- loads: the chunk's tiles, then this wavefront's state rows --------
+    // (issued last, so that the tiles' waits leave them in flight: they are
+    // first used by the state products)
     // state row d = 16 dt + l16, columns 32 s + 8 lg .. + 7: an A fragment
     uint4 st[4][KSV];
-    {
-        const __bf16* S0 = Hs + chn * 2 * DK * DV;
-        const __bf16* Sd = Hd + chn * 2 * DK * DV;
-        const __bf16* base[4] = {S0, S0 + DK * DV, Sd, Sd + DK * DV};   // S0, M0, dS', dM'
-        const int d = 16 * dt + l16;
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-            for (int s = 0; s < KSV; ++s)
-                st[x][s] = *reinterpret_cast<const uint4*>(base[x] + (size_t)d * DV + 32 * s + 8 * lg);
-    }
     // the chunk's rows into LDS: bf16 tiles as bf16 (a recomputed fp32 Vt is
     // rounded), dR as fp32; rows >= n are zero
     {
@@ -1568,76 +1582,97 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
         constexpr int PV = CH * DV / 8 / NT8;
         constexpr int PR = CH * DV / 4 / NT8;
         static_assert(PQ >= 1 && PV >= 1 && PR >= 1, "tiles split over the workgroup");
-        uint4 bq[PQ], bk[PQ], bo[PV], bvt[PV], bvf[2 * PV];
+        uint4 bq[PQ], bk[PQ], bo[PV], bvt[SAVED ? PV : 1], bvf[SAVED ? 1 : 2 * PV];
         float4 br[PR];
-        const bool saved = Vsaved != nullptr;
+        // every load is unconditional (rows >= n read row n - 1 and are zeroed
+        // when stored): a load under a branch makes the compiler wait for all
+        // outstanding loads where the branches join
+        const int nl = n - 1;
 #pragma unroll
         for (int u = 0; u < PQ; ++u) {
-            const int idx = tid + u * NT8, row = idx / (DK / 8), c8 = idx % (DK / 8);
-            const bool in = row < n;
+            const int idx = tid + u * NT8, row = min(idx / (DK / 8), nl), c8 = idx % (DK / 8);
             const size_t g = (tok0 + (size_t)row * H) * DK + 8 * c8;
-            bq[u] = in ? *reinterpret_cast<const uint4*>(q + g) : uint4{0u, 0u, 0u, 0u};
-            bk[u] = in ? *reinterpret_cast<const uint4*>(k + g) : uint4{0u, 0u, 0u, 0u};
+            bq[u] = *reinterpret_cast<const uint4*>(q + g);
+            bk[u] = *reinterpret_cast<const uint4*>(k + g);
         }
 #pragma unroll
         for (int u = 0; u < PV; ++u) {
-            const int idx = tid + u * NT8, row = idx / (DV / 8), c8 = idx % (DV / 8);
-            const bool in = row < n;
+            const int idx = tid + u * NT8, row = min(idx / (DV / 8), nl), c8 = idx % (DV / 8);
             const size_t g = (tok0 + (size_t)row * H) * DV + 8 * c8;
-            bo[u] = in ? *reinterpret_cast<const uint4*>(dO + g) : uint4{0u, 0u, 0u, 0u};
-            if (saved) {
-                bvt[u] = in ? *reinterpret_cast<const uint4*>(Vsaved + g) : uint4{0u, 0u, 0u, 0u};
+            bo[u] = *reinterpret_cast<const uint4*>(dO + g);
+            if constexpr (SAVED) {
+                bvt[u] = *reinterpret_cast<const uint4*>(Vsaved + g);
             } else {
                 const float* src = Vts + (chn * CH + row) * DV + 8 * c8;
-                bvf[2 * u] = in ? *reinterpret_cast<const uint4*>(src) : uint4{0u, 0u, 0u, 0u};
-                bvf[2 * u + 1] = in ? *reinterpret_cast<const uint4*>(src + 4) : uint4{0u, 0u, 0u, 0u};
+                bvf[2 * u] = *reinterpret_cast<const uint4*>(src);
+                bvf[2 * u + 1] = *reinterpret_cast<const uint4*>(src + 4);
             }
         }
 #pragma unroll
         for (int u = 0; u < PR; ++u) {
-            const int idx = tid + u * NT8, row = idx / (DV / 4), c4 = idx % (DV / 4);
-            br[u] = row < n ? *reinterpret_cast<const float4*>(dv + (tok0 + (size_t)row * H) * DV + 4 * c4)
-                            : float4{0.f, 0.f, 0.f, 0.f};
+            const int idx = tid + u * NT8, row = min(idx / (DV / 4), nl), c4 = idx % (DV / 4);
+            br[u] = *reinterpret_cast<const float4*>(dv + (tok0 + (size_t)row * H) * DV + 4 * c4);
         }
-        // gates (rows >= n: alpha 1, mu, eta, beta 0)
+        // gates of row lane (rows >= n: alpha 1, mu, eta, beta 0)
+        float ga_, gm_ = 0.f, ge_, gs_ = 1.f;
+        {
+            const size_t g = tok0 + (size_t)min(lane, nl) * H;
+            ga_ = alpha[g];
+            ge_ = eta[g];
+            if (mu) gm_ = mu[g];
+            if (beta) gs_ = beta[g];
+        }
+        {
+            const __bf16* S0 = Hs + chn * 2 * DK * DV;
+            const __bf16* Sd = Hd + chn * 2 * DK * DV;
+            const __bf16* base[4] = {S0, S0 + DK * DV, Sd, Sd + DK * DV};   // S0, M0, dS', dM'
+            const int d = 16 * dt + l16;
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int s = 0; s < KSV; ++s)
+                    st[x][s] = *reinterpret_cast<const uint4*>(base[x] + (size_t)d * DV + 32 * s + 8 * lg);
+        }
         if (tid < CH) {
-            const int i = tid;
-            const bool in = i < n;
-            const size_t g = tok0 + (size_t)i * H;
-            V(G_A)[i] = in ? alpha[g] : 1.f;
-            V(G_M)[i] = in && mu ? mu[g] : 0.f;
-            V(G_E)[i] = in ? eta[g] : 0.f;
-            V(G_S)[i] = in ? (beta ? beta[g] : 1.f) : 0.f;
+            const bool in = lane < n;
+            V(G_A)[lane] = in ? ga_ : 1.f;
+            V(G_M)[lane] = in ? gm_ : 0.f;
+            V(G_E)[lane] = in ? ge_ : 0.f;
+            V(G_S)[lane] = in ? gs_ : 0.f;
         }
+        const uint4 z4 = uint4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int u = 0; u < PQ; ++u) {
             const int idx = tid + u * NT8, row = idx / (DK / 8), c8 = idx % (DK / 8);
-            *reinterpret_cast<uint4*>(Qs + row * LQ + 8 * c8) = bq[u];
-            *reinterpret_cast<uint4*>(Ks + row * LQ + 8 * c8) = bk[u];
+            const bool in = row < n;
+            *reinterpret_cast<uint4*>(Qs + row * LQ + 8 * c8) = sel4(in, bq[u], z4);
+            *reinterpret_cast<uint4*>(Ks + row * LQ + 8 * c8) = sel4(in, bk[u], z4);
         }
 #pragma unroll
         for (int u = 0; u < PV; ++u) {
             const int idx = tid + u * NT8, row = idx / (DV / 8), c8 = idx % (DV / 8);
-            *reinterpret_cast<uint4*>(dOs + row * LV + 8 * c8) = bo[u];
-            if (saved) {
-                *reinterpret_cast<uint4*>(Vs + row * LV + 8 * c8) = bvt[u];
+            const bool in = row < n;
+            *reinterpret_cast<uint4*>(dOs + row * LV + 8 * c8) = sel4(in, bo[u], z4);
+            if constexpr (SAVED) {
+                *reinterpret_cast<uint4*>(Vs + row * LV + 8 * c8) = sel4(in, bvt[u], z4);
             } else {
                 const uint4 a = bvf[2 * u], e = bvf[2 * u + 1];
-                *reinterpret_cast<uint4*>(Vs + row * LV + 8 * c8) =
-                    uint4{bwd_pack_bf16(__uint_as_float(a.x), __uint_as_float(a.y)),
-                          bwd_pack_bf16(__uint_as_float(a.z), __uint_as_float(a.w)),
-                          bwd_pack_bf16(__uint_as_float(e.x), __uint_as_float(e.y)),
-                          bwd_pack_bf16(__uint_as_float(e.z), __uint_as_float(e.w))};
+                const uint4 w = uint4{bwd_pack_bf16(__uint_as_float(a.x), __uint_as_float(a.y)),
+                                      bwd_pack_bf16(__uint_as_float(a.z), __uint_as_float(a.w)),
+                                      bwd_pack_bf16(__uint_as_float(e.x), __uint_as_float(e.y)),
+                                      bwd_pack_bf16(__uint_as_float(e.z), __uint_as_float(e.w))};
+                *reinterpret_cast<uint4*>(Vs + row * LV + 8 * c8) = sel4(in, w, z4);
             }
         }
 #pragma unroll
         for (int u = 0; u < PR; ++u) {
             const int idx = tid + u * NT8, row = idx / (DV / 4), c4 = idx % (DV / 4);
-            *reinterpret_cast<float4*>(dRs + row * LR + 4 * c4) = br[u];
+            *reinterpret_cast<float4*>(dRs + row * LR + 4 * c4) =
+                row < n ? br[u] : float4{0.f, 0.f, 0.f, 0.f};
         }
     }
     for (int i = tid; i < (SM::NV - G_RX1) * CH; i += NT8) vec[G_RX1 * CH + i] = 0.f;
-    __syncthreads();
+    lds_barrier();
 
     // ---- coefficients: abar, mubar, b; Gamma and m by columns ---------------
     if (wave == 0) {
@@ -1654,23 +1689,73 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
         V(G_AB)[lane] = pa;
         V(G_MB)[lane] = pm;
         V(G_B)[lane] = prefix_affine(a, V(G_S)[lane] * pm, lane);
-    } else if (wave == 1) {
-        const int j = lane;
-        float g = 0.f, m = 1.f;
-        for (int i = 0; i < CH; ++i) {
-            if (i == j) {
-                g = V(G_S)[j];
-                m = 1.f;
-            } else if (i > j) {
-                m = V(G_M)[i] * m;
-                g = V(G_A)[i] * g + V(G_S)[i] * m;
+    }
+    {
+        // Gamma and m by 8-row blocks: wavefront I runs rows 8 I ..
+        // 8 I + 7 of every column j = lane from zero at the block's start
+        // (m gets 1 added on the diagonal row, which starts column j there
+        // and leaves the rows above it zero), with the gates of row i from
+        // lane i's registers, and stores these block-local values; the
+        // response of row i to the values (m0, g0) entering its block,
+        // m0 rp and g0 ra + m0 rg, is the same for every column and goes to
+        // a row table, the block's exits to the exchange (both in C2).
+        const int I = wave, j = lane;
+        const float ga = V(G_A)[lane], gm = V(G_M)[lane], gs = V(G_S)[lane];
+        float* xch = Cm2;   // 0: m exits, 512: Gamma exits, 1024 + 4 i: row responses
+        float m = 0.f, g = 0.f, rp = 1.f, ra = 1.f, rg = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int i = 8 * I + t;
+            const float ai = readlane_f(ga, i), mi = readlane_f(gm, i), si = readlane_f(gs, i);
+            m = mi * m + (i == j ? 1.f : 0.f);
+            g = ai * g + si * m;
+            Gm[i * LDC + j] = g;
+            Cm1[i * LDC + j] = m;
+            rp = mi * rp;
+            rg = ai * rg + si * rp;
+            ra = ai * ra;
+            if (lane == 0) {
+                xch[1024 + 4 * i] = rp;
+                xch[1025 + 4 * i] = ra;
+                xch[1026 + 4 * i] = rg;
             }
-            Gm[i * LDC + j] = i >= j ? g : 0.f;
-            Cm1[i * LDC + j] = i >= j ? m : 0.f;
+        }
+        xch[64 * I + j] = m;
+        xch[512 + 64 * I + j] = g;
+    }
+    lds_barrier();
+    {
+        // the values entering block I, composed from the exits of the blocks
+        // above it; then their response on every row of the block
+        const int I = wave, j = lane;
+        const float* xch = Cm2;
+        float m0 = 0.f, g0 = 0.f;
+        for (int K = 0; K < I; ++K) {
+            const int e = 1024 + 4 * (8 * K + 7);
+            const float mn = xch[64 * K + j] + m0 * xch[e];
+            g0 = xch[512 + 64 * K + j] + g0 * xch[e + 1] + m0 * xch[e + 2];
+            m0 = mn;
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int i = 8 * I + t;
+            const float4 r = *reinterpret_cast<const float4*>(xch + 1024 + 4 * i);
+            Gm[i * LDC + j] += g0 * r.y + m0 * r.z;
+            Cm1[i * LDC + j] += m0 * r.x;
         }
     }
+    lds_barrier();
+    // last-row weights ws_j = eta_j gamma_{n-1,j}, wm_j = eta_j m_{n-1,j}
+    if (tid < CH) {
+        const int j = tid;
+        V(G_WS)[j] = V(G_E)[j] * Gm[(n - 1) * LDC + j];
+        V(G_WM)[j] = V(G_E)[j] * Cm1[(n - 1) * LDC + j];
+    }
+    lds_barrier();
+
     // the three inner products <dS', S0>, <dS', M0>, <dM', M0> from the
-    // registers (each state element counted by one wavefront)
+    // registers (each state element counted by one wavefront); summed with
+    // the row dots
     {
         float a0 = 0.f, a1 = 0.f, a2 = 0.f;
         if (owner) {
@@ -1703,19 +1788,6 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
             scal[24 + wave] = a2;
         }
     }
-    __syncthreads();
-    // last-row weights ws_j = eta_j gamma_{n-1,j}, wm_j = eta_j m_{n-1,j}
-    if (tid < CH) {
-        const int j = tid;
-        V(G_WS)[j] = V(G_E)[j] * Gm[(n - 1) * LDC + j];
-        V(G_WM)[j] = V(G_E)[j] * Cm1[(n - 1) * LDC + j];
-    } else if (tid < CH + 3) {
-        const int x = tid - CH;
-        const float* p = scal + 8 * (x + 1);
-        scal[x] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-    }
-    __syncthreads();
-
     // ---- state products, transposed: P[x]^T = St X^T ----------------------
     // (P1 dO S0^T, P2 dO M0^T, P3 dR S0^T, P4 dR M0^T, P5 Vt dS'^T, P6 Vt dM'^T)
     f32x4 P[6][NIT];
@@ -1815,7 +1887,7 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
             }
         }
     }
-    __syncthreads();   // red complete; dO, Vt, dR read for the last time
+    lds_barrier();   // red complete; dO, Vt, dR read for the last time
     for (int i = tid; i < 6 * CH; i += NT8) {
         const int x = i / CH, r = i % CH;
         float sum = 0.f;
@@ -1823,7 +1895,11 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
         for (int u = 0; u < NDT; ++u) sum += red[(x * NDT + u) * CH + r];
         V(G_RX1 + x)[r] = sum;   // RX1, RX2, RY1, RY2, RZ1, RZ2 are consecutive rows
     }
-    __syncthreads();   // red consumed: C2 free for G_L
+    if (tid < 3) {
+        const float* p = scal + 8 * (tid + 1);
+        scal[tid] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    }
+    lds_barrier();   // red consumed: C2 free for G_L
 
     // ---- masks: dGamma, G_L, and the masked operands as bf16 planes --------
     float* GL = Cm2;
@@ -1849,11 +1925,12 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
             for (int o = 0; o < 4; ++o) {
                 const __bf16 hi = static_cast<__bf16>(xs[o]);
                 const __bf16 lo = static_cast<__bf16>(xs[o] - static_cast<float>(hi));
-                plane(2 * o)[rowp[o] * LP + colp[o]] = hi;
-                plane(2 * o + 1)[rowp[o] * LP + colp[o]] = lo;
+                const int cp = kperm(colp[o]);
+                plane(2 * o)[rowp[o] * LP + cp] = hi;
+                plane(2 * o + 1)[rowp[o] * LP + cp] = lo;
             }
         }
-    __syncthreads();
+    lds_barrier();
     // dGamma_{i,j} += G_L_{i+1,j}; the last row also gets eta_j k_j.(Vt dS'^T)_j
 #pragma unroll
     for (int e = 0; e < 2; ++e)
@@ -1886,10 +1963,9 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
 #pragma unroll
             for (int u = 0; u < NIT; ++u) {
                 const int i = 16 * (it0 + u) + l16;
+                // columns stored in k order: one 16-byte read per fragment
                 auto bfr = [&](int pl) {
-                    const __bf16* row = plane(pl) + i * LP + 32 * p + 4 * lg;
-                    return bwd_cat8(*reinterpret_cast<const bf16x4*>(row),
-                                *reinterpret_cast<const bf16x4*>(row + 16));
+                    return *reinterpret_cast<const bf16x8*>(plane(pl) + i * LP + 32 * p + 8 * lg);
                 };
                 dQa[u] = BM::mma(aK, bfr(0), dQa[u]);
                 dQa[u] = BM::mma(aK, bfr(1), dQa[u]);
@@ -1902,7 +1978,7 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
             }
         }
     }
-    __syncthreads();   // G_L read: C2 takes the last row-dot partials
+    lds_barrier();   // G_L read: C2 takes the last row-dot partials
     // dK += Diag(eta) dKhat + Diag(alpha) dP; row dots k.dKhat, k.dP
 #pragma unroll
     for (int u = 0; u < NIT; ++u) {
@@ -1930,7 +2006,7 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
             *reinterpret_cast<f32x4*>(dk + g) = dKa[u];
         }
     }
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < 2 * CH; i += NT8) {
         const int x = i / CH, r = i % CH;
         float sum = 0.f;
@@ -1938,7 +2014,7 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
         for (int u = 0; u < NDT; ++u) sum += red[(x * NDT + u) * CH + r];
         V(x == 0 ? G_RKH : G_RP)[r] = sum;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- coefficient gradients back to the gates (as in bwd_grad_kernel) ---
     float* dGm = Cm2;   // dGamma, row stride LDC
@@ -1948,8 +2024,7 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
         for (int r = 0; r < 4; ++r)
             dGm[(16 * rw + 4 * lg + r) * LDC + 16 * (cw + e) + l16] = dG[e][r];
     // scratch with row stride LDC in the tiles' area (all read by now)
-    float* Mt = reinterpret_cast<float*>(smem);
-    float* cA_ = Mt + CH * LDC;
+    float* cA_ = reinterpret_cast<float*>(smem);
     float* cS_ = cA_ + CH * LDC;
     float* cM_ = cS_ + CH * LDC;
     static_assert(4 * SM::CM <= SM::END_A, "tail scratch");
@@ -1963,7 +2038,7 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
         V(G_DS)[i] = 0.f;
         V(G_DM)[i] = 0.f;
     }
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < n; i += NT8) {
         if (i + 1 < n) V(G_DB)[i] += V(G_RY2)[i + 1] * V(G_A)[i + 1];
         if (i == n - 1) {
@@ -1972,36 +2047,125 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
             V(G_DMB)[i] += scal[2];
         }
     }
-    if (tid < CH) {
-        const int j = tid;
-        float m = 1.f;
-        for (int i = 0; i < CH; ++i) {
-            if (i > j) m = V(G_M)[i] * m;
-            Mt[i * LDC + j] = i >= j ? m : 0.f;
-            cA_[i * LDC + j] = 0.f;
-            cS_[i * LDC + j] = 0.f;
-            cM_[i * LDC + j] = 0.f;
+    // Column j of the recursions back through Gamma and m, by 8-row blocks
+    // as the forward ones: wavefront I takes rows 8 I .. 8 I + 7 of every
+    // column.  Going up the rows, with the carries (gcar, mcar) coming
+    // from row i + 1:
+    //   g = dGamma_{i,j} + gcar,  dmt = [i = n - 1] dml + mcar + beta_i g,
+    //   gcar <- alpha_i g,  mcar <- mu_i dmt
+    // on the rows j < i < n, and the contributions g Gamma_{i-1,j} (to
+    // dalpha_i), g m_{i,j} (to dbeta_i), dmt m_{i-1,j} (to dmu_i).  Each
+    // block runs from zero carries; the carries entering it are composed
+    // from the exits of the blocks below it in row order (above it in the
+    // recursion), and their response on the block's rows is the same for
+    // every column.  m is rebuilt the same way, going down.
+    // Pass 1 keeps the block-local values of m, g and dmt in the scratch
+    // (cS_, cA_, cM_ at their own (i, j)) and the rows' responses in a row
+    // table; pass 2 adds the responses to the entering values and stores
+    // the contributions over them.
+    {
+        const int I = wave, j = lane;
+        const float ga = V(G_A)[j], gm = V(G_M)[j], gs = V(G_S)[j];
+        // 0: m exits, 512: gcar exits, 1024: mcar exits, 1536 + 4 i: row
+        // responses, 1792 + 4 I: block exit responses
+        float* xch = Cm1;
+        float m = 0.f, rp = 1.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int i = 8 * I + t;
+            const float mi = readlane_f(gm, i);
+            m = mi * m + (i == j ? 1.f : 0.f);
+            cS_[i * LDC + j] = m;
+            rp = mi * rp;
+            if (j == 0) xch[1536 + 4 * i] = rp;
         }
-        if (j < n) {
-            const float dml = -V(G_E)[j] * V(G_RZ2)[j];
-            float gcar = 0.f, mcar = 0.f;
-            for (int i = n - 1; i > j; --i) {
-                const float g = dGm[i * LDC + j] + gcar;
-                const float dm = (i == n - 1 ? dml : 0.f) + mcar;
-                const float ai = V(G_A)[i], si = V(G_S)[i], mi = V(G_M)[i];
-                const float mij = Mt[i * LDC + j];
-                cA_[i * LDC + j] = g * Gm[(i - 1) * LDC + j];
-                cS_[i * LDC + j] = g * mij;
-                const float dmt = dm + g * si;
-                cM_[i * LDC + j] = dmt * Mt[(i - 1) * LDC + j];
-                gcar = g * ai;
-                mcar = dmt * mi;
+        xch[64 * I + j] = m;
+        const bool col = j < n;
+        const float dml = -V(G_E)[j] * V(G_RZ2)[j];
+        float dgc[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) dgc[t] = dGm[(8 * I + t) * LDC + j];
+        float gc = 0.f, mc = 0.f;
+        float PG = 1.f, QG = 0.f, QM = 1.f;   // response to carries (G, M) entering the block
+#pragma unroll
+        for (int t = 7; t >= 0; --t) {
+            const int i = 8 * I + t;
+            const bool act = col && i > j && i < n;
+            const float ai = readlane_f(ga, i), si = readlane_f(gs, i), mi = readlane_f(gm, i);
+            const float g = dgc[t] + gc;
+            const float dmt = (i == n - 1 ? dml : 0.f) + mc + si * g;
+            cA_[i * LDC + j] = g;
+            cM_[i * LDC + j] = dmt;
+            gc = act ? ai * g : gc;
+            mc = act ? mi * dmt : mc;
+            // the carries' response on row i: g += G PG, dmt += G (QG + beta_i
+            // PG) + M QM (rows i < n carry it on; the same for every column
+            // whose range covers the row)
+            if (j == 0) {
+                xch[1537 + 4 * i] = PG;
+                xch[1538 + 4 * i] = QG;
+                xch[1539 + 4 * i] = QM;
             }
-            cS_[j * LDC + j] = dGm[j * LDC + j] + gcar;
-            V(G_DE)[j] += -Mt[(n - 1) * LDC + j] * V(G_RZ2)[j];
+            if (i < n) {
+                QG = mi * (QG + si * PG);
+                QM = mi * QM;
+                PG = ai * PG;
+            }
+        }
+        xch[512 + 64 * I + j] = gc;
+        xch[1024 + 64 * I + j] = mc;
+        if (j == 0) {
+            xch[1792 + 4 * I] = PG;
+            xch[1793 + 4 * I] = QG;
+            xch[1794 + 4 * I] = QM;
         }
     }
-    __syncthreads();
+    lds_barrier();
+    {
+        const int I = wave, j = lane;
+        const float* xch = Cm1;
+        // m entering the block (from the blocks above it in row order)
+        float m0 = 0.f;
+        for (int K = 0; K < I; ++K) m0 = xch[64 * K + j] + m0 * xch[1536 + 4 * (8 * K + 7)];
+        // carries entering the block from row 8 I + 8 (the blocks below it
+        // in row order, which the recursion runs first)
+        float G = 0.f, M = 0.f;
+        for (int K = 7; K > I; --K) {
+            const float PGx = xch[1792 + 4 * K], QGx = xch[1793 + 4 * K], QMx = xch[1794 + 4 * K];
+            const float Gn = xch[512 + 64 * K + j] + PGx * G;
+            M = xch[1024 + 64 * K + j] + QGx * G + QMx * M;
+            G = Gn;
+        }
+        const bool col = j < n;
+        float mprev = m0;          // m_{i-1,j}
+        float gnext = 0.f;         // g of row j + 1
+        float mlast = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int i = 8 * I + t;
+            const float4 r = *reinterpret_cast<const float4*>(xch + 1536 + 4 * i);
+            const float si = V(G_S)[i];
+            const float mcur = cS_[i * LDC + j] + m0 * r.x;
+            const bool act = col && i > j && i < n;
+            const float g = cA_[i * LDC + j] + G * r.y;
+            const float dmt = cM_[i * LDC + j] + G * (r.z + si * r.y) + M * r.w;
+            const float gprev = i > 0 ? Gm[(i - 1) * LDC + j] : 0.f;
+            cA_[i * LDC + j] = act ? g * gprev : 0.f;
+            cS_[i * LDC + j] = act ? g * mcur : 0.f;
+            cM_[i * LDC + j] = act ? dmt * mprev : 0.f;
+            gnext = i == j + 1 ? g : gnext;
+            mlast = i == n - 1 ? mcur : mlast;
+            mprev = mcur;
+        }
+        // gamma_{j,j} = beta_j: the carry entering row j is alpha_{j+1} g_{j+1}
+        // (row j + 1 in this block) or, at the block's last row, G
+        if (j >> 3 == I) {
+            const float gin = (j & 7) == 7 ? G : (j + 1 < n ? V(G_A)[j + 1] * gnext : 0.f);
+            cS_[j * LDC + j] = col ? dGm[j * LDC + j] + gin : 0.f;
+        }
+        if (col && (n - 1) >> 3 == I) V(G_DE)[j] += -mlast * V(G_RZ2)[j];
+    }
+    lds_barrier();
     for (int i = tid; i < CH; i += NT8) {
         float sa = 0.f, ss = 0.f, sm = 0.f;
         for (int j = 0; j < CH; ++j) {
@@ -2013,7 +2177,7 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
         V(G_DS)[i] += ss;
         V(G_DM)[i] += sm;
     }
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {
         const int i = lane;
         const bool in = i < n;
@@ -2098,7 +2262,9 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     if constexpr (sizeof(E) == 2)
-        hipLaunchKernelGGL((bwd_grad_bf16_kernel<DK, DV>), dim3((unsigned)nchunks), dim3(NT8), 0,
+        hipLaunchKernelGGL((Vsaved ? bwd_grad_bf16_kernel<DK, DV, true>
+                                   : bwd_grad_bf16_kernel<DK, DV, false>),
+                           dim3((unsigned)nchunks), dim3(NT8), 0,
                            stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                            static_cast<const __bf16*>(dO), dv, Vts,
                            static_cast<const __bf16*>(Vsaved), Hs, Hd, alpha, mu, eta, beta, dq,
