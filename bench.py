@@ -109,7 +109,7 @@ FETCH_FACTOR = 262144.0 / 131093.9
 WRITE_FACTOR = 131072.0 / 131072.0
 CSRC = os.path.join(ROOT, "chunkwise_delta_rule_amd", "csrc")
 _SPLIT_SHA = "8af5c737255c1507ac8eae24ed24c172deed445ad75cc8377ea217c8d71e70d4"
-_BWD_SHA = "f902fbd7770cba646f9196b3bd96960b5abf9f88195739e2a05ade050015a2a0"
+_BWD_SHA = "93f282aebf6fd02936360330f2d53bb5a333799e69af6c226b43b66162b69b80"
 _LIO_SHA = "627a8009335ec269a3313bb348dbbb8e2230dded01b1dfc19a85d20d78a2a663"
 TRAFFIC = {
     # chunk_coef_kernel (3,109.0 / 51,459.4) + chunk_fwd_fused_kernel (223,498.9 / 147,456.1):
@@ -126,16 +126,18 @@ TRAFFIC = {
                                write_kib=525524.5, sha256="8fa39113008b99235e1abe57028f0d81"
                                "9b837f475aa87000a6b4e46e3ea6c4e5"),
     # one mdn_chunk_bwd call with the forward's saved residuals: chunk_prep_kernel
-    # (134,555.6 / 144,240.5) + bwd_scan_kernel (471,250.7 / 786,432.2) + bwd_rescan_kernel
-    # with saved residuals (208,988.7 / 524,291.0) + bwd_grad_kernel (1,688,671.1 / 552,350.9)
+    # (134,587.5 / 144,287.0) + bwd_scan_kernel (471,244.1 / 786,432.1) + bwd_rescan_kernel
+    # with saved residuals (208,989.8 / 524,289.7) + bwd_grad_bf16_kernel<..., true>
+    # (929,812.4 / 543,235.1)
     "chunk_bwd": dict(sources=("chunk_bwd.hip", "chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
-                      fetch_kib=134555.6 + 471250.7 + 208988.7 + 1688671.1,
-                      write_kib=144240.5 + 786432.2 + 524291.0 + 552350.9, sha256=_BWD_SHA),
-    # the same recomputing the residuals: bwd_rescan_kernel (274,556.1 / 786,432.1)
+                      fetch_kib=134587.5 + 471244.1 + 208989.8 + 929812.4,
+                      write_kib=144287.0 + 786432.1 + 524289.7 + 543235.1, sha256=_BWD_SHA),
+    # the same recomputing the residuals: bwd_rescan_kernel (274,556.8 / 786,432.7),
+    # bwd_grad_bf16_kernel<..., false> (994,874.7 / 543,403.2)
     "chunk_bwd_recompute": dict(sources=("chunk_bwd.hip", "chunk_fwd.hip", "chunk_common.hpp",
                                          "mfma.hpp"),
-                                fetch_kib=134555.6 + 471250.7 + 274556.1 + 1688671.1,
-                                write_kib=144240.5 + 786432.2 + 786432.1 + 552350.9,
+                                fetch_kib=134587.5 + 471244.1 + 274556.8 + 994874.7,
+                                write_kib=144287.0 + 786432.1 + 786432.7 + 543403.2,
                                 sha256=_BWD_SHA),
     "qk_prologue_kernel": dict(sources=("layer_io.hip", "mfma.hpp"), fetch_kib=131099.8,
                                write_kib=262144.0, sha256=_LIO_SHA),
@@ -145,6 +147,28 @@ TRAFFIC = {
                          sha256="2bde382d2f924a1318325130cdb94dab"
                          "7d2b47dcae9f102ec3b939b9dde52ce6"),
 }
+
+
+# MFMA-pipe busy fraction from rocprofv3 counters (SQ_VALU_MFMA_BUSY_CYCLES summed over the
+# 1,024 SIMDs / (GRBM_GUI_ACTIVE per XCD x 1,024), per dispatch, averaged), with the sources
+# they were taken at (profiles/mfma_counters_B8H16T4096d128.md); null once the sources differ.
+# It is the fraction of the kernel's duration the matrix pipes were busy, at the clock the GPU
+# ran, beside the FLOP-derived fraction of the datasheet peak.
+MFMA_BUSY = {
+    "chunk_fwd_fused_kernel": dict(sources=TRAFFIC["chunk_fwd_fused_kernel"]["sources"],
+                                   busy=0.385, sha256=TRAFFIC["chunk_fwd_fused_kernel"]["sha256"]),
+    "chunk_scan_bf16_kernel": dict(sources=TRAFFIC["chunk_scan_bf16_kernel"]["sources"],
+                                   busy=0.255, sha256=_SPLIT_SHA),
+    "chunk_prep_kernel": dict(sources=TRAFFIC["chunk_prep_kernel"]["sources"], busy=0.081,
+                              sha256=_SPLIT_SHA),
+}
+
+
+def mfma_busy(kernel):
+    t = MFMA_BUSY.get(kernel) if kernel else None
+    if t is None or sources_sha256(t["sources"]) != t["sha256"]:
+        return None
+    return t["busy"]
 
 
 def sources_sha256(names):
@@ -177,7 +201,8 @@ def roofline_of(kernel, us, flop, nbytes):
              "unit": "TFLOP/s", "frac": flop / sec / PEAK_BF16_FLOPS}
     r["traffic"] = traffic_bytes(kernel)
     r.update({"kernel": kernel, "us": us, "algorithmic_bytes": nbytes, "algorithmic_flop": flop,
-              "mfma_frac": flop / sec / PEAK_BF16_FLOPS, "hbm_frac": nbytes / sec / PEAK_HBM_BPS})
+              "mfma_frac": flop / sec / PEAK_BF16_FLOPS, "hbm_frac": nbytes / sec / PEAK_HBM_BPS,
+              "mfma_busy_counter": mfma_busy(kernel)})
     return r
 
 
