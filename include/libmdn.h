@@ -248,9 +248,12 @@ mdn_status mdn_decode_step(const void* q, const void* k, const void* v, const fl
  *   otherwise); dS0, dM0 [B, H, Dk, Dv] or NULL (not returned).
  * Every pointer is a device pointer aligned to 16 bytes; no output may
  * overlap an input, another output or the workspace.  Workspace:
- * mdn_chunk_bwd_workspace_bytes (T and A of every chunk, the coefficient
- * rows, two state pairs and the residuals of every chunk, in float32 but for
- * T and A).  T = 0 copies dS_T, dM_T to dS0, dM0.  Enqueued on `stream`.
+ * mdn_chunk_bwd_workspace_bytes: T and A of every chunk (dtype dt), the
+ * coefficient rows (float32), each chunk's entry-state pair and exit-state
+ * gradient pair (dtype dt: bf16 for MDN_BF16, float32 for MDN_F32) and each
+ * chunk's recomputed residuals (float32, written only when Vt is NULL); its
+ * contents on entry do not matter.  T = 0 copies dS_T, dM_T to dS0, dM0.
+ * Enqueued on `stream`.
  */
 size_t mdn_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
                                      mdn_dtype dt);
