@@ -25,8 +25,8 @@ hipError_t launch_chunk_fused(const void* q, const void* k, const void* v, const
                               hipStream_t stream);
 hipError_t launch_chunk_scan(const void* q, const void* k, const void* v, const float* S0,
                              const float* M0, void* O, void* Vto, float* ST, float* MT, int B,
-                             int T, int H, int Dk, int Dv, bool bf16, const void* workspace,
-                             hipStream_t stream);
+                             int T, int H, int Dk, int Dv, bool bf16, bool row_split,
+                             bool momentum, const void* workspace, hipStream_t stream);
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* alpha,
                          const float* mu, const float* eta, const float* beta, float* S, float* M,
                          void* o, int heads, int Dk, int Dv, bool bf16, hipStream_t stream);
@@ -88,6 +88,26 @@ bool mul_ok(size_t a, size_t b, size_t c, size_t d, size_t* out)
     return true;
 }
 
+// The bf16 forward's partition of the state (mdn_set_fwd_path).
+std::atomic<int> fwd_path{MDN_FWD_AUTO};
+
+// Under MDN_FWD_AUTO the row split runs up to this many 64-column head tiles
+// (an eighth of the 256 compute units).  Measured on MI355X (d = 128): at 8
+// to 32 tiles and 4K to 16K tokens the row split took 0.84-0.96 of the column
+// tiles' time, at 64 tiles 0.95-1.09 and at 128 tiles about 2x.
+constexpr size_t ROW_SPLIT_MAX_TILES = 32;
+
+// True when a bf16 forward of this shape runs the row-split scan; `want_vt`:
+// the caller asked for the residuals, which only the column tiles store.
+bool row_split_for(int B, int H, int Dv, mdn_dtype dt, bool want_vt)
+{
+    if (dt != MDN_BF16 || want_vt || B <= 0 || H <= 0) return false;
+    const int p = fwd_path.load(std::memory_order_relaxed);
+    if (p == MDN_FWD_COLUMN_TILES) return false;
+    if (p == MDN_FWD_ROW_SPLIT) return true;
+    return (size_t)B * (size_t)H * (size_t)(Dv / 64) <= ROW_SPLIT_MAX_TILES;
+}
+
 }  // namespace
 
 extern "C" {
@@ -120,11 +140,18 @@ static size_t split_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chu
 size_t mdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
                                      mdn_dtype dt)
 {
-    // the bf16 forward keeps T and A on chip and needs only the per-chunk
+    // the bf16 column tiles keep T and A on chip and need only the per-chunk
     // coefficient tables
     const size_t split = split_workspace_bytes(B, T, H, Dk, Dv, chunk, dt);
-    if (split == 0 || dt != MDN_BF16) return split;
+    if (split == 0 || dt != MDN_BF16 || row_split_for(B, H, Dv, dt, false)) return split;
     return mdn::chunk_fused_workspace_bytes((size_t)B * H * (((size_t)T + 63) / 64));
+}
+
+int mdn_set_fwd_path(int path)
+{
+    if (path != MDN_FWD_AUTO && path != MDN_FWD_COLUMN_TILES && path != MDN_FWD_ROW_SPLIT)
+        return -1;
+    return fwd_path.exchange(path);
 }
 
 size_t mdn_chunk_fwd_split_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
@@ -153,6 +180,9 @@ struct FwdArgs {
     // after validation: ws_bytes is its capacity, and it overlaps no
     // caller buffer
     bool static_ws = false;
+    // bf16: the row-split scan runs (after the prepare kernel when phase is
+    // BOTH) instead of the column-tiled kernels
+    bool row_split = false;
 };
 
 // Every host-side check of the forward entry points.  `phase` says which
@@ -190,7 +220,7 @@ mdn_status validate_fwd(const FwdArgs& a, int phase, bool* no_work)
         if (p && !aligned16(p)) return MDN_ERR_ALIGN;
 
     // the bf16 forward runs fused and needs only the per-chunk coefficient tables
-    const bool fused = phase == BOTH && a.dt == MDN_BF16;
+    const bool fused = phase == BOTH && a.dt == MDN_BF16 && !a.row_split;
     const size_t nchunks = (size_t)a.B * a.H * (((size_t)a.T + 63) / 64);
     const size_t need = !tok ? 0
                         : fused ? mdn::chunk_fused_workspace_bytes(nchunks)
@@ -235,7 +265,7 @@ mdn_status validate_fwd(const FwdArgs& a, int phase, bool* no_work)
 mdn_status launch_fwd(const FwdArgs& a, int phase, hipStream_t stream)
 {
     const bool bf16 = a.dt == MDN_BF16;
-    if (phase == BOTH && bf16 && a.T > 0) {
+    if (phase == BOTH && bf16 && !a.row_split && a.T > 0) {
         const hipError_t err =
             mdn::launch_chunk_fused(a.q, a.k, a.v, a.alpha, a.mu, a.eta, a.beta, a.S0, a.M0, a.O,
                                     a.Vt, a.S_T, a.M_T, a.B, a.T, a.H, a.Dk, a.Dv,
@@ -249,9 +279,13 @@ mdn_status launch_fwd(const FwdArgs& a, int phase, hipStream_t stream)
         if (err != hipSuccess) return MDN_ERR_HIP;
     }
     if (phase & SCAN) {
+        // a NULL mu (phase BOTH only: the scan entry point has no gates) means
+        // mu = 0, and then M0 is not read
+        const bool momentum = phase != BOTH || a.mu != nullptr;
+        const float* M0 = momentum || a.T == 0 ? a.M0 : nullptr;
         const hipError_t err =
-            mdn::launch_chunk_scan(a.q, a.k, a.v, a.S0, a.M0, a.O, a.Vt, a.S_T, a.M_T, a.B, a.T,
-                                   a.H, a.Dk, a.Dv, bf16, a.ws, stream);
+            mdn::launch_chunk_scan(a.q, a.k, a.v, a.S0, M0, a.O, a.Vt, a.S_T, a.M_T, a.B, a.T,
+                                   a.H, a.Dk, a.Dv, bf16, a.row_split, momentum, a.ws, stream);
         if (err != hipSuccess) return MDN_ERR_HIP;
     }
     return MDN_OK;
@@ -312,8 +346,9 @@ mdn_status mdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          int T, int H, int Dk, int Dv, int chunk, mdn_dtype dt, void* workspace,
                          size_t workspace_bytes, hipStream_t stream)
 {
-    const FwdArgs a{q, k, v, alpha, mu, eta, beta, S0, M0, O, Vt, S_T, M_T, B, T, H, Dk, Dv,
-                    chunk, dt, workspace, workspace_bytes};
+    FwdArgs a{q, k, v, alpha, mu, eta, beta, S0, M0, O, Vt, S_T, M_T, B, T, H, Dk, Dv,
+              chunk, dt, workspace, workspace_bytes};
+    a.row_split = row_split_for(B, H, Dv, dt, Vt != nullptr);
     return run_fwd(a, BOTH, stream);
 }
 
@@ -326,10 +361,13 @@ mdn_status mdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
     FwdArgs a{q, k, v, alpha, mu, eta, beta, S0, M0, O, Vt, S_T, M_T, B, T, H, Dk, Dv,
               chunk, dt, nullptr, MDN_NOALLOC_SCRATCH_BYTES};
     a.static_ws = true;
+    // the row split only where its workspace fits the array
+    a.row_split = row_split_for(B, H, Dv, dt, Vt != nullptr) &&
+                  split_workspace_bytes(B, T, H, Dk, Dv, chunk, dt) <= MDN_NOALLOC_SCRATCH_BYTES;
     bool no_work = false;
     mdn_status st = validate_fwd(a, BOTH, &no_work);
     if (st != MDN_OK || no_work) return st;
-    if (mdn_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, dt) > 0) {
+    if (split_workspace_bytes(B, T, H, Dk, Dv, chunk, dt) > 0) {
         void* p = nullptr;
         st = scratch_for_stream(stream, &p);
         if (st != MDN_OK) return st;
@@ -355,8 +393,9 @@ mdn_status mdn_chunk_fwd_scan(const void* q, const void* k, const void* v, const
                               int H, int Dk, int Dv, int chunk, mdn_dtype dt,
                               const void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    const FwdArgs a{q, k, v, nullptr, nullptr, nullptr, nullptr, S0, M0, O, nullptr, S_T, M_T, B,
-                    T, H, Dk, Dv, chunk, dt, workspace, workspace_bytes};
+    FwdArgs a{q, k, v, nullptr, nullptr, nullptr, nullptr, S0, M0, O, nullptr, S_T, M_T, B,
+              T, H, Dk, Dv, chunk, dt, workspace, workspace_bytes};
+    a.row_split = row_split_for(B, H, Dv, dt, false);
     return run_fwd(a, SCAN, stream);
 }
 

@@ -39,6 +39,8 @@
 //                      into the next products directly from the accumulators.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "chunk_common.hpp"
 #include "mfma.hpp"
 
@@ -946,6 +948,399 @@ __global__ __launch_bounds__(2 * NT) void chunk_scan_bf16_kernel(
     if (MT) store_state(MT, Ma);
 }
 
+// ---------------------------------------------------------------------------
+// bf16 scan for layers with few heads ("row split").  When B * H * DV / 64 is
+// well below the number of compute units, one workgroup per 64 value columns
+// leaves most of the chip idle, and each chunk costs the latency of one
+// wavefront's whole chain (K S, the substitution, the outputs, the update of
+// all DK state rows).  Here a workgroup owns 16 value columns, and its NW
+// compute wavefronts split the state rows: wavefront w holds rows
+// [RW w, RW w + RW), RW = DK / NW, of S and M for those columns, for the
+// whole sequence.  The chunk equations are those of chunk_scan_bf16_kernel;
+// per chunk:
+//   (a) products over the wavefront's own rows: K_w [S_w | M_w] gives its
+//       share of R = V - Diag(abar) K S0 + Diag(alpha b^-) K M0 (wavefront 0
+//       adds V), and [S_w | M_w]^T Q_w^T its share of the outputs' entry-state
+//       part; the shares go to LDS (each wavefront keeps its own);
+//   barrier;
+//   (b) every wavefront sums the R shares and forms all of Vt = T R (the same
+//       8 products on each wavefront, cheaper than a second exchange),
+//       updates its rows with K_w^T Diag(w) Vt, and finishes the output rows
+//       of its own 16-row tiles (the sum of the shares plus Vt^T A^T);
+//   barrier.
+// Four staging wavefronts bring chunk c + 1 into the other buffer
+// meanwhile, with direct global-to-LDS loads only: the transposed K of the
+// update and V in the layout of R are read from the row-major tiles with
+// transposing LDS reads.  The 16-column strips of one head run on one XCD,
+// so the head's K, Q, T and A come from HBM once and from that L2 after.
+// MU = false is the momentum-free case (mu = 0: b, alpha b^- and mubar_n
+// vanish, so M never feeds S): every product with M is dropped, M0 is not
+// read, and M_T is formed in the last chunk only, from the zero momentum.
+// ---------------------------------------------------------------------------
+template <int DK, int NW>
+struct ScanRsLayout {
+    using LK = TileLayout<DK * 2>;          // K, Q rows
+    using LC = TileLayout<CH * 2>;          // T, A rows
+    static constexpr int RW = DK / NW;      // state rows per compute wavefront
+    static constexpr int NS = 4;            // staging wavefronts
+    static constexpr int TS = 16;           // value columns per workgroup
+    static_assert(RW == 32 || RW == 64, "rows per wavefront");
+    static constexpr int OFF_Q = LK::BYTES;
+    static constexpr int OFF_T = 2 * LK::BYTES;
+    static constexpr int OFF_A = OFF_T + LC::BYTES;
+    static constexpr int OFF_V = OFF_A + LC::BYTES;     // 64 rows x 32 bytes, row-major
+    static constexpr int OFF_VEC = OFF_V + CH * TS * 2;
+    static constexpr int BUF_BYTES = OFF_VEC + 6 * CH * 4;
+    // one f32x4 per (wavefront, 16-row tile, lane)
+    static constexpr int SHARE_BYTES = NW * 4 * 64 * 16;
+    static constexpr int OFF_RP = 2 * BUF_BYTES;
+    static constexpr int OFF_OP = OFF_RP + SHARE_BYTES;
+    static constexpr int BYTES = OFF_OP + SHARE_BYTES;
+    // byte distance between the rows 32 s + x and x of a K tile
+    static constexpr int KSTEP_ROWS = 32 * (DK * 2) + (32 / LK::G) * LK::PAD;
+    static_assert(BYTES <= 160 * 1024, "LDS");
+};
+
+// The LDS buffer index of a chunk: a compile-time constant when the chunk
+// loop is unrolled by two, a run-time parity otherwise.
+template <int V>
+__device__ constexpr int buf_of(std::integral_constant<int, V>) { return V; }
+__device__ inline int buf_of(int b) { return b; }
+
+template <int DK, int DV, int NW, bool UNROLL, bool MU>
+__global__ __launch_bounds__(64 * (NW + 4)) void chunk_scan_rs_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ Tw, const __bf16* __restrict__ Aw, const float* __restrict__ Vw,
+    const float* S0, const float* M0, __bf16* __restrict__ O, float* ST, float* MT, int T, int H,
+    int NC, int xcd_groups)
+{
+    using E = __bf16;
+    using MM = Mma<E>;
+    using L = ScanRsLayout<DK, NW>;
+    using LK = typename L::LK;
+    using LC = typename L::LC;
+    constexpr int RW = L::RW;
+    constexpr int RT = RW / 16;             // state row tiles per wavefront
+    constexpr int SKW = RW / 32;            // k-steps of the shares
+    constexpr int TS = L::TS;
+    constexpr int NSTRIP = DV / TS;
+    constexpr int CTW = 4 / NW;             // output row tiles each compute wavefront finishes
+
+    __shared__ __align__(16) char smem[L::BYTES];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l16 = lane & 15;
+    const int lg = lane >> 4;
+
+    unsigned bid = blockIdx.x;
+    if (xcd_groups > 0) bid = (bid % 8u) * (unsigned)xcd_groups + bid / 8u;
+    const int strip = (int)(bid % NSTRIP);
+    const int bh = (int)(bid / NSTRIP);
+    const int h = bh % H;
+    const int b = bh / H;
+    const size_t tokb = (size_t)b * T * H + h;   // token (b, 0, h)
+
+    if (wave >= NW) {
+        // ---------------- staging wavefronts ----------------
+        const int hw = wave - NW;
+        const unsigned kq_stride = (unsigned)(H * DK);
+        const unsigned kq_lane = LK::lane_offset(kq_stride, lane);
+        const unsigned c_lane = LC::lane_offset(CH, lane);
+        auto stage = [&](int c, int bi) {
+            const int n = min(CH, T - c * CH);
+            const size_t tok0 = tokb + (size_t)c * CH * H;
+            const size_t chn = (size_t)bh * NC + c;
+            char* B = smem + bi * L::BUF_BYTES;
+            LK::load(B, k + tok0 * DK, kq_stride, kq_lane, n, hw, lane);
+            LK::load(B + L::OFF_Q, q + tok0 * DK, kq_stride, kq_lane, n, hw, lane);
+            LC::load(B + L::OFF_T, Tw + chn * CH * CH, CH, c_lane, CH, hw, lane);
+            LC::load(B + L::OFF_A, Aw + chn * CH * CH, CH, c_lane, CH, hw, lane);
+            if (hw < 2) {
+                // the strip of V: lane l brings half l % 2 of row 32 hw + l / 2
+                // (rows >= n read row n - 1)
+                const int row = min(32 * hw + (lane >> 1), n - 1);
+                direct_load16(v + (tok0 + (size_t)row * H) * DV + strip * TS + 8 * (lane & 1),
+                              B + L::OFF_V + 1024 * hw);
+            } else if (hw == 2 || lane < 32) {
+                // coefficient vectors: 6 x 64 floats = 96 pieces of 16 bytes
+                direct_load16(Vw + chn * NVEC * CH + 4 * (64 * (hw - 2) + lane),
+                              B + L::OFF_VEC + 1024 * (hw - 2));
+            }
+        };
+        stage(0, 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+        for (int c = 0; c < NC; ++c) {
+            if (c + 1 < NC) stage(c + 1, (c + 1) & 1);
+            lds_barrier();                                   // (a) -> (b)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();                                   // chunk c + 1 staged
+        }
+        return;
+    }
+
+    // ---------------- compute wavefronts ----------------
+    const int w = wave;
+    const int col = strip * TS + l16;                       // this lane's state column
+
+    // state slot (rt, lg, r): row RW w + phys_row(16 rt + 4 lg + r), column col
+    f32x4 Sa[RT], Ma[RT];
+    const size_t sbase = (size_t)bh * DK * DV;
+    auto srow = [&](int rt, int r) { return RW * w + phys_row(16 * rt + 4 * lg + r); };
+    auto load_state = [&](f32x4* X, const float* src) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                X[rt][r] = src ? src[sbase + (size_t)srow(rt, r) * DV + col] : 0.f;
+    };
+    if (S0) load_state(Sa, S0); else load_state(Sa, nullptr);
+    if (MU && M0) load_state(Ma, M0); else load_state(Ma, nullptr);
+
+    // per-lane LDS byte offsets, the same every chunk
+    int kq_base[4], c_base[4], v_off[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        const int r = phys_row(16 * x + l16);
+        // K_w / Q_w fragment of step s: row r, columns RW w + 32 s + 8 lg .. + 7
+        kq_base[x] = LK::chunk(r, (RW / 8) * w + lg);
+        c_base[x] = LC::chunk(r, lg);
+        // V rows phys_row(16 x + 4 lg) + j, columns 4 m .. + 3 (lane 4 j + m
+        // of its group): the transposing read hands lane l16 column l16
+        v_off[x] = L::OFF_V + (phys_row(16 * x + 4 * lg) + (l16 >> 2)) * (TS * 2) + 8 * (l16 & 3);
+    }
+    // The output row tiles in this wavefront's order: tile j is
+    // ct_j = (CTW w + j) mod 4, so that its own tiles (those it finishes) are
+    // j < CTW.  Everything indexed by ct_j is a per-lane constant, chosen
+    // here once, so the chunk loop has no wavefront-dependent branches.
+    int q_rot[4], a_rot[4], orow_rot[4], op_rot[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int ctj = (CTW * w + j) & 3;
+        const int r = phys_row(16 * ctj + l16);
+        q_rot[j] = LK::chunk(r, (RW / 8) * w + lg);
+        a_rot[j] = LC::chunk(r, lg);
+        orow_rot[j] = r;
+        op_rot[j] = ((w * 4 + ctj) * 64 + lane) * 16;             // this wavefront's share
+    }
+    // K_w^T fragments of the update (tile rt, half hf, step s): lane 4 j + m
+    // of group lg reads K row 32 s + 8 lg + 4 hf + j, columns
+    // RW w + phys_row(16 rt + 4 m) .. + 3; the transposing read hands lane l16
+    // column RW w + phys_row(16 rt + l16) of those four rows.  Rows 32 s + x
+    // lie L::KSTEP_ROWS bytes after row x.
+    int kt_off[RT][2];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+            kt_off[rt][hf] = LK::chunk(8 * lg + 4 * hf + (l16 >> 2),
+                                       (RW / 8) * w + 4 * (rt >> 1) + (l16 & 3)) + 8 * (rt & 1);
+    // the other wavefronts' shares, in the order w + 1, w + 2, ... (mod NW)
+    int peer[NW > 1 ? NW - 1 : 1];
+#pragma unroll
+    for (int u = 1; u < NW; ++u) peer[u - 1] = (w + u) % NW;
+    const float vsel = w == 0 ? 1.f : 0.f;                  // wavefront 0 adds V to its share
+    const unsigned ostride = (unsigned)(H * DV);
+    E* const Ocol = O + tokb * DV + strip * TS + 4 * lg;
+    char* const Rp = smem + L::OFF_RP;
+    char* const Op = smem + L::OFF_OP;
+    auto share = [](char* base, int off) -> f32x4& { return *reinterpret_cast<f32x4*>(base + off); };
+
+    // one chunk; `bi` is its LDS buffer (chunk c sits in buffer c mod 2)
+    auto chunk_step = [&](const int c, auto bi) {
+        const int t0 = c * CH;
+        const int n = min(CH, T - t0);
+        const char* Kb = smem + buf_of(bi) * L::BUF_BYTES;
+        const char* Qb = Kb + L::OFF_Q;
+        const char* Tb = Kb + L::OFF_T;
+        const char* Ab = Kb + L::OFF_A;
+        const float* vec = reinterpret_cast<const float*>(Kb + L::OFF_VEC);
+
+        // (a) shares over this wavefront's rows.  Operands are read in the
+        //     order they are needed: K first (the critical path), then what
+        //     the rest of the chunk reads from this buffer, so that those
+        //     reads overlap the products instead of following the exchange.
+        //     T is lower triangular by 16-row blocks: its upper right 32 x 32
+        //     block is neither read nor multiplied.
+        bf16x8 aK[SKW][4];
+#pragma unroll
+        for (int s = 0; s < SKW; ++s)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+                aK[s][ct] = *reinterpret_cast<const bf16x8*>(Kb + kq_base[ct] + 64 * s);
+        f32x4 ab[4], ab1[4];
+        bf16x4 vv[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            const int p0 = phys_row(16 * ct + 4 * lg);
+            ab[ct] = *reinterpret_cast<const f32x4*>(vec + V_ABAR * CH + p0);
+            if (MU) ab1[ct] = *reinterpret_cast<const f32x4*>(vec + V_AB1 * CH + p0);
+            vv[ct] = lds_read_tr4(Kb + v_off[ct]);
+        }
+        bf16x8 aQ[SKW][4], aT[2][4], aA[2][CTW];
+        bf16x4 kt[2][RT][2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+            for (int it = 2 * s; it < 4; ++it)
+                aT[s][it] = *reinterpret_cast<const bf16x8*>(Tb + c_base[it] + 64 * s);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+                    kt[s][rt][hf] = lds_read_tr4(Kb + kt_off[rt][hf] + s * L::KSTEP_ROWS);
+        }
+#pragma unroll
+        for (int s = 0; s < SKW; ++s)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                aQ[s][j] = *reinterpret_cast<const bf16x8*>(Qb + q_rot[j] + 64 * s);
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int u = 0; u < CTW; ++u)
+                aA[s][u] = *reinterpret_cast<const bf16x8*>(Ab + a_rot[u] + 64 * s);
+
+        f32x4 rown[4], oown[CTW];
+        {
+            f32x4 xs[4], xm[4];
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) xs[ct] = xm[ct] = zero4();
+#pragma unroll
+            for (int s = 0; s < SKW; ++s) {
+                const auto bS = MM::from_acc(Sa, s);
+                const auto bM = MM::from_acc(Ma, s);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    xs[ct] = MM::mma(aK[s][ct], bS, xs[ct]);
+                    if (MU) xm[ct] = MM::mma(aK[s][ct], bM, xm[ct]);
+                }
+            }
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                f32x4 rp;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    rp[r] = vsel * static_cast<float>(vv[ct][r]) - ab[ct][r] * xs[ct][r];
+                    if (MU) rp[r] += ab1[ct][r] * xm[ct][r];
+                }
+                rown[ct] = rp;
+                share(Rp, ((w * 4 + ct) * 64 + lane) * 16) = rp;
+            }
+        }
+        {
+            f32x4 ys[4], ym[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ys[j] = ym[j] = zero4();
+#pragma unroll
+            for (int s = 0; s < SKW; ++s) {
+                const auto bS = MM::from_acc(Sa, s);
+                const auto bM = MM::from_acc(Ma, s);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    ys[j] = MM::mma(bS, aQ[s][j], ys[j]);
+                    if (MU) ym[j] = MM::mma(bM, aQ[s][j], ym[j]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                f32x4 op = vec[V_ABAR * CH + orow_rot[j]] * ys[j];
+                if (MU) op -= vec[V_B * CH + orow_rot[j]] * ym[j];
+                if (j < CTW) oown[j] = op;
+                else share(Op, op_rot[j]) = op;
+            }
+        }
+        lds_barrier();
+
+        // (b) R, Vt = T R
+        f32x4 R[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            R[ct] = rown[ct];
+#pragma unroll
+            for (int u = 0; u < NW - 1; ++u)
+                R[ct] += share(Rp, ((peer[u] * 4 + ct) * 64 + lane) * 16);
+        }
+        f32x4 Vt[4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) Vt[it] = zero4();
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const auto bR = MM::from_acc(R, s);
+#pragma unroll
+            for (int it = 2 * s; it < 4; ++it) Vt[it] = MM::mma(aT[s][it], bR, Vt[it]);
+        }
+
+        // S' = abar_n S0 - b_n M0 + K^T Diag(eta gamma_n) Vt,
+        // M' = mubar_n M0 - K^T Diag(eta mubar_n / mubar) Vt, on this wavefront's rows
+        const float abn = vec[V_SCAL * CH + 0];
+        const float bn = vec[V_SCAL * CH + 1];
+        const float mbn = vec[V_SCAL * CH + 2];
+        // without momentum M' matters only after the last chunk
+        const bool upd_m = MU || (MT != nullptr && c == NC - 1);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            if (MU) {
+                Sa[rt] = abn * Sa[rt] - bn * Ma[rt];
+                Ma[rt] = mbn * Ma[rt];
+            } else {
+                Sa[rt] = abn * Sa[rt];
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const auto bS = MM::from_acc_scaled8(Vt, s, vec + V_WS * CH + 32 * s + 8 * lg, 1.f);
+            const auto bM = MM::from_acc_scaled8(Vt, s, vec + V_WM * CH + 32 * s + 8 * lg, -1.f);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const bf16x4 lo = kt[s][rt][0], hi = kt[s][rt][1];
+                const bf16x8 aKt = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                Sa[rt] = MM::mma(aKt, bS, Sa[rt]);
+                if (upd_m) Ma[rt] = MM::mma(aKt, bM, Ma[rt]);
+            }
+        }
+
+        // outputs of this wavefront's row tiles: O^T = sum of the shares + Vt^T A^T
+#pragma unroll
+        for (int u = 0; u < CTW; ++u) {
+            f32x4 ot = oown[u];
+            // the share of wavefront x for this tile sits (x - w) * 4 KB from ours
+#pragma unroll
+            for (int x = 0; x < NW - 1; ++x)
+                ot += share(Op, op_rot[u] + (peer[x] - w) * 4 * 64 * 16);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) ot = MM::mma(MM::from_acc(Vt, s), aA[s][u], ot);
+            if (orow_rot[u] < n)
+                store4<E>(Ocol + (size_t)(t0 + orow_rot[u]) * ostride, ot[0], ot[1], ot[2], ot[3]);
+        }
+        // this chunk's buffer and the shares are free; the next chunk is staged
+        lds_barrier();
+    };
+    lds_barrier();                                          // chunk 0 staged
+    if constexpr (UNROLL) {
+        // two chunks per iteration: every LDS address is a per-lane base
+        // plus an immediate
+        for (int c = 0; c < NC; c += 2) {
+            chunk_step(c, std::integral_constant<int, 0>{});
+            if (c + 1 < NC) chunk_step(c + 1, std::integral_constant<int, 1>{});
+        }
+    } else {
+        for (int c = 0; c < NC; ++c) chunk_step(c, c & 1);
+    }
+
+    auto store_state = [&](float* dst, const f32x4* X) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dst[sbase + (size_t)srow(rt, r) * DV + col] = X[rt][r];
+    };
+    if (ST) store_state(ST, Sa);
+    if (MT) store_state(MT, Ma);
+}
+
 // T = 0: the final state is the initial state (zero when absent)
 __global__ __launch_bounds__(NT) void state_passthrough_kernel(const float* __restrict__ src,
                                                                float* dst, size_t count)
@@ -997,6 +1392,35 @@ static hipError_t launch_scan_t(const void* q, const void* k, const void* v, con
     return hipGetLastError();
 }
 
+template <int DK, int DV>
+static hipError_t launch_scan_rs_t(const void* q, const void* k, const void* v, const float* S0,
+                                   const float* M0, void* O, float* ST, float* MT, int B, int T,
+                                   int H, bool momentum, const void* workspace,
+                                   hipStream_t stream)
+{
+    // Compute wavefronts per strip and loop shape, as measured fastest at
+    // B1 H16 T16384 d128: with momentum four wavefronts (32 rows each) and the
+    // loop unrolled by two; without, two wavefronts (64 rows each; unrolled,
+    // their registers would spill).  Dk = 64 always runs two.
+    constexpr int NW = DK == 64 ? 2 : 4;
+    using L = ScanRsLayout<DK, NW>;
+    using L2 = ScanRsLayout<DK, 2>;
+    const int NC = (T + CH - 1) / CH;
+    const size_t nchunks = (size_t)B * H * NC;
+    Workspace<__bf16> ws = ws_carve<__bf16>(const_cast<void*>(workspace), nchunks);
+    const size_t nblk = (size_t)B * H * (DV / L::TS);
+    if (nblk > 0xffffffffu) return hipErrorInvalidValue;
+    const int xcd_groups = nblk % 8 == 0 ? (int)(nblk / 8) : 0;
+    auto kern = momentum ? chunk_scan_rs_kernel<DK, DV, NW, DK != 64, true>
+                         : chunk_scan_rs_kernel<DK, DV, 2, false, false>;
+    const int waves = momentum ? NW + L::NS : 2 + L2::NS;
+    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(64 * waves), 0, stream,
+                       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                       static_cast<const __bf16*>(v), ws.T, ws.A, ws.vec, S0, M0,
+                       static_cast<__bf16*>(O), ST, MT, T, H, NC, xcd_groups);
+    return hipGetLastError();
+}
+
 // dst = src (src NULL: zero), count floats
 hipError_t launch_state_copy(const float* src, float* dst, size_t count, hipStream_t stream)
 {
@@ -1032,8 +1456,8 @@ hipError_t launch_chunk_prepare(const void* q, const void* k, const float* alpha
 
 hipError_t launch_chunk_scan(const void* q, const void* k, const void* v, const float* S0,
                              const float* M0, void* O, void* Vto, float* ST, float* MT, int B,
-                             int T, int H, int Dk, int Dv, bool bf16, const void* workspace,
-                             hipStream_t stream)
+                             int T, int H, int Dk, int Dv, bool bf16, bool row_split,
+                             bool momentum, const void* workspace, hipStream_t stream)
 {
     if (T == 0) {
         const size_t count = (size_t)B * H * Dk * Dv;
@@ -1050,6 +1474,16 @@ hipError_t launch_chunk_scan(const void* q, const void* k, const void* v, const 
             return hipGetLastError();
         }
         return hipSuccess;
+    }
+    if (bf16 && row_split) {
+        if (Vto) return hipErrorInvalidValue;   // the row-split scan does not store Vt
+#define MDN_SCAN_RS(DK, DV)                                                                      \
+    if (Dk == DK && Dv == DV)                                                                    \
+        return launch_scan_rs_t<DK, DV>(q, k, v, S0, M0, O, ST, MT, B, T, H, momentum,      \
+                                        workspace, stream);
+        MDN_SCAN_RS(64, 64) MDN_SCAN_RS(64, 128) MDN_SCAN_RS(128, 64) MDN_SCAN_RS(128, 128)
+#undef MDN_SCAN_RS
+        return hipErrorInvalidValue;
     }
 #define MDN_SCAN(E, DK, DV)                                                                      \
     if (Dk == DK && Dv == DV)                                                                    \

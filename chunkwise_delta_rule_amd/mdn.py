@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(_PKG, "libmdn.so")
 
 MDN_F32 = 0
 MDN_BF16 = 1
+# mdn_fwd_path: how the bf16 forward partitions the carried state
+FWD_PATHS = {"auto": 0, "column_tiles": 1, "row_split": 2}
 CHUNK = 64
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MDN_NOALLOC_SCRATCH_BYTES
 HEAD_DIMS = (64, 128)
@@ -36,11 +38,11 @@ STATUS_NAMES = {
 }
 
 # every symbol include/libmdn.h declares
-EXPORTED = ("mdn_chunk_fwd_workspace_bytes", "mdn_chunk_fwd_split_workspace_bytes",
-            "mdn_chunk_fwd", "mdn_chunk_fwd_noalloc", "mdn_chunk_fwd_prepare",
-            "mdn_chunk_fwd_scan", "mdn_decode_step", "mdn_gates_from_logits",
-            "mdn_chunk_bwd_workspace_bytes", "mdn_chunk_bwd", "mdn_qk_prologue",
-            "mdn_output_epilogue", "mdn_status_string")
+EXPORTED = ("mdn_set_fwd_path", "mdn_chunk_fwd_workspace_bytes",
+            "mdn_chunk_fwd_split_workspace_bytes", "mdn_chunk_fwd", "mdn_chunk_fwd_noalloc",
+            "mdn_chunk_fwd_prepare", "mdn_chunk_fwd_scan", "mdn_decode_step",
+            "mdn_gates_from_logits", "mdn_chunk_bwd_workspace_bytes", "mdn_chunk_bwd",
+            "mdn_qk_prologue", "mdn_output_epilogue", "mdn_status_string")
 
 
 class GateParams(ctypes.Structure):
@@ -68,6 +70,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                           "`python -m chunkwise_delta_rule_amd.build`")
     lib = ctypes.CDLL(path)
     P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.mdn_set_fwd_path.restype = I
+    lib.mdn_set_fwd_path.argtypes = [I]
     lib.mdn_chunk_fwd_workspace_bytes.restype = S
     lib.mdn_chunk_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.mdn_chunk_fwd_split_workspace_bytes.restype = S
@@ -129,6 +133,32 @@ def _check(t: torch.Tensor, name: str, shape, dtype, device):
 
 def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def set_fwd_path(path: str) -> str:
+    """Select the bf16 forward's state partition for every later call
+    (mdn_set_fwd_path): "auto", "column_tiles" or "row_split".  Returns the
+    previous setting's name."""
+    if path not in FWD_PATHS:
+        raise ValueError(f"unknown forward path {path!r}; one of {sorted(FWD_PATHS)}")
+    prev = load_library().mdn_set_fwd_path(FWD_PATHS[path])
+    return {v: k for k, v in FWD_PATHS.items()}[prev]
+
+
+class fwd_path:
+    """Context manager: run the enclosed calls with one forward path."""
+
+    def __init__(self, path: str):
+        self.path = path
+        self.prev = None
+
+    def __enter__(self):
+        self.prev = set_fwd_path(self.path)
+        return self
+
+    def __exit__(self, *exc):
+        set_fwd_path(self.prev)
+        return False
 
 
 def workspace_bytes(B: int, T: int, H: int, Dk: int, Dv: int, dtype: torch.dtype,

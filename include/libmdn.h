@@ -65,15 +65,58 @@ typedef enum {
 } mdn_dtype;
 
 /*
- * Bytes of device workspace mdn_chunk_fwd needs for this problem.  With
- * dt = MDN_BF16 the forward keeps the chunk-local matrices T and A on chip
+ * How the bf16 forward partitions the carried state over workgroups.  The
+ * scan over chunks is sequential, so its parallelism is the number of state
+ * tiles in flight:
+ *   MDN_FWD_COLUMN_TILES  one workgroup per 64 value columns of a head, each
+ *                         wavefront owning 16 columns and all Dk rows.
+ *                         mdn_chunk_fwd runs one fused kernel that also forms
+ *                         T and A on chip; mdn_chunk_fwd_scan runs the
+ *                         column-tiled scan.
+ *   MDN_FWD_ROW_SPLIT     one workgroup per 16 value columns (4x the
+ *                         workgroups), its Dk/32 wavefronts splitting the
+ *                         rows and exchanging partial products in LDS.
+ *                         mdn_chunk_fwd runs the two phases below
+ *                         (mdn_chunk_fwd_prepare's kernel, then this scan).
+ *                         It does not produce the residuals: a call with
+ *                         Vt != NULL runs the column-tiled kernels.
+ *   MDN_FWD_AUTO          (the default) the row split when the layer has at
+ *                         most 32 column tiles, B * H * (Dv / 64) <= 32,
+ *                         where it measured faster on MI355X (at 64 tiles the
+ *                         two are about even, at 128 the column tiles take
+ *                         half the time).
+ * Both partitions evaluate the same equations; their results agree to
+ * rounding, not bit for bit.  MDN_F32 always runs the two-phase path.
+ */
+typedef enum {
+    MDN_FWD_AUTO = 0,
+    MDN_FWD_COLUMN_TILES = 1,
+    MDN_FWD_ROW_SPLIT = 2
+} mdn_fwd_path;
+
+/*
+ * Sets the process-wide forward path for every later call (on any device
+ * and thread) and returns the previous setting; an unknown value changes
+ * nothing and returns -1.  Meant for benchmarking and testing both
+ * partitions: a workspace sized by mdn_chunk_fwd_workspace_bytes under one
+ * setting may be too small under another (MDN_ERR_WORKSPACE, nothing
+ * launched).
+ */
+int mdn_set_fwd_path(int path);
+
+/*
+ * Bytes of device workspace mdn_chunk_fwd needs for this problem under the
+ * current mdn_set_fwd_path setting.  When dt = MDN_BF16 selects the
+ * column tiles, the forward keeps the chunk-local matrices T and A on chip
  * and needs only per-chunk coefficient tables (6656 bytes per chunk of 64
  * tokens and head: the gates, the block products and boundary values of
  * the slides' Gamma of Eqs. (7)-(9), the lower triangles of its 16 x 16
- * diagonal blocks and the six coefficient rows the scan reads).  With MDN_F32 it runs as the two
- * phases below and needs what mdn_chunk_fwd_split_workspace_bytes returns.
- * Returns 0 for unsupported or invalid sizes and when no work is needed
- * (B, T or H is 0).
+ * diagonal blocks and the six coefficient rows the scan reads).  With
+ * MDN_F32, and with the row split, it runs as the two phases below and
+ * needs what mdn_chunk_fwd_split_workspace_bytes returns (the larger; it
+ * is returned whenever the row split may run, so it also covers a call
+ * that asks for Vt).  Returns 0 for unsupported or invalid sizes and when
+ * no work is needed (B, T or H is 0).
  */
 size_t mdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
                                      mdn_dtype dt);
@@ -131,16 +174,21 @@ mdn_status mdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  Same arguments, rules and results as
  * mdn_chunk_fwd (the same kernels run, so the outputs are bitwise those of
- * mdn_chunk_fwd); the workspace is instead a file-scope device array of
+ * mdn_chunk_fwd, except in the row-split case below); the workspace is
+ * instead a file-scope device array of
  * MDN_NOALLOC_SCRATCH_BYTES (64 MiB) in the library, one per GPU, loaded with
  * the library's code on that GPU and held until the process ends.  Its
  * address is looked up once per GPU on the first call there.  The call
  * allocates nothing (no hipMalloc, hipFree or allocating library routine).
  * Limits and errors:
- *   - a problem whose mdn_chunk_fwd_workspace_bytes(...) exceeds
+ *   - when mdn_set_fwd_path selects the row split (see mdn_fwd_path) but its
+ *     workspace (18,432 bytes per chunk of 64 tokens and head) exceeds the
+ *     array, the column tiles run instead;
+ *   - a problem whose workspace for the path it runs exceeds
  *     MDN_NOALLOC_SCRATCH_BYTES returns MDN_ERR_WORKSPACE before anything is
- *     enqueued (bf16: 6,656 bytes per chunk of 64 tokens and head, so up to
- *     10,082 chunks, e.g. B8 H16 T4096; fp32: the two-phase workspace);
+ *     enqueued (bf16 column tiles: 6,656 bytes per chunk of 64 tokens and
+ *     head, so up to 10,082 chunks, e.g. B8 H16 T4096; fp32: the two-phase
+ *     workspace);
  *   - MDN_ERR_HIP if the array's address cannot be looked up.
  * Every call on one GPU shares that GPU's array, and a call leaves its
  * contents behind: calls that overlap in time on one GPU (on different

@@ -52,13 +52,28 @@ def test_workspace_bytes(lib):
     assert split(8, 4096, 16, 128, 128, 64, mdn.MDN_BF16) == 8 * 16 * 64 * per_bf16
     assert split(1, 65, 2, 64, 64, 64, mdn.MDN_F32) == 2 * 2 * per_f32     # ragged: 2 chunks
     assert split(1, 1, 1, 64, 128, 64, mdn.MDN_BF16) == per_bf16
-    # the bf16 forward keeps T and A on chip and needs only per-chunk coefficient
-    # tables (gates, block products, boundary values, Gamma's diagonal blocks
-    # packed to their lower triangles, six coefficient rows: 1664 floats); fp32
-    # uses the split path
-    assert ws(8, 4096, 16, 128, 128, 64, mdn.MDN_BF16) == 8 * 16 * 64 * 1664 * 4
-    assert ws(1, 65, 2, 64, 64, 64, mdn.MDN_BF16) == 2 * 2 * 1664 * 4
+    # the bf16 column tiles keep T and A on chip and need only per-chunk
+    # coefficient tables (gates, block products, boundary values, Gamma's
+    # diagonal blocks packed to their lower triangles, six coefficient rows:
+    # 1664 floats); fp32 and the bf16 row split use the split workspace.  Under
+    # MDN_FWD_AUTO the row split runs up to 32 tiles of 64 value columns.
+    per_fused = 1664 * 4
+    assert ws(8, 4096, 16, 128, 128, 64, mdn.MDN_BF16) == 8 * 16 * 64 * per_fused   # 256 tiles
+    assert ws(1, 64, 33, 128, 64, 64, mdn.MDN_BF16) == 33 * per_fused                # 33 tiles
+    assert ws(2, 64, 8, 128, 128, 64, mdn.MDN_BF16) == 16 * per_bf16                 # 32 tiles
+    assert ws(1, 65, 2, 64, 64, 64, mdn.MDN_BF16) == 2 * 2 * per_bf16
     assert ws(1, 65, 2, 64, 64, 64, mdn.MDN_F32) == 2 * 2 * per_f32
+    prev = lib.mdn_set_fwd_path(mdn.FWD_PATHS["column_tiles"])
+    try:
+        assert prev == mdn.FWD_PATHS["auto"]
+        assert ws(1, 65, 2, 64, 64, 64, mdn.MDN_BF16) == 2 * 2 * per_fused
+        assert ws(1, 65, 2, 64, 64, 64, mdn.MDN_F32) == 2 * 2 * per_f32
+        assert lib.mdn_set_fwd_path(mdn.FWD_PATHS["row_split"]) == mdn.FWD_PATHS["column_tiles"]
+        assert ws(8, 4096, 16, 128, 128, 64, mdn.MDN_BF16) == 8 * 16 * 64 * per_bf16
+        assert lib.mdn_set_fwd_path(5) == -1          # unknown: nothing changes
+        assert ws(8, 4096, 16, 128, 128, 64, mdn.MDN_BF16) == 8 * 16 * 64 * per_bf16
+    finally:
+        lib.mdn_set_fwd_path(prev)
     for bad in [(0, 64, 1, 64, 64, 64, 1), (1, 0, 1, 64, 64, 64, 1), (1, 64, 1, 96, 64, 64, 1),
                 (1, 64, 1, 64, 64, 32, 1), (1, 64, 1, 64, 64, 64, 7), (-1, 64, 1, 64, 64, 64, 1)]:
         assert ws(*bad) == 0

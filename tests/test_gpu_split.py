@@ -1,15 +1,28 @@
 """GPU parity of the split entry points (mdn_chunk_fwd_prepare followed by
 mdn_chunk_fwd_scan, through the C ABI) against the fp64 oracle.  For bf16
-inputs these run a different pair of kernels from mdn_chunk_fwd's fused one,
-so they get their own cases; tolerances are in parity.py."""
+inputs the scan runs under either partition of the state (mdn_set_fwd_path):
+the column-tiled scan, which mdn_chunk_fwd never runs (it fuses the column
+tiles into one kernel), or the row-split scan; tolerances are in parity.py."""
 import dataclasses
 
 import pytest
 
 import synthetic_inputs as si
+from chunkwise_delta_rule_amd import mdn
 from parity import assert_close, gpu_forward, oracle_forward, split_forward
 
 pytestmark = pytest.mark.gpu
+
+PATHS = ("column_tiles", "row_split")
+
+
+@pytest.fixture(autouse=True)
+def _forward_path(request):
+    """A test parametrized over `path` runs under that partition."""
+    spec = getattr(request.node, "callspec", None)
+    path = spec.params.get("path", "auto") if spec is not None else "auto"
+    with mdn.fwd_path(path):
+        yield
 
 
 def check(io, got, ref, tag):
@@ -18,27 +31,37 @@ def check(io, got, ref, tag):
         assert_close(x, r, io, name)
 
 
-CASES = [(io, dk, dv, T) for io in ("bf16", "f32") for (dk, dv) in ((64, 128), (128, 128))
-         for T in (1, 65, 200)]
+CASES = [(io, dk, dv, T, p) for io in ("bf16", "f32")
+         for p in (PATHS if io == "bf16" else ("auto",))
+         for (dk, dv) in ((64, 128), (128, 128)) for T in (1, 65, 200)]
 
 
-@pytest.mark.parametrize("io,dk,dv,T", CASES, ids=[f"{a}-dk{b}-dv{c}-T{d}" for a, b, c, d in CASES])
-def test_split_small_shapes(io, dk, dv, T):
+@pytest.mark.parametrize("io,dk,dv,T,path", CASES,
+                         ids=[f"{a}-dk{b}-dv{c}-T{d}-{e}" for a, b, c, d, e in CASES])
+def test_split_small_shapes(io, dk, dv, T, path):
     cfg = dataclasses.replace(si.CONFIGS[1], B=2, T=T, H=3, Dk=dk, Dv=dv, io_dtype=io,
                               init_state_std=0.3, seed=2000 + T + dk + 2 * dv)
     inp = si.make_forward(cfg)
     check(io, split_forward(inp), oracle_forward(inp), f"split {io} dk{dk} dv{dv} T{T}")
 
 
-def test_split_400m_like_layer():
+@pytest.mark.parametrize("path", PATHS)
+def test_split_400m_like_layer(path):
     inp = si.make_forward(si.CONFIGS[1])
     check("bf16", split_forward(inp), oracle_forward(inp), "split B4H8T2048d128")
 
 
 def test_split_and_fused_agree():
-    """Both bf16 paths evaluate the same chunk equations: their difference is
-    rounding, bounded by the parity tolerance of each against the oracle."""
+    """The bf16 kernels evaluate the same chunk equations: the column-tiled
+    scan, the fused kernel and the row-split scan differ by rounding, bounded
+    by the parity tolerance of each against the oracle.  The row-split scan
+    is the same kernel under both entry points, so those agree bitwise."""
     inp = si.make_forward(si.CONFIGS[1], B=2, T=700, H=4, init_state_std=0.3, seed=91)
-    a, b = split_forward(inp), gpu_forward(inp)
-    for x, y, name in zip(a, b, ("O", "S_T", "M_T")):
-        assert_close(x, y, "bf16", f"split vs fused {name}")
+    with mdn.fwd_path("column_tiles"):
+        a, b = split_forward(inp), gpu_forward(inp)
+    with mdn.fwd_path("row_split"):
+        c, d = split_forward(inp), gpu_forward(inp)
+    for x, y, z, u, name in zip(a, b, c, d, ("O", "S_T", "M_T")):
+        assert_close(x, y, "bf16", f"column split vs fused {name}")
+        assert_close(z, y, "bf16", f"row split vs fused {name}")
+        assert (z == u).all(), f"row split: phases vs mdn_chunk_fwd {name}"

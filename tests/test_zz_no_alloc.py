@@ -1,10 +1,12 @@
 """mdn_chunk_fwd_noalloc, the forward on the library's own per-device
 scratch array (no workspace argument, no allocation), against mdn_chunk_fwd
 on the same inputs: two calls in a row, the second smaller (the array keeps
-the first call's contents), in bf16 (the fused path's coefficient tables)
-and fp32 (the two-phase path's T and A), each also against the oracle at the
-parity tolerances; the headline size near the array's limit; and a problem
-over the limit, which is refused before anything runs."""
+the first call's contents), in bf16 under both partitions of the state (the
+fused kernel's coefficient tables; the prepare kernel's T and A for the
+row-split scan) and fp32 (the two-phase path's T and A), each also against
+the oracle at the parity tolerances; the headline size near the array's
+limit; a row split whose workspace does not fit, which runs the column tiles;
+and a problem over the limit, which is refused before anything runs."""
 import dataclasses
 
 import numpy as np
@@ -25,8 +27,9 @@ def dev_args(inp, io):
             to_dev(inp["M0"]))
 
 
-@pytest.mark.parametrize("io", ["bf16", "f32"])
-def test_noalloc_matches_chunk_fwd_twice(io):
+@pytest.mark.parametrize("io,path", [("bf16", "column_tiles"), ("bf16", "row_split"),
+                                     ("f32", "auto")])
+def test_noalloc_matches_chunk_fwd_twice(io, path):
     shapes = [dict(B=2, T=700, H=4), dict(B=1, T=130, H=2)]      # the second call smaller
     for n, shp in enumerate(shapes):
         cfg = dataclasses.replace(si.CONFIGS[1], io_dtype=io, Dk=64 if io == "f32" else 128,
@@ -34,9 +37,10 @@ def test_noalloc_matches_chunk_fwd_twice(io):
                                   seed=7100 + n, **shp)
         inp = si.make_forward(cfg)
         args = dev_args(inp, io)
-        print(f"noalloc {io} call {n}: B{cfg.B} T{cfg.T} H{cfg.H} d{cfg.Dk}", flush=True)
-        ref = mdn.chunk_fwd(*args, beta=None)
-        got = mdn.chunk_fwd(*args, noalloc=True)
+        print(f"noalloc {io} {path} call {n}: B{cfg.B} T{cfg.T} H{cfg.H} d{cfg.Dk}", flush=True)
+        with mdn.fwd_path(path):
+            ref = mdn.chunk_fwd(*args, beta=None)
+            got = mdn.chunk_fwd(*args, noalloc=True)
         torch.cuda.synchronize()
         for x, y, name in zip(got, ref, ("O", "S_T", "M_T")):
             assert torch.equal(x, y), f"{name}: noalloc differs from mdn_chunk_fwd"
@@ -63,6 +67,27 @@ def test_noalloc_headline_size():
     args = dev_args(inp, "bf16")
     got = mdn.chunk_fwd(*args, noalloc=True)
     ref = mdn.chunk_fwd(*args)
+    torch.cuda.synchronize()
+    for x, y, name in zip(got, ref, ("O", "S_T", "M_T")):
+        assert torch.equal(x, y), name
+
+
+def test_noalloc_row_split_too_large_runs_column_tiles():
+    """B1 H16 T16384 d128 under the row split: its workspace (75.5 MB) exceeds
+    the 64 MiB array, so the no-alloc call runs the column tiles (27.3 MB of
+    tables) and equals mdn_chunk_fwd under the column tiles bitwise."""
+    cfg = si.CONFIGS[3]
+    lib = mdn.load_library()
+    assert lib.mdn_chunk_fwd_split_workspace_bytes(cfg.B, cfg.T, cfg.H, 128, 128, 64,
+                                                   mdn.MDN_BF16) > mdn.NOALLOC_SCRATCH_BYTES
+    inp = si.make_forward(cfg)
+    args = dev_args(inp, "bf16")
+    del inp
+    print("noalloc row split over the array: B1 H16 T16384", flush=True)
+    with mdn.fwd_path("row_split"):
+        got = mdn.chunk_fwd(*args, noalloc=True)
+    with mdn.fwd_path("column_tiles"):
+        ref = mdn.chunk_fwd(*args)
     torch.cuda.synchronize()
     for x, y, name in zip(got, ref, ("O", "S_T", "M_T")):
         assert torch.equal(x, y), name
