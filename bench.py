@@ -29,7 +29,9 @@ The same JSON line carries:
   timing_ab     the headline call timed one call at a time: median of 20 back to
                 back, and median of 20 with a 1 GiB write between calls;
   other_configs the 400M-like layer (B4 H8 T2048) and the 16K-context layer
-                (B1 H16 T16384) as drawn and with no mu, each with its roofline;
+                (B1 H16 T16384) as drawn and with no mu, each under both partitions
+                of the state (column tiles, row split) with its roofline, and the
+                one the default rule runs;
   sweep         tokens/s at T x B = 16384 tokens per call for T = 2K .. 16K;
   measured_peaks  a dense bf16 MFMA loop and a 2 GiB streaming copy on this GPU,
                 beside the datasheet peaks;
@@ -621,33 +623,49 @@ def bench_flush_ab(args, torch, plan):
 def bench_configs(args, torch, si, mdn):
     """The other forward configurations at their own sizes: the 400M-like
     layer (B4 H8 T2048) and the 16K-context layer (B1 H16 T16384) as drawn
-    and with no mu (the gated delta rule on the same inputs)."""
+    and with no mu (the gated delta rule on the same inputs).  Each is timed
+    under both partitions of the state; `us_per_step` is the one the default
+    rule picks (the row split up to 32 tiles of 64 value columns)."""
     bf, f32 = torch.bfloat16, torch.float32
     out = {}
     for key, cfg, mu_null in (("config1", si.CONFIGS[1], False),
                               ("config3_runA", si.CONFIGS[3], False),
                               ("config3_runB_no_mu", si.CONFIGS[3], True)):
         inp = si.make_forward(cfg)
-        plan = mdn.ChunkPlan(up(inp["q"], bf), up(inp["k"], bf), up(inp["v"], bf),
-                             up(inp["alpha"], f32), None if mu_null else up(inp["mu"], f32),
-                             up(inp["eta"], f32))
+        args_dev = (up(inp["q"], bf), up(inp["k"], bf), up(inp["v"], bf), up(inp["alpha"], f32),
+                    None if mu_null else up(inp["mu"], f32), up(inp["eta"], f32))
         del inp
-        settle(torch, [plan.forward], args.settle)
-        for _ in range(args.warmup):
-            plan.forward()
-        (call_ms,), step_ms = time_calls(torch, [plan.forward], args.steps)
         toh = cfg.B * cfg.T * cfg.H
         heads = cfg.B * cfg.H
-        r = roofline_of(None, call_ms * 1e3, FLOP_FWD * toh,
-                        BYTES_FWD * toh + STATE_BYTES_HEAD * heads)
-        r["kernel"] = "chunk_fwd_fused_kernel" + ("<no mu>" if mu_null else "")
-        r["timed_with"] = "chunk_coef_kernel (same call)"
+        tiles = heads * (cfg.Dv // 64)
+        auto = "row_split" if tiles <= mdn.ROW_SPLIT_MAX_TILES else "column_tiles"
+        per_path = {}
+        for path in ("column_tiles", "row_split"):
+            with mdn.fwd_path(path):
+                plan = mdn.ChunkPlan(*args_dev)
+                settle(torch, [plan.forward], args.settle)
+                for _ in range(args.warmup):
+                    plan.forward()
+                (call_ms,), step_ms = time_calls(torch, [plan.forward], args.steps)
+                del plan
+            r = roofline_of(None, call_ms * 1e3, FLOP_FWD * toh,
+                            BYTES_FWD * toh + STATE_BYTES_HEAD * heads)
+            if path == "column_tiles":
+                r["kernel"] = "chunk_fwd_fused_kernel" + ("<no mu>" if mu_null else "")
+                r["timed_with"] = "chunk_coef_kernel (same call)"
+            else:
+                r["kernel"] = "chunk_scan_rs_kernel" + ("<no mu>" if mu_null else "")
+                r["timed_with"] = "chunk_prep_kernel (same call)"
+            per_path[path] = {"us_per_step": step_ms * 1e3,
+                              "tokens_per_s": cfg.B * cfg.T / (step_ms * 1e-3), "roofline": r}
+            log(f"{key} {path}: {step_ms * 1e3:.1f} us/step, "
+                f"{cfg.B * cfg.T / (step_ms * 1e-3):.3e} tokens/s")
         out[key] = {"workload": f"{cfg.name}{' with mu = 0 (no mu given)' if mu_null else ''}",
-                    "B": cfg.B, "T": cfg.T, "H": cfg.H, "us_per_step": step_ms * 1e3,
-                    "tokens_per_s": cfg.B * cfg.T / (step_ms * 1e-3),
-                    "workgroups": heads * (cfg.Dv // 64), "roofline": r}
-        log(f"{key}: {step_ms * 1e3:.1f} us/step, {cfg.B * cfg.T / (step_ms * 1e-3):.3e} tokens/s")
-        del plan
+                    "B": cfg.B, "T": cfg.T, "H": cfg.H, "column_tiles": tiles,
+                    "default_path": auto, "us_per_step": per_path[auto]["us_per_step"],
+                    "tokens_per_s": per_path[auto]["tokens_per_s"],
+                    "roofline": per_path[auto]["roofline"], "paths": per_path}
+        del args_dev
     return out
 
 

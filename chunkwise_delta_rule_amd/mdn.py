@@ -22,6 +22,9 @@ MDN_F32 = 0
 MDN_BF16 = 1
 # mdn_fwd_path: how the bf16 forward partitions the carried state
 FWD_PATHS = {"auto": 0, "column_tiles": 1, "row_split": 2}
+# MDN_FWD_AUTO runs the row split up to this many tiles of 64 value columns,
+# B * H * (Dv / 64) (the rule in api.hip; a CPU test checks the two agree)
+ROW_SPLIT_MAX_TILES = 32
 CHUNK = 64
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MDN_NOALLOC_SCRATCH_BYTES
 HEAD_DIMS = (64, 128)

@@ -57,6 +57,7 @@ def test_workspace_bytes(lib):
     # diagonal blocks packed to their lower triangles, six coefficient rows:
     # 1664 floats); fp32 and the bf16 row split use the split workspace.  Under
     # MDN_FWD_AUTO the row split runs up to 32 tiles of 64 value columns.
+    assert mdn.ROW_SPLIT_MAX_TILES == 32
     per_fused = 1664 * 4
     assert ws(8, 4096, 16, 128, 128, 64, mdn.MDN_BF16) == 8 * 16 * 64 * per_fused   # 256 tiles
     assert ws(1, 64, 33, 128, 64, 64, mdn.MDN_BF16) == 33 * per_fused                # 33 tiles
