@@ -222,6 +222,8 @@ def parse():
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-peaks", action="store_true")
     p.add_argument("--no-configs", action="store_true")
+    p.add_argument("--cpu-configs", action="store_true",
+                   help="also time the oracle on every config (about a minute of CPU)")
     return p.parse_args()
 
 
@@ -628,6 +630,22 @@ def bench_configs(args, torch, si, mdn):
     rule picks (the row split up to 32 tiles of 64 value columns)."""
     bf, f32 = torch.bfloat16, torch.float32
     out = {}
+    # the fp32 case (one path: prepare, then the fp32 scan)
+    cfg = si.CONFIGS[0]
+    inp = si.make_forward(cfg)
+    plan = mdn.ChunkPlan(up(inp["q"], f32), up(inp["k"], f32), up(inp["v"], f32),
+                         up(inp["alpha"], f32), up(inp["mu"], f32), up(inp["eta"], f32))
+    del inp
+    settle(torch, [plan.forward], args.settle)
+    for _ in range(args.warmup):
+        plan.forward()
+    (call_ms,), step_ms = time_calls(torch, [plan.forward], args.steps)
+    del plan
+    out["config0"] = {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "H": cfg.H,
+                      "us_per_step": step_ms * 1e3,
+                      "tokens_per_s": cfg.B * cfg.T / (step_ms * 1e-3),
+                      "kernels": "chunk_prep_kernel<float>, chunk_scan_kernel<float>"}
+    log(f"config0: {step_ms * 1e3:.1f} us/step")
     for key, cfg, mu_null in (("config1", si.CONFIGS[1], False),
                               ("config3_runA", si.CONFIGS[3], False),
                               ("config3_runB_no_mu", si.CONFIGS[3], True)):
@@ -700,6 +718,44 @@ def cpu_baseline(inp, cfg):
                       f"fp64 token recurrence, {passes} passes, {sec:.1f}s"}
 
 
+def cpu_configs(si):
+    """The oracle timed on each config (the CPU-baseline leg, --cpu-configs):
+    one whole pass of configs 0-3, and decode steps of config 4 until about
+    5 s have run."""
+    import oracle
+    lib = oracle.load()
+    cores = oracle.max_threads(lib)
+    out = {}
+    for i in range(4):
+        cfg = si.CONFIGS[i]
+        inp = si.make_forward(cfg)
+        t0 = time.perf_counter()
+        oracle.recurrence(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["mu"], inp["eta"],
+                          inp.get("beta"), inp["S0"], inp["M0"], lib=lib)
+        sec = time.perf_counter() - t0
+        out[f"config{i}"] = {"seconds": sec, "tokens_per_s": cfg.B * cfg.T / sec,
+                             "threads": cores, "sample": "one whole pass"}
+        log(f"oracle config{i}: {sec:.2f}s on {cores} threads")
+    cfg = si.CONFIGS[4]
+    stream = si.decode_stream(cfg)
+    S, M = next(stream)
+    S = S.astype("float64")
+    M = M.astype("float64")
+    steps, sec = 0, 0.0
+    while steps < cfg.steps and (steps == 0 or sec < 5.0):
+        t = next(stream)
+        t0 = time.perf_counter()
+        _, S, M = oracle.decode_step(t["q"], t["k"], t["v"], t["alpha"], t["mu"], t["eta"], S, M,
+                                     lib=lib)
+        sec += time.perf_counter() - t0
+        steps += 1
+    out["config4"] = {"seconds_per_step": sec / steps, "head_steps_per_s":
+                      steps * cfg.N * cfg.H / sec, "threads": cores,
+                      "sample": f"{steps} of the {cfg.steps} decode steps"}
+    log(f"oracle config4: {sec / steps:.3f}s per step on {cores} threads")
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -723,6 +779,8 @@ def main():
     configs = None if args.no_configs else bench_configs(args, torch, si, mdn)
     peaks = None if args.no_peaks else bench_peaks(args, torch)
     base = None if args.no_cpu_baseline else cpu_baseline(inp, cfg)
+    if base is not None and args.cpu_configs:
+        base["per_config"] = cpu_configs(si)
     tokens = cfg.B * cfg.T
     line = {
         "metric": METRIC,
