@@ -196,15 +196,10 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
     const int n = min(CH, T - t0);
     const size_t tok0 = ((size_t)b * T + t0) * H + h;   // (b, t0, h)
 
-    {
-        RowTile<E, DK> kt, qt;
-        kt.load(k + tok0 * DK, (unsigned)(H * DK), n, tid);
-        qt.load(q + tok0 * DK, (unsigned)(H * DK), n, tid);
-        kt.template store<LDK>(Ks, tid);
-        qt.template store<LDK>(Qs, tid);
-    }
     // gates of this chunk, one row per lane (rows >= n: alpha 1, mu 0, eta 0,
-    // beta 0); beta is 1 when no beta gate is given
+    // beta 0); beta is 1 when no beta gate is given.  K and Q are loaded next
+    // into registers and stored to LDS only after the coefficient pass, which
+    // needs the gates alone, so their latency overlaps it.
     float a_l = 1.f, m_l = 0.f, e_l = 0.f, s_l = 0.f;
     if (lane < n) {
         const size_t g = tok0 + (size_t)lane * H;
@@ -213,6 +208,9 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
         e_l = eta[g];
         s_l = beta ? beta[g] : 1.f;
     }
+    RowTile<E, DK> kt, qt;
+    kt.load(k + tok0 * DK, (unsigned)(H * DK), n, tid);
+    qt.load(q + tok0 * DK, (unsigned)(H * DK), n, tid);
     if (wave == 0) {
         al[lane] = a_l;
         mus[lane] = m_l;
@@ -221,51 +219,148 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
     }
     __syncthreads();
 
-    // ---- coefficients (wave 0): one pass over the chunk rows r.  Lane j
-    //      carries the Gamma column j (rows r >= j) and lane i the prefix
-    //      product abar_i.  The gates of row r are broadcast reads from LDS
-    //      and the pass is straight-line (rows >= n are masked, not branched
-    //      over), so the reads run ahead of the arithmetic.  Since
+    // ---- coefficients, Gamma by 16-row blocks: block w (rows r0 = 16 w ..
+    //      r0 + 15) on wavefront w, lane j carrying the Gamma column j.  For
+    //      r > j the column runs m_{r,j} = mu_r m_{r-1,j},
+    //      gamma_{r,j} = alpha_r gamma_{r-1,j} + beta_r m_{r,j} (gamma_jj = beta_j,
+    //      m_jj = 1).  Inside a block this is linear in the entry state
+    //      (gamma, m) at row r0 - 1, with the same coefficients for every
+    //      column j < r0: gamma_{r,j} = a_r gamma_in + b_r m_in, m_{r,j} = c_r m_in,
+    //      where c_r = prod_{u=r0..r} mu_u, a_r = prod alpha_u and
+    //      b_r = alpha_r b_{r-1} + beta_r c_r.  Phase 1: every wavefront forms its
+    //      (a_r, b_r, c_r) and the columns that start inside its block; phase
+    //      2: it carries the earlier columns' exit states through the blocks
+    //      between.  abar_i = prod_{u<=i} alpha_u is the product of the earlier
+    //      blocks' a and the lane's own a_i.  Since
     //      mubar_r = mu_0 prod_{u=1..r} mu_u, column 0 gives b_i = mu_0 gamma_{i,0}
-    //      and mubar_{n-1} = mu_0 m_{n-1,0}.  With a beta gate, gamma_jj = beta_j
-    //      and gamma_{r,j} = alpha_r gamma_{r-1,j} + beta_r m_{r,j}.
+    //      and mubar_{n-1} = mu_0 m_{n-1,0}.  Rows >= n carry neutral gates
+    //      and are written as zero.
+    //      Gamma's row padding (columns 64..67) holds per-column values
+    //      exchanged between the phases: a block's exit state (gamma, m) of
+    //      its own columns, abar and m_{n-1,j}.
     float* Vch = Vw + ch * NVEC * CH;
-    if (wave == 0) {
-        float g = 0.f, mj = 1.f, ab = 1.f;
-        // blocks of 16 rows: the block's gates arrive in four 16-byte reads
-        // and its rows are unrolled; rows >= n are masked inside a block
-        for (int r0 = 0; r0 < n; r0 += 16) {
-            float ga[16], gm[16], gs[16];
+    __shared__ float comp[4][4];                 // a, b, c of each block's last row
+    constexpr int XG = 64, XM = 65, XAB = 66, XMF = 67;
+    const int r0 = 16 * wave;
+    float pa[16], pb[16], pc[16], mloc[16];
+    float abr = 1.f;
+    {
+        float ga[16], gm[16], gs[16];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float4 a4 = *reinterpret_cast<const float4*>(al + r0 + 4 * u);
-                const float4 m4 = *reinterpret_cast<const float4*>(mus + r0 + 4 * u);
-                const float4 s4 = *reinterpret_cast<const float4*>(bts + r0 + 4 * u);
-                ga[4 * u + 0] = a4.x; ga[4 * u + 1] = a4.y; ga[4 * u + 2] = a4.z; ga[4 * u + 3] = a4.w;
-                gm[4 * u + 0] = m4.x; gm[4 * u + 1] = m4.y; gm[4 * u + 2] = m4.z; gm[4 * u + 3] = m4.w;
-                gs[4 * u + 0] = s4.x; gs[4 * u + 1] = s4.y; gs[4 * u + 2] = s4.z; gs[4 * u + 3] = s4.w;
+        for (int u = 0; u < 4; ++u) {
+            const float4 a4 = *reinterpret_cast<const float4*>(al + r0 + 4 * u);
+            const float4 m4 = *reinterpret_cast<const float4*>(mus + r0 + 4 * u);
+            const float4 s4 = *reinterpret_cast<const float4*>(bts + r0 + 4 * u);
+            ga[4 * u + 0] = a4.x; ga[4 * u + 1] = a4.y; ga[4 * u + 2] = a4.z; ga[4 * u + 3] = a4.w;
+            gm[4 * u + 0] = m4.x; gm[4 * u + 1] = m4.y; gm[4 * u + 2] = m4.z; gm[4 * u + 3] = m4.w;
+            gs[4 * u + 0] = s4.x; gs[4 * u + 1] = s4.y; gs[4 * u + 2] = s4.z; gs[4 * u + 3] = s4.w;
+        }
+        float ca = 1.f, cb = 0.f, cc = 1.f;      // the block's coefficients
+        float gl = 0.f, ml = 1.f;                // column `lane` if it starts in this block
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int r = r0 + u;
+            cc *= gm[u];
+            ca *= ga[u];
+            cb = ga[u] * cb + gs[u] * cc;
+            pa[u] = ca;
+            pb[u] = cb;
+            pc[u] = cc;
+            abr = r == lane ? ca : abr;
+            const bool below = r > lane;
+            const float ml_n = below ? ml * gm[u] : 1.f;
+            const float gl_n = below ? ga[u] * gl + gs[u] * ml_n : (r == lane ? gs[u] : 0.f);
+            ml = ml_n;
+            gl = gl_n;
+            mloc[u] = ml_n;
+            // columns j >= r0 are final here (zero above the diagonal)
+            if (lane >= r0) Gam[r * LDG + lane] = r < n ? gl_n : 0.f;
+        }
+        if (lane >= r0 && lane < r0 + 16) {
+            Gam[lane * LDG + XG] = gl;
+            Gam[lane * LDG + XM] = ml;
+        }
+        if (lane == 0) {
+            comp[wave][0] = ca;
+            comp[wave][1] = cb;
+            comp[wave][2] = cc;
+        }
+    }
+    __syncthreads();
+    {
+        // phase 2: columns j < r0 from the exit state of their own block,
+        // carried through the blocks between
+        float gi = 0.f, mi = 0.f;
+        if (lane < r0) {
+            const int kb = lane >> 4;
+            gi = Gam[lane * LDG + XG];
+            mi = Gam[lane * LDG + XM];
+#pragma unroll
+            for (int kx = 1; kx < 3; ++kx) {
+                if (kx > kb && kx < wave) {
+                    const float g2 = comp[kx][0] * gi + comp[kx][1] * mi;
+                    mi = comp[kx][2] * mi;
+                    gi = g2;
+                }
             }
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                Gam[(r0 + u) * LDG + lane] = r0 + u < n ? pa[u] * gi + pb[u] * mi : 0.f;
+        }
+        // abar of the rows of this block
+        float pre = 1.f;
+#pragma unroll
+        for (int kx = 0; kx < 3; ++kx)
+            if (kx < wave) pre *= comp[kx][0];
+        if (lane >= r0 && lane < r0 + 16) Gam[lane * LDG + XAB] = pre * abr;
+        // m_{n-1,j} from the block that holds row n - 1
+        if (wave == (n - 1) >> 4) {
+            const int un = (n - 1) & 15;
+            float pcu = 0.f, mlu = 0.f;
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
-                const int r = r0 + u;
-                const bool act = r < n;
-                const bool below = r > lane;
-                const float mj_n = below ? mj * gm[u] : 1.f;
-                const float g_n = below ? ga[u] * g + gs[u] * mj_n : (r == lane ? gs[u] : 0.f);
-                mj = act ? mj_n : mj;
-                g = act ? g_n : g;
-                ab = (act && r <= lane) ? ab * ga[u] : ab;
-                Gam[r * LDG + lane] = act ? g_n : 0.f;
+                pcu = u == un ? pc[u] : pcu;
+                mlu = u == un ? mloc[u] : mlu;
+            }
+            Gam[lane * LDG + XMF] = lane < r0 ? pcu * mi : mlu;
+        }
+    }
+
+    kt.template store<LDK>(Ks, tid);
+    qt.template store<LDK>(Qs, tid);
+    __syncthreads();
+
+    // ---- G = K K^T and P = Q K^T on the lower block triangle: wave w owns
+    //      row tile w.  The accumulators hold the transposed tiles: lane
+    //      (l16, lg) ends with row i = 16 w + l16, columns 16 ct + 4 lg .. + 3,
+    //      so every later access of a row is one 16-byte piece.
+    f32x4 accG[4], accP[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) accG[ct] = accP[ct] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < DK; ks += MM::KSTEP) {
+        const int kk = ks + MM::KW * lg;
+        const auto aK = MM::load(Ks + (16 * wave + l16) * LDK + kk);
+        const auto aQ = MM::load(Qs + (16 * wave + l16) * LDK + kk);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            if (ct <= wave) {
+                const auto bK = MM::load(Ks + (16 * ct + l16) * LDK + kk);
+                accG[ct] = MM::mma(bK, aK, accG[ct]);
+                accP[ct] = MM::mma(bK, aQ, accP[ct]);
             }
         }
-        for (int r = (n + 15) & ~15; r < CH; ++r) Gam[r * LDG + lane] = 0.f;
-        // lane i reads b_i = mu_0 gamma_{i,0} and b_{i-1} written by lane 0
-        // of this wavefront (LDS operations of one wavefront complete in order)
-        __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();   // Gamma ready; K and Q no longer read
+
+    if (wave == 0) {
         const float mu0 = mus[0];
         const bool live = lane < n;
         const float bi = live ? mu0 * Gam[lane * LDG] : 0.f;
         const float bprev = live && lane >= 1 ? mu0 * Gam[(lane - 1) * LDG] : 0.f;
+        const float ab = Gam[lane * LDG + XAB];
+        const float g = Gam[(n - 1) * LDG + lane];     // gamma_{n-1, lane}
+        const float mj = Gam[lane * LDG + XMF];        // m_{n-1, lane}
         Vch[V_ABAR * CH + lane] = live ? ab : 0.f;
         Vch[V_AB1 * CH + lane] = live ? a_l * bprev : 0.f;
         Vch[V_B * CH + lane] = bi;
@@ -282,46 +377,32 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
         Vch[V_SCAL * CH + lane] = scal;
     }
 
-    // ---- G = K K^T and P = Q K^T on the lower block triangle: wave w owns
-    //      row tile w
-    f32x4 accG[4], accP[4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) accG[ct] = accP[ct] = zero4();
-#pragma unroll
-    for (int ks = 0; ks < DK; ks += MM::KSTEP) {
-        const int kk = ks + MM::KW * lg;
-        const auto aK = MM::load(Ks + (16 * wave + l16) * LDK + kk);
-        const auto aQ = MM::load(Qs + (16 * wave + l16) * LDK + kk);
+    // ---- L = I + (P Khat^T) o Gamma^- into LDS (over K/Q, no longer read)
+    //      and A = (Q Khat^T) o Gamma straight to the workspace, 4 columns of
+    //      row i per lane
+    E* Ach = Aw + ch * CH * CH;
+    {
+        const int i = 16 * wave + l16;
+        const float ai = al[i];
+        const float* g0row = Gam + i * LDG;
+        const float* gmrow = Gam + max(i - 1, 0) * LDG;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-            if (ct <= wave) {
-                const auto bK = MM::load(Ks + (16 * ct + l16) * LDK + kk);
-                accG[ct] = MM::mma(aK, bK, accG[ct]);
-                accP[ct] = MM::mma(aQ, bK, accP[ct]);
-            }
-        }
-    }
-    __syncthreads();   // Gamma ready; K and Q no longer read
-
-    // ---- L = I + (P Khat^T) o Gamma^- into LDS (over K/Q, no longer read)
-    //      and A = (Q Khat^T) o Gamma straight to the workspace
-    E* Ach = Aw + ch * CH * CH;
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 16 * wave + 4 * lg + r;
-            const int j = 16 * ct + l16;
-            float lv = 0.f, av = 0.f;
+            const int j0 = 16 * ct + 4 * lg;
+            f32x4 lv = zero4(), av = zero4();
             if (ct <= wave) {   // wave-uniform; the per-lane masks are selects
-                const float gm1 = Gam[max(i - 1, 0) * LDG + j];
-                const float g0 = Gam[i * LDG + j];
-                const float ej = et[j];
-                lv = j < i ? al[i] * accG[ct][r] * ej * gm1 : (i == j ? 1.f : 0.f);
-                av = j <= i ? accP[ct][r] * ej * g0 : 0.f;
+                const f32x4 g0 = *reinterpret_cast<const f32x4*>(g0row + j0);
+                const f32x4 gm1 = *reinterpret_cast<const f32x4*>(gmrow + j0);
+                const f32x4 e4 = *reinterpret_cast<const f32x4*>(et + j0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = j0 + r;
+                    lv[r] = j < i ? ai * accG[ct][r] * e4[r] * gm1[r] : (i == j ? 1.f : 0.f);
+                    av[r] = j <= i ? accP[ct][r] * e4[r] * g0[r] : 0.f;
+                }
             }
-            Ls[i * LDG + j] = lv;
-            Ach[i * CH + j] = to_elem<E>(av);
+            *reinterpret_cast<f32x4*>(Ls + i * LDG + j0) = lv;
+            store4<E>(Ach + i * CH + j0, av[0], av[1], av[2], av[3]);
         }
     }
     __syncthreads();
