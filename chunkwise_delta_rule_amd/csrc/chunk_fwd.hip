@@ -724,9 +724,10 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(
 //  * Roles.  Eight wavefronts: 0..3 compute (wavefront w owns 16 of the 64
 //    value columns of S and M for the whole sequence), 4..7 stage.  While
 //    the compute wavefronts work on chunk c, the staging wavefronts bring
-//    chunk c + 1 into the other LDS buffer (direct global-to-LDS loads of K,
-//    Q, T, A and the coefficient vectors) and build its K^T and V^T there.
-//    One barrier per chunk hands the buffers over.
+//    chunk c + 1 into the other LDS buffer with direct global-to-LDS loads
+//    only (K, Q, V, T, A and the coefficient vectors, row-major); the
+//    compute wavefronts read K^T and V in the layouts they need with
+//    transposing LDS reads.  One barrier per chunk hands the buffers over.
 //  * Row order.  The accumulator slot (tile t, lane group g, element j) of
 //    the state (rows d) and of the chunk-row results (rows c) stands for
 //    physical row phys_row(16 t + 4 g + j): inside each block of 32 rows,
@@ -742,15 +743,14 @@ struct ScanBf16Layout {
     using LK = TileLayout<DK * 2>;          // K, Q rows
     using LC = TileLayout<CH * 2>;          // T, A rows and K^T rows
     static constexpr int TV = 64;           // value columns per workgroup
-    static constexpr int VT_LD = 2 * CH + 8;                     // bytes per V^T row
-    static constexpr int KT_BYTES = DK * CH * 2 + (DK / LC::G) * LC::PAD;
     static constexpr int OFF_Q = LK::BYTES;
     static constexpr int OFF_T = 2 * LK::BYTES;
     static constexpr int OFF_A = OFF_T + LC::BYTES;
-    static constexpr int OFF_KT = OFF_A + LC::BYTES;
-    static constexpr int OFF_VT = OFF_KT + KT_BYTES;
-    static constexpr int OFF_VEC = OFF_VT + TV * VT_LD;
+    static constexpr int OFF_V = OFF_A + LC::BYTES;   // 64 rows x 64 value columns
+    static constexpr int OFF_VEC = OFF_V + LC::BYTES;
     static constexpr int BUF_BYTES = OFF_VEC + 6 * CH * 4;
+    // byte distance between the rows 32 s + x and x of a K tile
+    static constexpr int KSTEP_ROWS = 32 * (DK * 2) + (32 / LK::G) * LK::PAD;
 };
 
 template <int DK, int DV>
@@ -793,55 +793,24 @@ __global__ __launch_bounds__(2 * NT) void chunk_scan_bf16_kernel(
         const unsigned kq_stride = (unsigned)(H * DK);
         const unsigned kq_lane = LK::lane_offset(kq_stride, lane);
         const unsigned c_lane = LC::lane_offset(CH, lane);
-        // K^T: this wavefront transposes the 16 K rows its own direct loads
-        // brought in (groups 4u + hw), in blocks of 4 rows x 8 columns
-        constexpr int QD = DK / 8;                  // 8-column blocks per row
-        const int blk = lane / QD;                  // 4-row block (< 4 when active)
-        const int qd = lane % QD;
-        const bool kt_lane = lane < 4 * QD;
-        const int i4 = LK::G * (4 * (blk / (LK::G / 4)) + hw) + 4 * (blk % (LK::G / 4));
-        // V^T: rows 16 hw + 4 (lane / 16) .. + 3, columns 4 (lane % 16) .. + 3
-        const int vr0 = 16 * hw + 4 * lg;
-        const int vc0 = 4 * l16;
+        const unsigned v_stride = (unsigned)(H * DV);
+        const unsigned v_lane = LC::lane_offset(v_stride, lane);
         auto stage = [&](int c, int bi) {
             const int n = min(CH, T - c * CH);
             const size_t tok0 = ((size_t)b * T + c * CH) * H + h;
             const size_t chn = (size_t)bh * NC + c;
             char* B = buf[bi];
-            bf16x4 vx[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const unsigned row = (unsigned)min(vr0 + r, n - 1);
-                vx[r] = *reinterpret_cast<const bf16x4*>(v + (tok0 + (size_t)row * H) * DV +
-                                                         tile * TV + vc0);
-            }
             LK::load(B, k + tok0 * DK, kq_stride, kq_lane, n, hw, lane);
             LK::load(B + L::OFF_Q, q + tok0 * DK, kq_stride, kq_lane, n, hw, lane);
             LC::load(B + L::OFF_T, Tw + chn * CH * CH, CH, c_lane, CH, hw, lane);
             LC::load(B + L::OFF_A, Aw + chn * CH * CH, CH, c_lane, CH, hw, lane);
+            // this tile's 64 value columns of V (rows >= n read row n - 1)
+            LC::load(B + L::OFF_V, v + tok0 * DV + tile * TV, v_stride, v_lane, n, hw, lane);
             // coefficient vectors: 6 x 64 floats = 96 pieces of 16 bytes
             if (hw == 0 || (hw == 1 && lane < 32))
                 direct_load16(Vw + chn * NVEC * CH + 4 * (64 * hw + lane),
                               B + L::OFF_VEC + 1024 * hw);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bf16x4 w4 = {vx[0][j], vx[1][j], vx[2][j], vx[3][j]};
-                *reinterpret_cast<bf16x4*>(B + L::OFF_VT + (vc0 + j) * L::VT_LD + 2 * vr0) = w4;
-            }
-            if (kt_lane) {
-                bf16x8 x[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    x[r] = *reinterpret_cast<const bf16x8*>(B + LK::chunk(i4 + r, qd));
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int d = 8 * qd + j;
-                    const bf16x4 w4 = {x[0][j], x[1][j], x[2][j], x[3][j]};
-                    *reinterpret_cast<bf16x4*>(B + L::OFF_KT + LC::chunk(d, i4 >> 3) +
-                                               2 * (i4 & 7)) = w4;
-                }
-            }
         };
         stage(0, 0);
         lds_barrier();
@@ -870,16 +839,32 @@ __global__ __launch_bounds__(2 * NT) void chunk_scan_bf16_kernel(
     if (M0) load_state(Ma, M0); else load_state(Ma, nullptr);
 
     // per-lane fragment row bases (bytes), the same every chunk
-    int kq_base[4], c_base[4], kt_base[RT], orow[4];
+    int kq_base[4], c_base[4], v_off[4], orow[4];
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
         const int r = phys_row(16 * x + l16);
         kq_base[x] = LK::chunk(r, lg);
         c_base[x] = LC::chunk(r, lg);
         orow[x] = r;
+        // V rows phys_row(16 x + 4 lg) + j, columns 16 w + 4 m .. + 3 (lane
+        // 4 j + m of its group): the transposing read hands lane l16 column
+        // 16 w + l16 of those four rows
+        const int c4 = 16 * wave + 4 * (l16 & 3);
+        v_off[x] = L::OFF_V + LC::chunk(phys_row(16 * x + 4 * lg) + (l16 >> 2), c4 >> 3) +
+                   2 * (c4 & 7);
     }
+    // K^T fragments of the update (tile rt, half hf, step s): lane 4 j + m of
+    // group lg reads K row 32 s + 8 lg + 4 hf + j, columns
+    // phys_row(16 rt + 4 m) .. + 3; the transposing read hands lane l16
+    // column phys_row(16 rt + l16) of those four rows.  Rows 32 s + x lie
+    // L::KSTEP_ROWS bytes after row x.
+    int kt_off[RT][2];
 #pragma unroll
-    for (int x = 0; x < RT; ++x) kt_base[x] = LC::chunk(phys_row(16 * x + l16), lg);
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+            kt_off[rt][hf] = LK::chunk(8 * lg + 4 * hf + (l16 >> 2), 4 * (rt >> 1) + (l16 & 3)) +
+                             8 * (rt & 1);
     const unsigned ostride = (unsigned)(H * DV);
     E* const Ocol = O + ((size_t)b * T * H + h) * DV + tile * TV + 16 * wave + 4 * lg;
 
@@ -891,8 +876,6 @@ __global__ __launch_bounds__(2 * NT) void chunk_scan_bf16_kernel(
         const char* Qb = Kb + L::OFF_Q;
         const char* Tb = Kb + L::OFF_T;
         const char* Ab = Kb + L::OFF_A;
-        const char* KTb = Kb + L::OFF_KT;
-        const char* VTb = Kb + L::OFF_VT + wl * L::VT_LD;
         const float* vec = reinterpret_cast<const float*>(Kb + L::OFF_VEC);
 
         // (1) X = K [S | M]: the critical path first (the state update below
@@ -926,7 +909,7 @@ __global__ __launch_bounds__(2 * NT) void chunk_scan_bf16_kernel(
                 const int p0 = phys_row(16 * ct + 4 * lg);
                 const f32x4 ab = *reinterpret_cast<const f32x4*>(vec + V_ABAR * CH + p0);
                 const f32x4 ab1 = *reinterpret_cast<const f32x4*>(vec + V_AB1 * CH + p0);
-                const bf16x4 vv = *reinterpret_cast<const bf16x4*>(VTb + 2 * p0);
+                const bf16x4 vv = lds_read_tr4(Kb + v_off[ct]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     R[ct][r] = static_cast<float>(vv[r]) - ab[r] * xs[ct][r] + ab1[r] * xm[ct][r];
@@ -1009,7 +992,9 @@ __global__ __launch_bounds__(2 * NT) void chunk_scan_bf16_kernel(
             const auto bM = MM::from_acc_scaled8(Vt, s, vec + V_WM * CH + 32 * s + 8 * lg, -1.f);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                const auto aK = *reinterpret_cast<const bf16x8*>(KTb + kt_base[rt] + 64 * s);
+                const bf16x4 lo = lds_read_tr4(Kb + kt_off[rt][0] + s * L::KSTEP_ROWS);
+                const bf16x4 hi = lds_read_tr4(Kb + kt_off[rt][1] + s * L::KSTEP_ROWS);
+                const bf16x8 aK = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 Sa[rt] = MM::mma(aK, bS, Sa[rt]);
                 Ma[rt] = MM::mma(aK, bM, Ma[rt]);
             }
