@@ -110,8 +110,8 @@ GATE_TAU = (2048 / 16) ** 0.5            # the temperature sqrt(d_in / h) at d_i
 FETCH_FACTOR = 262144.0 / 131093.9
 WRITE_FACTOR = 131072.0 / 131072.0
 CSRC = os.path.join(ROOT, "chunkwise_delta_rule_amd", "csrc")
-_SPLIT_SHA = "8af5c737255c1507ac8eae24ed24c172deed445ad75cc8377ea217c8d71e70d4"
-_BWD_SHA = "93f282aebf6fd02936360330f2d53bb5a333799e69af6c226b43b66162b69b80"
+_SPLIT_SHA = "49f2445a533ed29d6aa5a6d029dce3611ac8a5a7096e4b4afc5d35e31dd5ec11"
+_BWD_SHA = "bdb0a9188bd6acdb04783ba9b61e0042963ee0efc2861f53b51f51a0afd8a74a"
 _LIO_SHA = "627a8009335ec269a3313bb348dbbb8e2230dded01b1dfc19a85d20d78a2a663"
 TRAFFIC = {
     # chunk_coef_kernel (3,109.0 / 51,459.4) + chunk_fwd_fused_kernel (223,498.9 / 147,456.1):
@@ -121,25 +121,25 @@ TRAFFIC = {
                                    sha256="6974036122debe9ff2a7e566310281d9"
                                    "cf59d301d216a22c7c443e2b7b4b602e"),
     "chunk_scan_bf16_kernel": dict(sources=("chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
-                                   fetch_kib=268388.0, write_kib=147457.8, sha256=_SPLIT_SHA),
+                                   fetch_kib=268387.1, write_kib=147457.1, sha256=_SPLIT_SHA),
     "chunk_prep_kernel": dict(sources=("chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
-                              fetch_kib=134785.1, write_kib=144779.8, sha256=_SPLIT_SHA),
+                              fetch_kib=134382.4, write_kib=143696.3, sha256=_SPLIT_SHA),
     "decode_step_kernel": dict(sources=("decode.hip", "mfma.hpp"), fetch_kib=264109.0,
                                write_kib=525524.5, sha256="8fa39113008b99235e1abe57028f0d81"
                                "9b837f475aa87000a6b4e46e3ea6c4e5"),
     # one mdn_chunk_bwd call with the forward's saved residuals: chunk_prep_kernel
-    # (134,587.5 / 144,287.0) + bwd_scan_kernel (471,244.1 / 786,432.1) + bwd_rescan_kernel
-    # with saved residuals (208,989.8 / 524,289.7) + bwd_grad_bf16_kernel<..., true>
-    # (929,812.4 / 543,235.1)
+    # (134,382.4 / 143,696.3) + bwd_scan_kernel (471,244.0 / 786,432.1) + bwd_rescan_kernel
+    # with saved residuals (208,989.7 / 524,288.0) + bwd_grad_bf16_kernel<..., true>
+    # (929,528.7 / 543,329.9)
     "chunk_bwd": dict(sources=("chunk_bwd.hip", "chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
-                      fetch_kib=134587.5 + 471244.1 + 208989.8 + 929812.4,
-                      write_kib=144287.0 + 786432.1 + 524289.7 + 543235.1, sha256=_BWD_SHA),
-    # the same recomputing the residuals: bwd_rescan_kernel (274,556.8 / 786,432.7),
-    # bwd_grad_bf16_kernel<..., false> (994,874.7 / 543,403.2)
+                      fetch_kib=134382.4 + 471244.0 + 208989.7 + 929528.7,
+                      write_kib=143696.3 + 786432.1 + 524288.0 + 543329.9, sha256=_BWD_SHA),
+    # the same recomputing the residuals: bwd_rescan_kernel (274,556.8 / 786,432.1),
+    # bwd_grad_bf16_kernel<..., false> (994,481.4 / 543,327.6)
     "chunk_bwd_recompute": dict(sources=("chunk_bwd.hip", "chunk_fwd.hip", "chunk_common.hpp",
                                          "mfma.hpp"),
-                                fetch_kib=134587.5 + 471244.1 + 274556.8 + 994874.7,
-                                write_kib=144287.0 + 786432.1 + 786432.7 + 543403.2,
+                                fetch_kib=134382.4 + 471244.0 + 274556.8 + 994481.4,
+                                write_kib=143696.3 + 786432.1 + 786432.1 + 543327.6,
                                 sha256=_BWD_SHA),
     "qk_prologue_kernel": dict(sources=("layer_io.hip", "mfma.hpp"), fetch_kib=131099.8,
                                write_kib=262144.0, sha256=_LIO_SHA),
@@ -160,8 +160,8 @@ MFMA_BUSY = {
     "chunk_fwd_fused_kernel": dict(sources=TRAFFIC["chunk_fwd_fused_kernel"]["sources"],
                                    busy=0.385, sha256=TRAFFIC["chunk_fwd_fused_kernel"]["sha256"]),
     "chunk_scan_bf16_kernel": dict(sources=TRAFFIC["chunk_scan_bf16_kernel"]["sources"],
-                                   busy=0.255, sha256=_SPLIT_SHA),
-    "chunk_prep_kernel": dict(sources=TRAFFIC["chunk_prep_kernel"]["sources"], busy=0.081,
+                                   busy=0.287, sha256=_SPLIT_SHA),
+    "chunk_prep_kernel": dict(sources=TRAFFIC["chunk_prep_kernel"]["sources"], busy=0.100,
                               sha256=_SPLIT_SHA),
 }
 
