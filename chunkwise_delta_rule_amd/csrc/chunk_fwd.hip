@@ -425,32 +425,61 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
         for (int i = 0; i < 16; ++i) Ts[(base + i) * LDG + base + lane] = t[i];
     }
     __syncthreads();
-    // ... then block rows I = 1..3: T_IJ = -T_II X_IJ, X_IJ = sum_{K<I} L_IK T_KJ,
-    //      on fp32 MFMA, block column J = wave.  X stays in accumulators and is
-    //      the B operand of the second product in k-permuted order.  Only
-    //      blocks on or below the diagonal are ever read.
-    for (int I = 1; I < 4; ++I) {
-        const int J = wave;
-        if (J < I) {
-            f32x4 x0 = zero4(), x1 = zero4();
-            for (int kk = 16 * J; kk < 16 * I; kk += 2 * MF::KSTEP) {
-                x0 = MF::mma(Ls[(16 * I + l16) * LDG + kk + lg], Ts[(kk + lg) * LDG + 16 * J + l16], x0);
-                x1 = MF::mma(Ls[(16 * I + l16) * LDG + kk + 4 + lg],
-                             Ts[(kk + 4 + lg) * LDG + 16 * J + l16], x1);
-            }
-            const f32x4 x = x0 + x1;
-            f32x4 t = zero4();
+    // ... then the blocks below the diagonal, by halves: with
+    //      L = [[L1, 0], [L21, L2]] (32 x 32 blocks) and T1 = L1^-1, T2 = L2^-1,
+    //      T = [[T1, 0], [-T2 L21 T1, T2]], and the same once more inside T1 and
+    //      T2 (T_10 = -D_1 L_10 D_0, T_32 = -D_3 L_32 D_2).  Three dependent
+    //      steps of 16 x 16 products on fp32 MFMA, spread over the wavefronts:
+    //      (1) T_10 and T_32; (2) Y = L21 T1, one block per wavefront, kept in
+    //      L's upper right 32 x 32 (zero, never read); (3) -T2 Y, one block per
+    //      wavefront.  Only blocks on or below the diagonal of T are read.
+    //      acc += A_blk(I, KA) B_blk(KB, J) for row-major A, B in LDS (16 x 16
+    //      blocks; A's block column KA against B's block row KB):
+    auto blk_mma = [&](const float* Am, int I, int KA, const float* Bm, int KB, int J,
+                       f32x4 acc) {
+        f32x4 a1 = zero4();
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                // k = 4 lg + s: this lane's accumulator element s
-                const float a = Ts[(16 * I + l16) * LDG + 16 * I + 4 * lg + s];
-                t = MF::mma(a, -x[s], t);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Ts[(16 * I + 4 * lg + r) * LDG + 16 * J + l16] = t[r];
+        for (int kk = 0; kk < 16; kk += 2 * MF::KSTEP) {
+            acc = MF::mma(Am[(16 * I + l16) * LDG + 16 * KA + kk + lg],
+                          Bm[(16 * KB + kk + lg) * LDG + 16 * J + l16], acc);
+            a1 = MF::mma(Am[(16 * I + l16) * LDG + 16 * KA + kk + 4 + lg],
+                         Bm[(16 * KB + kk + 4 + lg) * LDG + 16 * J + l16], a1);
         }
-        __syncthreads();
+        return acc + a1;
+    };
+    // -D_I X with X in accumulators (the B operand in k-permuted order:
+    // step s covers k = 4 lg + s, this lane's element s)
+    auto neg_diag_times = [&](int I, const f32x4& x) {
+        f32x4 t = zero4();
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2)
+            t = MF::mma(Ts[(16 * I + l16) * LDG + 16 * I + 4 * lg + s2], -x[s2], t);
+        return t;
+    };
+    auto store_blk = [&](float* M, int I, int J, const f32x4& t) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) M[(16 * I + 4 * lg + r) * LDG + 16 * J + l16] = t[r];
+    };
+    if (wave < 2) {
+        const int I = 1 + 2 * wave, J = 2 * wave;              // (1, 0) or (3, 2)
+        store_blk(Ts, I, J, neg_diag_times(I, blk_mma(Ls, I, J, Ts, J, J, zero4())));
     }
+    __syncthreads();
+    float* const Ys = Ls + 32;                                 // Y_{I-2, J} at rows 16 (I-2), columns 32 + 16 J
+    {
+        const int I = 2 + (wave >> 1), J = wave & 1;
+        f32x4 y = blk_mma(Ls, I, 1, Ts, 1, J, zero4());        // L_{I,1} T1_{1,J}
+        if (J == 0) y = blk_mma(Ls, I, 0, Ts, 0, 0, y);        // + L_{I,0} D_0
+        store_blk(Ys, I - 2, J, y);
+    }
+    __syncthreads();
+    {
+        const int I = 2 + (wave >> 1), J = wave & 1;
+        f32x4 t = blk_mma(Ts, I, 2, Ys, 0, J, zero4());         // T2_{I,2} Y_{2,J}: D_2 or T_32
+        if (I == 3) t = blk_mma(Ts, 3, 3, Ys, 1, J, t);         // + D_3 Y_{3,J}
+        store_blk(Ts, I, J, -t);
+    }
+    __syncthreads();
 
     // ---- write T (zero above the block diagonal) in the I/O type
     E* Tch = Tw + ch * CH * CH;
