@@ -2202,6 +2202,655 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Reverse scan for bf16 I/O: the equations, column ownership and operand
+// treatment of bwd_scan_kernel, in the layout of the forward's bf16 scan.
+//  * Roles.  Eight wavefronts: 0..3 compute (wavefront w keeps columns
+//    16 w .. 16 w + 15 of the workgroup's 64 of dS and dM for the whole
+//    sequence), 4..7 stage chunk c - 1 with direct global-to-LDS loads (K, Q,
+//    T, A, the workgroup's dO columns and the coefficient rows, all
+//    row-major) while the compute wavefronts work on chunk c.  One barrier
+//    per chunk hands the buffers over.
+//  * Row order.  The state rows d and the chunk rows i of every accumulator
+//    are in the forward scan's phys_row order, so a k-step fed from
+//    accumulator tiles 2 s and 2 s + 1 covers the 8 contiguous rows
+//    32 s + 8 g .. + 7.  Every operand whose k runs over chunk rows (A^T,
+//    T^T, Q^T, K^T, and dO itself) is two transposing LDS reads of its
+//    row-major tile; K's fragments for K dS' are 16-byte row reads.
+//  * The exit-state gradients go to the workspace in bf16 as [d][v] rows:
+//    each 16 x 16 tile is transposed on the matrix cores (a product with the
+//    identity, exact on bf16 values) and lane groups g, g ^ 1 swap halves, so
+//    that a lane stores 8 adjacent columns of one row.
+//  * Workgroups are remapped so that the column tiles of a head run on one
+//    XCD and read q, k, T and A through its L2 once.
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+struct BwdScanBf16Layout {
+    using LK = TileLayout<DK * 2>;   // K, Q rows
+    using LC = TileLayout<CH * 2>;   // T, A rows and the 64 dO columns
+    static constexpr int TV = 64;    // value columns per workgroup
+    static constexpr int OFF_Q = LK::BYTES;
+    static constexpr int OFF_T = 2 * LK::BYTES;
+    static constexpr int OFF_A = OFF_T + LC::BYTES;
+    static constexpr int OFF_G = OFF_A + LC::BYTES;
+    static constexpr int OFF_VEC = OFF_G + LC::BYTES;
+    static constexpr int BUF_BYTES = OFF_VEC + 6 * CH * 4;
+    // bytes from row x to row 32 s + x (s = 1), and from row x to row x + 4
+    // for the rows 8 g + (0..3) the transposing reads start at
+    static constexpr int KSTEP = 32 * (DK * 2) + (32 / LK::G) * LK::PAD;
+    static constexpr int CSTEP = 32 * (CH * 2) + (32 / LC::G) * LC::PAD;
+    static constexpr int KHALF = 4 * (DK * 2) + (LK::G == 4 ? LK::PAD : 0);
+    static constexpr int CHALF = 4 * (CH * 2) + (LC::G == 4 ? LC::PAD : 0);
+};
+
+__device__ __forceinline__ bf16x4 bwd_to_bf4(const f32x4& x)
+{
+    typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+    return __builtin_bit_cast(bf16x4, u32x2_t{bwd_pack_bf16(x[0], x[1]), bwd_pack_bf16(x[2], x[3])});
+}
+// x as a bf16 head and a bf16 remainder (x - head), both rounded to nearest
+__device__ __forceinline__ void bwd_split8(const float* x, bf16x8& hd, bf16x8& rs)
+{
+    typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+    u32x4_t h, r;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        h[u] = bwd_pack_bf16(x[2 * u], x[2 * u + 1]);
+        const float h0 = __uint_as_float(h[u] << 16);
+        const float h1 = __uint_as_float(h[u] & 0xffff0000u);
+        r[u] = bwd_pack_bf16(x[2 * u] - h0, x[2 * u + 1] - h1);
+    }
+    hd = __builtin_bit_cast(bf16x8, h);
+    rs = __builtin_bit_cast(bf16x8, r);
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(NT8) void bwd_scan_bf16_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ dO,
+    const __bf16* __restrict__ Tw, const __bf16* __restrict__ Aw, const float* __restrict__ Vw,
+    const float* dST, const float* dMT, __bf16* __restrict__ Hd, float* __restrict__ dv,
+    float* dS0, float* dM0, int T, int H, int NC, int xcd_groups)
+{
+    using MB = Mma<__bf16>;
+    using L = BwdScanBf16Layout<DK, DV>;
+    using LK = typename L::LK;
+    using LC = typename L::LC;
+    typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+    typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+    constexpr int TV = L::TV;
+    constexpr int NTILE = DV / TV;
+    constexpr int RT = DK / 16;   // state row tiles
+    constexpr int SK = DK / 32;   // k-steps over d
+    constexpr int SC = CH / 32;   // k-steps over the chunk rows
+    static_assert(DV % TV == 0 && RT % 2 == 0, "tiles");
+
+    __shared__ __align__(16) char buf[2][L::BUF_BYTES];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l16 = lane & 15;
+    const int lg = lane >> 4;
+
+    unsigned bid = blockIdx.x;
+    if (xcd_groups > 0) bid = (bid % 8u) * (unsigned)xcd_groups + bid / 8u;
+    const int tile = (int)(bid % NTILE);
+    const int bh = (int)(bid / NTILE);
+    const int h = bh % H;
+    const int b = bh / H;
+
+    if (wave >= 4) {
+        // ---------------- staging wavefronts ----------------
+        const int hw = wave - 4;
+        const unsigned kq_stride = (unsigned)(H * DK);
+        const unsigned kq_lane = LK::lane_offset(kq_stride, lane);
+        const unsigned c_lane = LC::lane_offset(CH, lane);
+        const unsigned g_stride = (unsigned)(H * DV);
+        const unsigned g_lane = LC::lane_offset(g_stride, lane);
+        auto stage = [&](int c, int bi) {
+            const int n = min(CH, T - c * CH);
+            const size_t tok0 = ((size_t)b * T + c * CH) * H + h;
+            const size_t chn = (size_t)bh * NC + c;
+            char* B = buf[bi];
+            LK::load(B, k + tok0 * DK, kq_stride, kq_lane, n, hw, lane);
+            LK::load(B + L::OFF_Q, q + tok0 * DK, kq_stride, kq_lane, n, hw, lane);
+            LC::load(B + L::OFF_T, Tw + chn * CH * CH, CH, c_lane, CH, hw, lane);
+            LC::load(B + L::OFF_A, Aw + chn * CH * CH, CH, c_lane, CH, hw, lane);
+            // this tile's 64 columns of dO (rows >= n read row n - 1; A's and
+            // the coefficient rows' zero rows >= n keep them out of every sum)
+            LC::load(B + L::OFF_G, dO + tok0 * DV + tile * TV, g_stride, g_lane, n, hw, lane);
+            // coefficient vectors: 6 x 64 floats = 96 pieces of 16 bytes
+            if (hw == 0 || (hw == 1 && lane < 32))
+                direct_load16(Vw + chn * NVEC * CH + 4 * (64 * hw + lane),
+                              B + L::OFF_VEC + 1024 * hw);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        };
+        stage(NC - 1, (NC - 1) & 1);
+        lds_barrier();
+        for (int c = NC - 1; c >= 0; --c) {
+            if (c > 0) stage(c - 1, (c - 1) & 1);
+            lds_barrier();
+        }
+        return;
+    }
+
+    // ---------------- compute wavefronts ----------------
+    const int wcol = tile * TV + 16 * wave;   // first column of this wavefront in the head
+    const int col = wcol + l16;
+    // dS, dM: slot (rt, lg, r) is state row phys_row(16 rt + 4 lg + r)
+    f32x4 Sa[RT], Ma[RT];
+    const size_t sbase = (size_t)bh * DK * DV;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const size_t x = sbase + (size_t)phys_row(16 * rt + 4 * lg + r) * DV + col;
+            Sa[rt][r] = dST ? dST[x] : 0.f;
+            Ma[rt][r] = dMT ? dMT[x] : 0.f;
+        }
+
+    // per-lane LDS offsets (bytes), the same every chunk
+    //  kq_base[x]: K row phys_row(16 x + l16), 16-byte chunk lg (the A
+    //    fragments of K dS'; step s is 64 s bytes further)
+    //  ktr: transposing reads of K or Q -- lane 4 j + m of group lg reads row
+    //    8 lg + 4 hf + j (+ 32 s), columns phys_row(16 rt + 4 m) .. + 3, so
+    //    lane l16 gets column phys_row(16 rt + l16) of those rows: the A
+    //    fragment of K^T or Q^T for state tile rt (+ 64 (rt >> 1) + 8 (rt & 1)
+    //    bytes, + KHALF for hf = 1, + KSTEP per step)
+    //  ctr: the same over a 64-column tile (T, A), columns phys_row(16 x + 4 m)
+    //  g_off: dO rows 8 lg + 4 hf + j, columns 16 w + 4 m .. + 3 of the 64:
+    //    lane l16 gets column 16 w + l16, the B fragment of dO
+    int kq_base[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) kq_base[x] = LK::chunk(phys_row(16 * x + l16), lg);
+    const int ktr = LK::chunk(8 * lg + (l16 >> 2), l16 & 3);
+    const int ctr = LC::chunk(8 * lg + (l16 >> 2), l16 & 3);
+    const int c4 = 16 * wave + 4 * (l16 & 3);
+    const int g_off = L::OFF_G + LC::chunk(8 * lg + (l16 >> 2), c4 >> 3) + 2 * (c4 & 7);
+    auto kt_at = [&](const char* base, int rt, int s) {
+        const int o = ktr + 64 * (rt >> 1) + 8 * (rt & 1) + s * L::KSTEP;
+        return bwd_cat8(lds_read_tr4(base + o), lds_read_tr4(base + o + L::KHALF));
+    };
+    auto ct_at = [&](const char* base, int x, int s) {
+        const int o = ctr + 64 * (x >> 1) + 8 * (x & 1) + s * L::CSTEP;
+        return bwd_cat8(lds_read_tr4(base + o), lds_read_tr4(base + o + L::CHALF));
+    };
+    // the 16 x 16 identity as a B fragment of mma16: B[4 lg + j][l16] = (4 lg + j == l16)
+    bf16x4 eye;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) eye[j] = static_cast<__bf16>(4 * lg + j == l16 ? 1.f : 0.f);
+    const unsigned vstride = (unsigned)(H * DV);
+
+    // The exit-state gradients go to the workspace in bf16, [d][v] rows: each
+    // 16 x 16 tile is transposed by a product with the identity, after which
+    // lane (l16, g) holds row phys_row(16 rt + l16), columns 4 g .. + 3; lane
+    // groups g and g ^ 1 then swap halves of tiles 2 p and 2 p + 1
+    // (permlane16_swap exchanges group 1 of its first operand with group 0 of
+    // its second, and group 3 with group 2), so that each lane holds columns
+    // 8 (g >> 1) .. + 7 of row phys_row(16 (2 p + (g & 1)) + l16).
+    auto store_pair = [&](__bf16* hd, int p, const bf16x4& t0, const bf16x4& t1) {
+        u32x2_t ua = __builtin_bit_cast(u32x2_t, bwd_to_bf4(mma16(t0, eye, zero4())));
+        u32x2_t ub = __builtin_bit_cast(u32x2_t, bwd_to_bf4(mma16(t1, eye, zero4())));
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            const auto r = __builtin_amdgcn_permlane16_swap(ua[d], ub[d], false, false);
+            ua[d] = r[0];
+            ub[d] = r[1];
+        }
+        const int row = phys_row(16 * (2 * p + (lg & 1)) + l16);
+        *reinterpret_cast<u32x4_t*>(hd + row * DV) = u32x4_t{ua[0], ua[1], ub[0], ub[1]};
+    };
+
+    // chunk c's exit-state gradients dS', dM' (the current dS, dM), as the
+    // bf16 values K dS' and K dM' use, to the workspace
+    auto store_exit = [&](int c) {
+        __bf16* const hd = Hd + ((size_t)bh * NC + c) * 2 * DK * DV + wcol + 8 * (lg >> 1);
+#pragma unroll
+        for (int p = 0; p < RT / 2; ++p) {
+            store_pair(hd, p, bwd_to_bf4(Sa[2 * p]), bwd_to_bf4(Sa[2 * p + 1]));
+            store_pair(hd + (size_t)DK * DV, p, bwd_to_bf4(Ma[2 * p]), bwd_to_bf4(Ma[2 * p + 1]));
+        }
+    };
+
+    store_exit(NC - 1);
+    lds_barrier();   // chunk NC - 1 staged
+    for (int c = NC - 1; c >= 0; --c) {
+        const int t0 = c * CH;
+        const int n = min(CH, T - t0);
+        const char* Kb = buf[c & 1];
+        const char* Qb = Kb + L::OFF_Q;
+        const char* Tb = Kb + L::OFF_T;
+        const char* Ab = Kb + L::OFF_A;
+        const float* vec = reinterpret_cast<const float*>(Kb + L::OFF_VEC);
+
+        // K dS', K dM': rows phys_row(16 ct + 4 lg + r) of the chunk
+        f32x4 xs[4], xm[4];
+        auto k_ds = [&]() {
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) xs[ct] = xm[ct] = zero4();
+#pragma unroll
+            for (int s = 0; s < SK; ++s) {
+                const bf16x8 bS = bwd_cat8(bwd_to_bf4(Sa[2 * s]), bwd_to_bf4(Sa[2 * s + 1]));
+                const bf16x8 bM = bwd_cat8(bwd_to_bf4(Ma[2 * s]), bwd_to_bf4(Ma[2 * s + 1]));
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    const bf16x8 aK = *reinterpret_cast<const bf16x8*>(Kb + kq_base[ct] + 64 * s);
+                    xs[ct] = MB::mma(aK, bS, xs[ct]);
+                    xm[ct] = MB::mma(aK, bM, xm[ct]);
+                }
+            }
+        };
+        // the state gradients' own carry: dS <- abar_n dS', dM <- mubar_n dM' - b_n dS'
+        auto decay = [&]() {
+            const float abn = vec[V_SCAL * CH + 0];
+            const float bn = vec[V_SCAL * CH + 1];
+            const float mbn = vec[V_SCAL * CH + 2];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const f32x4 so = Sa[rt];
+                Sa[rt] = abn * so;
+                Ma[rt] = mbn * Ma[rt] - bn * so;
+            }
+        };
+        // dO fragments: rows 32 s + 8 lg + (0..7), column col
+        bf16x8 gf[SC];
+#pragma unroll
+        for (int s = 0; s < SC; ++s)
+            gf[s] = bwd_cat8(lds_read_tr4(Kb + g_off + s * L::CSTEP),
+                             lds_read_tr4(Kb + g_off + s * L::CSTEP + L::CHALF));
+        // dS += X^T Diag(su u) Y, dM += X^T Diag(sw w) Y over the chunk rows,
+        // for X = Q or K (transposing reads) and Y given by y(s, j) (rows
+        // 32 s + 8 lg + j); the scaled rows as head and remainder
+        auto carry = [&](const char* Xb, const float* u, float su, const float* w, float sw,
+                         auto y, int s0, int s1) {
+#pragma unroll
+            for (int s = s0; s < s1; ++s) {
+                float xs8[8], xm8[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float yv = y(s, j);
+                    xs8[j] = su * u[32 * s + 8 * lg + j] * yv;
+                    xm8[j] = sw * w[32 * s + 8 * lg + j] * yv;
+                }
+                bf16x8 sh, sr, mh, mr;
+                bwd_split8(xs8, sh, sr);
+                bwd_split8(xm8, mh, mr);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const bf16x8 aX = kt_at(Xb, rt, s);
+                    Sa[rt] = MB::mma(aX, sh, Sa[rt]);
+                    Sa[rt] = MB::mma(aX, sr, Sa[rt]);
+                    Ma[rt] = MB::mma(aX, mh, Ma[rt]);
+                    Ma[rt] = MB::mma(aX, mr, Ma[rt]);
+                }
+            }
+        };
+        // dVt = Diag(ws) K dS' - Diag(wm) K dM' + A^T dO, then dR = T^T dVt (dVt
+        // as head and remainder), written as dv
+        f32x4 dR[4], dVt[4];
+        auto dvt = [&]() {
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int p0 = phys_row(16 * it + 4 * lg);
+                const f32x4 ws = *reinterpret_cast<const f32x4*>(vec + V_WS * CH + p0);
+                const f32x4 wm = *reinterpret_cast<const f32x4*>(vec + V_WM * CH + p0);
+                dVt[it] = ws * xs[it] - wm * xm[it];
+            }
+#pragma unroll
+            for (int s = 0; s < SC; ++s)
+#pragma unroll
+                for (int it = 0; it < 4; ++it) dVt[it] = MB::mma(ct_at(Ab, it, s), gf[s], dVt[it]);
+        };
+        auto dr = [&]() {
+#pragma unroll
+            for (int it = 0; it < 4; ++it) dR[it] = zero4();
+#pragma unroll
+            for (int s = 0; s < SC; ++s) {
+                float x[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    x[j] = dVt[2 * s][j];
+                    x[4 + j] = dVt[2 * s + 1][j];
+                }
+                bf16x8 vh, vr;
+                bwd_split8(x, vh, vr);
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const bf16x8 aT = ct_at(Tb, it, s);
+                    dR[it] = MB::mma(aT, vh, dR[it]);
+                    dR[it] = MB::mma(aT, vr, dR[it]);
+                }
+            }
+            // a wave-uniform base and 32-bit lane offsets; no row tests in a
+            // full chunk
+            float* dvb = dv + (((size_t)b * T + t0) * H + h) * DV + wcol;
+            if (n == CH) {
+#pragma unroll
+                for (int it = 0; it < 4; ++it)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        dvb[(unsigned)phys_row(16 * it + 4 * lg + r) * vstride + (unsigned)l16] =
+                            dR[it][r];
+            } else {
+#pragma unroll
+                for (int it = 0; it < 4; ++it)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = phys_row(16 * it + 4 * lg + r);
+                        if (i < n) dvb[(unsigned)i * vstride + (unsigned)l16] = dR[it][r];
+                    }
+            }
+        };
+
+        // dS += Q^T Diag(abar) dO - K^T Diag(abar) dR,
+        // dM += -Q^T Diag(b) dO + K^T Diag(ab1) dR
+        auto carry_q = [&](int s0, int s1) {
+            carry(Qb, vec + V_ABAR * CH, 1.f, vec + V_B * CH, -1.f,
+                  [&](int s, int j) { return static_cast<float>(gf[s][j]); }, s0, s1);
+        };
+        auto carry_k = [&](int s0, int s1) {
+            carry(Kb, vec + V_ABAR * CH, -1.f, vec + V_AB1 * CH, 1.f,
+                  [&](int s, int j) { return j < 4 ? dR[2 * s][j] : dR[2 * s + 1][j - 4]; }, s0,
+                  s1);
+        };
+        k_ds();
+        decay();
+        carry_q(0, SC);
+        dvt();
+        dr();
+        carry_k(0, SC);
+        if (c > 0) store_exit(c - 1);
+        lds_barrier();   // this chunk's buffer is free and the previous chunk is staged
+    }
+
+    // (the lane's row group through an empty asm: addresses formed here, not
+    // kept in registers across the loop)
+    int lgx = lg;
+    asm volatile("" : "+v"(lgx));
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const size_t x = sbase + (size_t)phys_row(16 * rt + 4 * lgx + r) * DV + col;
+            if (dS0) dS0[x] = Sa[rt][r];
+            if (dM0) dM0[x] = Ma[rt][r];
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Forward re-scan for bf16 I/O: the equations and operand treatment of
+// bwd_rescan_kernel (S and M rounded to bf16 in K S, K M; R and the
+// weight-scaled rows of Vt split into a bf16 head and remainder), in the
+// layout of the reverse scan above: four compute wavefronts with 16 state
+// columns each, four staging wavefronts loading chunk c + 1 (K, the
+// workgroup's columns of v or of the saved Vt, T unless Vt was saved, the
+// coefficient rows) with direct global-to-LDS loads, one barrier per chunk.
+// Each chunk's entry state goes to the workspace in bf16, [d][v] rows, as
+// the reverse scan stores the exit-state gradients; without saved residuals
+// the chunk's Vt goes there too, in fp32.
+// ---------------------------------------------------------------------------
+template <int DK, int DV, bool SAVED>
+struct BwdRescanBf16Layout {
+    using LK = TileLayout<DK * 2>;   // K rows
+    using LC = TileLayout<CH * 2>;   // T rows and the 64 columns of v (or Vt)
+    static constexpr int TV = 64;
+    static constexpr int OFF_V = LK::BYTES;
+    static constexpr int OFF_T = OFF_V + LC::BYTES;
+    static constexpr int OFF_VEC = OFF_T + (SAVED ? 0 : LC::BYTES);
+    static constexpr int BUF_BYTES = OFF_VEC + 6 * CH * 4;
+    static constexpr int KSTEP = 32 * (DK * 2) + (32 / LK::G) * LK::PAD;
+    static constexpr int CSTEP = 32 * (CH * 2) + (32 / LC::G) * LC::PAD;
+    static constexpr int KHALF = 4 * (DK * 2) + (LK::G == 4 ? LK::PAD : 0);
+    static constexpr int CHALF = 4 * (CH * 2) + (LC::G == 4 ? LC::PAD : 0);
+};
+
+template <int DK, int DV, bool SAVED>
+__global__ __launch_bounds__(NT8) void bwd_rescan_bf16_kernel(
+    const __bf16* __restrict__ k, const __bf16* __restrict__ v, const __bf16* __restrict__ Tw,
+    const float* __restrict__ Vw, const float* S0, const float* M0, __bf16* __restrict__ Hs,
+    float* __restrict__ Vts, int T, int H, int NC, int xcd_groups)
+{
+    using MB = Mma<__bf16>;
+    using L = BwdRescanBf16Layout<DK, DV, SAVED>;
+    using LK = typename L::LK;
+    using LC = typename L::LC;
+    typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+    typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+    constexpr int TV = L::TV;
+    constexpr int NTILE = DV / TV;
+    constexpr int RT = DK / 16;   // state row tiles
+    constexpr int SK = DK / 32;   // k-steps over d
+    constexpr int SC = CH / 32;   // k-steps over the chunk rows
+    static_assert(DV % TV == 0 && RT % 2 == 0, "tiles");
+
+    __shared__ __align__(16) char buf[2][L::BUF_BYTES];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l16 = lane & 15;
+    const int lg = lane >> 4;
+
+    unsigned bid = blockIdx.x;
+    if (xcd_groups > 0) bid = (bid % 8u) * (unsigned)xcd_groups + bid / 8u;
+    const int tile = (int)(bid % NTILE);
+    const int bh = (int)(bid / NTILE);
+    const int h = bh % H;
+    const int b = bh / H;
+
+    if (wave >= 4) {
+        // ---------------- staging wavefronts ----------------
+        const int hw = wave - 4;
+        const unsigned k_stride = (unsigned)(H * DK);
+        const unsigned k_lane = LK::lane_offset(k_stride, lane);
+        const unsigned c_lane = LC::lane_offset(CH, lane);
+        const unsigned v_stride = (unsigned)(H * DV);
+        const unsigned v_lane = LC::lane_offset(v_stride, lane);
+        auto stage = [&](int c, int bi) {
+            const int n = min(CH, T - c * CH);
+            const size_t tok0 = ((size_t)b * T + c * CH) * H + h;
+            const size_t chn = (size_t)bh * NC + c;
+            char* B = buf[bi];
+            LK::load(B, k + tok0 * DK, k_stride, k_lane, n, hw, lane);
+            // rows >= n read row n - 1; their weights (and R's rows, through
+            // T's identity rows) keep them out of the update
+            LC::load(B + L::OFF_V, v + tok0 * DV + tile * TV, v_stride, v_lane, n, hw, lane);
+            if constexpr (!SAVED) LC::load(B + L::OFF_T, Tw + chn * CH * CH, CH, c_lane, CH, hw, lane);
+            if (hw == 0 || (hw == 1 && lane < 32))
+                direct_load16(Vw + chn * NVEC * CH + 4 * (64 * hw + lane),
+                              B + L::OFF_VEC + 1024 * hw);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        };
+        stage(0, 0);
+        lds_barrier();
+        for (int c = 0; c < NC; ++c) {
+            if (c + 1 < NC) stage(c + 1, (c + 1) & 1);
+            lds_barrier();
+        }
+        return;
+    }
+
+    // ---------------- compute wavefronts ----------------
+    const int wcol = tile * TV + 16 * wave;   // first column of this wavefront in the head
+    const int col = wcol + l16;
+    // S, M: slot (rt, lg, r) is state row phys_row(16 rt + 4 lg + r)
+    f32x4 Sa[RT], Ma[RT];
+    const size_t sbase = (size_t)bh * DK * DV;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const size_t x = sbase + (size_t)phys_row(16 * rt + 4 * lg + r) * DV + col;
+            Sa[rt][r] = S0 ? S0[x] : 0.f;
+            Ma[rt][r] = M0 ? M0[x] : 0.f;
+        }
+
+    // per-lane LDS offsets (bytes), as in the reverse scan:
+    //  kq_base[x]: K row phys_row(16 x + l16), 16-byte chunk lg (K S, K M)
+    //  c_base[x]: T row phys_row(16 x + l16), 16-byte chunk lg (T R)
+    //  ktr: transposing reads of K (the A fragments of K^T)
+    //  v_r[x]: v rows phys_row(16 x + 4 lg) + j, columns 16 w + 4 m .. + 3:
+    //    lane l16 gets column col of those four rows, R's layout
+    //  v_t: the same tile's rows 8 lg + 4 hf + j (+ 32 s): the B fragment of
+    //    a saved Vt
+    int kq_base[4], c_base[4], v_r[4];
+    const int c4 = 16 * wave + 4 * (l16 & 3);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        const int r = phys_row(16 * x + l16);
+        kq_base[x] = LK::chunk(r, lg);
+        c_base[x] = L::OFF_T + LC::chunk(r, lg);
+        v_r[x] = L::OFF_V + LC::chunk(phys_row(16 * x + 4 * lg) + (l16 >> 2), c4 >> 3) + 2 * (c4 & 7);
+    }
+    const int ktr = LK::chunk(8 * lg + (l16 >> 2), l16 & 3);
+    const int v_t = L::OFF_V + LC::chunk(8 * lg + (l16 >> 2), c4 >> 3) + 2 * (c4 & 7);
+    auto kt_at = [&](const char* base, int rt, int s) {
+        const int o = ktr + 64 * (rt >> 1) + 8 * (rt & 1) + s * L::KSTEP;
+        return bwd_cat8(lds_read_tr4(base + o), lds_read_tr4(base + o + L::KHALF));
+    };
+    bf16x4 eye;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) eye[j] = static_cast<__bf16>(4 * lg + j == l16 ? 1.f : 0.f);
+
+    // chunk c's entry state (the current S, M) to the workspace in bf16, [d][v]
+    // rows, transposed per 16 x 16 tile on the matrix cores as in the reverse scan
+    auto store_pair = [&](__bf16* hs, int p, const bf16x4& t0, const bf16x4& t1) {
+        u32x2_t ua = __builtin_bit_cast(u32x2_t, bwd_to_bf4(mma16(t0, eye, zero4())));
+        u32x2_t ub = __builtin_bit_cast(u32x2_t, bwd_to_bf4(mma16(t1, eye, zero4())));
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            const auto r = __builtin_amdgcn_permlane16_swap(ua[d], ub[d], false, false);
+            ua[d] = r[0];
+            ub[d] = r[1];
+        }
+        const int row = phys_row(16 * (2 * p + (lg & 1)) + l16);
+        *reinterpret_cast<u32x4_t*>(hs + row * DV) = u32x4_t{ua[0], ua[1], ub[0], ub[1]};
+    };
+    auto store_entry = [&](int c) {
+        __bf16* const hs = Hs + ((size_t)bh * NC + c) * 2 * DK * DV + wcol + 8 * (lg >> 1);
+#pragma unroll
+        for (int p = 0; p < RT / 2; ++p) {
+            store_pair(hs, p, bwd_to_bf4(Sa[2 * p]), bwd_to_bf4(Sa[2 * p + 1]));
+            store_pair(hs + (size_t)DK * DV, p, bwd_to_bf4(Ma[2 * p]), bwd_to_bf4(Ma[2 * p + 1]));
+        }
+    };
+
+    store_entry(0);
+    lds_barrier();   // chunk 0 staged
+    for (int c = 0; c < NC; ++c) {
+        const char* Kb = buf[c & 1];
+        const float* vec = reinterpret_cast<const float*>(Kb + L::OFF_VEC);
+
+        // Vt of this chunk: rows 32 s + 8 lg + (0..7) of column col as the
+        // update's B operands (weighted and split below)
+        f32x4 Vt[4];
+        if constexpr (!SAVED) {
+            // X = K [S | M], R = V - Diag(abar) K S + Diag(ab1) K M, Vt = T R (R
+            // as head and remainder); rows phys_row(16 x + 4 lg + r)
+            f32x4 xs[4], xm[4];
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) xs[ct] = xm[ct] = zero4();
+#pragma unroll
+            for (int s = 0; s < SK; ++s) {
+                const bf16x8 bS = bwd_cat8(bwd_to_bf4(Sa[2 * s]), bwd_to_bf4(Sa[2 * s + 1]));
+                const bf16x8 bM = bwd_cat8(bwd_to_bf4(Ma[2 * s]), bwd_to_bf4(Ma[2 * s + 1]));
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    const bf16x8 aK = *reinterpret_cast<const bf16x8*>(Kb + kq_base[ct] + 64 * s);
+                    xs[ct] = MB::mma(aK, bS, xs[ct]);
+                    xm[ct] = MB::mma(aK, bM, xm[ct]);
+                }
+            }
+            f32x4 R[4];
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                const int p0 = phys_row(16 * ct + 4 * lg);
+                const f32x4 ab = *reinterpret_cast<const f32x4*>(vec + V_ABAR * CH + p0);
+                const f32x4 ab1 = *reinterpret_cast<const f32x4*>(vec + V_AB1 * CH + p0);
+                const bf16x4 vv = lds_read_tr4(Kb + v_r[ct]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    R[ct][r] = static_cast<float>(vv[r]) - ab[r] * xs[ct][r] + ab1[r] * xm[ct][r];
+            }
+#pragma unroll
+            for (int it = 0; it < 4; ++it) Vt[it] = zero4();
+#pragma unroll
+            for (int s = 0; s < SC; ++s) {
+                float x[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    x[j] = R[2 * s][j];
+                    x[4 + j] = R[2 * s + 1][j];
+                }
+                bf16x8 rh, rr;
+                bwd_split8(x, rh, rr);
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const bf16x8 aT = *reinterpret_cast<const bf16x8*>(Kb + c_base[it] + 64 * s);
+                    Vt[it] = MB::mma(aT, rh, Vt[it]);
+                    Vt[it] = MB::mma(aT, rr, Vt[it]);
+                }
+            }
+            // to the workspace in fp32, [chunk row][v]
+            float* vb = Vts + ((size_t)bh * NC + c) * CH * DV + wcol;
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    vb[(unsigned)phys_row(16 * it + 4 * lg + r) * DV + (unsigned)l16] = Vt[it][r];
+        }
+
+        // S' = abar_n S - b_n M + K^T Diag(ws) Vt,  M' = mubar_n M - K^T Diag(wm) Vt
+        {
+            const float abn = vec[V_SCAL * CH + 0];
+            const float bn = vec[V_SCAL * CH + 1];
+            const float mbn = vec[V_SCAL * CH + 2];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                Sa[rt] = abn * Sa[rt] - bn * Ma[rt];
+                Ma[rt] = mbn * Ma[rt];
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < SC; ++s) {
+            float y[8];
+            if constexpr (SAVED) {
+                const bf16x8 g = bwd_cat8(lds_read_tr4(Kb + v_t + s * L::CSTEP),
+                                          lds_read_tr4(Kb + v_t + s * L::CSTEP + L::CHALF));
+#pragma unroll
+                for (int j = 0; j < 8; ++j) y[j] = static_cast<float>(g[j]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    y[j] = Vt[2 * s][j];
+                    y[4 + j] = Vt[2 * s + 1][j];
+                }
+            }
+            const float* ws = vec + V_WS * CH + 32 * s + 8 * lg;
+            const float* wm = vec + V_WM * CH + 32 * s + 8 * lg;
+            float xs8[8], xm8[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                xs8[j] = ws[j] * y[j];
+                xm8[j] = -(wm[j] * y[j]);
+            }
+            bf16x8 sh, sr, mh, mr;
+            bwd_split8(xs8, sh, sr);
+            bwd_split8(xm8, mh, mr);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const bf16x8 aK = kt_at(Kb, rt, s);
+                Sa[rt] = MB::mma(aK, sh, Sa[rt]);
+                Sa[rt] = MB::mma(aK, sr, Sa[rt]);
+                Ma[rt] = MB::mma(aK, mh, Ma[rt]);
+                Ma[rt] = MB::mma(aK, mr, Ma[rt]);
+            }
+        }
+        if (c + 1 < NC) store_entry(c + 1);
+        lds_barrier();   // this chunk's buffer is free and the next one is staged
+    }
+}
+
 }  // namespace
 }  // namespace mdn
 
@@ -2245,20 +2894,42 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
                                           sizeof(E) == 2, workspace, stream);
     if (err != hipSuccess) return err;
     const unsigned nblk = (unsigned)((size_t)B * H * (DV / 64));
-    hipLaunchKernelGGL((bwd_scan_kernel<E, DK, DV>), dim3(nblk), dim3(NT), 0, stream,
-                       static_cast<const E*>(q), static_cast<const E*>(k),
-                       static_cast<const E*>(dO), Tw, Aw, Vw, dST, dMT, Hd, dv, dS0, dM0, T, H,
-                       NC);
+    if constexpr (sizeof(E) == 2) {
+        // column tiles of a head on one XCD (consecutive ids after the remap)
+        const int xcd_groups = nblk % 8 == 0 ? (int)(nblk / 8) : 0;
+        hipLaunchKernelGGL((bwd_scan_bf16_kernel<DK, DV>), dim3(nblk), dim3(NT8), 0, stream,
+                           static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                           static_cast<const __bf16*>(dO), Tw, Aw, Vw, dST, dMT, Hd, dv, dS0,
+                           dM0, T, H, NC, xcd_groups);
+    } else {
+        hipLaunchKernelGGL((bwd_scan_kernel<E, DK, DV>), dim3(nblk), dim3(NT), 0, stream,
+                           static_cast<const E*>(q), static_cast<const E*>(k),
+                           static_cast<const E*>(dO), Tw, Aw, Vw, dST, dMT, Hd, dv, dS0, dM0, T,
+                           H, NC);
+    }
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    if (Vsaved)
+    if constexpr (sizeof(E) == 2) {
+        const int xcd_groups = nblk % 8 == 0 ? (int)(nblk / 8) : 0;
+        if (Vsaved)
+            hipLaunchKernelGGL((bwd_rescan_bf16_kernel<DK, DV, true>), dim3(nblk), dim3(NT8), 0,
+                               stream, static_cast<const __bf16*>(k),
+                               static_cast<const __bf16*>(Vsaved), Tw, Vw, S0, M0, Hs, Vts, T, H,
+                               NC, xcd_groups);
+        else
+            hipLaunchKernelGGL((bwd_rescan_bf16_kernel<DK, DV, false>), dim3(nblk), dim3(NT8), 0,
+                               stream, static_cast<const __bf16*>(k),
+                               static_cast<const __bf16*>(v), Tw, Vw, S0, M0, Hs, Vts, T, H, NC,
+                               xcd_groups);
+    } else if (Vsaved) {
         hipLaunchKernelGGL((bwd_rescan_kernel<E, DK, DV, true>), dim3(nblk), dim3(NT), 0, stream,
                            static_cast<const E*>(k), static_cast<const E*>(Vsaved), Tw, Vw, S0,
                            M0, Hs, Vts, T, H, NC);
-    else
+    } else {
         hipLaunchKernelGGL((bwd_rescan_kernel<E, DK, DV, false>), dim3(nblk), dim3(NT), 0,
                            stream, static_cast<const E*>(k), static_cast<const E*>(v), Tw, Vw,
                            S0, M0, Hs, Vts, T, H, NC);
+    }
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     if constexpr (sizeof(E) == 2)
