@@ -110,8 +110,8 @@ GATE_TAU = (2048 / 16) ** 0.5            # the temperature sqrt(d_in / h) at d_i
 FETCH_FACTOR = 262144.0 / 131093.9
 WRITE_FACTOR = 131072.0 / 131072.0
 CSRC = os.path.join(ROOT, "chunkwise_delta_rule_amd", "csrc")
-_SPLIT_SHA = "49f2445a533ed29d6aa5a6d029dce3611ac8a5a7096e4b4afc5d35e31dd5ec11"
-_BWD_SHA = "bdb0a9188bd6acdb04783ba9b61e0042963ee0efc2861f53b51f51a0afd8a74a"
+_SPLIT_SHA = "3bd845db73cf61e7da7896336a49537137a0b747d5f7fa43b984ec9414a170b4"
+_BWD_SHA = "a7f788d3aff554dcd34c10fbcdf788a6c65c0f667502c46d67fe9ef0c9a3a665"
 _LIO_SHA = "627a8009335ec269a3313bb348dbbb8e2230dded01b1dfc19a85d20d78a2a663"
 TRAFFIC = {
     # chunk_coef_kernel (3,109.0 / 51,459.4) + chunk_fwd_fused_kernel (223,498.9 / 147,456.1):
@@ -121,25 +121,40 @@ TRAFFIC = {
                                    sha256="6974036122debe9ff2a7e566310281d9"
                                    "cf59d301d216a22c7c443e2b7b4b602e"),
     "chunk_scan_bf16_kernel": dict(sources=("chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
-                                   fetch_kib=268387.1, write_kib=147457.1, sha256=_SPLIT_SHA),
+                                   fetch_kib=268386.1, write_kib=147456.4, sha256=_SPLIT_SHA),
     "chunk_prep_kernel": dict(sources=("chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
-                              fetch_kib=134382.4, write_kib=143696.3, sha256=_SPLIT_SHA),
+                              fetch_kib=134381.8, write_kib=143890.6, sha256=_SPLIT_SHA),
+    # the other configurations' calls under the partition the default rule picks: the
+    # 400M-like layer (B4 H8 T2048) on the column tiles, chunk_coef_kernel (421.0 / 6,432.0)
+    # + chunk_fwd_fused_kernel (28,165.2 / 20,480.0); the 16K-context layer (B1 H16 T16384)
+    # on the row split, chunk_prep_kernel (68,481 / 71,793) + chunk_scan_rs_kernel
+    # (134,236.5 / 67,584.0), and with mu = 0 (67,515 / 71,782 + 134,215.5 / 67,584.0)
+    "config1_fused": dict(sources=("chunk_fused.hip", "chunk_common.hpp", "mfma.hpp"),
+                          fetch_kib=421.0 + 28165.2, write_kib=6432.0 + 20480.0,
+                          sha256="6974036122debe9ff2a7e566310281d9"
+                          "cf59d301d216a22c7c443e2b7b4b602e"),
+    "config3_row_split": dict(sources=("chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
+                              fetch_kib=68481.0 + 134236.5, write_kib=71793.0 + 67584.0,
+                              sha256=_SPLIT_SHA),
+    "config3_row_split_no_mu": dict(sources=("chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
+                                    fetch_kib=67515.0 + 134215.5, write_kib=71782.0 + 67584.0,
+                                    sha256=_SPLIT_SHA),
     "decode_step_kernel": dict(sources=("decode.hip", "mfma.hpp"), fetch_kib=264109.0,
                                write_kib=525524.5, sha256="8fa39113008b99235e1abe57028f0d81"
                                "9b837f475aa87000a6b4e46e3ea6c4e5"),
     # one mdn_chunk_bwd call with the forward's saved residuals: chunk_prep_kernel
-    # (134,382.4 / 143,696.3) + bwd_scan_kernel (471,244.0 / 786,432.1) + bwd_rescan_kernel
-    # with saved residuals (208,989.7 / 524,288.0) + bwd_grad_bf16_kernel<..., true>
-    # (929,528.7 / 543,329.9)
+    # (134,381.8 / 143,890.6) + bwd_scan_bf16_kernel (268,440.8 / 786,526.2) +
+    # bwd_rescan_bf16_kernel with saved residuals (137,322.5 / 524,289.4) +
+    # bwd_grad_bf16_kernel<..., true> (929,530.3 / 543,282.4)
     "chunk_bwd": dict(sources=("chunk_bwd.hip", "chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
-                      fetch_kib=134382.4 + 471244.0 + 208989.7 + 929528.7,
-                      write_kib=143696.3 + 786432.1 + 524288.0 + 543329.9, sha256=_BWD_SHA),
-    # the same recomputing the residuals: bwd_rescan_kernel (274,556.8 / 786,432.1),
-    # bwd_grad_bf16_kernel<..., false> (994,481.4 / 543,327.6)
+                      fetch_kib=134381.8 + 268440.8 + 137322.5 + 929530.3,
+                      write_kib=143890.6 + 786526.2 + 524289.4 + 543282.4, sha256=_BWD_SHA),
+    # the same recomputing the residuals: bwd_rescan_bf16_kernel (170,650.6 / 786,446.7),
+    # bwd_grad_bf16_kernel<..., false> (994,715.3 / 541,514.0)
     "chunk_bwd_recompute": dict(sources=("chunk_bwd.hip", "chunk_fwd.hip", "chunk_common.hpp",
                                          "mfma.hpp"),
-                                fetch_kib=134382.4 + 471244.0 + 274556.8 + 994481.4,
-                                write_kib=143696.3 + 786432.1 + 786432.1 + 543327.6,
+                                fetch_kib=134381.8 + 268440.8 + 170650.6 + 994715.3,
+                                write_kib=143890.6 + 786526.2 + 786446.7 + 541514.0,
                                 sha256=_BWD_SHA),
     "qk_prologue_kernel": dict(sources=("layer_io.hip", "mfma.hpp"), fetch_kib=131099.8,
                                write_kib=262144.0, sha256=_LIO_SHA),
@@ -158,10 +173,10 @@ TRAFFIC = {
 # ran, beside the FLOP-derived fraction of the datasheet peak.
 MFMA_BUSY = {
     "chunk_fwd_fused_kernel": dict(sources=TRAFFIC["chunk_fwd_fused_kernel"]["sources"],
-                                   busy=0.385, sha256=TRAFFIC["chunk_fwd_fused_kernel"]["sha256"]),
+                                   busy=0.389, sha256=TRAFFIC["chunk_fwd_fused_kernel"]["sha256"]),
     "chunk_scan_bf16_kernel": dict(sources=TRAFFIC["chunk_scan_bf16_kernel"]["sources"],
-                                   busy=0.287, sha256=_SPLIT_SHA),
-    "chunk_prep_kernel": dict(sources=TRAFFIC["chunk_prep_kernel"]["sources"], busy=0.100,
+                                   busy=0.300, sha256=_SPLIT_SHA),
+    "chunk_prep_kernel": dict(sources=TRAFFIC["chunk_prep_kernel"]["sources"], busy=0.107,
                               sha256=_SPLIT_SHA),
 }
 
@@ -674,6 +689,11 @@ def bench_configs(args, torch, si, mdn):
             else:
                 r["kernel"] = "chunk_scan_rs_kernel" + ("<no mu>" if mu_null else "")
                 r["timed_with"] = "chunk_prep_kernel (same call)"
+            # counter traffic of the whole call, recorded for the default path
+            tkey = {("config1", "column_tiles"): "config1_fused",
+                    ("config3_runA", "row_split"): "config3_row_split",
+                    ("config3_runB_no_mu", "row_split"): "config3_row_split_no_mu"}.get((key, path))
+            r["traffic"] = traffic_bytes(tkey)
             per_path[path] = {"us_per_step": step_ms * 1e3,
                               "tokens_per_s": cfg.B * cfg.T / (step_ms * 1e-3), "roofline": r}
             log(f"{key} {path}: {step_ms * 1e3:.1f} us/step, "

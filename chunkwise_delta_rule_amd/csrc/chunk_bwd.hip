@@ -38,23 +38,27 @@
 //
 // Kernels, in launch order (after chunk_prep_kernel has written T, A and the
 // coefficient rows of every chunk):
-//   bwd_scan_kernel     one workgroup per (b, h, 64 value columns), chunks last
+//   reverse scan        one workgroup per (b, h, 64 value columns), chunks last
 //                       to first: dVt, dR (written as dv), the state gradients
 //                       carried back, and each chunk's exit-state gradients
-//                       stored for the last kernel.
-//   bwd_rescan_kernel   the same grid, chunks first to last: the state update
+//                       stored for the last kernel (bwd_scan_kernel for fp32
+//                       I/O; bwd_scan_bf16_kernel, with staging wavefronts and
+//                       bf16 tiles, for bf16 I/O).
+//   re-scan             the same grid, chunks first to last: the state update
 //                       again (with R and Vt = T R unless Vt was saved),
-//                       storing each chunk's entry state (and Vt).
-//   bwd_grad_kernel     one workgroup per chunk, all columns: dq, dk and the
-//                       gate gradients.
+//                       storing each chunk's entry state (and Vt)
+//                       (bwd_rescan_kernel; bwd_rescan_bf16_kernel).
+//   per-chunk products  one workgroup per chunk, all columns: dq, dk and the
+//                       gate gradients (bwd_grad_kernel; bwd_grad_bf16_kernel).
 // Arithmetic is fp32 (v_mfma_f32_16x16x4_f32 and VALU; bf16 inputs are
 // widened when they are staged into LDS), except that with bf16 I/O the two
 // scans run all their products on v_mfma_f32_16x16x32_bf16 (each kernel
 // states which operands are exact in bf16, which are rounded and which are
-// split into two bf16 parts), and bwd_grad_kernel runs the six products of a
-// row operand with a stored bf16 state (the row operand rounded to bf16:
-// exact for dO and for saved Vt) and the chunk products dO Vt^T, K K^T and
-// Q K^T (exact operands, but for a recomputed Vt) on it.
+// split into two bf16 parts), and bwd_grad_bf16_kernel runs the six products
+// of a row operand with a stored bf16 state (the row operand rounded to bf16:
+// exact for dO and for saved Vt), the chunk products dO Vt^T, K K^T and Q K^T
+// (exact operands, but for a recomputed Vt) and the masked products (head
+// and remainder operands) on it.
 #include <hip/hip_runtime.h>
 
 #include "chunk_common.hpp"
