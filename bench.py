@@ -111,7 +111,7 @@ FETCH_FACTOR = 262144.0 / 131093.9
 WRITE_FACTOR = 131072.0 / 131072.0
 CSRC = os.path.join(ROOT, "chunkwise_delta_rule_amd", "csrc")
 _SPLIT_SHA = "3bd845db73cf61e7da7896336a49537137a0b747d5f7fa43b984ec9414a170b4"
-_BWD_SHA = "a7f788d3aff554dcd34c10fbcdf788a6c65c0f667502c46d67fe9ef0c9a3a665"
+_BWD_SHA = "c15050cc5a51e96c193a36c781615806dcd9adef3d059c7f677ee765f2551c2e"
 _LIO_SHA = "627a8009335ec269a3313bb348dbbb8e2230dded01b1dfc19a85d20d78a2a663"
 TRAFFIC = {
     # chunk_coef_kernel (3,109.0 / 51,459.4) + chunk_fwd_fused_kernel (223,498.9 / 147,456.1):
