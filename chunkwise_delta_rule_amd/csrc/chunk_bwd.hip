@@ -1532,7 +1532,8 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
     const __bf16* __restrict__ Hs, const __bf16* __restrict__ Hd, const float* __restrict__ alpha,
     const float* __restrict__ mu, const float* __restrict__ eta, const float* __restrict__ beta,
     float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dalpha,
-    float* __restrict__ dmu, float* __restrict__ deta, float* __restrict__ dbeta, int T, int H,
+    float* __restrict__ dmu, float* __restrict__ deta, float* __restrict__ dbeta,
+    const float* S0x, const float* M0x, const float* dSTx, const float* dMTx, int T, int H,
     int NC)
 {
     using SM = GradBfSmem<DK, DV>;
@@ -1759,10 +1760,51 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
 
     // the three inner products <dS', S0>, <dS', M0>, <dM', M0> from the
     // registers (each state element counted by one wavefront); summed with
-    // the row dots
+    // the row dots.  The first chunk's entry state and the last chunk's
+    // exit-state gradients are the call's own fp32 inputs (S0, M0, dS_T,
+    // dM_T; the stored copies are rounded to bf16): there the sums take them
+    // as they are.  A sum over d_k d_v products of two rounded states carries
+    // a rounding error of about 2^-9 sqrt(d_k d_v) rms(dS') rms(S0), which
+    // for a short sequence is a large part of the gate gradients themselves.
     {
         float a0 = 0.f, a1 = 0.f, a2 = 0.f;
-        if (owner) {
+        const float* xS = c == 0 ? S0x : nullptr;
+        const float* xM = c == 0 ? M0x : nullptr;
+        const float* xdS = c == NC - 1 ? dSTx : nullptr;
+        const float* xdM = c == NC - 1 ? dMTx : nullptr;
+        if (owner && (xS || xM || xdS || xdM)) {
+            // row 16 dt + l16 of the state, columns 32 s + 8 lg .. + 7
+            const size_t so = (size_t)bh * DK * DV + (size_t)(16 * dt + l16) * DV + 8 * lg;
+#pragma unroll
+            for (int s = 0; s < KSV; ++s) {
+                float v[4][8];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const unsigned w[4] = {st[x][s].x, st[x][s].y, st[x][s].z, st[x][s].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v[x][2 * e] = __uint_as_float(w[e] << 16);
+                        v[x][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+                    }
+                }
+                const float* xp[4] = {xS, xM, xdS, xdM};
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    if (xp[x]) {
+                        const float4 lo = *reinterpret_cast<const float4*>(xp[x] + so + 32 * s);
+                        const float4 hi = *reinterpret_cast<const float4*>(xp[x] + so + 32 * s + 4);
+                        v[x][0] = lo.x, v[x][1] = lo.y, v[x][2] = lo.z, v[x][3] = lo.w;
+                        v[x][4] = hi.x, v[x][5] = hi.y, v[x][6] = hi.z, v[x][7] = hi.w;
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    a0 += v[2][j] * v[0][j];
+                    a1 += v[2][j] * v[1][j];
+                    a2 += v[3][j] * v[1][j];
+                }
+            }
+        } else if (owner) {
 #pragma unroll
             for (int s = 0; s < KSV; ++s) {
                 const unsigned w0[4] = {st[0][s].x, st[0][s].y, st[0][s].z, st[0][s].w};
@@ -2943,7 +2985,7 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
                            stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                            static_cast<const __bf16*>(dO), dv, Vts,
                            static_cast<const __bf16*>(Vsaved), Hs, Hd, alpha, mu, eta, beta, dq,
-                           dk, dalpha, dmu, deta, dbeta, T, H, NC);
+                           dk, dalpha, dmu, deta, dbeta, S0, M0, dST, dMT, T, H, NC);
     else
         hipLaunchKernelGGL((bwd_grad_kernel<E, DK, DV>), dim3((unsigned)nchunks), dim3(NT), 0,
                            stream, static_cast<const E*>(q), static_cast<const E*>(k),

@@ -116,7 +116,7 @@ def test_bwd_mu_null(T):
     run_case(cfg, mu_null=True, with_beta=True, label="mu0")
 
 
-@pytest.mark.parametrize("T", [65, 200])
+@pytest.mark.parametrize("T", [1, 37, 64, 65, 200])
 @pytest.mark.parametrize("dims", [(64, 64), (128, 128), (64, 128), (128, 64)])
 def test_bwd_small_bf16(T, dims):
     cfg = si.replace(SMALL, B=1, T=T, H=2, Dk=dims[0], Dv=dims[1], io_dtype="bf16",
