@@ -111,7 +111,7 @@ FETCH_FACTOR = 262144.0 / 131093.9
 WRITE_FACTOR = 131072.0 / 131072.0
 CSRC = os.path.join(ROOT, "chunkwise_delta_rule_amd", "csrc")
 _SPLIT_SHA = "3bd845db73cf61e7da7896336a49537137a0b747d5f7fa43b984ec9414a170b4"
-_BWD_SHA = "c15050cc5a51e96c193a36c781615806dcd9adef3d059c7f677ee765f2551c2e"
+_BWD_SHA = "850282acd9770cc150484b96824b49054d526fad71a4ff6ecb3b3e7a6e252216"
 _LIO_SHA = "627a8009335ec269a3313bb348dbbb8e2230dded01b1dfc19a85d20d78a2a663"
 TRAFFIC = {
     # chunk_coef_kernel (3,109.0 / 51,459.4) + chunk_fwd_fused_kernel (223,498.9 / 147,456.1):
@@ -143,18 +143,18 @@ TRAFFIC = {
                                write_kib=525524.5, sha256="8fa39113008b99235e1abe57028f0d81"
                                "9b837f475aa87000a6b4e46e3ea6c4e5"),
     # one mdn_chunk_bwd call with the forward's saved residuals: chunk_prep_kernel
-    # (134,381.8 / 143,890.6) + bwd_scan_bf16_kernel (268,440.8 / 786,526.2) +
-    # bwd_rescan_bf16_kernel with saved residuals (137,322.5 / 524,289.4) +
-    # bwd_grad_bf16_kernel<..., true> (929,530.3 / 543,282.4)
+    # (134,382.7 / 143,912.2) + bwd_scan_bf16_kernel (268,439.3 / 786,475.7) +
+    # bwd_rescan_bf16_kernel with saved residuals (137,303.1 / 524,288.2) +
+    # bwd_grad_bf16_kernel<..., true> (929,677.6 / 544,525.6)
     "chunk_bwd": dict(sources=("chunk_bwd.hip", "chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
-                      fetch_kib=134381.8 + 268440.8 + 137322.5 + 929530.3,
-                      write_kib=143890.6 + 786526.2 + 524289.4 + 543282.4, sha256=_BWD_SHA),
-    # the same recomputing the residuals: bwd_rescan_bf16_kernel (170,650.6 / 786,446.7),
-    # bwd_grad_bf16_kernel<..., false> (994,715.3 / 541,514.0)
+                      fetch_kib=134382.7 + 268439.3 + 137303.1 + 929677.6,
+                      write_kib=143912.2 + 786475.7 + 524288.2 + 544525.6, sha256=_BWD_SHA),
+    # the same recomputing the residuals: bwd_rescan_bf16_kernel (170,163.9 / 786,458.9),
+    # bwd_grad_bf16_kernel<..., false> (994,748.0 / 542,642.5)
     "chunk_bwd_recompute": dict(sources=("chunk_bwd.hip", "chunk_fwd.hip", "chunk_common.hpp",
                                          "mfma.hpp"),
-                                fetch_kib=134381.8 + 268440.8 + 170650.6 + 994715.3,
-                                write_kib=143890.6 + 786526.2 + 786446.7 + 541514.0,
+                                fetch_kib=134382.7 + 268439.3 + 170163.9 + 994748.0,
+                                write_kib=143912.2 + 786475.7 + 786458.9 + 542642.5,
                                 sha256=_BWD_SHA),
     "qk_prologue_kernel": dict(sources=("layer_io.hip", "mfma.hpp"), fetch_kib=131099.8,
                                write_kib=262144.0, sha256=_LIO_SHA),
