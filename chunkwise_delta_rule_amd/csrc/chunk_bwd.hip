@@ -1482,6 +1482,119 @@ __device__ __forceinline__ bf16x8 bwd_cat8(const bf16x4& a, const bf16x4& b)
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// Sum over the four 16-lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48), in every
+// lane, without a trip through LDS: permlane16_swap of a value with itself
+// exchanges groups 1 and 0 and groups 3 and 2 between its two results, so
+// their sum holds p0 + p1 in groups 0, 1 and p2 + p3 in groups 2, 3;
+// permlane32_swap does the same with the halves.
+__device__ __forceinline__ float bwd_sum_groups(float p)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(p), __float_as_uint(p), false,
+                                                    false);
+    const float q = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(q), __float_as_uint(q), false,
+                                                    false);
+    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+// x of the lane d places further round its row of 16 (DPP row_ror:d)
+__device__ __forceinline__ float bwd_row_ror(float x, int d)
+{
+    int r = __float_as_int(x);
+    switch (d) {
+    case 1: r = __builtin_amdgcn_mov_dpp(r, 0x121, 0xf, 0xf, false); break;
+    case 2: r = __builtin_amdgcn_mov_dpp(r, 0x122, 0xf, 0xf, false); break;
+    case 4: r = __builtin_amdgcn_mov_dpp(r, 0x124, 0xf, 0xf, false); break;
+    default: r = __builtin_amdgcn_mov_dpp(r, 0x128, 0xf, 0xf, false); break;
+    }
+    return __int_as_float(r);
+}
+// Sum over the 64 lanes, in every lane.
+__device__ __forceinline__ float bwd_sum_wave(float p)
+{
+    p += bwd_row_ror(p, 8);
+    p += bwd_row_ror(p, 4);
+    p += bwd_row_ror(p, 2);
+    p += bwd_row_ror(p, 1);
+    return bwd_sum_groups(p);
+}
+
+// x of lane i - d (row_shr) or i + d (row_shl) of the lane's row of 16; lanes
+// whose source lies outside the row take `fill` (DPP)
+__device__ __forceinline__ float bwd_row_shr(float x, int d, float fill)
+{
+    int r = __float_as_int(fill);
+    switch (d) {
+    case 1: r = __builtin_amdgcn_update_dpp(r, __float_as_int(x), 0x111, 0xf, 0xf, false); break;
+    case 2: r = __builtin_amdgcn_update_dpp(r, __float_as_int(x), 0x112, 0xf, 0xf, false); break;
+    case 4: r = __builtin_amdgcn_update_dpp(r, __float_as_int(x), 0x114, 0xf, 0xf, false); break;
+    default: r = __builtin_amdgcn_update_dpp(r, __float_as_int(x), 0x118, 0xf, 0xf, false); break;
+    }
+    return __int_as_float(r);
+}
+__device__ __forceinline__ float bwd_row_shl(float x, int d, float fill)
+{
+    int r = __float_as_int(fill);
+    switch (d) {
+    case 1: r = __builtin_amdgcn_update_dpp(r, __float_as_int(x), 0x101, 0xf, 0xf, false); break;
+    case 2: r = __builtin_amdgcn_update_dpp(r, __float_as_int(x), 0x102, 0xf, 0xf, false); break;
+    case 4: r = __builtin_amdgcn_update_dpp(r, __float_as_int(x), 0x104, 0xf, 0xf, false); break;
+    default: r = __builtin_amdgcn_update_dpp(r, __float_as_int(x), 0x108, 0xf, 0xf, false); break;
+    }
+    return __int_as_float(r);
+}
+// The scans of prefix_affine and suffix_affine (lane i holding row i) with
+// the shuffles replaced: four DPP steps inside each row of 16 lanes, then the
+// rows composed from the values at their ends (read as uniform values) --
+// prefix: x_i = m_i x_{i-1} + c_i from x_{-1} = 0; suffix: y_i = c_i + m_i y_{i+1}
+// from y_64 = 0.  Each within-row step composes the lane's map with the one
+// of the d rows before (after) it, as the shuffle scans do.
+__device__ __forceinline__ float bwd_prefix_affine(float m, float c, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+        const float mp = bwd_row_shr(m, d, 1.f), cp = bwd_row_shr(c, d, 0.f);
+        c = m * cp + c;
+        m = m * mp;
+    }
+    // x entering rows 1, 2, 3 (the map of row r at its last lane 16 r + 15)
+    const float x1 = readlane_f(c, 15);
+    const float x2 = readlane_f(m, 31) * x1 + readlane_f(c, 31);
+    const float x3 = readlane_f(m, 47) * x2 + readlane_f(c, 47);
+    const int r = lane >> 4;
+    const float xin = r == 0 ? 0.f : r == 1 ? x1 : r == 2 ? x2 : x3;
+    return m * xin + c;
+}
+__device__ __forceinline__ float bwd_suffix_affine(float m, float c, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+        const float mn = bwd_row_shl(m, d, 1.f), cn = bwd_row_shl(c, d, 0.f);
+        c = c + m * cn;
+        m = m * mn;
+    }
+    // y at the first lanes of rows 3, 2, 1 (the map of row r at lane 16 r)
+    const float y3 = readlane_f(c, 48);
+    const float y2 = readlane_f(m, 32) * y3 + readlane_f(c, 32);
+    const float y1 = readlane_f(m, 16) * y2 + readlane_f(c, 16);
+    const int r = lane >> 4;
+    const float yout = r == 3 ? 0.f : r == 2 ? y3 : r == 1 ? y2 : y1;
+    return m * yout + c;
+}
+// inclusive prefix products of a and b over the 64 lanes
+__device__ __forceinline__ void bwd_prefix_prod2(float& a, float& b, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+        a *= bwd_row_shr(a, d, 1.f);
+        b *= bwd_row_shr(b, d, 1.f);
+    }
+    const float a0 = readlane_f(a, 15), a1 = a0 * readlane_f(a, 31), a2 = a1 * readlane_f(a, 47);
+    const float b0 = readlane_f(b, 15), b1 = b0 * readlane_f(b, 31), b2 = b1 * readlane_f(b, 47);
+    const int r = lane >> 4;
+    a *= r == 0 ? 1.f : r == 1 ? a0 : r == 2 ? a1 : a2;
+    b *= r == 0 ? 1.f : r == 1 ? b0 : r == 2 ? b1 : b2;
+}
+
 constexpr int NT8 = 512;
 
 template <int DK, int DV>
@@ -1683,17 +1796,10 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
     if (wave == 0) {
         const float a = V(G_A)[lane], m = V(G_M)[lane];
         float pa = a, pm = m;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const float ua = __shfl_up(pa, d), um = __shfl_up(pm, d);
-            if (lane >= d) {
-                pa *= ua;
-                pm *= um;
-            }
-        }
+        bwd_prefix_prod2(pa, pm, lane);
         V(G_AB)[lane] = pa;
         V(G_MB)[lane] = pm;
-        V(G_B)[lane] = prefix_affine(a, V(G_S)[lane] * pm, lane);
+        V(G_B)[lane] = bwd_prefix_affine(a, V(G_S)[lane] * pm, lane);
     }
     {
         // Gamma and m by 8-row blocks: wavefront I runs rows 8 I ..
@@ -1823,11 +1929,9 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
                 }
             }
         }
-        for (int o = 32; o >= 1; o >>= 1) {
-            a0 += __shfl_xor(a0, o);
-            a1 += __shfl_xor(a1, o);
-            a2 += __shfl_xor(a2, o);
-        }
+        a0 = bwd_sum_wave(a0);
+        a1 = bwd_sum_wave(a1);
+        a2 = bwd_sum_wave(a2);
         if (lane == 0) {
             scal[8 + wave] = a0;
             scal[16 + wave] = a1;
@@ -1885,8 +1989,7 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
             float p = 0.f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) p += P[x][u][r] * static_cast<float>(y[r]);
-            p += __shfl_xor(p, 16);
-            p += __shfl_xor(p, 32);
+            p = bwd_sum_groups(p);
             if (lg == 0) red[(x * NDT + dt) * CH + i] = p;
         }
     }
@@ -2037,10 +2140,8 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
             p0 += dKh[u][r] * static_cast<float>(kd[r]);
             p1 += dPa[u][r] * static_cast<float>(kd[r]);
         }
-        p0 += __shfl_xor(p0, 16);
-        p0 += __shfl_xor(p0, 32);
-        p1 += __shfl_xor(p1, 16);
-        p1 += __shfl_xor(p1, 32);
+        p0 = bwd_sum_groups(p0);
+        p1 = bwd_sum_groups(p1);
         if (lg == 0) {
             red[(0 * NDT + dt) * CH + i] = p0;
             red[(1 * NDT + dt) * CH + i] = p1;
@@ -2229,13 +2330,13 @@ __global__ __launch_bounds__(NT8) void bwd_grad_bf16_kernel(
         const bool in = i < n;
         const float anext = i + 1 < n ? V(G_A)[i + 1] : 0.f;
         const float mnext = i + 1 < n ? V(G_M)[i + 1] : 0.f;
-        const float gb = suffix_affine(anext, in ? V(G_DB)[i] : 0.f, lane);
+        const float gb = bwd_suffix_affine(anext, in ? V(G_DB)[i] : 0.f, lane);
         const float bp = i > 0 ? V(G_B)[i - 1] : 0.f;
         float da = V(G_DA)[i] + gb * bp;
         const float ds = V(G_DS)[i] + gb * V(G_MB)[i];
         const float gmb0 = (in ? V(G_DMB)[i] : 0.f) + gb * V(G_S)[i];
-        const float gab = suffix_affine(anext, in ? V(G_DAB)[i] : 0.f, lane);
-        const float gmb = suffix_affine(mnext, in ? gmb0 : 0.f, lane);
+        const float gab = bwd_suffix_affine(anext, in ? V(G_DAB)[i] : 0.f, lane);
+        const float gmb = bwd_suffix_affine(mnext, in ? gmb0 : 0.f, lane);
         da += gab * (i > 0 ? V(G_AB)[i - 1] : 1.f);
         const float dm = V(G_DM)[i] + gmb * (i > 0 ? V(G_MB)[i - 1] : 1.f);
         if (in) {
