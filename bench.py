@@ -111,7 +111,7 @@ FETCH_FACTOR = 262144.0 / 131093.9
 WRITE_FACTOR = 131072.0 / 131072.0
 CSRC = os.path.join(ROOT, "chunkwise_delta_rule_amd", "csrc")
 _SPLIT_SHA = "3bd845db73cf61e7da7896336a49537137a0b747d5f7fa43b984ec9414a170b4"
-_BWD_SHA = "850282acd9770cc150484b96824b49054d526fad71a4ff6ecb3b3e7a6e252216"
+_BWD_SHA = "5ff58afe0bb75c2015f230429ba788df447f227a8b8ef5682d654fa927c1b0e2"
 _LIO_SHA = "627a8009335ec269a3313bb348dbbb8e2230dded01b1dfc19a85d20d78a2a663"
 TRAFFIC = {
     # chunk_coef_kernel (3,109.0 / 51,459.4) + chunk_fwd_fused_kernel (223,498.9 / 147,456.1):
@@ -145,16 +145,16 @@ TRAFFIC = {
     # one mdn_chunk_bwd call with the forward's saved residuals: chunk_prep_kernel
     # (134,382.7 / 143,912.2) + bwd_scan_bf16_kernel (268,439.3 / 786,475.7) +
     # bwd_rescan_bf16_kernel with saved residuals (137,303.1 / 524,288.2) +
-    # bwd_grad_bf16_kernel<..., true> (929,677.6 / 544,525.6)
+    # bwd_grad_bf16_kernel<..., true> (929,689.8 / 544,367.0)
     "chunk_bwd": dict(sources=("chunk_bwd.hip", "chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
-                      fetch_kib=134382.7 + 268439.3 + 137303.1 + 929677.6,
-                      write_kib=143912.2 + 786475.7 + 524288.2 + 544525.6, sha256=_BWD_SHA),
+                      fetch_kib=134382.7 + 268439.3 + 137303.1 + 929689.8,
+                      write_kib=143912.2 + 786475.7 + 524288.2 + 544367.0, sha256=_BWD_SHA),
     # the same recomputing the residuals: bwd_rescan_bf16_kernel (170,163.9 / 786,458.9),
-    # bwd_grad_bf16_kernel<..., false> (994,748.0 / 542,642.5)
+    # bwd_grad_bf16_kernel<..., false> (994,752.8 / 543,059.3)
     "chunk_bwd_recompute": dict(sources=("chunk_bwd.hip", "chunk_fwd.hip", "chunk_common.hpp",
                                          "mfma.hpp"),
-                                fetch_kib=134382.7 + 268439.3 + 170163.9 + 994748.0,
-                                write_kib=143912.2 + 786475.7 + 786458.9 + 542642.5,
+                                fetch_kib=134382.7 + 268439.3 + 170163.9 + 994752.8,
+                                write_kib=143912.2 + 786475.7 + 786458.9 + 543059.3,
                                 sha256=_BWD_SHA),
     "qk_prologue_kernel": dict(sources=("layer_io.hip", "mfma.hpp"), fetch_kib=131099.8,
                                write_kib=262144.0, sha256=_LIO_SHA),
