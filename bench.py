@@ -29,9 +29,9 @@ The same JSON line carries:
   timing_ab     the headline call timed one call at a time: median of 20 back to
                 back, and median of 20 with a 1 GiB write between calls;
   other_configs the 400M-like layer (B4 H8 T2048) and the 16K-context layer
-                (B1 H16 T16384) as drawn and with no mu, each under both partitions
-                of the state (column tiles, row split) with its roofline, and the
-                one the default rule runs;
+                (B1 H16 T16384) as drawn and with no mu, each under the partitions
+                of the state (column tiles, row split, segment scan) with its
+                roofline, and the one the default rule runs;
   sweep         tokens/s at T x B = 16384 tokens per call for T = 2K .. 16K;
   measured_peaks  a dense bf16 MFMA loop and a 2 GiB streaming copy on this GPU,
                 beside the datasheet peaks;
@@ -551,14 +551,19 @@ def bench_sweep(args, torch, si, mdn):
             plan.forward()
         (call_ms,), step_ms = time_calls(torch, [plan.forward], args.steps)
         wg = B * cfg.H * (cfg.Dv // 64)
+        nseg = mdn.segment_count(B, T, cfg.H, cfg.Dk, cfg.Dv, True)
+        path = (f"segments ({nseg})" if nseg else
+                "row_split" if wg <= mdn.ROW_SPLIT_MAX_TILES else "column_tiles")
         out.append({"T": T, "B": B, "H": cfg.H, "us_per_step": step_ms * 1e3,
-                    "tokens_per_s": B * T / (step_ms * 1e-3), "workgroups": wg})
+                    "tokens_per_s": B * T / (step_ms * 1e-3), "column_tiles": wg, "path": path})
         log(f"sweep T{T} B{B}: {step_ms * 1e3:.1f} us/step, {B * T / (step_ms * 1e-3):.3e} tokens/s, "
-            f"{wg} workgroups")
+            f"{wg} column tiles, {path}")
         del plan
     return {"workload": "mdn_chunk_fwd, T x B = 16384 tokens per call, H16 d128, bf16",
-            "bound": "one workgroup per (b, h, 64 value columns) scans its chunks in sequence, "
-                     "so fewer than 256 workgroups leave CUs idle",
+            "bound": "the column tiles run one workgroup per (b, h, 64 value columns) through "
+                     "its chunks in sequence, so fewer than 256 of them leave CUs idle; the "
+                     "segment scan (the default for few heads and long sequences) walks about "
+                     "2 / nseg of the chunks in sequence",
             "points": out}
 
 
@@ -641,8 +646,10 @@ def bench_configs(args, torch, si, mdn):
     """The other forward configurations at their own sizes: the 400M-like
     layer (B4 H8 T2048) and the 16K-context layer (B1 H16 T16384) as drawn
     and with no mu (the gated delta rule on the same inputs).  Each is timed
-    under both partitions of the state; `us_per_step` is the one the default
-    rule picks (the row split up to 32 tiles of 64 value columns)."""
+    under the three partitions of the state (column tiles, row split, segment
+    scan); `us_per_step` is the one the default rule picks (the segment scan
+    where three or more segments of at least 16 chunks fit, else the row
+    split up to 32 tiles of 64 value columns, else the column tiles)."""
     bf, f32 = torch.bfloat16, torch.float32
     out = {}
     # the fp32 case (one path: prepare, then the fp32 scan)
@@ -671,10 +678,15 @@ def bench_configs(args, torch, si, mdn):
         toh = cfg.B * cfg.T * cfg.H
         heads = cfg.B * cfg.H
         tiles = heads * (cfg.Dv // 64)
-        auto = "row_split" if tiles <= mdn.ROW_SPLIT_MAX_TILES else "column_tiles"
+        nseg_auto = mdn.segment_count(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, not mu_null)
+        auto = ("segments" if nseg_auto else
+                "row_split" if tiles <= mdn.ROW_SPLIT_MAX_TILES else "column_tiles")
         per_path = {}
-        for path in ("column_tiles", "row_split"):
+        for path in ("column_tiles", "row_split", "segments"):
             with mdn.fwd_path(path):
+                nseg = mdn.segment_count(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, not mu_null)
+                if path == "segments" and nseg == 0:
+                    continue
                 plan = mdn.ChunkPlan(*args_dev)
                 settle(torch, [plan.forward], args.settle)
                 for _ in range(args.warmup):
@@ -686,13 +698,17 @@ def bench_configs(args, torch, si, mdn):
             if path == "column_tiles":
                 r["kernel"] = "chunk_fwd_fused_kernel" + ("<no mu>" if mu_null else "")
                 r["timed_with"] = "chunk_coef_kernel (same call)"
-            else:
+            elif path == "row_split":
                 r["kernel"] = "chunk_scan_rs_kernel" + ("<no mu>" if mu_null else "")
                 r["timed_with"] = "chunk_prep_kernel (same call)"
+            else:
+                r["kernel"] = "chunk_fwd_seg_kernel" + ("<no mu>" if mu_null else "")
+                r["timed_with"] = ("chunk_coef_kernel, the two passes and seg_combine_kernel "
+                                   f"(same call; {nseg} segments)")
             # counter traffic of the whole call, recorded for the default path
             tkey = {("config1", "column_tiles"): "config1_fused",
-                    ("config3_runA", "row_split"): "config3_row_split",
-                    ("config3_runB_no_mu", "row_split"): "config3_row_split_no_mu"}.get((key, path))
+                    ("config3_runA", "segments"): "config3_segments",
+                    ("config3_runB_no_mu", "segments"): "config3_segments_no_mu"}.get((key, path))
             r["traffic"] = traffic_bytes(tkey)
             per_path[path] = {"us_per_step": step_ms * 1e3,
                               "tokens_per_s": cfg.B * cfg.T / (step_ms * 1e-3), "roofline": r}

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <initializer_list>
@@ -18,6 +19,13 @@ hipError_t launch_chunk_prepare(const void* q, const void* k, const float* alpha
                                 const float* eta, const float* beta, int B, int T, int H, int Dk,
                                 bool bf16, void* workspace, hipStream_t stream);
 size_t chunk_fused_workspace_bytes(size_t nchunks);
+int chunk_seg_count(int B, int T, int H, int Dk, int Dv, bool mom, int min_ncs);
+size_t chunk_seg_workspace_bytes(int B, int T, int H, int Dk, int Dv, int nseg, bool mom);
+hipError_t launch_chunk_fused_seg(const void* q, const void* k, const void* v,
+                                  const float* alpha, const float* mu, const float* eta,
+                                  const float* beta, const float* S0, const float* M0, void* O,
+                                  float* ST, float* MT, int B, int T, int H, int Dk, int Dv,
+                                  int nseg, void* workspace, hipStream_t stream);
 hipError_t launch_chunk_fused(const void* q, const void* k, const void* v, const float* alpha,
                               const float* mu, const float* eta, const float* beta,
                               const float* S0, const float* M0, void* O, void* Vto, float* ST,
@@ -103,9 +111,31 @@ bool row_split_for(int B, int H, int Dv, mdn_dtype dt, bool want_vt)
 {
     if (dt != MDN_BF16 || want_vt || B <= 0 || H <= 0) return false;
     const int p = fwd_path.load(std::memory_order_relaxed);
-    if (p == MDN_FWD_COLUMN_TILES) return false;
+    if (p == MDN_FWD_COLUMN_TILES || p == MDN_FWD_SEGMENTS) return false;
     if (p == MDN_FWD_ROW_SPLIT) return true;
     return (size_t)B * (size_t)H * (size_t)(Dv / 64) <= ROW_SPLIT_MAX_TILES;
+}
+
+// Under MDN_FWD_AUTO the segment scan runs where it has three or more
+// segments of at least this many chunks.  Measured on MI355X (d = 128): with
+// 16 to 64 chunks per segment it took 0.11 to 0.9 of the best other path's
+// time (at B1 H16: T4096 0.90, T16384 0.67, with mu = 0 0.69 and 0.59; at
+// B1 H2 T65536 0.23), with 8 to 11 it was up to 1.16 times slower (B1 H16
+// T2048, B4 H8 T2048).
+constexpr int SEG_AUTO_MIN_CHUNKS = 16;
+constexpr int SEG_MIN_CHUNKS = 8;   // MDN_FWD_SEGMENTS
+
+// The number of segments when a bf16 forward of this shape runs the segment
+// scan, else 0; `mom`: mu is given.
+int segments_for(int B, int T, int H, int Dk, int Dv, mdn_dtype dt, bool want_vt, bool mom)
+{
+    if (dt != MDN_BF16 || want_vt || B <= 0 || H <= 0 || T <= 0) return 0;
+    if (!head_dim_ok(Dk) || !head_dim_ok(Dv)) return 0;
+    const int p = fwd_path.load(std::memory_order_relaxed);
+    if (p != MDN_FWD_SEGMENTS && p != MDN_FWD_AUTO) return 0;
+    const int n = mdn::chunk_seg_count(B, T, H, Dk, Dv, mom,
+                                       p == MDN_FWD_AUTO ? SEG_AUTO_MIN_CHUNKS : SEG_MIN_CHUNKS);
+    return n >= 3 ? n : 0;
 }
 
 }  // namespace
@@ -143,13 +173,32 @@ size_t mdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int ch
     // the bf16 column tiles keep T and A on chip and need only the per-chunk
     // coefficient tables
     const size_t split = split_workspace_bytes(B, T, H, Dk, Dv, chunk, dt);
-    if (split == 0 || dt != MDN_BF16 || row_split_for(B, H, Dv, dt, false)) return split;
-    return mdn::chunk_fused_workspace_bytes((size_t)B * H * (((size_t)T + 63) / 64));
+    if (split == 0 || dt != MDN_BF16) return split;
+    // the column tiles (a call that asks for the residuals runs them), the
+    // segment scan where it runs with or without mu, the row split where a
+    // call without segments runs it
+    size_t need = mdn::chunk_fused_workspace_bytes((size_t)B * H * (((size_t)T + 63) / 64));
+    bool every_call_segments = true;
+    for (bool mom : {false, true}) {
+        const int n = segments_for(B, T, H, Dk, Dv, dt, false, mom);
+        if (n > 0)
+            need = std::max(need, mdn::chunk_seg_workspace_bytes(B, T, H, Dk, Dv, n, mom));
+        else
+            every_call_segments = false;
+    }
+    if (!every_call_segments && row_split_for(B, H, Dv, dt, false)) need = std::max(need, split);
+    return need;
+}
+
+int mdn_fwd_segment_count(int B, int T, int H, int Dk, int Dv, int with_mu)
+{
+    return segments_for(B, T, H, Dk, Dv, MDN_BF16, false, with_mu != 0);
 }
 
 int mdn_set_fwd_path(int path)
 {
-    if (path != MDN_FWD_AUTO && path != MDN_FWD_COLUMN_TILES && path != MDN_FWD_ROW_SPLIT)
+    if (path != MDN_FWD_AUTO && path != MDN_FWD_COLUMN_TILES && path != MDN_FWD_ROW_SPLIT &&
+        path != MDN_FWD_SEGMENTS)
         return -1;
     return fwd_path.exchange(path);
 }
@@ -183,6 +232,8 @@ struct FwdArgs {
     // bf16: the row-split scan runs (after the prepare kernel when phase is
     // BOTH) instead of the column-tiled kernels
     bool row_split = false;
+    // bf16, phase BOTH: the segment scan of this many segments (0: not)
+    int nseg = 0;
 };
 
 // Every host-side check of the forward entry points.  `phase` says which
@@ -221,10 +272,13 @@ mdn_status validate_fwd(const FwdArgs& a, int phase, bool* no_work)
 
     // the bf16 forward runs fused and needs only the per-chunk coefficient tables
     const bool fused = phase == BOTH && a.dt == MDN_BF16 && !a.row_split;
+    const bool seg = fused && a.nseg >= 3;
     const size_t nchunks = (size_t)a.B * a.H * (((size_t)a.T + 63) / 64);
-    const size_t need = !tok ? 0
-                        : fused ? mdn::chunk_fused_workspace_bytes(nchunks)
-                                : mdn::chunk_workspace_bytes(a.B, a.T, a.H, a.dt == MDN_BF16);
+    const size_t need =
+        !tok  ? 0
+        : seg ? mdn::chunk_seg_workspace_bytes(a.B, a.T, a.H, a.Dk, a.Dv, a.nseg, a.mu != nullptr)
+        : fused ? mdn::chunk_fused_workspace_bytes(nchunks)
+                : mdn::chunk_workspace_bytes(a.B, a.T, a.H, a.dt == MDN_BF16);
     if (need > 0 && (a.static_ws ? need > a.ws_bytes : (!a.ws || a.ws_bytes < need)))
         return MDN_ERR_WORKSPACE;
 
@@ -265,6 +319,12 @@ mdn_status validate_fwd(const FwdArgs& a, int phase, bool* no_work)
 mdn_status launch_fwd(const FwdArgs& a, int phase, hipStream_t stream)
 {
     const bool bf16 = a.dt == MDN_BF16;
+    if (phase == BOTH && bf16 && !a.row_split && a.nseg >= 3 && a.T > 0) {
+        const hipError_t err = mdn::launch_chunk_fused_seg(
+            a.q, a.k, a.v, a.alpha, a.mu, a.eta, a.beta, a.S0, a.M0, a.O, a.S_T, a.M_T, a.B, a.T,
+            a.H, a.Dk, a.Dv, a.nseg, const_cast<void*>(a.ws), stream);
+        return err == hipSuccess ? MDN_OK : MDN_ERR_HIP;
+    }
     if (phase == BOTH && bf16 && !a.row_split && a.T > 0) {
         const hipError_t err =
             mdn::launch_chunk_fused(a.q, a.k, a.v, a.alpha, a.mu, a.eta, a.beta, a.S0, a.M0, a.O,
@@ -348,7 +408,8 @@ mdn_status mdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
 {
     FwdArgs a{q, k, v, alpha, mu, eta, beta, S0, M0, O, Vt, S_T, M_T, B, T, H, Dk, Dv,
               chunk, dt, workspace, workspace_bytes};
-    a.row_split = row_split_for(B, H, Dv, dt, Vt != nullptr);
+    a.nseg = segments_for(B, T, H, Dk, Dv, dt, Vt != nullptr, mu != nullptr);
+    a.row_split = a.nseg == 0 && row_split_for(B, H, Dv, dt, Vt != nullptr);
     return run_fwd(a, BOTH, stream);
 }
 

@@ -397,17 +397,52 @@ struct FusedLayout {
     static constexpr int BYTES = OFF_TB + 2 * TB_BYTES;
 };
 
+// The segment scan (layers with few heads).  The sequence is cut into nseg
+// segments of ncs chunks (the last may be shorter).  The state map of a
+// segment is affine: its exit pair (S, M) is its exit pair from a zero entry
+// (the local part) plus a linear map Phi_s of its entry pair, and Phi_s is
+// found by running the chunk recurrence with V = 0 from the columns of the
+// identity.  Pass A runs segment 0 from the given entry state (with outputs)
+// beside the local parts and maps of segments 1 .. nseg - 2; a small kernel
+// then composes the entry states of segments 2 .. nseg - 1; pass B runs
+// segments 1 .. nseg - 1 from those entries, with outputs.  Each pass is
+// one round of workgroups, each walking ncs chunks instead of the whole
+// sequence.
+//
+// A workgroup of a segment launch either runs segment s with outputs
+// (workgroups 0 .. nout - 1: tile, head, segment, batch row, fastest first)
+// or forms segment s's transition (the rest: tile of the transition's
+// columns, head, segment, batch row).  The transition's columns are the
+// local part (the DV value columns, from a zero entry) and then the columns
+// of Phi_s: DK columns from the entry S = e_j, M = 0, and with momentum DK
+// more from S = 0, M = e_j.
+struct SegArgs {
+    int ncs;              // chunks per segment
+    int nseg;
+    int out_s0, out_ns;   // the segments run with outputs
+    unsigned nout;        // workgroups of those segments
+    int tr_s0, tr_ns;     // the segments whose transitions are formed
+    int ncol;             // columns of a transition: DV + DK (no momentum) or DV + 2 DK
+    float* Sx;            // entry states [B][nseg][H][DK][DV] (segment 0: the caller's)
+    float* Mx;
+    float* ES;            // exit states of the transitions [B][tr_ns][H][DK][ncol]
+    float* EM;
+};
+
 // MOM = false is the momentum-free case mu = 0 (the gated delta rule): then
 // b = 0 and mubar = 0, so the momentum never feeds the memory, and the
 // final momentum is the last token's own write, -eta_T k_T vt_T^T (the last
 // chunk's update with the weights eta m_n, which are zero but on its last
 // row); the compute waves skip every product with M.
-template <int DK, int DV, bool MOM, bool SAVE>
-__global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const float* __restrict__ ctab, const float* S0, const float* M0, __bf16* __restrict__ O,
-    __bf16* __restrict__ Vto, float* ST, float* MT, int T, int H, int NC, int xcd_groups)
+// TRANS (segment scan only): this workgroup forms a transition.
+template <int DK, int DV, bool MOM, bool SAVE, bool SEG, bool TRANS>
+__device__ __forceinline__ void fused_body(
+    char* smem, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+    const __bf16* __restrict__ v, const float* __restrict__ ctab, const float* S0,
+    const float* M0, __bf16* __restrict__ O, __bf16* __restrict__ Vto, float* ST, float* MT,
+    int T, int H, int NC, int xcd_groups, const SegArgs& sg)
 {
+    static_assert(!(SEG && SAVE) && (SEG || !TRANS), "segment roles");
     using E = __bf16;
     using MM = Mma<E>;
     using L = FusedLayout<DK>;
@@ -420,7 +455,6 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
     constexpr int SK = DK / 32;             // 16x16x32 k-steps over d
     static_assert(DV % TV == 0, "value tile");
 
-    __shared__ __align__(16) char smem[L::BYTES];
     // coefficient tables of chunk c: set c & 1
     auto tables = [&](int c) {
         return reinterpret_cast<float*>(smem + L::OFF_TB + (c & 1) * L::TB_BYTES);
@@ -435,13 +469,45 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
 
     unsigned bid = blockIdx.x;
     if (xcd_groups > 0) bid = (bid % 8u) * (unsigned)xcd_groups + bid / 8u;
-    const int tile = (int)(bid % NTILE);
-    const int bh = (int)(bid / NTILE);
-    const int h = bh % H;
-    const int b = bh / H;
-    // token index of row 0 of chunk c of this head (rows are H tokens apart)
-    auto tok_base = [&](int c) { return ((size_t)b * T + (size_t)c * CH) * H + h; };
-    auto chunk_rows = [&](int c) { return min(CH, T - c * CH); };
+    // this workgroup's chunks c0 .. c0 + NCL - 1 (local index c: chunk c0 + c)
+    int tile, h, b, seg = 0, c0 = 0, NCL = NC;
+    constexpr bool trans = TRANS;           // forms a transition: no outputs
+    if constexpr (!SEG) {
+        tile = (int)(bid % NTILE);
+        const int bh0 = (int)(bid / NTILE);
+        h = bh0 % H;
+        b = bh0 / H;
+    } else {
+        constexpr int NTALL = NTILE + (MOM ? 2 : 1) * (DK / TV);
+        unsigned r;
+        if constexpr (!TRANS) {
+            tile = (int)(bid % NTILE);
+            r = bid / NTILE;
+            h = (int)(r % (unsigned)H);
+            r /= (unsigned)H;
+            seg = sg.out_s0 + (int)(r % (unsigned)sg.out_ns);
+            b = (int)(r / (unsigned)sg.out_ns);
+        } else {
+            const unsigned i = bid - sg.nout;
+            tile = (int)(i % NTALL);
+            r = i / NTALL;
+            h = (int)(r % (unsigned)H);
+            r /= (unsigned)H;
+            seg = sg.tr_s0 + (int)(r % (unsigned)sg.tr_ns);
+            b = (int)(r / (unsigned)sg.tr_ns);
+        }
+        c0 = seg * sg.ncs;
+        NCL = min(sg.ncs, NC - c0);
+    }
+    const int bh = b * H + h;
+    // the V tile the helpers stage (a transition's identity columns have no
+    // V; they stage tile 0, which the compute waves then ignore)
+    const int vtile = tile < NTILE ? tile : 0;
+    // local index of the sequence's last chunk
+    const int lastl = NC - 1 - c0;
+    // token index of row 0 of local chunk c of this head (rows are H tokens apart)
+    auto tok_base = [&](int c) { return ((size_t)b * T + (size_t)(c0 + c) * CH) * H + h; };
+    auto chunk_rows = [&](int c) { return min(CH, T - (c0 + c) * CH); };
 
     if (wave >= 4) {
         // =================== helper wavefronts ===================
@@ -474,14 +540,14 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
         const unsigned offQ_last = row_off(min(rQ + l16, n_last - 1));
         auto load_k = [&](int c) {
             const char* src = reinterpret_cast<const char*>(k + tok_base(c) * DK);
-            const unsigned o = c == NC - 1 ? offK_last : offK;
+            const unsigned o = c == lastl ? offK_last : offK;
 #pragma unroll
             for (int u = 0; u < SK; ++u) kf[u] = *reinterpret_cast<const MM::frag*>(src + o + 64 * u);
         };
         auto load_q = [&](int c, auto par) {
             constexpr int P = decltype(par)::value;
             const char* src = reinterpret_cast<const char*>(q + tok_base(c) * DK);
-            const unsigned o = c == NC - 1 ? offQ_last : offQ;
+            const unsigned o = c == lastl ? offQ_last : offQ;
 #pragma unroll
             for (int u = 0; u < SK; ++u) qf[P][u] = *reinterpret_cast<const MM::frag*>(src + o + 64 * u);
         };
@@ -507,16 +573,16 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
         // direct loads of chunk c's V tile and coefficient rows into buffer B
         auto load_v = [&](int c, char* B) {
             const int n = chunk_rows(c);
-            LC::load(B + L::OFF_V, v + tok_base(c) * DV + tile * TV, (unsigned)(H * DV), v_lane,
+            LC::load(B + L::OFF_V, v + tok_base(c) * DV + vtile * TV, (unsigned)(H * DV), v_lane,
                      n, hw, lane);
-            const float* src = ctab + ((size_t)bh * NC + c) * CTb::FLOATS + CTb::VEC;
+            const float* src = ctab + ((size_t)bh * NC + c0 + c) * CTb::FLOATS + CTb::VEC;
             if (hw == 0 || (hw == 1 && lane < 32))
                 direct_load16(src + 4 * (64 * hw + lane), B + L::OFF_VEC + 1024 * hw);
         };
         // direct loads of chunk c's tables into its table set: 5 pieces of
         // 1 KB, helper h takes pieces h and h + 4
         auto load_tables = [&](int c) {
-            const float* src = ctab + ((size_t)bh * NC + c) * CTb::FLOATS;
+            const float* src = ctab + ((size_t)bh * NC + c0 + c) * CTb::FLOATS;
             char* dst = reinterpret_cast<char*>(tables(c));
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -689,8 +755,8 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
                 // one branch for the whole of a live round, so that the
                 // compiler sees prepare() reached only through the wait below
                 // (a path around it would make it wait for every load)
-                if (nx < NC) {
-                    const bool more = nx + 1 < NC, more2 = nx + 2 < NC;
+                if (nx < NCL) {
+                    const bool more = nx + 1 < NCL, more2 = nx + 2 < NCL;
                     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                     if (more) {
                         zero_tail(nx + 1, rK, kf);
@@ -731,14 +797,14 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             zero_tail(0, rK, kf);
             store_rows(kbuf(0), stK, kf);
-            if (NC > 1) load_k(1);
+            if (NCL > 1) load_k(1);
             load_q(0, IConst<0>{});
             load_tables(0);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_barrier();       // chunk 0's K tile and tables visible
-            for (int c = -1; c < NC; c += 2) {
+            for (int c = -1; c < NCL; c += 2) {
                 round(c, IConst<0>{});
-                if (c + 1 < NC) round(c + 1, IConst<1>{});
+                if (c + 1 < NCL) round(c + 1, IConst<1>{});
             }
         };
         switch (hw) {
@@ -753,18 +819,72 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
 
     // =================== compute wavefronts ===================
     const int wl = 16 * wave + l16;            // this lane's column inside the tile
-    const int col = tile * TV + wl;            // ... inside the head
+    const int col = tile * TV + wl;            // ... inside the head (or the transition)
     f32x4 Sa[RT], Ma[RT];                      // slot (rt, lg, r): row phys_row(16 rt + 4 lg + r)
+    // entry and exit states: rows ld floats apart from a per-workgroup base
+    // (the state of head bh, or of segment seg of it)
     const size_t sbase = (size_t)bh * DK * DV;
+    const float* s0p = S0 ? S0 + sbase : nullptr;
+    const float* m0p = M0 ? M0 + sbase : nullptr;
+    float* stp = ST ? ST + sbase : nullptr;
+    float* mtp = MT ? MT + sbase : nullptr;
+    int ld = DV;
+    if constexpr (SEG) {
+        auto seg_state = [&](float* X, int s) {
+            return X + (((size_t)b * sg.nseg + s) * H + h) * DK * DV;
+        };
+        if (trans) {
+            const size_t tb = (((size_t)b * sg.tr_ns + (seg - sg.tr_s0)) * H + h) * DK * sg.ncol;
+            s0p = m0p = nullptr;
+            stp = sg.ES + tb;
+            mtp = MOM ? sg.EM + tb : nullptr;
+            ld = sg.ncol;
+        } else {
+            if (seg > 0) {
+                s0p = seg_state(sg.Sx, seg);
+                m0p = seg_state(sg.Mx, seg);
+            }
+            if (seg < sg.nseg - 1) {
+                // segment 0 hands its exit state to segment 1; the others'
+                // exits are already known
+                stp = seg == 0 ? seg_state(sg.Sx, 1) : nullptr;
+                mtp = seg == 0 && MOM ? seg_state(sg.Mx, 1) : nullptr;
+            }
+        }
+    }
     auto load_state = [&](f32x4* X, const float* src) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                X[rt][r] = src ? src[sbase + (size_t)phys_row(16 * rt + 4 * lg + r) * DV + col] : 0.f;
+                X[rt][r] = src ? src[(size_t)phys_row(16 * rt + 4 * lg + r) * ld + col] : 0.f;
     };
-    if (S0) load_state(Sa, S0); else load_state(Sa, nullptr);
-    if (MOM && M0) load_state(Ma, M0); else load_state(Ma, nullptr);
+    if constexpr (SEG) {
+        if (s0p) load_state(Sa, s0p); else load_state(Sa, nullptr);
+        if (MOM && m0p) load_state(Ma, m0p); else load_state(Ma, nullptr);
+    } else {
+        auto load0 = [&](f32x4* X, const float* src) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    X[rt][r] = src ? src[sbase + (size_t)phys_row(16 * rt + 4 * lg + r) * DV + col] : 0.f;
+        };
+        if (S0) load0(Sa, S0); else load0(Sa, nullptr);
+        if (MOM && M0) load0(Ma, M0); else load0(Ma, nullptr);
+    }
+    // a transition's identity columns: column j of Phi starts from S = e_j
+    // (the first DK) or M = e_j (the next DK)
+    const bool phi = SEG && trans && tile >= NTILE;
+    if (phi) {
+        const int j = (tile - NTILE) * TV + wl;
+        f32x4* X = MOM && j >= DK ? Ma : Sa;
+        const int jj = j % DK;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) X[rt][r] = phys_row(16 * rt + 4 * lg + r) == jj ? 1.f : 0.f;
+    }
 
     // per-lane LDS offsets, the same every chunk
     // row 16 x + l16, d-chunk lg: rows 16 apart share the swizzle, so the
@@ -797,8 +917,8 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
 
     lds_barrier();   // chunk 0's tables in LDS
     lds_barrier();   // B0: chunk 0 ready
-    for (int c = 0; c < NC; ++c) {
-        const int t0 = c * CH;
+    for (int c = 0; c < NCL; ++c) {
+        const int t0 = (c0 + c) * CH;
         const int n = min(CH, T - t0);
         const char* B = smem + (c & 1) * L::BUF;
         const char* Kb = kbuf(c);
@@ -833,7 +953,7 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
                 const bf16x4 vv = lds_read_tr4(Vb + vtr_base + ct * VJ);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    R[ct][r] = static_cast<float>(vv[r]) - ab[r] * xs[ct][r];
+                    R[ct][r] = (phi ? 0.f : static_cast<float>(vv[r])) - ab[r] * xs[ct][r];
                     if constexpr (MOM) R[ct][r] += ab1[r] * xm[ct][r];
                 }
             }
@@ -842,8 +962,11 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
         //     entry-state part now (it needs nothing the helpers produce);
         //     lane: output row 16 ct + l16, columns 4 lg .. + 3 of this
         //     wavefront's 16
+        // (a transition has no outputs: its workgroups skip the Q and A
+        // products and the stores)
+        const bool outputs = !(SEG && trans);
         f32x4 Ot[4];
-        {
+        if (outputs) {
             f32x4 ys[4], ym[4];
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) ys[ct] = ym[ct] = zero4();
@@ -896,7 +1019,7 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
         //     shape as its accumulator input, with no instruction between,
         //     has read a stale accumulator on gfx950 (the compiler inserts
         //     no wait there), and the 16x16x16 form is no faster here.
-        {
+        if (outputs) {
             bf16x4 vb[4];
 #pragma unroll
             for (int J = 0; J < 4; ++J) vb[J] = to_bf4(Vt[J]);
@@ -916,7 +1039,7 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
                 }
             }
         }
-        {
+        if (outputs) {
             // One 16-byte store per lane per pair of row tiles: lane groups
             // lg and lg ^ 1 (lg = 2 x, 2 x + 1) swap halves of row tiles 2 p and
             // 2 p + 1 (permlane16_swap exchanges group 1 of its first operand
@@ -1015,7 +1138,7 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
         };
         if constexpr (MOM) {
             update(IConst<1>{});
-        } else if (MT && c == NC - 1) {
+        } else if ((SEG ? mtp != nullptr : MT != nullptr) && c == NCL - 1) {
             // without momentum M' is the last token's own write; it is
             // formed once, with the last chunk (M is zero before it)
             update(IConst<1>{});
@@ -1030,10 +1153,133 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                dst[sbase + (size_t)phys_row(16 * rt + 4 * lg + r) * DV + col] = X[rt][r];
+                dst[(size_t)phys_row(16 * rt + 4 * lg + r) * ld + col] = X[rt][r];
     };
-    if (ST) store_state(ST, Sa);
-    if (MT) store_state(MT, Ma);
+    if constexpr (SEG) {
+        if (stp) store_state(stp, Sa);
+        if (mtp) store_state(mtp, Ma);
+    } else {
+        auto store0 = [&](float* dst, const f32x4* X) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dst[sbase + (size_t)phys_row(16 * rt + 4 * lg + r) * DV + col] = X[rt][r];
+        };
+        if (ST) store0(ST, Sa);
+        if (MT) store0(MT, Ma);
+    }
+}
+
+template <int DK, int DV, bool MOM, bool SAVE>
+__global__ __launch_bounds__(2 * NT) void chunk_fwd_fused_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const float* __restrict__ ctab, const float* S0, const float* M0, __bf16* __restrict__ O,
+    __bf16* __restrict__ Vto, float* ST, float* MT, int T, int H, int NC, int xcd_groups)
+{
+    __shared__ __align__(16) char smem[FusedLayout<DK>::BYTES];
+    fused_body<DK, DV, MOM, SAVE, false, false>(smem, q, k, v, ctab, S0, M0, O, Vto, ST, MT, T,
+                                                H, NC, xcd_groups, SegArgs{});
+}
+
+// One pass of the segment scan (see SegArgs): S0, M0, ST, MT are the
+// caller's states, read by segment 0 and written by the last segment.
+template <int DK, int DV, bool MOM>
+__global__ __launch_bounds__(2 * NT) void chunk_fwd_seg_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const float* __restrict__ ctab, const float* S0, const float* M0, __bf16* __restrict__ O,
+    float* ST, float* MT, int T, int H, int NC, int xcd_groups, SegArgs sg)
+{
+    __shared__ __align__(16) char smem[FusedLayout<DK>::BYTES];
+    unsigned bid = blockIdx.x;
+    if (xcd_groups > 0) bid = (bid % 8u) * (unsigned)xcd_groups + bid / 8u;
+    if (bid < sg.nout)
+        fused_body<DK, DV, MOM, false, true, false>(smem, q, k, v, ctab, S0, M0, O, nullptr, ST,
+                                                    MT, T, H, NC, xcd_groups, sg);
+    else
+        fused_body<DK, DV, MOM, false, true, true>(smem, q, k, v, ctab, S0, M0, O, nullptr, ST,
+                                                   MT, T, H, NC, xcd_groups, sg);
+}
+
+// ---------------------------------------------------------------------------
+// The entry states of the segment scan's segments 2 .. nseg - 1, in order:
+// [S; M] entering segment s + 1 is segment s's local exit [S; M] plus Phi_s
+// times [S; M] entering segment s (without momentum, S alone: M never feeds
+// the memory there).  One workgroup per (batch row, head, 16 value columns):
+// the columns are independent.  Products on bf16 MFMA with both operands
+// split into a bf16 head and a bf16 remainder (three products: the
+// remainder times remainder term is below fp32 rounding), so the states
+// carry about fp32 accuracy across the segments.
+// ---------------------------------------------------------------------------
+template <int DK, int DV, bool MOM>
+__global__ __launch_bounds__(NT) void seg_combine_kernel(SegArgs sg, int H)
+{
+    using MM = Mma<__bf16>;
+    constexpr int R2 = MOM ? 2 * DK : DK;   // rows of the carried pair
+    constexpr int TPW = R2 / 64;            // 16-row output tiles per wavefront
+    constexpr int KS = R2 / 32;             // 16x16x32 k-steps
+    constexpr int CB = DV / 16;             // column blocks per head
+    __shared__ float X[R2][17];             // the entry state, this block's 16 columns
+
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+    const int wave = tid >> 6;
+    const int cb = (int)(blockIdx.x % CB);
+    const int bh = (int)(blockIdx.x / CB);
+    const int h = bh % H, b = bh / H;
+    auto state_row = [&](int s, int row) {   // row of [S; M] entering segment s
+        float* base = row < DK ? sg.Sx : sg.Mx;
+        return base + ((((size_t)b * sg.nseg + s) * H + h) * DK + row % DK) * DV + 16 * cb;
+    };
+    for (int i = tid; i < R2 * 16; i += NT) X[i / 16][i % 16] = state_row(sg.tr_s0, i / 16)[i % 16];
+    __syncthreads();
+    auto split = [](const float* x, MM::frag& hi, MM::frag& lo) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            hi[j] = static_cast<__bf16>(x[j]);
+            lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(hi[j]));
+        }
+    };
+    for (int st = 0; st < sg.tr_ns; ++st) {
+        const size_t tb = (((size_t)b * sg.tr_ns + st) * H + h) * DK * sg.ncol;
+        auto erow = [&](int row) { return (row < DK ? sg.ES : sg.EM) + tb + (size_t)(row % DK) * sg.ncol; };
+        f32x4 acc[TPW];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[t][r] = erow(16 * (TPW * wave + t) + 4 * lg + r)[16 * cb + l16];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            float xb[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xb[j] = X[32 * ks + 8 * lg + j][l16];
+            MM::frag bh8, bl8;
+            split(xb, bh8, bl8);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const float* a = erow(16 * (TPW * wave + t) + l16) + DV + 32 * ks + 8 * lg;
+                const f32x4 a0 = *reinterpret_cast<const f32x4*>(a);
+                const f32x4 a1 = *reinterpret_cast<const f32x4*>(a + 4);
+                const float xa[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                MM::frag ah8, al8;
+                split(xa, ah8, al8);
+                acc[t] = MM::mma(ah8, bh8, acc[t]);
+                acc[t] = MM::mma(ah8, bl8, acc[t]);
+                acc[t] = MM::mma(al8, bh8, acc[t]);
+            }
+        }
+        __syncthreads();   // every read of X is done
+        const int s_next = sg.tr_s0 + st + 1;
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * (TPW * wave + t) + 4 * lg + r;
+                X[row][l16] = acc[t][r];
+                state_row(s_next, row)[l16] = acc[t][r];
+            }
+        __syncthreads();
+    }
 }
 
 template <int DK, int DV>
@@ -1083,6 +1329,141 @@ hipError_t launch_chunk_fused(const void* q, const void* k, const void* v, const
                                        workspace, stream);
     return launch_fused_t<64, 64>(q, k, v, alpha, mu, eta, beta, S0, M0, O, Vto, ST, MT, B, T, H,
                                   workspace, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Segment scan, host side.
+// ---------------------------------------------------------------------------
+// Workgroups one pass may take and still run as a single round: one per
+// compute unit (each takes 140 KB of LDS), on a 256-CU MI355X.
+constexpr int SEG_ROUND = 256;
+
+// The number of segments for this shape (0: the segment scan does not
+// apply).  Both passes must fit one round: pass A has the heads' tiles of
+// segment 0 and the transitions of nseg - 2 segments, pass B the tiles of
+// nseg - 1 segments.  A pass then walks ceil(NC / nseg) chunks, so the call
+// walks 2 ceil(NC / nseg) in sequence against NC for the column tiles: three
+// or more segments, each of at least min_ncs chunks.
+int chunk_seg_count(int B, int T, int H, int Dk, int Dv, bool mom, int min_ncs)
+{
+    if (B <= 0 || T <= 0 || H <= 0) return 0;
+    const long heads = (long)B * H;
+    const long ntile = Dv / 64, ntall = ntile + (mom ? 2 : 1) * (Dk / 64);
+    const long nc = ((long)T + CH - 1) / CH;
+    int best = 0;
+    for (int n = 3; n <= 64; ++n) {
+        const long ncs = (nc + n - 1) / n;
+        if (ncs < min_ncs || (n - 1) * ncs >= nc) break;
+        if (heads * ntile + (n - 2) * heads * ntall > SEG_ROUND) break;
+        if ((n - 1) * heads * ntile > SEG_ROUND) break;
+        best = n;
+    }
+    return best;
+}
+
+namespace {
+struct SegSizes {
+    size_t ctab, states, trans;   // bytes, each a multiple of 256
+};
+SegSizes seg_sizes(int B, int T, int H, int Dk, int Dv, int nseg, bool mom)
+{
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t nc = ((size_t)T + CH - 1) / CH;
+    const size_t ncol = (size_t)Dv + (mom ? 2 : 1) * (size_t)Dk;
+    SegSizes z;
+    z.ctab = up((size_t)B * H * nc * ChunkTables::FLOATS * sizeof(float));
+    z.states = up((size_t)B * nseg * H * Dk * Dv * sizeof(float));
+    z.trans = up((size_t)B * (nseg - 2) * H * Dk * ncol * sizeof(float));
+    return z;
+}
+}  // namespace
+
+// Workspace of the segment scan: the coefficient tables, the segments' entry
+// states (S and M) and their transitions (exit S and M).
+size_t chunk_seg_workspace_bytes(int B, int T, int H, int Dk, int Dv, int nseg, bool mom)
+{
+    if (nseg < 3) return 0;
+    const SegSizes z = seg_sizes(B, T, H, Dk, Dv, nseg, mom);
+    return z.ctab + 2 * z.states + 2 * z.trans;
+}
+
+template <int DK, int DV>
+static hipError_t launch_seg_t(const void* q, const void* k, const void* v, const float* alpha,
+                               const float* mu, const float* eta, const float* beta,
+                               const float* S0, const float* M0, void* O, float* ST, float* MT,
+                               int B, int T, int H, int nseg, void* workspace, hipStream_t stream)
+{
+    const bool mom = mu != nullptr;
+    const int NC = (T + CH - 1) / CH;
+    const SegSizes z = seg_sizes(B, T, H, DK, DV, nseg, mom);
+    char* w = static_cast<char*>(workspace);
+    float* ctab = reinterpret_cast<float*>(w);
+    SegArgs sg{};
+    sg.ncs = (NC + nseg - 1) / nseg;
+    sg.nseg = nseg;
+    sg.ncol = DV + (mom ? 2 : 1) * DK;
+    sg.Sx = reinterpret_cast<float*>(w + z.ctab);
+    sg.Mx = reinterpret_cast<float*>(w + z.ctab + z.states);
+    sg.ES = reinterpret_cast<float*>(w + z.ctab + 2 * z.states);
+    sg.EM = reinterpret_cast<float*>(w + z.ctab + 2 * z.states + z.trans);
+
+    const unsigned nhg = (unsigned)((H + COEF_HEADS - 1) / COEF_HEADS);
+    hipLaunchKernelGGL(chunk_coef_kernel, dim3((unsigned)B * nhg * (unsigned)NC),
+                       dim3(COEF_HEADS * 64), 0, stream, alpha, mu, eta, beta, ctab, T, H, NC,
+                       nhg);
+    auto kern = mom ? chunk_fwd_seg_kernel<DK, DV, true> : chunk_fwd_seg_kernel<DK, DV, false>;
+    const unsigned heads = (unsigned)B * (unsigned)H;
+    constexpr unsigned NTILE = DV / 64;
+    const unsigned ntall = NTILE + (mom ? 2u : 1u) * (DK / 64);   // transition tiles
+    auto launch = [&](const SegArgs& a, unsigned ntr) {
+        const unsigned nblk = a.nout + ntr;
+        const int xcd_groups = nblk % 8 == 0 ? (int)(nblk / 8) : 0;
+        hipLaunchKernelGGL(kern, dim3(nblk), dim3(2 * NT), 0, stream,
+                           static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                           static_cast<const __bf16*>(v), ctab, S0, M0, static_cast<__bf16*>(O),
+                           ST, MT, T, H, NC, xcd_groups, a);
+    };
+    // pass A: segment 0 with outputs, the transitions of 1 .. nseg - 2
+    SegArgs a = sg;
+    a.out_s0 = 0;
+    a.out_ns = 1;
+    a.nout = heads * NTILE;
+    a.tr_s0 = 1;
+    a.tr_ns = nseg - 2;
+    launch(a, (unsigned)a.tr_ns * heads * ntall);
+    // the entry states of segments 2 .. nseg - 1
+    auto comb = mom ? seg_combine_kernel<DK, DV, true> : seg_combine_kernel<DK, DV, false>;
+    hipLaunchKernelGGL(comb, dim3(heads * (DV / 16)), dim3(NT), 0, stream, a, H);
+    // pass B: segments 1 .. nseg - 1 with outputs
+    SegArgs c = sg;
+    c.out_s0 = 1;
+    c.out_ns = nseg - 1;
+    c.nout = (unsigned)(nseg - 1) * heads * NTILE;
+    c.tr_s0 = 1;
+    c.tr_ns = nseg - 2;
+    launch(c, 0);
+    return hipGetLastError();
+}
+
+// The bf16 forward as a segment scan of nseg >= 3 segments (chunk_seg_count).
+// `workspace` holds chunk_seg_workspace_bytes(B, T, H, Dk, Dv, nseg, mu != NULL).
+hipError_t launch_chunk_fused_seg(const void* q, const void* k, const void* v,
+                                  const float* alpha, const float* mu, const float* eta,
+                                  const float* beta, const float* S0, const float* M0, void* O,
+                                  float* ST, float* MT, int B, int T, int H, int Dk, int Dv,
+                                  int nseg, void* workspace, hipStream_t stream)
+{
+    if (Dk == 128 && Dv == 128)
+        return launch_seg_t<128, 128>(q, k, v, alpha, mu, eta, beta, S0, M0, O, ST, MT, B, T, H,
+                                      nseg, workspace, stream);
+    if (Dk == 128 && Dv == 64)
+        return launch_seg_t<128, 64>(q, k, v, alpha, mu, eta, beta, S0, M0, O, ST, MT, B, T, H,
+                                     nseg, workspace, stream);
+    if (Dk == 64 && Dv == 128)
+        return launch_seg_t<64, 128>(q, k, v, alpha, mu, eta, beta, S0, M0, O, ST, MT, B, T, H,
+                                     nseg, workspace, stream);
+    return launch_seg_t<64, 64>(q, k, v, alpha, mu, eta, beta, S0, M0, O, ST, MT, B, T, H, nseg,
+                                workspace, stream);
 }
 
 }  // namespace mdn

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libmdn.so")
 MDN_F32 = 0
 MDN_BF16 = 1
 # mdn_fwd_path: how the bf16 forward partitions the carried state
-FWD_PATHS = {"auto": 0, "column_tiles": 1, "row_split": 2}
+FWD_PATHS = {"auto": 0, "column_tiles": 1, "row_split": 2, "segments": 3}
 # MDN_FWD_AUTO runs the row split up to this many tiles of 64 value columns,
 # B * H * (Dv / 64) (the rule in api.hip; a CPU test checks the two agree)
 ROW_SPLIT_MAX_TILES = 32
@@ -41,7 +41,7 @@ STATUS_NAMES = {
 }
 
 # every symbol include/libmdn.h declares
-EXPORTED = ("mdn_set_fwd_path", "mdn_chunk_fwd_workspace_bytes",
+EXPORTED = ("mdn_set_fwd_path", "mdn_fwd_segment_count", "mdn_chunk_fwd_workspace_bytes",
             "mdn_chunk_fwd_split_workspace_bytes", "mdn_chunk_fwd", "mdn_chunk_fwd_noalloc",
             "mdn_chunk_fwd_prepare", "mdn_chunk_fwd_scan", "mdn_decode_step",
             "mdn_gates_from_logits", "mdn_chunk_bwd_workspace_bytes", "mdn_chunk_bwd",
@@ -75,6 +75,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.mdn_set_fwd_path.restype = I
     lib.mdn_set_fwd_path.argtypes = [I]
+    lib.mdn_fwd_segment_count.restype = I
+    lib.mdn_fwd_segment_count.argtypes = [I] * 6
     lib.mdn_chunk_fwd_workspace_bytes.restype = S
     lib.mdn_chunk_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.mdn_chunk_fwd_split_workspace_bytes.restype = S
@@ -140,12 +142,19 @@ def _stream(device: torch.device) -> int:
 
 def set_fwd_path(path: str) -> str:
     """Select the bf16 forward's state partition for every later call
-    (mdn_set_fwd_path): "auto", "column_tiles" or "row_split".  Returns the
-    previous setting's name."""
+    (mdn_set_fwd_path): "auto", "column_tiles", "row_split" or "segments".
+    Returns the previous setting's name."""
     if path not in FWD_PATHS:
         raise ValueError(f"unknown forward path {path!r}; one of {sorted(FWD_PATHS)}")
     prev = load_library().mdn_set_fwd_path(FWD_PATHS[path])
     return {v: k for k, v in FWD_PATHS.items()}[prev]
+
+
+def segment_count(B: int, T: int, H: int, Dk: int, Dv: int, with_mu: bool) -> int:
+    """Segments a bf16 forward of this shape runs the segment scan with under
+    the current forward path, 0 when it runs another path
+    (mdn_fwd_segment_count)."""
+    return load_library().mdn_fwd_segment_count(B, T, H, Dk, Dv, int(bool(with_mu)))
 
 
 class fwd_path:

@@ -67,7 +67,7 @@ typedef enum {
 /*
  * How the bf16 forward partitions the carried state over workgroups.  The
  * scan over chunks is sequential, so its parallelism is the number of state
- * tiles in flight:
+ * tiles in flight (times the number of segments, for the segment scan):
  *   MDN_FWD_COLUMN_TILES  one workgroup per 64 value columns of a head, each
  *                         wavefront owning 16 columns and all Dk rows.
  *                         mdn_chunk_fwd runs one fused kernel that also forms
@@ -80,18 +80,43 @@ typedef enum {
  *                         (mdn_chunk_fwd_prepare's kernel, then this scan).
  *                         It does not produce the residuals: a call with
  *                         Vt != NULL runs the column-tiled kernels.
- *   MDN_FWD_AUTO          (the default) the row split when the layer has at
- *                         most 32 column tiles, B * H * (Dv / 64) <= 32,
- *                         where it measured faster on MI355X (at 64 tiles the
- *                         two are about even, at 128 the column tiles take
- *                         half the time).
- * Both partitions evaluate the same equations; their results agree to
- * rounding, not bit for bit.  MDN_F32 always runs the two-phase path.
+ *   MDN_FWD_SEGMENTS      the sequence cut into nseg >= 3 segments of at
+ *                         least 8 chunks.  A segment's exit state is affine
+ *                         in its entry state (the chunk recurrence of
+ *                         "MDN: Parallelizing Stepwise Momentum for Delta
+ *                         Linear Attention", frame "Chunk outputs combine
+ *                         incoming states and local writes"): its exit from
+ *                         a zero entry plus a linear map of the entry, found
+ *                         by running the recurrence with V = 0 from the
+ *                         identity's columns.  Pass 1 runs segment 0 from
+ *                         the entry state beside the maps of segments
+ *                         1 .. nseg - 2; a small kernel chains them into the
+ *                         entry state of every segment; pass 2 runs segments
+ *                         1 .. nseg - 1 from those, so each pass walks
+ *                         1 / nseg of the chunks.  nseg is the largest with
+ *                         both passes within one workgroup per compute unit;
+ *                         where none of 3 or more fits (many heads, or fewer
+ *                         than 24 chunks) the column tiles run.  It does not
+ *                         produce the residuals (Vt != NULL: column tiles).
+ *   MDN_FWD_AUTO          (the default) the segment scan where three or more
+ *                         segments of at least 16 chunks fit (few heads and
+ *                         long sequences; measured on MI355X at d = 128 it
+ *                         took 0.23 to 0.90 of the other paths' time there,
+ *                         and up to 1.16 times theirs with 8 to 11 chunks per
+ *                         segment); otherwise the row split when the layer
+ *                         has at most 32 column tiles, B * H * (Dv / 64) <=
+ *                         32, where it measured faster than the column tiles
+ *                         (at 64 tiles the two are about even, at 128 the
+ *                         column tiles take half the time); otherwise the
+ *                         column tiles.
+ * All paths evaluate the same equations; their results agree to rounding,
+ * not bit for bit.  MDN_F32 always runs the two-phase path.
  */
 typedef enum {
     MDN_FWD_AUTO = 0,
     MDN_FWD_COLUMN_TILES = 1,
-    MDN_FWD_ROW_SPLIT = 2
+    MDN_FWD_ROW_SPLIT = 2,
+    MDN_FWD_SEGMENTS = 3
 } mdn_fwd_path;
 
 /*
@@ -103,6 +128,14 @@ typedef enum {
  * launched).
  */
 int mdn_set_fwd_path(int path);
+
+/*
+ * The number of segments a bf16 mdn_chunk_fwd call of this shape (with_mu:
+ * mu is given; no residuals asked for) runs the segment scan with under the
+ * current mdn_set_fwd_path setting; 0 when it runs another path.  Host only:
+ * no device is touched.  Negative or unsupported sizes return 0.
+ */
+int mdn_fwd_segment_count(int B, int T, int H, int Dk, int Dv, int with_mu);
 
 /*
  * Bytes of device workspace mdn_chunk_fwd needs for this problem under the

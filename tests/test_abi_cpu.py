@@ -81,6 +81,52 @@ def test_workspace_bytes(lib):
         assert split(*bad) == 0
 
 
+def test_segment_scan_choice_and_workspace(lib):
+    """The segment scan's size rule (mdn_fwd_segment_count) and workspace.
+    nseg is the largest count of segments, 3 or more, with both passes in one
+    round of 256 workgroups -- pass 1: the heads' Dv/64 tiles plus nseg - 2
+    transitions of Dv/64 + 2 Dk/64 tiles (Dk/64 without mu), pass 2: nseg - 1
+    segments' tiles -- and ceil(NC / nseg) >= 16 chunks per segment under
+    MDN_FWD_AUTO, >= 8 under MDN_FWD_SEGMENTS.  Its workspace: the
+    coefficient tables (1664 floats per chunk), entry states of every segment
+    (S and M), exit states of the nseg - 2 transitions (S and M, Dv + 2 Dk
+    columns, Dv + Dk without mu), fp32."""
+    count = lib.mdn_fwd_segment_count
+    ws = lib.mdn_chunk_fwd_workspace_bytes
+    assert count(1, 16384, 16, 128, 128, 1) == 4      # 32 + 2 * 96 = 224 workgroups
+    assert count(1, 16384, 16, 128, 128, 0) == 5      # 32 + 3 * 64 = 224
+    assert count(4, 2048, 8, 128, 128, 1) == 0        # 3 segments of 11 chunks: auto declines
+    assert count(1, 2048, 16, 128, 128, 1) == 0
+    assert count(8, 4096, 16, 128, 128, 1) == 0       # 256 tiles
+    assert count(1, 65536, 2, 128, 128, 1) == 23      # 4 + 21 * 12 = 256
+    assert count(1, 16384, 16, 128, 128, 1) == lib.mdn_fwd_segment_count(1, 16384, 16, 128, 128, 1)
+    nc, ctab = 256, 16 * 256 * 1664 * 4
+    seg_mu = ctab + 2 * 4 * 16 * 128 * 128 * 4 + 2 * 2 * 16 * 128 * 384 * 4
+    seg_nomu = ctab + 2 * 5 * 16 * 128 * 128 * 4 + 2 * 3 * 16 * 128 * 256 * 4
+    assert ws(1, 64 * nc, 16, 128, 128, 64, mdn.MDN_BF16) == max(seg_mu, seg_nomu)
+    prev = lib.mdn_set_fwd_path(mdn.FWD_PATHS["segments"])
+    try:
+        assert count(4, 2048, 8, 128, 128, 1) == 3    # 3 segments of 11 chunks
+        assert count(1, 1536, 2, 128, 128, 1) == 3    # 3 of 8
+        assert count(1, 1345, 2, 128, 128, 1) == 3    # 22 chunks (the last one row): 8, 8, 6
+        assert count(1, 1344, 2, 128, 128, 1) == 0    # 21 chunks: 7 per segment
+        assert count(1, 16384, 16, 128, 128, 1) == 4
+        assert count(1, 16384, 16, 64, 64, 1) == 7    # 16 + 5 * 48 = 256
+        assert ws(1, 64 * nc, 16, 128, 128, 64, mdn.MDN_BF16) == max(seg_mu, seg_nomu)
+        # where it does not apply, the column tiles' workspace
+        assert ws(8, 4096, 16, 128, 128, 64, mdn.MDN_BF16) == 8 * 16 * 64 * 1664 * 4
+    finally:
+        lib.mdn_set_fwd_path(prev)
+    for path in ("column_tiles", "row_split"):
+        prev = lib.mdn_set_fwd_path(mdn.FWD_PATHS[path])
+        try:
+            assert count(1, 16384, 16, 128, 128, 1) == 0
+        finally:
+            lib.mdn_set_fwd_path(prev)
+    for bad in [(0, 4096, 1, 128, 128, 1), (1, -5, 1, 128, 128, 1), (1, 4096, 1, 96, 128, 1)]:
+        assert count(*bad) == 0
+
+
 # fake, 16-byte aligned, non-overlapping "device" addresses
 BASE = 1 << 40
 STEP = 1 << 32
