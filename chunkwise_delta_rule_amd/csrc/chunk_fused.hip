@@ -423,6 +423,7 @@ struct SegArgs {
     unsigned nout;        // workgroups of those segments
     int tr_s0, tr_ns;     // the segments whose transitions are formed
     int ncol;             // columns of a transition: DV + DK (no momentum) or DV + 2 DK
+    int heads8;           // B H is a multiple of 8 (the combine's block order)
     float* Sx;            // entry states [B][nseg][H][DK][DV] (segment 0: the caller's)
     float* Mx;
     float* ES;            // exit states of the transitions [B][tr_ns][H][DK][ncol]
@@ -1206,31 +1207,42 @@ __global__ __launch_bounds__(2 * NT) void chunk_fwd_seg_kernel(
 // [S; M] entering segment s + 1 is segment s's local exit [S; M] plus Phi_s
 // times [S; M] entering segment s (without momentum, S alone: M never feeds
 // the memory there).  One workgroup per (batch row, head, 16 value columns):
-// the columns are independent.  Products on bf16 MFMA with both operands
+// the columns are independent; one wavefront per 16 rows of [S; M].
+// Products on bf16 MFMA with both operands
 // split into a bf16 head and a bf16 remainder (three products: the
 // remainder times remainder term is below fp32 rounding), so the states
 // carry about fp32 accuracy across the segments.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, bool MOM>
-__global__ __launch_bounds__(NT) void seg_combine_kernel(SegArgs sg, int H)
+__global__ __launch_bounds__((MOM ? 2 * DK : DK) * 4) void seg_combine_kernel(SegArgs sg, int H)
 {
     using MM = Mma<__bf16>;
     constexpr int R2 = MOM ? 2 * DK : DK;   // rows of the carried pair
-    constexpr int TPW = R2 / 64;            // 16-row output tiles per wavefront
+    constexpr int NTH = R2 * 4;             // one wavefront per 16-row output tile
     constexpr int KS = R2 / 32;             // 16x16x32 k-steps
     constexpr int CB = DV / 16;             // column blocks per head
     __shared__ float X[R2][17];             // the entry state, this block's 16 columns
 
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
     const int wave = tid >> 6;
-    const int cb = (int)(blockIdx.x % CB);
-    const int bh = (int)(blockIdx.x / CB);
+    // The column blocks of a head read the same maps: with the heads a
+    // multiple of 8, block i runs on XCD i mod 8, so blocks 8 (cb + CB j) + x
+    // (all cb) of head 8 j + x share that XCD's L2
+    int cb, bh;
+    if (sg.heads8) {
+        const unsigned x = blockIdx.x % 8u, r = blockIdx.x / 8u;
+        cb = (int)(r % CB);
+        bh = (int)(8u * (r / CB) + x);
+    } else {
+        cb = (int)(blockIdx.x % CB);
+        bh = (int)(blockIdx.x / CB);
+    }
     const int h = bh % H, b = bh / H;
     auto state_row = [&](int s, int row) {   // row of [S; M] entering segment s
         float* base = row < DK ? sg.Sx : sg.Mx;
         return base + ((((size_t)b * sg.nseg + s) * H + h) * DK + row % DK) * DV + 16 * cb;
     };
-    for (int i = tid; i < R2 * 16; i += NT) X[i / 16][i % 16] = state_row(sg.tr_s0, i / 16)[i % 16];
+    for (int i = tid; i < R2 * 16; i += NTH) X[i / 16][i % 16] = state_row(sg.tr_s0, i / 16)[i % 16];
     __syncthreads();
     auto split = [](const float* x, MM::frag& hi, MM::frag& lo) {
 #pragma unroll
@@ -1242,42 +1254,41 @@ __global__ __launch_bounds__(NT) void seg_combine_kernel(SegArgs sg, int H)
     for (int st = 0; st < sg.tr_ns; ++st) {
         const size_t tb = (((size_t)b * sg.tr_ns + st) * H + h) * DK * sg.ncol;
         auto erow = [&](int row) { return (row < DK ? sg.ES : sg.EM) + tb + (size_t)(row % DK) * sg.ncol; };
-        f32x4 acc[TPW];
+        // the step's A fragments (this wavefront's 16 rows of Phi) and its
+        // local exit, all loaded before the products so that their latency
+        // is paid once
+        const float* arow = erow(16 * wave + l16) + DV + 8 * lg;
+        f32x4 a0[KS], a1[KS];
 #pragma unroll
-        for (int t = 0; t < TPW; ++t)
+        for (int ks = 0; ks < KS; ++ks) {
+            a0[ks] = *reinterpret_cast<const f32x4*>(arow + 32 * ks);
+            a1[ks] = *reinterpret_cast<const f32x4*>(arow + 32 * ks + 4);
+        }
+        f32x4 acc;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                acc[t][r] = erow(16 * (TPW * wave + t) + 4 * lg + r)[16 * cb + l16];
+        for (int r = 0; r < 4; ++r) acc[r] = erow(16 * wave + 4 * lg + r)[16 * cb + l16];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             float xb[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) xb[j] = X[32 * ks + 8 * lg + j][l16];
-            MM::frag bh8, bl8;
+            MM::frag bh8, bl8, ah8, al8;
             split(xb, bh8, bl8);
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                const float* a = erow(16 * (TPW * wave + t) + l16) + DV + 32 * ks + 8 * lg;
-                const f32x4 a0 = *reinterpret_cast<const f32x4*>(a);
-                const f32x4 a1 = *reinterpret_cast<const f32x4*>(a + 4);
-                const float xa[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-                MM::frag ah8, al8;
-                split(xa, ah8, al8);
-                acc[t] = MM::mma(ah8, bh8, acc[t]);
-                acc[t] = MM::mma(ah8, bl8, acc[t]);
-                acc[t] = MM::mma(al8, bh8, acc[t]);
-            }
+            const float xa[8] = {a0[ks][0], a0[ks][1], a0[ks][2], a0[ks][3],
+                                 a1[ks][0], a1[ks][1], a1[ks][2], a1[ks][3]};
+            split(xa, ah8, al8);
+            acc = MM::mma(ah8, bh8, acc);
+            acc = MM::mma(ah8, bl8, acc);
+            acc = MM::mma(al8, bh8, acc);
         }
         __syncthreads();   // every read of X is done
         const int s_next = sg.tr_s0 + st + 1;
 #pragma unroll
-        for (int t = 0; t < TPW; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * (TPW * wave + t) + 4 * lg + r;
-                X[row][l16] = acc[t][r];
-                state_row(s_next, row)[l16] = acc[t][r];
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * wave + 4 * lg + r;
+            X[row][l16] = acc[r];
+            state_row(s_next, row)[l16] = acc[r];
+        }
         __syncthreads();
     }
 }
@@ -1432,8 +1443,10 @@ static hipError_t launch_seg_t(const void* q, const void* k, const void* v, cons
     a.tr_ns = nseg - 2;
     launch(a, (unsigned)a.tr_ns * heads * ntall);
     // the entry states of segments 2 .. nseg - 1
+    a.heads8 = heads % 8 == 0;
     auto comb = mom ? seg_combine_kernel<DK, DV, true> : seg_combine_kernel<DK, DV, false>;
-    hipLaunchKernelGGL(comb, dim3(heads * (DV / 16)), dim3(NT), 0, stream, a, H);
+    hipLaunchKernelGGL(comb, dim3(heads * (DV / 16)), dim3((mom ? 2 : 1) * DK * 4), 0, stream, a,
+                       H);
     // pass B: segments 1 .. nseg - 1 with outputs
     SegArgs c = sg;
     c.out_s0 = 1;

@@ -270,7 +270,11 @@ class ChunkPlan:
         self.Vt = torch.empty((B, T, H, Dv), dtype=q.dtype, device=dev) if save_vt else None
         self.S_T = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev) if final_state else None
         self.M_T = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev) if final_state else None
-        need = int(self.lib.mdn_chunk_fwd_split_workspace_bytes(B, T, H, Dk, Dv, chunk, self.code))
+        # room for the two phases and for a whole call under the current
+        # forward path (the segment scan's can be the larger)
+        need = max(int(self.lib.mdn_chunk_fwd_split_workspace_bytes(B, T, H, Dk, Dv, chunk,
+                                                                    self.code)),
+                   int(self.lib.mdn_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, self.code)))
         self.workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
         self.ws_bytes = need
         # one full call validates every argument (and fills the outputs)

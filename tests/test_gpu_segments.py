@@ -167,3 +167,22 @@ def test_segments_with_residuals_run_the_column_tiles():
     torch.cuda.synchronize()
     assert float(Vt.float().abs().max()) > 0
     check((to_np(O), to_np(ST), to_np(MT)), oracle_forward(inp), "segments + Vt")
+
+
+def test_segments_plan():
+    """mdn.ChunkPlan (fixed buffers, as the benchmark times them) under the
+    segment scan, where its workspace exceeds the two phases' (B4 H8 T2048:
+    3 segments), gives the same bits as a plain call."""
+    inp = si.make_forward(si.CONFIGS[1], seed=7800)
+    cfg = inp["cfg"]
+    segmented(cfg)
+    assert mdn.workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, torch.bfloat16) > \
+        mdn.workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.Dk, cfg.Dv, torch.bfloat16, split=True)
+    dt = torch.bfloat16
+    args = (to_dev(inp["q"], dt), to_dev(inp["k"], dt), to_dev(inp["v"], dt), to_dev(inp["alpha"]),
+            to_dev(inp["mu"]), to_dev(inp["eta"]), to_dev(inp["S0"]), to_dev(inp["M0"]))
+    plan = mdn.ChunkPlan(*args)
+    plan.forward()
+    O, ST, MT = mdn.chunk_fwd(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(plan.O, O) and torch.equal(plan.S_T, ST) and torch.equal(plan.M_T, MT)
