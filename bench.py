@@ -112,33 +112,35 @@ WRITE_FACTOR = 131072.0 / 131072.0
 CSRC = os.path.join(ROOT, "chunkwise_delta_rule_amd", "csrc")
 _SPLIT_SHA = "3bd845db73cf61e7da7896336a49537137a0b747d5f7fa43b984ec9414a170b4"
 _BWD_SHA = "5ff58afe0bb75c2015f230429ba788df447f227a8b8ef5682d654fa927c1b0e2"
+_FUSED_SHA = "1a883b8ae5a0a6829bb2e34f9cc05037f8b37adfbe58769936c3a87ec1d5f730"
 _LIO_SHA = "627a8009335ec269a3313bb348dbbb8e2230dded01b1dfc19a85d20d78a2a663"
 TRAFFIC = {
-    # chunk_coef_kernel (3,109.0 / 51,459.4) + chunk_fwd_fused_kernel (223,498.9 / 147,456.1):
+    # chunk_coef_kernel (3,211.4 / 51,459.4) + chunk_fwd_fused_kernel (223,494.3 / 147,456.4):
     # one mdn_chunk_fwd call, the unit the bench times
     "chunk_fwd_fused_kernel": dict(sources=("chunk_fused.hip", "chunk_common.hpp", "mfma.hpp"),
-                                   fetch_kib=3109.0 + 223498.9, write_kib=51459.4 + 147456.1,
-                                   sha256="6974036122debe9ff2a7e566310281d9"
-                                   "cf59d301d216a22c7c443e2b7b4b602e"),
+                                   fetch_kib=3211.4 + 223494.3, write_kib=51459.4 + 147456.4,
+                                   sha256=_FUSED_SHA),
     "chunk_scan_bf16_kernel": dict(sources=("chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
                                    fetch_kib=268386.1, write_kib=147456.4, sha256=_SPLIT_SHA),
     "chunk_prep_kernel": dict(sources=("chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
                               fetch_kib=134381.8, write_kib=143890.6, sha256=_SPLIT_SHA),
     # the other configurations' calls under the partition the default rule picks: the
     # 400M-like layer (B4 H8 T2048) on the column tiles, chunk_coef_kernel (421.0 / 6,432.0)
-    # + chunk_fwd_fused_kernel (28,165.2 / 20,480.0); the 16K-context layer (B1 H16 T16384)
-    # on the row split, chunk_prep_kernel (68,481 / 71,793) + chunk_scan_rs_kernel
-    # (134,236.5 / 67,584.0), and with mu = 0 (67,515 / 71,782 + 134,215.5 / 67,584.0)
+    # + chunk_fwd_fused_kernel (28,161.1 / 20,480.0); the 16K-context layer (B1 H16 T16384)
+    # on the segment scan (4 segments): chunk_coef_kernel (1,573.0 / 25,728.3), pass 1 of
+    # chunk_fwd_seg_kernel (89,964.5 / 30,720.0), seg_combine_kernel (7,219.5 / 4,096.0) and
+    # pass 2 (87,071.3 / 51,200.0); with mu = 0 (5 segments): 1,061.0 / 25,728.3,
+    # 90,976.2 / 20,480.0, 3,618.0 / 3,072.0, 91,258.6 / 54,272.0
     "config1_fused": dict(sources=("chunk_fused.hip", "chunk_common.hpp", "mfma.hpp"),
-                          fetch_kib=421.0 + 28165.2, write_kib=6432.0 + 20480.0,
-                          sha256="6974036122debe9ff2a7e566310281d9"
-                          "cf59d301d216a22c7c443e2b7b4b602e"),
-    "config3_row_split": dict(sources=("chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
-                              fetch_kib=68481.0 + 134236.5, write_kib=71793.0 + 67584.0,
-                              sha256=_SPLIT_SHA),
-    "config3_row_split_no_mu": dict(sources=("chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
-                                    fetch_kib=67515.0 + 134215.5, write_kib=71782.0 + 67584.0,
-                                    sha256=_SPLIT_SHA),
+                          fetch_kib=421.0 + 28161.1, write_kib=6432.0 + 20480.0,
+                          sha256=_FUSED_SHA),
+    "config3_segments": dict(sources=("chunk_fused.hip", "chunk_common.hpp", "mfma.hpp"),
+                             fetch_kib=1573.0 + 89964.5 + 7219.5 + 87071.3,
+                             write_kib=25728.3 + 30720.0 + 4096.0 + 51200.0, sha256=_FUSED_SHA),
+    "config3_segments_no_mu": dict(sources=("chunk_fused.hip", "chunk_common.hpp", "mfma.hpp"),
+                                   fetch_kib=1061.0 + 90976.2 + 3618.0 + 91258.6,
+                                   write_kib=25728.3 + 20480.0 + 3072.0 + 54272.0,
+                                   sha256=_FUSED_SHA),
     "decode_step_kernel": dict(sources=("decode.hip", "mfma.hpp"), fetch_kib=264109.0,
                                write_kib=525524.5, sha256="8fa39113008b99235e1abe57028f0d81"
                                "9b837f475aa87000a6b4e46e3ea6c4e5"),
@@ -173,7 +175,7 @@ TRAFFIC = {
 # ran, beside the FLOP-derived fraction of the datasheet peak.
 MFMA_BUSY = {
     "chunk_fwd_fused_kernel": dict(sources=TRAFFIC["chunk_fwd_fused_kernel"]["sources"],
-                                   busy=0.389, sha256=TRAFFIC["chunk_fwd_fused_kernel"]["sha256"]),
+                                   busy=0.390, sha256=TRAFFIC["chunk_fwd_fused_kernel"]["sha256"]),
     "chunk_scan_bf16_kernel": dict(sources=TRAFFIC["chunk_scan_bf16_kernel"]["sources"],
                                    busy=0.300, sha256=_SPLIT_SHA),
     "chunk_prep_kernel": dict(sources=TRAFFIC["chunk_prep_kernel"]["sources"], busy=0.107,
