@@ -10,9 +10,12 @@ the shape does segment (mdn_fwd_segment_count >= 3), then compares O, S_T
 and M_T element by element with the oracle at the bf16 bound of parity.py:
 ragged lengths (a partial last chunk, a short last segment), every head-size
 pair, nonzero entry states, mu given and mu NULL, beta, two batch rows; the
-long-context layer B1 H16 T16384 d128 in full (runs A and B); state passing,
-in-place final states, bitwise determinism, and the residual request, which
-the segment scan leaves to the column tiles.
+long-context layer B1 H16 T16384 d128 in full (runs A and B, and with slowly
+forgetting gates); gates that forget slowly at small shapes, where the oracle
+first shows that each segment's entry state moves its outputs far beyond the
+bound; state passing, in-place final states, bitwise determinism, the exact
+workspace, and the residual request, which the segment scan leaves to the
+column tiles.
 """
 import dataclasses
 
@@ -79,7 +82,8 @@ def test_segments_mu_null_and_beta(dk, dv):
 
 def test_segments_long_context():
     """B1 H16 T16384 d128, every head: run A as drawn, run B with mu = 0 (mu
-    given as zeros, and mu NULL)."""
+    given as zeros, and mu NULL), and run A's inputs with gates that forget
+    slowly (alpha in [0.999, 1], eta in [0.01, 0.05])."""
     cfg = si.CONFIGS[3]
     n = segmented(cfg)
     inp = si.make_forward(cfg)
@@ -91,6 +95,15 @@ def test_segments_long_context():
     check(gpu_forward(inp, mu=mu0), ref0, "T16384 run B (mu = 0) all heads")
     n0 = segmented(cfg, with_mu=False)
     check(gpu_forward(inp, mu_null=True), ref0, f"T16384 run B (mu NULL) all heads, {n0} segments")
+    # The workload's gates forget a state within a segment (the result is then
+    # the column tiles' bits); with gates that forget slowly every segment's
+    # entry state matters, and the maps and their chain decide the result.
+    rng = np.random.default_rng(cfg.seed + 1)
+    slow = dict(inp)
+    slow["alpha"] = rng.uniform(0.999, 1.0, size=inp["alpha"].shape).astype(np.float32)
+    slow["eta"] = rng.uniform(0.01, 0.05, size=inp["eta"].shape).astype(np.float32)
+    print("long context: slow gates", flush=True)
+    check(gpu_forward(slow), oracle_forward(slow), f"T16384 slow gates all heads, {n} segments")
 
 
 @pytest.mark.parametrize("T1", [1600, 1664])
@@ -186,3 +199,46 @@ def test_segments_plan():
     O, ST, MT = mdn.chunk_fwd(*args)
     torch.cuda.synchronize()
     assert torch.equal(plan.O, O) and torch.equal(plan.S_T, ST) and torch.equal(plan.M_T, MT)
+
+
+CARRY = [(dk, dv, mu_null) for (dk, dv) in ((128, 128), (64, 64), (128, 64)) for mu_null in (False, True)]
+
+
+@pytest.mark.parametrize("dk,dv,mu_null", CARRY,
+                         ids=[f"dk{a}-dv{b}-{'mu_null' if c else 'mu'}" for a, b, c in CARRY])
+def test_segments_carry_across_segments(dk, dv, mu_null):
+    """Gates that forget slowly (alpha in [0.999, 1], eta in [0.01, 0.05]),
+    so that every segment's entry state shapes its outputs: the state maps
+    and their chain decide the result.  With the workload's own gates a
+    state fades within a segment and the segment scan gives the column
+    tiles' bits.  The oracle first shows that dropping the entry state of
+    the segments after the first changes their outputs by far more than the
+    bound; then the GPU matches the oracle, and differs from the column
+    tiles only by rounding."""
+    cfg = dataclasses.replace(si.CONFIGS[1], B=1, T=2600, H=2, Dk=dk, Dv=dv, io_dtype="bf16",
+                              init_state_std=0.3, seed=7900 + dk + dv + int(mu_null))
+    n = segmented(cfg, with_mu=not mu_null)
+    inp = si.make_forward(cfg)
+    rng = np.random.default_rng(cfg.seed)
+    inp["alpha"] = rng.uniform(0.999, 1.0, size=inp["alpha"].shape).astype(np.float32)
+    inp["eta"] = rng.uniform(0.01, 0.05, size=inp["eta"].shape).astype(np.float32)
+    mu = np.zeros_like(inp["mu"]) if mu_null else None
+    ref = oracle_forward(inp, mu=mu)
+    # the tail from the second segment on, run from a zero state instead
+    nc = -(-cfg.T // 64)
+    t1 = 64 * -(-nc // n)
+    tok = ("q", "k", "v", "alpha", "mu", "eta")
+    tail = {key: (val[:, t1:] if key in tok else None if key in ("S0", "M0") else val)
+            for key, val in inp.items()}
+    tail_ref = oracle_forward(tail, mu=None if mu is None else mu[:, t1:])
+    gap = float(np.abs(tail_ref[0] - ref[0][:, t1:]).max())
+    print(f"[carry, {n} segments] dropping the entry at token {t1} moves O by {gap:.3e}")
+    assert gap > 0.1
+    got = gpu_forward(inp, mu_null=mu_null)
+    check(got, ref, f"segments ({n}), slow gates, dk{dk} dv{dv}{' mu NULL' if mu_null else ''}")
+    with mdn.fwd_path("column_tiles"):
+        tiles = gpu_forward(inp, mu_null=mu_null)
+    for name, a, b in zip(("O", "S_T", "M_T"), got, tiles):
+        d = float(np.abs(a.astype(np.float64) - b).max())
+        print(f"  {name} segments vs column tiles: {d:.3e}")
+        assert d <= 2e-2 * max(1.0, float(np.abs(b).max()))
