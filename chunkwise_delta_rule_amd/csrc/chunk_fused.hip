@@ -376,25 +376,26 @@ struct KQLayout {
     }
 };
 
-// LDS of the fused kernel.  Q, the V tile, T, A and the coefficient rows of
-// a chunk live in operand buffer c & 1; K in K buffer c % 3, since the
-// helpers store a chunk's K rows a round before they build its Gram products
-// from them (so that no helper waits for another's rows); the tables of a
-// chunk in table set c & 1.
+// LDS of the fused kernel.  The V tile, T, A and the coefficient rows of a
+// chunk live in operand buffer c & 1; K and Q in K/Q buffer c % 3: the
+// helpers' direct loads of chunk c + 1's rows land while the compute
+// wavefronts read chunk c - 1's and the helpers build chunk c's Gram
+// products from chunk c's.  The tables of a chunk in table set c & 1.
 template <int DK>
 struct FusedLayout {
     using LK = KQLayout<DK>;                // K, Q: 64 rows x DK
     using LC = TileLayout<CH * 2>;          // V tile: 64 rows x 64
-    static constexpr int OFF_Q = 0;
-    static constexpr int OFF_V = LK::BYTES;
+    static constexpr int OFF_V = 0;
     static constexpr int OFF_T = OFF_V + LC::BYTES;
     static constexpr int OFF_A = OFF_T + FRAG_AREA;
     static constexpr int OFF_VEC = OFF_A + FRAG_AREA;
     static constexpr int BUF = OFF_VEC + 6 * CH * 4;
     static constexpr int OFF_K = 2 * BUF;                 // three K buffers
+    static constexpr int OFF_Q = OFF_K + 3 * LK::BYTES;   // three Q buffers
     static constexpr int TB_BYTES = ChunkTables::LDS_FLOATS * 4;
-    static constexpr int OFF_TB = OFF_K + 3 * LK::BYTES;  // two table sets
+    static constexpr int OFF_TB = OFF_Q + 3 * LK::BYTES;  // two table sets
     static constexpr int BYTES = OFF_TB + 2 * TB_BYTES;
+    static_assert(BYTES <= 160 * 1024, "LDS of one workgroup");
 };
 
 // The segment scan (layers with few heads).  The sequence is cut into nseg
@@ -461,6 +462,7 @@ __device__ __forceinline__ void fused_body(
         return reinterpret_cast<float*>(smem + L::OFF_TB + (c & 1) * L::TB_BYTES);
     };
     auto kbuf = [&](int c) { return smem + L::OFF_K + (c % 3) * LK::BYTES; };
+    auto qbuf = [&](int c) { return smem + L::OFF_Q + (c % 3) * LK::BYTES; };
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -504,8 +506,6 @@ __device__ __forceinline__ void fused_body(
     // the V tile the helpers stage (a transition's identity columns have no
     // V; they stage tile 0, which the compute waves then ignore)
     const int vtile = tile < NTILE ? tile : 0;
-    // local index of the sequence's last chunk
-    const int lastl = NC - 1 - c0;
     // token index of row 0 of local chunk c of this head (rows are H tokens apart)
     auto tok_base = [&](int c) { return ((size_t)b * T + (size_t)(c0 + c) * CH) * H + h; };
     auto chunk_rows = [&](int c) { return min(CH, T - (c0 + c) * CH); };
@@ -517,11 +517,7 @@ __device__ __forceinline__ void fused_body(
         // and Q rows of block X into registers, one chunk ahead, and stores
         // them to LDS for everyone.
         const int hw = wave - 4;
-        const int rK = 16 * hw, rQ = 16 * (3 - hw);   // its K and Q rows
-        MM::frag kf[SK];                        // K rows of block W, next to store
-        MM::frag qf[2][SK];                     // Q rows of block X; set = chunk parity
         const unsigned v_lane = LC::lane_offset((unsigned)(H * DV), lane);
-        const MM::frag zfrag = __builtin_bit_cast(MM::frag, u32x4{0u, 0u, 0u, 0u});
         // 16x16 product X Y from acc(X^T) and acc(Y), where acc(Z) is the
         // accumulator layout (lane (l16, g), element r = Z[4 g + r][l16]): the
         // A operand of a 16x16x16 step is then acc(X^T) and the B operand
@@ -529,47 +525,53 @@ __device__ __forceinline__ void fused_body(
         auto prod = [](const f32x4& XT, const f32x4& YB) {
             return mma16(to_bf4(XT), to_bf4(YB), zero4());
         };
-        // byte offsets of this lane's K and Q rows inside a chunk, for full
-        // chunks and for a partial last chunk (whose rows past its end repeat
-        // its last row); 32-bit offsets from a uniform base let the loads use
-        // the scalar-base address form
+        // K and Q rows reach LDS by direct loads.  A K/Q tile is NWIN windows
+        // of 1 KB; helper W takes windows W, W + 4, ...  Lane l of window w
+        // fills tile bytes 1024 w + 16 l, which are one 16-byte slot of one
+        // row of the padded, XOR-permuted layout, so it reads the logical
+        // chunk stored in that slot (a slot past a row's data is padding: it
+        // reads the row's first chunk and is never read back).  Rows past a
+        // partial last chunk read its last row: their Gram entries reach only
+        // the Vt and O rows past its end, which no output and no state update
+        // uses (the coefficient rows and state weights vanish there).
+        constexpr int NWIN = LK::BYTES / 1024;
+        constexpr int NWH = (NWIN + 3) / 4;
+        static_assert(LK::BYTES % 1024 == 0, "whole windows");
         const unsigned rowbytes = (unsigned)(H * DK) * 2u;
-        const int n_last = T - (NC - 1) * CH;
-        auto row_off = [&](int r) { return (unsigned)r * rowbytes + 16u * (unsigned)lg; };
-        const unsigned offK = row_off(rK + l16), offQ = row_off(rQ + l16);
-        const unsigned offK_last = row_off(min(rK + l16, n_last - 1));
-        const unsigned offQ_last = row_off(min(rQ + l16, n_last - 1));
-        auto load_k = [&](int c) {
-            const char* src = reinterpret_cast<const char*>(k + tok_base(c) * DK);
-            const unsigned o = c == lastl ? offK_last : offK;
-#pragma unroll
-            for (int u = 0; u < SK; ++u) kf[u] = *reinterpret_cast<const MM::frag*>(src + o + 64 * u);
+        struct KQLane {
+            unsigned off[NWH];   // source byte offset of the lane's slot in a whole chunk
+            int row[NWH];        // its row
         };
-        auto load_q = [&](int c, auto par) {
-            constexpr int P = decltype(par)::value;
-            const char* src = reinterpret_cast<const char*>(q + tok_base(c) * DK);
-            const unsigned o = c == lastl ? offQ_last : offQ;
+        auto kq_lane = [&](auto wc) {
+            constexpr int W = decltype(wc)::value;
+            KQLane kl;
 #pragma unroll
-            for (int u = 0; u < SK; ++u) qf[P][u] = *reinterpret_cast<const MM::frag*>(src + o + 64 * u);
-        };
-        // rows >= n of a partial last chunk become zero (in the registers
-        // too), so that the Gram products, L and A vanish there
-        auto zero_tail = [&](int c, int r0, MM::frag* f) {
-            const int n = chunk_rows(c);
-            if (n < CH) {
-                const bool live = r0 + l16 < n;
-#pragma unroll
-                for (int u = 0; u < SK; ++u) f[u] = live ? f[u] : zfrag;
+            for (int u = 0; u < NWH; ++u) {
+                const int o = 1024 * (W + 4 * u) + 16 * lane;
+                const int row = min(o / LK::STRIDE, CH - 1);
+                const int p = (o - row * LK::STRIDE) / 16;
+                const int qc = p < DK / 8 ? p ^ ((row >> 2) & 3) : 0;
+                kl.row[u] = row;
+                kl.off[u] = (unsigned)row * rowbytes + 16u * (unsigned)qc;
             }
+            return kl;
         };
-        // the rows' LDS offsets: rows 16 apart share the swizzle, and d-chunk
-        // 4 u + lg lies 64 u bytes after d-chunk lg, so one lane offset plus
-        // immediates covers the four stores; the buffer's base is added once
-        const int stK = LK::chunk(rK + l16, lg), stQ = LK::chunk(rQ + l16, lg);
-        auto store_rows = [&](const char* dst, int st, const MM::frag* f) {
-            const int a = opaque((int)(dst - smem) + st);
+        // direct loads of chunk c's rows of K or Q (base) into tile dst
+        auto load_kq = [&](auto wc, const KQLane& kl, const E* base, int c, char* dst) {
+            constexpr int W = decltype(wc)::value;
+            const char* src = reinterpret_cast<const char*>(base + tok_base(c) * DK);
+            const int n = chunk_rows(c);
+            unsigned o[NWH];
 #pragma unroll
-            for (int u = 0; u < SK; ++u) *reinterpret_cast<MM::frag*>(smem + a + 64 * u) = f[u];
+            for (int u = 0; u < NWH; ++u) o[u] = kl.off[u];
+            if (n < CH) {
+#pragma unroll
+                for (int u = 0; u < NWH; ++u)
+                    o[u] = kl.off[u] - (unsigned)max(kl.row[u] - (n - 1), 0) * rowbytes;
+            }
+#pragma unroll
+            for (int u = 0; u < NWH; ++u)
+                if (W + 4 * u < NWIN) direct_load16(src + o[u], dst + 1024 * (W + 4 * u));
         };
         // direct loads of chunk c's V tile and coefficient rows into buffer B
         auto load_v = [&](int c, char* B) {
@@ -690,15 +692,13 @@ __device__ __forceinline__ void fused_body(
         };
 
         // Row block W of L (-N_{W,J}, J < W, and D_W) into T, row block X
-        // of A into A, for the chunk whose K tile is Kt and Q rows (block X)
-        // are in qf[P]; W is this helper's index, a compile-time constant in
-        // each copy.
-        auto prepare = [&](auto wc, char* B, const char* Kt, const Mult& m, const f32x4& Id,
-                           auto par) {
+        // of A into A, for the chunk whose K and Q tiles are Kt and Qt; W is
+        // this helper's index, a compile-time constant in each copy.
+        auto prepare = [&](auto wc, char* B, const char* Kt, const char* Qt, const Mult& m,
+                           const f32x4& Id) {
             constexpr int W = decltype(wc)::value;
             constexpr int X = 3 - W;
             constexpr int JN = W > X ? W : X;     // K blocks 0 .. JN are read
-            constexpr int P = decltype(par)::value;
             // ---- Gram tiles, transposed (lane: row 16 x + l16, columns 16 J + 4 lg + r)
             f32x4 Gt[W + 1], At[X + 1];
 #pragma unroll
@@ -711,10 +711,12 @@ __device__ __forceinline__ void fused_body(
 #pragma unroll
                 for (int J = 0; J <= JN; ++J)
                     aK[J] = *reinterpret_cast<const MM::frag*>(Kt + LK::chunk(16 * J + l16, 4 * s + lg));
+                const MM::frag aQ =
+                    *reinterpret_cast<const MM::frag*>(Qt + LK::chunk(16 * X + l16, 4 * s + lg));
 #pragma unroll
                 for (int J = 0; J <= W; ++J) Gt[J] = MM::mma(aK[J], aK[W], Gt[J]);
 #pragma unroll
-                for (int J = 0; J <= X; ++J) At[J] = MM::mma(aK[J], qf[P][s], At[J]);
+                for (int J = 0; J <= X; ++J) At[J] = MM::mma(aK[J], aQ, At[J]);
             }
             // N_WW in both accumulator layouts from the symmetric Gram tile:
             // NT = acc(N^T) (lane: row l16, cols 4 lg + r), NB = acc(N)
@@ -739,70 +741,39 @@ __device__ __forceinline__ void fused_body(
         };
 
         // The pipeline: in round c (c = -1 .. NC - 1) chunk nx = c + 1 is
-        // prepared into buffer nx & 1 while the compute wavefronts scan chunk
-        // c.  At the start of the round the registers hold the K rows of
-        // nx + 1 and the Q rows of nx, loaded in round c - 1; the K tile of
-        // nx is in LDS since round c - 1 and the tables of nx since its B0.
-        // Per helper and round the loads are issued as: tables of nx + 1, V
-        // tile and coefficient rows of nx, then the register loads (K rows of
-        // nx + 2, Q rows of nx + 1), so waiting for all but the register loads
-        // covers everything nx needs.
+        // prepared into operand buffer nx & 1 while the compute wavefronts
+        // scan chunk c.  At the start of the round the K and Q tiles and the
+        // tables of nx are in LDS (loaded in round c - 1).  The round issues
+        // the direct loads of the tables, K and Q rows of nx + 1 and of the V
+        // tile and coefficient rows of nx, builds nx's T and A, and waits for
+        // its loads before the barrier: everything the next round reads has
+        // then landed.
         auto run = [&](auto wc) {
             const MultLane ml = mult_lane(wc);
+            const KQLane kl = kq_lane(wc);
             auto round = [&](int c, auto par) {      // par: parity of nx
                 constexpr int P = decltype(par)::value;
                 const int nx = c + 1;
                 char* B = smem + P * L::BUF;
-                // one branch for the whole of a live round, so that the
-                // compiler sees prepare() reached only through the wait below
-                // (a path around it would make it wait for every load)
                 if (nx < NCL) {
-                    const bool more = nx + 1 < NCL, more2 = nx + 2 < NCL;
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                    if (more) {
-                        zero_tail(nx + 1, rK, kf);
-                        store_rows(kbuf(nx + 1), stK, kf);
+                    if (nx + 1 < NCL) {
+                        load_tables(nx + 1);
+                        load_kq(wc, kl, k, nx + 1, kbuf(nx + 1));
+                        load_kq(wc, kl, q, nx + 1, qbuf(nx + 1));
                     }
-                    zero_tail(nx, rQ, qf[P]);
-                    store_rows(B + L::OFF_Q, stQ, qf[P]);
-                    if (more) load_tables(nx + 1);
                     load_v(nx, B);
-                    // keep the register loads after the direct loads: the
-                    // wait below counts on that order
-                    asm volatile("" ::: "memory");
-                    if (more2) load_k(nx + 2);
-                    if (more) load_q(nx + 1, IConst<1 - P>{});
                     const Mult m = multipliers(wc, tables(nx), ml);
-                    prepare(wc, B, kbuf(nx), m, ml.id, par);
-                    // the tables of nx + 1, the V tile and coefficient rows of
-                    // nx have landed; the register loads, issued after them,
-                    // may still be in flight
-                    if (more2) {
-                        if constexpr (SK == 4)
-                            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-                        else
-                            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-                    } else if (more) {
-                        if constexpr (SK == 4)
-                            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-                        else
-                            asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-                    } else {
-                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                    }
+                    prepare(wc, B, kbuf(nx), qbuf(nx), m, ml.id);
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 }
                 lds_barrier();   // B0: chunk nx ready
             };
-            // K tile of chunk 0, then the registers for round -1
-            load_k(0);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            zero_tail(0, rK, kf);
-            store_rows(kbuf(0), stK, kf);
-            if (NCL > 1) load_k(1);
-            load_q(0, IConst<0>{});
+            // the K, Q tiles and tables of chunk 0
+            load_kq(wc, kl, k, 0, kbuf(0));
+            load_kq(wc, kl, q, 0, qbuf(0));
             load_tables(0);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            lds_barrier();       // chunk 0's K tile and tables visible
+            lds_barrier();       // chunk 0's K, Q tiles and tables visible
             for (int c = -1; c < NCL; c += 2) {
                 round(c, IConst<0>{});
                 if (c + 1 < NCL) round(c + 1, IConst<1>{});
@@ -923,7 +894,7 @@ __device__ __forceinline__ void fused_body(
         const int n = min(CH, T - t0);
         const char* B = smem + (c & 1) * L::BUF;
         const char* Kb = kbuf(c);
-        const char* Qb = B + L::OFF_Q;
+        const char* Qb = qbuf(c);
         const char* Vb = B + L::OFF_V;
         const char* Tb = B + L::OFF_T;
         const char* Ab = B + L::OFF_A;
