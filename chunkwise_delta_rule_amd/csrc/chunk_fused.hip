@@ -900,6 +900,13 @@ __device__ __forceinline__ void fused_body(
         const char* Ab = B + L::OFF_A;
         const float* vec = reinterpret_cast<const float*>(B + L::OFF_VEC);
 
+        // The chunk's products on the state and the substitution are each
+        // scheduled by the compiler's single-wave small-GEMM interleaving
+        // (LDS reads hoisted ahead of the MFMAs that take them, vector work
+        // placed between independent MFMAs): measured 4-5% faster per call
+        // than its default schedule at 1.3B-like, 400M-like and 16K-context
+        // shapes, bit-identical.
+        __builtin_amdgcn_iglp_opt(1);
         // (1) X = K [S | M]
         f32x4 R[4];
         {
@@ -960,6 +967,7 @@ __device__ __forceinline__ void fused_body(
             }
         }
 
+        __builtin_amdgcn_iglp_opt(1);
         // (4) Vt = L^{-1} R by block substitution; T's blocks: D on the
         //     diagonal, -N below it (pairs read as one 16-byte access)
         f32x4 Vt[4];
