@@ -399,7 +399,8 @@ struct FusedLayout {
 };
 
 // The segment scan (layers with few heads).  The sequence is cut into nseg
-// segments of ncs chunks (the last may be shorter).  The state map of a
+// segments: segment 0 of ncs0 chunks, the others of ncs (the last may be
+// shorter; see seg_lengths for why segment 0 is shorter).  The state map of a
 // segment is affine: its exit pair (S, M) is its exit pair from a zero entry
 // (the local part) plus a linear map Phi_s of its entry pair, and Phi_s is
 // found by running the chunk recurrence with V = 0 from the columns of the
@@ -407,8 +408,8 @@ struct FusedLayout {
 // beside the local parts and maps of segments 1 .. nseg - 2; a small kernel
 // then composes the entry states of segments 2 .. nseg - 1; pass B runs
 // segments 1 .. nseg - 1 from those entries, with outputs.  Each pass is
-// one round of workgroups, each walking ncs chunks instead of the whole
-// sequence.
+// one round of workgroups, each walking at most ncs chunks instead of the
+// whole sequence.
 //
 // A workgroup of a segment launch either runs segment s with outputs
 // (workgroups 0 .. nout - 1: tile, head, segment, batch row, fastest first)
@@ -418,7 +419,8 @@ struct FusedLayout {
 // of Phi_s: DK columns from the entry S = e_j, M = 0, and with momentum DK
 // more from S = 0, M = e_j.
 struct SegArgs {
-    int ncs;              // chunks per segment
+    int ncs;              // chunks per segment (the last may have fewer)
+    int ncs0;             // chunks of segment 0 (at most ncs)
     int nseg;
     int out_s0, out_ns;   // the segments run with outputs
     unsigned nout;        // workgroups of those segments
@@ -499,8 +501,8 @@ __device__ __forceinline__ void fused_body(
             seg = sg.tr_s0 + (int)(r % (unsigned)sg.tr_ns);
             b = (int)(r / (unsigned)sg.tr_ns);
         }
-        c0 = seg * sg.ncs;
-        NCL = min(sg.ncs, NC - c0);
+        c0 = seg == 0 ? 0 : sg.ncs0 + (seg - 1) * sg.ncs;
+        NCL = seg == 0 ? sg.ncs0 : min(sg.ncs, NC - c0);
     }
     const int bh = b * H + h;
     // the V tile the helpers stage (a transition's identity columns have no
@@ -698,7 +700,8 @@ __device__ __forceinline__ void fused_body(
                            const f32x4& Id) {
             constexpr int W = decltype(wc)::value;
             constexpr int X = 3 - W;
-            constexpr int JN = W > X ? W : X;     // K blocks 0 .. JN are read
+            // K blocks 0 .. JN are read (a transition forms no A: it has no outputs)
+            constexpr int JN = TRANS ? W : W > X ? W : X;
             // ---- Gram tiles, transposed (lane: row 16 x + l16, columns 16 J + 4 lg + r)
             f32x4 Gt[W + 1], At[X + 1];
 #pragma unroll
@@ -711,12 +714,14 @@ __device__ __forceinline__ void fused_body(
 #pragma unroll
                 for (int J = 0; J <= JN; ++J)
                     aK[J] = *reinterpret_cast<const MM::frag*>(Kt + LK::chunk(16 * J + l16, 4 * s + lg));
-                const MM::frag aQ =
-                    *reinterpret_cast<const MM::frag*>(Qt + LK::chunk(16 * X + l16, 4 * s + lg));
 #pragma unroll
                 for (int J = 0; J <= W; ++J) Gt[J] = MM::mma(aK[J], aK[W], Gt[J]);
+                if constexpr (!TRANS) {
+                    const MM::frag aQ =
+                        *reinterpret_cast<const MM::frag*>(Qt + LK::chunk(16 * X + l16, 4 * s + lg));
 #pragma unroll
-                for (int J = 0; J <= X; ++J) At[J] = MM::mma(aK[J], aQ, At[J]);
+                    for (int J = 0; J <= X; ++J) At[J] = MM::mma(aK[J], aQ, At[J]);
+                }
             }
             // N_WW in both accumulator layouts from the symmetric Gram tile:
             // NT = acc(N^T) (lane: row l16, cols 4 lg + r), NB = acc(N)
@@ -734,10 +739,12 @@ __device__ __forceinline__ void fused_body(
 #pragma unroll
             for (int J = 0; J < W; ++J) tW[J] = to_bf4(m.mL[J] * Gt[J]);
             tW[W] = to_bf4(DT);
-#pragma unroll
-            for (int J = 0; J <= X; ++J) aX[J] = to_bf4(m.mA[J] * At[J]);
             store_block_row(IConst<W>{}, B + L::OFF_T, tW);
-            store_block_row(IConst<X>{}, B + L::OFF_A, aX);
+            if constexpr (!TRANS) {
+#pragma unroll
+                for (int J = 0; J <= X; ++J) aX[J] = to_bf4(m.mA[J] * At[J]);
+                store_block_row(IConst<X>{}, B + L::OFF_A, aX);
+            }
         };
 
         // The pipeline: in round c (c = -1 .. NC - 1) chunk nx = c + 1 is
@@ -759,7 +766,7 @@ __device__ __forceinline__ void fused_body(
                     if (nx + 1 < NCL) {
                         load_tables(nx + 1);
                         load_kq(wc, kl, k, nx + 1, kbuf(nx + 1));
-                        load_kq(wc, kl, q, nx + 1, qbuf(nx + 1));
+                        if constexpr (!TRANS) load_kq(wc, kl, q, nx + 1, qbuf(nx + 1));
                     }
                     load_v(nx, B);
                     const Mult m = multipliers(wc, tables(nx), ml);
@@ -770,7 +777,7 @@ __device__ __forceinline__ void fused_body(
             };
             // the K, Q tiles and tables of chunk 0
             load_kq(wc, kl, k, 0, kbuf(0));
-            load_kq(wc, kl, q, 0, qbuf(0));
+            if constexpr (!TRANS) load_kq(wc, kl, q, 0, qbuf(0));
             load_tables(0);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_barrier();       // chunk 0's K, Q tiles and tables visible
@@ -1352,6 +1359,33 @@ int chunk_seg_count(int B, int T, int H, int Dk, int Dv, bool mom, int min_ncs)
 }
 
 namespace {
+// Segment lengths: segment 0 runs in pass A beside the transitions of the
+// middle segments, which form no outputs (no A, no Q products, no stores) and
+// so walk a chunk faster than a workgroup with outputs; segment 0 is made
+// shorter by the ratio below so that pass A ends about when its transitions
+// do, and the other segments share the rest.  Measured on MI355X (d = 128)
+// over ratios 0.4 .. 1.0: with mu, 0.7 at B1 H16 T16384 (268.6 -> 247.3 us)
+// and 0.65-0.7 at B2 H16 T8192; without mu, 0.6 at both (207.6 -> 185.6 us
+// at T16384).  ncs: chunks of segments 1 .. nseg - 2 (the last takes the
+// rest, at most ncs); ncs0: chunks of segment 0.
+constexpr double SEG0_RATIO_MOM = 0.7;
+constexpr double SEG0_RATIO_NOMOM = 0.6;
+void seg_lengths(int NC, int nseg, bool mom, int& ncs, int& ncs0)
+{
+    const double ratio = mom ? SEG0_RATIO_MOM : SEG0_RATIO_NOMOM;
+    ncs = ncs0 = (NC + nseg - 1) / nseg;   // equal lengths, if no other fits
+    for (int L = (int)(NC / (nseg - 1 + ratio)); L <= NC; ++L) {
+        const int r = (int)(ratio * L + 0.5);
+        const int L0 = r < 1 ? 1 : r > L ? L : r;
+        const int rest = NC - L0 - (nseg - 2) * L;   // the last segment's chunks
+        if (rest > L) continue;
+        if (rest >= 1) {
+            ncs = L;
+            ncs0 = L0;
+        }
+        break;
+    }
+}
 struct SegSizes {
     size_t ctab, states, trans;   // bytes, each a multiple of 256
 };
@@ -1389,7 +1423,7 @@ static hipError_t launch_seg_t(const void* q, const void* k, const void* v, cons
     char* w = static_cast<char*>(workspace);
     float* ctab = reinterpret_cast<float*>(w);
     SegArgs sg{};
-    sg.ncs = (NC + nseg - 1) / nseg;
+    seg_lengths(NC, nseg, mom, sg.ncs, sg.ncs0);
     sg.nseg = nseg;
     sg.ncol = DV + (mom ? 2 : 1) * DK;
     sg.Sx = reinterpret_cast<float*>(w + z.ctab);
