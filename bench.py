@@ -650,7 +650,7 @@ def bench_configs(args, torch, si, mdn):
     and with no mu (the gated delta rule on the same inputs).  Each is timed
     under the three partitions of the state (column tiles, row split, segment
     scan); `us_per_step` is the one the default rule picks (the segment scan
-    where three or more segments of at least 16 chunks fit, else the row
+    where three or more segments of at least 16 chunks fit (8 with no mu), else the row
     split up to 32 tiles of 64 value columns, else the column tiles)."""
     bf, f32 = torch.bfloat16, torch.float32
     out = {}

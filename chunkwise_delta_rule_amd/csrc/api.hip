@@ -120,9 +120,12 @@ bool row_split_for(int B, int H, int Dv, mdn_dtype dt, bool want_vt)
 // segments of at least this many chunks.  Measured on MI355X (d = 128): with
 // 16 to 64 chunks per segment it took 0.11 to 0.9 of the best other path's
 // time (at B1 H16: T4096 0.90, T16384 0.67, with mu = 0 0.69 and 0.59; at
-// B1 H2 T65536 0.23), with 8 to 11 it was up to 1.16 times slower (B1 H16
-// T2048, B4 H8 T2048).
+// B1 H2 T65536 0.23).  With 8 to 11 chunks per segment (B1 H16 T2048, B4 H8
+// T2048) it took 0.97 and 1.02 of the best other path's time with mu, and
+// 0.84 and 0.90 without (a transition without momentum has a third fewer
+// columns), so without mu the bar is lower.
 constexpr int SEG_AUTO_MIN_CHUNKS = 16;
+constexpr int SEG_AUTO_MIN_CHUNKS_NO_MU = 8;
 constexpr int SEG_MIN_CHUNKS = 8;   // MDN_FWD_SEGMENTS
 
 // The number of segments when a bf16 forward of this shape runs the segment
@@ -133,8 +136,9 @@ int segments_for(int B, int T, int H, int Dk, int Dv, mdn_dtype dt, bool want_vt
     if (!head_dim_ok(Dk) || !head_dim_ok(Dv)) return 0;
     const int p = fwd_path.load(std::memory_order_relaxed);
     if (p != MDN_FWD_SEGMENTS && p != MDN_FWD_AUTO) return 0;
+    const int auto_min = mom ? SEG_AUTO_MIN_CHUNKS : SEG_AUTO_MIN_CHUNKS_NO_MU;
     const int n = mdn::chunk_seg_count(B, T, H, Dk, Dv, mom,
-                                       p == MDN_FWD_AUTO ? SEG_AUTO_MIN_CHUNKS : SEG_MIN_CHUNKS);
+                                       p == MDN_FWD_AUTO ? auto_min : SEG_MIN_CHUNKS);
     return n >= 3 ? n : 0;
 }
 

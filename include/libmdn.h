@@ -99,11 +99,12 @@ typedef enum {
  *                         than 24 chunks) the column tiles run.  It does not
  *                         produce the residuals (Vt != NULL: column tiles).
  *   MDN_FWD_AUTO          (the default) the segment scan where three or more
- *                         segments of at least 16 chunks fit (few heads and
- *                         long sequences; measured on MI355X at d = 128 it
- *                         took 0.23 to 0.90 of the other paths' time there,
- *                         and up to 1.16 times theirs with 8 to 11 chunks per
- *                         segment); otherwise the row split when the layer
+ *                         segments of at least 16 chunks fit, at least 8
+ *                         with mu NULL (few heads and long sequences;
+ *                         measured on MI355X at d = 128 it took 0.23 to 0.90
+ *                         of the other paths' time there; with mu and 8 to
+ *                         11 chunks per segment about as long as theirs,
+ *                         without mu 0.84 to 0.90); otherwise the row split when the layer
  *                         has at most 32 column tiles, B * H * (Dv / 64) <=
  *                         32, where it measured faster than the column tiles
  *                         (at 64 tiles the two are about even, at 128 the

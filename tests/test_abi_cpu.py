@@ -87,7 +87,7 @@ def test_segment_scan_choice_and_workspace(lib):
     round of 256 workgroups -- pass 1: the heads' Dv/64 tiles plus nseg - 2
     transitions of Dv/64 + 2 Dk/64 tiles (Dk/64 without mu), pass 2: nseg - 1
     segments' tiles -- and ceil(NC / nseg) >= 16 chunks per segment under
-    MDN_FWD_AUTO, >= 8 under MDN_FWD_SEGMENTS.  Its workspace: the
+    MDN_FWD_AUTO (>= 8 with mu NULL), >= 8 under MDN_FWD_SEGMENTS.  Its workspace: the
     coefficient tables (1664 floats per chunk), entry states of every segment
     (S and M), exit states of the nseg - 2 transitions (S and M, Dv + 2 Dk
     columns, Dv + Dk without mu), fp32."""
@@ -96,7 +96,10 @@ def test_segment_scan_choice_and_workspace(lib):
     assert count(1, 16384, 16, 128, 128, 1) == 4      # 32 + 2 * 96 = 224 workgroups
     assert count(1, 16384, 16, 128, 128, 0) == 5      # 32 + 3 * 64 = 224
     assert count(4, 2048, 8, 128, 128, 1) == 0        # 3 segments of 11 chunks: auto declines
+    assert count(4, 2048, 8, 128, 128, 0) == 3        # ... but not without mu
     assert count(1, 2048, 16, 128, 128, 1) == 0
+    assert count(1, 2048, 16, 128, 128, 0) == 4        # 4 segments of 8 chunks without mu
+    assert count(1, 1024, 16, 128, 128, 0) == 0        # 16 chunks: too few for 3 segments of 8
     assert count(8, 4096, 16, 128, 128, 1) == 0       # 256 tiles
     assert count(1, 65536, 2, 128, 128, 1) == 23      # 4 + 21 * 12 = 256
     assert count(1, 16384, 16, 128, 128, 1) == lib.mdn_fwd_segment_count(1, 16384, 16, 128, 128, 1)
