@@ -112,13 +112,13 @@ WRITE_FACTOR = 131072.0 / 131072.0
 CSRC = os.path.join(ROOT, "chunkwise_delta_rule_amd", "csrc")
 _SPLIT_SHA = "3bd845db73cf61e7da7896336a49537137a0b747d5f7fa43b984ec9414a170b4"
 _BWD_SHA = "5ff58afe0bb75c2015f230429ba788df447f227a8b8ef5682d654fa927c1b0e2"
-_FUSED_SHA = "1a883b8ae5a0a6829bb2e34f9cc05037f8b37adfbe58769936c3a87ec1d5f730"
+_FUSED_SHA = "29317383f3b2499e720173d20ac1ff51e05fe9359b34fde2d60f3ca3428ee844"
 _LIO_SHA = "627a8009335ec269a3313bb348dbbb8e2230dded01b1dfc19a85d20d78a2a663"
 TRAFFIC = {
-    # chunk_coef_kernel (3,211.4 / 51,459.4) + chunk_fwd_fused_kernel (223,494.3 / 147,456.4):
+    # chunk_coef_kernel (3,211.4 / 51,459.6) + chunk_fwd_fused_kernel (223,501.4 / 147,456.2):
     # one mdn_chunk_fwd call, the unit the bench times
     "chunk_fwd_fused_kernel": dict(sources=("chunk_fused.hip", "chunk_common.hpp", "mfma.hpp"),
-                                   fetch_kib=3211.4 + 223494.3, write_kib=51459.4 + 147456.4,
+                                   fetch_kib=3211.4 + 223501.4, write_kib=51459.6 + 147456.2,
                                    sha256=_FUSED_SHA),
     "chunk_scan_bf16_kernel": dict(sources=("chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
                                    fetch_kib=268386.1, write_kib=147456.4, sha256=_SPLIT_SHA),
@@ -126,20 +126,20 @@ TRAFFIC = {
                               fetch_kib=134381.8, write_kib=143890.6, sha256=_SPLIT_SHA),
     # the other configurations' calls under the partition the default rule picks: the
     # 400M-like layer (B4 H8 T2048) on the column tiles, chunk_coef_kernel (421.0 / 6,432.0)
-    # + chunk_fwd_fused_kernel (28,161.1 / 20,480.0); the 16K-context layer (B1 H16 T16384)
+    # + chunk_fwd_fused_kernel (28,173.0 / 20,480.0); the 16K-context layer (B1 H16 T16384)
     # on the segment scan (4 segments): chunk_coef_kernel (1,573.0 / 25,728.3), pass 1 of
-    # chunk_fwd_seg_kernel (89,964.5 / 30,720.0), seg_combine_kernel (7,219.5 / 4,096.0) and
-    # pass 2 (87,071.3 / 51,200.0); with mu = 0 (5 segments): 1,061.0 / 25,728.3,
-    # 90,976.2 / 20,480.0, 3,618.0 / 3,072.0, 91,258.6 / 54,272.0
+    # chunk_fwd_seg_kernel (69,028.2 / 26,880.0), seg_combine_kernel (7,215.0 / 4,096.0) and
+    # pass 2 (93,609.3 / 55,040.0); with mu = 0 (5 segments): 1,061.0 / 25,728.3,
+    # 66,819.1 / 15,872.0, 3,618.0 / 3,072.0, 99,119.9 / 58,880.0
     "config1_fused": dict(sources=("chunk_fused.hip", "chunk_common.hpp", "mfma.hpp"),
-                          fetch_kib=421.0 + 28161.1, write_kib=6432.0 + 20480.0,
+                          fetch_kib=421.0 + 28173.0, write_kib=6432.0 + 20480.0,
                           sha256=_FUSED_SHA),
     "config3_segments": dict(sources=("chunk_fused.hip", "chunk_common.hpp", "mfma.hpp"),
-                             fetch_kib=1573.0 + 89964.5 + 7219.5 + 87071.3,
-                             write_kib=25728.3 + 30720.0 + 4096.0 + 51200.0, sha256=_FUSED_SHA),
+                             fetch_kib=1573.0 + 69028.2 + 7215.0 + 93609.3,
+                             write_kib=25728.3 + 26880.0 + 4096.0 + 55040.0, sha256=_FUSED_SHA),
     "config3_segments_no_mu": dict(sources=("chunk_fused.hip", "chunk_common.hpp", "mfma.hpp"),
-                                   fetch_kib=1061.0 + 90976.2 + 3618.0 + 91258.6,
-                                   write_kib=25728.3 + 20480.0 + 3072.0 + 54272.0,
+                                   fetch_kib=1061.0 + 66819.1 + 3618.0 + 99119.9,
+                                   write_kib=25728.3 + 15872.0 + 3072.0 + 58880.0,
                                    sha256=_FUSED_SHA),
     "decode_step_kernel": dict(sources=("decode.hip", "mfma.hpp"), fetch_kib=264109.0,
                                write_kib=525524.5, sha256="8fa39113008b99235e1abe57028f0d81"
@@ -175,7 +175,7 @@ TRAFFIC = {
 # ran, beside the FLOP-derived fraction of the datasheet peak.
 MFMA_BUSY = {
     "chunk_fwd_fused_kernel": dict(sources=TRAFFIC["chunk_fwd_fused_kernel"]["sources"],
-                                   busy=0.390, sha256=TRAFFIC["chunk_fwd_fused_kernel"]["sha256"]),
+                                   busy=0.415, sha256=TRAFFIC["chunk_fwd_fused_kernel"]["sha256"]),
     "chunk_scan_bf16_kernel": dict(sources=TRAFFIC["chunk_scan_bf16_kernel"]["sources"],
                                    busy=0.300, sha256=_SPLIT_SHA),
     "chunk_prep_kernel": dict(sources=TRAFFIC["chunk_prep_kernel"]["sources"], busy=0.107,
@@ -271,7 +271,10 @@ def settle(torch, fns, seconds):
 def time_calls(torch, fns, steps):
     """Mean time (ms) of each of the callables in `fns`, launched in order
     `steps` times on the current stream, from HIP events recorded between
-    them; also the span of the whole sequence per step."""
+    them; and the time per step of `steps` steps run back to back, bracketed
+    by a synchronisation and one HIP event on each side (no events between
+    the steps: each event is a marker the GPU processes between kernels,
+    which added about 5 us per step when recorded around every call)."""
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
           for _ in range(steps)]
     torch.cuda.synchronize()
@@ -282,7 +285,15 @@ def time_calls(torch, fns, steps):
             ev[s][i + 1].record()
     torch.cuda.synchronize()
     means = [sum(e[i].elapsed_time(e[i + 1]) for e in ev) / steps for i in range(len(fns))]
-    span = ev[0][0].elapsed_time(ev[-1][-1]) / steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        for fn in fns:
+            fn()
+    e1.record()
+    torch.cuda.synchronize()
+    span = e0.elapsed_time(e1) / steps
     return means, span
 
 
