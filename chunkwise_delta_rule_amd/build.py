@@ -52,7 +52,7 @@ def hipcc() -> str:
 # Kernels whose explicit vmcnt waits count only their own loads: a register
 # spill would add scratch traffic to the same counter and break those waits,
 # so these must compile without scratch.
-NO_SCRATCH = {"chunk_fused.hip": ("chunk_fwd_fused_kernel",),
+NO_SCRATCH = {"chunk_fused.hip": ("chunk_fwd_fused_kernel", "chunk_fwd_seg_kernel"),
               "chunk_fwd.hip": ("chunk_scan_bf16_kernel",),
               "chunk_bwd.hip": ("bwd_scan_bf16_kernel", "bwd_rescan_bf16_kernel")}
 
