@@ -44,20 +44,18 @@
 //                 fp32 accumulators for the whole sequence (rows of S in the
 //                 permuted order phys_row(), as in chunk_fwd.hip) and works
 //                 through chunk c: X = K [S|M], R, Q [S|M], the substitution,
-//                 O^T (stored as 8-byte rows), the state update.
-//   helper 4..7   helper h owns row block h (rows 16 h .. 16 h + 15).  While
-//                 chunk c is scanned it prepares chunk c + 1 in the other LDS
-//                 buffer: its K, Q rows (loaded into registers one chunk
-//                 earlier, in MFMA fragment layout) to LDS, the V tile and
-//                 the coefficient rows by direct loads, row block h of the
-//                 Gram product P Khat^T masked into -N and D_h, column block
-//                 h of A; and it loads the tables of chunk c + 2.
-// Synchronisation per chunk: B1, among the helpers only, once K, Q of chunk
-// c + 1 are in LDS (each helper's Gram products read the other helpers'
-// rows; the compute wavefronts need nothing from it), and the workgroup
-// barrier B0 once chunk c + 1 is complete, after which the compute
-// wavefronts move on to it and its buffer stops being written.  One more
-// workgroup barrier at the start, for chunk 0's tables.
+//                 O^T (stored as 16-byte row pieces), the state update.
+//   helper 4..7   helper h builds row block h of T and row block 3 - h of A.
+//                 While chunk c is scanned it prepares chunk c + 1 in the
+//                 other operand buffer (its V tile and coefficient rows by
+//                 direct loads, its Gram products from the K and Q tiles in
+//                 LDS, masked into -N, the block inverse D_h and A) and
+//                 issues the direct loads of chunk c + 2's K and Q rows and
+//                 tables.
+// Synchronisation: one workgroup barrier per chunk, B0, once chunk c + 1 is
+// complete and chunk c + 2's loads have landed, after which the compute
+// wavefronts move on to chunk c + 1 and its buffer stops being written; one
+// more at the start, for chunk 0's K, Q tiles and tables.
 #include <hip/hip_runtime.h>
 
 #include "chunk_common.hpp"
@@ -351,11 +349,12 @@ __global__ __launch_bounds__(COEF_HEADS * 64) void chunk_coef_kernel(
 }
 
 // LDS layout of the K and Q tiles of the fused kernel (64 rows x DK bf16),
-// written by the helpers from registers.  Three accesses use it: 16-byte
+// filled by the helpers' direct loads.  Three accesses use it: 16-byte
 // fragments of 16 consecutive rows at one 16-byte chunk (both waves' Gram
 // and state products), transposing reads in which each 16-lane group takes
 // four 8-byte pieces from each of 4 consecutive rows within one 64-byte
-// window, and the helpers' 16-byte stores.  Rows are 2 DK + 32 bytes apart
+// window, and 16-byte lane stores (measured when the helpers still stored
+// the rows from registers; the direct loads write it in 1 KB runs).  Rows are 2 DK + 32 bytes apart
 // and the 16-byte chunks of a row are XOR-permuted by bits 2..3 of the row.
 // Measured on gfx950 with every wavefront of a workgroup issuing each
 // access, all three then run at the rate of a linear access of the same
@@ -515,9 +514,8 @@ __device__ __forceinline__ void fused_body(
     if (wave >= 4) {
         // =================== helper wavefronts ===================
         // Helper W builds row block W of T and row block X = 3 - W of A (five
-        // 16x16 Gram tiles for every helper).  It loads K rows of block W
-        // and Q rows of block X into registers, one chunk ahead, and stores
-        // them to LDS for everyone.
+        // 16x16 Gram tiles for every helper), from the K and Q tiles that all
+        // four helpers' direct loads bring to LDS a chunk ahead.
         const int hw = wave - 4;
         const unsigned v_lane = LC::lane_offset((unsigned)(H * DV), lane);
         // 16x16 product X Y from acc(X^T) and acc(Y), where acc(Z) is the
