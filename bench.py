@@ -112,7 +112,7 @@ WRITE_FACTOR = 131072.0 / 131072.0
 CSRC = os.path.join(ROOT, "chunkwise_delta_rule_amd", "csrc")
 _SPLIT_SHA = "3bd845db73cf61e7da7896336a49537137a0b747d5f7fa43b984ec9414a170b4"
 _BWD_SHA = "5ff58afe0bb75c2015f230429ba788df447f227a8b8ef5682d654fa927c1b0e2"
-_FUSED_SHA = "d5aaa744a83163ea1e4c6b1a7b318643cb4ca6396cdcc2a618266eaafce9bf0d"
+_FUSED_SHA = "24ac34770bdef1e6240a3e3c8c87a37fd6ff035907f6b59407384dc8f95348b7"
 _LIO_SHA = "627a8009335ec269a3313bb348dbbb8e2230dded01b1dfc19a85d20d78a2a663"
 TRAFFIC = {
     # chunk_coef_kernel (3,211.4 / 51,459.6) + chunk_fwd_fused_kernel (223,501.4 / 147,456.2):

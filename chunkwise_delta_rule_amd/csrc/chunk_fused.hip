@@ -354,8 +354,9 @@ __global__ __launch_bounds__(COEF_HEADS * 64) void chunk_coef_kernel(
 // and state products), transposing reads in which each 16-lane group takes
 // four 8-byte pieces from each of 4 consecutive rows within one 64-byte
 // window, and 16-byte lane stores (measured when the helpers still stored
-// the rows from registers; the direct loads write it in 1 KB runs).  Rows are 2 DK + 32 bytes apart
-// and the 16-byte chunks of a row are XOR-permuted by bits 2..3 of the row.
+// the rows from registers; the direct loads write it in 1 KB runs).  Rows
+// are 2 DK + 32 bytes apart and the 16-byte chunks of a row are
+// XOR-permuted by bits 2..3 of the row.
 // Measured on gfx950 with every wavefront of a workgroup issuing each
 // access, all three then run at the rate of a linear access of the same
 // width; plain row strides of 2 DK or 2 DK + 64 bytes do not (the 16-row
