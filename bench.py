@@ -110,8 +110,8 @@ GATE_TAU = (2048 / 16) ** 0.5            # the temperature sqrt(d_in / h) at d_i
 FETCH_FACTOR = 262144.0 / 131093.9
 WRITE_FACTOR = 131072.0 / 131072.0
 CSRC = os.path.join(ROOT, "chunkwise_delta_rule_amd", "csrc")
-_SPLIT_SHA = "3bd845db73cf61e7da7896336a49537137a0b747d5f7fa43b984ec9414a170b4"
-_BWD_SHA = "5ff58afe0bb75c2015f230429ba788df447f227a8b8ef5682d654fa927c1b0e2"
+_SPLIT_SHA = "23db79fb54c36e5f70317570bd09800d39d9d5a55e4505d9a027b2441b2c81b4"
+_BWD_SHA = "baf873aafa47a4b440682fd18e54dd42c28bbc959f41197f7bbe40b079e065cd"
 _FUSED_SHA = "24ac34770bdef1e6240a3e3c8c87a37fd6ff035907f6b59407384dc8f95348b7"
 _LIO_SHA = "627a8009335ec269a3313bb348dbbb8e2230dded01b1dfc19a85d20d78a2a663"
 TRAFFIC = {
@@ -121,9 +121,9 @@ TRAFFIC = {
                                    fetch_kib=3211.4 + 223501.4, write_kib=51459.6 + 147456.2,
                                    sha256=_FUSED_SHA),
     "chunk_scan_bf16_kernel": dict(sources=("chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
-                                   fetch_kib=268386.1, write_kib=147456.4, sha256=_SPLIT_SHA),
+                                   fetch_kib=268387.0, write_kib=147457.6, sha256=_SPLIT_SHA),
     "chunk_prep_kernel": dict(sources=("chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
-                              fetch_kib=134381.8, write_kib=143890.6, sha256=_SPLIT_SHA),
+                              fetch_kib=134327.7, write_kib=143909.4, sha256=_SPLIT_SHA),
     # the other configurations' calls under the partition the default rule picks: the
     # 400M-like layer (B4 H8 T2048) on the column tiles, chunk_coef_kernel (421.0 / 6,432.0)
     # + chunk_fwd_fused_kernel (28,173.0 / 20,480.0); the 16K-context layer (B1 H16 T16384)
@@ -145,18 +145,18 @@ TRAFFIC = {
                                write_kib=525524.5, sha256="8fa39113008b99235e1abe57028f0d81"
                                "9b837f475aa87000a6b4e46e3ea6c4e5"),
     # one mdn_chunk_bwd call with the forward's saved residuals: chunk_prep_kernel
-    # (134,382.7 / 143,912.2) + bwd_scan_bf16_kernel (268,439.3 / 786,475.7) +
-    # bwd_rescan_bf16_kernel with saved residuals (137,303.1 / 524,288.2) +
-    # bwd_grad_bf16_kernel<..., true> (929,689.8 / 544,367.0)
+    # (134,327.7 / 143,909.4) + bwd_scan_bf16_kernel (268,439.2 / 786,490.1) +
+    # bwd_rescan_bf16_kernel with saved residuals (137,299.6 / 524,288.6) +
+    # bwd_grad_bf16_kernel<..., true> (929,570.3 / 544,532.0)
     "chunk_bwd": dict(sources=("chunk_bwd.hip", "chunk_fwd.hip", "chunk_common.hpp", "mfma.hpp"),
-                      fetch_kib=134382.7 + 268439.3 + 137303.1 + 929689.8,
-                      write_kib=143912.2 + 786475.7 + 524288.2 + 544367.0, sha256=_BWD_SHA),
-    # the same recomputing the residuals: bwd_rescan_bf16_kernel (170,163.9 / 786,458.9),
-    # bwd_grad_bf16_kernel<..., false> (994,752.8 / 543,059.3)
+                      fetch_kib=134327.7 + 268439.2 + 137299.6 + 929570.3,
+                      write_kib=143909.4 + 786490.1 + 524288.6 + 544532.0, sha256=_BWD_SHA),
+    # the same recomputing the residuals: bwd_rescan_bf16_kernel (170,149.6 / 786,461.9),
+    # bwd_grad_bf16_kernel<..., false> (994,744.1 / 542,284.8)
     "chunk_bwd_recompute": dict(sources=("chunk_bwd.hip", "chunk_fwd.hip", "chunk_common.hpp",
                                          "mfma.hpp"),
-                                fetch_kib=134382.7 + 268439.3 + 170163.9 + 994752.8,
-                                write_kib=143912.2 + 786475.7 + 786458.9 + 543059.3,
+                                fetch_kib=134327.7 + 268439.2 + 170149.6 + 994744.1,
+                                write_kib=143909.4 + 786490.1 + 786461.9 + 542284.8,
                                 sha256=_BWD_SHA),
     "qk_prologue_kernel": dict(sources=("layer_io.hip", "mfma.hpp"), fetch_kib=131099.8,
                                write_kib=262144.0, sha256=_LIO_SHA),
@@ -177,8 +177,8 @@ MFMA_BUSY = {
     "chunk_fwd_fused_kernel": dict(sources=TRAFFIC["chunk_fwd_fused_kernel"]["sources"],
                                    busy=0.415, sha256=TRAFFIC["chunk_fwd_fused_kernel"]["sha256"]),
     "chunk_scan_bf16_kernel": dict(sources=TRAFFIC["chunk_scan_bf16_kernel"]["sources"],
-                                   busy=0.300, sha256=_SPLIT_SHA),
-    "chunk_prep_kernel": dict(sources=TRAFFIC["chunk_prep_kernel"]["sources"], busy=0.107,
+                                   busy=0.293, sha256=_SPLIT_SHA),
+    "chunk_prep_kernel": dict(sources=TRAFFIC["chunk_prep_kernel"]["sources"], busy=0.111,
                               sha256=_SPLIT_SHA),
 }
 

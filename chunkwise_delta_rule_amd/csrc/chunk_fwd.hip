@@ -147,12 +147,18 @@ __device__ __forceinline__ float lane_bcast(float x, int lane)
 // ---------------------------------------------------------------------------
 // Per-chunk preparation
 // ---------------------------------------------------------------------------
+// With bf16 I/O, Q never enters LDS (each wavefront loads its own row tile's
+// MFMA fragments from memory) and L is written over Gamma once the masks have
+// read it: region0 holds K, later T; region1 Gamma, later L.  That is 35.9 KB
+// at DK = 128, four workgroups per CU.  With fp32 I/O, region0 holds K and Q,
+// later L and T.
 template <typename E, int DK>
 struct PrepSmem {
+    static constexpr bool QREG = sizeof(E) == 2;
     static constexpr int LDK = DK + Mma<E>::PAD;
     static constexpr int LDG = CH + 4;   // fp32 C x C matrices; 4 rows apart = 16 banks apart
-    static constexpr size_t kq_bytes = 2 * CH * LDK * sizeof(E);
-    static constexpr size_t lt_bytes = 2 * CH * LDG * sizeof(float);
+    static constexpr size_t kq_bytes = (QREG ? 1 : 2) * CH * LDK * sizeof(E);
+    static constexpr size_t lt_bytes = (QREG ? 1 : 2) * CH * LDG * sizeof(float);
     static constexpr size_t region0 = kq_bytes > lt_bytes ? kq_bytes : lt_bytes;
     static constexpr size_t region1 = CH * LDG * sizeof(float);
 };
@@ -168,8 +174,8 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
     using SM = PrepSmem<E, DK>;
     constexpr int LDK = SM::LDK;
     constexpr int LDG = SM::LDG;
+    constexpr bool QREG = SM::QREG;
 
-    // region0: K and Q rows, later L and T (fp32); region1: Gamma
     __shared__ __align__(16) char smem0[SM::region0];
     __shared__ __align__(16) char smem1[SM::region1];
     __shared__ __align__(16) float al[CH];
@@ -177,10 +183,10 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
     __shared__ __align__(16) float et[CH];
     __shared__ __align__(16) float bts[CH];
     E* Ks = reinterpret_cast<E*>(smem0);
-    E* Qs = Ks + CH * LDK;
-    float* Ls = reinterpret_cast<float*>(smem0);
-    float* Ts = Ls + CH * LDG;
+    E* Qs = Ks + CH * LDK;   // fp32 I/O only
     float* Gam = reinterpret_cast<float*>(smem1);
+    float* Ls = QREG ? Gam : reinterpret_cast<float*>(smem0);
+    float* Ts = QREG ? reinterpret_cast<float*>(smem0) : Ls + CH * LDG;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
@@ -210,7 +216,17 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
     }
     RowTile<E, DK> kt, qt;
     kt.load(k + tok0 * DK, (unsigned)(H * DK), n, tid);
-    qt.load(q + tok0 * DK, (unsigned)(H * DK), n, tid);
+    // bf16: this lane's A fragments of Q K^T, row 16 wave + l16 (rows >= n
+    // read row n - 1 and are zeroed where used)
+    typename MM::frag aQf[DK / MM::KSTEP];
+    const int qrow = 16 * wave + l16;
+    if constexpr (QREG) {
+        const E* qr = q + tok0 * DK + (size_t)min(qrow, n - 1) * (H * DK) + MM::KW * lg;
+#pragma unroll
+        for (int s = 0; s < DK / MM::KSTEP; ++s) aQf[s] = MM::load(qr + MM::KSTEP * s);
+    } else {
+        qt.load(q + tok0 * DK, (unsigned)(H * DK), n, tid);
+    }
     if (wave == 0) {
         al[lane] = a_l;
         mus[lane] = m_l;
@@ -327,7 +343,7 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
     }
 
     kt.template store<LDK>(Ks, tid);
-    qt.template store<LDK>(Qs, tid);
+    if constexpr (!QREG) qt.template store<LDK>(Qs, tid);
     __syncthreads();
 
     // ---- G = K K^T and P = Q K^T on the lower block triangle: wave w owns
@@ -341,7 +357,11 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
     for (int ks = 0; ks < DK; ks += MM::KSTEP) {
         const int kk = ks + MM::KW * lg;
         const auto aK = MM::load(Ks + (16 * wave + l16) * LDK + kk);
-        const auto aQ = MM::load(Qs + (16 * wave + l16) * LDK + kk);
+        typename MM::frag aQ;
+        if constexpr (QREG)
+            aQ = qrow < n ? aQf[ks / MM::KSTEP] : typename MM::frag{};
+        else
+            aQ = MM::load(Qs + (16 * wave + l16) * LDK + kk);
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
             if (ct <= wave) {
@@ -377,11 +397,13 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
         Vch[V_SCAL * CH + lane] = scal;
     }
 
-    // ---- L = I + (P Khat^T) o Gamma^- into LDS (over K/Q, no longer read)
-    //      and A = (Q Khat^T) o Gamma straight to the workspace, 4 columns of
-    //      row i per lane
+    // ---- L = I + (P Khat^T) o Gamma^- into LDS (bf16: over Gamma, after
+    //      every wavefront has read it; fp32: over K/Q, no longer read) and
+    //      A = (Q Khat^T) o Gamma straight to the workspace, 4 columns of row
+    //      i per lane
     E* Ach = Aw + ch * CH * CH;
     {
+        f32x4 lrow[4];
         const int i = 16 * wave + l16;
         const float ai = al[i];
         const float* g0row = Gam + i * LDG;
@@ -401,8 +423,15 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
                     av[r] = j <= i ? accP[ct][r] * e4[r] * g0[r] : 0.f;
                 }
             }
-            *reinterpret_cast<f32x4*>(Ls + i * LDG + j0) = lv;
+            lrow[ct] = lv;
+            if constexpr (!QREG) *reinterpret_cast<f32x4*>(Ls + i * LDG + j0) = lv;
             store4<E>(Ach + i * CH + j0, av[0], av[1], av[2], av[3]);
+        }
+        if constexpr (QREG) {
+            __syncthreads();   // Gamma no longer read
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+                *reinterpret_cast<f32x4*>(Ls + i * LDG + 16 * ct + 4 * lg) = lrow[ct];
         }
     }
     __syncthreads();
