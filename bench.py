@@ -110,8 +110,8 @@ GATE_TAU = (2048 / 16) ** 0.5            # the temperature sqrt(d_in / h) at d_i
 FETCH_FACTOR = 262144.0 / 131093.9
 WRITE_FACTOR = 131072.0 / 131072.0
 CSRC = os.path.join(ROOT, "chunkwise_delta_rule_amd", "csrc")
-_SPLIT_SHA = "23db79fb54c36e5f70317570bd09800d39d9d5a55e4505d9a027b2441b2c81b4"
-_BWD_SHA = "baf873aafa47a4b440682fd18e54dd42c28bbc959f41197f7bbe40b079e065cd"
+_SPLIT_SHA = "4c566b0ae7c2d13b3231f4104da8130aabf3c8d4d6bdd74f3a0e879a52ee8e85"
+_BWD_SHA = "69e0712028edb127a8a18ce0511732f031077c24d0119ba9b3e8389faf6a4536"
 _FUSED_SHA = "24ac34770bdef1e6240a3e3c8c87a37fd6ff035907f6b59407384dc8f95348b7"
 _LIO_SHA = "627a8009335ec269a3313bb348dbbb8e2230dded01b1dfc19a85d20d78a2a663"
 TRAFFIC = {

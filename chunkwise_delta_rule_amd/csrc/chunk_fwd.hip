@@ -204,8 +204,9 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
 
     // gates of this chunk, one row per lane (rows >= n: alpha 1, mu 0, eta 0,
     // beta 0); beta is 1 when no beta gate is given.  K and Q are loaded next
-    // into registers and stored to LDS only after the coefficient pass, which
-    // needs the gates alone, so their latency overlaps it.
+    // into registers (bf16: Q as this wavefront's MFMA fragments, never
+    // stored) and K (fp32: K and Q) reaches LDS only after the coefficient
+    // pass, which needs the gates alone, so their latency overlaps it.
     float a_l = 1.f, m_l = 0.f, e_l = 0.f, s_l = 0.f;
     if (lane < n) {
         const size_t g = tok0 + (size_t)lane * H;
